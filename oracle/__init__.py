@@ -1,0 +1,8 @@
+"""CPU oracle (test infrastructure only; see mxfp4_oracle's docstring)."""
+from .mxfp4_oracle import *  # noqa: F401,F403
+from .mxfp4_oracle import (  # noqa: F401
+    BLOCK, E2M1_TABLE, E2M1_MAGNITUDES, e2m1_value, e8m0_value,
+    bf16_bits_to_f64, f64_to_bf16_bits, shared_exponent, encode_e2m1_magnitude,
+    quantize_block_values, pack_codes, unpack_codes, quantize, dequantize,
+    gemm_nt, gemm_nt_f32, grouped_gemm_nt, round_output_bf16, floored_max_rel,
+)
