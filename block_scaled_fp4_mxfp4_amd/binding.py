@@ -1,0 +1,188 @@
+"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h).
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.  The
+functions carry the C entry points' names.  If the library is missing or the
+current device is not gfx950 these calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmxfp4.so")
+
+MXFP4_OK = 0
+MXFP4_OUT_BF16 = 0
+MXFP4_OUT_F32 = 1
+KERNELS = {"auto": 0, "tile256": 1, "tile128": 2, "splitk": 3}
+
+EXPORTED = (
+    "mxfp4_abi_version", "mxfp4_status_string", "mxfp4_last_error", "mxfp4_quantize",
+    "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
+    "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
+)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class MXFP4Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"mxfp4 status {status}: {detail}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libmxfp4.so and declares its signatures (raises if it is absent)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        lib.mxfp4_abi_version.restype = ctypes.c_int
+        lib.mxfp4_abi_version.argtypes = []
+        lib.mxfp4_status_string.restype = ctypes.c_char_p
+        lib.mxfp4_status_string.argtypes = [ctypes.c_int]
+        lib.mxfp4_last_error.restype = ctypes.c_char_p
+        lib.mxfp4_last_error.argtypes = []
+        lib.mxfp4_quantize.restype = ctypes.c_int
+        lib.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_gemm_nt_workspace_size.restype = sz
+        lib.mxfp4_gemm_nt_workspace_size.argtypes = [i64, i64, i64]
+        lib.mxfp4_gemm_nt.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]
+        lib.mxfp4_gemm_nt_ex_workspace_size.restype = sz
+        lib.mxfp4_gemm_nt_ex_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int, i32]
+        lib.mxfp4_gemm_nt_ex.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64,
+                                         ctypes.c_int, i32, vp, sz, vp]
+        lib.mxfp4_grouped_gemm_nt_workspace_size.restype = sz
+        lib.mxfp4_grouped_gemm_nt_workspace_size.argtypes = [i64, i32, i64, i64]
+        lib.mxfp4_grouped_gemm_nt.restype = ctypes.c_int
+        lib.mxfp4_grouped_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64,
+                                              vp, sz, vp]
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != MXFP4_OK:
+        lib = load_library()
+        raise MXFP4Error(status, f"{lib.mxfp4_status_string(status).decode()}: "
+                                 f"{lib.mxfp4_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, shape):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor | None:
+    """A zero-filled, reusable per-device workspace of at least `nbytes` bytes.
+
+    The library leaves a workspace zero-filled after every call, so one
+    buffer (grown on demand) serves every stream-ordered call on a device.
+    """
+    if nbytes == 0:
+        return None
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index)
+    ws = _workspaces.get(dev)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[dev] = ws
+    return ws
+
+
+def mxfp4_quantize(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   stream=None):
+    """x: bf16 [rows, k] -> (q uint8 [rows, k/2], scales uint8 [rows, k/32])."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, k]")
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(q, "q", torch.uint8, (rows, k // 2))
+    _require(scales, "scales", torch.uint8, (rows, k // 32))
+    _check(lib.mxfp4_quantize(_ptr(x), rows, k, _ptr(q), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def _out(c, m, n, out_dtype, device):
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=device)
+    code = MXFP4_OUT_F32 if c.dtype == torch.float32 else MXFP4_OUT_BF16
+    _require(c, "c", torch.float32 if code == MXFP4_OUT_F32 else torch.bfloat16, (m, n))
+    return c, code
+
+
+def mxfp4_gemm_nt(a_q, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: str = "auto",
+                  splits: int = 0, ws: torch.Tensor | None = None, stream=None):
+    """C[m, n] = A[m, k] . B[n, k]^T on MXFP4 operands (bf16 or fp32 output)."""
+    lib = load_library()
+    m, kh = a_q.shape
+    n = b_q.shape[0]
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (m, k // 2))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (n, k // 32))
+    c, code = _out(c, m, n, out_dtype, a_q.device)
+    kid = KERNELS[kernel]
+    need = lib.mxfp4_gemm_nt_ex_workspace_size(m, n, k, kid, splits)
+    if ws is None:
+        ws = workspace(need, a_q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxfp4_gemm_nt_ex(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
+                                kid, splits, _ptr(ws), nbytes, _stream(stream)))
+    return c
+
+
+def mxfp4_grouped_gemm_nt(a_q, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.bfloat16,
+                          ws: torch.Tensor | None = None, stream=None):
+    """Per-group NT GEMM; `offsets` is a device int32 [groups + 1] tensor."""
+    lib = load_library()
+    total_m, kh = a_q.shape
+    groups, n, _ = b_q.shape
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (total_m, k // 2))
+    _require(a_s, "a_s", torch.uint8, (total_m, k // 32))
+    _require(b_q, "b_q", torch.uint8, (groups, n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (groups, n, k // 32))
+    _require(offsets, "offsets", torch.int32, (groups + 1,))
+    c, code = _out(c, total_m, n, out_dtype, a_q.device)
+    need = lib.mxfp4_grouped_gemm_nt_workspace_size(total_m, groups, n, k)
+    if ws is None:
+        ws = workspace(need, a_q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxfp4_grouped_gemm_nt(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), groups,
+                                     total_m, _ptr(c), code, n, k, _ptr(ws), nbytes, _stream(stream)))
+    return c

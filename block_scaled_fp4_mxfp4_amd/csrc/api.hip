@@ -1,0 +1,262 @@
+// C ABI of the MXFP4 library: argument checks, per-shape kernel choice, launches.
+// Entry points and their contracts are documented in include/mxfp4.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mxfp4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mxfp4_status_t fail(mxfp4_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+struct DeviceInfo {
+  bool valid = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_devices_mutex;
+
+mxfp4_status_t current_device(DeviceInfo& out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MXFP4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MXFP4_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_devices_mutex);
+  DeviceInfo& d = g_devices[dev];
+  if (!d.valid) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MXFP4_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.valid = true;
+  }
+  out = d;
+  if (!out.gfx950) return fail(MXFP4_ERR_UNSUPPORTED, "the current device is not gfx950");
+  return MXFP4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // keeps every internal index in int32 range
+
+mxfp4_status_t check_k(int64_t k) {
+  if (k <= 0 || k % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "k must be a positive multiple of 32 (got %lld)", (long long)k);
+  if (k > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "k too large (%lld)", (long long)k);
+  return MXFP4_OK;
+}
+
+mxfp4_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MXFP4_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MXFP4_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MXFP4_OK;
+}
+
+mxfp4_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MXFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MXFP4_OK;
+}
+
+#define MXFP4_TRY(expr)                 \
+  do {                                  \
+    mxfp4_status_t s_ = (expr);         \
+    if (s_ != MXFP4_OK) return s_;      \
+  } while (0)
+
+struct Choice {
+  mxfp4_kernel_t kernel;
+  int splits;
+};
+
+// Per-shape kernel choice.
+Choice choose(int64_t m, int64_t n, int64_t k, int num_cus) {
+  if (m <= 128) return {MXFP4_KERNEL_SPLITK, mxfp4::splitk_auto_splits((int)m, (int)n, (int)k, num_cus)};
+  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+  if (tiles256 >= num_cus) return {MXFP4_KERNEL_TILE256, 0};
+  return {MXFP4_KERNEL_TILE128, 0};
+}
+
+mxfp4_status_t resolve(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits,
+                       int num_cus, Choice& out) {
+  switch (kernel) {
+    case MXFP4_KERNEL_AUTO: out = choose(m, n, k, num_cus); return MXFP4_OK;
+    case MXFP4_KERNEL_TILE256:
+    case MXFP4_KERNEL_TILE128: out = {kernel, 0}; return MXFP4_OK;
+    case MXFP4_KERNEL_SPLITK:
+      if (m > 128) return fail(MXFP4_ERR_INVALID_ARG, "the split-K kernel takes m <= 128 (got %lld)", (long long)m);
+      if (splits < 0 || splits > 64) return fail(MXFP4_ERR_INVALID_ARG, "splits must be 0..64 (got %d)", splits);
+      out = {kernel, splits == 0 ? mxfp4::splitk_auto_splits((int)m, (int)n, (int)k, num_cus) : splits};
+      return MXFP4_OK;
+  }
+  return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
+}
+
+size_t workspace_for(const Choice& c, int64_t m, int64_t n, int64_t k) {
+  if (c.kernel == MXFP4_KERNEL_SPLITK) return mxfp4::splitk_workspace_bytes((int)m, (int)n, (int)k, c.splits);
+  return 0;
+}
+
+int query_num_cus() {
+  DeviceInfo d;
+  if (current_device(d) != MXFP4_OK) return 256;
+  return d.num_cus;
+}
+
+mxfp4_status_t check_gemm_args(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
+                               const void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
+  MXFP4_TRY(check_k(k));
+  if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (m > 0) {
+    MXFP4_TRY(check_ptr(a_q, "a_q"));
+    MXFP4_TRY(check_ptr(a_s, "a_s"));
+  }
+  if (n > 0) {
+    MXFP4_TRY(check_ptr(b_q, "b_q"));
+    MXFP4_TRY(check_ptr(b_s, "b_s"));
+  }
+  if (m > 0 && n > 0) MXFP4_TRY(check_ptr(c, "c"));
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_abi_version(void) { return MXFP4_ABI_VERSION; }
+
+const char* mxfp4_status_string(mxfp4_status_t s) {
+  switch (s) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_INVALID_ARG: return "invalid argument";
+    case MXFP4_ERR_UNSUPPORTED: return "unsupported device";
+    case MXFP4_ERR_WORKSPACE: return "workspace too small";
+    case MXFP4_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mxfp4_last_error(void) { return g_last_error; }
+
+mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q, void* scales,
+                              void* stream) {
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
+  MXFP4_TRY(check_k(k));
+  if (rows > ((int64_t)1 << 40) / k) return fail(MXFP4_ERR_INVALID_ARG, "rows * k too large");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(q, "q"));
+  MXFP4_TRY(check_ptr(scales, "scales"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_quantize(x_bf16, rows, k, q, scales, (hipStream_t)stream, dev.num_cus),
+                    "quantize launch");
+}
+
+size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return 0;
+  Choice c;
+  if (resolve(m, n, k, kernel, splits, query_num_cus(), c) != MXFP4_OK) return 0;
+  return workspace_for(c, m, n, k);
+}
+
+size_t mxfp4_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {
+  return mxfp4_gemm_nt_ex_workspace_size(m, n, k, MXFP4_KERNEL_AUTO, 0);
+}
+
+mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
+                                void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                mxfp4_kernel_t kernel, int32_t splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q, a_s, b_q, b_s, c, c_type, m, n, k));
+  if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_SPLITK)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  Choice ch;
+  MXFP4_TRY(resolve(m, n, k, kernel, splits, dev.num_cus, ch));
+  const size_t need = workspace_for(ch, m, n, k);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(MXFP4_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  }
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  hipError_t e;
+  switch (ch.kernel) {
+    case MXFP4_KERNEL_SPLITK: e = mxfp4::launch_gemm_splitk(args, ch.splits, workspace, (hipStream_t)stream); break;
+    case MXFP4_KERNEL_TILE128: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile128, (hipStream_t)stream); break;
+    default: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile256, (hipStream_t)stream); break;
+  }
+  return hip_status(e, "gemm launch");
+}
+
+mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, void* c,
+                             mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return mxfp4_gemm_nt_ex(a_q, a_s, b_q, b_s, c, c_type, m, n, k, MXFP4_KERNEL_AUTO, 0, workspace,
+                          workspace_bytes, stream);
+}
+
+size_t mxfp4_grouped_gemm_nt_workspace_size(int64_t total_m, int32_t num_groups, int64_t n, int64_t k) {
+  (void)total_m; (void)num_groups; (void)n; (void)k;
+  return 0;
+}
+
+mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
+                                     const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
+                                     mxfp4_out_t c_type, int64_t n, int64_t k, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  MXFP4_TRY(check_gemm_args(a_q, a_s, b_q, b_s, c, c_type, total_m, n, k));
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(MXFP4_ERR_INVALID_ARG, "num_groups must be 1..1024 (got %d)", num_groups);
+  if (total_m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(offsets, "offsets"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)total_m;
+  args.n = (int)n;
+  args.k = (int)k;
+  args.offsets = offsets;
+  args.groups = num_groups;
+  const mxfp4::TileKind kind = (total_m / num_groups >= 192) ? mxfp4::kTile256 : mxfp4::kTile128;
+  return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
+}
+
+}  // extern "C"

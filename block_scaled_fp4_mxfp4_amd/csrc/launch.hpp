@@ -1,0 +1,37 @@
+// Host-side launch functions of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+struct GemmArgs {
+  const uint8_t* a_q;      // [m, k/2]
+  const uint8_t* a_s;      // [m, k/32]
+  const uint8_t* b_q;      // [n, k/2] (grouped: [groups, n, k/2])
+  const uint8_t* b_s;      // [n, k/32] (grouped: [groups, n, k/32])
+  void* c;                 // [m, n]
+  int c_f32;               // 0: bf16 output, 1: fp32 output
+  int m, n, k;             // grouped: m = total_m
+  const int32_t* offsets;  // grouped only: device [groups + 1]
+  int groups;              // grouped only
+};
+
+// Tile kernels (TILE256: 256x256 output tiles, TILE128: 128x128 output tiles).
+enum TileKind { kTile256 = 0, kTile128 = 1 };
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                           hipStream_t stream, int num_cus);
+
+hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
+
+hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
+
+// Bandwidth path for m <= 128: K split over `splits` workgroups per 64-column
+// tile, fp32 partials and per-tile arrival counters in `workspace`.
+size_t splitk_workspace_bytes(int m, int n, int k, int splits);
+int splitk_auto_splits(int m, int n, int k, int num_cus);
+hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
+                              hipStream_t stream);
+
+}  // namespace mxfp4

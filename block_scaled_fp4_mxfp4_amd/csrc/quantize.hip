@@ -1,0 +1,112 @@
+// BF16 -> MXFP4 dynamic block quantization for gfx950.
+//
+// Operation ("fp4_quantization" Mojo module page, quantize_dynamic_block_scaled_mxfp4:
+// BF16 elements to packed MXFP4 with E8M0 block scales over a flat buffer):
+// per 32-element block, amax -> shared exponent e = floor(log2 amax) - 2 clamped
+// to the E8M0 range -> each element x / 2^e rounded to nearest-even E2M1 with
+// saturation at 6, two codes per byte (element 2j in the low nibble).
+//
+// Layout: because K is a multiple of 32 and all three arrays are row-major, the
+// rows x K input is a flat sequence of blocks; block b reads bytes [64b, 64b+64)
+// of x, writes bytes [16b, 16b+16) of q and byte b of the scales.
+//
+// Mapping: 4 lanes per block, 16 bytes (8 BF16) per lane, so one wave64 covers
+// 16 blocks with 1 KiB of fully coalesced loads.  HBM-bound: 2.53125 bytes per
+// element (2 in, 0.5 + 1/32 out).
+//
+// Arithmetic:
+//  * amax is an integer max over the BF16 magnitude bits (x & 0x7FFF): for
+//    non-negative finite floats bit order equals value order.
+//  * floor(log2 amax) = E - 127 for a normal amax with biased exponent E, so the
+//    scale byte is e + 127 = E - 2.  Every amax below 2^-125 (E <= 2, including
+//    subnormals and zero) lands on the lower clamp e = -127, byte 0.  Finite
+//    BF16 has E <= 254, so the byte never exceeds 252 and the upper clamp never
+//    applies.  Hence byte = max(E - 2, 0).
+//  * The element encoding uses the CDNA4 convert v_cvt_scalef32_pk_fp4_bf16,
+//    which divides by the power of two held in the exponent field of its fp32
+//    scale operand (only that field is read, so exponent field 0 means 2^-127)
+//    and rounds to nearest-even with saturation.  Passing (byte << 23) as the
+//    scale's bits therefore applies exactly 2^-e.  That this instruction agrees
+//    with the reference encoding for every finite BF16 input and every scale
+//    byte was checked exhaustively on the device before it was adopted, and the
+//    parity tests re-check it through this kernel.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxfp4 {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantUnroll = 4;   // blocks in flight per lane group
+
+__device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
+  // independent max of the low and high 16-bit halves
+  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
+// max over the 4 lanes of an aligned quad (DPP quad permutes)
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);   // lane ^ 1
+  v = max(v, o);
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);            // lane ^ 2
+  return max(v, o);
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
+    const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ scales,
+    int64_t nblocks) {
+  const int lane4 = threadIdx.x & 3;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
+  int64_t blk = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2);
+
+  for (; blk < nblocks; blk += groups_per_grid * kQuantUnroll) {
+    uint4 v[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const int64_t b = blk + u * groups_per_grid;
+      // out-of-range groups load a valid block (block 0) and store nothing
+      v[u] = x[(b < nblocks ? b : 0) * 4 + lane4];
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const int64_t b = blk + u * groups_per_grid;
+      const uint32_t m01 = umax16x2(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu);
+      const uint32_t m23 = umax16x2(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu);
+      const uint32_t m = umax16x2(m01, m23);
+      uint32_t amax_bits = max(m & 0xFFFFu, m >> 16);
+      amax_bits = quad_max(amax_bits);
+      const int exp_field = (int)(amax_bits >> 7);
+      const uint32_t sbyte = (uint32_t)max(exp_field - 2, 0);
+      const float scale = __uint_as_float(sbyte << 23);
+      uint32_t packed = 0;
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].x), scale, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].y), scale, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].z), scale, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].w), scale, 3);
+      if (b < nblocks) {
+        q[b * 4 + lane4] = packed;
+        if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                           hipStream_t stream, int num_cus) {
+  const int64_t nblocks = rows * (k / 32);
+  const int64_t groups_needed = (nblocks + kQuantUnroll - 1) / kQuantUnroll;
+  int64_t grid = (groups_needed + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
+  const int64_t max_grid = (int64_t)num_cus * 8;
+  if (grid > max_grid) grid = max_grid;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                     (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,189 @@
+/*
+ * mxfp4.h - C ABI of the MI355X (gfx950) MXFP4 quantize / GEMM library.
+ *
+ * Formats (the "Packed MXFP4 & NVFP4 GEMM + mega-MoE (SM100, true 2-CTA
+ * multicast)" page, Summary; the "fp4_quantization" Mojo module page,
+ * quantize_dynamic_block_scaled_mxfp4 and matmul_dynamic_block_scaled_mxfp4):
+ *   - an MXFP4 operand of `rows` x `k` elements is a pair of row-major byte
+ *     arrays, K innermost:
+ *       q      uint8 [rows, k/2]   E2M1 codes, element 2j in the low nibble
+ *                                  of byte j, element 2j+1 in the high nibble;
+ *       scales uint8 [rows, k/32]  one E8M0 byte per 32 consecutive elements
+ *                                  of a row (byte b means 2^(b-127)).
+ *   - E2M1 code: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
+ *     magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *
+ * Conventions shared by every entry point:
+ *   - All buffer pointers are device pointers on the calling thread's current
+ *     HIP device.  Buffers are owned by the caller; the library never frees,
+ *     keeps or allocates memory on these paths.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous: they enqueue kernels and return without
+ *     synchronising, so they may be captured into a HIP graph.
+ *   - All arguments are checked on the host before anything is launched; a
+ *     failed check returns a non-OK status and launches nothing.  Device
+ *     buffers must be 16-byte aligned.  Sizes are elements, not bytes.
+ *   - A zero-sized problem (rows, m, n or total_m equal to 0) is a valid no-op.
+ *   - No call aborts or throws; mxfp4_last_error() gives a thread-local text
+ *     describing the last non-OK status.
+ *   - Calls are reentrant; the only global state is a per-device cache of
+ *     device properties filled on first use.
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP4_ABI_VERSION 1
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, bad enum */
+  MXFP4_ERR_UNSUPPORTED = 2,   /* the current device is not gfx950 */
+  MXFP4_ERR_WORKSPACE = 3,     /* workspace smaller than the size query returned */
+  MXFP4_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} mxfp4_status_t;
+
+typedef enum {
+  MXFP4_OUT_BF16 = 0,          /* C is bfloat16, rounded to nearest-even from fp32 */
+  MXFP4_OUT_F32 = 1            /* C is float32 (the fp32 accumulator, unrounded) */
+} mxfp4_out_t;
+
+/* ABI version of the loaded library (MXFP4_ABI_VERSION it was built with). */
+int mxfp4_abi_version(void);
+
+/* Text for a status code (static storage). */
+const char* mxfp4_status_string(mxfp4_status_t status);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char* mxfp4_last_error(void);
+
+/*
+ * Dynamic block-scaled quantization BF16 -> MXFP4 ("fp4_quantization" page,
+ * quantize_dynamic_block_scaled_mxfp4: BF16 elements to packed MXFP4 with
+ * E8M0 block scales; the quadbit README, Accuracy: per-32 single-level
+ * activation quantization with an amax recipe).
+ *
+ * For each row and each 32-element block x[0..31] along K:
+ *   amax = max |x_i|;
+ *   e = floor(log2 amax) - 2 (the exponent of E2M1's largest value 6 is 2),
+ *       e = -127 for amax == 0, clamped to [-127, 127];
+ *   scales byte = e + 127;
+ *   code_i = sign(x_i) | nearest E2M1 magnitude of |x_i| / 2^e, ties to the
+ *            even code, values above 6 saturated to 6; the sign bit is kept
+ *            for zero results (-0 and small negatives give code 8).
+ *
+ *   x_bf16 : bfloat16 [rows, k], row-major (read only)
+ *   q      : uint8 [rows, k/2]   (written)
+ *   scales : uint8 [rows, k/32]  (written)
+ *   k      : > 0 and a multiple of 32
+ * NaN or Inf inputs give unspecified codes (the format has no encoding for
+ * them); every finite input is encoded exactly as above.
+ */
+mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k,
+                              void* q, void* scales, void* stream);
+
+/*
+ * Block-scaled NT GEMM on MXFP4 operands ("Packed MXFP4 & NVFP4 GEMM +
+ * mega-MoE" page, Summary: mxfp4_gemm_nt, [M,K] @ [N,K].T -> [M,N], BF16 out,
+ * both operands packed E2M1 with UE8M0 scales at granularity 32):
+ *
+ *   C[i][j] = sum over 32-blocks t of 2^(sa[i][t] + sb[j][t] - 254)
+ *             * sum_{k in t} e2m1(a[i][k]) * e2m1(b[j][k]),
+ *
+ * accumulated in fp32 (each 32-block product sum is exact; the order of the
+ * fp32 additions across blocks is unspecified).
+ *
+ *   a_q, a_s : A operand, [m, k/2] and [m, k/32]
+ *   b_q, b_s : B operand, [n, k/2] and [n, k/32]
+ *   c        : [m, n] row-major, element type `c_type`
+ *   k        : > 0 and a multiple of 32
+ *   workspace: device scratch of at least mxfp4_gemm_nt_workspace_size(m, n, k)
+ *              bytes (may be NULL when that size is 0).  A workspace must be
+ *              zero-filled before its first use.  Its first 256-byte-aligned
+ *              part holds per-tile arrival counters that every call returns to
+ *              zero; the rest holds partial sums that need no initialisation.
+ *              So a workspace can be reused by later calls without clearing.
+ *              Calls that share one workspace must be stream-ordered;
+ *              concurrent calls on one workspace race.
+ */
+size_t mxfp4_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k);
+
+mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s,
+                             const void* b_q, const void* b_s,
+                             void* c, mxfp4_out_t c_type,
+                             int64_t m, int64_t n, int64_t k,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped per-expert NT GEMM ("fp4_quantization" page,
+ * grouped_matmul_block_scaled_mxfp4: per-expert grouped MXFP4 block-scaled
+ * matmul on CDNA4; the quadbit README, distributed MoE paragraph: one launch
+ * over routed rows segmented by expert).
+ *
+ * Rows of A are sorted by group: group g owns rows [offsets[g], offsets[g+1]).
+ * For every such row r:  C[r][:] = A[r][:] . B[g]^T, as in mxfp4_gemm_nt.
+ *
+ *   a_q, a_s  : [total_m, k/2], [total_m, k/32]
+ *   b_q, b_s  : [num_groups, n, k/2], [num_groups, n, k/32]
+ *   offsets   : DEVICE int32 [num_groups + 1], 0 = offsets[0] <= ... <=
+ *               offsets[num_groups] = total_m.  Not readable by the host
+ *               without a synchronisation, so it is not validated: every row
+ *               index the kernels form is clamped to [0, total_m), so
+ *               malformed offsets cannot cause out-of-bounds accesses, but the
+ *               result is then unspecified.  A group with no rows writes
+ *               nothing.
+ *   c         : [total_m, n], element type `c_type`
+ *   num_groups: 1 .. 1024
+ *   workspace : at least mxfp4_grouped_gemm_nt_workspace_size(...) bytes.
+ * One kernel launch; nothing depends on host knowledge of the group sizes.
+ */
+size_t mxfp4_grouped_gemm_nt_workspace_size(int64_t total_m, int32_t num_groups,
+                                            int64_t n, int64_t k);
+
+mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s,
+                                     const void* b_q, const void* b_s,
+                                     const int32_t* offsets, int32_t num_groups,
+                                     int64_t total_m, void* c, mxfp4_out_t c_type,
+                                     int64_t n, int64_t k,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel selection for tests and tuning.  mxfp4_gemm_nt chooses a kernel per
+ * shape; mxfp4_gemm_nt_ex lets a caller force one so every kernel can be
+ * checked on any shape.  `kernel` values:
+ *   MXFP4_KERNEL_AUTO      the shape-based choice mxfp4_gemm_nt makes
+ *   MXFP4_KERNEL_TILE256   256x256 output tiles, LDS-staged scaled MFMA
+ *   MXFP4_KERNEL_TILE128   128x128 output tiles (more tiles for mid sizes)
+ *   MXFP4_KERNEL_SPLITK    M<=128 bandwidth path, K split `splits` ways with
+ *                          an fp32 reduction in the workspace
+ * `splits` is only read for MXFP4_KERNEL_SPLITK (0 = automatic, else 1..64).
+ * The workspace needed is mxfp4_gemm_nt_ex_workspace_size(...).
+ */
+typedef enum {
+  MXFP4_KERNEL_AUTO = 0,
+  MXFP4_KERNEL_TILE256 = 1,
+  MXFP4_KERNEL_TILE128 = 2,
+  MXFP4_KERNEL_SPLITK = 3
+} mxfp4_kernel_t;
+
+size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k,
+                                       mxfp4_kernel_t kernel, int32_t splits);
+
+mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s,
+                                const void* b_q, const void* b_s,
+                                void* c, mxfp4_out_t c_type,
+                                int64_t m, int64_t n, int64_t k,
+                                mxfp4_kernel_t kernel, int32_t splits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H_ */

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/mxfp4.h declares, and rejects bad arguments on the host
+before any device call (argument validation runs before the device query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_mxfp4_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmxfp4.so is not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.mxfp4_abi_version() == 1
+    assert lib.mxfp4_status_string(0) == b"ok"
+    assert lib.mxfp4_status_string(1) == b"invalid argument"
+    assert lib.mxfp4_status_string(3) == b"workspace too small"
+    assert lib.mxfp4_status_string(99) == b"unknown status"
+
+
+def _fake(addr=0x1000):
+    return ctypes.c_void_p(addr)
+
+
+def test_quantize_rejects_bad_arguments_on_host(lib):
+    # k not a multiple of 32, k <= 0, negative rows, null and misaligned pointers
+    assert lib.mxfp4_quantize(_fake(), 4, 48, _fake(), _fake(), None) == 1
+    assert lib.mxfp4_quantize(_fake(), 4, 0, _fake(), _fake(), None) == 1
+    assert lib.mxfp4_quantize(_fake(), -1, 64, _fake(), _fake(), None) == 1
+    assert lib.mxfp4_quantize(None, 4, 64, _fake(), _fake(), None) == 1
+    assert b"x_bf16 is NULL" in lib.mxfp4_last_error()
+    assert lib.mxfp4_quantize(_fake(0x1008), 4, 64, _fake(), _fake(), None) == 1
+    assert b"16-byte aligned" in lib.mxfp4_last_error()
+    # zero rows: valid no-op, returns before touching the device
+    assert lib.mxfp4_quantize(None, 0, 64, None, None, None) == 0
+
+
+def test_gemm_rejects_bad_arguments_on_host(lib):
+    f = _fake()
+    args = dict(a_q=f, a_s=f, b_q=f, b_s=f, c=f)
+
+    def call(m=64, n=64, k=128, c_type=0, kernel=0, splits=0, **kw):
+        a = dict(args, **kw)
+        return lib.mxfp4_gemm_nt_ex(a["a_q"], a["a_s"], a["b_q"], a["b_s"], a["c"], c_type, m, n, k,
+                                    kernel, splits, None, 0, None)
+
+    assert call(k=100) == 1
+    assert call(k=-32) == 1
+    assert call(m=-1) == 1
+    assert call(c_type=7) == 1
+    assert call(kernel=9) == 1
+    assert call(b_s=None) == 1
+    assert b"b_s is NULL" in lib.mxfp4_last_error()
+    assert call(c=_fake(0x1004)) == 1
+    # empty problems are no-ops that launch nothing
+    assert call(m=0, a_q=None, a_s=None, c=None) == 0
+    assert call(n=0, b_q=None, b_s=None, c=None) == 0
+
+
+def test_grouped_rejects_bad_arguments_on_host(lib):
+    f = _fake()
+    assert lib.mxfp4_grouped_gemm_nt(f, f, f, f, f, 0, 64, f, 0, 64, 128, None, 0, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt(f, f, f, f, f, 2000, 64, f, 0, 64, 128, None, 0, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt(f, f, f, f, f, 4, 64, f, 0, 64, 100, None, 0, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt(f, f, f, f, None, 4, 64, f, 0, 64, 128, None, 0, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt(None, None, f, f, None, 4, 0, None, 0, 64, 128, None, 0, None) == 0
+
+
+def test_workspace_queries(lib):
+    assert lib.mxfp4_grouped_gemm_nt_workspace_size(100, 4, 64, 128) == 0
+    # tile kernels need no workspace; split-K with one split needs none either
+    assert lib.mxfp4_gemm_nt_ex_workspace_size(512, 512, 256, 1, 0) == 0
+    assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 256, 3, 1) == 0
+    # split-K with 4 splits: counters (256-byte padded) + 4 fp32 partial tiles per 64-column tile
+    n_tiles = 512 // 64
+    expect = 256 + n_tiles * 4 * (64 * 64) * 4
+    assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 1024, 3, 4) == expect
+    # invalid shapes report 0
+    assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 100, 3, 4) == 0
+    assert lib.mxfp4_gemm_nt_ex_workspace_size(500, 512, 1024, 3, 4) == 0
