@@ -62,11 +62,16 @@ mxfp4_status_t check_k(int64_t k) {
   return MXFP4_OK;
 }
 
-mxfp4_status_t check_ptr(const void* p, const char* name) {
+mxfp4_status_t check_ptr(const void* p, const char* name, unsigned align = 16) {
   if (!p) return fail(MXFP4_ERR_INVALID_ARG, "%s is NULL", name);
-  if (!aligned16(p)) return fail(MXFP4_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  if ((reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0)
+    return fail(MXFP4_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, align);
   return MXFP4_OK;
 }
+
+// Scale arrays are read as 32-bit words (four 32-blocks) when k % 128 == 0 and
+// byte by byte otherwise.
+unsigned scale_align(int64_t k) { return k % 128 == 0 ? 4u : 1u; }
 
 mxfp4_status_t hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MXFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -102,6 +107,8 @@ mxfp4_status_t resolve(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, i
       if (m > 128) return fail(MXFP4_ERR_INVALID_ARG, "the split-K kernel takes m <= 128 (got %lld)", (long long)m);
       if (splits < 0 || splits > 64) return fail(MXFP4_ERR_INVALID_ARG, "splits must be 0..64 (got %d)", splits);
       out = {kernel, splits == 0 ? mxfp4::splitk_auto_splits((int)m, (int)n, (int)k, num_cus) : splits};
+      if (out.splits > 1 && (n + 63) / 64 > mxfp4::splitk_max_tiles())
+        return fail(MXFP4_ERR_INVALID_ARG, "split-K with splits > 1 supports n <= %d", 64 * mxfp4::splitk_max_tiles());
       return MXFP4_OK;
   }
   return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
@@ -127,11 +134,11 @@ mxfp4_status_t check_gemm_args(const void* a_q, const void* a_s, const void* b_q
     return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
   if (m > 0) {
     MXFP4_TRY(check_ptr(a_q, "a_q"));
-    MXFP4_TRY(check_ptr(a_s, "a_s"));
+    MXFP4_TRY(check_ptr(a_s, "a_s", scale_align(k)));
   }
   if (n > 0) {
     MXFP4_TRY(check_ptr(b_q, "b_q"));
-    MXFP4_TRY(check_ptr(b_s, "b_s"));
+    MXFP4_TRY(check_ptr(b_s, "b_s", scale_align(k)));
   }
   if (m > 0 && n > 0) MXFP4_TRY(check_ptr(c, "c"));
   return MXFP4_OK;
@@ -163,8 +170,8 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void*
   if (rows > ((int64_t)1 << 40) / k) return fail(MXFP4_ERR_INVALID_ARG, "rows * k too large");
   if (rows == 0) return MXFP4_OK;
   MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
-  MXFP4_TRY(check_ptr(q, "q"));
-  MXFP4_TRY(check_ptr(scales, "scales"));
+  MXFP4_TRY(check_ptr(q, "q", 4));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_quantize(x_bf16, rows, k, q, scales, (hipStream_t)stream, dev.num_cus),
@@ -240,7 +247,7 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   if (num_groups < 1 || num_groups > 1024)
     return fail(MXFP4_ERR_INVALID_ARG, "num_groups must be 1..1024 (got %d)", num_groups);
   if (total_m == 0 || n == 0) return MXFP4_OK;
-  MXFP4_TRY(check_ptr(offsets, "offsets"));
+  MXFP4_TRY(check_ptr(offsets, "offsets", 4));
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   mxfp4::GemmArgs args{};

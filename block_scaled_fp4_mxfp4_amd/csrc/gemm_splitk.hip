@@ -16,7 +16,10 @@
 //  * with splits > 1 each workgroup writes its fp32 partial tile to the
 //    workspace and bumps a per-column-tile counter; the last of the `splits`
 //    workgroups to arrive sums all partials in split order (deterministic),
-//    writes C and resets the counter to zero for the next call.
+//    writes C and resets the counter to zero for the next call.  The counters
+//    live in the first 64 KiB of the workspace for every shape (so reuse across
+//    shapes never finds partial sums where a counter should be) and the
+//    partial tiles follow.
 // MFMA use is as in the tile kernels: v_mfma_scale_f32_32x32x64_f8f6f4 with
 // the B fragment as first operand, so each lane ends up with 4-column runs.
 #include "common.hpp"
@@ -240,6 +243,9 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
 }
 
 constexpr int kMaxM = 128;
+// The counters occupy a fixed region at the start of every workspace, whatever
+// the shape, so a workspace reused across shapes keeps them at zero.
+constexpr size_t kSplitkCounterBytes = 65536;
 
 int mblocks_for(int m) { return m <= 32 ? 1 : (m <= 64 ? 2 : 4); }
 
@@ -251,9 +257,10 @@ size_t splitk_workspace_bytes(int m, int n, int k, int splits) {
   const int tiles_n = (n + kBN - 1) / kBN;
   const size_t tile = (size_t)32 * mblocks_for(m) * kBN;
   const size_t part = (size_t)tiles_n * splits * tile * sizeof(float);
-  const size_t cnt = ((size_t)tiles_n * sizeof(int) + 255) & ~(size_t)255;
-  return cnt + part;
+  return kSplitkCounterBytes + part;
 }
+
+int splitk_max_tiles() { return (int)(kSplitkCounterBytes / sizeof(int)); }
 
 int splitk_auto_splits(int m, int n, int k, int num_cus) {
   (void)m;
@@ -261,6 +268,7 @@ int splitk_auto_splits(int m, int n, int k, int num_cus) {
   const int nchunks = (k + kChunk - 1) / kChunk;
   // enough workgroups to cover every CU, each wave keeping >= 2 chunks of work
   int s = 1;
+  if (tiles_n > splitk_max_tiles()) return 1;
   while (tiles_n * s < num_cus && nchunks / (4 * (s * 2)) >= 2 && s < 64) s *= 2;
   return s;
 }
@@ -271,9 +279,9 @@ hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
   int* counters = nullptr;
   float* partials = nullptr;
   if (splits > 1) {
-    const size_t cnt = ((size_t)tiles_n * sizeof(int) + 255) & ~(size_t)255;
+    if (tiles_n > splitk_max_tiles()) return hipErrorInvalidValue;
     counters = (int*)workspace;
-    partials = (float*)((char*)workspace + cnt);
+    partials = (float*)((char*)workspace + kSplitkCounterBytes);
   }
   const dim3 grid((unsigned)(tiles_n * splits));
   switch (mblocks_for(args.m)) {

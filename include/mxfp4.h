@@ -21,8 +21,12 @@
  *     stream-ordered and asynchronous: they enqueue kernels and return without
  *     synchronising, so they may be captured into a HIP graph.
  *   - All arguments are checked on the host before anything is launched; a
- *     failed check returns a non-OK status and launches nothing.  Device
- *     buffers must be 16-byte aligned.  Sizes are elements, not bytes.
+ *     failed check returns a non-OK status and launches nothing.  Sizes are
+ *     elements, not bytes.  Alignment: BF16 inputs, code arrays (q, a_q, b_q),
+ *     outputs (c) and workspaces 16 bytes, except the quantizer's q output
+ *     (4 bytes); scale arrays read by the GEMMs 4 bytes when k % 128 == 0,
+ *     otherwise any; the quantizer's scale output any; offsets 4 bytes.  A row
+ *     slice of a row-major operand therefore stays valid.
  *   - A zero-sized problem (rows, m, n or total_m equal to 0) is a valid no-op.
  *   - No call aborts or throws; mxfp4_last_error() gives a thread-local text
  *     describing the last non-OK status.
@@ -105,10 +109,11 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k,
  *   k        : > 0 and a multiple of 32
  *   workspace: device scratch of at least mxfp4_gemm_nt_workspace_size(m, n, k)
  *              bytes (may be NULL when that size is 0).  A workspace must be
- *              zero-filled before its first use.  Its first 256-byte-aligned
- *              part holds per-tile arrival counters that every call returns to
- *              zero; the rest holds partial sums that need no initialisation.
- *              So a workspace can be reused by later calls without clearing.
+ *              zero-filled before its first use.  Its first 64 KiB hold
+ *              per-tile arrival counters that every call returns to zero; the
+ *              rest holds partial sums that need no initialisation.  So a
+ *              workspace can be reused by later calls, of any shape, without
+ *              clearing.
  *              Calls that share one workspace must be stream-ordered;
  *              concurrent calls on one workspace race.
  */

@@ -55,6 +55,8 @@ def test_quantize_rejects_bad_arguments_on_host(lib):
     assert b"x_bf16 is NULL" in lib.mxfp4_last_error()
     assert lib.mxfp4_quantize(_fake(0x1008), 4, 64, _fake(), _fake(), None) == 1
     assert b"16-byte aligned" in lib.mxfp4_last_error()
+    assert lib.mxfp4_quantize(_fake(), 4, 64, _fake(0x1002), _fake(), None) == 1
+    assert b"q is not 4-byte aligned" in lib.mxfp4_last_error()
     # zero rows: valid no-op, returns before touching the device
     assert lib.mxfp4_quantize(None, 0, 64, None, None, None) == 0
 
@@ -76,6 +78,9 @@ def test_gemm_rejects_bad_arguments_on_host(lib):
     assert call(b_s=None) == 1
     assert b"b_s is NULL" in lib.mxfp4_last_error()
     assert call(c=_fake(0x1004)) == 1
+    assert call(a_s=_fake(0x1002)) == 1
+    assert b"a_s is not 4-byte aligned" in lib.mxfp4_last_error()
+    assert call(a_q=_fake(0x1008)) == 1
     # empty problems are no-ops that launch nothing
     assert call(m=0, a_q=None, a_s=None, c=None) == 0
     assert call(n=0, b_q=None, b_s=None, c=None) == 0
@@ -95,9 +100,9 @@ def test_workspace_queries(lib):
     # tile kernels need no workspace; split-K with one split needs none either
     assert lib.mxfp4_gemm_nt_ex_workspace_size(512, 512, 256, 1, 0) == 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 256, 3, 1) == 0
-    # split-K with 4 splits: counters (256-byte padded) + 4 fp32 partial tiles per 64-column tile
+    # split-K with 4 splits: the fixed 64 KiB counter region + 4 fp32 partial tiles per 64-column tile
     n_tiles = 512 // 64
-    expect = 256 + n_tiles * 4 * (64 * 64) * 4
+    expect = 65536 + n_tiles * 4 * (64 * 64) * 4
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 1024, 3, 4) == expect
     # invalid shapes report 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 100, 3, 4) == 0

@@ -114,10 +114,12 @@ def test_gemm_auto_dispatch_and_empty_problems():
 
 
 def test_splitk_workspace_reuse_across_calls():
-    """The arrival counters return to zero, so one workspace serves consecutive calls."""
+    """The arrival counters return to zero, so one workspace serves consecutive
+    calls of different shapes (the partial sums of a small-N call must not land
+    where a larger-N call keeps its counters)."""
     dev = device()
-    ws = workspace(1 << 24, dev)
-    for seed, (m, n, k) in enumerate([(64, 512, 2048), (128, 640, 4096), (7, 64, 1024)]):
+    ws = torch.zeros(1 << 25, dtype=torch.uint8, device=dev)
+    for seed, (m, n, k) in enumerate([(64, 512, 2048), (128, 640, 4096), (7, 64, 1024), (128, 9000, 1024)]):
         a = random_bf16((m, k), 100 + seed)
         b = random_bf16((n, k), 200 + seed)
         aq, as_ = oracle.quantize(workloads.bf16_bits(a))
@@ -126,7 +128,7 @@ def test_splitk_workspace_reuse_across_calls():
                           out_dtype=torch.float32, kernel="splitk", splits=4, ws=ws)
         torch.cuda.synchronize()
         assert oracle.floored_max_rel(to_np(c), oracle.gemm_nt(aq, as_, bq, bs)) <= 1e-5
-        assert torch.all(ws[:256] == 0), "counters not returned to zero"
+        assert torch.all(ws[:65536] == 0), "counters not returned to zero"
 
 
 @pytest.mark.parametrize("name", ["tiny_64x256x1024", "decode_128x14336x4096", "prefill_4096x4096x4096",
