@@ -11,38 +11,47 @@
 //  * v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in FP4: lane l holds
 //    16 bytes (one 32-element K-block) of row l % 32, K-block l / 32, and the
 //    E8M0 byte of exactly that (row, block) in its scale register (byte chosen
-//    by op_sel).  So a block scale is applied inside the MFMA: no dequantized
-//    operand ever exists, and the packed bytes go HBM -> LDS -> VGPR unchanged.
+//    by op_sel).  The block scale is applied inside the MFMA: no dequantized
+//    operand ever exists; packed bytes go HBM -> LDS -> VGPR unchanged.
 //  * The MFMA's first operand is fed from B and its second from A, so the
 //    result lands transposed: lane l holds output row (l % 32) and four runs of
-//    four consecutive output columns, which become 8-byte BF16 stores.
-//  * A stage covers 128 K elements: 64 code bytes per row and one 32-bit word
-//    of four scale bytes per row (one word per 128 K, read as the row's four
-//    scale bytes in little-endian order).  Stages are copied global -> LDS with
-//    global_load_lds_dwordx4 / _dword, without passing through VGPRs, double
-//    buffered so the next stage streams in while the MFMAs consume this one.
-//  * LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored
-//    at chunk position c ^ swz(r) so the ds_read_b128 of 8 or 16 consecutive
-//    rows at one logical chunk touches distinct banks.
+//    four consecutive output columns.
+//  * A stage covers 256 K elements = 128 code bytes per row, so each
+//    global_load_lds_dwordx4 (64 lanes x 16 bytes, straight into LDS) moves 8
+//    whole 128-byte rows; 64-byte row pieces measured about half the per-CU
+//    copy rate.  Two code stages are in flight (2 x 64 KiB for 256x256).
+//  * Scale bytes travel separately: one 16-byte piece per row covers two
+//    stages (512 K), so the scale copy costs an eighth of the code copy's
+//    requests instead of one 4-byte request per row per stage.  Two scale
+//    groups are in flight.
+//  * LDS rows are 128 bytes = eight 16-byte chunks; logical chunk c of row r
+//    sits at chunk c ^ ((r >> 1) & 7), which makes the ds_read_b128 of 32
+//    consecutive rows at one chunk conflict-free (measured on the device).
+//  * Pipeline: iteration kt computes stage kt in four 64-deep k-steps,
+//    reading the next k-step's fragments while the current MFMAs run.  Before
+//    the last k-step every wave waits for its copies of stage kt+1 and passes
+//    one barrier; then the buffer of stage kt is free, the copies of stage
+//    kt+2 go into it, and stage kt+1's first fragments are read while the last
+//    MFMAs of stage kt run.
 //  * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
-//    sub-tile as (BM/64) x (BN/64) MFMA blocks of 32x32.
+//    sub-tile as (BM/64) x (BN/64) MFMA blocks of 32x32 (accumulators in AGPRs).
 //  * Workgroup -> tile mapping is XCD-aware (see tile_coords in common.hpp).
 //
 // Ragged edges: rows past M (or N) read a clamped, valid row and are never
-// stored.  K must be a multiple of 32; when it is not a multiple of 128 every
-// stage goes through a register path that zero-fills the missing 32-blocks
-// (zero codes contribute nothing whatever their scale).
+// stored.  The copy path needs k % 512 == 0 and 16-byte aligned scale arrays;
+// any other k (a multiple of 32) goes through a register path that zero-fills
+// the missing 32-blocks (zero codes contribute nothing whatever their scale).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mxfp4 {
 namespace {
 
-constexpr int kBK = 128;            // K elements per stage
+constexpr int kBK = 256;            // K elements per stage
 constexpr int kRowBytes = kBK / 2;  // code bytes per row per stage
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 template <int BM_, int BN_>
 struct TileCfg {
@@ -50,14 +59,16 @@ struct TileCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  static constexpr int S_BYTES = (BM + BN) * 4;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int A_LOADS = BM * 4 / 64 / 4;       // 16-byte chunk loads per wave per stage
-  static constexpr int B_LOADS = BN * 4 / 64 / 4;
-  static constexpr int S_LOADS = (BM + BN) / 64 / 4;    // 4-byte scale-word loads per wave per stage
-  static constexpr int LOADS = A_LOADS + B_LOADS + S_LOADS;
+  static constexpr int CODE_STAGE = A_BYTES + B_BYTES;
+  static constexpr int SCALE_GROUP = (BM + BN) * 16;        // 16 scale bytes per row = two stages
+  static constexpr int LDS_BYTES = 2 * CODE_STAGE + 2 * SCALE_GROUP;
+  static constexpr int A_LOADS = BM * kRowBytes / 16 / kThreads;   // 16-byte copies per thread per stage
+  static constexpr int B_LOADS = BN * kRowBytes / 16 / kThreads;
+  static constexpr int S_LOADS = (BM + BN) / kThreads;            // 16-byte scale copies per thread per group
+  static constexpr int CODE_LOADS = A_LOADS + B_LOADS;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
-  static_assert((BM + BN) % 256 == 0, "scale loads must split evenly over 4 waves");
+  static_assert((BM + BN) % kThreads == 0, "scale copies must split evenly over the threads");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 // Row range of the A tile a workgroup works on (dense: [m0, min(m0+BM, M));
@@ -68,180 +79,312 @@ struct RowRange {
   int end;    // one past the last row that is stored
 };
 
+// Per-thread source offsets (bytes) of the copies, at stage 0 / scale group 0.
 template <class C>
-struct Pointers {
-  const uint8_t* a_code[C::A_LOADS];
-  const uint8_t* b_code[C::B_LOADS];
-  const uint8_t* scale[C::S_LOADS];
+struct Sources {
+  int64_t a_code[C::A_LOADS];
+  int64_t b_code[C::B_LOADS];
+  int64_t scale[C::S_LOADS];     // A rows use a_s, B rows use b_s (see is_b)
+  bool is_b[C::S_LOADS];
 };
 
-// Per-lane global source addresses of the DMA copies, for stage 0.
 template <class C>
-__device__ __forceinline__ void make_pointers(Pointers<C>& p, const uint8_t* a_q, const uint8_t* a_s,
-                                              const uint8_t* b_q, const uint8_t* b_s,
-                                              const RowRange& ar, int n0, int n, int k) {
+__device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t kb = k / 2, ks = k / 32;
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int r = slot >> 2, lc = (slot & 3) ^ swz(r);
-    const int row = min(ar.lo + r, ar.last);
-    p.a_code[j] = a_q + row * kb + lc * 16;
+    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
+    src.a_code[j] = min(ar.lo + r, ar.last) * kb + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int r = slot >> 2, lc = (slot & 3) ^ swz(r);
-    const int row = min(n0 + r, n - 1);
-    p.b_code[j] = b_q + row * kb + lc * 16;
+    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
+    src.b_code[j] = min(n0 + r, n - 1) * kb + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    if (slot < C::BM) {
-      const int row = min(ar.lo + slot, ar.last);
-      p.scale[j] = a_s + row * ks;
-    } else {
-      const int row = min(n0 + slot - C::BM, n - 1);
-      p.scale[j] = b_s + row * ks;
-    }
+    src.is_b[j] = slot >= C::BM;
+    src.scale[j] = src.is_b[j] ? min(n0 + slot - C::BM, n - 1) * ks : min(ar.lo + slot, ar.last) * ks;
   }
 }
 
-// Stage kt via direct global -> LDS copies (requires k % 128 == 0).
+// Code copies of stage kt into `stage` (direct global -> LDS).
 template <class C>
-__device__ __forceinline__ void load_stage_dma(uint8_t MXFP4_LDS* stage, const Pointers<C>& p, int kt) {
-  const int w = threadIdx.x >> 6;
+__device__ __forceinline__ void copy_codes(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const uint8_t* a_q,
+                                           const uint8_t* b_q, int kt) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS base goes to M0
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j)
-    g2lds_16(p.a_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + (j * 4 + w) * 64 * 16));
+    g2lds_16(a_q + src.a_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + (j * 4 + w) * 64 * 16));
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j)
-    g2lds_16(p.b_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + C::A_BYTES + (j * 4 + w) * 64 * 16));
-#pragma unroll
-  for (int j = 0; j < C::S_LOADS; ++j)
-    g2lds_4(p.scale[j] + kt * 4, (MXFP4_LDS void*)(stage + C::A_BYTES + C::B_BYTES + (j * 4 + w) * 64 * 4));
+    g2lds_16(b_q + src.b_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + C::A_BYTES + (j * 4 + w) * 64 * 16));
 }
 
-// Stage kt through registers, any k % 32 == 0: 32-blocks at or past k get zero
-// codes and scale byte 127.
+// Scale copies of group g (stages 2g and 2g+1): 16 bytes of every row.
 template <class C>
-__device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, const Pointers<C>& p,
-                                                   int kt, int k) {
+__device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const uint8_t* a_s,
+                                            const uint8_t* b_s, int g) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < C::S_LOADS; ++j)
+    g2lds_16((src.is_b[j] ? b_s : a_s) + src.scale[j] + g * 16, (MXFP4_LDS void*)(group + (j * 4 + w) * 64 * 16));
+}
+
+// Stage kt through registers for any k % 32 == 0: 32-blocks at or past k get
+// zero codes and scale byte 127.  Writes the same LDS layout as the copies
+// (scale bytes of stage kt at byte 8 * (kt & 1) of each row's 16-byte piece).
+template <class C>
+__device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uint8_t MXFP4_LDS* group,
+                                                   const Sources<C>& src, const GemmArgs& args,
+                                                   const uint8_t* b_q, const uint8_t* b_s, int kt) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kblocks_left = k / 32 - kt * 4;    // valid 32-blocks in this stage (may exceed 4)
+  const int blocks_left = args.k / 32 - kt * 8;   // valid 32-blocks in this stage (may exceed 8)
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int lc = (slot & 3) ^ swz(slot >> 2);
+    const int lc = (slot & 7) ^ swz(slot >> 3);
     v4i v = {0, 0, 0, 0};
-    if (lc < kblocks_left) v = *(const v4i*)(p.a_code[j] + kt * kRowBytes);
+    if (lc < blocks_left) v = *(const v4i*)(args.a_q + src.a_code[j] + kt * kRowBytes);
     *(v4i MXFP4_LDS*)(stage + slot * 16) = v;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int lc = (slot & 3) ^ swz(slot >> 2);
+    const int lc = (slot & 7) ^ swz(slot >> 3);
     v4i v = {0, 0, 0, 0};
-    if (lc < kblocks_left) v = *(const v4i*)(p.b_code[j] + kt * kRowBytes);
+    if (lc < blocks_left) v = *(const v4i*)(b_q + src.b_code[j] + kt * kRowBytes);
     *(v4i MXFP4_LDS*)(stage + C::A_BYTES + slot * 16) = v;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    uint32_t word = 0;
+    const uint8_t* sp = (src.is_b[j] ? b_s : args.a_s) + src.scale[j] + kt * 8;
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = b < kblocks_left ? (uint32_t)p.scale[j][kt * 4 + b] : 127u;
-      word |= byte << (8 * b);
+      lo |= (b < blocks_left ? (uint32_t)sp[b] : 127u) << (8 * b);
+      hi |= (b + 4 < blocks_left ? (uint32_t)sp[b + 4] : 127u) << (8 * b);
     }
-    *(uint32_t MXFP4_LDS*)(stage + C::A_BYTES + C::B_BYTES + slot * 4) = word;
+    v2i word = {(int)lo, (int)hi};
+    *(v2i MXFP4_LDS*)(group + slot * 16 + 8 * (kt & 1)) = word;
+  }
+}
+
+// Operand fragments of one 64-deep k-step for a wave's (BM/2) x (BN/2) sub-tile.
+template <class C>
+struct Frags {
+  v4i a[C::MI];
+  v4i b[C::NI];
+};
+
+// Scale words of one stage.  Row r's 8 stage bytes are two 32-bit words:
+// word 0 for k-steps 0-1, word 1 for k-steps 2-3.  Lanes 32..63 feed the odd
+// 32-block of each k-step, so their words are shifted right by one byte; k-step
+// s then takes byte 2 * (s & 1) of word s / 2.
+template <class C>
+struct Scales {
+  v2i a[C::MI];
+  v2i b[C::NI];
+};
+
+template <class C>
+__device__ __forceinline__ void read_scales_raw(const uint8_t MXFP4_LDS* group, int parity, Scales<C>& sc,
+                                                int wm0, int wn0, int lane) {
+  const uint8_t MXFP4_LDS* base = group + 8 * parity;
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) sc.a[i] = *(const v2i MXFP4_LDS*)(base + (wm0 + 32 * i + (lane & 31)) * 16);
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) sc.b[j] = *(const v2i MXFP4_LDS*)(base + (C::BM + wn0 + 32 * j + (lane & 31)) * 16);
+}
+
+template <class C>
+__device__ __forceinline__ void shift_scales(Scales<C>& sc, int lane) {
+  const int shift = 8 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) {
+    sc.a[i].x = (int)((uint32_t)sc.a[i].x >> shift);
+    sc.a[i].y = (int)((uint32_t)sc.a[i].y >> shift);
+  }
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    sc.b[j].x = (int)((uint32_t)sc.b[j].x >> shift);
+    sc.b[j].y = (int)((uint32_t)sc.b[j].y >> shift);
   }
 }
 
 template <class C, int S>
-__device__ __forceinline__ void compute_kstep(const uint8_t MXFP4_LDS* stage, v16f (&acc)[C::MI][C::NI],
-                                              const int (&asc)[C::MI], const int (&bsc)[C::NI],
-                                              int wm0, int wn0, int lane) {
+__device__ __forceinline__ void read_frags(const uint8_t MXFP4_LDS* stage, Frags<C>& f, int wm0, int wn0,
+                                           int lane) {
   const int c = 2 * S + (lane >> 5);
-  v4i af[C::MI], bf[C::NI];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm0 + 32 * i + (lane & 31);
-    af[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
   }
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
     const int r = wn0 + 32 * j + (lane & 31);
-    bf[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
+    f.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
   }
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-      acc[i][j] = mfma32_fp4<2 * S>(bf[j], af[i], acc[i][j], bsc[j], asc[i]);
 }
 
-template <class C>
-__device__ __forceinline__ void compute_stage(const uint8_t MXFP4_LDS* stage, v16f (&acc)[C::MI][C::NI],
-                                              int wm0, int wn0, int lane) {
-  const uint32_t MXFP4_LDS* sw = (const uint32_t MXFP4_LDS*)(stage + C::A_BYTES + C::B_BYTES);
-  const int shift = 8 * (lane >> 5);   // lanes 32..63 hold the odd 32-blocks
-  int asc[C::MI], bsc[C::NI];
+// MFMAs of k-step S over the MFMA blocks [I0, I1) x [0, NI).
+template <class C, int S, int I0, int I1>
+__device__ __forceinline__ void mma_kstep(const Frags<C>& f, const Scales<C>& sc, v16f (&acc)[C::MI][C::NI]) {
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) asc[i] = (int)(sw[wm0 + 32 * i + (lane & 31)] >> shift);
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) bsc[j] = (int)(sw[C::BM + wn0 + 32 * j + (lane & 31)] >> shift);
-  compute_kstep<C, 0>(stage, acc, asc, bsc, wm0, wn0, lane);
-  compute_kstep<C, 1>(stage, acc, asc, bsc, wm0, wn0, lane);
-}
-
-template <class C>
-__device__ __forceinline__ void store_tile(const GemmArgs& args, const v16f (&acc)[C::MI][C::NI],
-                                           const RowRange& ar, int n0, int wm0, int wn0, int lane) {
-  const int n = args.n;
-  const bool vec_ok = (n & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    const int row = ar.lo + wm0 + 32 * i + (lane & 31);
-    if (row >= ar.end) continue;
-    const int64_t rbase = (int64_t)row * n;
+  for (int i = I0; i < I1; ++i)
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
-        const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (args.c_f32) {
-          float* cp = (float*)args.c + rbase + col;
-          if (vec_ok && col + 3 < n) {
-            *(float4*)cp = make_float4(v0, v1, v2, v3);
-          } else {
-            if (col + 0 < n) cp[0] = v0;
-            if (col + 1 < n) cp[1] = v1;
-            if (col + 2 < n) cp[2] = v2;
-            if (col + 3 < n) cp[3] = v3;
-          }
-        } else {
-          uint16_t* cp = (uint16_t*)args.c + rbase + col;
-          if (vec_ok && col + 3 < n) {
-            *(uint2*)cp = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-          } else {
-            if (col + 0 < n) cp[0] = (uint16_t)f32_to_bf16_bits(v0);
-            if (col + 1 < n) cp[1] = (uint16_t)f32_to_bf16_bits(v1);
-            if (col + 2 < n) cp[2] = (uint16_t)f32_to_bf16_bits(v2);
-            if (col + 3 < n) cp[3] = (uint16_t)f32_to_bf16_bits(v3);
-          }
-        }
+      const int sa = (S < 2) ? sc.a[i].x : sc.a[i].y;
+      const int sb = (S < 2) ? sc.b[j].x : sc.b[j].y;
+      acc[i][j] = mfma32_fp4<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
+    }
+}
+
+// Workgroup barrier without a memory fence: copies into LDS are tracked with
+// explicit vmcnt waits, so the fence of __syncthreads() (which would also wait
+// for the copies still streaming in) is not wanted.  The asm memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  MXFP4_WAIT_LGKM0();
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Epilogue.  Each wave converts its accumulators and writes them into a
+// row-major tile in LDS (rows padded by 16 bytes so the 32 rows a wave writes
+// at one column spread over the banks); then all 256 threads copy the tile out
+// in 16-byte row-contiguous pieces, so global stores are fully coalesced and
+// the code stays small (edge guards live in one loop, not in every unrolled
+// store).  BF16 uses the hardware packed convert (nearest-even).  The fp32
+// tile does not fit in LDS at once and goes out in two halves by wave row.
+// The caller must have ended every LDS read and copy of the main loop.
+template <class C>
+__device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXFP4_LDS* tile, int pitch,
+                                         int row_begin, int rows, int esize, const RowRange& ar, int n0) {
+  const int n = args.n;
+  const int chunks_per_row = C::BN * esize / 16;
+  const int valid_rows = min(rows, ar.end - ar.lo - row_begin);
+  const int valid_cols = min(C::BN, n - n0);
+  const bool vec_ok = ((n * esize) & 15) == 0;
+  uint8_t* cbase = (uint8_t*)args.c;
+  for (int idx = threadIdx.x; idx < valid_rows * chunks_per_row; idx += kThreads) {
+    const int r = idx / chunks_per_row, cc = idx - r * chunks_per_row;
+    const int col = cc * 16 / esize;
+    if (col >= valid_cols) continue;
+    const v4i v = *(const v4i MXFP4_LDS*)(tile + r * pitch + cc * 16);
+    uint8_t* dst = cbase + ((int64_t)(ar.lo + row_begin + r) * n + n0 + col) * esize;
+    const int cnt = min(16 / esize, valid_cols - col);
+    if (vec_ok && cnt * esize == 16) {
+      *(v4i*)dst = v;
+    } else if (esize == 4) {
+      for (int e = 0; e < cnt; ++e) ((uint32_t*)dst)[e] = (uint32_t)(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+    } else {
+      for (int e = 0; e < cnt; ++e) {
+        const uint32_t word = (uint32_t)((e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w);
+        ((uint16_t*)dst)[e] = (uint16_t)(word >> (16 * (e & 1)));
       }
     }
   }
 }
 
+template <class C>
+__device__ __forceinline__ void store_tile(const GemmArgs& args, const v16f (&acc)[C::MI][C::NI],
+                                           const RowRange& ar, int n0, int wm0, int wn0, int lane,
+                                           uint8_t MXFP4_LDS* lds) {
+  if (!args.c_f32) {
+    constexpr int PITCH = C::BN * 2 + 16;
+    static_assert(C::BM * PITCH <= C::LDS_BYTES, "bf16 tile must fit in the pipeline LDS");
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = wm0 + 32 * i + (lane & 31);
+          const int col = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+          bf16x2_t lo = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1]};
+          bf16x2_t hi = {(__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
+          v2i pk = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+          *(v2i MXFP4_LDS*)(lds + r * PITCH + col * 2) = pk;
+        }
+    __syncthreads();
+    copy_out<C>(args, lds, PITCH, 0, C::BM, 2, ar, n0);
+  } else {
+    constexpr int PITCH = C::BN * 4 + 16;
+    static_assert(C::WM * PITCH <= C::LDS_BYTES, "fp32 half tile must fit in the pipeline LDS");
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm0 == half * C::WM) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 32 * i + (lane & 31);
+              const int col = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+              v4f val = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              *(v4f MXFP4_LDS*)(lds + r * PITCH + col * 4) = val;
+            }
+      }
+      __syncthreads();
+      copy_out<C>(args, lds, PITCH, half * C::WM, C::WM, 4, ar, n0);
+      __syncthreads();
+    }
+  }
+}
+
+// One pipelined stage (straight-line code: every branch is a template
+// parameter, so the compiler cannot sink the MFMAs past the barrier).
+// On entry fa holds k-step 0 of stage kt and sc its scales; on exit, if NEXT,
+// fa/sc hold k-step 0 of stage kt+1.  COPY_CODES / COPY_SCALES issue the copies
+// of stage kt+2 (and of its scale group) once stage kt's buffer is released.
+template <class C, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
+__device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
+                                                Scales<C>& sc, const Sources<C>& src, const GemmArgs& args,
+                                                const uint8_t* b_q, const uint8_t* b_s, uint8_t MXFP4_LDS* lds,
+                                                int kt, int wm0, int wn0, int lane) {
+  uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
+  uint8_t MXFP4_LDS* nxt = lds + ((kt + 1) & 1) * C::CODE_STAGE;
+  read_frags<C, 1>(cur, fb, wm0, wn0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_kstep<C, 0, 0, C::MI>(fa, sc, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<C, 2>(cur, fa, wm0, wn0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_kstep<C, 1, 0, C::MI>(fb, sc, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<C, 3>(cur, fb, wm0, wn0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_kstep<C, 2, 0, C::MI>(fa, sc, acc);
+  const Scales<C> sc_cur = sc;
+  __builtin_amdgcn_sched_barrier(0);
+  if (NEXT) {
+    // stage kt+1 and its scales have landed; stage kt is fully read once every
+    // wave has passed the barrier
+    MXFP4_WAIT_VMCNT(0);
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    if (COPY_SCALES)
+      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, args.a_s, b_s,
+                     (kt + 2) >> 1);
+    if (COPY_CODES) copy_codes<C>(cur, src, args.a_q, b_q, kt + 2);
+    read_scales_raw<C>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
+                       wm0, wn0, lane);
+    read_frags<C, 0>(nxt, fa, wm0, wn0, lane);
+  }
+  mma_kstep<C, 3, 0, C::MI>(fb, sc_cur, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (NEXT) shift_scales<C>(sc, lane);
+}
+
 // Main loop + epilogue for one output tile.
-template <class C, bool KALIGNED>
+template <class C, bool COPY>
 __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                          const RowRange& ar, int n0, uint8_t MXFP4_LDS* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -254,40 +397,55 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  Pointers<C> p;
-  make_pointers<C>(p, args.a_q, args.a_s, b_q, b_s, ar, n0, args.n, args.k);
-  uint8_t MXFP4_LDS* buf0 = lds;
-  uint8_t MXFP4_LDS* buf1 = lds + C::STAGE_BYTES;
+  Sources<C> src;
+  make_sources<C>(src, ar, n0, args.n, args.k);
+  uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
-  if (KALIGNED) {
-    const int nk = args.k / kBK;
-    load_stage_dma<C>(buf0, p, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      uint8_t MXFP4_LDS* cur = (kt & 1) ? buf1 : buf0;
-      uint8_t MXFP4_LDS* nxt = (kt & 1) ? buf0 : buf1;
-      if (kt + 1 < nk) {
-        load_stage_dma<C>(nxt, p, kt + 1);
-        MXFP4_WAIT_VMCNT(C::LOADS);
-      } else {
-        MXFP4_WAIT_VMCNT(0);
-      }
-      __syncthreads();
-      compute_stage<C>(cur, acc, wm0, wn0, lane);
-      __syncthreads();
+  if (COPY) {
+    const int nk = args.k / kBK;    // even, >= 2: k % 512 == 0
+    copy_scales<C>(group0, src, args.a_s, b_s, 0);
+    copy_codes<C>(lds, src, args.a_q, b_q, 0);
+    copy_codes<C>(lds + C::CODE_STAGE, src, args.a_q, b_q, 1);
+    MXFP4_WAIT_VMCNT(C::CODE_LOADS);            // scales and stage 0 have landed
+    barrier_lds();
+    Scales<C> sc;
+    Frags<C> fa, fb;
+    read_scales_raw<C>(group0, 0, sc, wm0, wn0, lane);
+    read_frags<C, 0>(lds, fa, wm0, wn0, lane);
+    shift_scales<C>(sc, lane);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      pipelined_stage<C, true, true, true>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt, wm0, wn0, lane);
+      pipelined_stage<C, true, true, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt + 1, wm0, wn0, lane);
     }
+    pipelined_stage<C, true, false, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt, wm0, wn0, lane);
+    pipelined_stage<C, false, false, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt + 1, wm0, wn0, lane);
   } else {
     const int nk = (args.k + kBK - 1) / kBK;
     for (int kt = 0; kt < nk; ++kt) {
-      load_stage_generic<C>(buf0, p, kt, args.k);
+      load_stage_generic<C>(lds, group0, src, args, b_q, b_s, kt);
       __syncthreads();
-      compute_stage<C>(buf0, acc, wm0, wn0, lane);
+      Scales<C> sc;
+      Frags<C> f;
+      read_scales_raw<C>(group0, kt & 1, sc, wm0, wn0, lane);
+      shift_scales<C>(sc, lane);
+      read_frags<C, 0>(lds, f, wm0, wn0, lane);
+      mma_kstep<C, 0, 0, C::MI>(f, sc, acc);
+      read_frags<C, 1>(lds, f, wm0, wn0, lane);
+      mma_kstep<C, 1, 0, C::MI>(f, sc, acc);
+      read_frags<C, 2>(lds, f, wm0, wn0, lane);
+      mma_kstep<C, 2, 0, C::MI>(f, sc, acc);
+      read_frags<C, 3>(lds, f, wm0, wn0, lane);
+      mma_kstep<C, 3, 0, C::MI>(f, sc, acc);
       __syncthreads();
     }
   }
-  store_tile<C>(args, acc, ar, n0, wm0, wn0, lane);
+  MXFP4_WAIT_VMCNT(0);
+  __syncthreads();   // every wave is done with the pipeline buffers
+  store_tile<C>(args, acc, ar, n0, wm0, wn0, lane, lds);
 }
 
-template <class C, bool KALIGNED>
+template <class C, bool COPY>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(GemmArgs args, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
@@ -296,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(GemmArgs args, int 
   ar.lo = tm * C::BM;
   ar.end = min(ar.lo + C::BM, args.m);
   ar.last = ar.end - 1;
-  run_tile<C, KALIGNED>(args, args.b_q, args.b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
+  run_tile<C, COPY>(args, args.b_q, args.b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
 // Finds the expert owning global m-tile `mt` (m-tiles are counted expert by
@@ -339,7 +497,7 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, i
   return false;
 }
 
-template <class C, bool KALIGNED>
+template <class C, bool COPY>
 __global__ __launch_bounds__(kThreads) void grouped_tile_kernel(GemmArgs args, int mt_bound, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int total = mt_bound * tiles_n;
@@ -352,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void grouped_tile_kernel(GemmArgs args, i
   const int64_t kb = args.k / 2, ks = args.k / 32;
   const uint8_t* b_q = args.b_q + (int64_t)g * args.n * kb;
   const uint8_t* b_s = args.b_s + (int64_t)g * args.n * ks;
-  run_tile<C, KALIGNED>(args, b_q, b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
+  run_tile<C, COPY>(args, b_q, b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
 using Cfg256 = TileCfg<256, 256>;
@@ -364,13 +522,19 @@ hipError_t allow_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// The copy path reads 16-byte scale pieces: k % 512 == 0 and 16-byte aligned
+// scale arrays (row starts are then aligned too).
+bool use_copy_path(const GemmArgs& args) {
+  return args.k % 512 == 0 && ((reinterpret_cast<uintptr_t>(args.a_s) | reinterpret_cast<uintptr_t>(args.b_s)) & 15) == 0;
+}
+
 template <class C>
 hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (args.m + C::BM - 1) / C::BM;
   const int tiles_n = (args.n + C::BN - 1) / C::BN;
-  const size_t lds = 2 * C::STAGE_BYTES;
+  const size_t lds = C::LDS_BYTES;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if (args.k % kBK == 0) {
+  if (use_copy_path(args)) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_tile_kernel<C, true>), grid, dim3(kThreads), lds, stream, args, tiles_m, tiles_n);
@@ -386,9 +550,9 @@ template <class C>
 hipError_t launch_grouped(const GemmArgs& args, hipStream_t stream) {
   const int mt_bound = (args.m + C::BM - 1) / C::BM + args.groups;
   const int tiles_n = (args.n + C::BN - 1) / C::BN;
-  const size_t lds = 2 * C::STAGE_BYTES;
+  const size_t lds = C::LDS_BYTES;
   const dim3 grid((unsigned)(mt_bound * tiles_n));
-  if (args.k % kBK == 0) {
+  if (use_copy_path(args)) {
     hipError_t e = allow_lds(grouped_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_tile_kernel<C, true>), grid, dim3(kThreads), lds, stream, args, mt_bound, tiles_n);
