@@ -263,23 +263,25 @@ __device__ __forceinline__ void barrier_lds() {
 // store).  BF16 uses the hardware packed convert (nearest-even).  The fp32
 // tile does not fit in LDS at once and goes out in two halves by wave row.
 // The caller must have ended every LDS read and copy of the main loop.
-template <class C>
-__device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXFP4_LDS* tile, int pitch,
-                                         int row_begin, int rows, int esize, const RowRange& ar, int n0) {
+template <class C, int ESIZE, int PITCH>
+__device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXFP4_LDS* tile, int row_begin,
+                                         int rows, const RowRange& ar, int n0) {
+  constexpr int esize = ESIZE;
+  constexpr int CPR = C::BN * ESIZE / 16;                  // 16-byte chunks per tile row (power of two)
   const int n = args.n;
-  const int chunks_per_row = C::BN * esize / 16;
   const int valid_rows = min(rows, ar.end - ar.lo - row_begin);
   const int valid_cols = min(C::BN, n - n0);
-  const bool vec_ok = ((n * esize) & 15) == 0;
-  uint8_t* cbase = (uint8_t*)args.c;
-  for (int idx = threadIdx.x; idx < valid_rows * chunks_per_row; idx += kThreads) {
-    const int r = idx / chunks_per_row, cc = idx - r * chunks_per_row;
-    const int col = cc * 16 / esize;
+  const bool vec_ok = ((n * ESIZE) & 15) == 0;
+  uint8_t* cbase = (uint8_t*)args.c + ((int64_t)(ar.lo + row_begin) * n + n0) * ESIZE;
+  const int64_t row_bytes = (int64_t)n * ESIZE;
+  for (int idx = threadIdx.x; idx < valid_rows * CPR; idx += kThreads) {
+    const int r = idx / CPR, cc = idx % CPR;
+    const int col = cc * (16 / ESIZE);
     if (col >= valid_cols) continue;
-    const v4i v = *(const v4i MXFP4_LDS*)(tile + r * pitch + cc * 16);
-    uint8_t* dst = cbase + ((int64_t)(ar.lo + row_begin + r) * n + n0 + col) * esize;
-    const int cnt = min(16 / esize, valid_cols - col);
-    if (vec_ok && cnt * esize == 16) {
+    const v4i v = *(const v4i MXFP4_LDS*)(tile + r * PITCH + cc * 16);
+    uint8_t* dst = cbase + r * row_bytes + cc * 16;
+    const int cnt = min(16 / ESIZE, valid_cols - col);
+    if (vec_ok && cnt * ESIZE == 16) {
       *(v4i*)dst = v;
     } else if (esize == 4) {
       for (int e = 0; e < cnt; ++e) ((uint32_t*)dst)[e] = (uint32_t)(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
@@ -313,7 +315,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const v16f (&ac
           *(v2i MXFP4_LDS*)(lds + r * PITCH + col * 2) = pk;
         }
     __syncthreads();
-    copy_out<C>(args, lds, PITCH, 0, C::BM, 2, ar, n0);
+    copy_out<C, 2, PITCH>(args, lds, 0, C::BM, ar, n0);
   } else {
     constexpr int PITCH = C::BN * 4 + 16;
     static_assert(C::WM * PITCH <= C::LDS_BYTES, "fp32 half tile must fit in the pipeline LDS");
@@ -333,10 +335,25 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const v16f (&ac
             }
       }
       __syncthreads();
-      copy_out<C>(args, lds, PITCH, half * C::WM, C::WM, 4, ar, n0);
+      copy_out<C, 4, PITCH>(args, lds, half * C::WM, C::WM, ar, n0);
       __syncthreads();
     }
   }
+}
+
+// Scheduling pattern for one region holding a k-step's MFMAs and the next
+// k-step's fragment reads: (1 LDS read, 1 MFMA) for every read, then the rest
+// of the MFMAs; sched_barrier(0) closes the region.
+template <class C>
+__device__ __forceinline__ void interleave_reads_mfma() {
+  constexpr int READS = C::MI + C::NI, MFMAS = C::MI * C::NI;
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One pipelined stage (straight-line code: every branch is a template
@@ -351,17 +368,25 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
                                                 int kt, int wm0, int wn0, int lane) {
   uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
   uint8_t MXFP4_LDS* nxt = lds + ((kt + 1) & 1) * C::CODE_STAGE;
+  // Fragment reads run one k-step ahead of the MFMAs.  Before a new batch of
+  // reads is issued, the previous batch (issued a whole k-step earlier, so
+  // already landed) is retired with lgkmcnt(0): the LDS counter holds at most
+  // 15 operations, and with two 8-read batches pending the compiler could
+  // only wait for both, stalling on the batch just issued.
+  // Within a k-step the next k-step's reads are interleaved one per MFMA over
+  // the first MFMAs, so no wave stalls issuing a burst of reads into a full LDS
+  // queue while its MFMAs wait behind them.
   read_frags<C, 1>(cur, fb, wm0, wn0, lane);
-  __builtin_amdgcn_sched_barrier(0);
   mma_kstep<C, 0, 0, C::MI>(fa, sc, acc);
-  __builtin_amdgcn_sched_barrier(0);
+  interleave_reads_mfma<C>();
+  MXFP4_WAIT_LGKM0();
   read_frags<C, 2>(cur, fa, wm0, wn0, lane);
-  __builtin_amdgcn_sched_barrier(0);
   mma_kstep<C, 1, 0, C::MI>(fb, sc, acc);
-  __builtin_amdgcn_sched_barrier(0);
+  interleave_reads_mfma<C>();
+  MXFP4_WAIT_LGKM0();
   read_frags<C, 3>(cur, fb, wm0, wn0, lane);
-  __builtin_amdgcn_sched_barrier(0);
   mma_kstep<C, 2, 0, C::MI>(fa, sc, acc);
+  interleave_reads_mfma<C>();
   const Scales<C> sc_cur = sc;
   __builtin_amdgcn_sched_barrier(0);
   if (NEXT) {
@@ -377,6 +402,8 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
     read_scales_raw<C>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
                        wm0, wn0, lane);
     read_frags<C, 0>(nxt, fa, wm0, wn0, lane);
+  } else {
+    MXFP4_WAIT_LGKM0();
   }
   mma_kstep<C, 3, 0, C::MI>(fb, sc_cur, acc);
   __builtin_amdgcn_sched_barrier(0);
