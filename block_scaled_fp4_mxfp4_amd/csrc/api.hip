@@ -219,7 +219,9 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_
   args.k = (int)k;
   hipError_t e;
   switch (ch.kernel) {
-    case MXFP4_KERNEL_SPLITK: e = mxfp4::launch_gemm_splitk(args, ch.splits, workspace, (hipStream_t)stream); break;
+    case MXFP4_KERNEL_SPLITK:
+      e = mxfp4::launch_gemm_splitk(args, ch.splits, workspace, (hipStream_t)stream, dev.num_cus);
+      break;
     case MXFP4_KERNEL_TILE128: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile128, (hipStream_t)stream); break;
     default: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile256, (hipStream_t)stream); break;
   }

@@ -5,23 +5,27 @@
 // memory-bound, and small shapes leave too few output tiles to fill the chip;
 // its serving section splits K over more CTAs with an fp32 reduction to fill
 // the machine).  Here:
-//  * a workgroup owns all M rows (up to 128) and 64 output columns, and a
-//    K-range given by `splits` (K is cut into 128-element chunks);
-//  * inside the workgroup the 4 waves split that K-range again, each streaming
-//    its own B rows straight from global memory into MFMA operand registers
-//    (no LDS round trip: every B byte is used by exactly one wave), with the
-//    next chunk's loads issued before the current chunk's MFMAs;
-//  * A (small, shared by every workgroup) is read through L2 the same way;
+//  * a workgroup owns all M rows (up to 128) and BN = 64 (or 32) output
+//    columns; with splits == 1 (the automatic choice) it covers the whole K, so
+//    no partial sums leave the workgroup;
+//  * its 4 waves split K into quarters.  Each wave streams its A and B
+//    fragments straight from global memory into MFMA operand registers (no LDS
+//    round trip: every byte is used by exactly one wave), in chunks of 128 K
+//    held in a 3-deep register ring, so up to three chunks are in flight while
+//    the MFMAs of the oldest run (fully unrolled for the common chunk counts);
 //  * the four wave accumulators are summed through LDS in a fixed order;
-//  * with splits > 1 each workgroup writes its fp32 partial tile to the
-//    workspace and bumps a per-column-tile counter; the last of the `splits`
-//    workgroups to arrive sums all partials in split order (deterministic),
-//    writes C and resets the counter to zero for the next call.  The counters
-//    live in the first 64 KiB of the workspace for every shape (so reuse across
-//    shapes never finds partial sums where a counter should be) and the
-//    partial tiles follow.
-// MFMA use is as in the tile kernels: v_mfma_scale_f32_32x32x64_f8f6f4 with
-// the B fragment as first operand, so each lane ends up with 4-column runs.
+//  * with splits > 1 (only when asked for) each workgroup covers a K-range,
+//    writes its fp32 partial tile to the workspace and bumps a per-column-tile
+//    counter; the last of the `splits` workgroups to arrive sums the partials
+//    in split order (deterministic), writes C and resets the counter to zero.
+//    The counters live in the first 64 KiB of the workspace for every shape;
+//    the partial tiles follow.  Cross-workgroup visibility needs agent-scope
+//    release/acquire, which on this chip writes back and invalidates L2, so
+//    this mode is slow and is never chosen automatically.
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with the B fragment as first operand,
+// so each lane ends up with runs of 4 consecutive output columns.  Within a
+// 128-K chunk, k-step s (0..1) reads 32-blocks 2s (lanes 0..31) and 2s+1
+// (lanes 32..63); a row's 4 scale bytes for the chunk arrive as one 32-bit load.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,23 +33,25 @@ namespace mxfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 64;          // output columns per workgroup
-constexpr int kNI = kBN / 32;    // 32-column MFMA blocks per wave
 constexpr int kChunk = 128;      // K elements per pipeline step (2 MFMA k-steps)
+constexpr int kMaxM = 128;
+// The counters occupy a fixed region at the start of every workspace, whatever
+// the shape, so a workspace reused across shapes keeps them at zero.
+constexpr size_t kSplitkCounterBytes = 65536;
 
-template <int MB>
-struct Frag {
+template <int MB, int NI>
+struct Chunk {
   v4i a[MB][2];     // [m-block][k-step]
-  v4i b[kNI][2];
-  int as[MB];       // scale words, already shifted for this lane's K-half
-  int bs[kNI];
+  v4i b[NI][2];
+  int as[MB];       // the row's 4 scale bytes of this chunk
+  int bs[NI];
 };
 
-// Loads one 128-element K chunk. FULL: k % 128 == 0, so every chunk lies inside
-// K and each row's scale word is an aligned 32-bit load; otherwise scales are
-// read byte by byte and 32-blocks past K get zero codes.
-template <int MB, bool FULL>
-__device__ __forceinline__ void load_chunk(Frag<MB>& f, const GemmArgs& args, int n0, int chunk, int lane) {
+// Loads one 128-element K chunk.  FULL: k % 128 == 0, every chunk lies inside
+// K and each row's 4 scale bytes are one aligned 32-bit load; otherwise scales
+// are read byte by byte and 32-blocks past K get zero codes.
+template <int MB, int NI, bool FULL>
+__device__ __forceinline__ void load_chunk(Chunk<MB, NI>& f, const GemmArgs& args, int n0, int chunk, int lane) {
   const int64_t kb = args.k / 2, ks = args.k / 32;
   const int half = lane >> 5;
   const int r32 = lane & 31;
@@ -60,18 +66,17 @@ __device__ __forceinline__ void load_chunk(Frag<MB>& f, const GemmArgs& args, in
       else f.a[i][s] = v4i{0, 0, 0, 0};
     }
     const uint8_t* sp = args.a_s + row * ks + chunk * 4;
-    uint32_t w;
     if (FULL) {
-      w = *(const uint32_t*)sp;
+      f.as[i] = *(const int*)sp;
     } else {
-      w = 0;
+      uint32_t w = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) w |= (chunk * 4 + b < kblocks ? (uint32_t)sp[b] : 127u) << (8 * b);
+      f.as[i] = (int)w;
     }
-    f.as[i] = (int)(w >> (8 * half));
   }
 #pragma unroll
-  for (int j = 0; j < kNI; ++j) {
+  for (int j = 0; j < NI; ++j) {
     const int row = min(n0 + 32 * j + r32, args.n - 1);
     const uint8_t* bp = args.b_q + row * kb + chunk * 64 + half * 16;
 #pragma unroll
@@ -80,27 +85,32 @@ __device__ __forceinline__ void load_chunk(Frag<MB>& f, const GemmArgs& args, in
       else f.b[j][s] = v4i{0, 0, 0, 0};
     }
     const uint8_t* sp = args.b_s + row * ks + chunk * 4;
-    uint32_t w;
     if (FULL) {
-      w = *(const uint32_t*)sp;
+      f.bs[j] = *(const int*)sp;
     } else {
-      w = 0;
+      uint32_t w = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) w |= (chunk * 4 + b < kblocks ? (uint32_t)sp[b] : 127u) << (8 * b);
+      f.bs[j] = (int)w;
     }
-    f.bs[j] = (int)(w >> (8 * half));
   }
 }
 
-template <int MB>
-__device__ __forceinline__ void mma_chunk(const Frag<MB>& f, v16f (&acc)[MB][kNI]) {
+// Lanes 32..63 feed the odd 32-block of each k-step: their scale word moves
+// right by one byte, so k-step s takes byte 2s.
+template <int MB, int NI>
+__device__ __forceinline__ void mma_chunk(const Chunk<MB, NI>& f, v16f (&acc)[MB][NI], int shift) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) {
-      acc[i][j] = mfma32_fp4<0>(f.b[j][0], f.a[i][0], acc[i][j], f.bs[j], f.as[i]);
-      acc[i][j] = mfma32_fp4<2>(f.b[j][1], f.a[i][1], acc[i][j], f.bs[j], f.as[i]);
-    }
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int sa = (int)((uint32_t)f.as[i] >> shift);
+        const int sb = (int)((uint32_t)f.bs[j] >> shift);
+        if (s == 0) acc[i][j] = mfma32_fp4<0>(f.b[j][0], f.a[i][0], acc[i][j], sb, sa);
+        else acc[i][j] = mfma32_fp4<2>(f.b[j][1], f.a[i][1], acc[i][j], sb, sa);
+      }
 }
 
 __device__ __forceinline__ void chunk_range(int nchunks, int parts, int idx, int& lo, int& hi) {
@@ -108,22 +118,59 @@ __device__ __forceinline__ void chunk_range(int nchunks, int parts, int idx, int
   hi = (int)((int64_t)nchunks * (idx + 1) / parts);
 }
 
-template <int MB>
+// A wave's NCH chunks, fully unrolled over a 3-deep register ring: chunk c+3
+// is requested as soon as chunk c's MFMAs are issued, so up to three chunks are
+// in flight.  Straight-line code lets the compiler place exact vmcnt waits.
+// `rot` rotates the chunk order (see the kernel); chunk indices wrap at nchunks.
+template <int MB, int NI, int NCH>
+__device__ __forceinline__ void wave_mainloop_fixed(v16f (&acc)[MB][NI], const GemmArgs& args, int n0, int lo,
+                                                    int rot, int nchunks, int lane) {
+  const int shift = 8 * (lane >> 5);
+  auto at = [&](int c) { const int x = lo + c + rot; return x >= nchunks ? x - nchunks : x; };
+  Chunk<MB, NI> ring[3];
+#pragma unroll
+  for (int c = 0; c < (NCH < 3 ? NCH : 3); ++c) load_chunk<MB, NI, true>(ring[c], args, n0, at(c), lane);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    mma_chunk<MB, NI>(ring[c % 3], acc, shift);
+    if (c + 3 < NCH) load_chunk<MB, NI, true>(ring[c % 3], args, n0, at(c + 3), lane);
+  }
+}
+
+// Any chunk count: two register buffers in a rolled loop.
+template <int MB, int NI, bool FULL>
+__device__ __forceinline__ void wave_mainloop(v16f (&acc)[MB][NI], const GemmArgs& args, int n0, int lo,
+                                              int hi, int lane) {
+  const int shift = 8 * (lane >> 5);
+  Chunk<MB, NI> b0, b1;
+  int c = lo;
+  if (c < hi) load_chunk<MB, NI, FULL>(b0, args, n0, c, lane);
+  if (c + 1 < hi) load_chunk<MB, NI, FULL>(b1, args, n0, c + 1, lane);
+  for (; c + 1 < hi; c += 2) {
+    mma_chunk<MB, NI>(b0, acc, shift);
+    if (c + 2 < hi) load_chunk<MB, NI, FULL>(b0, args, n0, c + 2, lane);
+    mma_chunk<MB, NI>(b1, acc, shift);
+    if (c + 3 < hi) load_chunk<MB, NI, FULL>(b1, args, n0, c + 3, lane);
+  }
+  if (c < hi) mma_chunk<MB, NI>(b0, acc, shift);
+}
+
+template <int MB, int NI>
 __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, int tiles_n, int splits,
                                                                float* __restrict__ partials,
                                                                int* __restrict__ counters) {
+  constexpr int BN = 32 * NI;
   constexpr int TM = 32 * MB;            // rows held per tile
-  constexpr int TILE = TM * kBN;         // fp32 elements per tile
+  constexpr int TILE = TM * BN;          // fp32 elements per tile
   __shared__ float red[4 * TILE];
   __shared__ int last_flag;
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tn = blockIdx.x % tiles_n;
   const int split = blockIdx.x / tiles_n;
-  const int n0 = tn * kBN;
+  const int n0 = tn * BN;
 
   const int nchunks = (args.k + kChunk - 1) / kChunk;
-  const bool aligned = (args.k % kChunk) == 0;
   int wlo, whi;
   {
     int slo, shi;
@@ -134,54 +181,61 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
     whi = slo + b;
   }
 
-  v16f acc[MB][kNI];
+  v16f acc[MB][NI];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNI; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  if (wlo < whi) {
-    Frag<MB> cur, nxt;
-    if (aligned) load_chunk<MB, true>(cur, args, n0, wlo, lane);
-    else load_chunk<MB, false>(cur, args, n0, wlo, lane);
-    for (int c = wlo; c < whi; ++c) {
-      if (c + 1 < whi) {
-        if (aligned) load_chunk<MB, true>(nxt, args, n0, c + 1, lane);
-        else load_chunk<MB, false>(nxt, args, n0, c + 1, lane);
-      }
-      mma_chunk<MB>(cur, acc);
-      cur = nxt;
+  // Every workgroup reads all of A.  Were they all to walk K in the same order,
+  // every CU would ask for the same A lines at the same moment and queue on
+  // one L2 channel; with splits == 1 each workgroup instead starts its K walk
+  // at its own offset (A is small enough to stay resident in L2).
+  const int rot = (splits == 1) ? (int)(((int64_t)tn * 7) % nchunks) : 0;
+  if (args.k % kChunk == 0 && (splits == 1 || rot == 0)) {
+    switch (whi - wlo) {   // wave-uniform
+      case 8: wave_mainloop_fixed<MB, NI, 8>(acc, args, n0, wlo, rot, nchunks, lane); break;
+      case 16: wave_mainloop_fixed<MB, NI, 16>(acc, args, n0, wlo, rot, nchunks, lane); break;
+      case 28: wave_mainloop_fixed<MB, NI, 28>(acc, args, n0, wlo, rot, nchunks, lane); break;
+      case 4: wave_mainloop_fixed<MB, NI, 4>(acc, args, n0, wlo, rot, nchunks, lane); break;
+      default: wave_mainloop<MB, NI, true>(acc, args, n0, wlo, whi, lane); break;
     }
+  } else {
+    wave_mainloop<MB, NI, false>(acc, args, n0, wlo, whi, lane);
   }
 
-  // each wave stores its accumulators as a row-major [TM][kBN] fp32 tile
+  // each wave stores its accumulators as a row-major [TM][BN] fp32 tile
   float* mine = red + w * TILE;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNI; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 32 * i + (lane & 31);
         const int col = 32 * j + 8 * q + 4 * (lane >> 5);
-        *(float4*)(mine + r * kBN + col) =
+        *(float4*)(mine + r * BN + col) =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   __syncthreads();
 
   // fixed-order sum of the 4 wave partials; thread t owns float4 slots t, t+256, ...
   constexpr int SLOTS = TILE / 4;
-  float4 sum[SLOTS / kThreads];
+  constexpr int PER_THREAD = (SLOTS + kThreads - 1) / kThreads;
+  float4 sum[PER_THREAD];
 #pragma unroll
-  for (int u = 0; u < SLOTS / kThreads; ++u) {
+  for (int u = 0; u < PER_THREAD; ++u) {
     const int e = (threadIdx.x + u * kThreads) * 4;
-    float4 s = *(const float4*)(red + e);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < TILE) {
+      s = *(const float4*)(red + e);
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
-      const float4 o = *(const float4*)(red + ww * TILE + e);
-      s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+      for (int ww = 1; ww < 4; ++ww) {
+        const float4 o = *(const float4*)(red + ww * TILE + e);
+        s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+      }
     }
     sum[u] = s;
   }
@@ -189,8 +243,8 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
   const int m = args.m, n = args.n;
   const bool vec_ok = (n & 3) == 0;
   auto store = [&](int e, float4 s) {
-    const int r = e / kBN, col = n0 + (e % kBN);
-    if (r >= m) return;
+    const int r = e / BN, col = n0 + (e % BN);
+    if (e >= TILE || r >= m) return;
     const int64_t off = (int64_t)r * n + col;
     if (args.c_f32) {
       float* cp = (float*)args.c + off;
@@ -211,14 +265,17 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
 
   if (splits == 1) {
 #pragma unroll
-    for (int u = 0; u < SLOTS / kThreads; ++u) store((threadIdx.x + u * kThreads) * 4, sum[u]);
+    for (int u = 0; u < PER_THREAD; ++u) store((threadIdx.x + u * kThreads) * 4, sum[u]);
     return;
   }
 
   // publish this split's partial tile: partials[tile][split][TILE]
   float* my_part = partials + ((int64_t)tn * splits + split) * TILE;
 #pragma unroll
-  for (int u = 0; u < SLOTS / kThreads; ++u) *(float4*)(my_part + (threadIdx.x + u * kThreads) * 4) = sum[u];
+  for (int u = 0; u < PER_THREAD; ++u) {
+    const int e = (threadIdx.x + u * kThreads) * 4;
+    if (e < TILE) *(float4*)(my_part + e) = sum[u];
+  }
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -230,8 +287,9 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
   __threadfence();
   const float* parts = partials + (int64_t)tn * splits * TILE;
 #pragma unroll
-  for (int u = 0; u < SLOTS / kThreads; ++u) {
+  for (int u = 0; u < PER_THREAD; ++u) {
     const int e = (threadIdx.x + u * kThreads) * 4;
+    if (e >= TILE) continue;
     float4 s = *(const float4*)(parts + e);
     for (int sp = 1; sp < splits; ++sp) {
       const float4 o = *(const float4*)(parts + (int64_t)sp * TILE + e);
@@ -242,40 +300,35 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
   if (threadIdx.x == 0) __hip_atomic_store(&counters[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kMaxM = 128;
-// The counters occupy a fixed region at the start of every workspace, whatever
-// the shape, so a workspace reused across shapes keeps them at zero.
-constexpr size_t kSplitkCounterBytes = 65536;
-
 int mblocks_for(int m) { return m <= 32 ? 1 : (m <= 64 ? 2 : 4); }
+
+// 64 output columns per workgroup when that still gives most CUs a workgroup,
+// 32 otherwise (each workgroup reads all of A, so wider tiles read A fewer times).
+int nblocks_for(int n, int num_cus) { return (n + 63) / 64 >= (num_cus * 3) / 4 ? 2 : 1; }
 
 }  // namespace
 
 size_t splitk_workspace_bytes(int m, int n, int k, int splits) {
   (void)k;
   if (splits <= 1) return 0;
-  const int tiles_n = (n + kBN - 1) / kBN;
-  const size_t tile = (size_t)32 * mblocks_for(m) * kBN;
-  const size_t part = (size_t)tiles_n * splits * tile * sizeof(float);
-  return kSplitkCounterBytes + part;
+  // partial tiles of the narrower (32-column) tiling, which needs the most room
+  const size_t per_split = (size_t)((n + 31) / 32) * 32 * (32 * mblocks_for(m)) * sizeof(float);
+  return kSplitkCounterBytes + per_split * splits;
 }
 
 int splitk_max_tiles() { return (int)(kSplitkCounterBytes / sizeof(int)); }
 
 int splitk_auto_splits(int m, int n, int k, int num_cus) {
-  (void)m;
-  const int tiles_n = (n + kBN - 1) / kBN;
-  const int nchunks = (k + kChunk - 1) / kChunk;
-  // enough workgroups to cover every CU, each wave keeping >= 2 chunks of work
-  int s = 1;
-  if (tiles_n > splitk_max_tiles()) return 1;
-  while (tiles_n * s < num_cus && nchunks / (4 * (s * 2)) >= 2 && s < 64) s *= 2;
-  return s;
+  (void)m; (void)n; (void)k; (void)num_cus;
+  return 1;   // full-K workgroups: no partial sums cross workgroups (see the file comment)
 }
 
-hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace, hipStream_t stream) {
+hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace, hipStream_t stream,
+                              int num_cus) {
   if (args.m > kMaxM) return hipErrorInvalidValue;
-  const int tiles_n = (args.n + kBN - 1) / kBN;
+  const int ni = nblocks_for(args.n, num_cus);
+  const int bn = 32 * ni;
+  const int tiles_n = (args.n + bn - 1) / bn;
   int* counters = nullptr;
   float* partials = nullptr;
   if (splits > 1) {
@@ -284,11 +337,20 @@ hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
     partials = (float*)((char*)workspace + kSplitkCounterBytes);
   }
   const dim3 grid((unsigned)(tiles_n * splits));
-  switch (mblocks_for(args.m)) {
-    case 1: hipLaunchKernelGGL((gemm_splitk_kernel<1>), grid, dim3(kThreads), 0, stream, args, tiles_n, splits, partials, counters); break;
-    case 2: hipLaunchKernelGGL((gemm_splitk_kernel<2>), grid, dim3(kThreads), 0, stream, args, tiles_n, splits, partials, counters); break;
-    default: hipLaunchKernelGGL((gemm_splitk_kernel<4>), grid, dim3(kThreads), 0, stream, args, tiles_n, splits, partials, counters); break;
+  const int mb = mblocks_for(args.m);
+#define MXFP4_LAUNCH(MB_, NI_)                                                                               \
+  hipLaunchKernelGGL((gemm_splitk_kernel<MB_, NI_>), grid, dim3(kThreads), 0, stream, args, tiles_n, splits, \
+                     partials, counters)
+  if (ni == 2) {
+    if (mb == 1) MXFP4_LAUNCH(1, 2);
+    else if (mb == 2) MXFP4_LAUNCH(2, 2);
+    else MXFP4_LAUNCH(4, 2);
+  } else {
+    if (mb == 1) MXFP4_LAUNCH(1, 1);
+    else if (mb == 2) MXFP4_LAUNCH(2, 1);
+    else MXFP4_LAUNCH(4, 1);
   }
+#undef MXFP4_LAUNCH
   return hipGetLastError();
 }
 

@@ -27,12 +27,13 @@ hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t str
 
 hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
 
-// Bandwidth path for m <= 128: K split over `splits` workgroups per 64-column
-// tile, fp32 partials and per-tile arrival counters in `workspace`.
+// Bandwidth path for m <= 128: 64- or 32-column tiles, K split over the 4 waves
+// of a workgroup and, when splits > 1, over `splits` workgroups per tile with
+// fp32 partials and per-tile arrival counters in `workspace`.
 size_t splitk_workspace_bytes(int m, int n, int k, int splits);
 int splitk_max_tiles();   // largest ceil(n / 64) that splits > 1 supports
 int splitk_auto_splits(int m, int n, int k, int num_cus);
 hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
-                              hipStream_t stream);
+                              hipStream_t stream, int num_cus);
 
 }  // namespace mxfp4

@@ -100,9 +100,9 @@ def test_workspace_queries(lib):
     # tile kernels need no workspace; split-K with one split needs none either
     assert lib.mxfp4_gemm_nt_ex_workspace_size(512, 512, 256, 1, 0) == 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 256, 3, 1) == 0
-    # split-K with 4 splits: the fixed 64 KiB counter region + 4 fp32 partial tiles per 64-column tile
-    n_tiles = 512 // 64
-    expect = 65536 + n_tiles * 4 * (64 * 64) * 4
+    # split-K with 4 splits: the fixed 64 KiB counter region + 4 fp32 partials of every
+    # 32-column tile (the narrower tiling needs the most room)
+    expect = 65536 + 4 * (512 // 32) * (64 * 32) * 4
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 1024, 3, 4) == expect
     # invalid shapes report 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 100, 3, 4) == 0
