@@ -89,20 +89,29 @@ struct Choice {
   int splits;
 };
 
-// Per-shape kernel choice.
-Choice choose(int64_t m, int64_t n, int64_t k, int num_cus) {
-  if (m <= 128) return {MXFP4_KERNEL_SPLITK, mxfp4::splitk_auto_splits((int)m, (int)n, (int)k, num_cus)};
+// Per-shape kernel choice (`stream_ok`: the streaming kernel's k and scale
+// alignment requirements hold).
+Choice choose(int64_t m, int64_t n, int64_t k, int num_cus, bool stream_ok) {
+  if (m <= 128) {
+    if (stream_ok) return {MXFP4_KERNEL_STREAM, 0};
+    return {MXFP4_KERNEL_SPLITK, mxfp4::splitk_auto_splits((int)m, (int)n, (int)k, num_cus)};
+  }
   const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
   if (tiles256 >= num_cus) return {MXFP4_KERNEL_TILE256, 0};
   return {MXFP4_KERNEL_TILE128, 0};
 }
 
 mxfp4_status_t resolve(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits,
-                       int num_cus, Choice& out) {
+                       int num_cus, bool stream_ok, Choice& out) {
   switch (kernel) {
-    case MXFP4_KERNEL_AUTO: out = choose(m, n, k, num_cus); return MXFP4_OK;
+    case MXFP4_KERNEL_AUTO: out = choose(m, n, k, num_cus, stream_ok); return MXFP4_OK;
     case MXFP4_KERNEL_TILE256:
     case MXFP4_KERNEL_TILE128: out = {kernel, 0}; return MXFP4_OK;
+    case MXFP4_KERNEL_STREAM:
+      if (!stream_ok)
+        return fail(MXFP4_ERR_INVALID_ARG, "the stream kernel needs k %% 512 == 0 and 16-byte aligned scale arrays");
+      out = {kernel, 0};
+      return MXFP4_OK;
     case MXFP4_KERNEL_SPLITK:
       if (m > 128) return fail(MXFP4_ERR_INVALID_ARG, "the split-K kernel takes m <= 128 (got %lld)", (long long)m);
       if (splits < 0 || splits > 64) return fail(MXFP4_ERR_INVALID_ARG, "splits must be 0..64 (got %d)", splits);
@@ -180,8 +189,10 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void*
 
 size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return 0;
+  // without the pointers the alignment is unknown: size for the non-streaming choice
   Choice c;
-  if (resolve(m, n, k, kernel, splits, query_num_cus(), c) != MXFP4_OK) return 0;
+  if (resolve(m, n, k, kernel, splits, query_num_cus(), kernel == MXFP4_KERNEL_STREAM && k % 512 == 0, c) != MXFP4_OK)
+    return 0;
   return workspace_for(c, m, n, k);
 }
 
@@ -194,13 +205,14 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_
                                 mxfp4_kernel_t kernel, int32_t splits, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   MXFP4_TRY(check_gemm_args(a_q, a_s, b_q, b_s, c, c_type, m, n, k));
-  if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_SPLITK)
+  if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_STREAM)
     return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
   if (m == 0 || n == 0) return MXFP4_OK;
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
+  const bool stream_ok = k % 512 == 0 && ((reinterpret_cast<uintptr_t>(a_s) | reinterpret_cast<uintptr_t>(b_s)) & 15) == 0;
   Choice ch;
-  MXFP4_TRY(resolve(m, n, k, kernel, splits, dev.num_cus, ch));
+  MXFP4_TRY(resolve(m, n, k, kernel, splits, dev.num_cus, stream_ok, ch));
   const size_t need = workspace_for(ch, m, n, k);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
@@ -222,6 +234,7 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_
     case MXFP4_KERNEL_SPLITK:
       e = mxfp4::launch_gemm_splitk(args, ch.splits, workspace, (hipStream_t)stream, dev.num_cus);
       break;
+    case MXFP4_KERNEL_STREAM: e = mxfp4::launch_gemm_stream(args, (hipStream_t)stream); break;
     case MXFP4_KERNEL_TILE128: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile128, (hipStream_t)stream); break;
     default: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile256, (hipStream_t)stream); break;
   }

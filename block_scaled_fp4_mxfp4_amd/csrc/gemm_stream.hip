@@ -1,0 +1,276 @@
+// Small-M block-scaled FP4 GEMM that streams the weight matrix (gfx950).
+//
+// Same operation as the tile kernels, C[m][n] = sum_k A[m][k] * B[n][k] over
+// MXFP4 operands ("Packed MXFP4 & NVFP4 GEMM + mega-MoE" page, Summary:
+// mxfp4_gemm_nt; its decode shapes are the small-M case), for M up to a few
+// hundred rows.  There B (the weights, N x K) is read once from HBM and A is
+// small and shared by every workgroup, so the kernel is laid out for bandwidth:
+//
+//  * One workgroup per 64 output columns of one (32*MB)-row M tile, over the
+//    whole K: B is read exactly once and no cross-workgroup reduction exists.
+//  * The copy unit is a "pair": 512 K elements = two 256-K stages of 128 code
+//    bytes per row (A rows then B rows, the tile kernels' conflict-free
+//    128-byte swizzled row layout) plus the 16 scale bytes of every row.
+//    Every copy is global_load_lds_dwordx4 straight into LDS, 8 whole 128-byte
+//    row pieces per wave instruction.  NP pair buffers form a ring; NP - 1 pairs
+//    are in flight while one is consumed.  Both operands go through LDS:
+//    loads straight into registers in the MFMA operand layout touch 32 rows
+//    per instruction and measured far slower on this path than whole-row
+//    copies.  A short kernel like this one is bound by the bytes each CU keeps
+//    in flight (delivery ~ bytes in flight / loaded latency), which the LDS
+//    ring caps; A's share of the ring is what limits larger M.
+//  * The 4 waves split each 256-K stage by k-step: wave w computes k-step w
+//    (K elements 64w..64w+63 of the stage) for the whole 32*MB x 64 tile, so
+//    every code byte copied into LDS is read by exactly one wave.  At the end
+//    the four fp32 partial tiles are reduce-scattered through LDS, each output
+//    summed in the fixed order wave 0 + wave 1 + wave 2 + wave 3, so results
+//    do not depend on timing.
+//  * MFMA operands as in the tile kernels: v_mfma_scale_f32_32x32x64_f8f6f4,
+//    FP4 on both sides, B fed as the first operand so lane l holds output row
+//    l % 32 and runs of four consecutive columns.
+//
+// Requirements (checked by the host): k % 512 == 0 and 16-byte aligned scale
+// arrays.  Rows past M and columns past N read a clamped valid row and are
+// never stored.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;    // code bytes per row per 256-K stage
+constexpr int kBN = 64;
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int MB_, int NP_>
+struct StreamCfg {
+  static constexpr int MB = MB_, NP = NP_;
+  static constexpr int BM = 32 * MB;
+  static constexpr int ROWS = BM + kBN;                   // A rows, then B rows
+  static constexpr int STAGE = ROWS * kRowBytes;
+  static constexpr int SCALES = kThreads * 16;            // one 16-byte piece per thread (rows >= ROWS: padding)
+  static constexpr int PAIR = 2 * STAGE + SCALES;
+  static constexpr int CODE_LOADS = ROWS * 8 / kThreads;  // 16-byte copies per thread per stage
+  static constexpr int PAIR_LOADS = 2 * CODE_LOADS + 1;   // vector-memory ops per thread per pair
+  static constexpr int XCH = 4 * MB * 8 * 64 * 16;        // reduce-scatter exchange: 4 waves x all units
+  static constexpr int LDS = (NP * PAIR > XCH) ? NP * PAIR : XCH;
+  static_assert(ROWS * 8 % kThreads == 0, "code copies must split evenly over the threads");
+  static_assert(ROWS <= kThreads, "one scale piece per row");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert((NP - 2) * PAIR_LOADS <= 63, "vmcnt range");
+};
+
+// Per-thread copy sources.  Copy j of a stage moves slot (j*4 + wave)*64 + lane:
+// row slot/8, logical 16-byte chunk (slot%8) ^ swz(row); pointers are at pair 0.
+template <class C>
+struct Sources {
+  const uint8_t* code[C::CODE_LOADS];
+  const uint8_t* scale;
+};
+
+template <class C>
+__device__ __forceinline__ void make_sources(Sources<C>& src, const GemmArgs& args, int m0, int n0) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t kb = args.k / 2, ks = args.k / 32;
+#pragma unroll
+  for (int j = 0; j < C::CODE_LOADS; ++j) {
+    const int slot = (j * 4 + w) * 64 + lane;
+    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
+    src.code[j] = (r < C::BM) ? args.a_q + min(m0 + r, args.m - 1) * kb + lc * 16
+                              : args.b_q + min(n0 + r - C::BM, args.n - 1) * kb + lc * 16;
+  }
+  const int r = threadIdx.x;   // padding rows re-read A's row m0 into the unused pieces
+  src.scale = (r < C::BM || r >= C::ROWS) ? args.a_s + min(m0 + (r < C::BM ? r : 0), args.m - 1) * ks
+                                          : args.b_s + min(n0 + r - C::BM, args.n - 1) * ks;
+}
+
+// All copies of pair p into `buf` (stage 2p, stage 2p+1, then the scale pieces).
+template <class C>
+__device__ __forceinline__ void copy_pair(uint8_t MXFP4_LDS* buf, const Sources<C>& src, int p) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // LDS base must be wave-uniform (M0)
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < C::CODE_LOADS; ++j)
+      g2lds_16(src.code[j] + (2 * p + s) * kRowBytes,
+               (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
+  g2lds_16(src.scale + p * 16, (MXFP4_LDS void*)(buf + 2 * C::STAGE + w * 64 * 16));
+}
+
+// Wait until at most `pairs` pairs of this thread's copies are outstanding.
+template <class C>
+__device__ __forceinline__ void wait_pairs(int pairs) {
+  switch (pairs) {
+    case 0: MXFP4_WAIT_VMCNT(0); break;
+    case 1: MXFP4_WAIT_VMCNT(C::PAIR_LOADS); break;
+    case 2: MXFP4_WAIT_VMCNT(2 * C::PAIR_LOADS); break;
+    default: MXFP4_WAIT_VMCNT(3 * C::PAIR_LOADS); break;
+  }
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  MXFP4_WAIT_LGKM0();
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Fragments and scale bytes of one wave's k-step of one stage.
+template <class C>
+struct Step {
+  v4i a[C::MB];
+  v4i b[2];
+  int sa[C::MB];
+  int sb[2];
+};
+
+template <class C>
+__device__ __forceinline__ void read_step(const uint8_t MXFP4_LDS* buf, int s, int w, int lane, Step<C>& st) {
+  const uint8_t MXFP4_LDS* stage = buf + s * C::STAGE;
+  const uint8_t MXFP4_LDS* scales = buf + 2 * C::STAGE + 8 * s + 2 * w + (lane >> 5);
+  const int c = 2 * w + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i) {
+    const int r = 32 * i + (lane & 31);
+    st.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    st.sa[i] = scales[r * 16];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = C::BM + 32 * j + (lane & 31);
+    st.b[j] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    st.sb[j] = scales[r * 16];
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mma_step(const Step<C>& st, v16f (&acc)[C::MB][2]) {
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_fp4<0>(st.b[j], st.a[i], acc[i][j], st.sb[j], st.sa[i]);
+}
+
+template <class C>
+__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * C::BM, n0 = tn * kBN;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  v16f acc[C::MB][2];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  Sources<C> src;
+  make_sources<C>(src, args, m0, n0);
+  const int np = args.k / 512;
+  for (int p = 0; p < C::NP - 1 && p < np; ++p) copy_pair<C>(lds + p * C::PAIR, src, p);
+
+  int slot = 0;                 // ring buffer of pair p
+  for (int p = 0; p < np; ++p) {
+    // pair p has landed for this thread; the pairs issued after it may still fly
+    wait_pairs<C>(min(C::NP - 2, np - 1 - p));
+    // ... and for every thread; every wave has also finished reading pair p - 1
+    barrier_lds();
+    if (p + C::NP - 1 < np) {
+      const int refill = (slot == 0) ? C::NP - 1 : slot - 1;   // buffer of pair p - 1
+      copy_pair<C>(lds + refill * C::PAIR, src, p + C::NP - 1);
+    }
+    const uint8_t MXFP4_LDS* buf = lds + slot * C::PAIR;
+    Step<C> s0, s1;
+    read_step<C>(buf, 0, w, lane, s0);
+    read_step<C>(buf, 1, w, lane, s1);
+    mma_step<C>(s0, acc);
+    mma_step<C>(s1, acc);
+    slot = (slot + 1 == C::NP) ? 0 : slot + 1;
+  }
+  MXFP4_WAIT_VMCNT(0);
+  __syncthreads();   // every wave is done with the ring
+
+  // Reduce-scatter of the four waves' fp32 partial tiles.  The accumulators
+  // split into U units of 64 lanes x 4 floats (row block i, column block j,
+  // column group q); wave w owns units [w*U/4, (w+1)*U/4).  Each wave parks the
+  // units it does not own in LDS, then sums each of its units over the waves in
+  // the fixed order 0, 1, 2, 3 and stores it straight from registers.
+  constexpr int U = C::MB * 8, UW = U / 4;
+  v4f MXFP4_LDS* xch = (v4f MXFP4_LDS*)lds;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u / 8, j = (u / 4) % 2, q = u % 4;
+    if (u / UW != w) {
+      v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      xch[(w * U + u) * 64 + lane] = v;
+    }
+  }
+  __syncthreads();
+
+  const int rows = min(C::BM, args.m - m0);
+  const int cols = min(kBN, args.n - n0);
+  const int n = args.n;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u / UW != w) continue;   // wave-uniform
+    const int i = u / 8, j = (u / 4) % 2, q = u % 4;
+    const v4f own = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    v4f v = (w == 0) ? own : xch[u * 64 + lane];
+#pragma unroll
+    for (int src = 1; src < 4; ++src) v += (w == src) ? own : xch[(src * U + u) * 64 + lane];
+    const int r = 32 * i + (lane & 31);
+    const int col = 32 * j + 8 * q + 4 * (lane >> 5);
+    const int cnt = min(4, cols - col);
+    if (r >= rows || cnt <= 0) continue;
+    const int64_t e0 = (int64_t)(m0 + r) * n + n0 + col;
+    if (args.c_f32) {
+      float* dst = (float*)args.c + e0;
+      if (cnt == 4 && (n & 3) == 0) {
+        *(v4f*)dst = v;
+      } else {
+        for (int e = 0; e < cnt; ++e) dst[e] = v[e];
+      }
+    } else {
+      uint16_t* dst = (uint16_t*)args.c + e0;
+      bf16x2_t lo = {(__bf16)v.x, (__bf16)v.y};
+      bf16x2_t hi = {(__bf16)v.z, (__bf16)v.w};
+      if (cnt == 4 && (n & 3) == 0) {
+        v2i pk = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+        *(v2i*)dst = pk;
+      } else {
+        const uint32_t words[2] = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        for (int e = 0; e < cnt; ++e) dst[e] = (uint16_t)(words[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
+  const auto kernel = gemm_stream_kernel<C>;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  const int tiles_n = (args.n + kBN - 1) / kBN;
+  const int tiles_m = (args.m + C::BM - 1) / C::BM;
+  hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(kThreads), C::LDS, stream, args, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool stream_supported(const GemmArgs& args) {
+  return args.k % 512 == 0 && ((reinterpret_cast<uintptr_t>(args.a_s) | reinterpret_cast<uintptr_t>(args.b_s)) & 15) == 0;
+}
+
+hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (!stream_supported(args)) return hipErrorInvalidValue;
+  if (args.m <= 32) return launch_cfg<StreamCfg<1, 5>>(args, stream);
+  if (args.m <= 64) return launch_cfg<StreamCfg<2, 4>>(args, stream);
+  return launch_cfg<StreamCfg<4, 3>>(args, stream);
+}
+
+}  // namespace mxfp4

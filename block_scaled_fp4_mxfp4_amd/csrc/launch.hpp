@@ -36,4 +36,10 @@ int splitk_auto_splits(int m, int n, int k, int num_cus);
 hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
                               hipStream_t stream, int num_cus);
 
+// Small-M weight-streaming kernel: 64-column tiles over the whole K with the
+// 4 waves of a workgroup splitting each 256-K stage by k-step; needs
+// k % 512 == 0 and 16-byte aligned scale arrays (hipErrorInvalidValue otherwise).
+bool stream_supported(const GemmArgs& args);
+hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream);
+
 }  // namespace mxfp4

@@ -167,14 +167,21 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s,
  *   MXFP4_KERNEL_TILE128   128x128 output tiles (more tiles for mid sizes)
  *   MXFP4_KERNEL_SPLITK    M<=128 bandwidth path, K split `splits` ways with
  *                          an fp32 reduction in the workspace
+ *   MXFP4_KERNEL_STREAM    small-M weight-streaming path: 64-column tiles over
+ *                          the whole K, operands copied into LDS in 512-K
+ *                          units; needs k % 512 == 0 and 16-byte aligned
+ *                          scale arrays (MXFP4_ERR_INVALID_ARG otherwise)
  * `splits` is only read for MXFP4_KERNEL_SPLITK (0 = automatic, else 1..64).
+ * For m <= 128 the automatic choice is MXFP4_KERNEL_STREAM when its
+ * requirements hold, else MXFP4_KERNEL_SPLITK; neither needs a workspace then.
  * The workspace needed is mxfp4_gemm_nt_ex_workspace_size(...).
  */
 typedef enum {
   MXFP4_KERNEL_AUTO = 0,
   MXFP4_KERNEL_TILE256 = 1,
   MXFP4_KERNEL_TILE128 = 2,
-  MXFP4_KERNEL_SPLITK = 3
+  MXFP4_KERNEL_SPLITK = 3,
+  MXFP4_KERNEL_STREAM = 4
 } mxfp4_kernel_t;
 
 size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k,

@@ -1,8 +1,8 @@
 """GPU block-scaled FP4 NT GEMM vs the CPU oracle.
 
 Each kernel the library can select (256x256 tiles, 128x128 tiles, the small-M
-split-K path at several split counts) runs on shapes with several tiles and
-ragged M, N and K tails.  Bars:
+split-K path at several split counts, the small-M streaming path) runs on
+shapes with several tiles and ragged M, N and K tails.  Bars:
   * exact regime (every partial sum representable in fp32): fp32 output
     bit-identical to the float64 oracle;
   * fp32 output: floored max-rel <= 1e-5 against the fp32 CPU reference and
@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from block_scaled_fp4_mxfp4_amd import mxfp4_gemm_nt, mxfp4_quantize, workspace
+from block_scaled_fp4_mxfp4_amd import MXFP4Error, mxfp4_gemm_nt, mxfp4_quantize, workspace
 from tests.gpu_common import (assert_bf16_matches_rounded, device, log, poisoned, random_bf16,
                               random_codes, sampled_indices, to_np, upload)
 
@@ -30,6 +30,8 @@ TILE_SHAPES = [  # (m, n, k): several tiles, ragged tails, k % 128 != 0 cases
 ]
 SPLITK_SHAPES = [(1, 64, 128), (17, 200, 1024), (32, 1000, 4096), (33, 70, 160), (100, 512, 2048),
                  (128, 320, 4096), (64, 129, 8192)]
+STREAM_SHAPES = [(1, 64, 512), (17, 200, 1024), (32, 1000, 4096), (33, 70, 512), (64, 129, 8192),
+                 (100, 512, 2048), (128, 320, 4096), (129, 66, 1536), (300, 190, 1024)]
 
 
 def _gemm(aq, as_, bq, bs, dev, kernel, splits, out_dtype, m, n):
@@ -51,6 +53,8 @@ def _cases():
     for splits in (1, 2, 3, 0):
         for shape in SPLITK_SHAPES:
             yield "splitk", splits, shape
+    for shape in STREAM_SHAPES:
+        yield "stream", 0, shape
 
 
 CASES = list(_cases())
@@ -111,6 +115,15 @@ def test_gemm_auto_dispatch_and_empty_problems():
     assert e.shape == (0, 80)
     e = mxfp4_gemm_nt(aq, as_, bq[:0], bs[:0])
     assert e.shape == (96, 0)
+
+
+def test_stream_kernel_rejects_unsupported_k():
+    """The streaming kernel copies 512-K units: any other k is refused, not miscomputed."""
+    dev = device()
+    aq, as_ = random_codes(8, 1056, 1)
+    bq, bs = random_codes(64, 1056, 2)
+    with pytest.raises(MXFP4Error):
+        mxfp4_gemm_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), kernel="stream")
 
 
 def test_splitk_workspace_reuse_across_calls():
