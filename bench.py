@@ -2,20 +2,27 @@
 """Benchmark of the MXFP4 hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input:
-  dynamic BF16 -> MXFP4 quantization of the activation A (the weight B is
-  quantized once beforehand with the same kernel, as a weight packer would),
-  then the block-scaled FP4 NT GEMM to BF16.
+  dynamic BF16 -> MXFP4 quantization of the activation A, then the
+  block-scaled FP4 NT GEMM to BF16.  The weight B is quantized once beforehand
+  with the same kernel (a weight packer's job, outside the step); its
+  quantization time is reported separately.
 Primary workload: M = N = K = 4096 (TFLOP/s, 2*M*N*K per step).
 Secondary workload: decode M=128, N=14336, K=4096 (achieved HBM GB/s).
 
 Inputs are resident in HBM before timing.  Steps rotate over enough copies of
 the inputs (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot serve
 them.  Each timed region is a HIP graph of whole steps replayed on the stream
-the kernels run on, bracketed by events and device synchronisations.
+the kernels run on, bracketed by events and device synchronisations; one event
+pair per graph replay also gives min / median / max per-step times.
 
 Prints one JSON line on stdout.  The roofline object is for the GEMM kernel:
 algorithmic flops (or bytes) per launch divided by the kernel's mean duration,
 measured with events over a region of back-to-back GEMM launches.
+
+`--only {step,gemm,quantize,quantize_b,copy}` instead runs that work eagerly
+`--steps` times and prints nothing on stdout: the mode used under rocprofv3
+(kernel traces and counter passes; `copy` is the plain device copy that
+calibrates the byte counters).
 """
 from __future__ import annotations
 
@@ -23,13 +30,13 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import workloads  # noqa: E402
@@ -37,6 +44,7 @@ import workloads  # noqa: E402
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATION_BYTES = 512 << 20
+COPY_BYTES = 512 << 20        # size of the counter-calibration copy
 
 
 def eprint(*a):
@@ -49,6 +57,7 @@ def gemm_algorithmic_bytes(m, n, k, out_bytes=2):
 
 
 def quant_algorithmic_bytes(rows, k):
+    """BF16 in, packed codes and scale bytes out."""
     return rows * k * 2 + rows * k // 2 + rows * k // 32
 
 
@@ -61,7 +70,7 @@ class DenseBench:
         a, b = w.make()
         self.a_cpu, self.b_cpu = a, b
         a_d, b_d = a.to(dev), b.to(dev)
-        bq, bs = B.mxfp4_quantize(b_d)            # weight quantized once (not timed)
+        bq, bs = B.mxfp4_quantize(b_d)            # weight quantized once (not in the step)
         m, n, k = w.m, w.n, w.k
         per_set = m * k * 2 + m * k // 2 + m * k // 32 + n * k // 2 + n * k // 32 + m * n * 2
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
@@ -72,58 +81,78 @@ class DenseBench:
                 a=a_d.clone(), aq=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
                 as_=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
                 bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
+        # the weight-packing kernel gets rotating sources of its own
+        self.b_sets = [b_d.clone() for _ in range(max(2, math.ceil(ROTATION_BYTES / (n * k * 2))))]
+        self.b_out = (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                      torch.empty((n, k // 32), dtype=torch.uint8, device=dev))
         need = B.load_library().mxfp4_gemm_nt_workspace_size(m, n, k)
         self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         del a_d, b_d
         torch.cuda.synchronize()
 
-    def quantize(self, s):
+    def quantize(self, i):
+        s = self.sets[i % self.sets_n]
         self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
-    def gemm(self, s):
+    def quantize_b(self, i):
+        self.B.mxfp4_quantize(self.b_sets[i % len(self.b_sets)], *self.b_out)
+
+    def gemm(self, i):
+        s = self.sets[i % self.sets_n]
         self.B.mxfp4_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"], ws=self.ws)
 
-    def step(self, s):
-        self.quantize(s)
-        self.gemm(s)
+    def step(self, i):
+        self.quantize(i)
+        self.gemm(i)
 
-    def _graph(self, fn, count, start=0):
+    @staticmethod
+    def _graph(fn, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(count):
-                fn(self.sets[(start + i) % self.sets_n])
+                fn(i)
         return g
 
-    def timed(self, fn, steps, warmup):
-        """Mean ms per call of fn over `steps` calls rotating through the input sets."""
+    def timed(self, fn, steps, warmup, period=None):
+        """Times exactly `steps` calls fn(0), fn(1), ... as graph replays of one
+        rotation period each.  Returns mean / min / median / max ms per call (the
+        spread is over the full periods)."""
+        period = period or self.sets_n
         for i in range(2):                    # eager warm-up before capture
-            fn(self.sets[i % self.sets_n])
+            fn(i)
         torch.cuda.synchronize()
-        cycle = self._graph(fn, self.sets_n)
-        rem = steps % self.sets_n
+        cycle = self._graph(fn, period)
+        rem = steps % period
         tail = self._graph(fn, rem) if rem else None
-        for _ in range(max(1, math.ceil(warmup / self.sets_n))):
+        for _ in range(max(1, math.ceil(warmup / period))):
             cycle.replay()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps // self.sets_n):
+        full = steps // period
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(full + 2)]
+        ev[0].record()
+        for r in range(full):
             cycle.replay()
+            ev[r + 1].record()
         if tail is not None:
             tail.replay()
-        t1.record()
+        ev[-1].record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        per = [ev[r].elapsed_time(ev[r + 1]) / period for r in range(full)]
+        total = ev[0].elapsed_time(ev[-1]) / steps
+        per = per or [total]
+        return {"mean": total, "min": min(per), "median": statistics.median(per), "max": max(per)}
 
 
 def cpu_baseline(bench: DenseBench, target_seconds: float):
-    """The CPU oracle (as it stands) on a bounded sample of the same step: quantize
-    `rows` rows of A and multiply them by the full pre-quantized B."""
+    """The CPU oracle, as it stands, on a bounded sample of the same step: oracle
+    quantization of A, then its float64 GEMM against the pre-quantized B (the
+    weight packing is outside the step, as on the GPU).  The whole step is
+    repeated to fill about `target_seconds`; if one step would take longer than
+    that, only the first rows of A are used."""
     import oracle
     from threadpoolctl import threadpool_info
     w = bench.w
-    bq, bs = oracle.quantize(workloads.bf16_bits(bench.b_cpu))   # weight packing, untimed
+    bq, bs = oracle.quantize(workloads.bf16_bits(bench.b_cpu))
     a_bits = workloads.bf16_bits(bench.a_cpu)
 
     def run(rows):
@@ -132,35 +161,75 @@ def cpu_baseline(bench: DenseBench, target_seconds: float):
         oracle.gemm_nt(aq, as_, bq, bs)
         return time.perf_counter() - t
 
-    pilot_rows = min(w.m, 32)
+    pilot_rows = min(w.m, 64)
     t_pilot = run(pilot_rows)
-    rows = int(min(w.m, max(pilot_rows, pilot_rows * target_seconds / max(t_pilot, 1e-3))))
-    t = run(rows)
-    flops = 2 * rows * w.n * w.k
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of {w.m} rows of A: oracle quantize + float64 GEMM against the full "
-                      f"pre-quantized {w.n}x{w.k} B ({t:.1f} s); numpy/BLAS threads as listed in cores"}
+    est_full = t_pilot * w.m / pilot_rows
+    if est_full <= target_seconds:
+        rows = w.m
+        reps = max(1, round(target_seconds / max(run(rows), 1e-3)))
+    else:
+        rows = max(pilot_rows, int(w.m * target_seconds / est_full))
+        reps = 1
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run(rows)
+    t = time.perf_counter() - t0
+    flops = 2 * rows * w.n * w.k * reps
+    blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+    avail = len(os.sched_getaffinity(0))
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{rows} of {w.m} rows of A, {reps} repetition(s), {t:.1f} s: oracle quantize of A "
+                      f"(NumPy, one thread) + float64 BLAS GEMM against the pre-quantized {w.n}x{w.k} B "
+                      f"({blas} BLAS threads of {avail} available cores)"}
 
 
-def traffic_from_profiles(kernel_key: str):
-    """HBM bytes per launch recorded under profiles/ for this kernel, if the kernel
-    sources have not changed since the counters were taken (else None)."""
+def sources_sha():
+    """Hash of the HIP sources: recorded counter data is only valid for these."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.md")
-    if not os.path.exists(path):
-        return None
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_mxfp4_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
-    sha = h.hexdigest()[:16]
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per GEMM launch recorded in profiles/traffic.md for this
+    workload, if the kernel sources have not changed since the counters were
+    taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    sha = sources_sha()
     for line in open(path):
         parts = dict(p.split("=", 1) for p in line.split() if "=" in p)
-        if parts.get("workload") == kernel_key and parts.get("sources") == sha and "bytes_per_launch" in parts:
+        if parts.get("workload") == workload and parts.get("sources") == sha and "bytes_per_launch" in parts:
             return float(parts["bytes_per_launch"])
     return None
+
+
+def run_only(args, dev):
+    """Eager launches for profiling runs."""
+    if args.only == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"[bench] {args.steps} copies of {COPY_BYTES} bytes")
+        return
+    w = workloads.DENSE[args.workload]
+    bench = DenseBench(w, dev)
+    fn = getattr(bench, args.only)
+    for i in range(args.warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        fn(i)
+    torch.cuda.synchronize()
+    eprint(f"[bench] {args.steps} eager '{args.only}' launches on {w.name}")
 
 
 def main():
@@ -173,6 +242,7 @@ def main():
                     help="second dense workload reported in the same line ('none' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -185,20 +255,30 @@ def main():
     dev = torch.device("cuda", 0)
     from block_scaled_fp4_mxfp4_amd import load_library
     load_library()
+    if args.only:
+        run_only(args, dev)
+        return
 
     w = workloads.DENSE[args.workload]
     eprint(f"[bench] building inputs for {w.name}")
     bench = DenseBench(w, dev)
     eprint(f"[bench] {bench.sets_n} rotating input sets of {bench.per_set_bytes / 2**20:.1f} MiB")
-    step_ms = bench.timed(bench.step, args.steps, args.warmup)
-    gemm_ms = bench.timed(bench.gemm, args.steps, args.warmup)
-    quant_ms = bench.timed(bench.quantize, args.steps, args.warmup)
-    eprint(f"[bench] step {step_ms*1e3:.2f} us, gemm {gemm_ms*1e3:.2f} us, quantize {quant_ms*1e3:.2f} us")
+    step = bench.timed(bench.step, args.steps, args.warmup)
+    gemm = bench.timed(bench.gemm, args.steps, args.warmup)
+    quant = bench.timed(bench.quantize, args.steps, args.warmup)
+    quant_b = bench.timed(bench.quantize_b, args.steps, args.warmup, period=len(bench.b_sets))
+    eprint(f"[bench] step {step['mean']*1e3:.2f} us, gemm {gemm['mean']*1e3:.2f} us, "
+           f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us")
 
     flops = w.flops
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    step_tflops = flops / (step_ms * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm["mean"] * 1e-3) / 1e12
+    step_tflops = flops / (step["mean"] * 1e-3) / 1e12
     qbytes = quant_algorithmic_bytes(w.m, w.k)
+    qbbytes = quant_algorithmic_bytes(w.n, w.k)
+
+    def us(t):
+        return {k: round(v * 1e3, 3) for k, v in t.items()}
+
     result = {
         "metric": "MXFP4 GEMM TFLOP/s at 4096^3; achieved HBM GB/s at decode M=128",
         "value": round(step_tflops, 2),
@@ -206,7 +286,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 6),
+        "ms_per_step": round(step["mean"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -218,11 +298,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic_from_profiles(w.name)},
+        "step_us": us(step),
         "kernels": {
-            "gemm_us": round(gemm_ms * 1e3, 3), "gemm_tflops": round(gemm_tflops, 2),
-            "quantize_us": round(quant_ms * 1e3, 3),
-            "quantize_gbs": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
-            "quantize_hbm_frac": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_us": us(gemm), "gemm_tflops": round(gemm_tflops, 2),
+            "quantize_a_us": us(quant),
+            "quantize_a_gbs": round(qbytes / (quant["mean"] * 1e-3) / 1e9, 1),
+            "quantize_a_hbm_frac": round(qbytes / (quant["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "quantize_b_us": us(quant_b),
+            "quantize_b_gbs": round(qbbytes / (quant_b["mean"] * 1e-3) / 1e9, 1),
         },
     }
 
@@ -235,19 +318,20 @@ def main():
         q2 = b2.timed(b2.quantize, args.steps, args.warmup)
         gbytes = gemm_algorithmic_bytes(w2.m, w2.n, w2.k)
         qb2 = quant_algorithmic_bytes(w2.m, w2.k)
-        gemm_gbs = gbytes / (g2 * 1e-3) / 1e9
+        gemm_gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
         result["secondary"] = {
             "metric": "achieved HBM GB/s at decode M=128", "workload": w2.name,
-            "value": round((gbytes + qb2) / (s2 * 1e-3) / 1e9, 1), "unit": "GB/s",
-            "ms_per_step": round(s2, 6), "rotating_input_sets": b2.sets_n,
-            "step": "quantize A + split-K mxfp4 GEMM (B pre-quantized)",
+            "value": round((gbytes + qb2) / (s2["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(s2["mean"], 6), "step_us": us(s2), "rotating_input_sets": b2.sets_n,
+            "step": "quantize A + streaming mxfp4 GEMM (B pre-quantized)",
             "roofline": {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_from_profiles(w2.name)},
-            "kernels": {"gemm_us": round(g2 * 1e3, 3), "quantize_us": round(q2 * 1e3, 3),
-                        "gemm_tflops": round(w2.flops / (g2 * 1e-3) / 1e12, 2)},
+            "kernels": {"gemm_us": us(g2), "quantize_a_us": us(q2),
+                        "gemm_tflops": round(w2.flops / (g2["mean"] * 1e-3) / 1e12, 2)},
         }
-        eprint(f"[bench] {w2.name}: step {s2*1e3:.2f} us, gemm {g2*1e3:.2f} us ({gemm_gbs:.0f} GB/s)")
+        eprint(f"[bench] {w2.name}: step {s2['mean']*1e3:.2f} us, gemm {g2['mean']*1e3:.2f} us "
+               f"({gemm_gbs:.0f} GB/s)")
         del b2
 
     if not args.no_cpu_baseline:
