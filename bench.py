@@ -8,6 +8,8 @@ One step = the whole path over one batch of synthetic input:
   quantization time is reported separately.
 Primary workload: M = N = K = 4096 (TFLOP/s, 2*M*N*K per step).
 Secondary workload: decode M=128, N=14336, K=4096 (achieved HBM GB/s).
+Also reported: the grouped MoE layer (8192 tokens, top-4 of 64 experts,
+N=2816, K=4096) in TFLOP/s and GB/s.
 
 Inputs are resident in HBM before timing.  Steps rotate over enough copies of
 the inputs (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot serve
@@ -143,6 +145,58 @@ class DenseBench:
         return {"mean": total, "min": min(per), "median": statistics.median(per), "max": max(per)}
 
 
+class MoEBench:
+    """The grouped per-expert workload: routed rows sorted by expert, one
+    weight matrix per expert (quantized once), device offsets."""
+
+    def __init__(self, w: workloads.MoEWorkload, dev):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        self.w = w
+        a, wts, offsets = w.make()
+        self.counts = (offsets[1:] - offsets[:-1]).tolist()
+        rows, n, k, e = w.total_rows, w.n, w.k, w.experts
+        a_d = a.to(dev)
+        wq, ws = B.mxfp4_quantize(wts.view(e * n, k).to(dev))
+        del wts
+        wq, ws = wq.view(e, n, k // 2), ws.view(e, n, k // 32)
+        off_d = offsets.to(dev)
+        per_set = rows * k * 2 + rows * k // 2 + rows * k // 32 + e * n * k // 2 + e * n * k // 32 + rows * n * 2
+        self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
+        self.sets = []
+        for _ in range(self.sets_n):
+            self.sets.append(dict(
+                a=a_d.clone(), aq=torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
+                as_=torch.empty((rows, k // 32), dtype=torch.uint8, device=dev),
+                wq=wq.clone(), ws=ws.clone(), off=off_d.clone(),
+                c=torch.empty((rows, n), dtype=torch.bfloat16, device=dev)))
+        del a_d, wq, ws
+        torch.cuda.synchronize()
+
+    def quantize(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
+
+    def gemm(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
+
+    def step(self, i):
+        self.quantize(i)
+        self.gemm(i)
+
+    def algorithmic_bytes(self):
+        """Codes and scales of A and of every expert that has rows, plus C."""
+        w = self.w
+        used = sum(1 for c in self.counts if c > 0)
+        rows = w.total_rows
+        return (used * (w.n * w.k // 2 + w.n * w.k // 32) + rows * w.k // 2 + rows * w.k // 32
+                + rows * w.n * 2)
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+
 def cpu_baseline(bench: DenseBench, target_seconds: float):
     """The CPU oracle, as it stands, on a bounded sample of the same step: oracle
     quantization of A, then its float64 GEMM against the pre-quantized B (the
@@ -240,6 +294,8 @@ def main():
     ap.add_argument("--workload", default=workloads.SQUARE4096.name, choices=sorted(workloads.DENSE))
     ap.add_argument("--secondary", default=workloads.DECODE.name,
                     help="second dense workload reported in the same line ('none' to skip)")
+    ap.add_argument("--moe", default=workloads.MOE.name,
+                    help="grouped MoE workload reported in the same line ('none' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy"])
@@ -333,6 +389,33 @@ def main():
         eprint(f"[bench] {w2.name}: step {s2['mean']*1e3:.2f} us, gemm {g2['mean']*1e3:.2f} us "
                f"({gemm_gbs:.0f} GB/s)")
         del b2
+
+    if args.moe != "none":
+        wm = workloads.ALL[args.moe]
+        eprint(f"[bench] building inputs for {wm.name}")
+        mb = MoEBench(wm, dev)
+        msteps = max(4, args.steps // 10)
+        sm = mb.timed(mb.step, msteps, 2)
+        gm = mb.timed(mb.gemm, msteps, 2)
+        qm = mb.timed(mb.quantize, msteps, 2)
+        mbytes = mb.algorithmic_bytes()
+        tf = wm.flops / (gm["mean"] * 1e-3) / 1e12
+        gbs = mbytes / (gm["mean"] * 1e-3) / 1e9
+        counts = mb.counts
+        result["moe"] = {
+            "workload": wm.name, "tokens": wm.tokens, "experts": wm.experts, "top_k": wm.top_k,
+            "n": wm.n, "k": wm.k, "steps": msteps, "rotating_input_sets": mb.sets_n,
+            "rows_per_expert": {"min": min(counts), "max": max(counts), "empty": sum(c == 0 for c in counts)},
+            "step": "quantize routed A + grouped mxfp4 GEMM (expert weights pre-quantized)",
+            "step_us": us(sm), "step_tflops": round(wm.flops / (sm["mean"] * 1e-3) / 1e12, 2),
+            "gemm_us": us(gm), "quantize_a_us": us(qm),
+            "gemm_tflops": round(tf, 2), "gemm_mfma_frac": round(tf / PEAK_FP4_TFLOPS, 4),
+            "gemm_gbs": round(gbs, 1), "gemm_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": mbytes,
+        }
+        eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
+               f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
+        del mb
 
     if not args.no_cpu_baseline:
         eprint("[bench] timing the CPU oracle on a bounded sample")
