@@ -1,0 +1,63 @@
+"""Writes tests/golden/oracle_digests.txt from the CPU oracle alone.
+
+The pages print no worked numerical example of the format or the GEMM, so the
+stored values here are the oracle's own results on the seeded workloads:
+SHA-256 digests of its quantized code and scale bytes and of the BF16
+(nearest-even) GEMM output, plus a few output values.  They freeze the oracle:
+a later change to its arithmetic shows up as a mismatch and has to be justified
+against the pages.  Run from the repository root:
+
+    python tests/golden/make_golden.py
+"""
+from __future__ import annotations
+
+import hashlib
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_digests.txt")
+
+
+def digest(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def entries():
+    tiny = workloads.TINY
+    a, b = tiny.make()
+    aq, as_ = oracle.quantize(workloads.bf16_bits(a))
+    bq, bs = oracle.quantize(workloads.bf16_bits(b))
+    c = oracle.gemm_nt(aq, as_, bq, bs)
+    c16 = oracle.f64_to_bf16_bits(c)
+    yield f"{tiny.name}.a_q", digest(aq)
+    yield f"{tiny.name}.a_s", digest(as_)
+    yield f"{tiny.name}.b_q", digest(bq)
+    yield f"{tiny.name}.b_s", digest(bs)
+    yield f"{tiny.name}.c_bf16", digest(c16)
+    for (i, j) in [(0, 0), (17, 100), (63, 255)]:
+        yield f"{tiny.name}.c[{i},{j}]", float(c[i, j]).hex()
+    dec = workloads.DECODE
+    a, _ = dec.make()
+    aq, as_ = oracle.quantize(workloads.bf16_bits(a))
+    yield f"{dec.name}.a_q", digest(aq)
+    yield f"{dec.name}.a_s", digest(as_)
+
+
+def main():
+    lines = [f"{k} {v}" for k, v in entries()]
+    with open(OUT, "w") as f:
+        f.write("# written by tests/golden/make_golden.py from the CPU oracle; do not edit by hand\n")
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

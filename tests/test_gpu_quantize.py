@@ -117,3 +117,20 @@ def test_quantize_workload_operands(name):
         oq, os_ = oracle.quantize(bits)
         assert np.array_equal(to_np(s)[rows], os_), f"{label} scales"
         assert np.array_equal(to_np(q)[rows], oq), f"{label} codes"
+
+
+def test_quantize_matches_stored_oracle_digests():
+    """Bytes of the tiny and decode operands equal the oracle's stored digests
+    (tests/golden/oracle_digests.txt, written from the oracle alone)."""
+    import hashlib
+    from tests.test_golden import load_golden
+    gold = load_golden()
+    dev = device()
+    a, b = workloads.TINY.make()
+    cases = [(workloads.TINY.name + ".a", a), (workloads.TINY.name + ".b", b),
+             (workloads.DECODE.name + ".a", workloads.DECODE.make()[0])]
+    for name, x in cases:
+        q, s = mxfp4_quantize(x.to(dev))
+        torch.cuda.synchronize()
+        assert hashlib.sha256(to_np(q).tobytes()).hexdigest() == gold[name + "_q"], name
+        assert hashlib.sha256(to_np(s).tobytes()).hexdigest() == gold[name + "_s"], name
