@@ -33,8 +33,17 @@
 //    one barrier; then the buffer of stage kt is free, the copies of stage
 //    kt+2 go into it, and stage kt+1's first fragments are read while the last
 //    MFMAs of stage kt run.
-//  * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
-//    sub-tile as (BM/64) x (BN/64) MFMA blocks of 32x32 (accumulators in AGPRs).
+//  * Waves form a 2 x WGN grid over the tile, each owning a (BM/2) x (BN/WGN)
+//    sub-tile of 32x32 MFMA blocks.  256x256 tiles use 8 waves (2 per SIMD,
+//    128x64 each, 256 registers per wave): with one wave per SIMD every stall
+//    of its in-order instruction stream (a fragment wait, a copy or read
+//    stuck at issue, a barrier) idled that SIMD's matrix unit, and counters
+//    showed waves waiting on instruction issue about half of the time; a
+//    second wave fills those gaps.  Copy sources are 32-bit offsets from
+//    workgroup-uniform tile bases so the register budget holds without
+//    spills in the main loop.
+//  * Copies of the next stage are issued spread over the MFMAs of the last
+//    k-step rather than in one burst.
 //  * Workgroup -> tile mapping is XCD-aware (see tile_coords in common.hpp).
 //
 // Ragged edges: rows past M (or N) read a clamped, valid row and are never
@@ -49,25 +58,28 @@ namespace {
 
 constexpr int kBK = 256;            // K elements per stage
 constexpr int kRowBytes = kBK / 2;  // code bytes per row per stage
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WGM_, int WGN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WGM = WGM_, WGN = WGN_;               // wave grid over the tile
+  static constexpr int NWAVES = WGM * WGN, THREADS = 64 * NWAVES;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   static constexpr int CODE_STAGE = A_BYTES + B_BYTES;
   static constexpr int SCALE_GROUP = (BM + BN) * 16;        // 16 scale bytes per row = two stages
   static constexpr int LDS_BYTES = 2 * CODE_STAGE + 2 * SCALE_GROUP;
-  static constexpr int A_LOADS = BM * kRowBytes / 16 / kThreads;   // 16-byte copies per thread per stage
-  static constexpr int B_LOADS = BN * kRowBytes / 16 / kThreads;
-  static constexpr int S_LOADS = (BM + BN) / kThreads;            // 16-byte scale copies per thread per group
+  static constexpr int A_LOADS = BM * kRowBytes / 16 / THREADS;   // 16-byte copies per thread per stage
+  static constexpr int B_LOADS = BN * kRowBytes / 16 / THREADS;
+  static constexpr int S_LOADS = (BM + BN) / THREADS;            // 16-byte scale copies per thread per group
   static constexpr int CODE_LOADS = A_LOADS + B_LOADS;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
-  static_assert((BM + BN) % kThreads == 0, "scale copies must split evenly over the threads");
+  static_assert((BM + BN) % THREADS == 0, "scale copies must split evenly over the threads");
+  static_assert(WGM == 2, "the fp32 epilogue stages the tile in two halves by wave row");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles of whole 32x32 MFMA blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -79,60 +91,96 @@ struct RowRange {
   int end;    // one past the last row that is stored
 };
 
-// Per-thread source offsets (bytes) of the copies, at stage 0 / scale group 0.
+// Workgroup-uniform bases of one output tile: its first A row, first B row,
+// and their scale rows.  Per-thread copy offsets are taken from these, so they
+// fit 32 bits (a tile spans at most 256 rows) and the bases stay in scalar
+// registers.
+struct TileBases {
+  const uint8_t* a_q;
+  const uint8_t* b_q;
+  const uint8_t* a_s;
+  const uint8_t* b_s;
+};
+
+__device__ __forceinline__ TileBases tile_bases(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
+                                                const RowRange& ar, int n0) {
+  const int64_t kb = args.k / 2, ks = args.k / 32;
+  return {args.a_q + ar.lo * kb, b_q + n0 * kb, args.a_s + ar.lo * ks, b_s + n0 * ks};
+}
+
+// Per-thread byte offsets of the copies from the tile bases, at stage 0 / scale
+// group 0.  Copy j of a stage moves slot (j*NWAVES + wave)*64 + lane: row slot/8,
+// logical 16-byte chunk (slot%8) ^ swz(row).  Rows past the operand's end read
+// its last row (never stored).
 template <class C>
 struct Sources {
-  int64_t a_code[C::A_LOADS];
-  int64_t b_code[C::B_LOADS];
-  int64_t scale[C::S_LOADS];     // A rows use a_s, B rows use b_s (see is_b)
-  bool is_b[C::S_LOADS];
+  uint32_t a_code[C::A_LOADS];
+  uint32_t b_code[C::B_LOADS];
+  uint32_t scale[C::S_LOADS];    // slots below BM are A rows, the rest B rows
 };
+
+// Whether scale slot group j of wave w holds B rows: BM is a multiple of 64,
+// so all 64 lanes of a wave instruction agree.
+template <class C>
+__device__ __forceinline__ bool scale_is_b(int j, int w) {
+  return (j * C::NWAVES + w) * 64 >= C::BM;
+}
 
 template <class C>
 __device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t kb = k / 2, ks = k / 32;
+  const uint32_t kb = k / 2, ks = k / 32;
+  const int a_rows = ar.last - ar.lo, b_rows = n - 1 - n0;   // largest valid row offsets
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
     const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
-    src.a_code[j] = min(ar.lo + r, ar.last) * kb + lc * 16;
+    src.a_code[j] = (uint32_t)min(r, a_rows) * kb + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
     const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
-    src.b_code[j] = min(n0 + r, n - 1) * kb + lc * 16;
+    src.b_code[j] = (uint32_t)min(r, b_rows) * kb + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
-    src.is_b[j] = slot >= C::BM;
-    src.scale[j] = src.is_b[j] ? min(n0 + slot - C::BM, n - 1) * ks : min(ar.lo + slot, ar.last) * ks;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
+    src.scale[j] = slot >= C::BM ? (uint32_t)min(slot - C::BM, b_rows) * ks : (uint32_t)min(slot, a_rows) * ks;
   }
 }
 
-// Code copies of stage kt into `stage` (direct global -> LDS).
+// Code copies of stage kt into `stage` (direct global -> LDS), A rows and B
+// rows separately: the pipeline issues them in different k-steps.
 template <class C>
-__device__ __forceinline__ void copy_codes(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const uint8_t* a_q,
-                                           const uint8_t* b_q, int kt) {
+__device__ __forceinline__ void copy_codes_a(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileBases& tb,
+                                             int kt) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS base goes to M0
+  const uint8_t* a = tb.a_q + kt * kRowBytes;
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j)
-    g2lds_16(a_q + src.a_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + (j * 4 + w) * 64 * 16));
+    g2lds_16(a + src.a_code[j], (MXFP4_LDS void*)(stage + (j * C::NWAVES + w) * 64 * 16));
+}
+
+template <class C>
+__device__ __forceinline__ void copy_codes_b(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileBases& tb,
+                                             int kt) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint8_t* b = tb.b_q + kt * kRowBytes;
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j)
-    g2lds_16(b_q + src.b_code[j] + kt * kRowBytes, (MXFP4_LDS void*)(stage + C::A_BYTES + (j * 4 + w) * 64 * 16));
+    g2lds_16(b + src.b_code[j], (MXFP4_LDS void*)(stage + C::A_BYTES + (j * C::NWAVES + w) * 64 * 16));
 }
 
 // Scale copies of group g (stages 2g and 2g+1): 16 bytes of every row.
 template <class C>
-__device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const uint8_t* a_s,
-                                            const uint8_t* b_s, int g) {
+__device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const TileBases& tb,
+                                            int g) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j)
-    g2lds_16((src.is_b[j] ? b_s : a_s) + src.scale[j] + g * 16, (MXFP4_LDS void*)(group + (j * 4 + w) * 64 * 16));
+    g2lds_16((scale_is_b<C>(j, w) ? tb.b_s : tb.a_s) + g * 16 + src.scale[j],
+             (MXFP4_LDS void*)(group + (j * C::NWAVES + w) * 64 * 16));
 }
 
 // Stage kt through registers for any k % 32 == 0: 32-blocks at or past k get
@@ -140,30 +188,29 @@ __device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sour
 // (scale bytes of stage kt at byte 8 * (kt & 1) of each row's 16-byte piece).
 template <class C>
 __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uint8_t MXFP4_LDS* group,
-                                                   const Sources<C>& src, const GemmArgs& args,
-                                                   const uint8_t* b_q, const uint8_t* b_s, int kt) {
+                                                   const Sources<C>& src, const TileBases& tb, int k, int kt) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int blocks_left = args.k / 32 - kt * 8;   // valid 32-blocks in this stage (may exceed 8)
+  const int blocks_left = k / 32 - kt * 8;   // valid 32-blocks in this stage (may exceed 8)
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
     const int lc = (slot & 7) ^ swz(slot >> 3);
     v4i v = {0, 0, 0, 0};
-    if (lc < blocks_left) v = *(const v4i*)(args.a_q + src.a_code[j] + kt * kRowBytes);
+    if (lc < blocks_left) v = *(const v4i*)(tb.a_q + kt * kRowBytes + src.a_code[j]);
     *(v4i MXFP4_LDS*)(stage + slot * 16) = v;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
     const int lc = (slot & 7) ^ swz(slot >> 3);
     v4i v = {0, 0, 0, 0};
-    if (lc < blocks_left) v = *(const v4i*)(b_q + src.b_code[j] + kt * kRowBytes);
+    if (lc < blocks_left) v = *(const v4i*)(tb.b_q + kt * kRowBytes + src.b_code[j]);
     *(v4i MXFP4_LDS*)(stage + C::A_BYTES + slot * 16) = v;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
-    const int slot = (j * 4 + w) * 64 + lane;
-    const uint8_t* sp = (src.is_b[j] ? b_s : args.a_s) + src.scale[j] + kt * 8;
+    const int slot = (j * C::NWAVES + w) * 64 + lane;
+    const uint8_t* sp = (scale_is_b<C>(j, w) ? tb.b_s : tb.a_s) + kt * 8 + src.scale[j];
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -274,7 +321,7 @@ __device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXF
   const bool vec_ok = ((n * ESIZE) & 15) == 0;
   uint8_t* cbase = (uint8_t*)args.c + ((int64_t)(ar.lo + row_begin) * n + n0) * ESIZE;
   const int64_t row_bytes = (int64_t)n * ESIZE;
-  for (int idx = threadIdx.x; idx < valid_rows * CPR; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < valid_rows * CPR; idx += C::THREADS) {
     const int r = idx / CPR, cc = idx % CPR;
     const int col = cc * (16 / ESIZE);
     if (col >= valid_cols) continue;
@@ -341,18 +388,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs& args, const v16f (&ac
   }
 }
 
-// Scheduling pattern for one region holding a k-step's MFMAs and the next
-// k-step's fragment reads: (1 LDS read, 1 MFMA) for every read, then the rest
-// of the MFMAs; sched_barrier(0) closes the region.
-template <class C>
-__device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int READS = C::MI + C::NI, MFMAS = C::MI * C::NI;
-#pragma unroll
-  for (int i = 0; i < READS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+// Scheduling pattern for one k-step's MFMAs: READS fragment reads for the next
+// k-step go out one per MFMA over the first MFMAs, and COPIES global -> LDS
+// copies are spread evenly over all of them.  A burst of reads or copies would
+// stall the wave at issue (full LDS or vector-memory queue) while its MFMAs
+// wait behind it; spread out, they drain while the MFMAs run.
+// sched_barrier(0) closes the region.
+template <int READS, int COPIES, int MFMAS, int I>
+__device__ __forceinline__ void kstep_slots() {
+  if constexpr (I < MFMAS) {
+    if constexpr (I < READS) __builtin_amdgcn_sched_group_barrier(0x100, I + 1 < MFMAS ? 1 : READS - I, 0);
+    constexpr int copies = COPIES * (I + 1) / MFMAS - COPIES * I / MFMAS;
+    if constexpr (copies > 0) __builtin_amdgcn_sched_group_barrier(0x020, copies, 0);   // VMEM copies
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // MFMA
+    kstep_slots<READS, COPIES, MFMAS, I + 1>();
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+}
+
+template <class C, int COPIES>
+__device__ __forceinline__ void kstep_pattern() {
+  kstep_slots<C::MI + C::NI, COPIES, C::MI * C::NI, 0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -360,54 +415,58 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 // parameter, so the compiler cannot sink the MFMAs past the barrier).
 // On entry fa holds k-step 0 of stage kt and sc its scales; on exit, if NEXT,
 // fa/sc hold k-step 0 of stage kt+1.  COPY_CODES / COPY_SCALES issue the copies
-// of stage kt+2 (and of its scale group) once stage kt's buffer is released.
+// of stage kt+2 (and of its scale group) once stage kt's buffer is released,
+// spread over the MFMAs of the last k-step.
 template <class C, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
 __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
-                                                Scales<C>& sc, const Sources<C>& src, const GemmArgs& args,
-                                                const uint8_t* b_q, const uint8_t* b_s, uint8_t MXFP4_LDS* lds,
-                                                int kt, int wm0, int wn0, int lane) {
+                                                Scales<C>& sc, const Sources<C>& src, const TileBases& tb,
+                                                uint8_t MXFP4_LDS* lds, int kt, int wm0, int wn0, int lane) {
   uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
   uint8_t MXFP4_LDS* nxt = lds + ((kt + 1) & 1) * C::CODE_STAGE;
   // Fragment reads run one k-step ahead of the MFMAs.  Before a new batch of
   // reads is issued, the previous batch (issued a whole k-step earlier, so
   // already landed) is retired with lgkmcnt(0): the LDS counter holds at most
-  // 15 operations, and with two 8-read batches pending the compiler could
-  // only wait for both, stalling on the batch just issued.
-  // Within a k-step the next k-step's reads are interleaved one per MFMA over
-  // the first MFMAs, so no wave stalls issuing a burst of reads into a full LDS
-  // queue while its MFMAs wait behind them.
+  // 15 operations, and with two batches pending the compiler could only wait
+  // for both, stalling on the batch just issued.
   read_frags<C, 1>(cur, fb, wm0, wn0, lane);
   mma_kstep<C, 0, 0, C::MI>(fa, sc, acc);
-  interleave_reads_mfma<C>();
+  kstep_pattern<C, 0>();
   MXFP4_WAIT_LGKM0();
   read_frags<C, 2>(cur, fa, wm0, wn0, lane);
   mma_kstep<C, 1, 0, C::MI>(fb, sc, acc);
-  interleave_reads_mfma<C>();
+  kstep_pattern<C, 0>();
   MXFP4_WAIT_LGKM0();
   read_frags<C, 3>(cur, fb, wm0, wn0, lane);
   mma_kstep<C, 2, 0, C::MI>(fa, sc, acc);
-  interleave_reads_mfma<C>();
-  const Scales<C> sc_cur = sc;
-  __builtin_amdgcn_sched_barrier(0);
+  kstep_pattern<C, 0>();
   if (NEXT) {
     // stage kt+1 and its scales have landed; stage kt is fully read once every
     // wave has passed the barrier
     MXFP4_WAIT_VMCNT(0);
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
+    read_frags<C, 0>(nxt, fa, wm0, wn0, lane);
     if (COPY_SCALES)
-      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, args.a_s, b_s,
-                     (kt + 2) >> 1);
-    if (COPY_CODES) copy_codes<C>(cur, src, args.a_q, b_q, kt + 2);
+      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, tb, (kt + 2) >> 1);
+    if (COPY_CODES) {
+      copy_codes_a<C>(cur, src, tb, kt + 2);
+      copy_codes_b<C>(cur, src, tb, kt + 2);
+    }
+    mma_kstep<C, 3, 0, C::MI>(fb, sc, acc);
+    // the next stage's first fragments go out before the copies (measured ~2 %
+    // faster than interleaving them one per MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NI, 0);
+    kstep_slots<0, (COPY_CODES ? C::CODE_LOADS : 0) + (COPY_SCALES ? C::S_LOADS : 0), C::MI * C::NI, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // the next stage's scale words replace this stage's once its last MFMAs are issued
     read_scales_raw<C>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
                        wm0, wn0, lane);
-    read_frags<C, 0>(nxt, fa, wm0, wn0, lane);
+    shift_scales<C>(sc, lane);
   } else {
     MXFP4_WAIT_LGKM0();
+    mma_kstep<C, 3, 0, C::MI>(fb, sc, acc);
   }
-  mma_kstep<C, 3, 0, C::MI>(fb, sc_cur, acc);
   __builtin_amdgcn_sched_barrier(0);
-  if (NEXT) shift_scales<C>(sc, lane);
 }
 
 // Main loop + epilogue for one output tile.
@@ -415,7 +474,7 @@ template <class C, bool COPY>
 __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                          const RowRange& ar, int n0, uint8_t MXFP4_LDS* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm0 = (w & 1) * C::WM, wn0 = (w >> 1) * C::WN;
+  const int wm0 = (w % C::WGM) * C::WM, wn0 = (w / C::WGM) * C::WN;
   v16f acc[C::MI][C::NI];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -426,13 +485,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
 
   Sources<C> src;
   make_sources<C>(src, ar, n0, args.n, args.k);
+  const TileBases tb = tile_bases(args, b_q, b_s, ar, n0);
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
   if (COPY) {
     const int nk = args.k / kBK;    // even, >= 2: k % 512 == 0
-    copy_scales<C>(group0, src, args.a_s, b_s, 0);
-    copy_codes<C>(lds, src, args.a_q, b_q, 0);
-    copy_codes<C>(lds + C::CODE_STAGE, src, args.a_q, b_q, 1);
+    copy_scales<C>(group0, src, tb, 0);
+    copy_codes_a<C>(lds, src, tb, 0);
+    copy_codes_b<C>(lds, src, tb, 0);
+    copy_codes_a<C>(lds + C::CODE_STAGE, src, tb, 1);
+    copy_codes_b<C>(lds + C::CODE_STAGE, src, tb, 1);
     MXFP4_WAIT_VMCNT(C::CODE_LOADS);            // scales and stage 0 have landed
     barrier_lds();
     Scales<C> sc;
@@ -442,15 +504,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
     shift_scales<C>(sc, lane);
     int kt = 0;
     for (; kt + 2 < nk; kt += 2) {
-      pipelined_stage<C, true, true, true>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt, wm0, wn0, lane);
-      pipelined_stage<C, true, true, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt + 1, wm0, wn0, lane);
+      pipelined_stage<C, true, true, true>(acc, fa, fb, sc, src, tb, lds, kt, wm0, wn0, lane);
+      pipelined_stage<C, true, true, false>(acc, fa, fb, sc, src, tb, lds, kt + 1, wm0, wn0, lane);
     }
-    pipelined_stage<C, true, false, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt, wm0, wn0, lane);
-    pipelined_stage<C, false, false, false>(acc, fa, fb, sc, src, args, b_q, b_s, lds, kt + 1, wm0, wn0, lane);
+    pipelined_stage<C, true, false, false>(acc, fa, fb, sc, src, tb, lds, kt, wm0, wn0, lane);
+    pipelined_stage<C, false, false, false>(acc, fa, fb, sc, src, tb, lds, kt + 1, wm0, wn0, lane);
   } else {
     const int nk = (args.k + kBK - 1) / kBK;
     for (int kt = 0; kt < nk; ++kt) {
-      load_stage_generic<C>(lds, group0, src, args, b_q, b_s, kt);
+      load_stage_generic<C>(lds, group0, src, tb, args.k, kt);
       __syncthreads();
       Scales<C> sc;
       Frags<C> f;
@@ -473,7 +535,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
 }
 
 template <class C, bool COPY>
-__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(C::THREADS) void gemm_tile_kernel(GemmArgs args, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
@@ -525,7 +587,7 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, i
 }
 
 template <class C, bool COPY>
-__global__ __launch_bounds__(kThreads) void grouped_tile_kernel(GemmArgs args, int mt_bound, int tiles_n) {
+__global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args, int mt_bound, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int total = mt_bound * tiles_n;
   int t = blockIdx.x;
@@ -540,8 +602,8 @@ __global__ __launch_bounds__(kThreads) void grouped_tile_kernel(GemmArgs args, i
   run_tile<C, COPY>(args, b_q, b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
-using Cfg256 = TileCfg<256, 256>;
-using Cfg128 = TileCfg<128, 128>;
+using Cfg256 = TileCfg<256, 256, 2, 4>;
+using Cfg128 = TileCfg<128, 128, 2, 2>;
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel.
 template <class K>
@@ -564,11 +626,11 @@ hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_tile_kernel<C, true>), grid, dim3(kThreads), lds, stream, args, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, true>), grid, dim3(C::THREADS), lds, stream, args, tiles_m, tiles_n);
   } else {
     hipError_t e = allow_lds(gemm_tile_kernel<C, false>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_tile_kernel<C, false>), grid, dim3(kThreads), lds, stream, args, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, false>), grid, dim3(C::THREADS), lds, stream, args, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
@@ -582,11 +644,11 @@ hipError_t launch_grouped(const GemmArgs& args, hipStream_t stream) {
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(grouped_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_tile_kernel<C, true>), grid, dim3(kThreads), lds, stream, args, mt_bound, tiles_n);
+    hipLaunchKernelGGL((grouped_tile_kernel<C, true>), grid, dim3(C::THREADS), lds, stream, args, mt_bound, tiles_n);
   } else {
     hipError_t e = allow_lds(grouped_tile_kernel<C, false>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_tile_kernel<C, false>), grid, dim3(kThreads), lds, stream, args, mt_bound, tiles_n);
+    hipLaunchKernelGGL((grouped_tile_kernel<C, false>), grid, dim3(C::THREADS), lds, stream, args, mt_bound, tiles_n);
   }
   return hipGetLastError();
 }
