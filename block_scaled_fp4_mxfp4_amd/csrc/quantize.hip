@@ -38,7 +38,8 @@ namespace mxfp4 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kQuantUnroll = 4;   // blocks in flight per lane group
+constexpr int kQuantUnroll = 2;   // blocks in flight per lane group per iteration (with the grid cap, large
+                                   // operands take several iterations, so stores overlap the next loads)
 
 __device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
   // independent max of the low and high 16-bit halves
