@@ -112,3 +112,33 @@ def test_grouped_moe_workload_full_size_sampled():
         got = got_all[np.ix_(rows, cols)]
         assert oracle.floored_max_rel(oracle.bf16_bits_to_f64(got), ref) <= 1e-2, f"expert {g}"
         assert_bf16_matches_rounded(got, ref)
+
+
+def test_grouped_malformed_offsets_stay_in_bounds():
+    """Offsets are only clamped on the device (the host cannot read them without a
+    sync): negative, decreasing and past-the-end offsets must neither write
+    outside C nor disturb rows that exactly one clamped group covers."""
+    dev = device()
+    total, n, k, groups = 300, 96, 512, 4
+    # clamped groups: g0 = [0, 120), g1 empty, g2 = [80, 300) (overlaps g0), g3 empty
+    offsets = np.array([-5, 120, 80, 500, 300], np.int32)
+    a = random_bf16((total, k), 31)
+    w = random_bf16((groups * n, k), 32)
+    aq, as_ = oracle.quantize(workloads.bf16_bits(a))
+    wq, ws = oracle.quantize(workloads.bf16_bits(w))
+    d_aq, d_as = upload(aq, dev), upload(as_, dev)
+    d_wq, d_ws = upload(wq.reshape(groups, n, k // 2), dev), upload(ws.reshape(groups, n, k // 32), dev)
+    c_all = poisoned((total + 3, n), torch.float32, dev, 0xFF)
+    c = c_all[:total]
+    mxfp4_grouped_gemm_nt(d_aq, d_as, d_wq, d_ws, upload(offsets, dev), c=c)
+    torch.cuda.synchronize()
+    assert torch.all(c_all[total:].view(torch.uint8) == 0xFF), "write past the end of C"
+    got = to_np(c)
+    tile = _tile_for(total, groups)
+    g0 = to_np(mxfp4_gemm_nt(d_aq[0:120], d_as[0:120], d_wq[0], d_ws[0], out_dtype=torch.float32, kernel=tile))
+    g2 = to_np(mxfp4_gemm_nt(d_aq[80:300], d_as[80:300], d_wq[2], d_ws[2], out_dtype=torch.float32, kernel=tile))
+    torch.cuda.synchronize()
+    assert np.array_equal(got[0:80], g0[0:80])
+    assert np.array_equal(got[120:300], g2[40:220])
+    overlap = got[80:120]
+    assert np.all((overlap == g0[80:120]) | (overlap == g2[0:40])), "overlapping rows hold neither group's result"
