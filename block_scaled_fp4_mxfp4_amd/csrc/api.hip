@@ -54,11 +54,14 @@ mxfp4_status_t current_device(DeviceInfo& out) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxDim = (int64_t)1 << 30;   // keeps every internal index in int32 range
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // m, n: keeps row and tile indices in int32 range
+// k: the tile kernels address a tile's operand rows with 32-bit byte offsets
+// from the tile's first row, (row in tile) * k/2 with up to 256 rows.
+constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 mxfp4_status_t check_k(int64_t k) {
   if (k <= 0 || k % 32 != 0) return fail(MXFP4_ERR_INVALID_ARG, "k must be a positive multiple of 32 (got %lld)", (long long)k);
-  if (k > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "k too large (%lld)", (long long)k);
+  if (k > kMaxK) return fail(MXFP4_ERR_INVALID_ARG, "k too large (%lld > %lld)", (long long)k, (long long)kMaxK);
   return MXFP4_OK;
 }
 
@@ -188,7 +191,7 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void*
 }
 
 size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits) {
-  if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxK) return 0;
   // without the pointers the alignment is unknown: size for the non-streaming choice
   Choice c;
   if (resolve(m, n, k, kernel, splits, query_num_cus(), kernel == MXFP4_KERNEL_STREAM && k % 512 == 0, c) != MXFP4_OK)

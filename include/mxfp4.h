@@ -28,6 +28,8 @@
  *     otherwise any; the quantizer's scale output any; offsets 4 bytes.  A row
  *     slice of a row-major operand therefore stays valid.
  *   - A zero-sized problem (rows, m, n or total_m equal to 0) is a valid no-op.
+ *     Limits: m, n, total_m <= 2^30; k <= 2^24 (the tile kernels address a
+ *     tile's rows with 32-bit offsets); quantizer rows * k <= 2^40.
  *   - No call aborts or throws; mxfp4_last_error() gives a thread-local text
  *     describing the last non-OK status.
  *   - Calls are reentrant; the only global state is a per-device cache of
@@ -85,7 +87,7 @@ const char* mxfp4_last_error(void);
  *   x_bf16 : bfloat16 [rows, k], row-major (read only)
  *   q      : uint8 [rows, k/2]   (written)
  *   scales : uint8 [rows, k/32]  (written)
- *   k      : > 0 and a multiple of 32
+ *   k      : > 0, a multiple of 32, at most 2^24
  * NaN or Inf inputs give unspecified codes (the format has no encoding for
  * them); every finite input is encoded exactly as above.
  */
@@ -106,7 +108,7 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k,
  *   a_q, a_s : A operand, [m, k/2] and [m, k/32]
  *   b_q, b_s : B operand, [n, k/2] and [n, k/32]
  *   c        : [m, n] row-major, element type `c_type`
- *   k        : > 0 and a multiple of 32
+ *   k        : > 0, a multiple of 32, at most 2^24
  *   workspace: device scratch of at least mxfp4_gemm_nt_workspace_size(m, n, k)
  *              bytes (may be NULL when that size is 0).  A workspace must be
  *              zero-filled before its first use.  Its first 64 KiB hold
@@ -144,6 +146,7 @@ mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s,
  *               result is then unspecified.  A group with no rows writes
  *               nothing.
  *   c         : [total_m, n], element type `c_type`
+ *   k         : > 0, a multiple of 32, at most 2^24
  *   num_groups: 1 .. 1024
  *   workspace : at least mxfp4_grouped_gemm_nt_workspace_size(...) bytes.
  * One kernel launch; nothing depends on host knowledge of the group sizes.

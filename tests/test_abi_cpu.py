@@ -81,6 +81,12 @@ def test_gemm_rejects_bad_arguments_on_host(lib):
     assert call(a_s=_fake(0x1002)) == 1
     assert b"a_s is not 4-byte aligned" in lib.mxfp4_last_error()
     assert call(a_q=_fake(0x1008)) == 1
+    # size limits: k at most 2^24, m and n at most 2^30
+    assert call(k=(1 << 24) + 32) == 1
+    assert b"k too large" in lib.mxfp4_last_error()
+    assert call(m=(1 << 30) + 1) == 1
+    assert call(n=(1 << 30) + 1) == 1
+    assert lib.mxfp4_gemm_nt_workspace_size(64, 64, (1 << 24) + 32) == 0
     # empty problems are no-ops that launch nothing
     assert call(m=0, a_q=None, a_s=None, c=None) == 0
     assert call(n=0, b_q=None, b_s=None, c=None) == 0

@@ -126,6 +126,26 @@ def test_stream_kernel_rejects_unsupported_k():
         mxfp4_gemm_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), kernel="stream")
 
 
+@pytest.mark.parametrize("kernel", ["tile256", "tile128", "stream", "splitk"])
+def test_gemm_long_k(kernel):
+    """A long reduction (k = 2^19): row offsets inside a tile reach 255 * k/2
+    bytes.  Codes of magnitude <= 1 with unit scales keep every partial sum a
+    multiple of 1/4 below 2^19, exact in fp32, so the result is bit-exact
+    whatever the summation order, and any misaddressed row or block shows."""
+    dev = device()
+    m, n, k = 3, 70, 1 << 19
+    log(f"long k {kernel} {m}x{n}x{k}")
+    g = np.random.default_rng(7)
+    small = np.array([0, 1, 2, 8, 9, 10], np.uint8)          # 0, +-0.5, +-1
+    aq = (small[g.integers(0, 6, (m, k // 2))] | (small[g.integers(0, 6, (m, k // 2))] << 4)).astype(np.uint8)
+    bq = (small[g.integers(0, 6, (n, k // 2))] | (small[g.integers(0, 6, (n, k // 2))] << 4)).astype(np.uint8)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    ref = oracle.gemm_nt(aq, as_, bq, bs)
+    got = _gemm(aq, as_, bq, bs, dev, kernel, 0, torch.float32, m, n)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
 def test_splitk_workspace_reuse_across_calls():
     """The arrival counters return to zero, so one workspace serves consecutive
     calls of different shapes (the partial sums of a small-N call must not land
