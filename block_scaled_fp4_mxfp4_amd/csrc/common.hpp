@@ -47,6 +47,22 @@ __device__ __forceinline__ void g2lds_4(const void* gptr, MXFP4_LDS void* lds_ba
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 4, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3:
+// 32-bit data format, no swizzle, no stride).  Loads at offsets past `bytes`
+// return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes at voffset + soffset in the
+// buffer land at lds_base + 16 * i.  The buffer base and soffset stay in scalar
+// registers, so each copy needs one 32-bit vector register and no address
+// arithmetic.  lds_base must be wave-uniform.
+__device__ __forceinline__ void buf2lds_16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                           MXFP4_LDS void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voffset, soffset, 0, 0);
+}
+
 // One 32x32x64 block-scaled FP4 MFMA step: D += (A scaled) x (B scaled)^T.
 // Lane l supplies row (l % 32), K-block (l / 32): 16 bytes of codes and the
 // E8M0 byte selected by OPSEL out of its 32-bit scale register.

@@ -336,7 +336,9 @@ hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
     counters = (int*)workspace;
     partials = (float*)((char*)workspace + kSplitkCounterBytes);
   }
-  const dim3 grid((unsigned)(tiles_n * splits));
+  const int64_t blocks = (int64_t)tiles_n * splits;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   const int mb = mblocks_for(args.m);
 #define MXFP4_LAUNCH(MB_, NI_)                                                                               \
   hipLaunchKernelGGL((gemm_splitk_kernel<MB_, NI_>), grid, dim3(kThreads), 0, stream, args, tiles_n, splits, \

@@ -255,7 +255,9 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int tiles_n = (args.n + kBN - 1) / kBN;
   const int tiles_m = (args.m + C::BM - 1) / C::BM;
-  hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(kThreads), C::LDS, stream, args, tiles_n);
+  const int64_t blocks = (int64_t)tiles_m * tiles_n;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), C::LDS, stream, args, tiles_n);
   return hipGetLastError();
 }
 

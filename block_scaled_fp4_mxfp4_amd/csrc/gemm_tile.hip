@@ -17,9 +17,14 @@
 //    result lands transposed: lane l holds output row (l % 32) and four runs of
 //    four consecutive output columns.
 //  * A stage covers 256 K elements = 128 code bytes per row, so each
-//    global_load_lds_dwordx4 (64 lanes x 16 bytes, straight into LDS) moves 8
-//    whole 128-byte rows; 64-byte row pieces measured about half the per-CU
-//    copy rate.  Two code stages are in flight (2 x 64 KiB for 256x256).
+//    buffer_load_dwordx4 ... lds (64 lanes x 16 bytes, straight into LDS)
+//    moves 8 whole 128-byte rows; 64-byte row pieces measured about half the
+//    per-CU copy rate.  Two code stages are in flight (2 x 64 KiB for 256x256).
+//    The copies go through buffer resources over the tile's operand rows: the
+//    base and the stage offset live in scalar registers and each copy needs
+//    one 32-bit vector register, which keeps the 8-wave main loop free of
+//    spills (64-bit global addresses measured 3-5 % slower and spilled once the
+//    loop was specialized below).
 //  * Scale bytes travel separately: one 16-byte piece per row covers two
 //    stages (512 K), so the scale copy costs an eighth of the code copy's
 //    requests instead of one 4-byte request per row per stage.  Two scale
@@ -39,12 +44,15 @@
 //    of its in-order instruction stream (a fragment wait, a copy or read
 //    stuck at issue, a barrier) idled that SIMD's matrix unit, and counters
 //    showed waves waiting on instruction issue about half of the time; a
-//    second wave fills those gaps.  Copy sources are 32-bit offsets from
-//    workgroup-uniform tile bases so the register budget holds without
-//    spills in the main loop.
+//    second wave fills those gaps.  Wave w runs on SIMD w % 4 and the two
+//    waves of a SIMD sit in different wave rows.
+//  * Row blocks past the tile's last stored row (an expert's last rows, a
+//    ragged M) are skipped: each wave runs a main loop specialized for its
+//    number of 32-row MFMA blocks that hold stored rows.
 //  * Copies of the next stage are issued spread over the MFMAs of the last
 //    k-step rather than in one burst.
-//  * Workgroup -> tile mapping is XCD-aware (see tile_coords in common.hpp).
+//  * Workgroup -> tile mapping is XCD-aware (see tile_coords in common.hpp);
+//    the grouped kernel splits its real tiles evenly over the XCDs.
 //
 // Ragged edges: rows past M (or N) read a clamped, valid row and are never
 // stored.  The copy path needs k % 512 == 0 and 16-byte aligned scale arrays;
@@ -108,6 +116,20 @@ __device__ __forceinline__ TileBases tile_bases(const GemmArgs& args, const uint
   return {args.a_q + ar.lo * kb, b_q + n0 * kb, args.a_s + ar.lo * ks, b_s + n0 * ks};
 }
 
+// Buffer resources over the same tile operands, sized to the rows the tile
+// reads (at most 256 rows, so at most 2^31 code bytes for k <= 2^24).
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t a_q, b_q, a_s, b_s;
+};
+
+template <class C>
+__device__ __forceinline__ TileRsrc tile_rsrc(const TileBases& tb, const RowRange& ar, int n0, int n, int k) {
+  const uint32_t kb = k / 2, ks = k / 32;
+  const uint32_t a_rows = ar.last - ar.lo + 1, b_rows = min(C::BN, n - n0);
+  return {make_rsrc(tb.a_q, a_rows * kb), make_rsrc(tb.b_q, b_rows * kb), make_rsrc(tb.a_s, a_rows * ks),
+          make_rsrc(tb.b_s, b_rows * ks)};
+}
+
 // Per-thread byte offsets of the copies from the tile bases, at stage 0 / scale
 // group 0.  Copy j of a stage moves slot (j*NWAVES + wave)*64 + lane: row slot/8,
 // logical 16-byte chunk (slot%8) ^ swz(row).  Rows past the operand's end read
@@ -153,34 +175,33 @@ __device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar
 // Code copies of stage kt into `stage` (direct global -> LDS), A rows and B
 // rows separately: the pipeline issues them in different k-steps.
 template <class C>
-__device__ __forceinline__ void copy_codes_a(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileBases& tb,
+__device__ __forceinline__ void copy_codes_a(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileRsrc& tr,
                                              int kt) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS base goes to M0
-  const uint8_t* a = tb.a_q + kt * kRowBytes;
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j)
-    g2lds_16(a + src.a_code[j], (MXFP4_LDS void*)(stage + (j * C::NWAVES + w) * 64 * 16));
+    buf2lds_16(tr.a_q, src.a_code[j], kt * kRowBytes, (MXFP4_LDS void*)(stage + (j * C::NWAVES + w) * 64 * 16));
 }
 
 template <class C>
-__device__ __forceinline__ void copy_codes_b(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileBases& tb,
+__device__ __forceinline__ void copy_codes_b(uint8_t MXFP4_LDS* stage, const Sources<C>& src, const TileRsrc& tr,
                                              int kt) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint8_t* b = tb.b_q + kt * kRowBytes;
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j)
-    g2lds_16(b + src.b_code[j], (MXFP4_LDS void*)(stage + C::A_BYTES + (j * C::NWAVES + w) * 64 * 16));
+    buf2lds_16(tr.b_q, src.b_code[j], kt * kRowBytes,
+               (MXFP4_LDS void*)(stage + C::A_BYTES + (j * C::NWAVES + w) * 64 * 16));
 }
 
 // Scale copies of group g (stages 2g and 2g+1): 16 bytes of every row.
 template <class C>
-__device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const TileBases& tb,
+__device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const TileRsrc& tr,
                                             int g) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j)
-    g2lds_16((scale_is_b<C>(j, w) ? tb.b_s : tb.a_s) + g * 16 + src.scale[j],
-             (MXFP4_LDS void*)(group + (j * C::NWAVES + w) * 64 * 16));
+    buf2lds_16(scale_is_b<C>(j, w) ? tr.b_s : tr.a_s, src.scale[j], g * 16,
+               (MXFP4_LDS void*)(group + (j * C::NWAVES + w) * 64 * 16));
 }
 
 // Stage kt through registers for any k % 32 == 0: 32-blocks at or past k get
@@ -239,44 +260,53 @@ struct Scales {
   v2i b[C::NI];
 };
 
-template <class C>
+// MA is the number of the wave's 32-row MFMA blocks that are computed (see
+// run_tile); the others need no operands.
+template <class C, int MA = C::MI>
 __device__ __forceinline__ void read_scales_raw(const uint8_t MXFP4_LDS* group, int parity, Scales<C>& sc,
                                                 int wm0, int wn0, int lane) {
-  const uint8_t MXFP4_LDS* base = group + 8 * parity;
+  if constexpr (MA > 0) {
+    const uint8_t MXFP4_LDS* base = group + 8 * parity;
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) sc.a[i] = *(const v2i MXFP4_LDS*)(base + (wm0 + 32 * i + (lane & 31)) * 16);
+    for (int i = 0; i < MA; ++i) sc.a[i] = *(const v2i MXFP4_LDS*)(base + (wm0 + 32 * i + (lane & 31)) * 16);
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) sc.b[j] = *(const v2i MXFP4_LDS*)(base + (C::BM + wn0 + 32 * j + (lane & 31)) * 16);
+    for (int j = 0; j < C::NI; ++j)
+      sc.b[j] = *(const v2i MXFP4_LDS*)(base + (C::BM + wn0 + 32 * j + (lane & 31)) * 16);
+  }
 }
 
-template <class C>
+template <class C, int MA = C::MI>
 __device__ __forceinline__ void shift_scales(Scales<C>& sc, int lane) {
-  const int shift = 8 * (lane >> 5);
+  if constexpr (MA > 0) {
+    const int shift = 8 * (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    sc.a[i].x = (int)((uint32_t)sc.a[i].x >> shift);
-    sc.a[i].y = (int)((uint32_t)sc.a[i].y >> shift);
-  }
+    for (int i = 0; i < MA; ++i) {
+      sc.a[i].x = (int)((uint32_t)sc.a[i].x >> shift);
+      sc.a[i].y = (int)((uint32_t)sc.a[i].y >> shift);
+    }
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-    sc.b[j].x = (int)((uint32_t)sc.b[j].x >> shift);
-    sc.b[j].y = (int)((uint32_t)sc.b[j].y >> shift);
+    for (int j = 0; j < C::NI; ++j) {
+      sc.b[j].x = (int)((uint32_t)sc.b[j].x >> shift);
+      sc.b[j].y = (int)((uint32_t)sc.b[j].y >> shift);
+    }
   }
 }
 
-template <class C, int S>
+template <class C, int S, int MA = C::MI>
 __device__ __forceinline__ void read_frags(const uint8_t MXFP4_LDS* stage, Frags<C>& f, int wm0, int wn0,
                                            int lane) {
-  const int c = 2 * S + (lane >> 5);
+  if constexpr (MA > 0) {
+    const int c = 2 * S + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    const int r = wm0 + 32 * i + (lane & 31);
-    f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
-  }
+    for (int i = 0; i < MA; ++i) {
+      const int r = wm0 + 32 * i + (lane & 31);
+      f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    }
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-    const int r = wn0 + 32 * j + (lane & 31);
-    f.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
+    for (int j = 0; j < C::NI; ++j) {
+      const int r = wn0 + 32 * j + (lane & 31);
+      f.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
+    }
   }
 }
 
@@ -407,9 +437,9 @@ __device__ __forceinline__ void kstep_slots() {
   }
 }
 
-template <class C, int COPIES>
+template <class C, int COPIES, int MA = C::MI>
 __device__ __forceinline__ void kstep_pattern() {
-  kstep_slots<C::MI + C::NI, COPIES, C::MI * C::NI, 0>();
+  kstep_slots<(MA > 0 ? MA + C::NI : 0), COPIES, MA * C::NI, 0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -419,9 +449,9 @@ __device__ __forceinline__ void kstep_pattern() {
 // fa/sc hold k-step 0 of stage kt+1.  COPY_CODES / COPY_SCALES issue the copies
 // of stage kt+2 (and of its scale group) once stage kt's buffer is released,
 // spread over the MFMAs of the last k-step.
-template <class C, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
+template <class C, int MA, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
 __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
-                                                Scales<C>& sc, const Sources<C>& src, const TileBases& tb,
+                                                Scales<C>& sc, const Sources<C>& src, const TileRsrc& tr,
                                                 uint8_t MXFP4_LDS* lds, int kt, int wm0, int wn0, int lane) {
   uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
   uint8_t MXFP4_LDS* nxt = lds + ((kt + 1) & 1) * C::CODE_STAGE;
@@ -430,45 +460,87 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
   // already landed) is retired with lgkmcnt(0): the LDS counter holds at most
   // 15 operations, and with two batches pending the compiler could only wait
   // for both, stalling on the batch just issued.
-  read_frags<C, 1>(cur, fb, wm0, wn0, lane);
-  mma_kstep<C, 0, 0, C::MI>(fa, sc, acc);
-  kstep_pattern<C, 0>();
+  read_frags<C, 1, MA>(cur, fb, wm0, wn0, lane);
+  mma_kstep<C, 0, 0, MA>(fa, sc, acc);
+  kstep_pattern<C, 0, MA>();
   MXFP4_WAIT_LGKM0();
-  read_frags<C, 2>(cur, fa, wm0, wn0, lane);
-  mma_kstep<C, 1, 0, C::MI>(fb, sc, acc);
-  kstep_pattern<C, 0>();
+  read_frags<C, 2, MA>(cur, fa, wm0, wn0, lane);
+  mma_kstep<C, 1, 0, MA>(fb, sc, acc);
+  kstep_pattern<C, 0, MA>();
   MXFP4_WAIT_LGKM0();
-  read_frags<C, 3>(cur, fb, wm0, wn0, lane);
-  mma_kstep<C, 2, 0, C::MI>(fa, sc, acc);
-  kstep_pattern<C, 0>();
+  read_frags<C, 3, MA>(cur, fb, wm0, wn0, lane);
+  mma_kstep<C, 2, 0, MA>(fa, sc, acc);
+  kstep_pattern<C, 0, MA>();
   if (NEXT) {
     // stage kt+1 and its scales have landed; stage kt is fully read once every
     // wave has passed the barrier
     MXFP4_WAIT_VMCNT(0);
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags<C, 0>(nxt, fa, wm0, wn0, lane);
+    read_frags<C, 0, MA>(nxt, fa, wm0, wn0, lane);
     if (COPY_SCALES)
-      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, tb, (kt + 2) >> 1);
+      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, tr, (kt + 2) >> 1);
     if (COPY_CODES) {
-      copy_codes_a<C>(cur, src, tb, kt + 2);
-      copy_codes_b<C>(cur, src, tb, kt + 2);
+      copy_codes_a<C>(cur, src, tr, kt + 2);
+      copy_codes_b<C>(cur, src, tr, kt + 2);
     }
-    mma_kstep<C, 3, 0, C::MI>(fb, sc, acc);
+    mma_kstep<C, 3, 0, MA>(fb, sc, acc);
     // the next stage's first fragments go out before the copies (measured ~2 %
     // faster than interleaving them one per MFMA)
-    __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NI, 0);
-    kstep_slots<0, (COPY_CODES ? C::CODE_LOADS : 0) + (COPY_SCALES ? C::S_LOADS : 0), C::MI * C::NI, 0>();
+    if constexpr (MA > 0) __builtin_amdgcn_sched_group_barrier(0x100, MA + C::NI, 0);
+    kstep_slots<0, (COPY_CODES ? C::CODE_LOADS : 0) + (COPY_SCALES ? C::S_LOADS : 0), MA * C::NI, 0>();
     __builtin_amdgcn_sched_barrier(0);
     // the next stage's scale words replace this stage's once its last MFMAs are issued
-    read_scales_raw<C>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
-                       wm0, wn0, lane);
-    shift_scales<C>(sc, lane);
+    read_scales_raw<C, MA>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
+                           wm0, wn0, lane);
+    shift_scales<C, MA>(sc, lane);
   } else {
     MXFP4_WAIT_LGKM0();
-    mma_kstep<C, 3, 0, C::MI>(fb, sc, acc);
+    mma_kstep<C, 3, 0, MA>(fb, sc, acc);
   }
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Main loop of the copy path with MA computed row blocks per wave.
+// nk = k / 256 is even and >= 2 (k % 512 == 0).
+template <class C, int MA>
+__device__ __forceinline__ void copy_loop(v16f (&acc)[C::MI][C::NI], const Sources<C>& src, const TileRsrc& tr,
+                                          uint8_t MXFP4_LDS* lds, int nk, int wm0, int wn0, int lane) {
+  uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
+  copy_scales<C>(group0, src, tr, 0);
+  copy_codes_a<C>(lds, src, tr, 0);
+  copy_codes_b<C>(lds, src, tr, 0);
+  copy_codes_a<C>(lds + C::CODE_STAGE, src, tr, 1);
+  copy_codes_b<C>(lds + C::CODE_STAGE, src, tr, 1);
+  MXFP4_WAIT_VMCNT(C::CODE_LOADS);            // scales and stage 0 have landed
+  barrier_lds();
+  Scales<C> sc;
+  Frags<C> fa, fb;
+  read_scales_raw<C, MA>(group0, 0, sc, wm0, wn0, lane);
+  read_frags<C, 0, MA>(lds, fa, wm0, wn0, lane);
+  shift_scales<C, MA>(sc, lane);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    pipelined_stage<C, MA, true, true, true>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
+    pipelined_stage<C, MA, true, true, false>(acc, fa, fb, sc, src, tr, lds, kt + 1, wm0, wn0, lane);
+  }
+  pipelined_stage<C, MA, true, false, false>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
+  pipelined_stage<C, MA, false, false, false>(acc, fa, fb, sc, src, tr, lds, kt + 1, wm0, wn0, lane);
+}
+
+// copy_loop<C, active> for a wave-uniform active in [0, C::MI].
+template <class C, int MA>
+__device__ __forceinline__ void copy_loop_dispatch(int active, v16f (&acc)[C::MI][C::NI], const Sources<C>& src,
+                                                   const TileRsrc& tr, uint8_t MXFP4_LDS* lds, int nk, int wm0,
+                                                   int wn0, int lane) {
+  if constexpr (MA == 0) {
+    copy_loop<C, 0>(acc, src, tr, lds, nk, wm0, wn0, lane);
+  } else {
+    if (active >= MA)
+      copy_loop<C, MA>(acc, src, tr, lds, nk, wm0, wn0, lane);
+    else
+      copy_loop_dispatch<C, MA - 1>(active, acc, src, tr, lds, nk, wm0, wn0, lane);
+  }
 }
 
 // Main loop + epilogue for one output tile.
@@ -476,7 +548,10 @@ template <class C, bool COPY>
 __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                          const RowRange& ar, int n0, uint8_t MXFP4_LDS* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm0 = (w % C::WGM) * C::WM, wn0 = (w / C::WGM) * C::WN;
+  // Wave w runs on SIMD w % 4.  With 8 waves, the two waves sharing a SIMD sit
+  // in different wave rows, so in a tile whose last rows are padding both
+  // SIMD's waves are not both fully busy (see copy_loop_dispatch).
+  const int wm0 = (w / C::WGN) * C::WM, wn0 = (w % C::WGN) * C::WN;
   v16f acc[C::MI][C::NI];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -491,26 +566,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
   if (COPY) {
-    const int nk = args.k / kBK;    // even, >= 2: k % 512 == 0
-    copy_scales<C>(group0, src, tb, 0);
-    copy_codes_a<C>(lds, src, tb, 0);
-    copy_codes_b<C>(lds, src, tb, 0);
-    copy_codes_a<C>(lds + C::CODE_STAGE, src, tb, 1);
-    copy_codes_b<C>(lds + C::CODE_STAGE, src, tb, 1);
-    MXFP4_WAIT_VMCNT(C::CODE_LOADS);            // scales and stage 0 have landed
-    barrier_lds();
-    Scales<C> sc;
-    Frags<C> fa, fb;
-    read_scales_raw<C>(group0, 0, sc, wm0, wn0, lane);
-    read_frags<C, 0>(lds, fa, wm0, wn0, lane);
-    shift_scales<C>(sc, lane);
-    int kt = 0;
-    for (; kt + 2 < nk; kt += 2) {
-      pipelined_stage<C, true, true, true>(acc, fa, fb, sc, src, tb, lds, kt, wm0, wn0, lane);
-      pipelined_stage<C, true, true, false>(acc, fa, fb, sc, src, tb, lds, kt + 1, wm0, wn0, lane);
-    }
-    pipelined_stage<C, true, false, false>(acc, fa, fb, sc, src, tb, lds, kt, wm0, wn0, lane);
-    pipelined_stage<C, false, false, false>(acc, fa, fb, sc, src, tb, lds, kt + 1, wm0, wn0, lane);
+    // Row blocks of 32 that lie wholly past the tile's last stored row (the
+    // tail of an expert's rows, or of a ragged M) need no MFMAs or operand
+    // reads; their accumulators stay zero and are never stored.  Every wave
+    // still issues all copies and meets every barrier.
+    const int active = __builtin_amdgcn_readfirstlane(min(max((ar.end - ar.lo - wm0 + 31) / 32, 0), C::MI));
+    const TileRsrc tr = tile_rsrc<C>(tb, ar, n0, args.n, args.k);
+    copy_loop_dispatch<C, C::MI>(active, acc, src, tr, lds, args.k / kBK, wm0, wn0, lane);
   } else {
     const int nk = (args.k + kBK - 1) / kBK;
     for (int kt = 0; kt < nk; ++kt) {
@@ -548,6 +610,27 @@ __global__ __launch_bounds__(C::THREADS) void gemm_tile_kernel(GemmArgs args, in
   run_tile<C, COPY>(args, args.b_q, args.b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
+// Clamped rows [lo, hi) of group g: every offset is clamped into [0, total_m]
+// and each end is kept at or after its start, so any offsets give in-range rows.
+__device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int total_m, int& lo, int& hi) {
+  lo = min(max(offsets[g], 0), total_m);
+  hi = min(max(offsets[g + 1], lo), total_m);
+}
+
+// Number of m-tiles over all groups, ceil(rows_g / bm) each (wave-uniform).
+__device__ __forceinline__ int count_mtiles(const int32_t* offsets, int groups, int total_m, int bm) {
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int g = lane; g < groups; g += 64) {
+    int lo, hi;
+    group_rows(offsets, g, total_m, lo, hi);
+    cnt += (hi - lo + bm - 1) / bm;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  return cnt;
+}
+
 // Finds the expert owning global m-tile `mt` (m-tiles are counted expert by
 // expert, ceil(rows_g / BM) per expert).  Every offset is clamped into
 // [0, total_m] and made non-decreasing first, so any offsets give in-range rows.
@@ -559,8 +642,7 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, i
     const int g = base + lane;
     int lo = 0, hi = 0, cnt = 0;
     if (g < groups) {
-      lo = min(max(offsets[g], 0), total_m);
-      hi = min(max(offsets[g + 1], lo), total_m);
+      group_rows(offsets, g, total_m, lo, hi);
       cnt = (hi - lo + bm - 1) / bm;
     }
     int incl = cnt;
@@ -588,12 +670,19 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, i
   return false;
 }
 
+// The grid is a multiple of 8 workgroups covering at least every possible
+// m-tile (the host cannot see the device offsets).  Workgroups are dispatched
+// to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; the real tiles
+// are split evenly over the XCDs as contiguous ranges (consecutive tiles of one
+// expert share that XCD's L2), and the spare workgroups of every XCD exit.
 template <class C, bool COPY>
-__global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args, int mt_bound, int tiles_n) {
+__global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int total = mt_bound * tiles_n;
-  int t = blockIdx.x;
-  if ((total & 7) == 0) t = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int total = count_mtiles(args.offsets, args.groups, args.m, C::BM) * tiles_n;
+  const int share = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * share + slot;
+  if (slot >= share || t >= total) return;
   const int mt = t / tiles_n, tn = t - mt * tiles_n;
   int g;
   RowRange ar;
@@ -624,7 +713,9 @@ hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (args.m + C::BM - 1) / C::BM;
   const int tiles_n = (args.n + C::BN - 1) / C::BN;
   const size_t lds = C::LDS_BYTES;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const int64_t blocks = (int64_t)tiles_m * tiles_n;
+  if (!grid_fits(blocks, C::THREADS)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
@@ -639,18 +730,20 @@ hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
 
 template <class C>
 hipError_t launch_grouped(const GemmArgs& args, hipStream_t stream) {
-  const int mt_bound = (args.m + C::BM - 1) / C::BM + args.groups;
+  const int64_t mt_bound = (args.m + C::BM - 1) / C::BM + args.groups;
   const int tiles_n = (args.n + C::BN - 1) / C::BN;
   const size_t lds = C::LDS_BYTES;
-  const dim3 grid((unsigned)(mt_bound * tiles_n));
+  const int64_t blocks = (mt_bound * tiles_n + 7) / 8 * 8;
+  if (!grid_fits(blocks, C::THREADS)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(grouped_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_tile_kernel<C, true>), grid, dim3(C::THREADS), lds, stream, args, mt_bound, tiles_n);
+    hipLaunchKernelGGL((grouped_tile_kernel<C, true>), grid, dim3(C::THREADS), lds, stream, args, tiles_n);
   } else {
     hipError_t e = allow_lds(grouped_tile_kernel<C, false>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_tile_kernel<C, false>), grid, dim3(C::THREADS), lds, stream, args, mt_bound, tiles_n);
+    hipLaunchKernelGGL((grouped_tile_kernel<C, false>), grid, dim3(C::THREADS), lds, stream, args, tiles_n);
   }
   return hipGetLastError();
 }

@@ -17,6 +17,14 @@ struct GemmArgs {
   int groups;              // grouped only
 };
 
+// One HIP launch holds at most 2^32 - 1 threads.  Grid sizes are computed in
+// 64 bits and checked with this before every launch, so a problem too large
+// for one launch is refused (hipErrorInvalidConfiguration) instead of running
+// a truncated grid.
+inline bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 1 && blocks * threads <= (int64_t)0xFFFFFFFF;
+}
+
 // Tile kernels (TILE256: 256x256 output tiles, TILE128: 128x128 output tiles).
 enum TileKind { kTile256 = 0, kTile128 = 1 };
 

@@ -29,7 +29,10 @@
  *     slice of a row-major operand therefore stays valid.
  *   - A zero-sized problem (rows, m, n or total_m equal to 0) is a valid no-op.
  *     Limits: m, n, total_m <= 2^30; k <= 2^24 (the tile kernels address a
- *     tile's rows with 32-bit offsets); quantizer rows * k <= 2^40.
+ *     tile's rows with 32-bit offsets); quantizer rows * k <= 2^40.  A GEMM
+ *     whose grid would exceed one launch (2^32 - 1 threads; only outputs far
+ *     larger than device memory come near it) returns MXFP4_ERR_HIP and
+ *     launches nothing.
  *   - No call aborts or throws; mxfp4_last_error() gives a thread-local text
  *     describing the last non-OK status.
  *   - Calls are reentrant; the only global state is a per-device cache of
