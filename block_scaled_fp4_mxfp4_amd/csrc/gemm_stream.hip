@@ -24,7 +24,8 @@
 //    every code byte copied into LDS is read by exactly one wave.  At the end
 //    the four fp32 partial tiles are reduce-scattered through LDS, each output
 //    summed in the fixed order wave 0 + wave 1 + wave 2 + wave 3, so results
-//    do not depend on timing.
+//    do not depend on timing.  BF16 results are gathered into a row-major
+//    tile in LDS and leave as whole 128-byte rows in 16-byte stores.
 //  * MFMA operands as in the tile kernels: v_mfma_scale_f32_32x32x64_f8f6f4,
 //    FP4 on both sides, B fed as the first operand so lane l holds output row
 //    l % 32 and runs of four consecutive columns.
@@ -55,7 +56,9 @@ struct StreamCfg {
   static constexpr int CODE_LOADS = ROWS * 8 / kThreads;  // 16-byte copies per thread per stage
   static constexpr int PAIR_LOADS = 2 * CODE_LOADS + 1;   // vector-memory ops per thread per pair
   static constexpr int XCH = 4 * MB * 8 * 64 * 16;        // reduce-scatter exchange: 4 waves x all units
-  static constexpr int LDS = (NP * PAIR > XCH) ? NP * PAIR : XCH;
+  static constexpr int C_PITCH = kBN * 2 + 16;             // bf16 output tile row, padded
+  static constexpr int C_TILE = BM * C_PITCH;              // placed after the exchange area
+  static constexpr int LDS = (NP * PAIR > XCH + C_TILE) ? NP * PAIR : XCH + C_TILE;
   static_assert(ROWS * 8 % kThreads == 0, "code copies must split evenly over the threads");
   static_assert(ROWS <= kThreads, "one scale piece per row");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, in
   // split into U units of 64 lanes x 4 floats (row block i, column block j,
   // column group q); wave w owns units [w*U/4, (w+1)*U/4).  Each wave parks the
   // units it does not own in LDS, then sums each of its units over the waves in
-  // the fixed order 0, 1, 2, 3 and stores it straight from registers.
+  // the fixed order 0, 1, 2, 3.
   constexpr int U = C::MB * 8, UW = U / 4;
   v4f MXFP4_LDS* xch = (v4f MXFP4_LDS*)lds;
 #pragma unroll
@@ -213,6 +216,46 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, in
   const int rows = min(C::BM, args.m - m0);
   const int cols = min(kBN, args.n - n0);
   const int n = args.n;
+  if (!args.c_f32) {
+    // BF16: the summed units go into a row-major tile in LDS, then whole
+    // 128-byte output rows leave in 16-byte non-temporal stores (8-byte stores
+    // scattered over 32 rows measured far slower in the tile kernels).
+    uint8_t MXFP4_LDS* ctile = lds + C::XCH;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u / UW != w) continue;   // wave-uniform
+      const int i = u / 8, j = (u / 4) % 2, q = u % 4;
+      const v4f own = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      v4f v = (w == 0) ? own : xch[u * 64 + lane];
+#pragma unroll
+      for (int src = 1; src < 4; ++src) v += (w == src) ? own : xch[(src * U + u) * 64 + lane];
+      const int r = 32 * i + (lane & 31);
+      const int col = 32 * j + 8 * q + 4 * (lane >> 5);
+      bf16x2_t lo = {(__bf16)v.x, (__bf16)v.y};
+      bf16x2_t hi = {(__bf16)v.z, (__bf16)v.w};
+      v2i pk = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+      *(v2i MXFP4_LDS*)(ctile + r * C::C_PITCH + col * 2) = pk;
+    }
+    __syncthreads();
+    const bool vec_ok = (n & 7) == 0;   // 16-byte aligned output rows
+    for (int idx = threadIdx.x; idx < rows * 8; idx += kThreads) {
+      const int r = idx >> 3, cc = idx & 7;
+      const int col = cc * 8;
+      if (col >= cols) continue;
+      const v4i v = *(const v4i MXFP4_LDS*)(ctile + r * C::C_PITCH + cc * 16);
+      uint16_t* dst = (uint16_t*)args.c + (int64_t)(m0 + r) * n + n0 + col;
+      const int cnt = min(8, cols - col);
+      if (vec_ok && cnt == 8) {
+        __builtin_nontemporal_store(v, (v4i*)dst);
+      } else {
+        for (int e = 0; e < cnt; ++e) {
+          const uint32_t word = (uint32_t)((e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w);
+          dst[e] = (uint16_t)(word >> (16 * (e & 1)));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u / UW != w) continue;   // wave-uniform
@@ -225,25 +268,11 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, in
     const int col = 32 * j + 8 * q + 4 * (lane >> 5);
     const int cnt = min(4, cols - col);
     if (r >= rows || cnt <= 0) continue;
-    const int64_t e0 = (int64_t)(m0 + r) * n + n0 + col;
-    if (args.c_f32) {
-      float* dst = (float*)args.c + e0;
-      if (cnt == 4 && (n & 3) == 0) {
-        *(v4f*)dst = v;
-      } else {
-        for (int e = 0; e < cnt; ++e) dst[e] = v[e];
-      }
+    float* dst = (float*)args.c + (int64_t)(m0 + r) * n + n0 + col;
+    if (cnt == 4 && (n & 3) == 0) {
+      *(v4f*)dst = v;
     } else {
-      uint16_t* dst = (uint16_t*)args.c + e0;
-      bf16x2_t lo = {(__bf16)v.x, (__bf16)v.y};
-      bf16x2_t hi = {(__bf16)v.z, (__bf16)v.w};
-      if (cnt == 4 && (n & 3) == 0) {
-        v2i pk = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
-        *(v2i*)dst = pk;
-      } else {
-        const uint32_t words[2] = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        for (int e = 0; e < cnt; ++e) dst[e] = (uint16_t)(words[e >> 1] >> (16 * (e & 1)));
-      }
+      for (int e = 0; e < cnt; ++e) dst[e] = v[e];
     }
   }
 }
