@@ -17,6 +17,10 @@ them.  Each timed region is a HIP graph of whole steps replayed on the stream
 the kernels run on, bracketed by events and device synchronisations; one event
 pair per graph replay also gives min / median / max per-step times.
 
+Measured ceilings (probe kernels in the same library) are reported beside the
+published peaks: the FP4 MFMA rate of a kernel that only runs MFMAs, and the
+streaming read rate (`--no-ceilings` skips them).
+
 Prints one JSON line on stdout.  The roofline object is for the GEMM kernel:
 algorithmic flops (or bytes) per launch divided by the kernel's mean duration,
 measured with events over a region of back-to-back GEMM launches.
@@ -197,6 +201,54 @@ class MoEBench:
     timed = DenseBench.timed
 
 
+class Ceilings:
+    """Measured ceilings on this GPU (include/mxfp4_probe.h), reported next to the
+    published peaks: the FP4 scaled-MFMA rate of a kernel that only runs MFMAs
+    (8 waves per CU like the tile GEMM; one launch about as long as the 4096^3
+    GEMM, and one ~8x longer), and the streaming read rate over buffers of the
+    decode weight's size (rotated past the Infinity Cache) and over 1 GiB."""
+
+    READ_SMALL = 14336 * 4096 // 2        # the decode weight's packed codes
+
+    def __init__(self, dev):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        props = torch.cuda.get_device_properties(dev)
+        self.cus = props.multi_processor_count
+        g = torch.Generator(device="cpu").manual_seed(7)
+        self.seed = torch.randint(0, 256, (B.PROBE_SEED_BYTES,), dtype=torch.uint8, generator=g).to(dev)
+        self.mfma_out = torch.empty(self.cus * 512, dtype=torch.float32, device=dev)
+        self.read_blocks = self.cus          # one 256-thread workgroup per CU reads fastest
+        self.read_out = torch.empty(self.read_blocks * 256, dtype=torch.int32, device=dev)
+        self.small = [torch.full((self.READ_SMALL,), i + 1, dtype=torch.uint8, device=dev)
+                      for i in range(max(2, math.ceil(ROTATION_BYTES / self.READ_SMALL)))]
+        self.big = torch.full((1 << 30,), 3, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+    def measure(self, steps):
+        out = {}
+        for label, iters in (("short", 128), ("long", 1024)):
+            self.sets_n = 1
+            flops = self.B.load_library().mxfp4_probe_mfma_flops(self.cus, iters)
+            t = self.timed(lambda i: self.B.mxfp4_probe_mfma(self.seed, self.mfma_out, self.cus, iters),
+                           steps, max(4, steps // 10))
+            out[f"mfma_fp4_tflops_{label}"] = round(flops / (t["mean"] * 1e-3) / 1e12, 1)
+            out[f"mfma_probe_{label}_us"] = round(t["mean"] * 1e3, 2)
+        self.sets_n = len(self.small)
+        t = self.timed(lambda i: self.B.mxfp4_probe_read(self.small[i % self.sets_n], self.read_out,
+                                                          self.read_blocks), steps, max(4, steps // 10))
+        out["read_gbs_29MB"] = round(self.READ_SMALL / (t["mean"] * 1e-3) / 1e9, 1)
+        out["read_29MB_us"] = round(t["mean"] * 1e3, 2)
+        self.sets_n = 1
+        t = self.timed(lambda i: self.B.mxfp4_probe_read(self.big, self.read_out, self.read_blocks),
+                       max(4, steps // 20), 2)
+        out["read_gbs_1GiB"] = round((1 << 30) / (t["mean"] * 1e-3) / 1e9, 1)
+        return out
+
+
 def cpu_baseline(bench: DenseBench, target_seconds: float):
     """The CPU oracle, as it stands, on a bounded sample of the same step: oracle
     quantization of A, then its float64 GEMM against the pre-quantized B (the
@@ -298,6 +350,7 @@ def main():
                     help="grouped MoE workload reported in the same line ('none' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy"])
     args = ap.parse_args()
 
@@ -416,6 +469,20 @@ def main():
         eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
         del mb
+
+    if not args.no_ceilings:
+        eprint("[bench] measuring MFMA and streaming-read ceilings with the probe kernels")
+        cl = Ceilings(dev)
+        ceil = cl.measure(args.steps)
+        del cl
+        ceil["gemm_frac_of_mfma_ceiling"] = round(gemm_tflops / ceil["mfma_fp4_tflops_short"], 4)
+        if "secondary" in result:
+            ceil["decode_gemm_frac_of_read_ceiling"] = round(
+                result["secondary"]["roofline"]["achieved"] / ceil["read_gbs_29MB"], 4)
+        ceil["note"] = ("measured on this GPU by probe kernels (include/mxfp4_probe.h); "
+                        "roofline.peak stays the published figure")
+        result["ceilings"] = ceil
+        eprint(f"[bench] ceilings: {ceil}")
 
     if not args.no_cpu_baseline:
         eprint("[bench] timing the CPU oracle on a bounded sample")

@@ -25,7 +25,9 @@ EXPORTED = (
     "mxfp4_abi_version", "mxfp4_status_string", "mxfp4_last_error", "mxfp4_quantize",
     "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
+    "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read",
 )
+PROBE_SEED_BYTES = 6144
 
 _lib = None
 _lock = threading.Lock()
@@ -69,6 +71,12 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_grouped_gemm_nt.restype = ctypes.c_int
         lib.mxfp4_grouped_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64,
                                               vp, sz, vp]
+        lib.mxfp4_probe_mfma.restype = ctypes.c_int
+        lib.mxfp4_probe_mfma.argtypes = [vp, vp, i32, i32, vp]
+        lib.mxfp4_probe_mfma_flops.restype = ctypes.c_double
+        lib.mxfp4_probe_mfma_flops.argtypes = [i32, i32]
+        lib.mxfp4_probe_read.restype = ctypes.c_int
+        lib.mxfp4_probe_read.argtypes = [vp, i64, vp, i32, vp]
         _lib = lib
         return lib
 
@@ -186,3 +194,26 @@ def mxfp4_grouped_gemm_nt(a_q, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.b
     _check(lib.mxfp4_grouped_gemm_nt(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), groups,
                                      total_m, _ptr(c), code, n, k, _ptr(ws), nbytes, _stream(stream)))
     return c
+
+
+def mxfp4_probe_mfma(seed: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
+    """Runs the FP4 scaled-MFMA probe (include/mxfp4_probe.h); returns the flops of the call."""
+    lib = load_library()
+    if seed.numel() * seed.element_size() < PROBE_SEED_BYTES or not seed.is_contiguous():
+        raise ValueError(f"seed must be a contiguous device tensor of at least {PROBE_SEED_BYTES} bytes")
+    if out.dtype != torch.float32 or out.numel() < blocks * 512 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 device tensor of at least blocks * 512 elements")
+    _check(lib.mxfp4_probe_mfma(_ptr(seed), _ptr(out), blocks, iters, _stream(stream)))
+    return lib.mxfp4_probe_mfma_flops(blocks, iters)
+
+
+def mxfp4_probe_read(src: torch.Tensor, out: torch.Tensor, blocks: int, stream=None) -> int:
+    """Runs the streaming-read probe over all of `src`; returns the bytes read."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if out.dtype not in (torch.int32, torch.uint32) or out.numel() < blocks * 256 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 32-bit integer device tensor of at least blocks * 256 elements")
+    _check(lib.mxfp4_probe_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(stream)))
+    return nbytes

@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "../../include/mxfp4.h"
+#include "../../include/mxfp4_probe.h"
 #include "launch.hpp"
 
 namespace {
@@ -282,6 +283,33 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   args.groups = num_groups;
   const mxfp4::TileKind kind = (total_m / num_groups >= 192) ? mxfp4::kTile256 : mxfp4::kTile128;
   return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
+}
+
+mxfp4_status_t mxfp4_probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream) {
+  if (blocks < 1 || blocks > 65536) return fail(MXFP4_ERR_INVALID_ARG, "blocks must be 1..65536 (got %d)", blocks);
+  if (iters < 1 || iters > (1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "iters must be 1..2^24 (got %d)", iters);
+  MXFP4_TRY(check_ptr(seed, "seed"));
+  MXFP4_TRY(check_ptr(out, "out"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_probe_mfma(seed, out, blocks, iters, (hipStream_t)stream), "mfma probe launch");
+}
+
+double mxfp4_probe_mfma_flops(int32_t blocks, int32_t iters) {
+  if (blocks < 1 || iters < 1) return 0.0;
+  return mxfp4::probe_mfma_flops(blocks, iters);
+}
+
+mxfp4_status_t mxfp4_probe_read(const void* src, int64_t bytes, void* out, int32_t blocks, void* stream) {
+  if (bytes <= 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40))
+    return fail(MXFP4_ERR_INVALID_ARG, "bytes must be a positive multiple of 16, at most 2^40 (got %lld)",
+                (long long)bytes);
+  if (blocks < 1 || blocks > 65536) return fail(MXFP4_ERR_INVALID_ARG, "blocks must be 1..65536 (got %d)", blocks);
+  MXFP4_TRY(check_ptr(src, "src"));
+  MXFP4_TRY(check_ptr(out, "out", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_probe_read(src, bytes, out, blocks, (hipStream_t)stream), "read probe launch");
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
 """Host-side checks of the C ABI that need no GPU: the library loads, exports
-every function include/mxfp4.h declares, and rejects bad arguments on the host
-before any device call (argument validation runs before the device query)."""
+every function the headers in include/ declare, and rejects bad arguments on the
+host before any device call (argument validation runs before the device query)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,13 +11,15 @@ import pytest
 from block_scaled_fp4_mxfp4_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mxfp4_\w+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names.update(re.findall(r"\b(mxfp4_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -113,3 +116,23 @@ def test_workspace_queries(lib):
     # invalid shapes report 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(64, 512, 100, 3, 4) == 0
     assert lib.mxfp4_gemm_nt_ex_workspace_size(500, 512, 1024, 3, 4) == 0
+
+
+def test_probes_reject_bad_arguments_on_host(lib):
+    f = _fake()
+    assert lib.mxfp4_probe_mfma(f, f, 0, 16, None) == 1
+    assert lib.mxfp4_probe_mfma(f, f, 65537, 16, None) == 1
+    assert lib.mxfp4_probe_mfma(f, f, 4, 0, None) == 1
+    assert lib.mxfp4_probe_mfma(f, f, 4, (1 << 24) + 1, None) == 1
+    assert lib.mxfp4_probe_mfma(None, f, 4, 16, None) == 1
+    assert b"seed is NULL" in lib.mxfp4_last_error()
+    assert lib.mxfp4_probe_mfma(f, _fake(0x1004), 4, 16, None) == 1
+    assert lib.mxfp4_probe_read(f, 0, f, 4, None) == 1
+    assert lib.mxfp4_probe_read(f, 24, f, 4, None) == 1
+    assert lib.mxfp4_probe_read(f, (1 << 40) + 16, f, 4, None) == 1
+    assert lib.mxfp4_probe_read(f, 4096, f, 0, None) == 1
+    assert lib.mxfp4_probe_read(_fake(0x1008), 4096, f, 4, None) == 1
+    assert lib.mxfp4_probe_read(f, 4096, _fake(0x1002), 4, None) == 1
+    # 8 waves x iters x 8 MFMAs of 2*32*32*64 flops per workgroup
+    assert lib.mxfp4_probe_mfma_flops(3, 5) == 3 * 8 * 5 * 8 * 131072
+    assert lib.mxfp4_probe_mfma_flops(0, 5) == 0.0
