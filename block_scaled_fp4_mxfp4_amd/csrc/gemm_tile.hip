@@ -549,8 +549,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
                                          const RowRange& ar, int n0, uint8_t MXFP4_LDS* lds) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // Wave w runs on SIMD w % 4.  With 8 waves, the two waves sharing a SIMD sit
-  // in different wave rows, so in a tile whose last rows are padding both
-  // SIMD's waves are not both fully busy (see copy_loop_dispatch).
+  // in different wave rows: in a tile whose last rows are padding, the work
+  // the second wave row skips (copy_loop_dispatch) is spread over all SIMDs
+  // instead of idling two of them.
   const int wm0 = (w / C::WGN) * C::WM, wn0 = (w % C::WGN) * C::WN;
   v16f acc[C::MI][C::NI];
 #pragma unroll

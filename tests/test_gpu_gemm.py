@@ -27,6 +27,9 @@ pytestmark = pytest.mark.gpu
 TILE_SHAPES = [  # (m, n, k): several tiles, ragged tails, k % 128 != 0 cases
     (256, 256, 128), (300, 520, 1024), (513, 263, 2048), (130, 900, 1056), (64, 64, 32),
     (257, 129, 4096), (1, 300, 96),
+    # last 256-row tile with 96 and with 200 stored rows: a wave row with 3 of its
+    # 4 row blocks stored (first / second wave row)
+    (352, 520, 1024), (200, 300, 512),
 ]
 SPLITK_SHAPES = [(1, 64, 128), (17, 200, 1024), (32, 1000, 4096), (33, 70, 160), (100, 512, 2048),
                  (128, 320, 4096), (64, 129, 8192)]
