@@ -229,9 +229,11 @@ class Ceilings:
     timed = DenseBench.timed
 
     def measure(self, steps):
+        # Several launches per captured graph, as for the GEMMs: a graph of one
+        # launch adds a replay gap of several microseconds to every launch.
         out = {}
         for label, iters in (("short", 128), ("long", 1024)):
-            self.sets_n = 1
+            self.sets_n = 16
             flops = self.B.load_library().mxfp4_probe_mfma_flops(self.cus, iters)
             t = self.timed(lambda i: self.B.mxfp4_probe_mfma(self.seed, self.mfma_out, self.cus, iters),
                            steps, max(4, steps // 10))
@@ -242,9 +244,9 @@ class Ceilings:
                                                           self.read_blocks), steps, max(4, steps // 10))
         out["read_gbs_29MB"] = round(self.READ_SMALL / (t["mean"] * 1e-3) / 1e9, 1)
         out["read_29MB_us"] = round(t["mean"] * 1e3, 2)
-        self.sets_n = 1
+        self.sets_n = 4
         t = self.timed(lambda i: self.B.mxfp4_probe_read(self.big, self.read_out, self.read_blocks),
-                       max(4, steps // 20), 2)
+                       max(8, steps // 10), 4)
         out["read_gbs_1GiB"] = round((1 << 30) / (t["mean"] * 1e-3) / 1e9, 1)
         return out
 
