@@ -328,8 +328,11 @@ def run_only(args, dev):
         torch.cuda.synchronize()
         eprint(f"[bench] {args.steps} copies of {COPY_BYTES} bytes")
         return
-    w = workloads.DENSE[args.workload]
-    bench = DenseBench(w, dev)
+    w = workloads.ALL[args.workload]
+    bench = MoEBench(w, dev) if isinstance(w, workloads.MoEWorkload) else DenseBench(w, dev)
+    if not hasattr(bench, args.only):
+        eprint(f"'{args.only}' is not a mode of {w.name}")
+        sys.exit(2)
     fn = getattr(bench, args.only)
     for i in range(args.warmup):
         fn(i)
@@ -345,7 +348,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=workloads.SQUARE4096.name, choices=sorted(workloads.DENSE))
+    ap.add_argument("--workload", default=workloads.SQUARE4096.name, choices=sorted(workloads.ALL),
+                    help="primary dense workload; with --only, any workload (MoE: gemm, quantize, step)")
     ap.add_argument("--secondary", default=workloads.DECODE.name,
                     help="second dense workload reported in the same line ('none' to skip)")
     ap.add_argument("--moe", default=workloads.MOE.name,
@@ -370,6 +374,10 @@ def main():
         run_only(args, dev)
         return
 
+    if args.workload not in workloads.DENSE:
+        eprint(f"the primary workload must be dense ({', '.join(sorted(workloads.DENSE))}); "
+               f"use --moe for the grouped one")
+        sys.exit(2)
     w = workloads.DENSE[args.workload]
     eprint(f"[bench] building inputs for {w.name}")
     bench = DenseBench(w, dev)
