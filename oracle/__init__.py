@@ -6,3 +6,7 @@ from .mxfp4_oracle import (  # noqa: F401
     quantize_block_values, pack_codes, unpack_codes, quantize, dequantize,
     gemm_nt, gemm_nt_f32, grouped_gemm_nt, round_output_bf16, floored_max_rel,
 )
+from .mxfp8_oracle import (  # noqa: F401
+    E4M3_TABLE, E4M3_MAGNITUDES, E4M3_MAX, e4m3_value, shared_exponent_e4m3, encode_e4m3_magnitude,
+    quantize_block_values_e4m3, quantize_mxfp8, dequantize_mxfp8, gemm_w4a8_nt,
+)
