@@ -1,7 +1,7 @@
-"""MI355X (gfx950) MXFP4 engine: BF16 -> MXFP4 quantization, block-scaled FP4 NT GEMM
-and grouped per-expert GEMM, as hand-written HIP kernels behind a C ABI
-(include/mxfp4.h).  The Python layer is a thin ctypes binding."""
+"""MI355X (gfx950) MXFP4 engine: BF16 -> MXFP4 quantization, block-scaled FP4 NT GEMM,
+grouped per-expert GEMM and BF16 -> MXFP8 activation quantization, as hand-written
+HIP kernels behind a C ABI (include/mxfp4.h, include/mxfp8.h).  The Python layer is a thin ctypes binding."""
 from .binding import (  # noqa: F401
-    MXFP4Error, load_library, mxfp4_quantize, mxfp4_gemm_nt, mxfp4_grouped_gemm_nt, workspace,
+    MXFP4Error, load_library, mxfp4_quantize, mxfp8_quantize, mxfp4_gemm_nt, mxfp4_grouped_gemm_nt, workspace,
     LIB_PATH, EXPORTED, KERNELS,
 )

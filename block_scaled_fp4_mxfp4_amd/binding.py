@@ -1,4 +1,4 @@
-"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h).
+"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h and include/mxfp8.h).
 
 Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the computation runs in the library's kernels.  The
@@ -25,7 +25,7 @@ EXPORTED = (
     "mxfp4_abi_version", "mxfp4_status_string", "mxfp4_last_error", "mxfp4_quantize",
     "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
-    "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read",
+    "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_last_error.argtypes = []
         lib.mxfp4_quantize.restype = ctypes.c_int
         lib.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp8_quantize.restype = ctypes.c_int
+        lib.mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp4_gemm_nt_workspace_size.restype = sz
         lib.mxfp4_gemm_nt_workspace_size.argtypes = [i64, i64, i64]
         lib.mxfp4_gemm_nt.restype = ctypes.c_int
@@ -142,6 +144,24 @@ def mxfp4_quantize(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch
     _require(scales, "scales", torch.uint8, (rows, k // 32))
     _check(lib.mxfp4_quantize(_ptr(x), rows, k, _ptr(q), _ptr(scales), _stream(stream)))
     return q, scales
+
+
+def mxfp8_quantize(x: torch.Tensor, q8: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   stream=None):
+    """x: bf16 [rows, k] -> (q8 uint8 [rows, k] E4M3 codes, scales uint8 [rows, k/32])."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, k]")
+    rows, k = x.shape
+    if q8 is None:
+        q8 = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(q8, "q8", torch.uint8, (rows, k))
+    _require(scales, "scales", torch.uint8, (rows, k // 32))
+    _check(lib.mxfp8_quantize(_ptr(x), rows, k, _ptr(q8), _ptr(scales), _stream(stream)))
+    return q8, scales
 
 
 def _out(c, m, n, out_dtype, device):

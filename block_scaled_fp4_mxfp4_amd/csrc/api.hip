@@ -1,5 +1,5 @@
 // C ABI of the MXFP4 library: argument checks, per-shape kernel choice, launches.
-// Entry points and their contracts are documented in include/mxfp4.h.
+// Entry points and their contracts are documented in include/mxfp4.h and include/mxfp8.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -9,6 +9,7 @@
 
 #include "../../include/mxfp4.h"
 #include "../../include/mxfp4_probe.h"
+#include "../../include/mxfp8.h"
 #include "launch.hpp"
 
 namespace {
@@ -189,6 +190,20 @@ mxfp4_status_t mxfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void*
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_quantize(x_bf16, rows, k, q, scales, (hipStream_t)stream, dev.num_cus),
                     "quantize launch");
+}
+
+mxfp4_status_t mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q8, void* scales, void* stream) {
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
+  MXFP4_TRY(check_k(k));
+  if (rows > ((int64_t)1 << 40) / k) return fail(MXFP4_ERR_INVALID_ARG, "rows * k too large");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(q8, "q8", 8));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_quantize_mxfp8(x_bf16, rows, k, q8, scales, (hipStream_t)stream, dev.num_cus),
+                    "mxfp8 quantize launch");
 }
 
 size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, int32_t splits) {

@@ -30,6 +30,8 @@ enum TileKind { kTile256 = 0, kTile128 = 1 };
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                            hipStream_t stream, int num_cus);
+hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                 hipStream_t stream, int num_cus);
 
 hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
 

@@ -95,7 +95,88 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// BF16 -> MXFP8 (E4M3 elements, E8M0 scales): the activation format of the W4A8
+// GEMM ("fp4_quantization" page, quantize_dynamic_scaled_fp4fp8: BF16 to
+// NVFP4 / MXFP4 / MXFP8 with per-block scale factors).  Same block mapping as
+// above; each lane writes its 8 elements as 8 code bytes.
+//  * e = floor(log2 amax) - 8 (E4M3's largest exponent is 8), clamped to the
+//    E8M0 range: byte = max(E - 8, 0) for amax's biased exponent E.
+//  * Elements: x / 2^e rounded to nearest-even E4M3, magnitudes above 448
+//    saturating to 448.  Every magnitude is first clamped to 448 * 2^e, which
+//    BF16 represents exactly (exponent field 8 + byte, mantissa 0x60): values
+//    in (448, 464] * 2^e round to 448 anyway and larger ones saturate there,
+//    so after the clamp the convert only ever sees in-range values and the
+//    result does not depend on its overflow handling.  The scaled convert
+//    v_cvt_scalef32_pk_fp8_bf16 then applies 2^-e from the scale's exponent
+//    field and rounds to nearest-even; the parity tests check it against the
+//    reference encoding for every finite BF16 value at every scale byte.
+// ---------------------------------------------------------------------------
+
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t clamp_mag16x2(uint32_t w, uint32_t bound) {
+  const uint32_t lo = min(w & 0x7FFFu, bound) | (w & 0x8000u);
+  const uint32_t hi = min((w >> 16) & 0x7FFFu, bound) | ((w >> 16) & 0x8000u);
+  return lo | (hi << 16);
+}
+
+__device__ __forceinline__ uint32_t cvt_fp8x4(uint32_t w01, uint32_t w23, float scale) {
+  short2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w01), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w23), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
+    const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ scales, int64_t nblocks) {
+  const int lane4 = threadIdx.x & 3;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
+  int64_t blk = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2);
+
+  for (; blk < nblocks; blk += groups_per_grid * kQuantUnroll) {
+    uint4 v[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const int64_t b = blk + u * groups_per_grid;
+      v[u] = x[(b < nblocks ? b : 0) * 4 + lane4];
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const int64_t b = blk + u * groups_per_grid;
+      const uint32_t m01 = umax16x2(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu);
+      const uint32_t m23 = umax16x2(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu);
+      const uint32_t m = umax16x2(m01, m23);
+      uint32_t amax_bits = max(m & 0xFFFFu, m >> 16);
+      amax_bits = quad_max(amax_bits);
+      const int exp_field = (int)(amax_bits >> 7);
+      const uint32_t sbyte = (uint32_t)max(exp_field - 8, 0);
+      const float scale = __uint_as_float(sbyte << 23);
+      const uint32_t bound = ((8u + sbyte) << 7) | 0x60u;      // 448 * 2^e as BF16 magnitude bits
+      const uint32_t lo = cvt_fp8x4(clamp_mag16x2(v[u].x, bound), clamp_mag16x2(v[u].y, bound), scale);
+      const uint32_t hi = cvt_fp8x4(clamp_mag16x2(v[u].z, bound), clamp_mag16x2(v[u].w, bound), scale);
+      if (b < nblocks) {
+        q[b * 4 + lane4] = make_uint2(lo, hi);
+        if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                 hipStream_t stream, int num_cus) {
+  const int64_t nblocks = rows * (k / 32);
+  const int64_t groups_needed = (nblocks + kQuantUnroll - 1) / kQuantUnroll;
+  int64_t grid = (groups_needed + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
+  const int64_t max_grid = (int64_t)num_cus * 8;
+  if (grid > max_grid) grid = max_grid;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                     (const uint4*)x, (uint2*)q, (uint8_t*)scales, nblocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                            hipStream_t stream, int num_cus) {

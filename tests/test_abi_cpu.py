@@ -18,7 +18,7 @@ def _declared_functions():
     names = set()
     for header in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
-        names.update(re.findall(r"\b(mxfp4_\w+)\s*\(", text))
+        names.update(re.findall(r"\b(mxfp[48]_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -62,6 +62,19 @@ def test_quantize_rejects_bad_arguments_on_host(lib):
     assert b"q is not 4-byte aligned" in lib.mxfp4_last_error()
     # zero rows: valid no-op, returns before touching the device
     assert lib.mxfp4_quantize(None, 0, 64, None, None, None) == 0
+
+
+def test_mxfp8_quantize_rejects_bad_arguments_on_host(lib):
+    assert lib.mxfp8_quantize(_fake(), 4, 48, _fake(), _fake(), None) == 1
+    assert lib.mxfp8_quantize(_fake(), -1, 64, _fake(), _fake(), None) == 1
+    assert lib.mxfp8_quantize(_fake(), 4, (1 << 24) + 32, _fake(), _fake(), None) == 1
+    assert lib.mxfp8_quantize(None, 4, 64, _fake(), _fake(), None) == 1
+    assert b"x_bf16 is NULL" in lib.mxfp4_last_error()
+    assert lib.mxfp8_quantize(_fake(0x1008), 4, 64, _fake(), _fake(), None) == 1
+    assert lib.mxfp8_quantize(_fake(), 4, 64, _fake(0x1004), _fake(), None) == 1
+    assert b"q8 is not 8-byte aligned" in lib.mxfp4_last_error()
+    assert lib.mxfp8_quantize(_fake(), 4, 64, _fake(), None, None) == 1
+    assert lib.mxfp8_quantize(None, 0, 64, None, None, None) == 0
 
 
 def test_gemm_rejects_bad_arguments_on_host(lib):
