@@ -1,7 +1,9 @@
 """MI355X (gfx950) MXFP4 engine: BF16 -> MXFP4 quantization, block-scaled FP4 NT GEMM,
-grouped per-expert GEMM and BF16 -> MXFP8 activation quantization, as hand-written
-HIP kernels behind a C ABI (include/mxfp4.h, include/mxfp8.h).  The Python layer is a thin ctypes binding."""
+grouped per-expert GEMM, BF16 -> MXFP8 activation quantization and W4A8 GEMMs
+(MXFP8 A x MXFP4 B), as hand-written HIP kernels behind a C ABI (include/mxfp4.h,
+include/mxfp8.h).  The Python layer is a thin ctypes binding."""
 from .binding import (  # noqa: F401
     MXFP4Error, load_library, mxfp4_quantize, mxfp8_quantize, mxfp4_gemm_nt, mxfp4_grouped_gemm_nt, workspace,
+    mxfp8_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt,
     LIB_PATH, EXPORTED, KERNELS,
 )

@@ -26,6 +26,7 @@ EXPORTED = (
     "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
+    "mxfp8_gemm_w4a8_nt", "mxfp8_grouped_gemm_w4a8_nt",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -59,6 +60,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp8_quantize.restype = ctypes.c_int
         lib.mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp8_gemm_w4a8_nt.restype = ctypes.c_int
+        lib.mxfp8_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp8_grouped_gemm_w4a8_nt.restype = ctypes.c_int
+        lib.mxfp8_grouped_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64, vp]
         lib.mxfp4_gemm_nt_workspace_size.restype = sz
         lib.mxfp4_gemm_nt_workspace_size.argtypes = [i64, i64, i64]
         lib.mxfp4_gemm_nt.restype = ctypes.c_int
@@ -213,6 +218,37 @@ def mxfp4_grouped_gemm_nt(a_q, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.b
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxfp4_grouped_gemm_nt(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), groups,
                                      total_m, _ptr(c), code, n, k, _ptr(ws), nbytes, _stream(stream)))
+    return c
+
+
+def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, stream=None):
+    """C[m, n] = A[m, k] . B[n, k]^T with A in MXFP8 ([m, k] codes) and B in MXFP4."""
+    lib = load_library()
+    m, k = a_q8.shape
+    n = b_q.shape[0]
+    _require(a_q8, "a_q8", torch.uint8, (m, k))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (n, k // 32))
+    c, code = _out(c, m, n, out_dtype, a_q8.device)
+    _check(lib.mxfp8_gemm_w4a8_nt(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
+                                  _stream(stream)))
+    return c
+
+
+def mxfp8_grouped_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.bfloat16, stream=None):
+    """Per-group W4A8 NT GEMM; `offsets` is a device int32 [groups + 1] tensor."""
+    lib = load_library()
+    total_m, k = a_q8.shape
+    groups, n, _ = b_q.shape
+    _require(a_q8, "a_q8", torch.uint8, (total_m, k))
+    _require(a_s, "a_s", torch.uint8, (total_m, k // 32))
+    _require(b_q, "b_q", torch.uint8, (groups, n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (groups, n, k // 32))
+    _require(offsets, "offsets", torch.int32, (groups + 1,))
+    c, code = _out(c, total_m, n, out_dtype, a_q8.device)
+    _check(lib.mxfp8_grouped_gemm_w4a8_nt(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), groups,
+                                          total_m, _ptr(c), code, n, k, _stream(stream)))
     return c
 
 

@@ -300,6 +300,50 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
 }
 
+mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                  mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s, b_q, b_s, c, c_type, m, n, k));
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q8;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  return hip_status(mxfp4::launch_gemm_w4a8_tile(args, (hipStream_t)stream), "w4a8 gemm launch");
+}
+
+mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,
+                                          const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
+                                          mxfp4_out_t c_type, int64_t n, int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s, b_q, b_s, c, c_type, total_m, n, k));
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(MXFP4_ERR_INVALID_ARG, "num_groups must be 1..1024 (got %d)", num_groups);
+  if (total_m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(offsets, "offsets", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q8;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)total_m;
+  args.n = (int)n;
+  args.k = (int)k;
+  args.offsets = offsets;
+  args.groups = num_groups;
+  return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile(args, (hipStream_t)stream), "grouped w4a8 gemm launch");
+}
+
 mxfp4_status_t mxfp4_probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream) {
   if (blocks < 1 || blocks > 65536) return fail(MXFP4_ERR_INVALID_ARG, "blocks must be 1..65536 (got %d)", blocks);
   if (iters < 1 || iters > (1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "iters must be 1..2^24 (got %d)", iters);

@@ -14,7 +14,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 #define MXFP4_LDS __attribute__((address_space(3)))
 
-// Element formats of the scaled f8f6f4 MFMA: 4 selects FP4 E2M1 for an operand.
+// Element formats of the scaled f8f6f4 MFMA: 0 selects FP8 E4M3 for an
+// operand, 4 selects FP4 E2M1.
+constexpr int kMfmaFmtFp8 = 0;
 constexpr int kMfmaFmtFp4 = 4;
 
 // s_waitcnt immediate on gfx9: wait until at most `n` vector-memory operations
@@ -71,6 +73,17 @@ __device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f acc, int sa, int s
   v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
   v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, kMfmaFmtFp4, kMfmaFmtFp4,
+                                                         OPSEL, sa, OPSEL, sb);
+}
+
+// The same step with the second operand in FP8 E4M3: lane l supplies 32
+// codes of row (l % 32), K [16h, 16h + 16) in its first four registers and
+// [32 + 16h, 48 + 16h) in the last four (h = l / 32); its scale byte still
+// covers K-block h.  With an FP8 operand the MFMA runs at the FP8 rate.
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma32_fp4_fp8(v4i a, v8i b, v16f acc, int sa, int sb) {
+  v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, acc, kMfmaFmtFp4, kMfmaFmtFp8,
                                                          OPSEL, sa, OPSEL, sb);
 }
 

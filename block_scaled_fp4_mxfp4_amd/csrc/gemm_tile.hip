@@ -54,10 +54,28 @@
 //  * Workgroup -> tile mapping is XCD-aware (see tile_coords in common.hpp);
 //    the grouped kernel splits its real tiles evenly over the XCDs.
 //
+// W4A8 (MXFP8 activations x MXFP4 weights, "fp4_quantization" page: the
+// block-scaled matmul also takes MXFP8 operands; quantize_dynamic_scaled_fp4fp8
+// produces them): the same kernel with A in FP8 E4M3, one code byte per
+// element, on the same MFMA with A's format set to FP8.
+//  * Lane l then supplies 32 bytes of A for row l % 32: with h = l / 32, K
+//    [16h, 16h + 16) and [32 + 16h, 48 + 16h) of the 64-deep k-step (an FP8
+//    operand interleaves 16-element groups, unlike FP4's one 32-run per lane
+//    half); two ds_read_b128 per fragment.  The E8M0 byte of lane l still
+//    scales K-block l / 32.  A row of a stage is 256 bytes = sixteen
+//    16-byte chunks; logical chunk c of row r sits at c ^ (r & 15), so 16
+//    consecutive rows at one chunk hit 16 different bank groups.
+//  * An FP8 A stage is twice as large and a mixed FP8 x FP4 MFMA runs at the
+//    FP8 rate (half the FP4 rate), so the W4A8 tile is 128 x 256: two stages
+//    (64 KiB each) fit in LDS and LDS bytes per MFMA cycle equal the 256 x 256
+//    FP4 kernel's.  Scale bytes are unchanged (one per 32 elements).
+//
 // Ragged edges: rows past M (or N) read a clamped, valid row and are never
 // stored.  The copy path needs k % 512 == 0 and 16-byte aligned scale arrays;
 // any other k (a multiple of 32) goes through a register path that zero-fills
 // the missing 32-blocks (zero codes contribute nothing whatever their scale).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,23 +87,39 @@ constexpr int kRowBytes = kBK / 2;  // code bytes per row per stage
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+// Chunk swizzle of an A row: FP4 rows have 8 chunks, FP8 rows 16.
+template <class C>
+__device__ __forceinline__ int a_swz(int row) {
+  return C::A8 ? (row & 15) : swz(row);
+}
+
+template <int BM_, int BN_, int WGM_, int WGN_, bool A8_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;               // wave grid over the tile
   static constexpr int NWAVES = WGM * WGN, THREADS = 64 * NWAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NI = WN / 32;
-  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr bool A8 = A8_;                            // A in FP8 E4M3 (W4A8) instead of FP4
+  static constexpr int A_ROW = A8 ? kBK : kRowBytes;         // A code bytes per row per stage
+  static constexpr int A_SHIFT = A8 ? 4 : 3;                 // log2 of the 16-byte chunks in an A row
+  static constexpr int A_READS = A8 ? 2 : 1;                 // ds_read_b128 per A fragment
+  using AFrag = typename std::conditional<A8, v8i, v4i>::type;
+  static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BN * kRowBytes;
   static constexpr int CODE_STAGE = A_BYTES + B_BYTES;
-  static constexpr int SCALE_GROUP = (BM + BN) * 16;        // 16 scale bytes per row = two stages
+  // 16-byte scale copies per thread per group (16 scale bytes per row = two
+  // stages); when BM + BN is not a multiple of the thread count the last
+  // copies re-read a valid row into padding
+  static constexpr int S_LOADS = (BM + BN + THREADS - 1) / THREADS;
+  static constexpr int SCALE_GROUP = S_LOADS * THREADS * 16;
   static constexpr int LDS_BYTES = 2 * CODE_STAGE + 2 * SCALE_GROUP;
-  static constexpr int A_LOADS = BM * kRowBytes / 16 / THREADS;   // 16-byte copies per thread per stage
+  static constexpr int A_LOADS = BM * A_ROW / 16 / THREADS;      // 16-byte copies per thread per stage
   static constexpr int B_LOADS = BN * kRowBytes / 16 / THREADS;
-  static constexpr int S_LOADS = (BM + BN) / THREADS;            // 16-byte scale copies per thread per group
   static constexpr int CODE_LOADS = A_LOADS + B_LOADS;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
-  static_assert((BM + BN) % THREADS == 0, "scale copies must split evenly over the threads");
+  static_assert(BM * A_ROW % (16 * THREADS) == 0 && BN * kRowBytes % (16 * THREADS) == 0,
+                "code copies must split evenly over the threads");
+  static_assert(!A8 || BM <= 128, "FP8 A: a tile's A bytes (BM * k) must stay below 2^32 for k <= 2^24");
   static_assert(WGM == 2, "the fp32 epilogue stages the tile in two halves by wave row");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles of whole 32x32 MFMA blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -110,30 +144,32 @@ struct TileBases {
   const uint8_t* b_s;
 };
 
+template <class C>
 __device__ __forceinline__ TileBases tile_bases(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                                 const RowRange& ar, int n0) {
-  const int64_t kb = args.k / 2, ks = args.k / 32;
-  return {args.a_q + ar.lo * kb, b_q + n0 * kb, args.a_s + ar.lo * ks, b_s + n0 * ks};
+  const int64_t kb = args.k / 2, ks = args.k / 32, ka = C::A8 ? args.k : kb;
+  return {args.a_q + ar.lo * ka, b_q + n0 * kb, args.a_s + ar.lo * ks, b_s + n0 * ks};
 }
 
 // Buffer resources over the same tile operands, sized to the rows the tile
-// reads (at most 256 rows, so at most 2^31 code bytes for k <= 2^24).
+// reads (at most 256 FP4 rows or 128 FP8 rows, so at most 2^31 code bytes
+// for k <= 2^24).
 struct TileRsrc {
   __amdgpu_buffer_rsrc_t a_q, b_q, a_s, b_s;
 };
 
 template <class C>
 __device__ __forceinline__ TileRsrc tile_rsrc(const TileBases& tb, const RowRange& ar, int n0, int n, int k) {
-  const uint32_t kb = k / 2, ks = k / 32;
+  const uint32_t kb = k / 2, ks = k / 32, ka = C::A8 ? k : kb;
   const uint32_t a_rows = ar.last - ar.lo + 1, b_rows = min(C::BN, n - n0);
-  return {make_rsrc(tb.a_q, a_rows * kb), make_rsrc(tb.b_q, b_rows * kb), make_rsrc(tb.a_s, a_rows * ks),
+  return {make_rsrc(tb.a_q, a_rows * ka), make_rsrc(tb.b_q, b_rows * kb), make_rsrc(tb.a_s, a_rows * ks),
           make_rsrc(tb.b_s, b_rows * ks)};
 }
 
 // Per-thread byte offsets of the copies from the tile bases, at stage 0 / scale
-// group 0.  Copy j of a stage moves slot (j*NWAVES + wave)*64 + lane: row slot/8,
-// logical 16-byte chunk (slot%8) ^ swz(row).  Rows past the operand's end read
-// its last row (never stored).
+// group 0.  Copy j of a stage moves slot (j*NWAVES + wave)*64 + lane: row
+// slot / chunks-per-row, logical 16-byte chunk (slot % chunks-per-row) ^ the
+// row's swizzle.  Rows past the operand's end read its last row (never stored).
 template <class C>
 struct Sources {
   uint32_t a_code[C::A_LOADS];
@@ -151,13 +187,13 @@ __device__ __forceinline__ bool scale_is_b(int j, int w) {
 template <class C>
 __device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t kb = k / 2, ks = k / 32;
+  const uint32_t kb = k / 2, ks = k / 32, ka = C::A8 ? k : kb;
   const int a_rows = ar.last - ar.lo, b_rows = n - 1 - n0;   // largest valid row offsets
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
-    src.a_code[j] = (uint32_t)min(r, a_rows) * kb + lc * 16;
+    const int r = slot >> C::A_SHIFT, lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ a_swz<C>(r);
+    src.a_code[j] = (uint32_t)min(r, a_rows) * ka + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
@@ -180,7 +216,7 @@ __device__ __forceinline__ void copy_codes_a(uint8_t MXFP4_LDS* stage, const Sou
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS base goes to M0
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j)
-    buf2lds_16(tr.a_q, src.a_code[j], kt * kRowBytes, (MXFP4_LDS void*)(stage + (j * C::NWAVES + w) * 64 * 16));
+    buf2lds_16(tr.a_q, src.a_code[j], kt * C::A_ROW, (MXFP4_LDS void*)(stage + (j * C::NWAVES + w) * 64 * 16));
 }
 
 template <class C>
@@ -215,9 +251,10 @@ __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uin
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int lc = (slot & 7) ^ swz(slot >> 3);
+    const int lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ a_swz<C>(slot >> C::A_SHIFT);
     v4i v = {0, 0, 0, 0};
-    if (lc < blocks_left) v = *(const v4i*)(tb.a_q + kt * kRowBytes + src.a_code[j]);
+    // a 32-block is one chunk of FP4 codes or two chunks of FP8 codes
+    if ((lc >> (C::A8 ? 1 : 0)) < blocks_left) v = *(const v4i*)(tb.a_q + kt * C::A_ROW + src.a_code[j]);
     *(v4i MXFP4_LDS*)(stage + slot * 16) = v;
   }
 #pragma unroll
@@ -246,7 +283,7 @@ __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uin
 // Operand fragments of one 64-deep k-step for a wave's (BM/2) x (BN/2) sub-tile.
 template <class C>
 struct Frags {
-  v4i a[C::MI];
+  typename C::AFrag a[C::MI];
   v4i b[C::NI];
 };
 
@@ -300,7 +337,18 @@ __device__ __forceinline__ void read_frags(const uint8_t MXFP4_LDS* stage, Frags
 #pragma unroll
     for (int i = 0; i < MA; ++i) {
       const int r = wm0 + 32 * i + (lane & 31);
-      f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+      if constexpr (C::A8) {
+        // An FP8 operand interleaves 16-element groups: lane half h holds K
+        // [16h, 16h + 16) of the k-step in its first four registers and
+        // [32 + 16h, 48 + 16h) in the last four (measured through the
+        // library with one-hot rows), i.e. chunks 4S + h and 4S + 2 + h.
+        const int h = lane >> 5;
+        const v4i lo = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * S + h) ^ a_swz<C>(r)) << 4));
+        const v4i hi = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * S + 2 + h) ^ a_swz<C>(r)) << 4));
+        f.a[i] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+      }
     }
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
@@ -319,7 +367,10 @@ __device__ __forceinline__ void mma_kstep(const Frags<C>& f, const Scales<C>& sc
     for (int j = 0; j < C::NI; ++j) {
       const int sa = (S < 2) ? sc.a[i].x : sc.a[i].y;
       const int sb = (S < 2) ? sc.b[j].x : sc.b[j].y;
-      acc[i][j] = mfma32_fp4<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
+      if constexpr (C::A8)
+        acc[i][j] = mfma32_fp4_fp8<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
+      else
+        acc[i][j] = mfma32_fp4<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
     }
 }
 
@@ -439,7 +490,7 @@ __device__ __forceinline__ void kstep_slots() {
 
 template <class C, int COPIES, int MA = C::MI>
 __device__ __forceinline__ void kstep_pattern() {
-  kstep_slots<(MA > 0 ? MA + C::NI : 0), COPIES, MA * C::NI, 0>();
+  kstep_slots<(MA > 0 ? MA * C::A_READS + C::NI : 0), COPIES, MA * C::NI, 0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -487,7 +538,7 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
     mma_kstep<C, 3, 0, MA>(fb, sc, acc);
     // the next stage's first fragments go out before the copies (measured ~2 %
     // faster than interleaving them one per MFMA)
-    if constexpr (MA > 0) __builtin_amdgcn_sched_group_barrier(0x100, MA + C::NI, 0);
+    if constexpr (MA > 0) __builtin_amdgcn_sched_group_barrier(0x100, MA * C::A_READS + C::NI, 0);
     kstep_slots<0, (COPY_CODES ? C::CODE_LOADS : 0) + (COPY_SCALES ? C::S_LOADS : 0), MA * C::NI, 0>();
     __builtin_amdgcn_sched_barrier(0);
     // the next stage's scale words replace this stage's once its last MFMAs are issued
@@ -563,7 +614,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
 
   Sources<C> src;
   make_sources<C>(src, ar, n0, args.n, args.k);
-  const TileBases tb = tile_bases(args, b_q, b_s, ar, n0);
+  const TileBases tb = tile_bases<C>(args, b_q, b_s, ar, n0);
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
   if (COPY) {
@@ -700,6 +751,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
 
 using Cfg256 = TileCfg<256, 256, 2, 4>;
 using Cfg128 = TileCfg<128, 128, 2, 2>;
+using CfgW4A8 = TileCfg<128, 256, 2, 4, true>;
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel.
 template <class K>
@@ -761,6 +813,14 @@ hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t str
 
 hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream) {
   return kind == kTile256 ? launch_grouped<Cfg256>(args, stream) : launch_grouped<Cfg128>(args, stream);
+}
+
+hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream) {
+  return launch_dense<CfgW4A8>(args, stream);
+}
+
+hipError_t launch_grouped_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream) {
+  return launch_grouped<CfgW4A8>(args, stream);
 }
 
 }  // namespace mxfp4

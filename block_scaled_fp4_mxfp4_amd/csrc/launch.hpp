@@ -37,6 +37,11 @@ hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t str
 
 hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
 
+// W4A8 tile kernels: A in MXFP8 (a_q is [m, k] E4M3 codes), B in MXFP4;
+// 128 x 256 output tiles.
+hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_grouped_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
+
 // Bandwidth path for m <= 128: 64- or 32-column tiles, K split over the 4 waves
 // of a workgroup and, when splits > 1, over `splits` workgroups per tile with
 // fp32 partials and per-tile arrival counters in `workspace`.

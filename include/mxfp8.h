@@ -1,7 +1,6 @@
 /*
- * mxfp8.h - MXFP8 activations of the MI355X (gfx950) MXFP4 library: the
- * activation format of a W4A8 GEMM, MXFP8 (E4M3) activations times MXFP4
- * (E2M1) weights.
+ * mxfp8.h - MXFP8 activations and W4A8 GEMMs of the MI355X (gfx950) MXFP4
+ * library: MXFP8 (E4M3) activations times MXFP4 (E2M1) weights.
  *
  * The "fp4_quantization" Mojo module page lists quantizers that turn BF16
  * into NVFP4, MXFP4 or MXFP8 with per-block scale factors
@@ -45,6 +44,40 @@ extern "C" {
  * k <= 2^24, rows * k <= 2^40; rows == 0 is a no-op.
  */
 mxfp4_status_t mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q8, void* scales, void* stream);
+
+/*
+ * W4A8 NT GEMM: C[m][n] = sum_k A[m][k] * B[n][k] with A in MXFP8 and B in
+ * MXFP4 ("fp4_quantization" page, block_scaled_matmul: block-scaled matmul
+ * over MXFP4 / MXFP8 operands), on the scaled MFMA with fp32 accumulation; C
+ * is written as BF16 (nearest-even) or fp32 by c_type, as in mxfp4_gemm_nt.
+ * Numerics: with an FP8 operand the gfx950 MFMA sums each aligned group of 8
+ * products along K after aligning them to the group's largest exponent sum E
+ * (E4M3 plus E2M1 exponent) and truncating each toward zero to a multiple of
+ * 2^(E-13) (measured; FP4 x FP4 products always lie on that grid).  So C
+ * differs from the exact sum by less than, per group, (nonzero products) x
+ * 2^(E-13) x the two block scales, plus fp32 accumulation rounding.
+ *   a_q8 [m, k]    E4M3 codes;   a_s [m, k/32] E8M0 bytes;
+ *   b_q  [n, k/2]  packed E2M1;  b_s [n, k/32] E8M0 bytes (layout of mxfp4.h);
+ *   c    [m, n].
+ * k a positive multiple of 32, k <= 2^24; m, n <= 2^30; m == 0 or n == 0 is a
+ * no-op.  Alignment as in mxfp4.h (codes and c 16 bytes; scale arrays 4 bytes
+ * when k % 128 == 0).  The fast path takes k % 512 == 0 with 16-byte aligned
+ * scale arrays.  Codes S.1111.111 (NaN) in A are outside the format: the
+ * result is then unspecified.  No workspace; one kernel launch.
+ */
+mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                  mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * Grouped per-expert W4A8 NT GEMM: as mxfp4_grouped_gemm_nt with A in MXFP8
+ * ([total_m, k] codes, [total_m, k/32] scales), B in MXFP4 ([num_groups, n,
+ * k/2], [num_groups, n, k/32]) and the same device `offsets` contract (every
+ * row index clamped to [0, total_m); a group with no rows writes nothing);
+ * num_groups 1..1024.  No workspace; one kernel launch.
+ */
+mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,
+                                          const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
+                                          mxfp4_out_t c_type, int64_t n, int64_t k, void* stream);
 
 #ifdef __cplusplus
 }

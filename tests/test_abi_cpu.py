@@ -108,6 +108,23 @@ def test_gemm_rejects_bad_arguments_on_host(lib):
     assert call(n=0, b_q=None, b_s=None, c=None) == 0
 
 
+def test_w4a8_rejects_bad_arguments_on_host(lib):
+    f = _fake()
+    assert lib.mxfp8_gemm_w4a8_nt(f, f, f, f, f, 0, 64, 64, 100, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(f, f, f, f, f, 5, 64, 64, 128, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(f, f, f, f, f, 0, -1, 64, 128, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(None, f, f, f, f, 0, 64, 64, 128, None) == 1
+    assert b"a_q is NULL" in lib.mxfp4_last_error()
+    assert lib.mxfp8_gemm_w4a8_nt(_fake(0x1008), f, f, f, f, 0, 64, 64, 128, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(f, _fake(0x1002), f, f, f, 0, 64, 64, 128, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(f, f, f, f, f, 0, 64, 64, (1 << 24) + 32, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt(None, None, f, f, None, 0, 0, 64, 128, None) == 0
+    assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, f, 0, 64, f, 0, 64, 128, None) == 1
+    assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, None, 4, 64, f, 0, 64, 128, None) == 1
+    assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, f, 4, 64, f, 0, 64, 100, None) == 1
+    assert lib.mxfp8_grouped_gemm_w4a8_nt(None, None, f, f, None, 4, 0, None, 0, 64, 128, None) == 0
+
+
 def test_grouped_rejects_bad_arguments_on_host(lib):
     f = _fake()
     assert lib.mxfp4_grouped_gemm_nt(f, f, f, f, f, 0, 64, f, 0, 64, 128, None, 0, None) == 1
