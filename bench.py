@@ -17,6 +17,10 @@ them.  Each timed region is a HIP graph of whole steps replayed on the stream
 the kernels run on, bracketed by events and device synchronisations; one event
 pair per graph replay also gives min / median / max per-step times.
 
+Also reported (`--no-w4a8` skips it): the same workloads with MXFP8 activations
+(W4A8: MXFP8 quantization of A + the MXFP8 x MXFP4 GEMM), against the FP8 MFMA
+peak (a mixed FP8 x FP4 MFMA runs at the FP8 rate) or HBM.
+
 Measured ceilings (probe kernels in the same library) are reported beside the
 published peaks: the FP4 MFMA rate of a kernel that only runs MFMAs, and the
 streaming read rate (`--no-ceilings` skips them).
@@ -28,7 +32,7 @@ measured with events over a region of back-to-back GEMM launches.
 `--only {step,gemm,quantize,quantize_b,copy}` instead runs that work eagerly
 `--steps` times and prints nothing on stdout: the mode used under rocprofv3
 (kernel traces and counter passes; `copy` is the plain device copy that
-calibrates the byte counters).
+calibrates the byte counters; `--w4a8-only` selects the W4A8 kernels).
 """
 from __future__ import annotations
 
@@ -48,6 +52,7 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (an FP8 x FP4 MFMA runs at the FP8 rate)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATION_BYTES = 512 << 20
 COPY_BYTES = 512 << 20        # size of the counter-calibration copy
@@ -62,29 +67,39 @@ def gemm_algorithmic_bytes(m, n, k, out_bytes=2):
     return m * k // 2 + m * k // 32 + n * k // 2 + n * k // 32 + m * n * out_bytes
 
 
-def quant_algorithmic_bytes(rows, k):
-    """BF16 in, packed codes and scale bytes out."""
-    return rows * k * 2 + rows * k // 2 + rows * k // 32
+def quant_algorithmic_bytes(rows, k, code_bytes_per_elem=0.5):
+    """BF16 in, codes (half a byte per element for MXFP4, one for MXFP8) and scale bytes out."""
+    return rows * k * 2 + int(rows * k * code_bytes_per_elem) + rows * k // 32
+
+
+def w4a8_algorithmic_bytes(m, n, k, out_bytes=2):
+    """MXFP8 A (one byte per element + scales), MXFP4 B, C once."""
+    return m * k + m * k // 32 + n * k // 2 + n * k // 32 + m * n * out_bytes
 
 
 class DenseBench:
-    def __init__(self, w: workloads.DenseWorkload, dev):
+    """act = "mxfp4": the MXFP4 path; act = "mxfp8": W4A8 (MXFP8 activations,
+    MXFP4 weights)."""
+
+    def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4"):
         from block_scaled_fp4_mxfp4_amd import binding as B
         self.B = B
         self.w = w
         self.dev = dev
+        self.act = act
+        k_a = w.k if act == "mxfp8" else w.k // 2       # A code bytes per row
         a, b = w.make()
         self.a_cpu, self.b_cpu = a, b
         a_d, b_d = a.to(dev), b.to(dev)
         bq, bs = B.mxfp4_quantize(b_d)            # weight quantized once (not in the step)
         m, n, k = w.m, w.n, w.k
-        per_set = m * k * 2 + m * k // 2 + m * k // 32 + n * k // 2 + n * k // 32 + m * n * 2
+        per_set = m * k * 2 + m * k_a + m * k // 32 + n * k // 2 + n * k // 32 + m * n * 2
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
         self.per_set_bytes = per_set
         self.sets = []
         for _ in range(self.sets_n):
             self.sets.append(dict(
-                a=a_d.clone(), aq=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+                a=a_d.clone(), aq=torch.empty((m, k_a), dtype=torch.uint8, device=dev),
                 as_=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
                 bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
         # the weight-packing kernel gets rotating sources of its own
@@ -98,14 +113,20 @@ class DenseBench:
 
     def quantize(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
+        if self.act == "mxfp8":
+            self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+        else:
+            self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
     def quantize_b(self, i):
         self.B.mxfp4_quantize(self.b_sets[i % len(self.b_sets)], *self.b_out)
 
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"], ws=self.ws)
+        if self.act == "mxfp8":
+            self.B.mxfp8_gemm_w4a8_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+        else:
+            self.B.mxfp4_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"], ws=self.ws)
 
     def step(self, i):
         self.quantize(i)
@@ -153,10 +174,11 @@ class MoEBench:
     """The grouped per-expert workload: routed rows sorted by expert, one
     weight matrix per expert (quantized once), device offsets."""
 
-    def __init__(self, w: workloads.MoEWorkload, dev):
+    def __init__(self, w: workloads.MoEWorkload, dev, act: str = "mxfp4"):
         from block_scaled_fp4_mxfp4_amd import binding as B
         self.B = B
         self.w = w
+        self.act = act
         a, wts, offsets = w.make()
         self.counts = (offsets[1:] - offsets[:-1]).tolist()
         rows, n, k, e = w.total_rows, w.n, w.k, w.experts
@@ -165,12 +187,13 @@ class MoEBench:
         del wts
         wq, ws = wq.view(e, n, k // 2), ws.view(e, n, k // 32)
         off_d = offsets.to(dev)
-        per_set = rows * k * 2 + rows * k // 2 + rows * k // 32 + e * n * k // 2 + e * n * k // 32 + rows * n * 2
+        k_a = k if act == "mxfp8" else k // 2
+        per_set = rows * k * 2 + rows * k_a + rows * k // 32 + e * n * k // 2 + e * n * k // 32 + rows * n * 2
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
         self.sets = []
         for _ in range(self.sets_n):
             self.sets.append(dict(
-                a=a_d.clone(), aq=torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
+                a=a_d.clone(), aq=torch.empty((rows, k_a), dtype=torch.uint8, device=dev),
                 as_=torch.empty((rows, k // 32), dtype=torch.uint8, device=dev),
                 wq=wq.clone(), ws=ws.clone(), off=off_d.clone(),
                 c=torch.empty((rows, n), dtype=torch.bfloat16, device=dev)))
@@ -179,11 +202,17 @@ class MoEBench:
 
     def quantize(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
+        if self.act == "mxfp8":
+            self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+        else:
+            self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
+        if self.act == "mxfp8":
+            self.B.mxfp8_grouped_gemm_w4a8_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
+        else:
+            self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
 
     def step(self, i):
         self.quantize(i)
@@ -194,7 +223,8 @@ class MoEBench:
         w = self.w
         used = sum(1 for c in self.counts if c > 0)
         rows = w.total_rows
-        return (used * (w.n * w.k // 2 + w.n * w.k // 32) + rows * w.k // 2 + rows * w.k // 32
+        a_code = w.k if self.act == "mxfp8" else w.k // 2
+        return (used * (w.n * w.k // 2 + w.n * w.k // 32) + rows * a_code + rows * w.k // 32
                 + rows * w.n * 2)
 
     _graph = staticmethod(DenseBench._graph)
@@ -232,13 +262,17 @@ class Ceilings:
         # Several launches per captured graph, as for the GEMMs: a graph of one
         # launch adds a replay gap of several microseconds to every launch.
         out = {}
-        for label, iters in (("short", 128), ("long", 1024)):
-            self.sets_n = 16
-            flops = self.B.load_library().mxfp4_probe_mfma_flops(self.cus, iters)
-            t = self.timed(lambda i: self.B.mxfp4_probe_mfma(self.seed, self.mfma_out, self.cus, iters),
-                           steps, max(4, steps // 10))
-            out[f"mfma_fp4_tflops_{label}"] = round(flops / (t["mean"] * 1e-3) / 1e12, 1)
-            out[f"mfma_probe_{label}_us"] = round(t["mean"] * 1e3, 2)
+        for fmt, a_fp8 in (("fp4", False), ("w4a8", True)):
+            for label, iters in (("short", 128), ("long", 1024)):
+                if a_fp8:
+                    iters //= 2           # FP8-rate MFMAs take twice as long each
+                self.sets_n = 16
+                flops = self.B.load_library().mxfp4_probe_mfma_flops(self.cus, iters)
+                t = self.timed(lambda i: self.B.mxfp4_probe_mfma(self.seed, self.mfma_out, self.cus, iters,
+                                                                 a_fp8=a_fp8),
+                               steps, max(4, steps // 10))
+                out[f"mfma_{fmt}_tflops_{label}"] = round(flops / (t["mean"] * 1e-3) / 1e12, 1)
+                out[f"mfma_{fmt}_probe_{label}_us"] = round(t["mean"] * 1e3, 2)
         self.sets_n = len(self.small)
         t = self.timed(lambda i: self.B.mxfp4_probe_read(self.small[i % self.sets_n], self.read_out,
                                                           self.read_blocks), steps, max(4, steps // 10))
@@ -317,6 +351,58 @@ def traffic_from_profiles(workload: str):
     return None
 
 
+def measure_w4a8(args, dev, w, us):
+    """W4A8 (MXFP8 activations x MXFP4 weights) on the primary, decode and MoE
+    workloads: step = MXFP8 quantization of A + the W4A8 GEMM."""
+    out = {"dtype": "mxfp8 e4m3 x mxfp4 e2m1, e8m0 block scales, fp32 accumulate, bf16 out"}
+    eprint(f"[bench] W4A8 on {w.name}")
+    b = DenseBench(w, dev, "mxfp8")
+    s = b.timed(b.step, args.steps, args.warmup)
+    g = b.timed(b.gemm, args.steps, args.warmup)
+    q = b.timed(b.quantize, args.steps, args.warmup)
+    tf = w.flops / (g["mean"] * 1e-3) / 1e12
+    qbytes = quant_algorithmic_bytes(w.m, w.k, 1.0)
+    out["prefill"] = {
+        "workload": w.name, "step_us": us(s), "step_tflops": round(w.flops / (s["mean"] * 1e-3) / 1e12, 2),
+        "gemm_us": us(g), "quantize_a_us": us(q),
+        "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+    }
+    eprint(f"[bench] W4A8 {w.name}: step {s['mean']*1e3:.2f} us, gemm {g['mean']*1e3:.2f} us ({tf:.0f} TFLOP/s)")
+    del b
+    if args.secondary != "none":
+        w2 = workloads.DENSE[args.secondary]
+        b2 = DenseBench(w2, dev, "mxfp8")
+        s2 = b2.timed(b2.step, args.steps, args.warmup)
+        g2 = b2.timed(b2.gemm, args.steps, args.warmup)
+        gbytes = w4a8_algorithmic_bytes(w2.m, w2.n, w2.k)
+        gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": w2.name, "step_us": us(s2), "gemm_us": us(g2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)},
+        }
+        eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s)")
+        del b2
+    if args.moe != "none":
+        wm = workloads.ALL[args.moe]
+        mb = MoEBench(wm, dev, "mxfp8")
+        msteps = max(4, args.steps // 10)
+        sm = mb.timed(mb.step, msteps, 2)
+        gm = mb.timed(mb.gemm, msteps, 2)
+        tfm = wm.flops / (gm["mean"] * 1e-3) / 1e12
+        out["moe"] = {
+            "workload": wm.name, "step_us": us(sm), "gemm_us": us(gm),
+            "step_tflops": round(wm.flops / (sm["mean"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tfm, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfm / PEAK_FP8_TFLOPS, 4)},
+        }
+        eprint(f"[bench] W4A8 {wm.name}: grouped gemm {gm['mean']*1e3:.1f} us ({tfm:.0f} TFLOP/s)")
+        del mb
+    return out
+
+
 def run_only(args, dev):
     """Eager launches for profiling runs."""
     if args.only == "copy":
@@ -329,7 +415,8 @@ def run_only(args, dev):
         eprint(f"[bench] {args.steps} copies of {COPY_BYTES} bytes")
         return
     w = workloads.ALL[args.workload]
-    bench = MoEBench(w, dev) if isinstance(w, workloads.MoEWorkload) else DenseBench(w, dev)
+    act = "mxfp8" if args.w4a8_only else "mxfp4"
+    bench = MoEBench(w, dev, act) if isinstance(w, workloads.MoEWorkload) else DenseBench(w, dev, act)
     if not hasattr(bench, args.only):
         eprint(f"'{args.only}' is not a mode of {w.name}")
         sys.exit(2)
@@ -358,6 +445,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy"])
+    ap.add_argument("--w4a8-only", action="store_true",
+                    help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
+    ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -480,12 +570,18 @@ def main():
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
         del mb
 
+    if not args.no_w4a8:
+        result["w4a8"] = measure_w4a8(args, dev, w, us)
+
     if not args.no_ceilings:
         eprint("[bench] measuring MFMA and streaming-read ceilings with the probe kernels")
         cl = Ceilings(dev)
         ceil = cl.measure(args.steps)
         del cl
         ceil["gemm_frac_of_mfma_ceiling"] = round(gemm_tflops / ceil["mfma_fp4_tflops_short"], 4)
+        if "w4a8" in result:
+            ceil["w4a8_gemm_frac_of_mfma_ceiling"] = round(
+                result["w4a8"]["prefill"]["roofline"]["achieved"] / ceil["mfma_w4a8_tflops_short"], 4)
         if "secondary" in result:
             ceil["decode_gemm_frac_of_read_ceiling"] = round(
                 result["secondary"]["roofline"]["achieved"] / ceil["read_gbs_29MB"], 4)

@@ -26,7 +26,7 @@ EXPORTED = (
     "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
-    "mxfp8_gemm_w4a8_nt", "mxfp8_grouped_gemm_w4a8_nt",
+    "mxfp8_gemm_w4a8_nt", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH):
                                               vp, sz, vp]
         lib.mxfp4_probe_mfma.restype = ctypes.c_int
         lib.mxfp4_probe_mfma.argtypes = [vp, vp, i32, i32, vp]
+        lib.mxfp4_probe_mfma_w4a8.restype = ctypes.c_int
+        lib.mxfp4_probe_mfma_w4a8.argtypes = [vp, vp, i32, i32, vp]
         lib.mxfp4_probe_mfma_flops.restype = ctypes.c_double
         lib.mxfp4_probe_mfma_flops.argtypes = [i32, i32]
         lib.mxfp4_probe_read.restype = ctypes.c_int
@@ -252,14 +254,17 @@ def mxfp8_grouped_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, offsets, c=None, out_dtype=t
     return c
 
 
-def mxfp4_probe_mfma(seed: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
-    """Runs the FP4 scaled-MFMA probe (include/mxfp4_probe.h); returns the flops of the call."""
+def mxfp4_probe_mfma(seed: torch.Tensor, out: torch.Tensor, blocks: int, iters: int, stream=None,
+                     a_fp8: bool = False) -> float:
+    """Runs the scaled-MFMA probe (include/mxfp4_probe.h), FP4 x FP4 or, with
+    a_fp8, FP4 x FP8; returns the flops of the call."""
     lib = load_library()
     if seed.numel() * seed.element_size() < PROBE_SEED_BYTES or not seed.is_contiguous():
         raise ValueError(f"seed must be a contiguous device tensor of at least {PROBE_SEED_BYTES} bytes")
     if out.dtype != torch.float32 or out.numel() < blocks * 512 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 device tensor of at least blocks * 512 elements")
-    _check(lib.mxfp4_probe_mfma(_ptr(seed), _ptr(out), blocks, iters, _stream(stream)))
+    fn = lib.mxfp4_probe_mfma_w4a8 if a_fp8 else lib.mxfp4_probe_mfma
+    _check(fn(_ptr(seed), _ptr(out), blocks, iters, _stream(stream)))
     return lib.mxfp4_probe_mfma_flops(blocks, iters)
 
 

@@ -344,14 +344,25 @@ mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, con
   return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile(args, (hipStream_t)stream), "grouped w4a8 gemm launch");
 }
 
-mxfp4_status_t mxfp4_probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream) {
+namespace {
+mxfp4_status_t probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, bool a_fp8, void* stream) {
   if (blocks < 1 || blocks > 65536) return fail(MXFP4_ERR_INVALID_ARG, "blocks must be 1..65536 (got %d)", blocks);
   if (iters < 1 || iters > (1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "iters must be 1..2^24 (got %d)", iters);
   MXFP4_TRY(check_ptr(seed, "seed"));
   MXFP4_TRY(check_ptr(out, "out"));
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
-  return hip_status(mxfp4::launch_probe_mfma(seed, out, blocks, iters, (hipStream_t)stream), "mfma probe launch");
+  return hip_status(mxfp4::launch_probe_mfma(seed, out, blocks, iters, a_fp8, (hipStream_t)stream),
+                    "mfma probe launch");
+}
+}  // namespace
+
+mxfp4_status_t mxfp4_probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream) {
+  return probe_mfma(seed, out, blocks, iters, false, stream);
+}
+
+mxfp4_status_t mxfp4_probe_mfma_w4a8(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream) {
+  return probe_mfma(seed, out, blocks, iters, true, stream);
 }
 
 double mxfp4_probe_mfma_flops(int32_t blocks, int32_t iters) {

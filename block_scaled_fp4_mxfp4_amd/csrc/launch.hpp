@@ -59,7 +59,7 @@ hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream);
 
 // Measurement probes (include/mxfp4_probe.h).
 double probe_mfma_flops(int blocks, int iters);
-hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, hipStream_t stream);
+hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, bool a_fp8, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, int64_t bytes, void* out, int blocks, hipStream_t stream);
 
 }  // namespace mxfp4

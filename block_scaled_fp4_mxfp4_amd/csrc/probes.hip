@@ -1,6 +1,7 @@
 // Measurement probes for the ceilings the GEMM kernels are compared against
-// (declared in include/mxfp4_probe.h): the FP4 scaled-MFMA rate of a kernel
-// that does nothing else, and the read rate of a plain streaming kernel.
+// (declared in include/mxfp4_probe.h): the scaled-MFMA rate of a kernel that
+// does nothing else (FP4 x FP4, or FP4 x FP8 as in the W4A8 GEMM), and the
+// read rate of a plain streaming kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -13,12 +14,20 @@ constexpr int kReadProbeThreads = 256;
 // One wave: a 4 x 2 grid of 32x32 accumulator blocks fed by four A and two B
 // operand registers, the MFMA pattern of one k-step of a tile-kernel wave.
 // After every k-step the operands are rotated and mixed (VALU work that
-// overlaps the matrix core), so consecutive MFMAs see new data.
+// overlaps the matrix core), so consecutive MFMAs see new data.  With A8 the A
+// operands are FP8 (32 bytes per lane; the upper half is derived from the
+// seed's next row) with every NaN pattern masked off (exponent bit 0 cleared).
+template <bool A8>
 __global__ __launch_bounds__(kMfmaProbeThreads) void mfma_probe_kernel(const v4i* seed, float* out, int iters) {
   const int lane = threadIdx.x & 63;
+  constexpr int kNoNaN = (int)0xF7F7F7F7u;
   v4i a[4], b[2];
+  v4i a_hi[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = seed[i * 64 + lane];
+  for (int i = 0; i < 4; ++i) {
+    a[i] = seed[i * 64 + lane];
+    a_hi[i] = seed[((i + 1) & 3) * 64 + lane] ^ (v4i){0x1b873593, 0x6b43a9b5, 0x3c6ef372, 0x0f1bbcdc};
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) b[j] = seed[(4 + j) * 64 + lane];
   const int scale = 0x7f7f7f7f;   // E8M0 byte 127 (2^0) in every byte
@@ -33,9 +42,21 @@ __global__ __launch_bounds__(kMfmaProbeThreads) void mfma_probe_kernel(const v4i
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_fp4<0>(b[j], a[i], acc[i][j], scale, scale);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (A8) {
+          const v8i a8 = {a[i].x & kNoNaN, a[i].y & kNoNaN, a[i].z & kNoNaN, a[i].w & kNoNaN,
+                          a_hi[i].x & kNoNaN, a_hi[i].y & kNoNaN, a_hi[i].z & kNoNaN, a_hi[i].w & kNoNaN};
+          acc[i][j] = mfma32_fp4_fp8<0>(b[j], a8, acc[i][j], scale, scale);
+        } else {
+          acc[i][j] = mfma32_fp4<0>(b[j], a[i], acc[i][j], scale, scale);
+        }
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = (v4i){a[i].y, a[i].z, a[i].w, a[i].x ^ 0x5bd1e995};
+    if constexpr (A8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_hi[i] = (v4i){a_hi[i].w ^ 0x2545f491, a_hi[i].x, a_hi[i].y, a_hi[i].z};
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) b[j] = (v4i){b[j].w, b[j].x ^ 0x27d4eb2f, b[j].y, b[j].z};
   }
@@ -77,10 +98,14 @@ double probe_mfma_flops(int blocks, int iters) {
   return (double)blocks * (kMfmaProbeThreads / 64) * iters * 8 * (2.0 * 32 * 32 * 64);
 }
 
-hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, hipStream_t stream) {
+hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, bool a_fp8, hipStream_t stream) {
   if (!grid_fits(blocks, kMfmaProbeThreads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(kMfmaProbeThreads), 0, stream,
-                     (const v4i*)seed, (float*)out, iters);
+  if (a_fp8)
+    hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3((unsigned)blocks), dim3(kMfmaProbeThreads), 0, stream,
+                       (const v4i*)seed, (float*)out, iters);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3((unsigned)blocks), dim3(kMfmaProbeThreads), 0, stream,
+                       (const v4i*)seed, (float*)out, iters);
   return hipGetLastError();
 }
 

@@ -3,9 +3,9 @@
  *
  * Not part of the GEMM path.  They measure the two ceilings the GEMM kernels
  * are compared against, on the machine at hand, next to the published peaks:
- *   - the rate at which the matrix cores retire block-scaled FP4 MFMAs when a
- *     kernel does nothing else (the clock they sustain under that load sets
- *     it, not only the unit counts);
+ *   - the rate at which the matrix cores retire block-scaled MFMAs (FP4 x FP4,
+ *     or FP4 x FP8 as in the W4A8 GEMM) when a kernel does nothing else (the
+ *     clock they sustain under that load sets it, not only the unit counts);
  *   - the HBM read rate of a plain streaming kernel.
  * Both live in libmxfp4.so and follow the conventions of mxfp4.h: device
  * pointers on the current device, caller-owned buffers, stream-ordered
@@ -40,6 +40,13 @@ extern "C" {
 #define MXFP4_PROBE_SEED_BYTES 6144
 mxfp4_status_t mxfp4_probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream);
 double mxfp4_probe_mfma_flops(int32_t blocks, int32_t iters);
+
+/*
+ * The same probe with the MFMA's second operand in FP8 E4M3 (the W4A8
+ * GEMM's A operand), built from the same seed with NaN codes masked off;
+ * same arguments, same flop count (mxfp4_probe_mfma_flops).
+ */
+mxfp4_status_t mxfp4_probe_mfma_w4a8(const void* seed, void* out, int32_t blocks, int32_t iters, void* stream);
 
 /*
  * Read probe: `blocks` workgroups of 256 threads read `bytes` bytes of `src`

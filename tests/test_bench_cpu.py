@@ -1,7 +1,7 @@
 """Host-side checks of bench.py's contract that need no GPU: it refuses more
 than one GPU with a message and prints nothing on stdout, and its algorithmic
-byte counts match their definitions (each packed code and scale byte of A and
-B once, plus C once; the quantizer's BF16 in, codes and scale bytes out)."""
+byte counts match their definitions (each code and scale byte of A and B once,
+plus C once; the quantizers' BF16 in, codes and scale bytes out)."""
 import os
 import subprocess
 import sys
@@ -30,3 +30,8 @@ def test_algorithmic_bytes():
     assert bench.gemm_algorithmic_bytes(4096, 4096, 4096) == 51_380_224
     # 2 bytes in, 0.5 + 1/32 out per element
     assert bench.quant_algorithmic_bytes(4096, 4096) == 4096 * 4096 * 2 + 4096 * 2048 + 4096 * 128
+    # MXFP8: 2 bytes in, 1 + 1/32 out per element
+    assert bench.quant_algorithmic_bytes(4096, 4096, 1.0) == 4096 * 4096 * 3 + 4096 * 128
+    # W4A8 decode: A one byte per element + scales, B packed + scales, C bf16
+    assert bench.w4a8_algorithmic_bytes(128, 14336, 4096) == (128 * 4096 + 128 * 128 + 14336 * 2048
+                                                               + 14336 * 128 + 128 * 14336 * 2)

@@ -46,3 +46,24 @@ def test_mfma_probe_runs_deterministically():
     assert flops == blocks * 8 * iters * 8 * 2 * 32 * 32 * 64
     assert np.all(np.isfinite(runs[0]))
     assert np.array_equal(runs[0], runs[1])
+
+
+def test_mfma_w4a8_probe_runs_deterministically():
+    """FP8 operands are built with NaN codes masked off, so the sums stay finite."""
+    dev = device()
+    blocks, iters = 8, 16
+    g = torch.Generator().manual_seed(8)
+    seed = torch.randint(0, 256, (B.PROBE_SEED_BYTES,), dtype=torch.uint8, generator=g).to(dev)
+    runs = []
+    for _ in range(2):
+        out = torch.full((blocks * 512,), float("nan"), dtype=torch.float32, device=dev)
+        B.mxfp4_probe_mfma(seed, out, blocks, iters, a_fp8=True)
+        torch.cuda.synchronize()
+        runs.append(to_np(out))
+    assert np.all(np.isfinite(runs[0]))
+    assert np.array_equal(runs[0], runs[1])
+    # the FP8 probe computes something different from the FP4 one on the same seed
+    out4 = torch.empty((blocks * 512,), dtype=torch.float32, device=dev)
+    B.mxfp4_probe_mfma(seed, out4, blocks, iters)
+    torch.cuda.synchronize()
+    assert not np.array_equal(to_np(out4), runs[0])
