@@ -26,7 +26,7 @@ EXPORTED = (
     "mxfp4_gemm_nt_workspace_size", "mxfp4_gemm_nt", "mxfp4_grouped_gemm_nt_workspace_size",
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
-    "mxfp8_gemm_w4a8_nt", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
+    "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -62,6 +62,8 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp8_gemm_w4a8_nt.restype = ctypes.c_int
         lib.mxfp8_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp8_gemm_w4a8_nt_ex.restype = ctypes.c_int
+        lib.mxfp8_gemm_w4a8_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp]
         lib.mxfp8_grouped_gemm_w4a8_nt.restype = ctypes.c_int
         lib.mxfp8_grouped_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64, vp]
         lib.mxfp4_gemm_nt_workspace_size.restype = sz
@@ -223,8 +225,9 @@ def mxfp4_grouped_gemm_nt(a_q, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.b
     return c
 
 
-def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, stream=None):
-    """C[m, n] = A[m, k] . B[n, k]^T with A in MXFP8 ([m, k] codes) and B in MXFP4."""
+def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: str = "auto", stream=None):
+    """C[m, n] = A[m, k] . B[n, k]^T with A in MXFP8 ([m, k] codes) and B in MXFP4.
+    kernel: "auto", "tile128" (128 x 256 tiles) or "stream"."""
     lib = load_library()
     m, k = a_q8.shape
     n = b_q.shape[0]
@@ -233,8 +236,8 @@ def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, st
     _require(b_q, "b_q", torch.uint8, (n, k // 2))
     _require(b_s, "b_s", torch.uint8, (n, k // 32))
     c, code = _out(c, m, n, out_dtype, a_q8.device)
-    _check(lib.mxfp8_gemm_w4a8_nt(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
-                                  _stream(stream)))
+    _check(lib.mxfp8_gemm_w4a8_nt_ex(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
+                                     KERNELS[kernel], _stream(stream)))
     return c
 
 

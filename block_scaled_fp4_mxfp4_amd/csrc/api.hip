@@ -300,9 +300,15 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
 }
 
-mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
-                                  mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+mxfp4_status_t mxfp8_gemm_w4a8_nt_ex(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                     mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel,
+                                     void* stream) {
   MXFP4_TRY(check_gemm_args(a_q8, a_s, b_q, b_s, c, c_type, m, n, k));
+  if (kernel != MXFP4_KERNEL_AUTO && kernel != MXFP4_KERNEL_TILE128 && kernel != MXFP4_KERNEL_STREAM)
+    return fail(MXFP4_ERR_INVALID_ARG, "W4A8 kernels: auto, tile128 or stream (got %d)", (int)kernel);
+  const bool stream_ok = k % 512 == 0 && ((reinterpret_cast<uintptr_t>(a_s) | reinterpret_cast<uintptr_t>(b_s)) & 15) == 0;
+  if (kernel == MXFP4_KERNEL_STREAM && !stream_ok)
+    return fail(MXFP4_ERR_INVALID_ARG, "the stream kernel needs k %% 512 == 0 and 16-byte aligned scale arrays");
   if (m == 0 || n == 0) return MXFP4_OK;
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
@@ -316,7 +322,14 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void*
   args.m = (int)m;
   args.n = (int)n;
   args.k = (int)k;
+  const bool use_stream = kernel == MXFP4_KERNEL_STREAM || (kernel == MXFP4_KERNEL_AUTO && m <= 128 && stream_ok);
+  if (use_stream) return hip_status(mxfp4::launch_gemm_w4a8_stream(args, (hipStream_t)stream), "w4a8 gemm launch");
   return hip_status(mxfp4::launch_gemm_w4a8_tile(args, (hipStream_t)stream), "w4a8 gemm launch");
+}
+
+mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                  mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  return mxfp8_gemm_w4a8_nt_ex(a_q8, a_s, b_q, b_s, c, c_type, m, n, k, MXFP4_KERNEL_AUTO, stream);
 }
 
 mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,

@@ -30,9 +30,19 @@
 //    FP4 on both sides, B fed as the first operand so lane l holds output row
 //    l % 32 and runs of four consecutive columns.
 //
+// W4A8 (MXFP8 activations): A rows carry one code byte per element, 256 bytes
+// per stage in sixteen chunks at c ^ (r & 15), and the MFMA takes A as an FP8
+// operand (lane half h holds K [16h, 16h + 16) and [32 + 16h, 48 + 16h) of its
+// k-step).  Doubling A's share of the ring limits the M tile to 64 rows; for
+// M up to 128 the two M tiles of one 64-column slice are dispatched next to
+// each other on the same XCD, so the second reads the weight slice from that
+// XCD's L2 rather than HBM.
+//
 // Requirements (checked by the host): k % 512 == 0 and 16-byte aligned scale
 // arrays.  Rows past M and columns past N read a clamped valid row and are
 // never stored.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -45,28 +55,35 @@ constexpr int kBN = 64;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-template <int MB_, int NP_>
+template <int MB_, int NP_, bool A8_ = false>
 struct StreamCfg {
   static constexpr int MB = MB_, NP = NP_;
+  static constexpr bool A8 = A8_;                          // A in FP8 E4M3 (W4A8)
   static constexpr int BM = 32 * MB;
   static constexpr int ROWS = BM + kBN;                   // A rows, then B rows
-  static constexpr int STAGE = ROWS * kRowBytes;
+  static constexpr int A_ROW = A8 ? 2 * kRowBytes : kRowBytes;
+  static constexpr int A_SHIFT = A8 ? 4 : 3;               // log2 of the 16-byte chunks in an A row
+  static constexpr int A_BYTES = BM * A_ROW;
+  static constexpr int A_SLOTS = A_BYTES / 16;
+  static constexpr int STAGE = A_BYTES + kBN * kRowBytes;
   static constexpr int SCALES = kThreads * 16;            // one 16-byte piece per thread (rows >= ROWS: padding)
   static constexpr int PAIR = 2 * STAGE + SCALES;
-  static constexpr int CODE_LOADS = ROWS * 8 / kThreads;  // 16-byte copies per thread per stage
+  static constexpr int CODE_LOADS = STAGE / 16 / kThreads;  // 16-byte copies per thread per stage
   static constexpr int PAIR_LOADS = 2 * CODE_LOADS + 1;   // vector-memory ops per thread per pair
   static constexpr int XCH = 4 * MB * 8 * 64 * 16;        // reduce-scatter exchange: 4 waves x all units
   static constexpr int C_PITCH = kBN * 2 + 16;             // bf16 output tile row, padded
   static constexpr int C_TILE = BM * C_PITCH;              // placed after the exchange area
   static constexpr int LDS = (NP * PAIR > XCH + C_TILE) ? NP * PAIR : XCH + C_TILE;
-  static_assert(ROWS * 8 % kThreads == 0, "code copies must split evenly over the threads");
+  static_assert(STAGE % (16 * kThreads) == 0, "code copies must split evenly over the threads");
+  static_assert(A_SLOTS % 64 == 0, "a wave's copy instruction lies wholly in A or in B");
   static_assert(ROWS <= kThreads, "one scale piece per row");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert((NP - 2) * PAIR_LOADS <= 63, "vmcnt range");
 };
 
 // Per-thread copy sources.  Copy j of a stage moves slot (j*4 + wave)*64 + lane:
-// row slot/8, logical 16-byte chunk (slot%8) ^ swz(row); pointers are at pair 0.
+// A slots first (row slot / chunks-per-row, logical chunk (slot % chunks) ^ the
+// row's swizzle), then B slots; pointers are at pair 0.
 template <class C>
 struct Sources {
   const uint8_t* code[C::CODE_LOADS];
@@ -76,13 +93,19 @@ struct Sources {
 template <class C>
 __device__ __forceinline__ void make_sources(Sources<C>& src, const GemmArgs& args, int m0, int n0) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t kb = args.k / 2, ks = args.k / 32;
+  const int64_t kb = args.k / 2, ks = args.k / 32, ka = C::A8 ? args.k : kb;
 #pragma unroll
   for (int j = 0; j < C::CODE_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
-    src.code[j] = (r < C::BM) ? args.a_q + min(m0 + r, args.m - 1) * kb + lc * 16
-                              : args.b_q + min(n0 + r - C::BM, args.n - 1) * kb + lc * 16;
+    if (slot < C::A_SLOTS) {
+      const int r = slot >> C::A_SHIFT;
+      const int lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ (C::A8 ? (r & 15) : swz(r));
+      src.code[j] = args.a_q + min(m0 + r, args.m - 1) * ka + lc * 16;
+    } else {
+      const int bs = slot - C::A_SLOTS;
+      const int r = bs >> 3, lc = (bs & 7) ^ swz(r);
+      src.code[j] = args.b_q + min(n0 + r, args.n - 1) * kb + lc * 16;
+    }
   }
   const int r = threadIdx.x;   // padding rows re-read A's row m0 into the unused pieces
   src.scale = (r < C::BM || r >= C::ROWS) ? args.a_s + min(m0 + (r < C::BM ? r : 0), args.m - 1) * ks
@@ -96,9 +119,12 @@ __device__ __forceinline__ void copy_pair(uint8_t MXFP4_LDS* buf, const Sources<
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < C::CODE_LOADS; ++j)
-      g2lds_16(src.code[j] + (2 * p + s) * kRowBytes,
+    for (int j = 0; j < C::CODE_LOADS; ++j) {
+      // wave-uniform: A_SLOTS is a multiple of 64
+      const int stride = ((j * 4 + w) * 64 < C::A_SLOTS) ? C::A_ROW : kRowBytes;
+      g2lds_16(src.code[j] + (2 * p + s) * stride,
                (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
+    }
   g2lds_16(src.scale + p * 16, (MXFP4_LDS void*)(buf + 2 * C::STAGE + w * 64 * 16));
 }
 
@@ -121,7 +147,7 @@ __device__ __forceinline__ void barrier_lds() {
 // Fragments and scale bytes of one wave's k-step of one stage.
 template <class C>
 struct Step {
-  v4i a[C::MB];
+  typename std::conditional<C::A8, v8i, v4i>::type a[C::MB];
   v4i b[2];
   int sa[C::MB];
   int sb[2];
@@ -135,14 +161,22 @@ __device__ __forceinline__ void read_step(const uint8_t MXFP4_LDS* buf, int s, i
 #pragma unroll
   for (int i = 0; i < C::MB; ++i) {
     const int r = 32 * i + (lane & 31);
-    st.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    if constexpr (C::A8) {
+      // FP8 fragment of k-step w: chunks 4w + h and 4w + 2 + h (h = lane half)
+      const int h = lane >> 5;
+      const v4i lo = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * w + h) ^ (r & 15)) << 4));
+      const v4i hi = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * w + 2 + h) ^ (r & 15)) << 4));
+      st.a[i] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+      st.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
+    }
     st.sa[i] = scales[r * 16];
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = C::BM + 32 * j + (lane & 31);
-    st.b[j] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
-    st.sb[j] = scales[r * 16];
+    const int r = 32 * j + (lane & 31);
+    st.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
+    st.sb[j] = scales[(C::BM + r) * 16];
   }
 }
 
@@ -151,14 +185,32 @@ __device__ __forceinline__ void mma_step(const Step<C>& st, v16f (&acc)[C::MB][2
 #pragma unroll
   for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_fp4<0>(st.b[j], st.a[i], acc[i][j], st.sb[j], st.sa[i]);
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (C::A8)
+        acc[i][j] = mfma32_fp4_fp8<0>(st.b[j], st.a[i], acc[i][j], st.sb[j], st.sa[i]);
+      else
+        acc[i][j] = mfma32_fp4<0>(st.b[j], st.a[i], acc[i][j], st.sb[j], st.sa[i]);
+    }
+}
+
+// Workgroup -> (M tile, 64-column slice).  Workgroups go to the 8 XCDs round
+// robin (b % 8), so in every run of 8 * tiles_m workgroups the M tiles of one
+// slice share an XCD (its L2 serves the slice's weights to all but the first)
+// and are dispatched close together; workgroups past the last slice exit.
+__device__ __forceinline__ bool stream_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int run = 8 * tiles_m;
+  const int g = b / run, r = b - g * run;
+  tm = r >> 3;
+  tn = g * 8 + (r & 7);
+  return tn < tiles_n;
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, int tiles_n) {
+__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  int tm, tn;
+  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
   const int m0 = tm * C::BM, n0 = tn * kBN;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
@@ -284,9 +336,9 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int tiles_n = (args.n + kBN - 1) / kBN;
   const int tiles_m = (args.m + C::BM - 1) / C::BM;
-  const int64_t blocks = (int64_t)tiles_m * tiles_n;
+  const int64_t blocks = (int64_t)tiles_m * ((tiles_n + 7) / 8) * 8;   // whole runs of 8 * tiles_m
   if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), C::LDS, stream, args, tiles_n);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), C::LDS, stream, args, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -302,6 +354,13 @@ hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream) {
   if (args.m <= 32) return launch_cfg<StreamCfg<1, 5>>(args, stream);
   if (args.m <= 64) return launch_cfg<StreamCfg<2, 4>>(args, stream);
   return launch_cfg<StreamCfg<4, 3>>(args, stream);
+}
+
+hipError_t launch_gemm_w4a8_stream(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (!stream_supported(args)) return hipErrorInvalidValue;
+  if (args.m <= 32) return launch_cfg<StreamCfg<1, 4, true>>(args, stream);
+  return launch_cfg<StreamCfg<2, 3, true>>(args, stream);
 }
 
 }  // namespace mxfp4

@@ -56,6 +56,8 @@ hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
 // k % 512 == 0 and 16-byte aligned scale arrays (hipErrorInvalidValue otherwise).
 bool stream_supported(const GemmArgs& args);
 hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream);
+// The same with A in MXFP8 (W4A8); M tiles of 32 or 64 rows.
+hipError_t launch_gemm_w4a8_stream(const GemmArgs& args, hipStream_t stream);
 
 // Measurement probes (include/mxfp4_probe.h).
 double probe_mfma_flops(int blocks, int iters);

@@ -61,12 +61,27 @@ mxfp4_status_t mxfp8_quantize(const void* x_bf16, int64_t rows, int64_t k, void*
  *   c    [m, n].
  * k a positive multiple of 32, k <= 2^24; m, n <= 2^30; m == 0 or n == 0 is a
  * no-op.  Alignment as in mxfp4.h (codes and c 16 bytes; scale arrays 4 bytes
- * when k % 128 == 0).  The fast path takes k % 512 == 0 with 16-byte aligned
+ * when k % 128 == 0).  The fast paths take k % 512 == 0 with 16-byte aligned
  * scale arrays.  Codes S.1111.111 (NaN) in A are outside the format: the
  * result is then unspecified.  No workspace; one kernel launch.
  */
 mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
                                   mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * mxfp8_gemm_w4a8_nt with the kernel forced, for tests and tuning:
+ *   MXFP4_KERNEL_AUTO     the choice mxfp8_gemm_w4a8_nt makes: the streaming
+ *                         kernel for m <= 128 when k % 512 == 0 and both scale
+ *                         arrays are 16-byte aligned, else the tile kernel;
+ *   MXFP4_KERNEL_TILE128  128 x 256 output tiles, LDS-staged scaled MFMA;
+ *   MXFP4_KERNEL_STREAM   weight-streaming kernel (32- or 64-row M tiles, 64
+ *                         columns, whole K); needs k % 512 == 0 and 16-byte
+ *                         aligned scale arrays, any m.
+ * Other kernel ids are rejected (MXFP4_ERR_INVALID_ARG).
+ */
+mxfp4_status_t mxfp8_gemm_w4a8_nt_ex(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                     mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel,
+                                     void* stream);
 
 /*
  * Grouped per-expert W4A8 NT GEMM: as mxfp4_grouped_gemm_nt with A in MXFP8

@@ -119,6 +119,12 @@ def test_w4a8_rejects_bad_arguments_on_host(lib):
     assert lib.mxfp8_gemm_w4a8_nt(f, _fake(0x1002), f, f, f, 0, 64, 64, 128, None) == 1
     assert lib.mxfp8_gemm_w4a8_nt(f, f, f, f, f, 0, 64, 64, (1 << 24) + 32, None) == 1
     assert lib.mxfp8_gemm_w4a8_nt(None, None, f, f, None, 0, 0, 64, 128, None) == 0
+    # forced kernels: only auto (0), tile128 (2) and stream (4); stream needs k % 512 == 0
+    assert lib.mxfp8_gemm_w4a8_nt_ex(f, f, f, f, f, 0, 64, 64, 512, 1, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt_ex(f, f, f, f, f, 0, 64, 64, 512, 3, None) == 1
+    assert lib.mxfp8_gemm_w4a8_nt_ex(f, f, f, f, f, 0, 64, 64, 256, 4, None) == 1
+    assert b"stream kernel needs" in lib.mxfp4_last_error()
+    assert lib.mxfp8_gemm_w4a8_nt_ex(None, None, f, f, None, 0, 0, 64, 512, 4, None) == 0
     assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, f, 0, 64, f, 0, 64, 128, None) == 1
     assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, None, 4, 64, f, 0, 64, 128, None) == 1
     assert lib.mxfp8_grouped_gemm_w4a8_nt(f, f, f, f, f, 4, 64, f, 0, 64, 100, None) == 1

@@ -22,7 +22,7 @@ Bars:
     <= 1e-2 against the float64 oracle;
   * bf16 output: the nearest-even rounding of the kernel's own fp32 result;
   * outputs poisoned with NaN bytes beforehand, a canary row after C untouched;
-  * grouped: bit-identical to the dense kernel on each expert's row slice.
+  * grouped: bit-identical to the dense tile kernel on each expert's row slice.
 """
 import numpy as np
 import pytest
@@ -41,6 +41,12 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(128, 256, 512), (300, 520, 1024), (513, 263, 2048), (130, 900, 1056), (64, 64, 32),
           (257, 129, 4096), (1, 300, 96), (200, 300, 512), (40, 256, 512), (80, 256, 512),
           (100, 256, 512), (129, 1000, 1536)]
+# streaming kernel (k % 512 == 0): 32- and 64-row M tiles, several M tiles sharing a
+# 64-column slice, ragged M / N, a column count that is not a multiple of 8 slices
+STREAM_SHAPES = [(1, 64, 512), (17, 200, 1024), (32, 1000, 4096), (33, 70, 512), (64, 129, 8192),
+                 (100, 512, 2048), (128, 320, 4096), (129, 66, 1536), (300, 190, 1024), (128, 14336, 512)]
+CASES = [("tile128", s) for s in SHAPES] + [("stream", s) for s in STREAM_SHAPES]
+CASE_IDS = [f"{kern}-{m}x{n}x{k}" for kern, (m, n, k) in CASES]
 
 
 def _fp8_exponents(q8):
@@ -88,10 +94,10 @@ def _check_general(got32, got16, c64, tol):
         assert np.array_equal(got16, oracle.f64_to_bf16_bits(got32.astype(np.float64)))
 
 
-def _gemm(aq, as_, bq, bs, dev, out_dtype, m, n):
+def _gemm(aq, as_, bq, bs, dev, out_dtype, m, n, kernel="auto"):
     c_all = poisoned((m + 1, n), out_dtype, dev, 0xFF)        # NaN poison, one canary row after
     c = c_all[:m]
-    mxfp8_gemm_w4a8_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), c=c)
+    mxfp8_gemm_w4a8_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), c=c, kernel=kernel)
     torch.cuda.synchronize()
     assert np.all(to_np(c_all[m:].view(torch.uint8)) == 0xFF), "write past the end of C"
     return to_np(c.float()) if out_dtype == torch.float32 else to_np(c.view(torch.int16)).view(np.uint16)
@@ -106,8 +112,8 @@ def _exact_fp8_codes(rows, k, seed, top_field):
     return mag | sign
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
-def test_w4a8_exact_regime_bitexact(shape):
+@pytest.mark.parametrize("kernel,shape", CASES, ids=CASE_IDS)
+def test_w4a8_exact_regime_bitexact(kernel, shape):
     """A values are multiples of 1/8 with exponents 0 .. 3 and B values multiples
     of 1/2 up to 6 (exponents 0 .. 2): every exponent sum is at most 5, so the
     group grid is at most 2**-8 and every product (a multiple of 1/16 before
@@ -118,7 +124,7 @@ def test_w4a8_exact_regime_bitexact(shape):
     fp32, so the result is bit-exact."""
     dev = device()
     m, n, k = shape
-    log(f"w4a8 exact regime {shape}")
+    log(f"w4a8 exact regime {kernel} {shape}")
     bq, _ = random_codes(n, k, 2)
     if k <= 2048:
         aq = _exact_fp8_codes(m, k, 1, 8)
@@ -130,7 +136,7 @@ def test_w4a8_exact_regime_bitexact(shape):
         as_ = np.full((m, k // 32), 127, np.uint8)
         bs = np.full((n, k // 32), 127, np.uint8)
     ref = oracle.gemm_w4a8_nt(aq, as_, bq, bs)
-    got = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n)
+    got = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n, kernel)
     assert np.array_equal(got, ref.astype(np.float32))
 
 
@@ -172,15 +178,15 @@ def _quantized_operands(m, n, k, seed):
     return aq, as_, bq, bs
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
-def test_w4a8_quantized_gaussian(shape):
+@pytest.mark.parametrize("kernel,shape", CASES, ids=CASE_IDS)
+def test_w4a8_quantized_gaussian(kernel, shape):
     dev = device()
     m, n, k = shape
-    log(f"w4a8 gaussian {shape}")
+    log(f"w4a8 gaussian {kernel} {shape}")
     aq, as_, bq, bs = _quantized_operands(m, n, k, m + n)
     c64 = oracle.gemm_w4a8_nt(aq, as_, bq, bs)
-    got32 = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n)
-    got16 = _gemm(aq, as_, bq, bs, dev, torch.bfloat16, m, n)
+    got32 = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n, kernel)
+    got16 = _gemm(aq, as_, bq, bs, dev, torch.bfloat16, m, n, kernel)
     _check_general(got32, got16, c64, w4a8_tolerance(aq, as_, bq, bs))
 
 
@@ -221,6 +227,22 @@ def test_w4a8_long_k():
     ref = oracle.gemm_w4a8_nt(aq, as_, bq, bs)
     got = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n)
     assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_w4a8_kernels_agree_and_stream_rejects_unsupported_k():
+    """The tile and streaming kernels give results within each other's bound on
+    one decode-like shape, and the streaming kernel refuses k % 512 != 0."""
+    dev = device()
+    m, n, k = 128, 640, 4096
+    aq, as_, bq, bs = _quantized_operands(m, n, k, 77)
+    tile = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n, "tile128")
+    strm = _gemm(aq, as_, bq, bs, dev, torch.float32, m, n, "stream")
+    tol = w4a8_tolerance(aq, as_, bq, bs)
+    assert np.all(np.abs(tile.astype(np.float64) - strm) <= 2 * tol)
+    from block_scaled_fp4_mxfp4_amd import MXFP4Error
+    aq2, as2, bq2, bs2 = (upload(t, dev) for t in _quantized_operands(8, 64, 1056, 3))
+    with pytest.raises(MXFP4Error):
+        mxfp8_gemm_w4a8_nt(aq2, as2, bq2, bs2, kernel="stream")
 
 
 def test_w4a8_empty_problems():
@@ -303,7 +325,7 @@ def test_grouped_w4a8_bitexact_vs_dense_per_group(pattern):
         if hi == lo:
             continue
         a_s_g = d_as[lo:hi] if k % 128 == 0 else d_as[lo:hi].clone()
-        dense = mxfp8_gemm_w4a8_nt(d_aq[lo:hi], a_s_g, d_wq[g], d_ws[g], out_dtype=torch.float32)
+        dense = mxfp8_gemm_w4a8_nt(d_aq[lo:hi], a_s_g, d_wq[g], d_ws[g], out_dtype=torch.float32, kernel="tile128")
         torch.cuda.synchronize()
         assert np.array_equal(got[lo:hi], to_np(dense)), f"group {g}"
         ref = oracle.gemm_w4a8_nt(aq[lo:hi], as_[lo:hi], wq[g], ws[g])
@@ -374,8 +396,10 @@ def test_grouped_w4a8_malformed_offsets_stay_in_bounds():
     torch.cuda.synchronize()
     assert torch.all(c_all[total:].view(torch.uint8) == 0xFF), "write past the end of C"
     got = to_np(c)
-    g0 = to_np(mxfp8_gemm_w4a8_nt(d_aq[0:120], d_as[0:120], d_wq[0], d_ws[0], out_dtype=torch.float32))
-    g2 = to_np(mxfp8_gemm_w4a8_nt(d_aq[80:300], d_as[80:300], d_wq[2], d_ws[2], out_dtype=torch.float32))
+    g0 = to_np(mxfp8_gemm_w4a8_nt(d_aq[0:120], d_as[0:120], d_wq[0], d_ws[0], out_dtype=torch.float32,
+                                  kernel="tile128"))
+    g2 = to_np(mxfp8_gemm_w4a8_nt(d_aq[80:300], d_as[80:300], d_wq[2], d_ws[2], out_dtype=torch.float32,
+                                  kernel="tile128"))
     torch.cuda.synchronize()
     assert np.array_equal(got[0:80], g0[0:80])
     assert np.array_equal(got[120:300], g2[40:220])
