@@ -93,6 +93,20 @@ class MoEWorkload:
     w_sigma: float = 0.02
     extra: dict = field(default_factory=dict)
 
+    def logits(self) -> torch.Tensor:
+        """Router logits as float32 [tokens, experts]: z + beta drawn in float64
+        from the seeds routing() uses, rounded once to float32 (the input of the
+        on-device top-k routing)."""
+        gb = torch.Generator(device="cpu").manual_seed(self.seed + ROLE_ROUTE_BIAS)
+        beta = torch.randn((self.experts,), generator=gb, dtype=torch.float64) * self.bias_sigma
+        gz = torch.Generator(device="cpu").manual_seed(self.seed + ROLE_ROUTE_NOISE)
+        z = torch.randn((self.tokens, self.experts), generator=gz, dtype=torch.float64)
+        return (z + beta[None, :]).to(torch.float32)
+
+    def tokens_bf16(self) -> torch.Tensor:
+        """The layer's token activations [tokens, K], BF16 ~N(0, 1)."""
+        return gaussian_bf16((self.tokens, self.k), 1.0, self.seed + ROLE_A)
+
     def routing(self):
         """Top-k experts per token from Gaussian logits plus a per-expert bias.
 
