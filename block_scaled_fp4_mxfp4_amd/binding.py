@@ -1,4 +1,4 @@
-"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h and include/mxfp8.h).
+"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h, include/mxfp8.h and include/mxfp4_moe.h).
 
 Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the computation runs in the library's kernels.  The
@@ -27,6 +27,8 @@ EXPORTED = (
     "mxfp4_grouped_gemm_nt", "mxfp4_gemm_nt_ex_workspace_size", "mxfp4_gemm_nt_ex",
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
     "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
+    "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
+    "mxfp4_moe_combine",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -88,6 +90,15 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_probe_mfma_flops.argtypes = [i32, i32]
         lib.mxfp4_probe_read.restype = ctypes.c_int
         lib.mxfp4_probe_read.argtypes = [vp, i64, vp, i32, vp]
+        lib.mxfp4_moe_route.restype = ctypes.c_int
+        lib.mxfp4_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        lib.mxfp4_moe_permute.restype = ctypes.c_int
+        lib.mxfp4_moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+        for name in ("mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter"):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = [vp, i64, i64, i32, vp, i64, vp, vp, vp]
+        lib.mxfp4_moe_combine.restype = ctypes.c_int
+        lib.mxfp4_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, ctypes.c_int, vp]
         _lib = lib
         return lib
 
@@ -281,3 +292,89 @@ def mxfp4_probe_read(src: torch.Tensor, out: torch.Tensor, blocks: int, stream=N
         raise ValueError("out must be a contiguous 32-bit integer device tensor of at least blocks * 256 elements")
     _check(lib.mxfp4_probe_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(stream)))
     return nbytes
+
+
+# ---------------------------------------------------------------------------
+# MoE steps (include/mxfp4_moe.h)
+# ---------------------------------------------------------------------------
+
+def mxfp4_moe_route(logits: torch.Tensor, top_k: int, ids=None, weights=None, stream=None):
+    """logits float32 [tokens, experts] -> (ids int32 [tokens, top_k], weights float32 [tokens, top_k])."""
+    lib = load_library()
+    tokens, experts = logits.shape
+    if ids is None:
+        ids = torch.empty((tokens, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((tokens, top_k), dtype=torch.float32, device=logits.device)
+    _require(logits, "logits", torch.float32, (tokens, experts))
+    _require(ids, "ids", torch.int32, (tokens, top_k))
+    _require(weights, "weights", torch.float32, (tokens, top_k))
+    _check(lib.mxfp4_moe_route(_ptr(logits), tokens, experts, top_k, _ptr(ids), _ptr(weights), _stream(stream)))
+    return ids, weights
+
+
+def mxfp4_moe_permute(ids: torch.Tensor, experts: int, offsets=None, row_token=None, token_rows=None,
+                      stream=None):
+    """ids int32 [tokens, top_k] -> (offsets int32 [experts + 1], row_token int32 [tokens * top_k],
+    token_rows int32 [tokens, top_k])."""
+    lib = load_library()
+    tokens, top_k = ids.shape
+    dev = ids.device
+    if offsets is None:
+        offsets = torch.empty((experts + 1,), dtype=torch.int32, device=dev)
+    if row_token is None:
+        row_token = torch.empty((tokens * top_k,), dtype=torch.int32, device=dev)
+    if token_rows is None:
+        token_rows = torch.empty((tokens, top_k), dtype=torch.int32, device=dev)
+    _require(ids, "ids", torch.int32, (tokens, top_k))
+    _require(offsets, "offsets", torch.int32, (experts + 1,))
+    _require(row_token, "row_token", torch.int32, (tokens * top_k,))
+    _require(token_rows, "token_rows", torch.int32, (tokens, top_k))
+    _check(lib.mxfp4_moe_permute(_ptr(ids), tokens, experts, top_k, _ptr(offsets), _ptr(row_token),
+                                 _ptr(token_rows), _stream(stream)))
+    return offsets, row_token, token_rows
+
+
+def _quantize_scatter(fn, x, token_rows, total_rows, q, scales, code_cols, stream):
+    tokens, k = x.shape
+    top_k = token_rows.shape[1]
+    if q is None:
+        q = torch.empty((total_rows, code_cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((total_rows, k // 32), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (tokens, k))
+    _require(token_rows, "token_rows", torch.int32, (tokens, top_k))
+    _require(q, "q", torch.uint8, (total_rows, code_cols))
+    _require(scales, "scales", torch.uint8, (total_rows, k // 32))
+    _check(fn(_ptr(x), tokens, k, top_k, _ptr(token_rows), total_rows, _ptr(q), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def mxfp4_moe_quantize_scatter(x, token_rows, total_rows: int, q=None, scales=None, stream=None):
+    """x bf16 [tokens, k] -> MXFP4 rows (q uint8 [total_rows, k/2], scales uint8 [total_rows, k/32]);
+    row token_rows[t, j] receives token t's quantized row."""
+    lib = load_library()
+    return _quantize_scatter(lib.mxfp4_moe_quantize_scatter, x, token_rows, total_rows, q, scales,
+                             x.shape[1] // 2, stream)
+
+
+def mxfp8_moe_quantize_scatter(x, token_rows, total_rows: int, q8=None, scales=None, stream=None):
+    """The same with MXFP8 rows (q8 uint8 [total_rows, k])."""
+    lib = load_library()
+    return _quantize_scatter(lib.mxfp8_moe_quantize_scatter, x, token_rows, total_rows, q8, scales,
+                             x.shape[1], stream)
+
+
+def mxfp4_moe_combine(y, token_rows, weights, out=None, out_dtype=torch.bfloat16, stream=None):
+    """y bf16 [total_rows, n], token_rows int32 [tokens, top_k], weights float32 [tokens, top_k]
+    -> out [tokens, n] = sum_j weights[t, j] * y[token_rows[t, j]] (bf16 or float32)."""
+    lib = load_library()
+    total_rows, n = y.shape
+    tokens, top_k = token_rows.shape
+    _require(y, "y", torch.bfloat16, (total_rows, n))
+    _require(token_rows, "token_rows", torch.int32, (tokens, top_k))
+    _require(weights, "weights", torch.float32, (tokens, top_k))
+    out, code = _out(out, tokens, n, out_dtype, y.device)
+    _check(lib.mxfp4_moe_combine(_ptr(y), total_rows, n, _ptr(token_rows), _ptr(weights), tokens, top_k,
+                                 _ptr(out), code, _stream(stream)))
+    return out

@@ -1,5 +1,6 @@
 // C ABI of the MXFP4 library: argument checks, per-shape kernel choice, launches.
-// Entry points and their contracts are documented in include/mxfp4.h and include/mxfp8.h.
+// Entry points and their contracts are documented in include/mxfp4.h, include/mxfp8.h and
+// include/mxfp4_moe.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -10,6 +11,7 @@
 #include "../../include/mxfp4.h"
 #include "../../include/mxfp4_probe.h"
 #include "../../include/mxfp8.h"
+#include "../../include/mxfp4_moe.h"
 #include "launch.hpp"
 
 namespace {
@@ -393,6 +395,102 @@ mxfp4_status_t mxfp4_probe_read(const void* src, int64_t bytes, void* out, int32
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_probe_read(src, bytes, out, blocks, (hipStream_t)stream), "read probe launch");
+}
+
+// ---------------------------------------------------------------------------
+// MoE steps (include/mxfp4_moe.h)
+// ---------------------------------------------------------------------------
+
+mxfp4_status_t mxfp4_moe_route(const float* logits, int64_t tokens, int32_t experts, int32_t top_k,
+                               int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (tokens < 0 || tokens > ((int64_t)1 << 28)) return fail(MXFP4_ERR_INVALID_ARG, "tokens must be 0..2^28 (got %lld)", (long long)tokens);
+  if (experts < 1 || experts > mxfp4::kMoeMaxRouteExperts)
+    return fail(MXFP4_ERR_INVALID_ARG, "experts must be 1..%d (got %d)", mxfp4::kMoeMaxRouteExperts, experts);
+  if (top_k < 1 || top_k > mxfp4::kMoeMaxTopK || top_k > experts)
+    return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..min(%d, experts) (got %d)", mxfp4::kMoeMaxTopK, top_k);
+  if (tokens == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(logits, "logits", 4));
+  MXFP4_TRY(check_ptr(topk_ids, "topk_ids", 4));
+  MXFP4_TRY(check_ptr(topk_weights, "topk_weights", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_moe_route(logits, (int)tokens, experts, top_k, topk_ids, topk_weights,
+                                            (hipStream_t)stream), "moe route launch");
+}
+
+mxfp4_status_t mxfp4_moe_permute(const int32_t* topk_ids, int64_t tokens, int32_t experts, int32_t top_k,
+                                 int32_t* offsets, int32_t* row_token, int32_t* token_rows, void* stream) {
+  if (tokens < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative tokens");
+  if (experts < 1 || experts > 1024) return fail(MXFP4_ERR_INVALID_ARG, "experts must be 1..1024 (got %d)", experts);
+  if (top_k < 1 || top_k > 256) return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..256 (got %d)", top_k);
+  if (tokens > ((int64_t)1 << 30) / top_k) return fail(MXFP4_ERR_INVALID_ARG, "tokens * top_k too large");
+  MXFP4_TRY(check_ptr(offsets, "offsets", 4));
+  if (tokens > 0) {
+    MXFP4_TRY(check_ptr(topk_ids, "topk_ids", 4));
+    MXFP4_TRY(check_ptr(row_token, "row_token", 4));
+    MXFP4_TRY(check_ptr(token_rows, "token_rows", 4));
+  }
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_moe_permute(topk_ids, (int)(tokens * top_k), top_k, experts, offsets, row_token,
+                                              token_rows, (hipStream_t)stream), "moe permute launch");
+}
+
+namespace {
+mxfp4_status_t moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                    const int32_t* token_rows, int64_t total_rows, void* q, void* scales,
+                                    bool fp8, void* stream) {
+  if (tokens < 0 || total_rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  MXFP4_TRY(check_k(k));
+  if (top_k < 1 || top_k > 256) return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..256 (got %d)", top_k);
+  if (tokens >= ((int64_t)1 << 31) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "tokens * k / 32 too large");
+  if (total_rows >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "total_rows too large");
+  if (tokens == 0 || total_rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(token_rows, "token_rows", 4));
+  MXFP4_TRY(check_ptr(q, fp8 ? "q8" : "q", fp8 ? 8 : 4));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_moe_quantize_scatter(x_bf16, (int)tokens, (int)k, top_k, token_rows,
+                                                       (int)total_rows, q, scales, fp8, (hipStream_t)stream,
+                                                       dev.num_cus), "moe quantize-scatter launch");
+}
+}  // namespace
+
+mxfp4_status_t mxfp4_moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                          const int32_t* token_rows, int64_t total_rows, void* q, void* scales,
+                                          void* stream) {
+  return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q, scales, false, stream);
+}
+
+mxfp4_status_t mxfp8_moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                          const int32_t* token_rows, int64_t total_rows, void* q8, void* scales,
+                                          void* stream) {
+  return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q8, scales, true, stream);
+}
+
+mxfp4_status_t mxfp4_moe_combine(const void* y_bf16, int64_t total_rows, int64_t n, const int32_t* token_rows,
+                                 const float* topk_weights, int64_t tokens, int32_t top_k, void* out,
+                                 mxfp4_out_t out_type, void* stream) {
+  if (tokens < 0 || total_rows < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "n too large");
+  if (total_rows >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "total_rows too large");
+  if (top_k < 1 || top_k > 256) return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..256 (got %d)", top_k);
+  if (out_type != MXFP4_OUT_BF16 && out_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)out_type);
+  if (n > 0 && tokens >= ((int64_t)1 << 31) / ((n + 7) / 8)) return fail(MXFP4_ERR_INVALID_ARG, "tokens * ceil(n / 8) too large");
+  if (tokens == 0 || n == 0) return MXFP4_OK;
+  const bool f32 = out_type == MXFP4_OUT_F32;
+  MXFP4_TRY(check_ptr(y_bf16, "y_bf16", 2));
+  MXFP4_TRY(check_ptr(token_rows, "token_rows", 4));
+  MXFP4_TRY(check_ptr(topk_weights, "topk_weights", 4));
+  MXFP4_TRY(check_ptr(out, "out", f32 ? 4 : 2));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  const bool vec = n % 8 == 0 && aligned16(y_bf16) && aligned16(out);
+  return hip_status(mxfp4::launch_moe_combine(y_bf16, (int)total_rows, (int)n, token_rows, topk_weights, (int)tokens,
+                                              top_k, out, f32, vec, (hipStream_t)stream), "moe combine launch");
 }
 
 }  // extern "C"

@@ -59,6 +59,19 @@ hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream);
 // The same with A in MXFP8 (W4A8); M tiles of 32 or 64 rows.
 hipError_t launch_gemm_w4a8_stream(const GemmArgs& args, hipStream_t stream);
 
+// MoE steps around the grouped GEMM (include/mxfp4_moe.h).
+constexpr int kMoeMaxTopK = 8;          // routing: experts per token
+constexpr int kMoeMaxRouteExperts = 256;  // routing: four logits per lane of a wave
+hipError_t launch_moe_route(const float* logits, int tokens, int experts, int top_k, int32_t* ids, float* weights,
+                            hipStream_t stream);
+hipError_t launch_moe_permute(const int32_t* ids, int n, int top_k, int experts, int32_t* offsets,
+                              int32_t* row_token, int32_t* token_rows, hipStream_t stream);
+hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top_k, const int32_t* token_rows,
+                                       int total_rows, void* q, void* scales, bool fp8, hipStream_t stream,
+                                       int num_cus);
+hipError_t launch_moe_combine(const void* y, int total_rows, int n, const int32_t* token_rows, const float* weights,
+                              int tokens, int top_k, void* out, bool f32_out, bool vec, hipStream_t stream);
+
 // Measurement probes (include/mxfp4_probe.h).
 double probe_mfma_flops(int blocks, int iters);
 hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, bool a_fp8, hipStream_t stream);

@@ -172,3 +172,43 @@ def test_probes_reject_bad_arguments_on_host(lib):
     # 8 waves x iters x 8 MFMAs of 2*32*32*64 flops per workgroup
     assert lib.mxfp4_probe_mfma_flops(3, 5) == 3 * 8 * 5 * 8 * 131072
     assert lib.mxfp4_probe_mfma_flops(0, 5) == 0.0
+
+
+def test_moe_entry_points_reject_bad_arguments_on_host(lib):
+    f = _fake
+    # routing: experts 1..256, top_k 1..min(8, experts), tokens 0..2^28
+    assert lib.mxfp4_moe_route(f(), 4, 0, 1, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(f(), 4, 257, 1, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(f(), 4, 64, 9, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(f(), 4, 2, 3, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(f(), -1, 64, 4, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(f(), (1 << 28) + 1, 64, 4, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(None, 4, 64, 4, f(), f(), None) == 1
+    assert b"logits is NULL" in lib.mxfp4_last_error()
+    assert lib.mxfp4_moe_route(f(0x1002), 4, 64, 4, f(), f(), None) == 1
+    assert lib.mxfp4_moe_route(None, 0, 64, 4, None, None, None) == 0          # no tokens: no-op
+    # permutation: experts 1..1024, top_k 1..256, tokens * top_k <= 2^30
+    assert lib.mxfp4_moe_permute(f(), 4, 0, 2, f(), f(), f(), None) == 1
+    assert lib.mxfp4_moe_permute(f(), 4, 1025, 2, f(), f(), f(), None) == 1
+    assert lib.mxfp4_moe_permute(f(), 4, 8, 0, f(), f(), f(), None) == 1
+    assert lib.mxfp4_moe_permute(f(), 1 << 29, 8, 4, f(), f(), f(), None) == 1
+    assert lib.mxfp4_moe_permute(f(), 4, 8, 2, None, f(), f(), None) == 1
+    assert lib.mxfp4_moe_permute(f(), 4, 8, 2, f(), None, f(), None) == 1
+    # scatter-quantize: k a positive multiple of 32, top_k 1..256, alignment of x and q
+    for fn in (lib.mxfp4_moe_quantize_scatter, lib.mxfp8_moe_quantize_scatter):
+        assert fn(f(), 4, 48, 2, f(), 8, f(), f(), None) == 1
+        assert fn(f(), 4, 64, 0, f(), 8, f(), f(), None) == 1
+        assert fn(f(), -1, 64, 2, f(), 8, f(), f(), None) == 1
+        assert fn(f(), 4, 64, 2, f(), 1 << 31, f(), f(), None) == 1
+        assert fn(f(0x1008), 4, 64, 2, f(), 8, f(), f(), None) == 1
+        assert fn(None, 0, 64, 2, None, 8, None, None, None) == 0              # no tokens: no-op
+        assert fn(None, 4, 64, 2, None, 0, None, None, None) == 0              # no rows: no-op
+    assert lib.mxfp4_moe_quantize_scatter(f(), 4, 64, 2, f(), 8, f(0x1002), f(), None) == 1
+    assert lib.mxfp8_moe_quantize_scatter(f(), 4, 64, 2, f(), 8, f(0x1004), f(), None) == 1
+    # combine: output type, sizes, alignment
+    assert lib.mxfp4_moe_combine(f(), 8, 64, f(), f(), 4, 2, f(), 7, None) == 1
+    assert lib.mxfp4_moe_combine(f(), 8, -1, f(), f(), 4, 2, f(), 0, None) == 1
+    assert lib.mxfp4_moe_combine(f(), 8, 64, f(), f(), 4, 0, f(), 0, None) == 1
+    assert lib.mxfp4_moe_combine(f(0x1001), 8, 64, f(), f(), 4, 2, f(), 0, None) == 1
+    assert lib.mxfp4_moe_combine(f(), 8, 64, f(), f(), 4, 2, f(0x1002), 1, None) == 1
+    assert lib.mxfp4_moe_combine(None, 8, 64, None, None, 0, 2, None, 0, None) == 0   # no tokens: no-op
