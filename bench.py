@@ -9,7 +9,11 @@ One step = the whole path over one batch of synthetic input:
 Primary workload: M = N = K = 4096 (TFLOP/s, 2*M*N*K per step).
 Secondary workload: decode M=128, N=14336, K=4096 (achieved HBM GB/s).
 Also reported: the grouped MoE layer (8192 tokens, top-4 of 64 experts,
-N=2816, K=4096) in TFLOP/s and GB/s.
+N=2816, K=4096) in TFLOP/s and GB/s, and the same layer run wholly on the
+device (`moe_layer`: top-k routing of the router logits, the expert-sorted
+permutation, MXFP4 quantization scattered into the routed rows, the grouped
+GEMM and the weighted combine), each step's time against its algorithmic
+bytes.
 
 Inputs are resident in HBM before timing.  Steps rotate over enough copies of
 the inputs (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot serve
@@ -231,6 +235,120 @@ class MoEBench:
     timed = DenseBench.timed
 
 
+class MoELayerBench:
+    """The whole MoE layer on the device: top-k routing of the router logits,
+    the expert-sorted permutation, MXFP4 quantization scattered into the routed
+    rows, the grouped GEMM over the expert weights (quantized once), and the
+    weighted combine back to tokens."""
+
+    def __init__(self, w: workloads.MoEWorkload, dev):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        self.w = w
+        t, e, kk, n, k = w.tokens, w.experts, w.top_k, w.n, w.k
+        rows = t * kk
+        x_d = w.tokens_bf16().to(dev)
+        lg_d = w.logits().to(dev)
+        wts = workloads.gaussian_bf16((e * n, k), w.w_sigma, w.seed + workloads.ROLE_B)
+        wq, ws = B.mxfp4_quantize(wts.to(dev))
+        del wts
+        wq, ws = wq.view(e, n, k // 2), ws.view(e, n, k // 32)
+        per_set = (t * k * 2 + t * e * 4 + rows * (k // 2 + k // 32) + e * n * (k // 2 + k // 32)
+                   + rows * n * 2 + t * n * 2)
+        self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
+        self.sets = []
+        for _ in range(self.sets_n):
+            self.sets.append(dict(
+                x=x_d.clone(), lg=lg_d.clone(), wq=wq.clone(), ws=ws.clone(),
+                ids=torch.empty((t, kk), dtype=torch.int32, device=dev),
+                gate=torch.empty((t, kk), dtype=torch.float32, device=dev),
+                off=torch.empty((e + 1,), dtype=torch.int32, device=dev),
+                rt=torch.empty((rows,), dtype=torch.int32, device=dev),
+                tr=torch.empty((t, kk), dtype=torch.int32, device=dev),
+                aq=torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
+                as_=torch.empty((rows, k // 32), dtype=torch.uint8, device=dev),
+                y=torch.empty((rows, n), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((t, n), dtype=torch.bfloat16, device=dev)))
+        del x_d, lg_d, wq, ws
+        for i in range(self.sets_n):   # every set holds a complete layer's intermediates before timing
+            self.step(i)
+        torch.cuda.synchronize()
+        self.counts = torch.diff(self.sets[0]["off"]).cpu().tolist()
+
+    def route(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_moe_route(s["lg"], self.w.top_k, s["ids"], s["gate"])
+
+    def permute(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_moe_permute(s["ids"], self.w.experts, s["off"], s["rt"], s["tr"])
+
+    def scatter(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_moe_quantize_scatter(s["x"], s["tr"], self.w.total_rows, s["aq"], s["as_"])
+
+    def gemm(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["y"])
+
+    def combine(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_moe_combine(s["y"], s["tr"], s["gate"], out=s["out"])
+
+    def step(self, i):
+        self.route(i)
+        self.permute(i)
+        self.scatter(i)
+        self.gemm(i)
+        self.combine(i)
+
+    def algorithmic_bytes(self):
+        """What each step must move once: inputs read, outputs written."""
+        w = self.w
+        t, e, kk, n, k, rows = w.tokens, w.experts, w.top_k, w.n, w.k, w.total_rows
+        used = sum(1 for c in self.counts if c > 0)
+        return {
+            "route": t * e * 4 + rows * 8,
+            "permute": rows * 4 + (e + 1) * 4 + rows * 8,
+            "scatter": t * k * 2 + rows * (k // 2 + k // 32) + rows * 4,
+            "gemm": used * n * (k // 2 + k // 32) + rows * (k // 2 + k // 32) + rows * n * 2,
+            "combine": rows * n * 2 + rows * 8 + t * n * 2,
+        }
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+
+def measure_moe_layer(args, dev, us):
+    wm = workloads.ALL[args.moe]
+    eprint(f"[bench] building inputs for the on-device MoE layer of {wm.name}")
+    lb = MoELayerBench(wm, dev)
+    # 16 launches per captured graph: a graph of only the two rotation sets would add a
+    # replay gap of several microseconds to each of the short routing and permutation launches
+    msteps = max(32, args.steps // 2)
+    period = 16
+    nbytes = lb.algorithmic_bytes()
+    out = {"workload": wm.name, "steps": msteps, "rotating_input_sets": lb.sets_n,
+           "step": "route + permute + scatter-quantize + grouped mxfp4 GEMM + combine",
+           "rows_per_expert": {"min": min(lb.counts), "max": max(lb.counts),
+                               "empty": sum(c == 0 for c in lb.counts)}}
+    st = lb.timed(lb.step, msteps, 2, period=period)
+    out["step_us"] = us(st)
+    out["step_tflops"] = round(wm.flops / (st["mean"] * 1e-3) / 1e12, 2)
+    kern = {}
+    for name in ("route", "permute", "scatter", "gemm", "combine"):
+        tk = lb.timed(getattr(lb, name), msteps, 2, period=period)
+        gbs = nbytes[name] / (tk["mean"] * 1e-3) / 1e9
+        kern[name] = {"us": us(tk), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    kern["gemm"]["tflops"] = round(wm.flops / (kern["gemm"]["us"]["mean"] * 1e-6) / 1e12, 2)
+    out["kernels"] = kern
+    eprint(f"[bench] MoE layer {wm.name}: step {st['mean']*1e3:.1f} us; " +
+           ", ".join(f"{k} {v['us']['mean']:.1f} us" for k, v in kern.items()))
+    del lb
+    return out
+
+
 class Ceilings:
     """Measured ceilings on this GPU (include/mxfp4_probe.h), reported next to the
     published peaks: the FP4 scaled-MFMA rate of a kernel that only runs MFMAs
@@ -416,7 +534,17 @@ def run_only(args, dev):
         return
     w = workloads.ALL[args.workload]
     act = "mxfp8" if args.w4a8_only else "mxfp4"
-    bench = MoEBench(w, dev, act) if isinstance(w, workloads.MoEWorkload) else DenseBench(w, dev, act)
+    if args.only in ("route", "permute", "scatter", "combine", "layer"):
+        if not isinstance(w, workloads.MoEWorkload):
+            eprint(f"--only {args.only} needs the MoE workload")
+            sys.exit(2)
+        bench = MoELayerBench(w, dev)
+        if args.only == "layer":
+            args.only = "step"
+    elif isinstance(w, workloads.MoEWorkload):
+        bench = MoEBench(w, dev, act)
+    else:
+        bench = DenseBench(w, dev, act)
     if not hasattr(bench, args.only):
         eprint(f"'{args.only}' is not a mode of {w.name}")
         sys.exit(2)
@@ -444,7 +572,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
-    ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy"])
+    ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy",
+                                       "route", "permute", "scatter", "combine", "layer"],
+                    help="eager launches for profiling; route/permute/scatter/combine/layer run the "
+                         "on-device MoE layer's steps (layer = all five) on the MoE workload")
+    ap.add_argument("--no-moe-layer", action="store_true", help="skip the on-device MoE layer measurement")
     ap.add_argument("--w4a8-only", action="store_true",
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
@@ -569,6 +701,9 @@ def main():
         eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
         del mb
+
+    if args.moe != "none" and not args.no_moe_layer:
+        result["moe_layer"] = measure_moe_layer(args, dev, us)
 
     if not args.no_w4a8:
         result["w4a8"] = measure_w4a8(args, dev, w, us)

@@ -443,7 +443,7 @@ mxfp4_status_t moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t 
   if (tokens < 0 || total_rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
   MXFP4_TRY(check_k(k));
   if (top_k < 1 || top_k > 256) return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..256 (got %d)", top_k);
-  if (tokens >= ((int64_t)1 << 31) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "tokens * k / 32 too large");
+  if (tokens > ((int64_t)1 << 30) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "tokens * k / 32 too large");
   if (total_rows >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "total_rows too large");
   if (tokens == 0 || total_rows == 0) return MXFP4_OK;
   MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));

@@ -9,15 +9,17 @@
 // grouped_quantize_dynamic_scaled_fp4_async).  The steps here produce that
 // layout on the device and fold the expert outputs back per token:
 //
-//  route:    one wave per token; lane e holds logits e, e + 64, e + 128,
-//            e + 192.  Each of the k rounds takes a wave-wide max of a 64-bit
-//            key (order-preserving integer image of the logit, then 0xFFFF - id
-//            so equal logits go to the lower id) and removes the winner.  Gate
-//            weights are the softmax of the k selected logits in fp32.
-//  permute:  one workgroup per expert scans the flat id array twice: a count
-//            of the kept ids below its expert (its segment's first row), then
-//            a block-wide prefix scan in (token, slot) order that numbers its
-//            rows.  Rows of an expert are therefore in ascending token order
+//  route:    four lanes per token, each keeping the top k of a contiguous
+//            quarter of the experts in registers: each logit, mapped to an
+//            order-preserving integer key, enters or climbs the descending list
+//            only when strictly greater, so equal logits go to the lower id.
+//            Two DPP quad merges combine the quarters.  Gate weights are the
+//            softmax of the k selected logits in fp32.
+//  permute:  one workgroup per expert stages the flat id array in LDS
+//            (chunks of 32768, one padded row of 32 consecutive entries per
+//            thread of 1024): a count of the kept ids below its expert gives its
+//            segment's first row, then one block-wide prefix scan per chunk in
+//            (token, slot) order numbers its rows.  Rows of an expert are therefore in ascending token order
 //            and the result does not depend on timing.  One extra workgroup
 //            writes the segment end, marks dropped entries and clears the
 //            unused row slots.
@@ -38,7 +40,7 @@ namespace {
 // routing
 // ---------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 256;   // 4 tokens per workgroup, one wave each
+constexpr int kRouteThreads = 256;   // four lanes per token, 64 tokens per workgroup
 
 // Order-preserving map of a float onto uint32 (negative zero taken as +0, so
 // the two zeros tie as they compare equal).
@@ -52,60 +54,113 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// One candidate into the descending top-K list.  Keys carry the logit's order
+// key above a presence bit (an empty slot is 0, below every logit), so the
+// first K candidates always fill the list.  A candidate passes an entry only
+// when strictly greater: candidates offered in ascending expert id lose ties
+// to the entries already held.  Branch-free over the K slots; every
+// comparison uses the old list.
+template <int K>
+__device__ __forceinline__ void topk_insert(uint64_t (&bk)[K], int (&bi)[K], uint64_t c, int e) {
+  bool gt[K];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off);
-    v = umax64(v, ((uint64_t)hi << 32) | lo);
-  }
-  return v;
-}
-
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int tokens,
-                                                             int experts, int top_k, int32_t* __restrict__ ids,
-                                                             float* __restrict__ weights) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
-  if (t >= tokens) return;   // wave-uniform
-  const float* row = logits + (int64_t)t * experts;
-  // key 0 = no candidate; every real candidate is at least 0xFFFF - 255
-  uint64_t cand[4];
+  for (int j = 0; j < K; ++j) gt[j] = c > bk[j];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    cand[i] = (e < experts) ? (((uint64_t)order_key(row[e]) << 16) | (uint64_t)(0xFFFF - e)) : 0;
-  }
-  int sel_id[kMoeMaxTopK];
-  float sel_val[kMoeMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMoeMaxTopK; ++j) {
-    sel_id[j] = 0;
-    sel_val[j] = 0.0f;
-    if (j < top_k) {
-      const uint64_t best = wave_max_u64(umax64(umax64(cand[0], cand[1]), umax64(cand[2], cand[3])));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (cand[i] == best) cand[i] = 0;   // ids are distinct, so only the winner matches
-      sel_id[j] = 0xFFFF - (int)(best & 0xFFFFu);
-      sel_val[j] = key_value((uint32_t)(best >> 16));
+  for (int j = K - 1; j >= 0; --j) {
+    if (gt[j]) {
+      const bool shift = j > 0 && gt[j > 0 ? j - 1 : 0];
+      bk[j] = shift ? bk[j > 0 ? j - 1 : 0] : c;
+      bi[j] = shift ? bi[j > 0 ? j - 1 : 0] : e;
     }
   }
+}
+
+// Merge the partner lane's top-K list (DPP quad permute CTRL) into this one.
+// The lane whose bit MASK is clear holds the lower expert ids; both lanes end
+// with that lane's list as the base and the other's entries inserted into it
+// in order, so ties keep going to the lower id.
+template <int K, int CTRL, int MASK>
+__device__ __forceinline__ void topk_merge(uint64_t (&bk)[K], int (&bi)[K], int lane) {
+  uint64_t ok[K];
+  int oi[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)bk[j], CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(bk[j] >> 32), CTRL, 0xF, 0xF, false);
+    ok[j] = ((uint64_t)hi << 32) | lo;
+    oi[j] = __builtin_amdgcn_mov_dpp(bi[j], CTRL, 0xF, 0xF, false);
+  }
+  const bool upper = (lane & MASK) != 0;
+  uint64_t base_k[K], add_k[K];
+  int base_i[K], add_i[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    base_k[j] = upper ? ok[j] : bk[j];
+    base_i[j] = upper ? oi[j] : bi[j];
+    add_k[j] = upper ? bk[j] : ok[j];
+    add_i[j] = upper ? bi[j] : oi[j];
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) topk_insert<K>(base_k, base_i, add_k[j], add_i[j]);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    bk[j] = base_k[j];
+    bi[j] = base_i[j];
+  }
+}
+
+// Four lanes (one quad) per token: lane L takes the contiguous experts
+// [L * span, (L + 1) * span), keeps their top K in registers, then two quad
+// merges (lanes 0+1 and 2+3, then the pairs) give every lane the token's top K.
+template <int K, bool VEC>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int tokens,
+                                                             int experts, int32_t* __restrict__ ids,
+                                                             float* __restrict__ weights) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRouteThreads / 4) + (threadIdx.x >> 2);
+  if (t >= tokens) return;   // uniform over the quad
+  const int q = lane & 3;
+  const int span = (experts + 3) >> 2;
+  const int e_lo = min(q * span, experts), e_hi = min(e_lo + span, experts);
+  const float* row = logits + (int64_t)t * experts;
+  uint64_t bk[K];
+  int bi[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    bk[j] = 0;
+    bi[j] = 0;
+  }
+  if (VEC) {   // experts % 16 == 0 and 16-byte aligned rows: span is a multiple of 4
+    for (int e0 = e_lo; e0 < e_hi; e0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 f = (e0 + 4 * c < e_hi) ? *(const float4*)(row + e0 + 4 * c) : make_float4(0, 0, 0, 0);
+        v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (e0 + u < e_hi) topk_insert<K>(bk, bi, ((uint64_t)order_key(v[u]) << 1) | 1u, e0 + u);
+    }
+  } else {
+    for (int e = e_lo; e < e_hi; ++e) topk_insert<K>(bk, bi, ((uint64_t)order_key(row[e]) << 1) | 1u, e);
+  }
+  topk_merge<K, 0xB1, 1>(bk, bi, lane);   // quad lanes 1,0,3,2
+  topk_merge<K, 0x4E, 2>(bk, bi, lane);   // quad lanes 2,3,0,1
   // softmax of the selected logits; the first is the largest
-  float ex[kMoeMaxTopK];
+  const float top = key_value((uint32_t)(bk[0] >> 1));
+  float ex[K];
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kMoeMaxTopK; ++j) {
-    ex[j] = (j < top_k) ? expf(sel_val[j] - sel_val[0]) : 0.0f;
+  for (int j = 0; j < K; ++j) {
+    ex[j] = expf(key_value((uint32_t)(bk[j] >> 1)) - top);
     sum += ex[j];
   }
 #pragma unroll
-  for (int j = 0; j < kMoeMaxTopK; ++j) {
-    if (j < top_k && lane == j) {
-      ids[(int64_t)t * top_k + j] = sel_id[j];
-      weights[(int64_t)t * top_k + j] = ex[j] / sum;
+  for (int j = 0; j < K; ++j) {
+    if ((j & 3) == q) {
+      ids[(int64_t)t * K + j] = bi[j];
+      weights[(int64_t)t * K + j] = ex[j] / sum;
     }
   }
 }
@@ -114,8 +169,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
 // permutation
 // ---------------------------------------------------------------------------
 
-constexpr int kPermThreads = 256;
-constexpr int kPermPerThread = 4;
+constexpr int kPermThreads = 1024;                   // 16 waves: 4 per SIMD hide the LDS and memory latency
+constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermSeg = 32;                         // consecutive entries per thread per chunk
+constexpr int kPermChunk = kPermThreads * kPermSeg;  // entries per chunk (32768)
+constexpr int kPermPitch = kPermSeg + 1;             // LDS words per thread segment (odd: no bank conflicts)
+constexpr int kPermLds = kPermThreads * kPermPitch * 4;
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -132,68 +191,115 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  const int total = red[0] + red[1] + red[2] + red[3];
+  int total = 0;
+#pragma unroll
+  for (int q = 0; q < kPermWaves; ++q) total += red[q];
   __syncthreads();
   return total;
 }
 
+// Ids [c0, c0 + 32768) into LDS, entry c0 + i at word (i / 32) * 33 + i % 32,
+// so thread t's 32 consecutive entries form one padded row; entries past n
+// read as -1 (dropped).  Coalesced 16-byte loads, eight in flight per thread.
+template <bool VEC>
+__device__ __forceinline__ void stage_chunk(const int32_t* __restrict__ ids, int n, int c0, int* lds) {
+  __syncthreads();   // the previous chunk is no longer read
+  for (int q0 = 0; q0 < kPermChunk / 4; q0 += 8 * kPermThreads) {
+    int4 x[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int i = c0 + 4 * (q0 + a * kPermThreads + threadIdx.x);
+      if (VEC && i + 4 <= n) {
+        x[a] = *(const int4*)(ids + i);
+      } else {
+        x[a].x = (i < n) ? ids[i] : -1;
+        x[a].y = (i + 1 < n) ? ids[i + 1] : -1;
+        x[a].z = (i + 2 < n) ? ids[i + 2] : -1;
+        x[a].w = (i + 3 < n) ? ids[i + 3] : -1;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int l = 4 * (q0 + a * kPermThreads + threadIdx.x);   // 4 entries, all in one thread row
+      int* dst = lds + (l / kPermSeg) * kPermPitch + (l % kPermSeg);
+      dst[0] = x[a].x; dst[1] = x[a].y; dst[2] = x[a].z; dst[3] = x[a].w;
+    }
+  }
+  __syncthreads();
+}
+
+// Workgroup e < experts numbers the rows of expert e; workgroup `experts`
+// writes the segment end, marks dropped entries and clears unused row slots.
+// The ids go through LDS in chunks of 32768; when all of them fit one chunk
+// they are staged once and serve both passes.
+template <bool VEC>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n, int top_k,
                                                               int experts, int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_token,
                                                               int32_t* __restrict__ token_rows) {
-  __shared__ int red[4];
-  __shared__ int wave_tot[2][4];
-  const int e = blockIdx.x;   // e == experts: segment end, dropped entries, unused rows
+  extern __shared__ __attribute__((aligned(16))) int lds_ids[];
+  __shared__ int red[kPermWaves];
+  __shared__ int wave_tot[2][kPermWaves];
+  const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool one_chunk = n <= kPermChunk;
+  const int* mine_row = lds_ids + tid * kPermPitch;
 
-  // kept ids below e: the first row of expert e (for e == experts, all kept ids)
+  // kept ids below e: the first row of expert e (for e == experts, every kept id)
   int cnt = 0;
-  for (int i = tid; i < n; i += kPermThreads) {
-    const int v = ids[i];
-    cnt += (v >= 0 && v < e) ? 1 : 0;
+  for (int c0 = 0; c0 < n; c0 += kPermChunk) {
+    stage_chunk<VEC>(ids, n, c0, lds_ids);
+#pragma unroll 8
+    for (int u = 0; u < kPermSeg; ++u) {
+      const int v = mine_row[u];
+      cnt += (v >= 0 && v < e) ? 1 : 0;
+    }
   }
   const int base = block_sum(cnt, red);
   if (tid == 0) offsets[e] = base;
 
   if (e == experts) {
     for (int i = base + tid; i < n; i += kPermThreads) row_token[i] = -1;
-    for (int i = tid; i < n; i += kPermThreads) {
-      const int v = ids[i];
-      if (v < 0 || v >= experts) token_rows[i] = -1;
+    for (int c0 = 0; c0 < n; c0 += kPermChunk) {
+      if (!one_chunk) stage_chunk<VEC>(ids, n, c0, lds_ids);
+      const int i0 = c0 + tid * kPermSeg;
+#pragma unroll 8
+      for (int u = 0; u < kPermSeg; ++u) {
+        const int v = mine_row[u];
+        if ((v < 0 || v >= experts) && i0 + u < n) token_rows[i0 + u] = -1;
+      }
     }
     return;
   }
 
-  // number the entries of expert e in flat (token, slot) order
+  // number the entries of expert e in flat (token, slot) order: one block-wide
+  // exclusive scan of per-thread match counts per chunk
   int run = base;
   int parity = 0;
-  for (int c0 = 0; c0 < n; c0 += kPermThreads * kPermPerThread, parity ^= 1) {
-    int v[kPermPerThread];
+  for (int c0 = 0; c0 < n; c0 += kPermChunk, parity ^= 1) {
+    if (!one_chunk) stage_chunk<VEC>(ids, n, c0, lds_ids);
     int mine = 0;
-#pragma unroll
-    for (int u = 0; u < kPermPerThread; ++u) {
-      const int i = c0 + tid * kPermPerThread + u;
-      v[u] = (i < n) ? ids[i] : -1;
-      mine += (v[u] == e) ? 1 : 0;
-    }
+#pragma unroll 8
+    for (int u = 0; u < kPermSeg; ++u) mine += (mine_row[u] == e) ? 1 : 0;
     const int incl = wave_incl_scan(mine, lane);
     if (lane == 63) wave_tot[parity][w] = incl;
     __syncthreads();   // the other parity's totals are not rewritten before the next barrier
     int before = 0, total = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kPermWaves; ++q) {
       const int tq = wave_tot[parity][q];
       before += (q < w) ? tq : 0;
       total += tq;
     }
-    int r = run + before + incl - mine;
-#pragma unroll
-    for (int u = 0; u < kPermPerThread; ++u) {
-      if (v[u] == e) {
-        const int i = c0 + tid * kPermPerThread + u;
-        row_token[r] = i / top_k;
-        token_rows[i] = r;
-        ++r;
+    if (mine > 0) {
+      int r = run + before + incl - mine;
+      const int i0 = c0 + tid * kPermSeg;
+      for (int u = 0; u < kPermSeg; ++u) {
+        if (mine_row[u] == e) {
+          row_token[r] = (i0 + u) / top_k;
+          token_rows[i0 + u] = r;
+          ++r;
+        }
       }
     }
     run += total;
@@ -205,6 +311,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
 // ---------------------------------------------------------------------------
 
 constexpr int kScatterThreads = 256;
+constexpr int kScatterUnroll = 2;
 
 __device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
   return max(a & 0xFFFFu, b & 0xFFFFu) | (max(a >> 16, b >> 16) << 16);
@@ -242,36 +349,49 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
     int total_rows, uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
   const int lane4 = threadIdx.x & 3;
   const int groups_per_grid = gridDim.x * (kScatterThreads / 4);
-  for (int b = blockIdx.x * (kScatterThreads / 4) + (threadIdx.x >> 2); b < nblocks; b += groups_per_grid) {
-    const uint4 v = x[(int64_t)b * 4 + lane4];
-    const int t = b / kblocks, kb = b - t * kblocks;
-    const uint32_t m = umax16x2(umax16x2(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
-                                umax16x2(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
-    const uint32_t amax_bits = quad_max(max(m & 0xFFFFu, m >> 16));
-    const int exp_field = (int)(amax_bits >> 7);
-    const uint32_t sbyte = (uint32_t)max(exp_field - (FP8 ? 8 : 2), 0);
-    const float scale = __uint_as_float(sbyte << 23);
-    uint2 codes8 = make_uint2(0u, 0u);
-    uint32_t codes4 = 0;
-    if constexpr (FP8) {
-      const uint32_t bound = ((8u + sbyte) << 7) | 0x60u;   // 448 * 2^e as BF16 magnitude bits
-      codes8.x = cvt_fp8x4(clamp_mag16x2(v.x, bound), clamp_mag16x2(v.y, bound), scale);
-      codes8.y = cvt_fp8x4(clamp_mag16x2(v.z, bound), clamp_mag16x2(v.w, bound), scale);
-    } else {
-      codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
-      codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
-      codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);
-      codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v.w), scale, 3);
+  // two blocks per lane group per iteration: both loads are in flight before
+  // either block's stores
+  for (int blk = blockIdx.x * (kScatterThreads / 4) + (threadIdx.x >> 2); blk < nblocks;
+       blk += kScatterUnroll * groups_per_grid) {
+    uint4 v[kScatterUnroll];
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      const int b = blk + u * groups_per_grid;
+      v[u] = x[(int64_t)(b < nblocks ? b : 0) * 4 + lane4];   // out-of-range groups load block 0, store nothing
     }
-    for (int j = 0; j < top_k; ++j) {
-      const int r = token_rows[(int64_t)t * top_k + j];
-      if (r < 0 || r >= total_rows) continue;   // dropped entry (or a malformed row index)
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      const int b = blk + u * groups_per_grid;
+      const int t = b / kblocks, kb = b - t * kblocks;
+      const uint32_t m = umax16x2(umax16x2(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu),
+                                  umax16x2(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu));
+      const uint32_t amax_bits = quad_max(max(m & 0xFFFFu, m >> 16));
+      const int exp_field = (int)(amax_bits >> 7);
+      const uint32_t sbyte = (uint32_t)max(exp_field - (FP8 ? 8 : 2), 0);
+      const float scale = __uint_as_float(sbyte << 23);
+      uint2 codes8 = make_uint2(0u, 0u);
+      uint32_t codes4 = 0;
       if constexpr (FP8) {
-        *(uint2*)(q + (int64_t)r * kblocks * 32 + kb * 32 + lane4 * 8) = codes8;
+        const uint32_t bound = ((8u + sbyte) << 7) | 0x60u;   // 448 * 2^e as BF16 magnitude bits
+        codes8.x = cvt_fp8x4(clamp_mag16x2(v[u].x, bound), clamp_mag16x2(v[u].y, bound), scale);
+        codes8.y = cvt_fp8x4(clamp_mag16x2(v[u].z, bound), clamp_mag16x2(v[u].w, bound), scale);
       } else {
-        *(uint32_t*)(q + (int64_t)r * kblocks * 16 + kb * 16 + lane4 * 4) = codes4;
+        codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v[u].x), scale, 0);
+        codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v[u].y), scale, 1);
+        codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v[u].z), scale, 2);
+        codes4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes4, __builtin_bit_cast(bf16x2_t, v[u].w), scale, 3);
       }
-      if (lane4 == 0) scales[(int64_t)r * kblocks + kb] = (uint8_t)sbyte;
+      if (b >= nblocks) continue;   // uniform over the lane group
+      for (int j = 0; j < top_k; ++j) {
+        const int r = token_rows[(int64_t)t * top_k + j];
+        if (r < 0 || r >= total_rows) continue;   // dropped entry (or a malformed row index)
+        if constexpr (FP8) {
+          *(uint2*)(q + (int64_t)r * kblocks * 32 + kb * 32 + lane4 * 8) = codes8;
+        } else {
+          *(uint32_t*)(q + (int64_t)r * kblocks * 16 + kb * 16 + lane4 * 4) = codes4;
+        }
+        if (lane4 == 0) scales[(int64_t)r * kblocks + kb] = (uint8_t)sbyte;
+      }
     }
   }
 }
@@ -340,18 +460,43 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
 
 }  // namespace
 
+template <int K>
+hipError_t launch_route_k(const float* logits, int tokens, int experts, int32_t* ids, float* weights,
+                          hipStream_t stream) {
+  const int64_t blocks = ((int64_t)tokens + kRouteThreads / 4 - 1) / (kRouteThreads / 4);
+  if (!grid_fits(blocks, kRouteThreads)) return hipErrorInvalidConfiguration;
+  const bool vec = experts % 16 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL((route_kernel<K, true>), dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream, logits,
+                       tokens, experts, ids, weights);
+  else
+    hipLaunchKernelGGL((route_kernel<K, false>), dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream, logits,
+                       tokens, experts, ids, weights);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_route(const float* logits, int tokens, int experts, int top_k, int32_t* ids, float* weights,
                             hipStream_t stream) {
-  const int64_t blocks = ((int64_t)tokens + 3) / 4;
-  if (!grid_fits(blocks, kRouteThreads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream, logits, tokens, experts,
-                     top_k, ids, weights);
-  return hipGetLastError();
+  switch (top_k) {
+    case 1: return launch_route_k<1>(logits, tokens, experts, ids, weights, stream);
+    case 2: return launch_route_k<2>(logits, tokens, experts, ids, weights, stream);
+    case 3: return launch_route_k<3>(logits, tokens, experts, ids, weights, stream);
+    case 4: return launch_route_k<4>(logits, tokens, experts, ids, weights, stream);
+    case 5: return launch_route_k<5>(logits, tokens, experts, ids, weights, stream);
+    case 6: return launch_route_k<6>(logits, tokens, experts, ids, weights, stream);
+    case 7: return launch_route_k<7>(logits, tokens, experts, ids, weights, stream);
+    case 8: return launch_route_k<8>(logits, tokens, experts, ids, weights, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_moe_permute(const int32_t* ids, int n, int top_k, int experts, int32_t* offsets,
                               int32_t* row_token, int32_t* token_rows, hipStream_t stream) {
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)(experts + 1)), dim3(kPermThreads), 0, stream, ids, n, top_k,
+  const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15) == 0;
+  const auto kernel = vec ? permute_kernel<true> : permute_kernel<false>;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kPermLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(experts + 1)), dim3(kPermThreads), kPermLds, stream, ids, n, top_k,
                      experts, offsets, row_token, token_rows);
   return hipGetLastError();
 }
@@ -361,7 +506,8 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
                                        int num_cus) {
   const int kblocks = k / 32;
   const int nblocks = tokens * kblocks;   // the host keeps this below 2^31
-  int64_t grid = ((int64_t)nblocks + (kScatterThreads / 4) - 1) / (kScatterThreads / 4);
+  const int64_t groups_needed = ((int64_t)nblocks + kScatterUnroll - 1) / kScatterUnroll;
+  int64_t grid = (groups_needed + (kScatterThreads / 4) - 1) / (kScatterThreads / 4);
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;

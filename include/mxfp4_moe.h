@@ -81,7 +81,7 @@ mxfp4_status_t mxfp4_moe_permute(const int32_t* topk_ids, int64_t tokens, int32_
  * once.  Rows no slot points at are left untouched.
  *   x_bf16 [tokens, k] (16-byte aligned); q [total_rows, k/2] (4-byte
  *   aligned); scales [total_rows, k/32] (any alignment).
- * Limits: k a positive multiple of 32, k <= 2^24; tokens * k / 32 < 2^31;
+ * Limits: k a positive multiple of 32, k <= 2^24; tokens * k / 32 <= 2^30;
  * 1 <= top_k <= 256; 0 <= total_rows < 2^31.  tokens == 0 or
  * total_rows == 0 is a no-op.
  */

@@ -212,3 +212,9 @@ def test_moe_entry_points_reject_bad_arguments_on_host(lib):
     assert lib.mxfp4_moe_combine(f(0x1001), 8, 64, f(), f(), 4, 2, f(), 0, None) == 1
     assert lib.mxfp4_moe_combine(f(), 8, 64, f(), f(), 4, 2, f(0x1002), 1, None) == 1
     assert lib.mxfp4_moe_combine(None, 8, 64, None, None, 0, 2, None, 0, None) == 0   # no tokens: no-op
+
+
+def test_moe_scatter_block_limit(lib):
+    # tokens * k / 32 <= 2^30 (32-bit block indices with room for the unrolled grid stride)
+    assert lib.mxfp4_moe_quantize_scatter(_fake(), (1 << 30) // 2 + 1, 64, 1, _fake(), 8, _fake(), _fake(), None) == 1
+    assert b"too large" in lib.mxfp4_last_error()
