@@ -13,3 +13,6 @@ from .mxfp8_oracle import (  # noqa: F401
 from .moe_oracle import (  # noqa: F401
     route_topk, permute, quantize_scatter, quantize_scatter_mxfp8, combine, combine_abs,
 )
+from .producers_oracle import (  # noqa: F401
+    add_residual, rmsnorm_f64, rmsnorm_bf16, swiglu_f64, swiglu_bf16,
+)
