@@ -1,4 +1,5 @@
-"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h, include/mxfp8.h and include/mxfp4_moe.h).
+"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h, include/mxfp8.h, include/mxfp4_moe.h and
+include/mxfp4_producers.h).
 
 Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the computation runs in the library's kernels.  The
@@ -28,7 +29,7 @@ EXPORTED = (
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
     "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
-    "mxfp4_moe_combine",
+    "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -97,6 +98,10 @@ def load_library(path: str = LIB_PATH):
         for name in ("mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter"):
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = [vp, i64, i64, i32, vp, i64, vp, vp, vp]
+        lib.mxfp4_rmsnorm_quantize.restype = ctypes.c_int
+        lib.mxfp4_rmsnorm_quantize.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
+        lib.mxfp4_swiglu_quantize.restype = ctypes.c_int
+        lib.mxfp4_swiglu_quantize.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.mxfp4_moe_combine.restype = ctypes.c_int
         lib.mxfp4_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, ctypes.c_int, vp]
         _lib = lib
@@ -378,3 +383,52 @@ def mxfp4_moe_combine(y, token_rows, weights, out=None, out_dtype=torch.bfloat16
     _check(lib.mxfp4_moe_combine(_ptr(y), total_rows, n, _ptr(token_rows), _ptr(weights), tokens, top_k,
                                  _ptr(out), code, _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Fused producers (include/mxfp4_producers.h)
+# ---------------------------------------------------------------------------
+
+def mxfp4_rmsnorm_quantize(x, gamma, eps: float, residual=None, residual_out=None, y=None, q=None, scales=None,
+                           stream=None):
+    """(x [+ residual]) -> RMSNorm(., gamma, eps) -> MXFP4 (q [rows, k/2], scales [rows, k/32]).
+    residual_out (optional) receives x + residual; y (optional) the BF16 RMSNorm output."""
+    lib = load_library()
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(gamma, "gamma", torch.bfloat16, (k,))
+    for t, name in ((residual, "residual"), (residual_out, "residual_out"), (y, "y")):
+        if t is not None:
+            _require(t, name, torch.bfloat16, (rows, k))
+    _require(q, "q", torch.uint8, (rows, k // 2))
+    _require(scales, "scales", torch.uint8, (rows, k // 32))
+    _check(lib.mxfp4_rmsnorm_quantize(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), rows, k, _ptr(residual_out),
+                                      _ptr(y), _ptr(q), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None):
+    """silu(gate) * up -> MXFP4.  gate and up are [rows, k] views sharing one row stride (for example the two
+    halves of a [rows, 2k] projection output); y (optional) receives the BF16 activation."""
+    lib = load_library()
+    rows, k = gate.shape
+    if tuple(up.shape) != (rows, k) or gate.stride() != up.stride() or gate.stride(1) != 1:
+        raise ValueError("gate and up must be [rows, k] views with the same row stride and unit column stride")
+    if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16 or not gate.is_cuda or not up.is_cuda:
+        raise TypeError("gate and up must be bfloat16 device tensors")
+    ld = gate.stride(0) if rows > 1 else k
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=gate.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=gate.device)
+    if y is not None:
+        _require(y, "y", torch.bfloat16, (rows, k))
+    _require(q, "q", torch.uint8, (rows, k // 2))
+    _require(scales, "scales", torch.uint8, (rows, k // 32))
+    _check(lib.mxfp4_swiglu_quantize(_ptr(gate), _ptr(up), ld, rows, k, _ptr(y), _ptr(q), _ptr(scales),
+                                     _stream(stream)))
+    return q, scales

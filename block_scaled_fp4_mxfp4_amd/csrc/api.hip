@@ -1,6 +1,6 @@
 // C ABI of the MXFP4 library: argument checks, per-shape kernel choice, launches.
-// Entry points and their contracts are documented in include/mxfp4.h, include/mxfp8.h and
-// include/mxfp4_moe.h.
+// Entry points and their contracts are documented in include/mxfp4.h, include/mxfp8.h,
+// include/mxfp4_moe.h and include/mxfp4_producers.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -12,6 +12,7 @@
 #include "../../include/mxfp4_probe.h"
 #include "../../include/mxfp8.h"
 #include "../../include/mxfp4_moe.h"
+#include "../../include/mxfp4_producers.h"
 #include "launch.hpp"
 
 namespace {
@@ -491,6 +492,55 @@ mxfp4_status_t mxfp4_moe_combine(const void* y_bf16, int64_t total_rows, int64_t
   const bool vec = n % 8 == 0 && aligned16(y_bf16) && aligned16(out);
   return hip_status(mxfp4::launch_moe_combine(y_bf16, (int)total_rows, (int)n, token_rows, topk_weights, (int)tokens,
                                               top_k, out, f32, vec, (hipStream_t)stream), "moe combine launch");
+}
+
+// ---------------------------------------------------------------------------
+// Fused producers (include/mxfp4_producers.h)
+// ---------------------------------------------------------------------------
+
+mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_bf16, const void* gamma_bf16,
+                                      float eps, int64_t rows, int64_t k, void* residual_out_bf16, void* y_bf16,
+                                      void* q, void* scales, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 30)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^30 (got %lld)", (long long)rows);
+  MXFP4_TRY(check_k(k));
+  if (k > 256 * 8 * mxfp4::kNormMaxSlots)
+    return fail(MXFP4_ERR_INVALID_ARG, "k must be at most %d for the RMSNorm producer (got %lld)",
+                256 * 8 * mxfp4::kNormMaxSlots, (long long)k);
+  if (!(eps >= 0.0f) || eps == __builtin_huge_valf()) return fail(MXFP4_ERR_INVALID_ARG, "eps must be finite and non-negative");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(gamma_bf16, "gamma_bf16"));
+  MXFP4_TRY(check_ptr(q, "q", 4));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
+  if (residual_bf16) MXFP4_TRY(check_ptr(residual_bf16, "residual_bf16"));
+  if (residual_out_bf16) {
+    if (!residual_bf16) return fail(MXFP4_ERR_INVALID_ARG, "residual_out_bf16 needs residual_bf16");
+    MXFP4_TRY(check_ptr(residual_out_bf16, "residual_out_bf16"));
+  }
+  if (y_bf16) MXFP4_TRY(check_ptr(y_bf16, "y_bf16"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_rmsnorm_quantize(x_bf16, residual_bf16, gamma_bf16, eps, (int)rows, (int)k,
+                                                   residual_out_bf16, y_bf16, q, scales, (hipStream_t)stream),
+                    "rmsnorm quantize launch");
+}
+
+mxfp4_status_t mxfp4_swiglu_quantize(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
+                                     int64_t k, void* y_bf16, void* q, void* scales, void* stream) {
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
+  MXFP4_TRY(check_k(k));
+  if (ld < k || ld % 8 != 0) return fail(MXFP4_ERR_INVALID_ARG, "ld must be a multiple of 8 and at least k (got %lld)", (long long)ld);
+  if (rows > ((int64_t)1 << 30) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "rows * k / 32 too large");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(gate_bf16, "gate_bf16"));
+  MXFP4_TRY(check_ptr(up_bf16, "up_bf16"));
+  MXFP4_TRY(check_ptr(q, "q", 4));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
+  if (y_bf16) MXFP4_TRY(check_ptr(y_bf16, "y_bf16"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_swiglu_quantize(gate_bf16, up_bf16, ld, (int)rows, (int)k, y_bf16, q, scales,
+                                                  (hipStream_t)stream, dev.num_cus), "swiglu quantize launch");
 }
 
 }  // extern "C"

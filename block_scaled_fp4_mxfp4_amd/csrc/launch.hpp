@@ -72,6 +72,13 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
 hipError_t launch_moe_combine(const void* y, int total_rows, int n, const int32_t* token_rows, const float* weights,
                               int tokens, int top_k, void* out, bool f32_out, bool vec, hipStream_t stream);
 
+// Fused producers emitting MXFP4 activations (include/mxfp4_producers.h).
+constexpr int kNormMaxSlots = 16;   // RMSNorm rows: k <= 256 threads * 8 elements * 16 = 32768
+hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
+                                   void* h_out, void* y_out, void* q, void* scales, hipStream_t stream);
+hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
+                                  void* scales, hipStream_t stream, int num_cus);
+
 // Measurement probes (include/mxfp4_probe.h).
 double probe_mfma_flops(int blocks, int iters);
 hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, bool a_fp8, hipStream_t stream);

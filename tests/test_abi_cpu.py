@@ -218,3 +218,28 @@ def test_moe_scatter_block_limit(lib):
     # tokens * k / 32 <= 2^30 (32-bit block indices with room for the unrolled grid stride)
     assert lib.mxfp4_moe_quantize_scatter(_fake(), (1 << 30) // 2 + 1, 64, 1, _fake(), 8, _fake(), _fake(), None) == 1
     assert b"too large" in lib.mxfp4_last_error()
+
+
+def test_producers_reject_bad_arguments_on_host(lib):
+    f = _fake
+    rms = lib.mxfp4_rmsnorm_quantize
+    assert rms(f(), None, f(), 1e-5, 4, 48, None, None, f(), f(), None) == 1           # k % 32
+    assert rms(f(), None, f(), 1e-5, 4, 32768 + 32, None, None, f(), f(), None) == 1   # k too large
+    assert rms(f(), None, f(), -1.0, 4, 64, None, None, f(), f(), None) == 1           # eps < 0
+    assert rms(f(), None, f(), float("nan"), 4, 64, None, None, f(), f(), None) == 1
+    assert rms(f(), None, f(), float("inf"), 4, 64, None, None, f(), f(), None) == 1
+    assert rms(f(), None, f(), 1e-5, -1, 64, None, None, f(), f(), None) == 1
+    assert rms(None, None, f(), 1e-5, 4, 64, None, None, f(), f(), None) == 1
+    assert rms(f(), None, None, 1e-5, 4, 64, None, None, f(), f(), None) == 1
+    assert rms(f(), None, f(), 1e-5, 4, 64, f(), None, f(), f(), None) == 1            # residual_out without residual
+    assert b"needs residual" in lib.mxfp4_last_error()
+    assert rms(f(), f(0x1008), f(), 1e-5, 4, 64, None, None, f(), f(), None) == 1      # misaligned residual
+    assert rms(f(), None, f(), 1e-5, 4, 64, None, None, f(0x1002), f(), None) == 1     # misaligned q
+    assert rms(None, None, None, 1e-5, 0, 64, None, None, None, None, None) == 0       # no rows: no-op
+    sw = lib.mxfp4_swiglu_quantize
+    assert sw(f(), f(), 64, 4, 48, None, f(), f(), None) == 1                           # k % 32
+    assert sw(f(), f(), 60, 4, 64, None, f(), f(), None) == 1                           # ld < k
+    assert sw(f(), f(), 68, 4, 64, None, f(), f(), None) == 1                           # ld % 8
+    assert sw(f(), f(0x1008), 64, 4, 64, None, f(), f(), None) == 1                     # misaligned up
+    assert sw(f(), f(), 64, (1 << 30) // 2 + 1, 64, None, f(), f(), None) == 1          # rows * k / 32
+    assert sw(None, None, 64, 0, 64, None, None, None, None) == 0                       # no rows: no-op
