@@ -13,7 +13,8 @@ N=2816, K=4096) in TFLOP/s and GB/s, and the same layer run wholly on the
 device (`moe_layer`: top-k routing of the router logits, the expert-sorted
 permutation, MXFP4 quantization scattered into the routed rows, the grouped
 GEMM and the weighted combine), each step's time against its algorithmic
-bytes.
+bytes.  Also the fused producers (`producers`): residual add + RMSNorm and
+SwiGLU kernels that write their output straight as MXFP4, against HBM.
 
 Inputs are resident in HBM before timing.  Steps rotate over enough copies of
 the inputs (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot serve
@@ -349,6 +350,73 @@ def measure_moe_layer(args, dev, us):
     return out
 
 
+class ProducerBench:
+    """Fused producers on the prefill shapes: residual add + RMSNorm + MXFP4 of
+    a [4096, 4096] activation (writing the updated residual stream), and
+    SwiGLU + MXFP4 of the [4096, 14336] FFN activation read from the two
+    halves of a [4096, 28672] gate|up buffer."""
+
+    def __init__(self, dev, rows=4096, hidden=4096, inter=14336):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        self.rows, self.hidden, self.inter = rows, hidden, inter
+        x = workloads.activation_bf16(rows, hidden, 300, outliers=True).to(dev)
+        res = workloads.activation_bf16(rows, hidden, 301, outliers=False).to(dev)
+        gamma = workloads.gaussian_bf16((hidden,), 0.1, 302).to(dev)
+        gu = workloads.gaussian_bf16((rows, 2 * inter), 1.0, 401).to(dev)
+        per_set = rows * hidden * 2 * 3 + rows * hidden * 17 // 32 + rows * inter * 4 + rows * inter * 17 // 32
+        self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
+        self.sets = []
+        for _ in range(self.sets_n):
+            self.sets.append(dict(
+                x=x.clone(), res=res.clone(), gamma=gamma.clone(), h=torch.empty_like(x), gu=gu.clone(),
+                q=torch.empty((rows, hidden // 2), dtype=torch.uint8, device=dev),
+                s=torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev),
+                qi=torch.empty((rows, inter // 2), dtype=torch.uint8, device=dev),
+                si=torch.empty((rows, inter // 32), dtype=torch.uint8, device=dev)))
+        del x, res, gamma, gu
+        torch.cuda.synchronize()
+
+    def rmsnorm(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_rmsnorm_quantize(s["x"], s["gamma"], 1e-5, residual=s["res"], residual_out=s["h"],
+                                      q=s["q"], scales=s["s"])
+
+    def swiglu(self, i):
+        s = self.sets[i % self.sets_n]
+        k = self.inter
+        self.B.mxfp4_swiglu_quantize(s["gu"][:, :k], s["gu"][:, k:], q=s["qi"], scales=s["si"])
+
+    def algorithmic_bytes(self):
+        r, h, f = self.rows, self.hidden, self.inter
+        return {
+            # x, residual and gamma in; the updated residual, codes and scales out
+            "rmsnorm": r * h * 2 * 2 + h * 2 + r * h * 2 + r * h // 2 + r * h // 32,
+            # gate and up in; codes and scales out
+            "swiglu": r * f * 2 * 2 + r * f // 2 + r * f // 32,
+        }
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+
+def measure_producers(args, dev, us):
+    eprint("[bench] fused producers (RMSNorm and SwiGLU emitting MXFP4)")
+    pb = ProducerBench(dev)
+    nbytes = pb.algorithmic_bytes()
+    out = {}
+    for name, shape in (("rmsnorm", f"{pb.rows}x{pb.hidden}, residual add"),
+                        ("swiglu", f"{pb.rows}x{pb.inter} from a {pb.rows}x{2 * pb.inter} gate|up buffer")):
+        t = pb.timed(getattr(pb, name), max(32, args.steps // 2), 4, period=16)
+        gbs = nbytes[name] / (t["mean"] * 1e-3) / 1e9
+        out[name] = {"shape": shape, "us": us(t), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+        eprint(f"[bench] {name}_quantize {shape}: {t['mean']*1e3:.2f} us ({gbs:.0f} GB/s)")
+    del pb
+    return out
+
+
 class Ceilings:
     """Measured ceilings on this GPU (include/mxfp4_probe.h), reported next to the
     published peaks: the FP4 scaled-MFMA rate of a kernel that only runs MFMAs
@@ -534,7 +602,9 @@ def run_only(args, dev):
         return
     w = workloads.ALL[args.workload]
     act = "mxfp8" if args.w4a8_only else "mxfp4"
-    if args.only in ("route", "permute", "scatter", "combine", "layer"):
+    if args.only in ("rmsnorm", "swiglu"):
+        bench = ProducerBench(dev)
+    elif args.only in ("route", "permute", "scatter", "combine", "layer"):
         if not isinstance(w, workloads.MoEWorkload):
             eprint(f"--only {args.only} needs the MoE workload")
             sys.exit(2)
@@ -573,10 +643,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "quantize", "quantize_b", "copy",
-                                       "route", "permute", "scatter", "combine", "layer"],
+                                       "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu"],
                     help="eager launches for profiling; route/permute/scatter/combine/layer run the "
                          "on-device MoE layer's steps (layer = all five) on the MoE workload")
     ap.add_argument("--no-moe-layer", action="store_true", help="skip the on-device MoE layer measurement")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the fused producer (RMSNorm / SwiGLU emitting MXFP4) measurement")
     ap.add_argument("--w4a8-only", action="store_true",
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
@@ -704,6 +776,9 @@ def main():
 
     if args.moe != "none" and not args.no_moe_layer:
         result["moe_layer"] = measure_moe_layer(args, dev, us)
+
+    if not args.no_producers:
+        result["producers"] = measure_producers(args, dev, us)
 
     if not args.no_w4a8:
         result["w4a8"] = measure_w4a8(args, dev, w, us)

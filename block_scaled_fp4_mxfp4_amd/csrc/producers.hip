@@ -16,9 +16,11 @@
 //    y = RNE_bf16((h * inv) * gamma) from fp64 with a single rounding.  The
 //    fp64 path makes y equal to the nearest BF16 of the exact value except
 //    where that value lies within ~2^-50 of a BF16 rounding midpoint.
-//  swiglu_quantize_kernel: elementwise y = RNE_bf16(g * u / (1 + expf(-g))) in
-//    fp32 over the flat 32-element blocks of the [rows, k] output, gate and up
-//    read with a row stride (so one [rows, 2k] gate|up buffer serves).
+//  swiglu_quantize_kernel: elementwise y = RNE_bf16(g * u / (1 + exp(-g))) in
+//    fp32 with the hardware exp2 and reciprocal (the accurate library expf and
+//    IEEE divide cost about 30 instructions per element, which made the kernel
+//    ALU-bound) over the flat 32-element blocks of the [rows, k] output, gate
+//    and up read with a row stride (so one [rows, 2k] gate|up buffer serves).
 //
 // Both quantize y exactly as the MXFP4 quantizer does (4 lanes per 32-element
 // block, integer amax, scale byte max(E - 2, 0), the CDNA4 scaled FP4 convert)
@@ -100,13 +102,17 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
   __shared__ double red[kNormThreads / 64];
   const int chunks = k >> 3;                         // 8 elements (one uint4) per chunk
   const int64_t rbase = (int64_t)blockIdx.x * chunks;
-  uint4 h[SLOTS];
+  uint4 h[SLOTS], gm[SLOTS];
   double ss = 0.0;
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int c = s * kNormThreads + threadIdx.x;
     h[s] = make_uint4(0u, 0u, 0u, 0u);
-    if (c < chunks) h[s] = x[rbase + c];
+    gm[s] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < chunks) {
+      h[s] = x[rbase + c];
+      gm[s] = gamma[c];   // loaded with the row, so the second phase waits on nothing
+    }
   }
   if (HAS_RES) {
 #pragma unroll
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
   for (int s = 0; s < SLOTS; ++s) {
     const int c = s * kNormThreads + threadIdx.x;
     if (c >= chunks) continue;   // uniform over each lane quad (chunks % 4 == 0)
-    const uint4 g = gamma[c];
+    const uint4 g = gm[s];
     const uint32_t hw[4] = {h[s].x, h[s].y, h[s].z, h[s].w};
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     uint32_t yw[4];
@@ -153,8 +159,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
   }
 }
 
+// silu(g) * u with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
+// each about 1 ulp): exp(-g) = exp2(-g * log2 e).  Relative error at most
+// about (|g| + 6) * 2^-24: the product -g * log2 e rounds by |g| * 2^-24 in the
+// exponent, exp2 and rcp add an ulp each, 1 + t and the final product half an
+// ulp each.  Very negative g gives exp2 = inf, rcp = 0 and a signed zero; very
+// positive g gives t = 0 and y = g * u.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return (g * u) / (1.0f + expf(-g));
+  const float t = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
 __device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t g, uint32_t u) {

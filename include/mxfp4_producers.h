@@ -62,9 +62,10 @@ mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_b
  *     ld >= k);
  *   y_bf16 [rows, k] or NULL: receives the BF16 activation;
  *   q [rows, k/2], scales [rows, k/32]: MXFP4 of y.
- * Arithmetic: (g * u) / (1 + expf(-g)) in fp32, then nearest-even BF16; y
- * is within one BF16 step of the exact value and equals its nearest BF16
- * except within a few fp32 ulps of a rounding midpoint.
+ * Arithmetic: (g * u) * rcp(1 + exp2(-g * log2 e)) in fp32 with the hardware
+ * exp2 and reciprocal (relative error at most about (|g| + 6) * 2^-24), then
+ * nearest-even BF16; y is within one BF16 step of the exact value and equals
+ * its nearest BF16 except that close to a rounding midpoint.
  * Limits: k a positive multiple of 32, rows * k / 32 <= 2^30; rows == 0 is a
  * no-op.
  */

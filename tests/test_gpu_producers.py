@@ -6,9 +6,11 @@
   rounding midpoint (fp64 arithmetic in the kernel differs from the oracle's
   correctly rounded sum of squares by a few fp64 ulps at most);
 * SwiGLU: the kernel's BF16 output is within one BF16 step of the oracle's
-  float64 value and equals its nearest BF16 except within 2^-20 (relative) of a
-  rounding midpoint (fp32 arithmetic: g*u exact, expf within a few ulp, one
-  add and one divide);
+  float64 value and equals its nearest BF16 except within (|g| + 8) * 2^-24
+  (relative) of a rounding midpoint (fp32 arithmetic with the hardware exp2 and
+  reciprocal: g*u exact, -g*log2(e) rounding by |g| * 2^-24 in the exponent,
+  about an ulp each for exp2 and rcp, half an ulp each for the add and the
+  final product);
 * MXFP4: codes and scale bytes bit-exact against the oracle's quantization of
   the kernel's own BF16 output (and so of the oracle's wherever the two agree);
   a call without the BF16 output writes the same bytes.
@@ -37,7 +39,8 @@ def _assert_nearest_or_midpoint(got_bits, y64, rel_window):
     lo = oracle.bf16_bits_to_f64(want[bad])
     hi = oracle.bf16_bits_to_f64(got_bits[bad])
     mid = (lo + hi) / 2
-    near = np.abs(y64[bad] - mid) <= rel_window * np.abs(y64[bad])
+    window = rel_window[bad] if np.ndim(rel_window) else rel_window
+    near = np.abs(y64[bad] - mid) <= window * np.abs(y64[bad])
     one_step = np.abs(got_bits[bad].astype(np.int32) - want[bad].astype(np.int32)) == 1
     assert np.all(near & one_step), f"{int((~(near & one_step)).sum())} outputs are not the nearest BF16"
 
@@ -115,6 +118,11 @@ def test_rmsnorm_prefill_activation_full_size_sampled():
 SWIGLU_CASES = [(1, 32, 32), (17, 96, 192), (64, 2816, 5632), (40, 14336, 14336), (7, 160, 168)]
 
 
+def _silu_window(gate_bf16):
+    """Relative distance from a BF16 midpoint within which the fp32 kernel may round either way."""
+    return (np.abs(oracle.bf16_bits_to_f64(_bits(gate_bf16))) + 8.0) * 2.0 ** -24
+
+
 def _gate_up(rows, k, ld, seed, dev):
     g = torch.Generator().manual_seed(seed)
     base = (torch.randn(rows, ld + k, generator=g) * 3).to(torch.bfloat16)
@@ -135,7 +143,7 @@ def test_swiglu_quantize_matches_oracle(rows, k, ld):
     torch.cuda.synchronize()
     y64 = oracle.swiglu_f64(_bits(gate_c), _bits(up_c))
     yb = _bits(y)
-    _assert_nearest_or_midpoint(yb, y64, 2.0 ** -20)
+    _assert_nearest_or_midpoint(yb, y64, _silu_window(gate_c))
     rq, rs = oracle.quantize(yb)
     assert np.array_equal(to_np(q), rq) and np.array_equal(to_np(s), rs)
     assert torch.equal(q, q2) and torch.equal(s, s2)
@@ -153,6 +161,6 @@ def test_swiglu_ffn_full_size_sampled():
     idx = sampled_indices(rows, 24, 10)
     y64 = oracle.swiglu_f64(_bits(gu[idx, :k]), _bits(gu[idx, k:]))
     yb = _bits(y)[idx]
-    _assert_nearest_or_midpoint(yb, y64, 2.0 ** -20)
+    _assert_nearest_or_midpoint(yb, y64, _silu_window(gu[idx, :k]))
     rq, rs = oracle.quantize(yb)
     assert np.array_equal(to_np(q)[idx], rq) and np.array_equal(to_np(s)[idx], rs)
