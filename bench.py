@@ -342,6 +342,9 @@ def measure_moe_layer(args, dev, us):
         gbs = nbytes[name] / (tk["mean"] * 1e-3) / 1e9
         kern[name] = {"us": us(tk), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        kname = {"scatter": "quantize_scatter_kernel", "combine": "combine_kernel"}.get(name)
+        if kname:
+            kern[name]["traffic"] = traffic_from_profiles(wm.name, kname)
     kern["gemm"]["tflops"] = round(wm.flops / (kern["gemm"]["us"]["mean"] * 1e-6) / 1e12, 2)
     out["kernels"] = kern
     eprint(f"[bench] MoE layer {wm.name}: step {st['mean']*1e3:.1f} us; " +
@@ -409,9 +412,11 @@ def measure_producers(args, dev, us):
                         ("swiglu", f"{pb.rows}x{pb.inter} from a {pb.rows}x{2 * pb.inter} gate|up buffer")):
         t = pb.timed(getattr(pb, name), max(32, args.steps // 2), 4, period=16)
         gbs = nbytes[name] / (t["mean"] * 1e-3) / 1e9
+        kname = f"{name}_quantize_kernel"
         out[name] = {"shape": shape, "us": us(t), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic_from_profiles(f"producer_{name}", kname)}}
         eprint(f"[bench] {name}_quantize {shape}: {t['mean']*1e3:.2f} us ({gbs:.0f} GB/s)")
     del pb
     return out
@@ -511,28 +516,41 @@ def cpu_baseline(bench: DenseBench, target_seconds: float):
                       f"({blas} BLAS threads of {avail} available cores)"}
 
 
-def sources_sha():
-    """Hash of the HIP sources: recorded counter data is only valid for these."""
+# The sources each measured kernel is built from: recorded counter data stays
+# valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "gemm_tile_kernel": ("gemm_tile.hip", "common.hpp"),
+    "gemm_stream_kernel": ("gemm_stream.hip", "common.hpp"),
+    "quantize_kernel": ("quantize.hip", "common.hpp"),
+    "quantize_scatter_kernel": ("moe.hip", "common.hpp"),
+    "combine_kernel": ("moe.hip", "common.hpp"),
+    "rmsnorm_quantize_kernel": ("producers.hip", "common.hpp"),
+    "swiglu_quantize_kernel": ("producers.hip", "common.hpp"),
+}
+
+
+def sources_sha(kernel: str) -> str:
+    """Hash of the HIP sources of one kernel (first 16 hex digits of a SHA-256)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_mxfp4_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per GEMM launch recorded in profiles/traffic.md for this
-    workload, if the kernel sources have not changed since the counters were
-    taken (else None)."""
+def traffic_from_profiles(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` recorded in profiles/traffic.md,
+    if the kernel's sources have not changed since the counters were taken (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.md")
     if not os.path.exists(path):
         return None
-    sha = sources_sha()
+    sha = sources_sha(kernel)
     for line in open(path):
         parts = dict(p.split("=", 1) for p in line.split() if "=" in p)
-        if parts.get("workload") == workload and parts.get("sources") == sha and "bytes_per_launch" in parts:
+        if (parts.get("workload") == workload and parts.get("kernel") == kernel and parts.get("sources") == sha
+                and "bytes_per_launch" in parts):
             return float(parts["bytes_per_launch"])
     return None
 
@@ -710,7 +728,7 @@ def main():
                    "rotating_input_sets": bench.sets_n, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(w.name)},
+                     "traffic": traffic_from_profiles(w.name, "gemm_tile_kernel")},
         "step_us": us(step),
         "kernels": {
             "gemm_us": us(gemm), "gemm_tflops": round(gemm_tflops, 2),
@@ -739,7 +757,7 @@ def main():
             "step": "quantize A + streaming mxfp4 GEMM (B pre-quantized)",
             "roofline": {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_from_profiles(w2.name)},
+                         "traffic": traffic_from_profiles(w2.name, "gemm_stream_kernel")},
             "kernels": {"gemm_us": us(g2), "quantize_a_us": us(q2),
                         "gemm_tflops": round(w2.flops / (g2["mean"] * 1e-3) / 1e12, 2)},
         }
