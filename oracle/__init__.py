@@ -16,3 +16,6 @@ from .moe_oracle import (  # noqa: F401
 from .producers_oracle import (  # noqa: F401
     add_residual, rmsnorm_f64, rmsnorm_bf16, swiglu_f64, swiglu_bf16,
 )
+from .nvfp4_oracle import (  # noqa: F401
+    NVFP4_BLOCK, global_scales, quantize_nvfp4, dequantize_nvfp4, gemm_nvfp4_nt,
+)
