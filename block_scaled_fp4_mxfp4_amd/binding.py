@@ -1,5 +1,5 @@
-"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h, include/mxfp8.h, include/mxfp4_moe.h and
-include/mxfp4_producers.h).
+"""ctypes binding of libmxfp4.so (the C ABI in include/mxfp4.h, include/mxfp8.h, include/mxfp4_moe.h,
+include/mxfp4_producers.h and include/nvfp4.h).
 
 Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the computation runs in the library's kernels.  The
@@ -29,7 +29,7 @@ EXPORTED = (
     "mxfp4_probe_mfma", "mxfp4_probe_mfma_flops", "mxfp4_probe_read", "mxfp8_quantize",
     "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
-    "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize",
+    "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -102,6 +102,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_rmsnorm_quantize.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
         lib.mxfp4_swiglu_quantize.restype = ctypes.c_int
         lib.mxfp4_swiglu_quantize.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
+        lib.nvfp4_quantize.restype = ctypes.c_int
+        lib.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        lib.nvfp4_gemm_nt.restype = ctypes.c_int
+        lib.nvfp4_gemm_nt.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp4_moe_combine.restype = ctypes.c_int
         lib.mxfp4_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, ctypes.c_int, vp]
         _lib = lib
@@ -432,3 +436,43 @@ def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None):
     _check(lib.mxfp4_swiglu_quantize(_ptr(gate), _ptr(up), ld, rows, k, _ptr(y), _ptr(q), _ptr(scales),
                                      _stream(stream)))
     return q, scales
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 (include/nvfp4.h)
+# ---------------------------------------------------------------------------
+
+def nvfp4_quantize(x, q=None, scales=None, gs=None, stream=None):
+    """x bf16 [rows, k] -> (q uint8 [rows, k/2], scales uint8 [rows, k/16] UE4M3, gs float32 [rows])."""
+    lib = load_library()
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device)
+    if gs is None:
+        gs = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(q, "q", torch.uint8, (rows, k // 2))
+    _require(scales, "scales", torch.uint8, (rows, k // 16))
+    _require(gs, "gs", torch.float32, (rows,))
+    _check(lib.nvfp4_quantize(_ptr(x), rows, k, _ptr(q), _ptr(scales), _ptr(gs), _stream(stream)))
+    return q, scales, gs
+
+
+def nvfp4_gemm_nt(a_q, a_s, a_gs, b_q, b_s, b_gs, c=None, out_dtype=torch.bfloat16, stream=None):
+    """C[m, n] = A[m, k] . B[n, k]^T on NVFP4 operands (codes, UE4M3 scales, per-row global scales)."""
+    lib = load_library()
+    m, kh = a_q.shape
+    n = b_q.shape[0]
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (m, k // 2))
+    _require(a_s, "a_s", torch.uint8, (m, k // 16))
+    _require(a_gs, "a_gs", torch.float32, (m,))
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (n, k // 16))
+    _require(b_gs, "b_gs", torch.float32, (n,))
+    c, code = _out(c, m, n, out_dtype, a_q.device)
+    _check(lib.nvfp4_gemm_nt(_ptr(a_q), _ptr(a_s), _ptr(a_gs), _ptr(b_q), _ptr(b_s), _ptr(b_gs), _ptr(c), code,
+                             m, n, k, _stream(stream)))
+    return c

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmxfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm_tile.hip", "gemm_splitk.hip", "gemm_stream.hip", "probes.hip", "moe.hip", "producers.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_tile.hip", "gemm_splitk.hip", "gemm_stream.hip", "probes.hip", "moe.hip", "producers.hip", "nvfp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

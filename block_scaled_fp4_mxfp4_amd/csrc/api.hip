@@ -1,6 +1,6 @@
 // C ABI of the MXFP4 library: argument checks, per-shape kernel choice, launches.
 // Entry points and their contracts are documented in include/mxfp4.h, include/mxfp8.h,
-// include/mxfp4_moe.h and include/mxfp4_producers.h.
+// include/mxfp4_moe.h, include/mxfp4_producers.h and include/nvfp4.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -13,6 +13,7 @@
 #include "../../include/mxfp8.h"
 #include "../../include/mxfp4_moe.h"
 #include "../../include/mxfp4_producers.h"
+#include "../../include/nvfp4.h"
 #include "launch.hpp"
 
 namespace {
@@ -541,6 +542,51 @@ mxfp4_status_t mxfp4_swiglu_quantize(const void* gate_bf16, const void* up_bf16,
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_swiglu_quantize(gate_bf16, up_bf16, ld, (int)rows, (int)k, y_bf16, q, scales,
                                                   (hipStream_t)stream, dev.num_cus), "swiglu quantize launch");
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 (include/nvfp4.h)
+// ---------------------------------------------------------------------------
+
+mxfp4_status_t nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q, void* scales,
+                              float* global_scales, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 30)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^30 (got %lld)", (long long)rows);
+  MXFP4_TRY(check_k(k));
+  if (k > 256 * 8 * mxfp4::kNormMaxSlots)
+    return fail(MXFP4_ERR_INVALID_ARG, "k must be at most %d for the NVFP4 quantizer (got %lld)",
+                256 * 8 * mxfp4::kNormMaxSlots, (long long)k);
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(q, "q", 4));
+  MXFP4_TRY(check_ptr(scales, "scales", 1));
+  MXFP4_TRY(check_ptr(global_scales, "global_scales", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_nvfp4_quantize(x_bf16, (int)rows, (int)k, q, scales, global_scales,
+                                                 (hipStream_t)stream), "nvfp4 quantize launch");
+}
+
+mxfp4_status_t nvfp4_gemm_nt(const void* a_q, const void* a_s, const float* a_gs, const void* b_q, const void* b_s,
+                             const float* b_gs, void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                             void* stream) {
+  if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
+  MXFP4_TRY(check_k(k));
+  if (k % 64 != 0) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 64 for the NVFP4 GEMM (got %lld)", (long long)k);
+  if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(a_q, "a_q"));
+  MXFP4_TRY(check_ptr(a_s, "a_s", 4));
+  MXFP4_TRY(check_ptr(a_gs, "a_gs", 4));
+  MXFP4_TRY(check_ptr(b_q, "b_q"));
+  MXFP4_TRY(check_ptr(b_s, "b_s", 4));
+  MXFP4_TRY(check_ptr(b_gs, "b_gs", 4));
+  MXFP4_TRY(check_ptr(c, "c"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_nvfp4_gemm(a_q, a_s, a_gs, b_q, b_s, b_gs, c, c_type == MXFP4_OUT_F32, (int)m,
+                                             (int)n, (int)k, (hipStream_t)stream), "nvfp4 gemm launch");
 }
 
 }  // extern "C"

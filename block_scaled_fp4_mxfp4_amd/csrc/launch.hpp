@@ -79,6 +79,13 @@ hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const vo
 hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
                                   void* scales, hipStream_t stream, int num_cus);
 
+// NVFP4 (include/nvfp4.h): quantization (k <= 32768, one workgroup per row) and
+// the dequantizing NT GEMM on the BF16 MFMA (k % 64 == 0).
+hipError_t launch_nvfp4_quantize(const void* x, int rows, int k, void* q, void* scales, float* gs,
+                                 hipStream_t stream);
+hipError_t launch_nvfp4_gemm(const void* a_q, const void* a_s, const float* a_gs, const void* b_q, const void* b_s,
+                             const float* b_gs, void* c, bool c_f32, int m, int n, int k, hipStream_t stream);
+
 // Measurement probes (include/mxfp4_probe.h).
 double probe_mfma_flops(int blocks, int iters);
 hipError_t launch_probe_mfma(const void* seed, void* out, int blocks, int iters, bool a_fp8, hipStream_t stream);

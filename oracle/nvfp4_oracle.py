@@ -26,8 +26,8 @@ What it follows
             saturated at 448; the block's scale byte is its code;
     d     = fp32(s * gs);
     code  = sign(x) | E2M1 magnitude code of fp32(|x| / d), nearest with ties
-            to the even code, saturated at 6; a block whose scale is 0 encodes
-            every element as a (signed) zero.
+            to the even code, saturated at 6; a block whose scale is 0 (or whose
+            d underflows to 0) encodes every element as a (signed) zero.
   Dequantization: x = e2m1(code) * s * gs, exact in float64.
 * GEMM: C[m, n] = sum_k A[m, k] * B[n, k] on the dequantized operands, float64.
 """
@@ -71,7 +71,8 @@ def quantize_nvfp4(x_bits):
     d = (s_val * gs[:, None]).astype(np.float32)                               # fp32(s * gs)
     with np.errstate(divide="ignore", invalid="ignore"):
         v = (np.abs(blocks) / d[:, :, None]).astype(np.float32)                # fp32(|x| / d)
-    v = np.where(s_val[:, :, None] == 0, np.float32(0.0), v)
+    # a zero scale, or a scale whose product with gs underflows to zero, encodes signed zeros
+    v = np.where((s_val[:, :, None] == 0) | (d[:, :, None] == 0), np.float32(0.0), v)
     v = np.minimum(v, np.float32(6.0))                                         # saturation at 6
     mag = encode_e2m1_magnitude(v.astype(np.float64))
     sign = (np.signbit(blocks).astype(np.uint8) << 3)

@@ -18,7 +18,7 @@ def _declared_functions():
     names = set()
     for header in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
-        names.update(re.findall(r"\b(mxfp[48]_\w+)\s*\(", text))
+        names.update(re.findall(r"\b((?:mxfp[48]|nvfp4)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -243,3 +243,20 @@ def test_producers_reject_bad_arguments_on_host(lib):
     assert sw(f(), f(0x1008), 64, 4, 64, None, f(), f(), None) == 1                     # misaligned up
     assert sw(f(), f(), 64, (1 << 30) // 2 + 1, 64, None, f(), f(), None) == 1          # rows * k / 32
     assert sw(None, None, 64, 0, 64, None, None, None, None) == 0                       # no rows: no-op
+
+
+def test_nvfp4_entry_points_reject_bad_arguments_on_host(lib):
+    f = _fake
+    assert lib.nvfp4_quantize(f(), 4, 48, f(), f(), f(), None) == 1                # k % 32
+    assert lib.nvfp4_quantize(f(), 4, 32768 + 32, f(), f(), f(), None) == 1        # k too large
+    assert lib.nvfp4_quantize(f(), -1, 64, f(), f(), f(), None) == 1
+    assert lib.nvfp4_quantize(f(), 4, 64, f(), f(), None, None) == 1               # null global scales
+    assert lib.nvfp4_quantize(f(), 4, 64, f(), f(), f(0x1002), None) == 1          # misaligned global scales
+    assert lib.nvfp4_quantize(None, 0, 64, None, None, None, None) == 0            # no rows: no-op
+    g = lib.nvfp4_gemm_nt
+    assert g(f(), f(), f(), f(), f(), f(), f(), 0, 4, 4, 96, None) == 1             # k % 64
+    assert b"multiple of 64" in lib.mxfp4_last_error()
+    assert g(f(), f(), f(), f(), f(), f(), f(), 5, 4, 4, 64, None) == 1             # output type
+    assert g(f(), f(0x1002), f(), f(), f(), f(), f(), 0, 4, 4, 64, None) == 1       # misaligned a_s
+    assert g(f(), f(), f(), f(), f(), None, f(), 0, 4, 4, 64, None) == 1            # null b_gs
+    assert g(None, None, None, None, None, None, None, 0, 0, 4, 64, None) == 0      # m == 0: no-op
