@@ -14,7 +14,9 @@ device (`moe_layer`: top-k routing of the router logits, the expert-sorted
 permutation, MXFP4 quantization scattered into the routed rows, the grouped
 GEMM and the weighted combine), each step's time against its algorithmic
 bytes.  Also the fused producers (`producers`): residual add + RMSNorm and
-SwiGLU kernels that write their output straight as MXFP4, against HBM.
+SwiGLU kernels that write their output straight as MXFP4, against HBM; and
+NVFP4 (`nvfp4`: two-level quantization of A and the dequantizing GEMM, which
+runs on the BF16 MFMA) on the primary workload, against the BF16 peak.
 
 Inputs are resident in HBM before timing.  Steps rotate over enough copies of
 the inputs (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot serve
@@ -58,6 +60,7 @@ import workloads  # noqa: E402
 
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (an FP8 x FP4 MFMA runs at the FP8 rate)
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA (the NVFP4 GEMM's dequantized operands)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATION_BYTES = 512 << 20
 COPY_BYTES = 512 << 20        # size of the counter-calibration copy
@@ -422,6 +425,69 @@ def measure_producers(args, dev, us):
     return out
 
 
+class NvBench:
+    """NVFP4 on the prefill workload: two-level quantization of A (the step's
+    activation), and the dequantizing NT GEMM against a weight quantized once."""
+
+    def __init__(self, w: workloads.DenseWorkload, dev):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        self.w = w
+        a, b = w.make()
+        a_d = a.to(dev)
+        bq, bs, bg = B.nvfp4_quantize(b.to(dev))
+        m, n, k = w.m, w.n, w.k
+        per_set = m * k * 2 + m * (k // 2 + k // 16 + 4) + n * (k // 2 + k // 16 + 4) + m * n * 2
+        self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
+        self.sets = []
+        for _ in range(self.sets_n):
+            self.sets.append(dict(
+                a=a_d.clone(), aq=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+                as_=torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
+                ag=torch.empty((m,), dtype=torch.float32, device=dev),
+                bq=bq.clone(), bs=bs.clone(), bg=bg.clone(),
+                c=torch.empty((m, n), dtype=torch.bfloat16, device=dev)))
+        for i in range(self.sets_n):
+            self.quantize(i)
+        del a_d
+        torch.cuda.synchronize()
+
+    def quantize(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.nvfp4_quantize(s["a"], s["aq"], s["as_"], s["ag"])
+
+    def gemm(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.nvfp4_gemm_nt(s["aq"], s["as_"], s["ag"], s["bq"], s["bs"], s["bg"], c=s["c"])
+
+    def step(self, i):
+        self.quantize(i)
+        self.gemm(i)
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+
+def measure_nvfp4(args, dev, w, us):
+    eprint(f"[bench] NVFP4 on {w.name}")
+    nb = NvBench(w, dev)
+    s = nb.timed(nb.step, args.steps, args.warmup)
+    g = nb.timed(nb.gemm, args.steps, args.warmup)
+    q = nb.timed(nb.quantize, args.steps, args.warmup)
+    tf = w.flops / (g["mean"] * 1e-3) / 1e12
+    qbytes = w.m * w.k * 2 + w.m * (w.k // 2 + w.k // 16 + 4)
+    out = {"workload": w.name,
+           "dtype": "nvfp4 (e2m1, ue4m3 per 16, fp32 per row), exact bf16 dequantization, bf16 MFMA, fp32 accumulate",
+           "step_us": us(s), "gemm_us": us(g), "quantize_a_us": us(q),
+           "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+    eprint(f"[bench] NVFP4 {w.name}: step {s['mean']*1e3:.2f} us, gemm {g['mean']*1e3:.2f} us ({tf:.0f} TFLOP/s), "
+           f"quantize {q['mean']*1e3:.2f} us")
+    del nb
+    return out
+
+
 class Ceilings:
     """Measured ceilings on this GPU (include/mxfp4_probe.h), reported next to the
     published peaks: the FP4 scaled-MFMA rate of a kernel that only runs MFMAs
@@ -620,7 +686,9 @@ def run_only(args, dev):
         return
     w = workloads.ALL[args.workload]
     act = "mxfp8" if args.w4a8_only else "mxfp4"
-    if args.only in ("rmsnorm", "swiglu"):
+    if args.nvfp4_only and isinstance(w, workloads.DenseWorkload) and args.only in ("gemm", "quantize", "step"):
+        bench = NvBench(w, dev)
+    elif args.only in ("rmsnorm", "swiglu"):
         bench = ProducerBench(dev)
     elif args.only in ("route", "permute", "scatter", "combine", "layer"):
         if not isinstance(w, workloads.MoEWorkload):
@@ -665,8 +733,11 @@ def main():
                     help="eager launches for profiling; route/permute/scatter/combine/layer run the "
                          "on-device MoE layer's steps (layer = all five) on the MoE workload")
     ap.add_argument("--no-moe-layer", action="store_true", help="skip the on-device MoE layer measurement")
+    ap.add_argument("--no-nvfp4", action="store_true", help="skip the NVFP4 measurement")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the fused producer (RMSNorm / SwiGLU emitting MXFP4) measurement")
+    ap.add_argument("--nvfp4-only", action="store_true",
+                    help="with --only gemm/quantize/step: the NVFP4 kernels on the dense workload")
     ap.add_argument("--w4a8-only", action="store_true",
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
@@ -800,6 +871,9 @@ def main():
 
     if not args.no_w4a8:
         result["w4a8"] = measure_w4a8(args, dev, w, us)
+
+    if not args.no_nvfp4:
+        result["nvfp4"] = measure_nvfp4(args, dev, w, us)
 
     if not args.no_ceilings:
         eprint("[bench] measuring MFMA and streaming-read ceilings with the probe kernels")
