@@ -502,7 +502,8 @@ mxfp4_status_t mxfp4_moe_combine(const void* y_bf16, int64_t total_rows, int64_t
 mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_bf16, const void* gamma_bf16,
                                       float eps, int64_t rows, int64_t k, void* residual_out_bf16, void* y_bf16,
                                       void* q, void* scales, void* stream) {
-  if (rows < 0 || rows > ((int64_t)1 << 30)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^30 (got %lld)", (long long)rows);
+  // one 256-thread workgroup per row: a launch holds fewer than 2^32 threads
+  if (rows < 0 || rows > ((int64_t)1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^24 (got %lld)", (long long)rows);
   MXFP4_TRY(check_k(k));
   if (k > 256 * 8 * mxfp4::kNormMaxSlots)
     return fail(MXFP4_ERR_INVALID_ARG, "k must be at most %d for the RMSNorm producer (got %lld)",
@@ -550,7 +551,8 @@ mxfp4_status_t mxfp4_swiglu_quantize(const void* gate_bf16, const void* up_bf16,
 
 mxfp4_status_t nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q, void* scales,
                               float* global_scales, void* stream) {
-  if (rows < 0 || rows > ((int64_t)1 << 30)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^30 (got %lld)", (long long)rows);
+  // one 256-thread workgroup per row: a launch holds fewer than 2^32 threads
+  if (rows < 0 || rows > ((int64_t)1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^24 (got %lld)", (long long)rows);
   MXFP4_TRY(check_k(k));
   if (k > 256 * 8 * mxfp4::kNormMaxSlots)
     return fail(MXFP4_ERR_INVALID_ARG, "k must be at most %d for the NVFP4 quantizer (got %lld)",

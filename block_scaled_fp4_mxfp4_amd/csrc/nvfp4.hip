@@ -339,6 +339,7 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int ti
 
 hipError_t launch_nvfp4_quantize(const void* x, int rows, int k, void* q, void* scales, float* gs,
                                  hipStream_t stream) {
+  if (!grid_fits(rows, kNvQThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)rows), block(kNvQThreads);
   if (k <= 2 * 8 * kNvQThreads)
     hipLaunchKernelGGL(nvfp4_quantize_kernel<2>, grid, block, 0, stream, (const uint4*)x, k, (uint32_t*)q,

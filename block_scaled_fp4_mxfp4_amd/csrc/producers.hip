@@ -227,6 +227,7 @@ void launch_rmsnorm_slots(const void* x, const void* residual, const void* gamma
 // with it the rows in flight per CU, low.
 hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
                                    void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
+  if (!grid_fits(rows, kNormThreads)) return hipErrorInvalidConfiguration;
   if (k <= 2 * 8 * kNormThreads)
     launch_rmsnorm_slots<2>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
   else if (k <= 4 * 8 * kNormThreads)

@@ -47,8 +47,8 @@ extern "C" {
  * inv = 1 / sqrt(sum / k + eps) in fp64, y rounded once to BF16.  y therefore
  * equals the nearest BF16 of the exact value except where that value lies
  * within about 2^-50 (relative) of a BF16 rounding midpoint.
- * Limits: k a positive multiple of 32, k <= 32768; 0 <= rows <= 2^30;
- * rows == 0 is a no-op.
+ * Limits: k a positive multiple of 32, k <= 32768; 0 <= rows <= 2^24 (one
+ * workgroup per row); rows == 0 is a no-op.
  */
 mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_bf16, const void* gamma_bf16,
                                       float eps, int64_t rows, int64_t k, void* residual_out_bf16, void* y_bf16,

@@ -50,8 +50,8 @@ extern "C" {
  *   underflowing) encodes signed zeros.
  * x_bf16 [rows, k] (16-byte aligned); q [rows, k/2] (4-byte aligned); scales
  * [rows, k/16] (any alignment); global_scales [rows] (4-byte aligned).
- * Limits: k a positive multiple of 32, k <= 32768; 0 <= rows <= 2^30;
- * rows == 0 is a no-op.
+ * Limits: k a positive multiple of 32, k <= 32768; 0 <= rows <= 2^24 (one
+ * workgroup per row); rows == 0 is a no-op.
  */
 mxfp4_status_t nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t k, void* q, void* scales,
                               float* global_scales, void* stream);

@@ -260,3 +260,11 @@ def test_nvfp4_entry_points_reject_bad_arguments_on_host(lib):
     assert g(f(), f(0x1002), f(), f(), f(), f(), f(), 0, 4, 4, 64, None) == 1       # misaligned a_s
     assert g(f(), f(), f(), f(), f(), None, f(), 0, 4, 4, 64, None) == 1            # null b_gs
     assert g(None, None, None, None, None, None, None, 0, 0, 4, 64, None) == 0      # m == 0: no-op
+
+
+def test_row_per_workgroup_kernels_cap_rows(lib):
+    # RMSNorm producer and NVFP4 quantizer run one 256-thread workgroup per row
+    f = _fake
+    assert lib.mxfp4_rmsnorm_quantize(f(), None, f(), 1e-5, (1 << 24) + 1, 64, None, None, f(), f(), None) == 1
+    assert lib.nvfp4_quantize(f(), (1 << 24) + 1, 64, f(), f(), f(), None) == 1
+    assert b"2^24" in lib.mxfp4_last_error()
