@@ -481,7 +481,8 @@ def measure_nvfp4(args, dev, w, us):
            "step_us": us(s), "gemm_us": us(g), "quantize_a_us": us(q),
            "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_from_profiles(w.name, "nvfp4_gemm_kernel")}}
     eprint(f"[bench] NVFP4 {w.name}: step {s['mean']*1e3:.2f} us, gemm {g['mean']*1e3:.2f} us ({tf:.0f} TFLOP/s), "
            f"quantize {q['mean']*1e3:.2f} us")
     del nb
@@ -592,6 +593,8 @@ KERNEL_SOURCES = {
     "combine_kernel": ("moe.hip", "common.hpp"),
     "rmsnorm_quantize_kernel": ("producers.hip", "common.hpp"),
     "swiglu_quantize_kernel": ("producers.hip", "common.hpp"),
+    "nvfp4_quantize_kernel": ("nvfp4.hip", "common.hpp"),
+    "nvfp4_gemm_kernel": ("nvfp4.hip", "common.hpp"),
 }
 
 
