@@ -72,3 +72,42 @@ def test_moe_layer_and_producer_graph_replays_match_eager():
                                     "out", "producer q", "producer scales"),
                                    (ids, gate, off, rt, tr, aq, as_, y, out, pq, ps), eager):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}: {name}"
+
+
+def test_nvfp4_graph_replays_match_eager():
+    from block_scaled_fp4_mxfp4_amd import nvfp4_gemm_nt, nvfp4_quantize
+    dev = device()
+    m, n, k = 256, 384, 1024
+    log(f"graph: nvfp4 quantize + gemm m={m} n={n} k={k}")
+    a = workloads.activation_bf16(m, k, 960, outliers=True).to(dev)
+    b = workloads.gaussian_bf16((n, k), 0.02, 961).to(dev)
+    bq, bs, bg = nvfp4_quantize(b)
+    aq = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+    ag = torch.empty((m,), dtype=torch.float32, device=dev)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        nvfp4_quantize(a, aq, as_, ag)
+        nvfp4_gemm_nt(aq, as_, ag, bq, bs, bg, c=c)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (aq, as_, ag, c)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (aq, as_, ag, c):
+            t.view(torch.uint8).fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("q", "scales", "global scales", "c"), (aq, as_, ag, c), eager):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}: {name}"

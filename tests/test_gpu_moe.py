@@ -14,7 +14,10 @@
   nearest-even rounding of the kernel's own fp32 result;
 * the whole layer at the MoE workload's size (route -> permute ->
   scatter-quantize -> grouped GEMM -> combine), the index work checked in
-  full and the numbers on sampled tokens and columns.
+  full and the numbers on sampled tokens and columns; and a smaller layer with
+  MXFP8 activations (W4A8 grouped GEMM), its scattered bytes exact and its
+  outputs within 1e-2 floored max-rel of the float64 oracle (the GEMM's BF16
+  output and the MFMA's FP8 group rule each add a few 2^-9 at most).
 """
 import numpy as np
 import pytest
@@ -25,7 +28,7 @@ import workloads
 from block_scaled_fp4_mxfp4_amd import (mxfp4_grouped_gemm_nt, mxfp4_moe_combine, mxfp4_moe_permute,
                                         mxfp4_moe_quantize_scatter, mxfp4_moe_route, mxfp4_quantize,
                                         mxfp8_moe_quantize_scatter)
-from tests.gpu_common import device, log, poisoned, random_bf16, to_np, upload
+from tests.gpu_common import device, log, poisoned, random_bf16, sampled_indices, to_np, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -219,3 +222,39 @@ def test_moe_layer_full_size_sampled():
             ref += rgate[t, j] * oracle.gemm_nt(xq[i:i + 1], xs[i:i + 1], eq, es)[0]
         err = oracle.floored_max_rel(got[t, cols], ref)
         assert err <= 1e-2, f"token {t}: floored max-rel {err}"
+
+
+def test_w4a8_moe_layer_sampled():
+    """The same layer with MXFP8 activations: route -> permute -> MXFP8 scatter-quantize ->
+    W4A8 grouped GEMM -> combine, on a 1024-token, 16-expert layer."""
+    from block_scaled_fp4_mxfp4_amd import mxfp8_grouped_gemm_w4a8_nt
+    dev = device()
+    tokens, experts, top_k, n, k = 1024, 16, 2, 256, 1024
+    log(f"w4a8 moe layer T={tokens} E={experts} k={top_k} N={n} K={k}")
+    x = workloads.activation_bf16(tokens, k, 950, outliers=True)
+    lg = workloads.gaussian_bf16((tokens, experts), 1.5, 951).float()
+    w = workloads.gaussian_bf16((experts * n, k), 0.02, 952)
+    wq, ws = mxfp4_quantize(w.to(dev))
+    wq, ws = wq.view(experts, n, k // 2), ws.view(experts, n, k // 32)
+    rows = tokens * top_k
+    ids, gate = mxfp4_moe_route(lg.to(dev), top_k)
+    off, rt, tr = mxfp4_moe_permute(ids, experts)
+    aq, as_ = mxfp8_moe_quantize_scatter(x.to(dev), tr, rows)
+    y = mxfp8_grouped_gemm_w4a8_nt(aq, as_, wq, ws, off)
+    out = mxfp4_moe_combine(y, tr, gate, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rid, rgate = oracle.route_topk(lg.numpy(), top_k)
+    ro, rrt, rtr = oracle.permute(rid, experts)
+    assert np.array_equal(to_np(ids), rid) and np.array_equal(to_np(off), ro) and np.array_equal(to_np(tr), rtr)
+    rq, rs, written = oracle.quantize_scatter_mxfp8(workloads.bf16_bits(x), rtr, rows)
+    assert written.all() and np.array_equal(to_np(aq), rq) and np.array_equal(to_np(as_), rs)
+    # float64 reference from the oracle's own operands: per token, the gate-weighted expert outputs
+    wq_np, ws_np = to_np(wq), to_np(ws)
+    toks = sampled_indices(tokens, 24, 12)
+    got = to_np(out).astype(np.float64)
+    for t in toks:
+        ref = np.zeros(n)
+        for j in range(top_k):
+            e, r = int(rid[t, j]), int(rtr[t, j])
+            ref += rgate[t, j] * oracle.gemm_w4a8_nt(rq[r:r + 1], rs[r:r + 1], wq_np[e], ws_np[e])[0]
+        assert oracle.floored_max_rel(got[t], ref) <= 1e-2, f"token {t}"
