@@ -140,13 +140,27 @@ __global__ __launch_bounds__(kNvQThreads) void nvfp4_quantize_kernel(const uint4
 // GEMM
 // ---------------------------------------------------------------------------
 
-constexpr int kNvBM = 128, kNvBN = 128, kNvBK = 64;
-constexpr int kNvThreads = 256;                 // 4 waves, 2 x 2 over the tile, 64 x 64 each
+constexpr int kNvBK = 64;                       // K elements per stage
 constexpr int kNvPitch = kNvBK * 2 + 16;        // bytes per BF16 LDS row (padded)
-constexpr int kNvTile = kNvBM * kNvPitch;       // one operand's BF16 stage
-constexpr int kNvStage = 2 * kNvTile;           // A then B
-constexpr int kNvLds = 2 * kNvStage;
 constexpr int kNvRing = 4;                      // packed stages in flight per thread
+
+// Square BM x BM output tiles; each of the 2 * BM threads loads and
+// dequantizes one 32-element half row of A and one of B per stage.  The waves
+// form a WGM x WGN grid, each owning (BM / WGM) x (BM / WGN) in 32 x 32 MFMA
+// blocks.
+template <int BM_, int WGM_, int WGN_>
+struct NvCfg {
+  static constexpr int BM = BM_, WGM = WGM_, WGN = WGN_;
+  static constexpr int THREADS = 2 * BM;
+  static constexpr int MI = BM / WGM / 32, NI = BM / WGN / 32;
+  static constexpr int TILE = BM * kNvPitch;    // one operand's BF16 stage
+  static constexpr int STAGE = 2 * TILE;        // A then B
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(WGM * WGN * 64 == THREADS, "one wave per 64 threads");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+using NvSmall = NvCfg<128, 2, 2>;   // 4 waves of 64 x 64
+using NvLarge = NvCfg<256, 2, 4>;   // 8 waves of 128 x 64: half the dequantized elements per flop
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
@@ -217,10 +231,11 @@ __device__ __forceinline__ void nv_dequant(const NvLoad& L, NvDeq& D) {
   }
 }
 
+template <class C>
 __device__ __forceinline__ void nv_write(const NvDeq& D, uint8_t MXFP4_LDS* stage) {
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
   uint8_t MXFP4_LDS* arow = stage + r * kNvPitch + half * 64;
-  uint8_t MXFP4_LDS* brow = stage + kNvTile + r * kNvPitch + half * 64;
+  uint8_t MXFP4_LDS* brow = stage + C::TILE + r * kNvPitch + half * 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     *(v4i MXFP4_LDS*)(arow + 16 * i) = D.a[i];
@@ -228,21 +243,22 @@ __device__ __forceinline__ void nv_write(const NvDeq& D, uint8_t MXFP4_LDS* stag
   }
 }
 
-__global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int tiles_m, int tiles_n) {
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void nvfp4_gemm_kernel(NvArgs p, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-  const int m0 = tm * kNvBM, n0 = tn * kNvBN;
+  const int m0 = tm * C::BM, n0 = tn * C::BM;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm0 = (w >> 1) * 64, wn0 = (w & 1) * 64;
+  const int wm0 = (w / C::WGN) * (C::BM / C::WGM), wn0 = (w % C::WGN) * (C::BM / C::WGN);
   const int nk = p.k / kNvBK;
 
-  v16f acc[2][2];
+  v16f acc[C::MI][C::NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int ti
   {
     NvDeq D0;
     nv_dequant(L[0], D0);
-    nv_write(D0, lds);
+    nv_write<C>(D0, lds);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; kt += kNvRing) {
@@ -265,21 +281,21 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int ti
       const int t = kt + u;
       if (t >= nk) break;
       if (t + kNvRing < nk) nv_load(p, m0, n0, t + kNvRing, L[u]);   // L[u] held stage t, stored already
-      const uint8_t MXFP4_LDS* st = lds + (t & 1) * kNvStage;
+      const uint8_t MXFP4_LDS* st = lds + (t & 1) * C::STAGE;
 #pragma unroll
       for (int ks = 0; ks < kNvBK / 16; ++ks) {
         const int koff = ks * 32 + (lane >> 5) * 16;       // bytes: 16 K per step, 8 per lane half
-        bf16x8_t af[2], bfr[2];
+        bf16x8_t af[C::MI], bfr[C::NI];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < C::MI; ++i)
           af[i] = *(const bf16x8_t MXFP4_LDS*)(st + (wm0 + 32 * i + (lane & 31)) * kNvPitch + koff);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *(const bf16x8_t MXFP4_LDS*)(st + kNvTile + (wn0 + 32 * j + (lane & 31)) * kNvPitch + koff);
+        for (int j = 0; j < C::NI; ++j)
+          bfr[j] = *(const bf16x8_t MXFP4_LDS*)(st + C::TILE + (wn0 + 32 * j + (lane & 31)) * kNvPitch + koff);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < C::NI; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
       // the other buffer was last read before the previous barrier
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int ti
       if (t + 1 < nk) {
         NvDeq D;
         nv_dequant(L[(u + 1) % kNvRing], D);
-        nv_write(D, lds + ((t + 1) & 1) * kNvStage);
+        nv_write<C>(D, lds + ((t + 1) & 1) * C::STAGE);
       }
       __syncthreads();
     }
@@ -298,12 +314,12 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_gemm_kernel(NvArgs p, int ti
   // lane l holds output row (l % 32) of each 32-row block and, in register
   // r, column (r / 4) * 8 + (l / 32) * 4 + r % 4 of each 32-column block
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < C::MI; ++i) {
     const int row = m0 + wm0 + 32 * i + (lane & 31);
     if (row >= p.m) continue;
     const float ga = p.a_gs[row];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::NI; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = n0 + wn0 + 32 * j + g * 8 + (lane >> 5) * 4;
@@ -353,17 +369,25 @@ hipError_t launch_nvfp4_quantize(const void* x, int rows, int k, void* q, void* 
   return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_nv_cfg(const NvArgs& p, hipStream_t stream) {
+  const int tiles_m = (p.m + C::BM - 1) / C::BM, tiles_n = (p.n + C::BM - 1) / C::BM;
+  const int64_t blocks = (int64_t)tiles_m * tiles_n;
+  if (!grid_fits(blocks, C::THREADS)) return hipErrorInvalidConfiguration;
+  hipError_t e = hipFuncSetAttribute((const void*)nvfp4_gemm_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nvfp4_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), C::LDS, stream, p, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// 256 x 256 tiles once they fill the chip (256 tiles), 128 x 128 below that.
 hipError_t launch_nvfp4_gemm(const void* a_q, const void* a_s, const float* a_gs, const void* b_q, const void* b_s,
                              const float* b_gs, void* c, bool c_f32, int m, int n, int k, hipStream_t stream) {
   NvArgs p{(const uint8_t*)a_q, (const uint8_t*)a_s, a_gs, (const uint8_t*)b_q, (const uint8_t*)b_s, b_gs,
            c, c_f32 ? 1 : 0, m, n, k};
-  const int tiles_m = (m + kNvBM - 1) / kNvBM, tiles_n = (n + kNvBN - 1) / kNvBN;
-  const int64_t blocks = (int64_t)tiles_m * tiles_n;
-  if (!grid_fits(blocks, kNvThreads)) return hipErrorInvalidConfiguration;
-  hipError_t e = hipFuncSetAttribute((const void*)nvfp4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kNvLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nvfp4_gemm_kernel, dim3((unsigned)blocks), dim3(kNvThreads), kNvLds, stream, p, tiles_m, tiles_n);
-  return hipGetLastError();
+  const int64_t large_tiles = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+  if (large_tiles >= 256) return launch_nv_cfg<NvLarge>(p, stream);
+  return launch_nv_cfg<NvSmall>(p, stream);
 }
 
 }  // namespace mxfp4

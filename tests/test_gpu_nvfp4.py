@@ -117,3 +117,21 @@ def test_nvfp4_gemm_prefill_full_size_sampled():
     ref = oracle.gemm_nvfp4_nt(*ra, *rb)
     got = to_np(c)[np.ix_(rows, cols)].astype(np.float64)
     assert oracle.floored_max_rel(got, ref) <= 1e-5
+
+
+def test_nvfp4_gemm_large_tiles_ragged_sampled():
+    """4100 x 4000 needs 17 x 16 >= 256 tiles of 256 x 256: the large-tile configuration, ragged on both edges."""
+    dev = device()
+    m, n, k = 4100, 4000, 128
+    log(f"nvfp4 gemm large tiles m={m} n={n} k={k}")
+    aq, as_, ag = _random_nvfp4(m, k, 31)
+    bq, bs, bg = _random_nvfp4(n, k, 32)
+    c_all = poisoned((m + 1, n), torch.float32, dev, 0xFF)
+    nvfp4_gemm_nt(*[upload(t, dev) for t in (aq, as_, ag, bq, bs, bg)], c=c_all[:m])
+    torch.cuda.synchronize()
+    assert torch.all(c_all[m:].view(torch.uint8) == 0xFF), "write past C"
+    rows = np.unique(np.concatenate([sampled_indices(m, 24, 6), np.arange(m - 8, m)]))
+    cols = np.unique(np.concatenate([sampled_indices(n, 48, 7), np.arange(n - 8, n)]))
+    ref = oracle.gemm_nvfp4_nt(aq[rows], as_[rows], ag[rows], bq[cols], bs[cols], bg[cols])
+    got = to_np(c_all[:m])[np.ix_(rows, cols)].astype(np.float64)
+    assert oracle.floored_max_rel(got, ref) <= 1e-5
