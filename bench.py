@@ -747,8 +747,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        eprint("bench.py runs on one GPU only: this build has no multi-GPU path "
-               "(sharding across GPUs is described in the design notes, not implemented).")
+        eprint("bench.py runs on one GPU only: the library has no multi-GPU path "
+               "(how the GEMMs would shard across GPUs is described in the design notes, not implemented).")
         sys.exit(2)
     if not torch.cuda.is_available():
         eprint("no GPU visible")

@@ -50,7 +50,7 @@ def load_library(path: str = LIB_PATH):
         if _lib is not None:
             return _lib
         if not os.path.exists(path):
-            raise ImportError(f"{path} is not built; run __graft_entry__.build()")
+            raise ImportError(f"{path} is not built; build it with: python -m block_scaled_fp4_mxfp4_amd.build")
         lib = ctypes.CDLL(path)
         i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
         lib.mxfp4_abi_version.restype = ctypes.c_int

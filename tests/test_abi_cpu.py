@@ -25,7 +25,7 @@ def _declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(binding.LIB_PATH):
-        pytest.fail("libmxfp4.so is not built (run __graft_entry__.build())")
+        pytest.fail("libmxfp4.so is not built (build it with: python -m block_scaled_fp4_mxfp4_amd.build)")
     return binding.load_library()
 
 
