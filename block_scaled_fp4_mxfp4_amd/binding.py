@@ -30,6 +30,7 @@ EXPORTED = (
     "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
+    "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -78,6 +79,12 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_gemm_nt_ex.restype = ctypes.c_int
         lib.mxfp4_gemm_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64,
                                          ctypes.c_int, i32, vp, sz, vp]
+        lib.mxfp4_prepacked_weight_size.restype = ctypes.c_int
+        lib.mxfp4_prepacked_weight_size.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.mxfp4_prepack_weight.restype = ctypes.c_int
+        lib.mxfp4_prepack_weight.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_gemm_nt_prepacked.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_prepacked.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp4_grouped_gemm_nt_workspace_size.restype = sz
         lib.mxfp4_grouped_gemm_nt_workspace_size.argtypes = [i64, i32, i64, i64]
         lib.mxfp4_grouped_gemm_nt.restype = ctypes.c_int
@@ -220,6 +227,48 @@ def mxfp4_gemm_nt(a_q, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxfp4_gemm_nt_ex(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
                                 kid, splits, _ptr(ws), nbytes, _stream(stream)))
+    return c
+
+
+def mxfp4_prepacked_weight_size(n: int, k: int) -> tuple[int, int]:
+    """(code_bytes, scale_bytes) of a prepacked [n, k] MXFP4 weight (k % 512 == 0)."""
+    lib = load_library()
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.mxfp4_prepacked_weight_size(n, k, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def mxfp4_prepack_weight(b_q, b_s, bp_q=None, bp_s=None, stream=None):
+    """Rearranges an MXFP4 weight [n, k] into the prepacked layout; returns (bp_q, bp_s) as flat uint8."""
+    lib = load_library()
+    n, kh = b_q.shape
+    k = kh * 2
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (n, k // 32))
+    cb, sb = mxfp4_prepacked_weight_size(n, k)
+    if bp_q is None:
+        bp_q = torch.empty(cb, dtype=torch.uint8, device=b_q.device)
+    if bp_s is None:
+        bp_s = torch.empty(sb, dtype=torch.uint8, device=b_q.device)
+    _require(bp_q, "bp_q", torch.uint8, (cb,))
+    _require(bp_s, "bp_s", torch.uint8, (sb,))
+    _check(lib.mxfp4_prepack_weight(_ptr(b_q), _ptr(b_s), n, k, _ptr(bp_q), _ptr(bp_s), _stream(stream)))
+    return bp_q, bp_s
+
+
+def mxfp4_gemm_nt_prepacked(a_q, a_s, bp_q, bp_s, n: int, c=None, out_dtype=torch.bfloat16, stream=None):
+    """C[m, n] = A . B^T with B given in the prepacked layout (mxfp4_prepack_weight)."""
+    lib = load_library()
+    m, kh = a_q.shape
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (m, k // 2))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    cb, sb = mxfp4_prepacked_weight_size(n, k)
+    _require(bp_q, "bp_q", torch.uint8, (cb,))
+    _require(bp_s, "bp_s", torch.uint8, (sb,))
+    c, code = _out(c, m, n, out_dtype, a_q.device)
+    _check(lib.mxfp4_gemm_nt_prepacked(_ptr(a_q), _ptr(a_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
+                                       _stream(stream)))
     return c
 
 

@@ -271,6 +271,61 @@ mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, 
                           workspace_bytes, stream);
 }
 
+mxfp4_status_t mxfp4_prepacked_weight_size(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return fail(MXFP4_ERR_INVALID_ARG, "size outputs are NULL");
+  if (n < 0 || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "n out of range");
+  MXFP4_TRY(check_k(k));
+  if (k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  mxfp4::prepacked_sizes(n, k, code_bytes, scale_bytes);
+  return MXFP4_OK;
+}
+
+mxfp4_status_t mxfp4_prepack_weight(const void* b_q, const void* b_s, int64_t n, int64_t k, void* bp_q, void* bp_s,
+                                    void* stream) {
+  int64_t cb, sb;
+  MXFP4_TRY(mxfp4_prepacked_weight_size(n, k, &cb, &sb));
+  if (n == 0) return MXFP4_OK;
+  if ((n + 63) / 64 * (k / 512) > (int64_t)0xFFFFFFFF / 256) return fail(MXFP4_ERR_INVALID_ARG, "weight too large");
+  MXFP4_TRY(check_ptr(b_q, "b_q"));
+  MXFP4_TRY(check_ptr(b_s, "b_s", 1));
+  MXFP4_TRY(check_ptr(bp_q, "bp_q"));
+  MXFP4_TRY(check_ptr(bp_s, "bp_s"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_prepack_weight((const uint8_t*)b_q, (const uint8_t*)b_s, (int)n, (int)k,
+                                                 (uint8_t*)bp_q, (uint8_t*)bp_s, (hipStream_t)stream),
+                    "prepack launch");
+}
+
+mxfp4_status_t mxfp4_gemm_nt_prepacked(const void* a_q, const void* a_s, const void* bp_q, const void* bp_s, void* c,
+                                       mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
+  MXFP4_TRY(check_k(k));
+  if (k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(a_q, "a_q"));
+  MXFP4_TRY(check_ptr(a_s, "a_s"));
+  MXFP4_TRY(check_ptr(bp_q, "bp_q"));
+  MXFP4_TRY(check_ptr(bp_s, "bp_s"));
+  MXFP4_TRY(check_ptr(c, "c"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)bp_q;
+  args.b_s = (const uint8_t*)bp_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  return hip_status(mxfp4::launch_gemm_stream_prepacked(args, (hipStream_t)stream), "prepacked gemm launch");
+}
+
 size_t mxfp4_grouped_gemm_nt_workspace_size(int64_t total_m, int32_t num_groups, int64_t n, int64_t k) {
   (void)total_m; (void)num_groups; (void)n; (void)k;
   return 0;

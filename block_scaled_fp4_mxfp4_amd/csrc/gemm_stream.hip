@@ -55,17 +55,19 @@ constexpr int kBN = 64;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-template <int MB_, int NP_, bool A8_ = false>
+template <int MB_, int NP_, bool A8_ = false, bool PRE_ = false>
 struct StreamCfg {
   static constexpr int MB = MB_, NP = NP_;
   static constexpr bool A8 = A8_;                          // A in FP8 E4M3 (W4A8)
+  static constexpr bool PRE = PRE_;                        // B prepacked, loaded into registers
   static constexpr int BM = 32 * MB;
-  static constexpr int ROWS = BM + kBN;                   // A rows, then B rows
+  static constexpr int B_LDS_ROWS = PRE ? 0 : kBN;         // B rows staged in LDS
+  static constexpr int ROWS = BM + B_LDS_ROWS;             // A rows, then B rows
   static constexpr int A_ROW = A8 ? 2 * kRowBytes : kRowBytes;
   static constexpr int A_SHIFT = A8 ? 4 : 3;               // log2 of the 16-byte chunks in an A row
   static constexpr int A_BYTES = BM * A_ROW;
   static constexpr int A_SLOTS = A_BYTES / 16;
-  static constexpr int STAGE = A_BYTES + kBN * kRowBytes;
+  static constexpr int STAGE = A_BYTES + B_LDS_ROWS * kRowBytes;
   static constexpr int SCALES = kThreads * 16;            // one 16-byte piece per thread (rows >= ROWS: padding)
   static constexpr int PAIR = 2 * STAGE + SCALES;
   static constexpr int CODE_LOADS = STAGE / 16 / kThreads;  // 16-byte copies per thread per stage
@@ -76,7 +78,7 @@ struct StreamCfg {
   static constexpr int LDS = (NP * PAIR > XCH + C_TILE) ? NP * PAIR : XCH + C_TILE;
   static_assert(STAGE % (16 * kThreads) == 0, "code copies must split evenly over the threads");
   static_assert(A_SLOTS % 64 == 0, "a wave's copy instruction lies wholly in A or in B");
-  static_assert(ROWS <= kThreads, "one scale piece per row");
+  static_assert(ROWS <= (PRE ? 3 * 64 : kThreads), "one scale piece per row (prepacked B: wave 3 copies B's scales)");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert((NP - 2) * PAIR_LOADS <= 63, "vmcnt range");
 };
@@ -172,11 +174,13 @@ __device__ __forceinline__ void read_step(const uint8_t MXFP4_LDS* buf, int s, i
     }
     st.sa[i] = scales[r * 16];
   }
+  if constexpr (!C::PRE) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 32 * j + (lane & 31);
-    st.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
-    st.sb[j] = scales[(C::BM + r) * 16];
+    for (int j = 0; j < 2; ++j) {
+      const int r = 32 * j + (lane & 31);
+      st.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
+      st.sb[j] = scales[(C::BM + r) * 16];
+    }
   }
 }
 
@@ -205,54 +209,14 @@ __device__ __forceinline__ bool stream_coords(int b, int tiles_m, int tiles_n, i
   return tn < tiles_n;
 }
 
+// Reduce-scatter of the four waves' fp32 partial tiles and the stores of C.
 template <class C>
-__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
-  int tm, tn;
-  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
-  const int m0 = tm * C::BM, n0 = tn * kBN;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-
-  v16f acc[C::MB][2];
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  Sources<C> src;
-  make_sources<C>(src, args, m0, n0);
-  const int np = args.k / 512;
-  for (int p = 0; p < C::NP - 1 && p < np; ++p) copy_pair<C>(lds + p * C::PAIR, src, p);
-
-  int slot = 0;                 // ring buffer of pair p
-  for (int p = 0; p < np; ++p) {
-    // pair p has landed for this thread; the pairs issued after it may still fly
-    wait_pairs<C>(min(C::NP - 2, np - 1 - p));
-    // ... and for every thread; every wave has also finished reading pair p - 1
-    barrier_lds();
-    if (p + C::NP - 1 < np) {
-      const int refill = (slot == 0) ? C::NP - 1 : slot - 1;   // buffer of pair p - 1
-      copy_pair<C>(lds + refill * C::PAIR, src, p + C::NP - 1);
-    }
-    const uint8_t MXFP4_LDS* buf = lds + slot * C::PAIR;
-    Step<C> s0, s1;
-    read_step<C>(buf, 0, w, lane, s0);
-    read_step<C>(buf, 1, w, lane, s1);
-    mma_step<C>(s0, acc);
-    mma_step<C>(s1, acc);
-    slot = (slot + 1 == C::NP) ? 0 : slot + 1;
-  }
-  MXFP4_WAIT_VMCNT(0);
-  __syncthreads();   // every wave is done with the ring
-
-  // Reduce-scatter of the four waves' fp32 partial tiles.  The accumulators
-  // split into U units of 64 lanes x 4 floats (row block i, column block j,
-  // column group q); wave w owns units [w*U/4, (w+1)*U/4).  Each wave parks the
-  // units it does not own in LDS, then sums each of its units over the waves in
-  // the fixed order 0, 1, 2, 3.
+__device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const GemmArgs& args, int m0, int n0,
+                                                uint8_t MXFP4_LDS* lds, int w, int lane) {
+  // The accumulators split into U units of 64 lanes x 4 floats (row block i,
+  // column block j, column group q); wave w owns units [w*U/4, (w+1)*U/4).
+  // Each wave parks the units it does not own in LDS, then sums each of its
+  // units over the waves in the fixed order 0, 1, 2, 3.
   constexpr int U = C::MB * 8, UW = U / 4;
   v4f MXFP4_LDS* xch = (v4f MXFP4_LDS*)lds;
 #pragma unroll
@@ -330,6 +294,52 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, in
 }
 
 template <class C>
+__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
+  int tm, tn;
+  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  const int m0 = tm * C::BM, n0 = tn * kBN;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  v16f acc[C::MB][2];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  Sources<C> src;
+  make_sources<C>(src, args, m0, n0);
+  const int np = args.k / 512;
+  for (int p = 0; p < C::NP - 1 && p < np; ++p) copy_pair<C>(lds + p * C::PAIR, src, p);
+
+  int slot = 0;                 // ring buffer of pair p
+  for (int p = 0; p < np; ++p) {
+    // pair p has landed for this thread; the pairs issued after it may still fly
+    wait_pairs<C>(min(C::NP - 2, np - 1 - p));
+    // ... and for every thread; every wave has also finished reading pair p - 1
+    barrier_lds();
+    if (p + C::NP - 1 < np) {
+      const int refill = (slot == 0) ? C::NP - 1 : slot - 1;   // buffer of pair p - 1
+      copy_pair<C>(lds + refill * C::PAIR, src, p + C::NP - 1);
+    }
+    const uint8_t MXFP4_LDS* buf = lds + slot * C::PAIR;
+    Step<C> s0, s1;
+    read_step<C>(buf, 0, w, lane, s0);
+    read_step<C>(buf, 1, w, lane, s1);
+    mma_step<C>(s0, acc);
+    mma_step<C>(s1, acc);
+    slot = (slot + 1 == C::NP) ? 0 : slot + 1;
+  }
+  MXFP4_WAIT_VMCNT(0);
+  __syncthreads();   // every wave is done with the ring
+
+  stream_epilogue<C>(acc, args, m0, n0, lds, w, lane);
+}
+
+template <class C>
 hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
   const auto kernel = gemm_stream_kernel<C>;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
@@ -342,6 +352,314 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Prepacked weights.  A weight matrix is quantized once, so its layout in HBM
+// is free: the prepacked form stores, for every 64-row panel of B and every
+// 512-K pair, the exact bytes each lane of each wave feeds the MFMA, so a wave
+// loads B straight into registers with whole 1 KB contiguous reads and B needs
+// no LDS at all.  Per (panel, pair):
+//   codes, 16 KB: byte w*4096 + u*1024 + l*16 + c, u = 2s + j, is code byte c
+//     of row 64*panel + 32j + (l % 32) at row byte 256*pair + 128s + 32w +
+//     16*(l / 32) (wave w's k-step of stage s, column block j, lane l);
+//   scales, 1 KB: byte w*256 + l*4 + (2s + j) is the scale of that row for
+//     the 32-element block 16*pair + 8s + 2w + l / 32.
+// Rows past N are zero codes with scale byte 0.  Panels are stored in order,
+// pairs in order within a panel.
+constexpr int kPreCodeBlock = 16 * 1024;
+constexpr int kPreScaleBlock = 1024;
+constexpr int kPreDepth = 8;   // B pairs in each wave's register ring
+constexpr int kPreBLoads = 4;  // vector-memory ops per B pair per thread
+
+__global__ __launch_bounds__(kThreads) void prepack_kernel(const uint8_t* __restrict__ b_q,
+                                                           const uint8_t* __restrict__ b_s, int n, int k,
+                                                           uint8_t* __restrict__ bp_q, uint8_t* __restrict__ bp_s) {
+  const int np = k / 512;
+  const int64_t blk = blockIdx.x;                    // panel * np + pair
+  const int panel = (int)(blk / np), p = (int)(blk - (int64_t)panel * np);
+  const int64_t kb = k / 2, ks = k / 32;
+  for (int c = threadIdx.x; c < kPreCodeBlock / 16; c += kThreads) {
+    const int w = c >> 8, u = (c >> 6) & 3, l = c & 63;
+    const int s = u >> 1, j = u & 1;
+    const int row = panel * kBN + 32 * j + (l & 31);
+    v4i v = {0, 0, 0, 0};
+    if (row < n) v = *(const v4i*)(b_q + row * kb + 256 * p + 128 * s + 32 * w + 16 * (l >> 5));
+    *(v4i*)(bp_q + blk * kPreCodeBlock + c * 16) = v;
+  }
+  const int d = threadIdx.x, w = d >> 6, l = d & 63;   // one scale word per thread
+  uint32_t word = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int s = b >> 1, j = b & 1;
+    const int row = panel * kBN + 32 * j + (l & 31);
+    if (row < n) word |= (uint32_t)b_s[row * ks + 16 * p + 8 * s + 2 * w + (l >> 5)] << (8 * b);
+  }
+  *(uint32_t*)(bp_s + blk * kPreScaleBlock + d * 4) = word;
+}
+
+// A's copies in the prepacked kernel: buffer_load ... lds (MUBUF) rather than
+// global_load_lds.  The latter is a FLAT-encoded instruction that also writes
+// LDS, and while one is outstanding the compiler takes the vector-memory
+// counter to be out of order and waits for zero before any use of a register
+// loaded from memory, which would drain the whole B ring.  Buffer copies keep
+// every vector-memory op in one in-order class.  Offsets past a resource's
+// bytes read zeros, so no copy can leave the tile's A rows or the panel.
+//   code copies: resource over A rows [m0, m0 + rows), per-thread voffset of
+//                its row and chunk, soffset = the 128-byte stage step;
+//   scale pieces: waves 0-2 copy A rows' 16-byte pieces (rows past the tile
+//                 re-read its first row), wave 3 copies the panel's prepacked
+//                 B scale block (1 KB per pair), landing at LDS byte 3072 of
+//                 the pair's scale area.
+template <class C>
+struct PreCopies {
+  __amdgpu_buffer_rsrc_t code;
+  __amdgpu_buffer_rsrc_t scale;   // wave-uniform: A scales (waves 0-2) or B's prepacked scales (wave 3)
+  uint32_t code_off[C::CODE_LOADS];
+  uint32_t scale_off;
+  uint32_t scale_step;            // bytes per pair in the scale resource
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  return make_rsrc((const void*)(uintptr_t)u, bytes);
+}
+
+template <class C>
+__device__ __forceinline__ void make_pre_copies(PreCopies<C>& cp, const GemmArgs& args, int m0, int tn, int np,
+                                                int w, int lane) {
+  const int kb = args.k / 2, ks = args.k / 32;
+  const int rows = min(C::BM, args.m - m0);
+  cp.code = uniform_rsrc(args.a_q + (int64_t)m0 * kb, (uint32_t)rows * kb);
+#pragma unroll
+  for (int j = 0; j < C::CODE_LOADS; ++j) {
+    const int slot = (j * 4 + w) * 64 + lane;
+    const int r = slot >> 3;
+    const int lc = (slot & 7) ^ swz(r);
+    cp.code_off[j] = (uint32_t)min(r, rows - 1) * kb + lc * 16;
+  }
+  if (w == 3) {
+    cp.scale = uniform_rsrc(args.b_s + (int64_t)tn * np * kPreScaleBlock, (uint32_t)np * kPreScaleBlock);
+    cp.scale_off = lane * 16;
+    cp.scale_step = kPreScaleBlock;
+  } else {
+    cp.scale = uniform_rsrc(args.a_s + (int64_t)m0 * ks, (uint32_t)rows * ks);
+    const int r = w * 64 + lane;
+    cp.scale_off = (uint32_t)(r < rows ? r : 0) * ks;
+    cp.scale_step = 16;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void copy_pair_pre(uint8_t MXFP4_LDS* buf, const PreCopies<C>& cp, int p, int w) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < C::CODE_LOADS; ++j)
+      buf2lds_16(cp.code, cp.code_off[j], (uint32_t)(2 * p + s) * kRowBytes,
+                 (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
+  buf2lds_16(cp.scale, cp.scale_off, (uint32_t)p * cp.scale_step, (MXFP4_LDS void*)(buf + 2 * C::STAGE + w * 64 * 16));
+}
+
+// One wave's B operands of one pair: q[2s + j] feeds stage s, column block j.
+struct BPair {
+  v4i q[4];
+};
+
+// The four 1 KB loads of pair p.  The pair's offset goes in the per-lane
+// offset, which the buffer's range check covers, so a pair past the panel's
+// last one reads zeros without touching memory.  The empty asm statements keep
+// these loads and the LDS copies in program order, which the vmcnt arithmetic
+// counts on.
+__device__ __forceinline__ void load_bpair(BPair& b, __amdgpu_buffer_rsrc_t r, uint32_t voff, int p) {
+  asm volatile("" ::: "memory");
+  const uint32_t off = voff + (uint32_t)p * kPreCodeBlock;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    b.q[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + u * 1024, 0, 0));
+  asm volatile("" ::: "memory");
+}
+
+// Issue order: a prologue of steps q = 0 .. D-2, each [A pair q if q <= NP-2]
+// [B pair q], then in iteration t [A pair t+NP-1 if it exists][B pair t+D-1].
+// Prologue A copies past the last pair re-copy the last pair (only when
+// K < 512 * (NP - 1)).  Loads past the last B pair fall outside the panel's
+// buffer and return zeros without touching memory; the runtime-K loop issues
+// them so that no path through it skips a load (which keeps the compiler's
+// own waits for the B registers tight), but their results are never used and
+// the compiler may delete them.  Loads complete in order, so "A pair p has
+// landed" is "at most the ops issued after it are outstanding".  This counts
+// those ops at the top of iteration p, leaving out every B load past the last
+// pair: if such a load was issued, the wait is only stricter than needed.
+// At most NP - 1 A pairs and D - 1 B pairs are ever outstanding, which keeps
+// the count inside the counter's range (< 64).
+template <class C>
+__host__ __device__ constexpr int pre_ops_after_a(int p, int np) {
+  constexpr int LA = C::PAIR_LOADS, LB = kPreBLoads, NP = C::NP, D = kPreDepth;
+  int cnt = 0, t = 0;
+  if (p <= NP - 2) {
+    cnt += LB;           // B pair p follows A pair p in prologue step p
+    for (int q = p + 1; q <= D - 2; ++q) cnt += (q <= NP - 2 ? LA : 0) + (q < np ? LB : 0);
+  } else {
+    const int t0 = p - NP + 1;   // the iteration that issued A pair p
+    cnt += (t0 + D - 1 < np) ? LB : 0;
+    t = t0 + 1;
+  }
+  for (; t < p; ++t) cnt += ((t + NP - 1 < np) ? LA : 0) + ((t + D - 1 < np) ? LB : 0);
+  return cnt;
+}
+
+#define MXFP4_VM_CASE(n) \
+  case n:                \
+    MXFP4_WAIT_VMCNT(n); \
+    break;
+#define MXFP4_VM_CASE8(n) \
+  MXFP4_VM_CASE(n) MXFP4_VM_CASE(n + 1) MXFP4_VM_CASE(n + 2) MXFP4_VM_CASE(n + 3) \
+  MXFP4_VM_CASE(n + 4) MXFP4_VM_CASE(n + 5) MXFP4_VM_CASE(n + 6) MXFP4_VM_CASE(n + 7)
+
+// s_waitcnt takes an immediate: dispatch a wave-uniform count to it.
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    MXFP4_VM_CASE8(0) MXFP4_VM_CASE8(8) MXFP4_VM_CASE8(16) MXFP4_VM_CASE8(24)
+    MXFP4_VM_CASE8(32) MXFP4_VM_CASE8(40) MXFP4_VM_CASE8(48) MXFP4_VM_CASE8(56)
+    default: MXFP4_WAIT_VMCNT(0); break;
+  }
+}
+#undef MXFP4_VM_CASE8
+#undef MXFP4_VM_CASE
+
+// The 32x32x64 block-scaled FP4 MFMA with the scale byte selected separately
+// for the two operands (OPSEL_A picks a byte of sa, OPSEL_B a byte of sb).
+template <int OPSEL_A, int OPSEL_B>
+__device__ __forceinline__ v16f mfma32_fp4_sel(v4i a, v4i b, v16f acc, int sa, int sb) {
+  v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, kMfmaFmtFp4, kMfmaFmtFp4,
+                                                         OPSEL_A, sa, OPSEL_B, sb);
+}
+
+template <class C, int S>
+__device__ __forceinline__ void mma_pre(const Step<C>& st, const BPair& b, int bsc, v16f (&acc)[C::MB][2]) {
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i) {
+    acc[i][0] = mfma32_fp4_sel<2 * S, 0>(b.q[2 * S], st.a[i], acc[i][0], bsc, st.sa[i]);
+    acc[i][1] = mfma32_fp4_sel<2 * S + 1, 0>(b.q[2 * S + 1], st.a[i], acc[i][1], bsc, st.sa[i]);
+  }
+}
+
+// One pair of the prepacked-B loop (iteration p, B pair p in `cur`, the ring
+// slot of pair p - 1 refilled with pair p + kPreDepth - 1).
+template <class C, bool SKIP_PAST_END>
+__device__ __forceinline__ void pre_pair(uint8_t MXFP4_LDS* lds, const PreCopies<C>& src, int p, int np, int& slot,
+                                         const BPair& cur, BPair& refill_b, __amdgpu_buffer_rsrc_t rb, uint32_t voff,
+                                         int w, int lane, v16f (&acc)[C::MB][2]) {
+  barrier_lds();                // A pair p is in LDS for every wave; pair p - 1 is read
+  if (p + C::NP - 1 < np) {
+    const int refill = (slot == 0) ? C::NP - 1 : slot - 1;   // buffer of pair p - 1
+    copy_pair_pre<C>(lds + refill * C::PAIR, src, p + C::NP - 1, w);
+  }
+  if (!SKIP_PAST_END || p + kPreDepth - 1 < np) load_bpair(refill_b, rb, voff, p + kPreDepth - 1);
+  const uint8_t MXFP4_LDS* buf = lds + slot * C::PAIR;
+  const int bsc = *(const int MXFP4_LDS*)(buf + 2 * C::STAGE + 3 * 64 * 16 + w * 256 + lane * 4);
+  Step<C> s0, s1;
+  read_step<C>(buf, 0, w, lane, s0);
+  read_step<C>(buf, 1, w, lane, s1);
+  mma_pre<C, 0>(s0, cur, bsc, acc);
+  mma_pre<C, 1>(s1, cur, bsc, acc);
+  slot = (slot + 1 == C::NP) ? 0 : slot + 1;
+}
+
+// The streaming kernel on prepacked B: A goes through the same LDS ring of
+// pairs (its scale pieces share the copy with B's prepacked scale block), B
+// through a ring of kPreDepth pairs in each wave's registers.  The per-wave
+// k-step split, the MFMA order and the reduction are those of
+// gemm_stream_kernel, so both give bit-identical fp32 sums.
+//
+// NPC > 0 compiles the kernel for exactly NPC pairs (K = 512 * NPC) as
+// straight-line code: ring slots and wait counts are constants and no
+// register crosses a loop back-edge.  NPC = 0 takes any K with a loop
+// unrolled by kPreDepth; there the compiler keeps the ring alive across the
+// back-edge with register copies that must wait for the loads in flight, so
+// that form overlaps less and is kept for the other values of K.
+template <class C, int NPC>
+__global__ __launch_bounds__(kThreads) void gemm_stream_pre_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  static_assert(C::PRE && !C::A8, "prepacked-B configuration");
+  static_assert(kPreDepth >= C::NP, "B runs at least as far ahead as A");
+  static_assert((C::NP - 1) * C::PAIR_LOADS + (kPreDepth - 1) * kPreBLoads <= 63, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
+  int tm, tn;
+  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  // Wave-uniform values go to scalar registers, so the buffer resource below is
+  // provably uniform (no per-lane loop around each load) and the loop control
+  // stays scalar.
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int m0 = tm * C::BM, n0 = tn * kBN;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+
+  v16f acc[C::MB][2];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int np = __builtin_amdgcn_readfirstlane(args.k / 512);
+  PreCopies<C> src;
+  make_pre_copies<C>(src, args, m0, tn, np, w, lane);
+  // this panel's prepacked codes: np blocks of 16 KB (32 * k <= 2^29 bytes)
+  const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(args.b_q + (int64_t)tn * np * kPreCodeBlock,
+                                                 (uint32_t)np * kPreCodeBlock);
+  const uint32_t voff = w * 4096 + lane * 16;
+
+  BPair ring[kPreDepth];
+#pragma unroll
+  for (int q = 0; q < kPreDepth - 1; ++q) {
+    if (q <= C::NP - 2) copy_pair_pre<C>(lds + q * C::PAIR, src, min(q, np - 1), w);
+    if (NPC == 0 || q < NPC) load_bpair(ring[q], rb, voff, q);
+  }
+
+  int slot = 0;                 // LDS ring buffer of A pair p
+  if constexpr (NPC > 0) {
+#pragma unroll
+    for (int p = 0; p < NPC; ++p) {   // B pair p sits in ring[p % kPreDepth]
+      wait_vm_at_most(pre_ops_after_a<C>(p, NPC));   // a constant once unrolled
+      pre_pair<C, true>(lds, src, p, NPC, slot, ring[p % kPreDepth], ring[(p + kPreDepth - 1) % kPreDepth], rb, voff, w,
+                  lane, acc);
+    }
+  } else {
+    for (int p0 = 0;; p0 += kPreDepth) {
+#pragma unroll
+      for (int r = 0; r < kPreDepth; ++r) {
+        const int p = p0 + r;     // B pair p sits in ring[r]
+        if (p >= np) goto done;   // leaves the loop: no path skips a load and then reaches an MFMA
+        wait_vm_at_most(pre_ops_after_a<C>(p, np));
+        pre_pair<C, false>(lds, src, p, np, slot, ring[r], ring[(r + kPreDepth - 1) % kPreDepth], rb, voff, w, lane, acc);
+      }
+    }
+  }
+done:
+  MXFP4_WAIT_VMCNT(0);
+  __syncthreads();   // every wave is done with the ring
+
+  stream_epilogue<C>(acc, args, m0, n0, lds, w, lane);
+}
+
+template <class C, int NPC>
+hipError_t launch_pre_cfg(const GemmArgs& args, hipStream_t stream) {
+  const auto kernel = gemm_stream_pre_kernel<C, NPC>;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  const int tiles_n = (args.n + kBN - 1) / kBN;
+  const int tiles_m = (args.m + C::BM - 1) / C::BM;
+  const int64_t blocks = (int64_t)tiles_m * ((tiles_n + 7) / 8) * 8;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), C::LDS, stream, args, tiles_m, tiles_n);
+  return hipGetLastError();
+}
 }  // namespace
 
 bool stream_supported(const GemmArgs& args) {
@@ -361,6 +679,39 @@ hipError_t launch_gemm_w4a8_stream(const GemmArgs& args, hipStream_t stream) {
   if (!stream_supported(args)) return hipErrorInvalidValue;
   if (args.m <= 32) return launch_cfg<StreamCfg<1, 4, true>>(args, stream);
   return launch_cfg<StreamCfg<2, 3, true>>(args, stream);
+}
+
+void prepacked_sizes(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_bytes) {
+  const int64_t panels = (n + kBN - 1) / kBN;
+  *code_bytes = panels * kBN * (k / 2);
+  *scale_bytes = panels * kBN * (k / 32);
+}
+
+hipError_t launch_prepack_weight(const uint8_t* b_q, const uint8_t* b_s, int n, int k, uint8_t* bp_q, uint8_t* bp_s,
+                                 hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (k <= 0 || k % 512) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)((n + kBN - 1) / kBN) * (k / 512);
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, b_q, b_s, n, k, bp_q, bp_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (!stream_supported(args)) return hipErrorInvalidValue;
+  using Pre1 = StreamCfg<1, 4, false, true>;
+  using Pre2 = StreamCfg<2, 4, false, true>;
+  using Pre4 = StreamCfg<4, 4, false, true>;
+  const int np = args.k / 512;
+  if (np == 8) {   // K = 4096
+    if (args.m <= 32) return launch_pre_cfg<Pre1, 8>(args, stream);
+    if (args.m <= 64) return launch_pre_cfg<Pre2, 8>(args, stream);
+    return launch_pre_cfg<Pre4, 8>(args, stream);
+  }
+  if (args.m <= 32) return launch_pre_cfg<Pre1, 0>(args, stream);
+  if (args.m <= 64) return launch_pre_cfg<Pre2, 0>(args, stream);
+  return launch_pre_cfg<Pre4, 0>(args, stream);
 }
 
 }  // namespace mxfp4

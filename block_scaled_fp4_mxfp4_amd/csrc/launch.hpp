@@ -59,6 +59,13 @@ hipError_t launch_gemm_stream(const GemmArgs& args, hipStream_t stream);
 // The same with A in MXFP8 (W4A8); M tiles of 32 or 64 rows.
 hipError_t launch_gemm_w4a8_stream(const GemmArgs& args, hipStream_t stream);
 
+// The same on a prepacked weight (include/mxfp4.h, mxfp4_prepack_weight): B is
+// loaded straight into registers; A as in launch_gemm_stream.
+void prepacked_sizes(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_bytes);
+hipError_t launch_prepack_weight(const uint8_t* b_q, const uint8_t* b_s, int n, int k, uint8_t* bp_q, uint8_t* bp_s,
+                                 hipStream_t stream);
+hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream);
+
 // MoE steps around the grouped GEMM (include/mxfp4_moe.h).
 constexpr int kMoeMaxTopK = 8;          // routing: experts per token
 constexpr int kMoeMaxRouteExperts = 256;  // routing: four logits per lane of a wave

@@ -165,6 +165,52 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prepacked weights for the small-M (decode) GEMM.  The same NT GEMM as
+ * mxfp4_gemm_nt (the "Packed MXFP4 & NVFP4 GEMM + mega-MoE" page, Summary:
+ * mxfp4_gemm_nt; its decode shapes are the small-M case), with B, a weight
+ * quantized once ahead of time, stored in a layout that hands every lane of
+ * the MFMA its operand bytes in one contiguous 1 KB read per wave.  The result
+ * is bit-identical to mxfp4_gemm_nt_ex with MXFP4_KERNEL_STREAM on the
+ * unpacked B, for both output types.
+ *
+ * Layout (the bytes are B's codes and scales, rearranged; rows past n are zero
+ * codes with scale byte 0): for each 64-row panel P of B (P = 0 ..
+ * ceil(n/64) - 1, rows 64P .. 64P+63) and each 512-element K pair t, in that
+ * order,
+ *   codes,  16384 bytes: byte w*4096 + u*1024 + l*16 + c (w, u in 0..3,
+ *           l in 0..63, c in 0..15, u = 2s + j) is code byte c of row
+ *           64P + 32j + (l % 32) at that row's byte 256t + 128s + 32w +
+ *           16*(l / 32);
+ *   scales,  1024 bytes: byte w*256 + l*4 + (2s + j) is the scale byte of the
+ *           same row for the 32-element block 16t + 8s + 2w + l / 32.
+ *
+ * mxfp4_prepacked_weight_size gives the two array sizes:
+ *   code_bytes = ceil(n/64) * 64 * k/2,  scale_bytes = ceil(n/64) * 64 * k/32.
+ * k must be a positive multiple of 512 (MXFP4_ERR_INVALID_ARG otherwise).
+ */
+mxfp4_status_t mxfp4_prepacked_weight_size(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_bytes);
+
+/*
+ * Rearranges an MXFP4 weight into the prepacked layout.
+ *   b_q, b_s   : [n, k/2], [n, k/32] row-major (read only; b_q 16-byte aligned)
+ *   bp_q, bp_s : device buffers of code_bytes and scale_bytes (written;
+ *                16-byte aligned), owned by the caller
+ *   k          : a positive multiple of 512, at most 2^24
+ */
+mxfp4_status_t mxfp4_prepack_weight(const void* b_q, const void* b_s, int64_t n, int64_t k,
+                                    void* bp_q, void* bp_s, void* stream);
+
+/*
+ * C[m, n] = A . B^T with B prepacked (above).  a_q, a_s: A as in
+ * mxfp4_gemm_nt, both 16-byte aligned; c: [m, n] row-major of type `c_type`,
+ * 16-byte aligned; k a positive multiple of 512.  No workspace.  Built for
+ * m up to 128 (one workgroup per 64 columns per 128 rows of A); larger m is
+ * computed correctly by more row tiles that each stream the weight again.
+ */
+mxfp4_status_t mxfp4_gemm_nt_prepacked(const void* a_q, const void* a_s, const void* bp_q, const void* bp_s,
+                                       void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
  * Kernel selection for tests and tuning.  mxfp4_gemm_nt chooses a kernel per
  * shape; mxfp4_gemm_nt_ex lets a caller force one so every kernel can be
  * checked on any shape.  `kernel` values:

@@ -1,0 +1,146 @@
+"""GPU decode GEMM on prepacked weights against the CPU oracle and the streaming kernel.
+
+* prepacking: the rearranged code and scale bytes equal a NumPy re-indexing of
+  B written from the layout's definition (a pure byte permutation, zero rows
+  past n), over ragged n and several k;
+* GEMM: fp32 output within 1e-5 (floored max-rel) of the float64 oracle and
+  bit-identical to the streaming kernel on the unpacked weight (same per-wave
+  k-step split, same MFMA order, same fixed-order reduction), BF16 output
+  bit-identical too; shapes cover both kernel forms (K = 4096 straight-line,
+  other K looped, including more pairs than the register ring holds), the
+  three row-tile sizes, ragged m and n, a single 512-K pair, and m > 128;
+* the full decode workload (128 x 14336 x 4096) bit-identical to the streaming
+  kernel over the whole output and within tolerance of the oracle on samples.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from block_scaled_fp4_mxfp4_amd import (MXFP4Error, mxfp4_gemm_nt, mxfp4_gemm_nt_prepacked, mxfp4_prepack_weight,
+                                        mxfp4_prepacked_weight_size, mxfp4_quantize)
+from tests.gpu_common import device, log, poisoned, random_bf16, random_codes, sampled_indices, to_np, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _prepack_numpy(bq, bs):
+    """The prepacked layout from its definition: per 64-row panel and 512-K pair,
+    codes[w, u=2s+j, l, c] = B code byte c of row 32j + l%32 at 256t + 128s + 32w + 16(l//32),
+    scales[w, l, b=2s+j] = B scale of that row for block 16t + 8s + 2w + l//32."""
+    n, kh = bq.shape
+    k = kh * 2
+    panels, pairs = -(-n // 64), k // 512
+    qpad = np.zeros((panels * 64, kh), np.uint8)
+    qpad[:n] = bq
+    spad = np.zeros((panels * 64, k // 32), np.uint8)
+    spad[:n] = bs
+    codes = np.zeros((panels, pairs, 4, 4, 64, 16), np.uint8)
+    scales = np.zeros((panels, pairs, 4, 64, 4), np.uint8)
+    for w in range(4):
+        for s in range(2):
+            for j in range(2):
+                for l in range(64):
+                    rows = np.arange(panels) * 64 + 32 * j + l % 32
+                    for t in range(pairs):
+                        off = 256 * t + 128 * s + 32 * w + 16 * (l // 32)
+                        codes[:, t, w, 2 * s + j, l, :] = qpad[rows, off:off + 16]
+                        scales[:, t, w, l, 2 * s + j] = spad[rows, 16 * t + 8 * s + 2 * w + l // 32]
+    return codes.reshape(-1), scales.reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(1, 512), (64, 512), (100, 1024), (130, 4096), (200, 1536)])
+def test_prepack_layout_matches_definition(n, k):
+    dev = device()
+    log(f"prepack n={n} k={k}")
+    bq, bs = random_codes(n, k, seed=n + k, lo=0, hi=254)
+    cb, sb = mxfp4_prepacked_weight_size(n, k)
+    assert cb == -(-n // 64) * 64 * k // 2 and sb == -(-n // 64) * 64 * k // 32
+    bp_q = poisoned((cb,), torch.uint8, dev, 0xA5)
+    bp_s = poisoned((sb,), torch.uint8, dev, 0xA5)
+    mxfp4_prepack_weight(upload(bq, dev), upload(bs, dev), bp_q, bp_s)
+    torch.cuda.synchronize()
+    want_q, want_s = _prepack_numpy(bq, bs)
+    assert np.array_equal(to_np(bp_q), want_q)
+    assert np.array_equal(to_np(bp_s), want_s)
+
+
+def _both(aq, as_, bq, bs, dev, out_dtype):
+    a_q, a_s, b_q, b_s = (upload(t, dev) for t in (aq, as_, bq, bs))
+    bp_q, bp_s = mxfp4_prepack_weight(b_q, b_s)
+    m, n = a_q.shape[0], b_q.shape[0]
+    c_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
+    mxfp4_gemm_nt_prepacked(a_q, a_s, bp_q, bp_s, n, c=c_all[:m])
+    ref = mxfp4_gemm_nt(a_q, a_s, b_q, b_s, out_dtype=out_dtype, kernel="stream")
+    torch.cuda.synchronize()
+    assert torch.all(c_all[m:].view(torch.uint8) == 0x7F), "write past C"
+    return c_all[:m], ref
+
+
+# (m, n, k): K = 4096 runs the straight-line form; other K the looped form
+# (K = 512: one pair; 4608: 9 pairs, one more than the register ring;
+# 8192: two full trips of the ring).
+SHAPES = [(1, 64, 512), (5, 100, 1024), (33, 200, 512), (64, 256, 2048), (96, 130, 4096), (128, 192, 4096),
+          (17, 640, 4096), (130, 64, 4096), (128, 320, 4608), (40, 96, 8192), (200, 72, 1536)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_prepacked_gemm_matches_oracle_and_stream_kernel(m, n, k):
+    dev = device()
+    log(f"prepacked gemm m={m} n={n} k={k}")
+    a = random_bf16((m, k), 7 * m + k, spread=3, outlier_frac=0.01)
+    b = random_bf16((n, k), 11 * n + k, spread=2)
+    aq, as_ = oracle.quantize(workloads.bf16_bits(a))
+    bq, bs = oracle.quantize(workloads.bf16_bits(b))
+    c32, s32 = _both(aq, as_, bq, bs, dev, torch.float32)
+    c16, s16 = _both(aq, as_, bq, bs, dev, torch.bfloat16)
+    got = to_np(c32).astype(np.float64)
+    assert oracle.floored_max_rel(got, oracle.gemm_nt(aq, as_, bq, bs)) <= 1e-5
+    assert torch.equal(c32.view(torch.int32), s32.view(torch.int32)), "fp32 differs from the streaming kernel"
+    assert torch.equal(c16.view(torch.int16), s16.view(torch.int16)), "bf16 differs from the streaming kernel"
+
+
+def test_prepacked_gemm_every_code_and_scale():
+    """Random code bytes (every E2M1 pattern) and a wide scale range, m = 1 and 128."""
+    dev = device()
+    for m, n, k in [(1, 192, 4096), (128, 130, 2048)]:
+        aq, as_ = random_codes(m, k, seed=m + 1, lo=110, hi=140)
+        bq, bs = random_codes(n, k, seed=n + 2, lo=110, hi=140)
+        c32, s32 = _both(aq, as_, bq, bs, dev, torch.float32)
+        assert oracle.floored_max_rel(to_np(c32).astype(np.float64), oracle.gemm_nt(aq, as_, bq, bs)) <= 1e-5
+        assert torch.equal(c32.view(torch.int32), s32.view(torch.int32))
+
+
+def test_prepacked_rejects_bad_k_and_empty_problems_are_noops():
+    dev = device()
+    aq, as_ = random_codes(4, 1024, seed=3)
+    bq, bs = random_codes(64, 1024, seed=4)
+    bp_q, bp_s = mxfp4_prepack_weight(upload(bq, dev), upload(bs, dev))
+    with pytest.raises(MXFP4Error):
+        mxfp4_prepacked_weight_size(64, 992)
+    with pytest.raises(MXFP4Error):
+        mxfp4_prepack_weight(upload(bq[:, :496], dev), upload(bs[:, :31], dev))
+    c = mxfp4_gemm_nt_prepacked(upload(aq[:0], dev), upload(as_[:0], dev), bp_q, bp_s, 64)
+    assert c.shape == (0, 64)
+
+
+def test_prepacked_decode_full_size():
+    dev = device()
+    w = workloads.DECODE
+    log(f"prepacked gemm {w.name}")
+    a, b = w.make()
+    aq, as_ = mxfp4_quantize(a.to(dev))
+    bq, bs = mxfp4_quantize(b.to(dev))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    c = mxfp4_gemm_nt_prepacked(aq, as_, bp_q, bp_s, w.n)
+    c32 = mxfp4_gemm_nt_prepacked(aq, as_, bp_q, bp_s, w.n, out_dtype=torch.float32)
+    s = mxfp4_gemm_nt(aq, as_, bq, bs, kernel="stream")
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), s.view(torch.int16)), "bf16 differs from the streaming kernel"
+    rows = sampled_indices(w.m, 32, seed=5)
+    cols = sampled_indices(w.n, 96, seed=6)
+    oaq, oas = oracle.quantize(workloads.bf16_bits(a[torch.from_numpy(rows)]))
+    obq, obs = oracle.quantize(workloads.bf16_bits(b[torch.from_numpy(cols)]))
+    ref = oracle.gemm_nt(oaq, oas, obq, obs)
+    assert oracle.floored_max_rel(to_np(c32)[np.ix_(rows, cols)].astype(np.float64), ref) <= 1e-5
