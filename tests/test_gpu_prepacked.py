@@ -10,7 +10,9 @@
   other K looped, including more pairs than the register ring holds), the
   three row-tile sizes, ragged m and n, a single 512-K pair, and m > 128;
 * the full decode workload (128 x 14336 x 4096) bit-identical to the streaming
-  kernel over the whole output and within tolerance of the oracle on samples.
+  kernel over the whole output and within tolerance of the oracle on samples;
+* the tiny workload's fp32 C at the points whose oracle values are stored in
+  tests/golden; quantize + prepacked GEMM replayed from a HIP graph.
 """
 import numpy as np
 import pytest
@@ -79,8 +81,8 @@ def _both(aq, as_, bq, bs, dev, out_dtype):
 
 
 # (m, n, k): K = 4096 runs the straight-line form; other K the looped form
-# (K = 512: one pair; 4608: 9 pairs, one more than the register ring;
-# 8192: two full trips of the ring).
+# (K = 512: one pair, fewer than the 4-pair register ring; 2048: one full trip
+# of the ring; 4608: 9 pairs, a partial last trip; 8192: four trips).
 SHAPES = [(1, 64, 512), (5, 100, 1024), (33, 200, 512), (64, 256, 2048), (96, 130, 4096), (128, 192, 4096),
           (17, 640, 4096), (130, 64, 4096), (128, 320, 4608), (40, 96, 8192), (200, 72, 1536)]
 
@@ -144,3 +146,58 @@ def test_prepacked_decode_full_size():
     obq, obs = oracle.quantize(workloads.bf16_bits(b[torch.from_numpy(cols)]))
     ref = oracle.gemm_nt(oaq, oas, obq, obs)
     assert oracle.floored_max_rel(to_np(c32)[np.ix_(rows, cols)].astype(np.float64), ref) <= 1e-5
+
+
+def test_prepacked_tiny_workload_matches_stored_oracle_values():
+    """GPU quantize of the tiny workload, prepack, GEMM: fp32 C at the points whose
+    float64 oracle values are stored in tests/golden/oracle_digests.txt."""
+    from tests.test_golden import load_golden
+    dev = device()
+    gold = load_golden()
+    w = workloads.TINY
+    a, b = w.make()
+    aq, as_ = mxfp4_quantize(a.to(dev))
+    bq, bs = mxfp4_quantize(b.to(dev))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    c = to_np(mxfp4_gemm_nt_prepacked(aq, as_, bp_q, bp_s, w.n, out_dtype=torch.float32))
+    for (i, j) in [(0, 0), (17, 100), (63, 255)]:
+        want = float.fromhex(gold[f"{w.name}.c[{i},{j}]"])
+        assert abs(float(c[i, j]) - want) <= 1e-5 * max(abs(want), 1.0), (i, j, float(c[i, j]), want)
+
+
+def test_prepacked_graph_replays_match_eager():
+    """Quantize + prepacked GEMM captured in a HIP graph: every replay, with eager
+    work and synchronisation between replays, equals the eager result."""
+    dev = device()
+    m, n, k = 128, 448, 4096
+    log(f"graph: quantize + prepacked gemm m={m} n={n} k={k}")
+    a = workloads.activation_bf16(m, k, 970, outliers=True).to(dev)
+    b = workloads.gaussian_bf16((n, k), 0.02, 971).to(dev)
+    bq, bs = mxfp4_quantize(b)
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    aq = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((m, k // 32), dtype=torch.uint8, device=dev)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mxfp4_quantize(a, aq, as_)
+        mxfp4_gemm_nt_prepacked(aq, as_, bp_q, bp_s, n, c=c)
+
+    step()
+    torch.cuda.synchronize()
+    eager = c.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        c.view(torch.uint8).fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
