@@ -113,6 +113,9 @@ class DenseBench:
                       bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev))
             if self.prepacked:
                 st["bp_q"], st["bp_s"] = B.mxfp4_prepack_weight(st["bq"], st["bs"])
+                cb, sb = B.mxfp4_prepacked_weight_size(m, k)
+                st["ap_q"] = torch.empty(cb, dtype=torch.uint8, device=dev)
+                st["ap_s"] = torch.empty(sb, dtype=torch.uint8, device=dev)
             self.sets.append(st)
         # the weight-packing kernel gets rotating sources of its own
         self.b_sets = [b_d.clone() for _ in range(max(2, math.ceil(ROTATION_BYTES / (n * k * 2))))]
@@ -151,6 +154,19 @@ class DenseBench:
     def step_prepacked(self, i):
         self.quantize(i)
         self.gemm_prepacked(i)
+
+    def quantize_prepacked(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_quantize_prepacked(s["a"], s["ap_q"], s["ap_s"])
+
+    def gemm_prepacked_ab(self, i):
+        s = self.sets[i % self.sets_n]
+        w = self.w
+        self.B.mxfp4_gemm_nt_prepacked_ab(s["ap_q"], s["ap_s"], s["bp_q"], s["bp_s"], w.m, w.n, w.k, c=s["c"])
+
+    def step_prepacked_ab(self, i):
+        self.quantize_prepacked(i)
+        self.gemm_prepacked_ab(i)
 
     @staticmethod
     def _graph(fn, count):
@@ -601,6 +617,7 @@ KERNEL_SOURCES = {
     "gemm_tile_kernel": ("gemm_tile.hip", "common.hpp"),
     "gemm_stream_kernel": ("gemm_stream.hip", "common.hpp"),
     "gemm_stream_pre_kernel": ("gemm_stream.hip", "common.hpp"),
+    "gemm_pp_kernel": ("gemm_stream.hip", "common.hpp"),
     "quantize_kernel": ("quantize.hip", "common.hpp"),
     "quantize_scatter_kernel": ("moe.hip", "common.hpp"),
     "combine_kernel": ("moe.hip", "common.hpp"),
@@ -744,7 +761,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
-    ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "quantize", "quantize_b", "copy",
+    ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "gemm_prepacked_ab",
+                                       "step_prepacked_ab", "quantize_prepacked", "quantize", "quantize_b", "copy",
                                        "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu"],
                     help="eager launches for profiling; route/permute/scatter/combine/layer run the "
                          "on-device MoE layer's steps (layer = all five) on the MoE workload")
@@ -831,31 +849,37 @@ def main():
         w2 = workloads.DENSE[args.secondary]
         eprint(f"[bench] building inputs for {w2.name}")
         b2 = DenseBench(w2, dev)
-        pre = b2.prepacked      # the weight is also held prepacked: the decode step uses that GEMM
-        s2 = b2.timed(b2.step_prepacked if pre else b2.step, args.steps, args.warmup)
-        g2 = b2.timed(b2.gemm_prepacked if pre else b2.gemm, args.steps, args.warmup)
+        # With the weight held prepacked, the decode step quantizes A straight into
+        # the prepacked layout and runs the GEMM that loads both operands into registers.
+        pre = b2.prepacked
+        s2 = b2.timed(b2.step_prepacked_ab if pre else b2.step, args.steps, args.warmup)
+        g2 = b2.timed(b2.gemm_prepacked_ab if pre else b2.gemm, args.steps, args.warmup)
+        gb = b2.timed(b2.gemm_prepacked, args.steps, args.warmup) if pre else g2
         gu = b2.timed(b2.gemm, args.steps, args.warmup) if pre else g2
-        q2 = b2.timed(b2.quantize, args.steps, args.warmup)
+        q2 = b2.timed(b2.quantize_prepacked if pre else b2.quantize, args.steps, args.warmup)
         gbytes = gemm_algorithmic_bytes(w2.m, w2.n, w2.k)
         qb2 = quant_algorithmic_bytes(w2.m, w2.k)
         gemm_gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
-        kname = "gemm_stream_pre_kernel" if pre else "gemm_stream_kernel"
+        kname = "gemm_pp_kernel" if pre else "gemm_stream_kernel"
         result["secondary"] = {
             "metric": "achieved HBM GB/s at decode M=128", "workload": w2.name,
             "value": round((gbytes + qb2) / (s2["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
             "ms_per_step": round(s2["mean"], 6), "step_us": us(s2), "rotating_input_sets": b2.sets_n,
-            "step": ("quantize A + mxfp4 GEMM on the prepacked weight (B quantized and prepacked once)" if pre
+            "step": ("quantize A into the prepacked layout + mxfp4 GEMM on prepacked A and B "
+                     "(B quantized and prepacked once)" if pre
                      else "quantize A + streaming mxfp4 GEMM (B pre-quantized)"),
             "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_from_profiles(w2.name, kname)},
             "kernels": {"gemm_us": us(g2), "quantize_a_us": us(q2),
                         "gemm_tflops": round(w2.flops / (g2["mean"] * 1e-3) / 1e12, 2),
+                        "gemm_prepacked_b_only_us": us(gb),
+                        "gemm_prepacked_b_only_gbs": round(gbytes / (gb["mean"] * 1e-3) / 1e9, 1),
                         "gemm_unpacked_weight_us": us(gu),
                         "gemm_unpacked_weight_gbs": round(gbytes / (gu["mean"] * 1e-3) / 1e9, 1)},
         }
         eprint(f"[bench] {w2.name}: step {s2['mean']*1e3:.2f} us, gemm {g2['mean']*1e3:.2f} us "
-               f"({gemm_gbs:.0f} GB/s; unpacked weight {gu['mean']*1e3:.2f} us)")
+               f"({gemm_gbs:.0f} GB/s; B-only prepacked {gb['mean']*1e3:.2f} us, unpacked {gu['mean']*1e3:.2f} us)")
         del b2
 
     if args.moe != "none":

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     mxfp8_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt,
     mxfp4_moe_route, mxfp4_moe_permute, mxfp4_moe_quantize_scatter, mxfp8_moe_quantize_scatter, mxfp4_moe_combine,
     mxfp4_rmsnorm_quantize, mxfp4_swiglu_quantize, nvfp4_quantize, nvfp4_gemm_nt,
-    mxfp4_prepacked_weight_size, mxfp4_prepack_weight, mxfp4_gemm_nt_prepacked,
+    mxfp4_prepacked_weight_size, mxfp4_prepack_weight, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,
+    mxfp4_quantize_prepacked,
     LIB_PATH, EXPORTED, KERNELS,
 )

@@ -30,7 +30,8 @@ EXPORTED = (
     "mxfp8_gemm_w4a8_nt", "mxfp8_gemm_w4a8_nt_ex", "mxfp8_grouped_gemm_w4a8_nt", "mxfp4_probe_mfma_w4a8",
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
-    "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked",
+    "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
+    "mxfp4_quantize_prepacked",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_prepack_weight.argtypes = [vp, vp, i64, i64, vp, vp, vp]
         lib.mxfp4_gemm_nt_prepacked.restype = ctypes.c_int
         lib.mxfp4_gemm_nt_prepacked.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp4_quantize_prepacked.restype = ctypes.c_int
+        lib.mxfp4_quantize_prepacked.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_gemm_nt_prepacked_ab.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_prepacked_ab.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp4_grouped_gemm_nt_workspace_size.restype = sz
         lib.mxfp4_grouped_gemm_nt_workspace_size.argtypes = [i64, i32, i64, i64]
         lib.mxfp4_grouped_gemm_nt.restype = ctypes.c_int
@@ -269,6 +274,38 @@ def mxfp4_gemm_nt_prepacked(a_q, a_s, bp_q, bp_s, n: int, c=None, out_dtype=torc
     c, code = _out(c, m, n, out_dtype, a_q.device)
     _check(lib.mxfp4_gemm_nt_prepacked(_ptr(a_q), _ptr(a_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
                                        _stream(stream)))
+    return c
+
+
+def mxfp4_quantize_prepacked(x, ap_q=None, ap_s=None, stream=None):
+    """BF16 [rows, k] -> MXFP4 in the prepacked layout; returns (ap_q, ap_s) as flat uint8."""
+    lib = load_library()
+    rows, k = x.shape
+    _require(x, "x", torch.bfloat16, (rows, k))
+    cb, sb = mxfp4_prepacked_weight_size(rows, k)
+    if ap_q is None:
+        ap_q = torch.empty(cb, dtype=torch.uint8, device=x.device)
+    if ap_s is None:
+        ap_s = torch.empty(sb, dtype=torch.uint8, device=x.device)
+    _require(ap_q, "ap_q", torch.uint8, (cb,))
+    _require(ap_s, "ap_s", torch.uint8, (sb,))
+    _check(lib.mxfp4_quantize_prepacked(_ptr(x), rows, k, _ptr(ap_q), _ptr(ap_s), _stream(stream)))
+    return ap_q, ap_s
+
+
+def mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m: int, n: int, k: int, c=None, out_dtype=torch.bfloat16,
+                               stream=None):
+    """C[m, n] = A . B^T with both A [m, k] and B [n, k] prepacked (mxfp4_prepack_weight)."""
+    lib = load_library()
+    for t, rows, name in ((ap_q, m, "ap_q"), (bp_q, n, "bp_q")):
+        cb, _ = mxfp4_prepacked_weight_size(rows, k)
+        _require(t, name, torch.uint8, (cb,))
+    for t, rows, name in ((ap_s, m, "ap_s"), (bp_s, n, "bp_s")):
+        _, sb = mxfp4_prepacked_weight_size(rows, k)
+        _require(t, name, torch.uint8, (sb,))
+    c, code = _out(c, m, n, out_dtype, ap_q.device)
+    _check(lib.mxfp4_gemm_nt_prepacked_ab(_ptr(ap_q), _ptr(ap_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
+                                          _stream(stream)))
     return c
 
 

@@ -660,6 +660,176 @@ hipError_t launch_pre_cfg(const GemmArgs& args, hipStream_t stream) {
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), C::LDS, stream, args, tiles_m, tiles_n);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Both operands prepacked.  The prepacked layout is defined for any [rows, K]
+// MXFP4 operand (64-row panels, 512-K pairs), so A can take it too.  Then each
+// wave loads its A and B operands straight into registers, 1 KB contiguous per
+// load, and the main loop touches no LDS: no copies into LDS, no barriers and
+// no hand-counted waits (the compiler's waits on the loaded registers are
+// exact, every vector-memory op being a plain load).  The per-wave k-step
+// split, the MFMA order and the fixed-order reduction are those of
+// gemm_stream_kernel, so the results are bit-identical to it.
+//
+// Row tiles: BM = 32 * MB rows of A.  MB = 4 and 2 cover whole 64-row A
+// panels (two and one); MB = 1 covers half a panel (j_a = tile % 2).
+template <int MB>
+struct PPPair {
+  v4i a[MB][2];   // [row block][stage]
+  v4i b[4];       // [2s + j]
+  int sa[MB > 1 ? MB / 2 : 1];   // one scale word per A panel
+  int sb;
+};
+
+constexpr int kPPDepth = 4;   // pairs in each wave's register ring
+
+template <int MB>
+__device__ __forceinline__ void pp_load(PPPair<MB>& r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
+                                        __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsb, uint32_t qoff,
+                                        uint32_t soff, uint32_t a_panel_q, uint32_t a_panel_s, int ja, int p) {
+  // Every offset is in the per-lane offset, which the buffer range check
+  // covers: a pair past the last reads zeros without touching memory.  The
+  // scheduling barriers keep each pair's loads together where they are
+  // written: without them the scheduler pulls every MFMA up next to the loads
+  // it consumes, the registers are then reused pair after pair, and each load
+  // waits for the MFMAs of the pair before it (no prefetch at all).
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t pq = qoff + (uint32_t)p * kPreCodeBlock, ps = soff + (uint32_t)p * kPreScaleBlock;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    r.b[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, pq + u * 1024, 0, 0));
+  r.sb = (int)__builtin_amdgcn_raw_buffer_load_b32(rsb, ps, 0, 0);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int panel = MB > 1 ? i / 2 : 0;
+    const int j = MB > 1 ? (i & 1) : ja;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      r.a[i][s] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, pq + panel * a_panel_q + (2 * s + j) * 1024, 0, 0));
+  }
+#pragma unroll
+  for (int pn = 0; pn < (MB > 1 ? MB / 2 : 1); ++pn)
+    r.sa[pn] = (int)__builtin_amdgcn_raw_buffer_load_b32(rsa, ps + pn * a_panel_s, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MB, int S>
+__device__ __forceinline__ void pp_mma_stage(const PPPair<MB>& r, int ja, v16f (&acc)[MB][2]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    if constexpr (MB > 1) {
+      const int sa = r.sa[i / 2];
+      if (i & 1) {
+        acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S + 1>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+        acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S + 1>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+      } else {
+        acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+        acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+      }
+    } else {
+      const int sa = r.sa[0] >> (8 * ja);   // byte 2s + ja moved to byte 2s
+      acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+      acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+    }
+  }
+}
+
+// Stage 0 then stage 1, row blocks in order: the streaming kernel's order.
+template <int MB>
+__device__ __forceinline__ void pp_mma(const PPPair<MB>& r, int ja, v16f (&acc)[MB][2]) {
+  pp_mma_stage<MB, 0>(r, ja, acc);
+  pp_mma_stage<MB, 1>(r, ja, acc);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pp_rsrc(const uint8_t* base, int64_t bytes) {
+  return uniform_rsrc(base, (uint32_t)bytes);
+}
+
+// CH pairs starting at pair p0 as straight-line code: a ring of kPPDepth
+// pairs, loads for pair p + kPPDepth - 1 issued before the MFMAs of pair p.
+// The ring lives only inside one chunk, so no register crosses a loop
+// back-edge (a ring carried round a loop made the compiler copy and spill it).
+template <int MB, int CH>
+__device__ __forceinline__ void pp_chunk(int p0, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
+                                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsb, uint32_t qoff,
+                                         uint32_t soff, uint32_t panel_q, uint32_t panel_s, int ja,
+                                         v16f (&acc)[MB][2]) {
+  PPPair<MB> ring[kPPDepth];
+#pragma unroll
+  for (int q = 0; q < kPPDepth - 1; ++q)
+    if (q < CH) pp_load<MB>(ring[q], ra, rsa, rb, rsb, qoff, soff, panel_q, panel_s, ja, p0 + q);
+#pragma unroll
+  for (int p = 0; p < CH; ++p) {
+    if (p + kPPDepth - 1 < CH)
+      pp_load<MB>(ring[(p + kPPDepth - 1) % kPPDepth], ra, rsa, rb, rsb, qoff, soff, panel_q, panel_s, ja,
+                  p0 + p + kPPDepth - 1);
+    pp_mma<MB>(ring[p % kPPDepth], ja, acc);
+  }
+}
+
+// K in chunks of 8 pairs (K = 4096 is one chunk), then one of 4, then single
+// pairs; the pipeline refills at each chunk boundary.
+template <int MB>
+__global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  using EC = StreamCfg<MB, 2, false, true>;   // epilogue layout (reduction area and C tile)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
+  int tm, tn;
+  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int m0 = tm * EC::BM, n0 = tn * kBN;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int np = __builtin_amdgcn_readfirstlane(args.k / 512);
+
+  // B: this column panel.  A: the tile's row panels (MB = 1: half of one);
+  // the A panels that exist for this tile (the last tile of a ragged m may
+  // have fewer): loads past them fall outside the resource and read zeros.
+  const int64_t panel_q = (int64_t)np * kPreCodeBlock, panel_s = (int64_t)np * kPreScaleBlock;
+  const int a_panel0 = m0 / 64;
+  const int a_panels = min(MB > 1 ? MB / 2 : 1, (args.m + 63) / 64 - a_panel0);
+  const int ja = MB > 1 ? 0 : (tm & 1);
+  const __amdgpu_buffer_rsrc_t rb = pp_rsrc(args.b_q + tn * panel_q, panel_q);
+  const __amdgpu_buffer_rsrc_t rsb = pp_rsrc(args.b_s + tn * panel_s, panel_s);
+  const __amdgpu_buffer_rsrc_t ra = pp_rsrc(args.a_q + a_panel0 * panel_q, a_panels * panel_q);
+  const __amdgpu_buffer_rsrc_t rsa = pp_rsrc(args.a_s + a_panel0 * panel_s, a_panels * panel_s);
+  const uint32_t qoff = w * 4096 + lane * 16, soff = w * 256 + lane * 4;
+
+  v16f acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const uint32_t pq = (uint32_t)panel_q, ps = (uint32_t)panel_s;
+  int p0 = 0;
+  for (; p0 + 8 <= np; p0 += 8) pp_chunk<MB, 8>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+  if (p0 + 4 <= np) {
+    pp_chunk<MB, 4>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+    p0 += 4;
+  }
+  for (; p0 < np; ++p0) pp_chunk<MB, 1>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+
+  stream_epilogue<EC>(acc, args, m0, n0, lds, w, lane);
+}
+
+template <int MB>
+hipError_t launch_pp_cfg(const GemmArgs& args, hipStream_t stream) {
+  using EC = StreamCfg<MB, 2, false, true>;
+  constexpr int lds_bytes = EC::XCH + EC::C_TILE;
+  const auto kernel = gemm_pp_kernel<MB>;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  const int tiles_n = (args.n + kBN - 1) / kBN;
+  const int tiles_m = (args.m + EC::BM - 1) / EC::BM;
+  const int64_t blocks = (int64_t)tiles_m * ((tiles_n + 7) / 8) * 8;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), lds_bytes, stream, args, tiles_m, tiles_n);
+  return hipGetLastError();
+}
 }  // namespace
 
 bool stream_supported(const GemmArgs& args) {
@@ -712,6 +882,14 @@ hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream
   if (args.m <= 32) return launch_pre_cfg<Pre1, 0>(args, stream);
   if (args.m <= 64) return launch_pre_cfg<Pre2, 0>(args, stream);
   return launch_pre_cfg<Pre4, 0>(args, stream);
+}
+
+hipError_t launch_gemm_both_prepacked(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (args.k <= 0 || args.k % 512) return hipErrorInvalidValue;
+  if (args.m <= 32) return launch_pp_cfg<1>(args, stream);
+  if (args.m <= 64) return launch_pp_cfg<2>(args, stream);
+  return launch_pp_cfg<4>(args, stream);
 }
 
 }  // namespace mxfp4

@@ -30,6 +30,10 @@ enum TileKind { kTile256 = 0, kTile128 = 1 };
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                            hipStream_t stream, int num_cus);
+// The same codes and scale bytes stored in the prepacked GEMM operand layout
+// (k % 512 == 0; rows up to the next multiple of 64 written as zero blocks).
+hipError_t launch_quantize_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                     hipStream_t stream, int num_cus);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                                  hipStream_t stream, int num_cus);
 
@@ -65,6 +69,9 @@ void prepacked_sizes(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_b
 hipError_t launch_prepack_weight(const uint8_t* b_q, const uint8_t* b_s, int n, int k, uint8_t* bp_q, uint8_t* bp_s,
                                  hipStream_t stream);
 hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream);
+// Both operands prepacked (a_q / a_s and b_q / b_s in the prepacked layout):
+// no LDS in the main loop.
+hipError_t launch_gemm_both_prepacked(const GemmArgs& args, hipStream_t stream);
 
 // MoE steps around the grouped GEMM (include/mxfp4_moe.h).
 constexpr int kMoeMaxTopK = 8;          // routing: experts per token

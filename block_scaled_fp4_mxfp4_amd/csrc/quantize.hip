@@ -96,6 +96,52 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same quantization written straight into the prepacked operand layout of
+// the small-M GEMM (include/mxfp4.h, mxfp4_prepack_weight): per 64-row panel
+// P and 512-K pair t, a block's 16 code bytes form one lane's operand, at
+//   (P * pairs + t) * 16384 + w * 4096 + (2s + j) * 1024 + l * 16,
+// and its scale byte sits at (P * pairs + t) * 1024 + w * 256 + l * 4 + 2s + j,
+// where for row r and 32-element block kb of that row: j = (r % 64) / 32,
+// t = kb / 16, s = (kb / 8) % 2, w = (kb / 2) % 4, l = r % 32 + 32 * (kb % 2).
+// Rows from `rows` up to the panel boundary are written as zero blocks (code
+// 0, scale byte 0: what a zero row quantizes to).  Codes and scale bytes are
+// those of quantize_kernel, bit for bit; only where they are stored differs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kQuantThreads) void quantize_prepacked_kernel(
+    const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ scales, int64_t rows,
+    int kblocks, int64_t nblocks) {
+  const int lane4 = threadIdx.x & 3;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
+  const int pairs = kblocks / 16;
+  for (int64_t b = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2); b < nblocks;
+       b += groups_per_grid) {
+    const int64_t r = b / kblocks;
+    const int kb = (int)(b - r * kblocks);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < rows) v = x[b * 4 + lane4];   // padded rows past `rows` encode a zero block
+    const uint32_t m01 = umax16x2(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu);
+    const uint32_t m23 = umax16x2(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu);
+    const uint32_t m = umax16x2(m01, m23);
+    uint32_t amax_bits = max(m & 0xFFFFu, m >> 16);
+    amax_bits = quad_max(amax_bits);
+    const uint32_t sbyte = (uint32_t)max((int)(amax_bits >> 7) - 2, 0);
+    const float scale = __uint_as_float(sbyte << 23);
+    uint32_t packed = 0;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.w), scale, 3);
+    const int64_t panel = r / 64;
+    const int rr = (int)(r - panel * 64);
+    const int j = rr >> 5, t = kb >> 4, s = (kb >> 3) & 1, w = (kb >> 1) & 3;
+    const int l = (rr & 31) + 32 * (kb & 1);
+    const int64_t blk = panel * pairs + t;
+    q[(blk * 16384 + w * 4096 + (2 * s + j) * 1024 + l * 16) / 4 + lane4] = packed;
+    if (lane4 == 0) scales[blk * 1024 + w * 256 + l * 4 + 2 * s + j] = (uint8_t)sbyte;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // BF16 -> MXFP8 (E4M3 elements, E8M0 scales): the activation format of the W4A8
 // GEMM ("fp4_quantization" page, quantize_dynamic_scaled_fp4fp8: BF16 to
 // NVFP4 / MXFP4 / MXFP8 with per-block scale factors).  Same block mapping as
@@ -188,6 +234,19 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
                      (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                     hipStream_t stream, int num_cus) {
+  const int64_t padded = (rows + 63) / 64 * 64;
+  const int64_t nblocks = padded * (k / 32);
+  int64_t grid = (nblocks + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
+  const int64_t max_grid = (int64_t)num_cus * 8;
+  if (grid > max_grid) grid = max_grid;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quantize_prepacked_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                     (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, rows, (int)(k / 32), nblocks);
   return hipGetLastError();
 }
 

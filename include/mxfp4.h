@@ -211,6 +211,28 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked(const void* a_q, const void* a_s, const v
                                        void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
 
 /*
+ * Quantization (as mxfp4_quantize, bit for bit) written straight into the
+ * prepacked layout above, for an activation that feeds
+ * mxfp4_gemm_nt_prepacked_ab.  x_bf16: [rows, k] row-major, 16-byte aligned;
+ * ap_q, ap_s: code_bytes and scale_bytes of mxfp4_prepacked_weight_size(rows,
+ * k) (ap_q 16-byte aligned), every byte written (rows up to the next multiple
+ * of 64 as zero blocks); k a positive multiple of 512.
+ */
+mxfp4_status_t mxfp4_quantize_prepacked(const void* x_bf16, int64_t rows, int64_t k, void* ap_q, void* ap_s,
+                                        void* stream);
+
+/*
+ * C[m, n] = A . B^T with BOTH operands prepacked: ap_q / ap_s are A [m, k]
+ * rearranged by mxfp4_prepack_weight (the layout is defined for any [rows, k]
+ * MXFP4 operand; rows past m are zero), bp_q / bp_s as above.  Each wave then
+ * loads A and B straight into registers and the main loop uses no LDS.  Same
+ * result, bit for bit, as mxfp4_gemm_nt_prepacked.  Alignment, k and output
+ * as for mxfp4_gemm_nt_prepacked.
+ */
+mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, const void* bp_q, const void* bp_s,
+                                          void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
  * Kernel selection for tests and tuning.  mxfp4_gemm_nt chooses a kernel per
  * shape; mxfp4_gemm_nt_ex lets a caller force one so every kernel can be
  * checked on any shape.  `kernel` values:

@@ -12,7 +12,11 @@
 * the full decode workload (128 x 14336 x 4096) bit-identical to the streaming
   kernel over the whole output and within tolerance of the oracle on samples;
 * the tiny workload's fp32 C at the points whose oracle values are stored in
-  tests/golden; quantize + prepacked GEMM replayed from a HIP graph.
+  tests/golden; quantize + prepacked GEMM replayed from a HIP graph;
+* both operands prepacked: the quantizer writing the prepacked layout equals
+  the layout definition applied to the oracle's quantization (padded rows
+  zero), and the GEMM on prepacked A and B is bit-identical to the other two
+  kernels on every shape above and on the full decode workload.
 """
 import numpy as np
 import pytest
@@ -20,8 +24,9 @@ import torch
 
 import oracle
 import workloads
-from block_scaled_fp4_mxfp4_amd import (MXFP4Error, mxfp4_gemm_nt, mxfp4_gemm_nt_prepacked, mxfp4_prepack_weight,
-                                        mxfp4_prepacked_weight_size, mxfp4_quantize)
+from block_scaled_fp4_mxfp4_amd import (MXFP4Error, mxfp4_gemm_nt, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,
+                                        mxfp4_prepack_weight, mxfp4_prepacked_weight_size, mxfp4_quantize,
+                                        mxfp4_quantize_prepacked)
 from tests.gpu_common import device, log, poisoned, random_bf16, random_codes, sampled_indices, to_np, upload
 
 pytestmark = pytest.mark.gpu
@@ -69,14 +74,22 @@ def test_prepack_layout_matches_definition(n, k):
 
 
 def _both(aq, as_, bq, bs, dev, out_dtype):
+    """(prepacked-B result, streaming-kernel result); the result with A prepacked
+    too is checked bit for bit against the first here."""
     a_q, a_s, b_q, b_s = (upload(t, dev) for t in (aq, as_, bq, bs))
     bp_q, bp_s = mxfp4_prepack_weight(b_q, b_s)
+    ap_q, ap_s = mxfp4_prepack_weight(a_q, a_s)
     m, n = a_q.shape[0], b_q.shape[0]
+    k = a_q.shape[1] * 2
     c_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
     mxfp4_gemm_nt_prepacked(a_q, a_s, bp_q, bp_s, n, c=c_all[:m])
+    c2_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
+    mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, c=c2_all[:m])
     ref = mxfp4_gemm_nt(a_q, a_s, b_q, b_s, out_dtype=out_dtype, kernel="stream")
     torch.cuda.synchronize()
     assert torch.all(c_all[m:].view(torch.uint8) == 0x7F), "write past C"
+    assert torch.all(c2_all[m:].view(torch.uint8) == 0x7F), "write past C (A prepacked)"
+    assert torch.equal(c2_all[:m].view(torch.uint8), c_all[:m].view(torch.uint8)), "A-prepacked result differs"
     return c_all[:m], ref
 
 
@@ -201,3 +214,60 @@ def test_prepacked_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("rows,k", [(1, 512), (63, 1024), (64, 512), (130, 4096), (200, 1536)])
+def test_quantize_prepacked_matches_oracle_layout(rows, k):
+    dev = device()
+    log(f"quantize prepacked rows={rows} k={k}")
+    x = random_bf16((rows, k), 31 * rows + k, spread=8, outlier_frac=0.01)
+    cb, sb = mxfp4_prepacked_weight_size(rows, k)
+    ap_q = poisoned((cb,), torch.uint8, dev, 0xA5)
+    ap_s = poisoned((sb,), torch.uint8, dev, 0xA5)
+    mxfp4_quantize_prepacked(x.to(dev), ap_q, ap_s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize(workloads.bf16_bits(x))
+    want_q, want_s = _prepack_numpy(rq, rs)
+    assert np.array_equal(to_np(ap_q), want_q)
+    assert np.array_equal(to_np(ap_s), want_s)
+
+
+def test_prepacked_ab_decode_full_size_and_graph():
+    """Decode 128 x 14336 x 4096 from BF16 A: quantize into the prepacked layout and
+    multiply, bit-identical to quantize + streaming kernel; then the same two
+    launches replayed from a HIP graph."""
+    dev = device()
+    w = workloads.DECODE
+    log(f"prepacked A and B {w.name}")
+    a, b = w.make()
+    a_d = a.to(dev)
+    aq, as_ = mxfp4_quantize(a_d)
+    bq, bs = mxfp4_quantize(b.to(dev))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    ap_q, ap_s = mxfp4_quantize_prepacked(a_d)
+    c = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+    mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, w.m, w.n, w.k, c=c)
+    s = mxfp4_gemm_nt(aq, as_, bq, bs, kernel="stream")
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), s.view(torch.int16))
+
+    def step():
+        mxfp4_quantize_prepacked(a_d, ap_q, ap_s)
+        mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, w.m, w.n, w.k, c=c)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        c.view(torch.uint8).fill_(0xCD)
+        ap_q.fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), s.view(torch.int16)), f"replay {rep}"
