@@ -619,6 +619,7 @@ KERNEL_SOURCES = {
     "gemm_stream_pre_kernel": ("gemm_stream.hip", "common.hpp"),
     "gemm_pp_kernel": ("gemm_stream.hip", "common.hpp"),
     "quantize_kernel": ("quantize.hip", "common.hpp"),
+    "quantize_prepacked_kernel": ("quantize.hip", "common.hpp"),
     "quantize_scatter_kernel": ("moe.hip", "common.hpp"),
     "combine_kernel": ("moe.hip", "common.hpp"),
     "rmsnorm_quantize_kernel": ("producers.hip", "common.hpp"),
