@@ -268,3 +268,32 @@ def test_row_per_workgroup_kernels_cap_rows(lib):
     assert lib.mxfp4_rmsnorm_quantize(f(), None, f(), 1e-5, (1 << 24) + 1, 64, None, None, f(), f(), None) == 1
     assert lib.nvfp4_quantize(f(), (1 << 24) + 1, 64, f(), f(), f(), None) == 1
     assert b"2^24" in lib.mxfp4_last_error()
+
+
+def test_prepacked_entry_points_reject_bad_arguments_on_host(lib):
+    f = _fake
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    size = lib.mxfp4_prepacked_weight_size
+    assert size(100, 1024, ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert (cb.value, sb.value) == (128 * 512, 128 * 32)                       # rows padded to 64
+    assert size(64, 992, ctypes.byref(cb), ctypes.byref(sb)) == 1               # k % 512
+    assert b"multiple of 512" in lib.mxfp4_last_error()
+    assert size(-1, 512, ctypes.byref(cb), ctypes.byref(sb)) == 1
+    assert size(64, 512, None, ctypes.byref(sb)) == 1
+    assert lib.mxfp4_prepack_weight(f(), f(), 64, 544, f(), f(), None) == 1     # k % 512
+    assert lib.mxfp4_prepack_weight(f(), f(), 64, 512, f(0x1004), f(), None) == 1   # misaligned bp_q
+    assert lib.mxfp4_prepack_weight(None, None, 0, 512, None, None, None) == 0  # no rows: no-op
+    assert lib.mxfp4_quantize_prepacked(f(), 4, 1024 + 32, f(), f(), None) == 1
+    assert lib.mxfp4_quantize_prepacked(f(0x1008), 4, 1024, f(), f(), None) == 1     # misaligned x
+    assert lib.mxfp4_quantize_prepacked(None, 0, 1024, None, None, None) == 0
+    for g in (lib.mxfp4_gemm_nt_prepacked,):
+        assert g(f(), f(), f(), f(), f(), 0, 4, 64, 1000, None) == 1           # k % 512
+        assert g(f(), f(), f(), f(), f(), 3, 4, 64, 512, None) == 1            # output type
+        assert g(f(), f(), None, f(), f(), 0, 4, 64, 512, None) == 1           # null bp_q
+        assert g(f(), f(0x1004), f(), f(), f(), 0, 4, 64, 512, None) == 1      # misaligned a_s
+        assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0         # m == 0: no-op
+    g = lib.mxfp4_gemm_nt_prepacked_ab
+    assert g(f(), f(), f(), f(), f(), 0, 4, 64, 1000, None) == 1
+    assert g(f(), None, f(), f(), f(), 0, 4, 64, 512, None) == 1               # null ap_s
+    assert g(f(), f(), f(), f(), f(), 0, (1 << 30) + 1, 64, 512, None) == 1    # m too large
+    assert g(None, None, None, None, None, 0, 4, 0, 512, None) == 0            # n == 0: no-op
