@@ -367,6 +367,10 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
 // Rows past N are zero codes with scale byte 0.  Panels are stored in order,
 // pairs in order within a panel.
 constexpr int kPreCodeBlock = 16 * 1024;
+// Cache policy of the weight loads: non-temporal (the weight is read once per
+// launch; streaming it past the caches leaves the L2 to the activation, which
+// every workgroup re-reads).  Same-box A/B on the decode GEMM: 4 % faster.
+constexpr int kLoadNT = 2;
 constexpr int kPreScaleBlock = 1024;
 constexpr int kPreDepth = 4;   // B pairs in each wave's register ring (depths 4-8 measured within 2 %)
 constexpr int kPreBLoads = 4;  // vector-memory ops per B pair per thread
@@ -477,7 +481,7 @@ __device__ __forceinline__ void load_bpair(BPair& b, __amdgpu_buffer_rsrc_t r, u
   const uint32_t off = voff + (uint32_t)p * kPreCodeBlock;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    b.q[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + u * 1024, 0, 0));
+    b.q[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + u * 1024, 0, kLoadNT));
   asm volatile("" ::: "memory");
 }
 
@@ -697,8 +701,8 @@ __device__ __forceinline__ void pp_load(PPPair<MB>& r, __amdgpu_buffer_rsrc_t ra
   const uint32_t pq = qoff + (uint32_t)p * kPreCodeBlock, ps = soff + (uint32_t)p * kPreScaleBlock;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    r.b[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, pq + u * 1024, 0, 0));
-  r.sb = (int)__builtin_amdgcn_raw_buffer_load_b32(rsb, ps, 0, 0);
+    r.b[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, pq + u * 1024, 0, kLoadNT));
+  r.sb = (int)__builtin_amdgcn_raw_buffer_load_b32(rsb, ps, 0, kLoadNT);
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int panel = MB > 1 ? i / 2 : 0;
