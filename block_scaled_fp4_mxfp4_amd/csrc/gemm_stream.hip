@@ -51,6 +51,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;    // code bytes per row per 256-K stage
+// Cache policy of the weight loads and copies: non-temporal.  The weight is
+// read once per launch; streaming it past the caches leaves the L2 to the
+// activation, which every workgroup re-reads.  Same-box A/B: 4 % faster for
+// the prepacked decode GEMM, 1.5-2.5 % for this streaming kernel.
+constexpr int kLoadNT = 2;
 constexpr int kBN = 64;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
@@ -123,9 +128,13 @@ __device__ __forceinline__ void copy_pair(uint8_t MXFP4_LDS* buf, const Sources<
 #pragma unroll
     for (int j = 0; j < C::CODE_LOADS; ++j) {
       // wave-uniform: A_SLOTS is a multiple of 64
-      const int stride = ((j * 4 + w) * 64 < C::A_SLOTS) ? C::A_ROW : kRowBytes;
-      g2lds_16(src.code[j] + (2 * p + s) * stride,
-               (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
+      if ((j * 4 + w) * 64 < C::A_SLOTS)
+        g2lds_16(src.code[j] + (2 * p + s) * C::A_ROW,
+                 (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
+      else   // weight rows: read once per launch, streamed past the caches (non-temporal)
+        __builtin_amdgcn_global_load_lds(src.code[j] + (2 * p + s) * kRowBytes,
+                                         (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16), 16, 0,
+                                         kLoadNT);
     }
   g2lds_16(src.scale + p * 16, (MXFP4_LDS void*)(buf + 2 * C::STAGE + w * 64 * 16));
 }
@@ -367,10 +376,6 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
 // Rows past N are zero codes with scale byte 0.  Panels are stored in order,
 // pairs in order within a panel.
 constexpr int kPreCodeBlock = 16 * 1024;
-// Cache policy of the weight loads: non-temporal (the weight is read once per
-// launch; streaming it past the caches leaves the L2 to the activation, which
-// every workgroup re-reads).  Same-box A/B on the decode GEMM: 4 % faster.
-constexpr int kLoadNT = 2;
 constexpr int kPreScaleBlock = 1024;
 constexpr int kPreDepth = 4;   // B pairs in each wave's register ring (depths 4-8 measured within 2 %)
 constexpr int kPreBLoads = 4;  // vector-memory ops per B pair per thread
