@@ -188,8 +188,12 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
       b = b < nblocks ? b : 0;   // out-of-range groups load block 0 and store nothing
       const int row = b / kblocks, kb = b - row * kblocks;
       const int64_t off = (int64_t)row * ld + kb * 32 + lane4 * 8;
-      gv[u] = *(const uint4*)(gate + off);
-      uv[u] = *(const uint4*)(up + off);
+      // gate and up are read once: non-temporal (same-box A/B on 4096 x 14336: 48.6-49.2 vs 54.4-55.0 us;
+      // the same policy on the RMSNorm kernel's loads measured 8 % slower and is not used there)
+      const v4i gt = __builtin_nontemporal_load((const v4i*)(gate + off));
+      const v4i ut = __builtin_nontemporal_load((const v4i*)(up + off));
+      gv[u] = make_uint4((uint32_t)gt.x, (uint32_t)gt.y, (uint32_t)gt.z, (uint32_t)gt.w);
+      uv[u] = make_uint4((uint32_t)ut.x, (uint32_t)ut.y, (uint32_t)ut.z, (uint32_t)ut.w);
     }
 #pragma unroll
     for (int u = 0; u < kProdUnroll; ++u) {

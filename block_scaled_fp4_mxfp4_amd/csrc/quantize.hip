@@ -69,7 +69,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     for (int u = 0; u < kQuantUnroll; ++u) {
       const int64_t b = blk + u * groups_per_grid;
       // out-of-range groups load a valid block (block 0) and store nothing
-      v[u] = x[(b < nblocks ? b : 0) * 4 + lane4];
+      // BF16 input read once: non-temporal (same-box A/B on 4096 x 4096: 9.73-9.84 vs 9.84-10.19 us)
+      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? b : 0) * 4 + lane4));
+      v[u] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
     }
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
@@ -185,7 +187,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
       const int64_t b = blk + u * groups_per_grid;
-      v[u] = x[(b < nblocks ? b : 0) * 4 + lane4];
+      // BF16 input read once: non-temporal (same-box A/B on 4096 x 4096: 9.73-9.84 vs 9.84-10.19 us)
+      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? b : 0) * 4 + lane4));
+      v[u] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
     }
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
