@@ -718,6 +718,18 @@ def run_only(args, dev):
         torch.cuda.synchronize()
         eprint(f"[bench] {args.steps} copies of {COPY_BYTES} bytes")
         return
+    if args.only in ("probe_mfma", "probe_mfma_w4a8"):
+        # the MFMA-only probe at the tile kernel's occupancy, one 4096^3-length launch each
+        cl = Ceilings(dev)
+        a_fp8 = args.only == "probe_mfma_w4a8"
+        iters = 64 if a_fp8 else 128
+        for i in range(args.warmup + args.steps):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+            cl.B.mxfp4_probe_mfma(cl.seed, cl.mfma_out, cl.cus, iters, a_fp8=a_fp8)
+        torch.cuda.synchronize()
+        eprint(f"[bench] {args.steps} eager '{args.only}' launches ({cl.cus} workgroups, {iters} iterations)")
+        return
     w = workloads.ALL[args.workload]
     act = "mxfp8" if args.w4a8_only else "mxfp4"
     if args.nvfp4_only and isinstance(w, workloads.DenseWorkload) and args.only in ("gemm", "quantize", "step"):
@@ -764,7 +776,8 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "gemm_prepacked_ab",
                                        "step_prepacked_ab", "quantize_prepacked", "quantize", "quantize_b", "copy",
-                                       "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu"],
+                                       "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu",
+                                       "probe_mfma", "probe_mfma_w4a8"],
                     help="eager launches for profiling; route/permute/scatter/combine/layer run the "
                          "on-device MoE layer's steps (layer = all five) on the MoE workload")
     ap.add_argument("--no-moe-layer", action="store_true", help="skip the on-device MoE layer measurement")
