@@ -85,16 +85,67 @@ def w4a8_algorithmic_bytes(m, n, k, out_bytes=2):
     return m * k + m * k // 32 + n * k // 2 + n * k // 32 + m * n * out_bytes
 
 
+def calls_per_replay(steps: int) -> int:
+    """Calls per graph replay for `steps` timed calls: the largest divisor of
+    `steps` that leaves at least four replays (samples), at most 64 calls; one
+    call per replay below four steps."""
+    if steps < 4:
+        return 1
+    return max(d for d in range(1, min(64, steps // 4) + 1) if steps % d == 0)
+
+
+def summarize(samples, calls_per_sample=1):
+    """mean / min / median / max (ms per call) over one list of per-call samples."""
+    return {"mean": statistics.fmean(samples), "min": min(samples), "median": statistics.median(samples),
+            "max": max(samples), "samples": len(samples), "calls_per_sample": calls_per_sample}
+
+
+def us(t):
+    """A timing summary in microseconds (sample counts kept as they are)."""
+    return {k: (v if k in ("samples", "calls_per_sample") else round(v * 1e3, 3)) for k, v in t.items()}
+
+
+def roofline(bound, achieved, peak, unit, traffic=None, kernel=None):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+def dense_inputs_record(w) -> dict:
+    """Seeds and SHA-256 of the BF16 operands a dense workload draws."""
+    a, b = w.make()
+    return {"seeds": {"a": w.seed + workloads.ROLE_A, "a_outlier_channels": w.seed + workloads.ROLE_OUTLIER,
+                      "b": w.seed + workloads.ROLE_B},
+            "a_outliers": w.a_outliers, "b_sigma": w.b_sigma,
+            "sha256": {"a_bf16": workloads.sha256_of(a), "b_bf16": workloads.sha256_of(b)}}
+
+
+def moe_inputs_record(w) -> dict:
+    """Seeds and SHA-256 of the MoE workload's inputs: token activations, router
+    logits, expert weights and the offsets of the host routing."""
+    x = w.tokens_bf16()
+    wts = workloads.gaussian_bf16((w.experts, w.n, w.k), w.w_sigma, w.seed + workloads.ROLE_B)
+    _, offsets = w.routing()
+    return {"seeds": {"x": w.seed + workloads.ROLE_A, "w": w.seed + workloads.ROLE_B,
+                      "route_bias": w.seed + workloads.ROLE_ROUTE_BIAS, "route_noise": w.seed + workloads.ROLE_ROUTE_NOISE},
+            "bias_sigma": w.bias_sigma, "w_sigma": w.w_sigma,
+            "sha256": {"x_bf16": workloads.sha256_of(x), "logits_f32": workloads.sha256_of(w.logits()),
+                       "w_bf16": workloads.sha256_of(wts), "offsets_i32": workloads.sha256_of(offsets)}}
+
+
 class DenseBench:
     """act = "mxfp4": the MXFP4 path; act = "mxfp8": W4A8 (MXFP8 activations,
     MXFP4 weights)."""
 
-    def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4"):
+    def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4", quantize_b_in_step: bool = False):
         from block_scaled_fp4_mxfp4_amd import binding as B
         self.B = B
         self.w = w
         self.dev = dev
         self.act = act
+        self.with_b = quantize_b_in_step
         k_a = w.k if act == "mxfp8" else w.k // 2       # A code bytes per row
         a, b = w.make()
         self.a_cpu, self.b_cpu = a, b
@@ -102,6 +153,8 @@ class DenseBench:
         bq, bs = B.mxfp4_quantize(b_d)            # weight quantized once (not in the step)
         m, n, k = w.m, w.n, w.k
         per_set = m * k * 2 + m * k_a + m * k // 32 + n * k // 2 + n * k // 32 + m * n * 2
+        if self.with_b:
+            per_set += n * k * 2       # each set also holds the weight in BF16, quantized in the step
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
         self.per_set_bytes = per_set
         self.sets = []
@@ -111,16 +164,14 @@ class DenseBench:
             st = dict(a=a_d.clone(), aq=torch.empty((m, k_a), dtype=torch.uint8, device=dev),
                       as_=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
                       bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev))
+            if self.with_b:
+                st["b"] = b_d.clone()
             if self.prepacked:
                 st["bp_q"], st["bp_s"] = B.mxfp4_prepack_weight(st["bq"], st["bs"])
                 cb, sb = B.mxfp4_prepacked_weight_size(m, k)
                 st["ap_q"] = torch.empty(cb, dtype=torch.uint8, device=dev)
                 st["ap_s"] = torch.empty(sb, dtype=torch.uint8, device=dev)
             self.sets.append(st)
-        # the weight-packing kernel gets rotating sources of its own
-        self.b_sets = [b_d.clone() for _ in range(max(2, math.ceil(ROTATION_BYTES / (n * k * 2))))]
-        self.b_out = (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
-                      torch.empty((n, k // 32), dtype=torch.uint8, device=dev))
         need = B.load_library().mxfp4_gemm_nt_workspace_size(m, n, k)
         self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         del a_d, b_d
@@ -134,7 +185,15 @@ class DenseBench:
             self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
     def quantize_b(self, i):
-        self.B.mxfp4_quantize(self.b_sets[i % len(self.b_sets)], *self.b_out)
+        """Quantizes the set's BF16 weight into the set's B operand (the bytes it
+        already holds: the same quantization of the same weight)."""
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp4_quantize(s["b"], s["bq"], s["bs"])
+
+    def step_quantize_both(self, i):
+        self.quantize(i)
+        self.quantize_b(i)
+        self.gemm(i)
 
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
@@ -169,41 +228,41 @@ class DenseBench:
         self.gemm_prepacked_ab(i)
 
     @staticmethod
-    def _graph(fn, count):
+    def _graph(fn, first, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(count):
+            for i in range(first, first + count):
                 fn(i)
         return g
 
     def timed(self, fn, steps, warmup, period=None):
-        """Times exactly `steps` calls fn(0), fn(1), ... as graph replays of one
-        rotation period each.  Returns mean / min / median / max ms per call (the
-        spread is over the full periods)."""
+        """Times exactly `steps` calls fn(0), fn(1), ..., fn(steps - 1).
+
+        The calls run as `samples` graph replays of p calls each (p from
+        calls_per_replay: p divides `steps`).  The input rotation continues across
+        replays: replay r runs calls r*p ... r*p + p - 1, so with `period` (default:
+        the number of input sets) rotating sets, ceil-free graph reuse needs
+        lcm(p, period) / p distinct graphs.  Every statistic is over the same
+        per-call samples (one replay's event time / p); the mean over the samples
+        is the events' total over exactly `steps` calls divided by `steps`."""
         period = period or self.sets_n
+        p = calls_per_replay(steps)
+        graphs_n = math.lcm(p, period) // p
         for i in range(2):                    # eager warm-up before capture
             fn(i)
         torch.cuda.synchronize()
-        cycle = self._graph(fn, period)
-        rem = steps % period
-        tail = self._graph(fn, rem) if rem else None
-        for _ in range(max(1, math.ceil(warmup / period))):
-            cycle.replay()
+        graphs = [self._graph(fn, j * p, p) for j in range(graphs_n)]
+        for r in range(max(1, math.ceil(warmup / p))):
+            graphs[r % graphs_n].replay()
         torch.cuda.synchronize()
-        full = steps // period
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(full + 2)]
+        samples_n = steps // p
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples_n + 1)]
         ev[0].record()
-        for r in range(full):
-            cycle.replay()
+        for r in range(samples_n):
+            graphs[r % graphs_n].replay()
             ev[r + 1].record()
-        if tail is not None:
-            tail.replay()
-        ev[-1].record()
         torch.cuda.synchronize()
-        per = [ev[r].elapsed_time(ev[r + 1]) / period for r in range(full)]
-        total = ev[0].elapsed_time(ev[-1]) / steps
-        per = per or [total]
-        return {"mean": total, "min": min(per), "median": statistics.median(per), "max": max(per)}
+        return summarize([ev[r].elapsed_time(ev[r + 1]) / p for r in range(samples_n)], p)
 
 
 class MoEBench:
@@ -355,21 +414,20 @@ def measure_moe_layer(args, dev, us):
     wm = workloads.ALL[args.moe]
     eprint(f"[bench] building inputs for the on-device MoE layer of {wm.name}")
     lb = MoELayerBench(wm, dev)
-    # 16 launches per captured graph: a graph of only the two rotation sets would add a
-    # replay gap of several microseconds to each of the short routing and permutation launches
-    msteps = max(32, args.steps // 2)
-    period = 16
+    # at least 16 launches per graph replay (64 steps = 4 samples of 16): replays of only a few
+    # short routing and permutation launches would add the replay gap to each of them
+    msteps = max(64, args.steps // 2)
     nbytes = lb.algorithmic_bytes()
     out = {"workload": wm.name, "steps": msteps, "rotating_input_sets": lb.sets_n,
            "step": "route + permute + scatter-quantize + grouped mxfp4 GEMM + combine",
            "rows_per_expert": {"min": min(lb.counts), "max": max(lb.counts),
                                "empty": sum(c == 0 for c in lb.counts)}}
-    st = lb.timed(lb.step, msteps, 2, period=period)
+    st = lb.timed(lb.step, msteps, 2)
     out["step_us"] = us(st)
     out["step_tflops"] = round(wm.flops / (st["mean"] * 1e-3) / 1e12, 2)
     kern = {}
     for name in ("route", "permute", "scatter", "gemm", "combine"):
-        tk = lb.timed(getattr(lb, name), msteps, 2, period=period)
+        tk = lb.timed(getattr(lb, name), msteps, 2)
         gbs = nbytes[name] / (tk["mean"] * 1e-3) / 1e9
         kern[name] = {"us": us(tk), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -441,7 +499,7 @@ def measure_producers(args, dev, us):
     out = {}
     for name, shape in (("rmsnorm", f"{pb.rows}x{pb.hidden}, residual add"),
                         ("swiglu", f"{pb.rows}x{pb.inter} from a {pb.rows}x{2 * pb.inter} gate|up buffer")):
-        t = pb.timed(getattr(pb, name), max(32, args.steps // 2), 4, period=16)
+        t = pb.timed(getattr(pb, name), max(64, args.steps // 2), 4)
         gbs = nbytes[name] / (t["mean"] * 1e-3) / 1e9
         kname = f"{name}_quantize_kernel"
         out[name] = {"shape": shape, "us": us(t), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
@@ -552,7 +610,7 @@ class Ceilings:
             for label, iters in (("short", 128), ("long", 1024)):
                 if a_fp8:
                     iters //= 2           # FP8-rate MFMAs take twice as long each
-                self.sets_n = 16
+                self.sets_n = 1
                 flops = self.B.load_library().mxfp4_probe_mfma_flops(self.cus, iters)
                 t = self.timed(lambda i: self.B.mxfp4_probe_mfma(self.seed, self.mfma_out, self.cus, iters,
                                                                  a_fp8=a_fp8),
@@ -605,10 +663,21 @@ def cpu_baseline(bench: DenseBench, target_seconds: float):
     flops = 2 * rows * w.n * w.k * reps
     blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
     avail = len(os.sched_getaffinity(0))
+    # the oracle quantizer alone (NumPy, one thread) on A's rows, about a fifth of the budget
+    q_rows, q_reps, tq = w.m, 0, 0.0
+    while tq < target_seconds / 5:
+        t1 = time.perf_counter()
+        oracle.quantize(a_bits[:q_rows])
+        tq += time.perf_counter() - t1
+        q_reps += 1
+    q_bytes = quant_algorithmic_bytes(q_rows, w.k) * q_reps
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
             "sample": f"{rows} of {w.m} rows of A, {reps} repetition(s), {t:.1f} s: oracle quantize of A "
                       f"(NumPy, one thread) + float64 BLAS GEMM against the pre-quantized {w.n}x{w.k} B "
-                      f"({blas} BLAS threads of {avail} available cores)"}
+                      f"({blas} BLAS threads of {avail} available cores)",
+            "quantize": {"value": round(q_bytes / tq / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle quantize of the {q_rows}x{w.k} BF16 A, {q_reps} repetition(s), "
+                                   f"{tq:.1f} s (NumPy, one thread; bytes = 2 in + 0.5 + 1/32 out per element)"}}
 
 
 # The sources each measured kernel is built from: recorded counter data stays
@@ -692,7 +761,7 @@ def measure_w4a8(args, dev, w, us):
     if args.moe != "none":
         wm = workloads.ALL[args.moe]
         mb = MoEBench(wm, dev, "mxfp8")
-        msteps = max(4, args.steps // 10)
+        msteps = max(8, args.steps // 2)
         sm = mb.timed(mb.step, msteps, 2)
         gm = mb.timed(mb.gemm, msteps, 2)
         tfm = wm.flops / (gm["mean"] * 1e-3) / 1e12
@@ -704,6 +773,76 @@ def measure_w4a8(args, dev, w, us):
         }
         eprint(f"[bench] W4A8 {wm.name}: grouped gemm {gm['mean']*1e3:.1f} us ({tfm:.0f} TFLOP/s)")
         del mb
+    return out
+
+
+def measure_large(args, dev):
+    """The two larger prefill GEMMs: ffn-down 4096x4096x14336 and square 8192^3
+    (step: quantize A + GEMM against the pre-quantized weight), each with its
+    roofline against the FP4 MFMA peak."""
+    out = {}
+    for wl in (workloads.FFN_DOWN, workloads.SQUARE8192):
+        eprint(f"[bench] building inputs for {wl.name}")
+        b = DenseBench(wl, dev)
+        s = b.timed(b.step, args.steps, args.warmup)
+        g = b.timed(b.gemm, args.steps, args.warmup)
+        q = b.timed(b.quantize, args.steps, args.warmup)
+        tf = wl.flops / (g["mean"] * 1e-3) / 1e12
+        qbytes = quant_algorithmic_bytes(wl.m, wl.k)
+        out[wl.name] = {
+            "m": wl.m, "n": wl.n, "k": wl.k, "rotating_input_sets": b.sets_n,
+            "step": "quantize A + mxfp4 NT GEMM -> bf16 (B pre-quantized)",
+            "step_us": us(s), "step_tflops": round(wl.flops / (s["mean"] * 1e-3) / 1e12, 2),
+            "gemm_us": us(g), "gemm_tflops": round(tf, 2),
+            "quantize_a_us": us(q), "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
+            "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s",
+                                 traffic_from_profiles(wl.name, "gemm_tile_kernel"), kernel="gemm_tile_kernel"),
+            "inputs": dense_inputs_record(wl),
+        }
+        eprint(f"[bench] {wl.name}: step {s['mean']*1e3:.1f} us, gemm {g['mean']*1e3:.1f} us ({tf:.0f} TFLOP/s)")
+        del b
+    return out
+
+
+def measure_decode(args, dev, w2, primary: bool):
+    """A decode-shaped workload.  With the weight held prepacked, the step quantizes
+    A straight into the prepacked layout and runs the GEMM that loads both operands
+    into registers; the same GEMM with only B prepacked and on the row-major weight
+    is timed beside it."""
+    eprint(f"[bench] building inputs for {w2.name}")
+    b2 = DenseBench(w2, dev)
+    pre = b2.prepacked
+    s2 = b2.timed(b2.step_prepacked_ab if pre else b2.step, args.steps, args.warmup)
+    g2 = b2.timed(b2.gemm_prepacked_ab if pre else b2.gemm, args.steps, args.warmup)
+    gb = b2.timed(b2.gemm_prepacked, args.steps, args.warmup) if pre else g2
+    gu = b2.timed(b2.gemm, args.steps, args.warmup) if pre else g2
+    q2 = b2.timed(b2.quantize_prepacked if pre else b2.quantize, args.steps, args.warmup)
+    gbytes = gemm_algorithmic_bytes(w2.m, w2.n, w2.k)
+    qb2 = quant_algorithmic_bytes(w2.m, w2.k)
+    gemm_gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
+    kname = "gemm_pp_kernel" if pre else "gemm_stream_kernel"
+    out = {
+        "workload": w2.name, "m": w2.m, "n": w2.n, "k": w2.k,
+        "value": round((gbytes + qb2) / (s2["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "ms_per_step": round(s2["mean"], 6), "step_us": us(s2), "rotating_input_sets": b2.sets_n,
+        "step": ("quantize A into the prepacked layout + mxfp4 GEMM on prepacked A and B "
+                 "(B quantized and prepacked once)" if pre
+                 else "quantize A + streaming mxfp4 GEMM (B pre-quantized)"),
+        "roofline": roofline("hbm", gemm_gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profiles(w2.name, kname),
+                             kernel=kname),
+        "kernels": {"gemm_us": us(g2), "quantize_a_us": us(q2),
+                    "gemm_tflops": round(w2.flops / (g2["mean"] * 1e-3) / 1e12, 2),
+                    "gemm_prepacked_b_only_us": us(gb),
+                    "gemm_prepacked_b_only_gbs": round(gbytes / (gb["mean"] * 1e-3) / 1e9, 1),
+                    "gemm_unpacked_weight_us": us(gu),
+                    "gemm_unpacked_weight_gbs": round(gbytes / (gu["mean"] * 1e-3) / 1e9, 1)},
+        "inputs": dense_inputs_record(w2),
+    }
+    if primary:
+        out["metric"] = "achieved HBM GB/s at decode M=128"
+    eprint(f"[bench] {w2.name}: step {s2['mean']*1e3:.2f} us, gemm {g2['mean']*1e3:.2f} us "
+           f"({gemm_gbs:.0f} GB/s; B-only prepacked {gb['mean']*1e3:.2f} us, unpacked {gu['mean']*1e3:.2f} us)")
+    del b2
     return out
 
 
@@ -746,7 +885,7 @@ def run_only(args, dev):
     elif isinstance(w, workloads.MoEWorkload):
         bench = MoEBench(w, dev, act)
     else:
-        bench = DenseBench(w, dev, act)
+        bench = DenseBench(w, dev, act, quantize_b_in_step=args.only in ("quantize_b", "step_quantize_both"))
     if not hasattr(bench, args.only):
         eprint(f"'{args.only}' is not a mode of {w.name}")
         sys.exit(2)
@@ -777,10 +916,14 @@ def main():
     ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "gemm_prepacked_ab",
                                        "step_prepacked_ab", "quantize_prepacked", "quantize", "quantize_b", "copy",
                                        "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu",
-                                       "probe_mfma", "probe_mfma_w4a8"],
+                                       "probe_mfma", "probe_mfma_w4a8", "step_quantize_both"],
                     help="eager launches for profiling; route/permute/scatter/combine/layer run the "
                          "on-device MoE layer's steps (layer = all five) on the MoE workload")
     ap.add_argument("--no-moe-layer", action="store_true", help="skip the on-device MoE layer measurement")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the ffn-down 4096x4096x14336 and square 8192^3 prefill GEMMs")
+    ap.add_argument("--no-decode-down", action="store_true",
+                    help="skip the ffn-down decode shape 128x4096x14336")
     ap.add_argument("--no-nvfp4", action="store_true", help="skip the NVFP4 measurement")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the fused producer (RMSNorm / SwiGLU emitting MXFP4) measurement")
@@ -811,23 +954,22 @@ def main():
         sys.exit(2)
     w = workloads.DENSE[args.workload]
     eprint(f"[bench] building inputs for {w.name}")
-    bench = DenseBench(w, dev)
+    bench = DenseBench(w, dev, quantize_b_in_step=True)
     eprint(f"[bench] {bench.sets_n} rotating input sets of {bench.per_set_bytes / 2**20:.1f} MiB")
     step = bench.timed(bench.step, args.steps, args.warmup)
     gemm = bench.timed(bench.gemm, args.steps, args.warmup)
     quant = bench.timed(bench.quantize, args.steps, args.warmup)
-    quant_b = bench.timed(bench.quantize_b, args.steps, args.warmup, period=len(bench.b_sets))
+    quant_b = bench.timed(bench.quantize_b, args.steps, args.warmup)
+    step_ab = bench.timed(bench.step_quantize_both, args.steps, args.warmup)
     eprint(f"[bench] step {step['mean']*1e3:.2f} us, gemm {gemm['mean']*1e3:.2f} us, "
-           f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us")
+           f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us, "
+           f"step quantizing both operands {step_ab['mean']*1e3:.2f} us")
 
     flops = w.flops
     gemm_tflops = flops / (gemm["mean"] * 1e-3) / 1e12
     step_tflops = flops / (step["mean"] * 1e-3) / 1e12
     qbytes = quant_algorithmic_bytes(w.m, w.k)
     qbbytes = quant_algorithmic_bytes(w.n, w.k)
-
-    def us(t):
-        return {k: round(v * 1e3, 3) for k, v in t.items()}
 
     result = {
         "metric": "MXFP4 GEMM TFLOP/s at 4096^3; achieved HBM GB/s at decode M=128",
@@ -845,9 +987,9 @@ def main():
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k,
                    "step": "quantize A (bf16->mxfp4) + mxfp4 NT GEMM -> bf16",
                    "rotating_input_sets": bench.sets_n, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(w.name, "gemm_tile_kernel")},
+        "roofline": roofline("mfma", gemm_tflops, PEAK_FP4_TFLOPS, "TFLOP/s",
+                             traffic_from_profiles(w.name, "gemm_tile_kernel"), kernel="gemm_tile_kernel"),
+        "inputs": dense_inputs_record(w),
         "step_us": us(step),
         "kernels": {
             "gemm_us": us(gemm), "gemm_tflops": round(gemm_tflops, 2),
@@ -857,50 +999,25 @@ def main():
             "quantize_b_us": us(quant_b),
             "quantize_b_gbs": round(qbbytes / (quant_b["mean"] * 1e-3) / 1e9, 1),
         },
+        # the step as the workload states it: both operands quantized on the fly
+        "step_quantize_both": {"step": "quantize A + quantize B + mxfp4 NT GEMM -> bf16",
+                               "step_us": us(step_ab),
+                               "step_tflops": round(flops / (step_ab["mean"] * 1e-3) / 1e12, 2)},
     }
 
+    if not args.no_large:
+        result["prefill_large"] = measure_large(args, dev)
+
     if args.secondary != "none":
-        w2 = workloads.DENSE[args.secondary]
-        eprint(f"[bench] building inputs for {w2.name}")
-        b2 = DenseBench(w2, dev)
-        # With the weight held prepacked, the decode step quantizes A straight into
-        # the prepacked layout and runs the GEMM that loads both operands into registers.
-        pre = b2.prepacked
-        s2 = b2.timed(b2.step_prepacked_ab if pre else b2.step, args.steps, args.warmup)
-        g2 = b2.timed(b2.gemm_prepacked_ab if pre else b2.gemm, args.steps, args.warmup)
-        gb = b2.timed(b2.gemm_prepacked, args.steps, args.warmup) if pre else g2
-        gu = b2.timed(b2.gemm, args.steps, args.warmup) if pre else g2
-        q2 = b2.timed(b2.quantize_prepacked if pre else b2.quantize, args.steps, args.warmup)
-        gbytes = gemm_algorithmic_bytes(w2.m, w2.n, w2.k)
-        qb2 = quant_algorithmic_bytes(w2.m, w2.k)
-        gemm_gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
-        kname = "gemm_pp_kernel" if pre else "gemm_stream_kernel"
-        result["secondary"] = {
-            "metric": "achieved HBM GB/s at decode M=128", "workload": w2.name,
-            "value": round((gbytes + qb2) / (s2["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
-            "ms_per_step": round(s2["mean"], 6), "step_us": us(s2), "rotating_input_sets": b2.sets_n,
-            "step": ("quantize A into the prepacked layout + mxfp4 GEMM on prepacked A and B "
-                     "(B quantized and prepacked once)" if pre
-                     else "quantize A + streaming mxfp4 GEMM (B pre-quantized)"),
-            "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_from_profiles(w2.name, kname)},
-            "kernels": {"gemm_us": us(g2), "quantize_a_us": us(q2),
-                        "gemm_tflops": round(w2.flops / (g2["mean"] * 1e-3) / 1e12, 2),
-                        "gemm_prepacked_b_only_us": us(gb),
-                        "gemm_prepacked_b_only_gbs": round(gbytes / (gb["mean"] * 1e-3) / 1e9, 1),
-                        "gemm_unpacked_weight_us": us(gu),
-                        "gemm_unpacked_weight_gbs": round(gbytes / (gu["mean"] * 1e-3) / 1e9, 1)},
-        }
-        eprint(f"[bench] {w2.name}: step {s2['mean']*1e3:.2f} us, gemm {g2['mean']*1e3:.2f} us "
-               f"({gemm_gbs:.0f} GB/s; B-only prepacked {gb['mean']*1e3:.2f} us, unpacked {gu['mean']*1e3:.2f} us)")
-        del b2
+        result["secondary"] = measure_decode(args, dev, workloads.DENSE[args.secondary], primary=True)
+        if not args.no_decode_down:
+            result["decode_down"] = measure_decode(args, dev, workloads.DECODE_DOWN, primary=False)
 
     if args.moe != "none":
         wm = workloads.ALL[args.moe]
         eprint(f"[bench] building inputs for {wm.name}")
         mb = MoEBench(wm, dev)
-        msteps = max(4, args.steps // 10)
+        msteps = max(8, args.steps // 2)
         sm = mb.timed(mb.step, msteps, 2)
         gm = mb.timed(mb.gemm, msteps, 2)
         qm = mb.timed(mb.quantize, msteps, 2)
@@ -918,6 +1035,13 @@ def main():
             "gemm_tflops": round(tf, 2), "gemm_mfma_frac": round(tf / PEAK_FP4_TFLOPS, 4),
             "gemm_gbs": round(gbs, 1), "gemm_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": mbytes,
+            # the workload sits near the ridge: report both roofs and the fraction of the
+            # binding one (roof time = max(flops / MFMA peak, bytes / HBM peak))
+            "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s", kernel="grouped_tile_kernel"),
+            "roofline_hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", kernel="grouped_tile_kernel"),
+            "min_roof_frac": round(max(wm.flops / (PEAK_FP4_TFLOPS * 1e12), mbytes / (PEAK_HBM_GBS * 1e9))
+                                   / (gm["mean"] * 1e-3), 4),
+            "inputs": moe_inputs_record(wm),
         }
         eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")

@@ -557,18 +557,19 @@ __device__ __forceinline__ void mma_pre(const Step<C>& st, const BPair& b, int b
   }
 }
 
-// One pair of the prepacked-B loop (iteration p, B pair p in `cur`, the ring
-// slot of pair p - 1 refilled with pair p + kPreDepth - 1).
-template <class C, bool SKIP_PAST_END>
-__device__ __forceinline__ void pre_pair(uint8_t MXFP4_LDS* lds, const PreCopies<C>& src, int p, int np, int& slot,
-                                         const BPair& cur, BPair& refill_b, __amdgpu_buffer_rsrc_t rb, uint32_t voff,
-                                         int w, int lane, v16f (&acc)[C::MB][2]) {
+// One pair of the prepacked-B pipeline (pair p of a chunk of np pairs that
+// starts at pair p0 of the panel; B pair p in `cur`; the ring slot of pair
+// p - 1 refilled with pair p + kPreDepth - 1).
+template <class C>
+__device__ __forceinline__ void pre_pair(uint8_t MXFP4_LDS* lds, const PreCopies<C>& src, int p0, int p, int np,
+                                         int& slot, const BPair& cur, BPair& refill_b, __amdgpu_buffer_rsrc_t rb,
+                                         uint32_t voff, int w, int lane, v16f (&acc)[C::MB][2]) {
   barrier_lds();                // A pair p is in LDS for every wave; pair p - 1 is read
   if (p + C::NP - 1 < np) {
     const int refill = (slot == 0) ? C::NP - 1 : slot - 1;   // buffer of pair p - 1
-    copy_pair_pre<C>(lds + refill * C::PAIR, src, p + C::NP - 1, w);
+    copy_pair_pre<C>(lds + refill * C::PAIR, src, p0 + p + C::NP - 1, w);
   }
-  if (!SKIP_PAST_END || p + kPreDepth - 1 < np) load_bpair(refill_b, rb, voff, p + kPreDepth - 1);
+  if (p + kPreDepth - 1 < np) load_bpair(refill_b, rb, voff, p0 + p + kPreDepth - 1);
   const uint8_t MXFP4_LDS* buf = lds + slot * C::PAIR;
   const int bsc = *(const int MXFP4_LDS*)(buf + 2 * C::STAGE + 3 * 64 * 16 + w * 256 + lane * 4);
   Step<C> s0, s1;
@@ -579,19 +580,41 @@ __device__ __forceinline__ void pre_pair(uint8_t MXFP4_LDS* lds, const PreCopies
   slot = (slot + 1 == C::NP) ? 0 : slot + 1;
 }
 
+// CH pairs starting at pair p0 as straight-line code: the A ring in LDS and
+// the B ring in registers both start empty and drain within the chunk, so ring
+// slots and wait counts are constants and no register crosses a loop back-edge
+// (a B ring carried round a runtime-K loop made the compiler copy it across
+// the back-edge and spill).  The barrier first: the previous chunk's waves may
+// still read the LDS slots this chunk's first copies overwrite.
+template <class C, int CH>
+__device__ __forceinline__ void pre_chunk(uint8_t MXFP4_LDS* lds, const PreCopies<C>& src, int p0,
+                                          __amdgpu_buffer_rsrc_t rb, uint32_t voff, int w, int lane,
+                                          v16f (&acc)[C::MB][2]) {
+  barrier_lds();
+  BPair ring[kPreDepth];
+#pragma unroll
+  for (int q = 0; q < kPreDepth - 1; ++q) {
+    if (q <= C::NP - 2) copy_pair_pre<C>(lds + q * C::PAIR, src, p0 + min(q, CH - 1), w);
+    if (q < CH) load_bpair(ring[q], rb, voff, p0 + q);
+  }
+  int slot = 0;                 // LDS ring buffer of A pair p
+#pragma unroll
+  for (int p = 0; p < CH; ++p) {   // B pair p sits in ring[p % kPreDepth]
+    wait_vm_at_most(pre_ops_after_a<C>(p, CH));   // a constant once unrolled
+    pre_pair<C>(lds, src, p0, p, CH, slot, ring[p % kPreDepth], ring[(p + kPreDepth - 1) % kPreDepth], rb, voff, w,
+                lane, acc);
+  }
+}
+
 // The streaming kernel on prepacked B: A goes through the same LDS ring of
 // pairs (its scale pieces share the copy with B's prepacked scale block), B
 // through a ring of kPreDepth pairs in each wave's registers.  The per-wave
 // k-step split, the MFMA order and the reduction are those of
 // gemm_stream_kernel, so both give bit-identical fp32 sums.
 //
-// NPC > 0 compiles the kernel for exactly NPC pairs (K = 512 * NPC) as
-// straight-line code: ring slots and wait counts are constants and no
-// register crosses a loop back-edge.  NPC = 0 takes any K with a loop
-// unrolled by kPreDepth; there the compiler keeps the ring alive across the
-// back-edge with register copies that must wait for the loads in flight, so
-// that form overlaps less and is kept for the other values of K.
-template <class C, int NPC>
+// K runs in straight-line chunks of 8, 4 and 1 pairs (K = 4096 is one chunk);
+// both rings refill at each chunk boundary.
+template <class C>
 __global__ __launch_bounds__(kThreads) void gemm_stream_pre_kernel(GemmArgs args, int tiles_m, int tiles_n) {
   static_assert(C::PRE && !C::A8, "prepacked-B configuration");
   static_assert(kPreDepth >= C::NP, "B runs at least as far ahead as A");
@@ -624,42 +647,23 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_pre_kernel(GemmArgs args
                                                  (uint32_t)np * kPreCodeBlock);
   const uint32_t voff = w * 4096 + lane * 16;
 
-  BPair ring[kPreDepth];
-#pragma unroll
-  for (int q = 0; q < kPreDepth - 1; ++q) {
-    if (q <= C::NP - 2) copy_pair_pre<C>(lds + q * C::PAIR, src, min(q, np - 1), w);
-    if (NPC == 0 || q < NPC) load_bpair(ring[q], rb, voff, q);
+  int p0 = 0;
+  for (; p0 + 8 <= np; p0 += 8) pre_chunk<C, 8>(lds, src, p0, rb, voff, w, lane, acc);
+  if (p0 + 4 <= np) {
+    pre_chunk<C, 4>(lds, src, p0, rb, voff, w, lane, acc);
+    p0 += 4;
   }
+  for (; p0 < np; ++p0) pre_chunk<C, 1>(lds, src, p0, rb, voff, w, lane, acc);
 
-  int slot = 0;                 // LDS ring buffer of A pair p
-  if constexpr (NPC > 0) {
-#pragma unroll
-    for (int p = 0; p < NPC; ++p) {   // B pair p sits in ring[p % kPreDepth]
-      wait_vm_at_most(pre_ops_after_a<C>(p, NPC));   // a constant once unrolled
-      pre_pair<C, true>(lds, src, p, NPC, slot, ring[p % kPreDepth], ring[(p + kPreDepth - 1) % kPreDepth], rb, voff, w,
-                  lane, acc);
-    }
-  } else {
-    for (int p0 = 0;; p0 += kPreDepth) {
-#pragma unroll
-      for (int r = 0; r < kPreDepth; ++r) {
-        const int p = p0 + r;     // B pair p sits in ring[r]
-        if (p >= np) goto done;   // leaves the loop: no path skips a load and then reaches an MFMA
-        wait_vm_at_most(pre_ops_after_a<C>(p, np));
-        pre_pair<C, false>(lds, src, p, np, slot, ring[r], ring[(r + kPreDepth - 1) % kPreDepth], rb, voff, w, lane, acc);
-      }
-    }
-  }
-done:
   MXFP4_WAIT_VMCNT(0);
   __syncthreads();   // every wave is done with the ring
 
   stream_epilogue<C>(acc, args, m0, n0, lds, w, lane);
 }
 
-template <class C, int NPC>
+template <class C>
 hipError_t launch_pre_cfg(const GemmArgs& args, hipStream_t stream) {
-  const auto kernel = gemm_stream_pre_kernel<C, NPC>;
+  const auto kernel = gemm_stream_pre_kernel<C>;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
   const int tiles_n = (args.n + kBN - 1) / kBN;
@@ -882,15 +886,9 @@ hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream
   using Pre1 = StreamCfg<1, 4, false, true>;
   using Pre2 = StreamCfg<2, 4, false, true>;
   using Pre4 = StreamCfg<4, 4, false, true>;
-  const int np = args.k / 512;
-  if (np == 8) {   // K = 4096
-    if (args.m <= 32) return launch_pre_cfg<Pre1, 8>(args, stream);
-    if (args.m <= 64) return launch_pre_cfg<Pre2, 8>(args, stream);
-    return launch_pre_cfg<Pre4, 8>(args, stream);
-  }
-  if (args.m <= 32) return launch_pre_cfg<Pre1, 0>(args, stream);
-  if (args.m <= 64) return launch_pre_cfg<Pre2, 0>(args, stream);
-  return launch_pre_cfg<Pre4, 0>(args, stream);
+  if (args.m <= 32) return launch_pre_cfg<Pre1>(args, stream);
+  if (args.m <= 64) return launch_pre_cfg<Pre2>(args, stream);
+  return launch_pre_cfg<Pre4>(args, stream);
 }
 
 hipError_t launch_gemm_both_prepacked(const GemmArgs& args, hipStream_t stream) {

@@ -662,20 +662,41 @@ __global__ __launch_bounds__(C::THREADS) void gemm_tile_kernel(GemmArgs args, in
   run_tile<C, COPY>(args, args.b_q, args.b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
-// Clamped rows [lo, hi) of group g: every offset is clamped into [0, total_m]
-// and each end is kept at or after its start, so any offsets give in-range rows.
-__device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int total_m, int& lo, int& hi) {
-  lo = min(max(offsets[g], 0), total_m);
-  hi = min(max(offsets[g + 1], lo), total_m);
+// Rows [lo, hi) of group g = base + lane within one chunk of 64 groups.  Each
+// offset is clamped into [0, total_m] and replaced by the running maximum of
+// the clamped offsets before it (`carry` holds it from the previous chunk), so
+// any offsets give non-decreasing, disjoint, in-range segments: hi of group g is
+// lo of group g + 1, the segments cover at most total_m rows in all, and their
+// m-tiles number at most ceil(total_m / bm) + groups (the grid's bound).  For
+// valid offsets (non-decreasing, 0 .. total_m) the segments are the offsets'.
+// Lanes past the last group get an empty segment.  Returns the chunk's last hi
+// (wave-uniform), the carry of the next chunk.
+__device__ __forceinline__ int chunk_rows(const int32_t* offsets, int groups, int total_m, int base, int carry,
+                                          int& lo, int& hi) {
+  const int lane = threadIdx.x & 63;
+  const int g = base + lane;
+  const bool valid = g < groups;
+  const int c = valid ? min(max(offsets[g], 0), total_m) : 0;
+  const int e = valid ? min(max(offsets[g + 1], 0), total_m) : 0;
+  int pm = c;   // inclusive running maximum of the chunk's clamped start offsets
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(pm, d, 64);
+    if (lane >= d) pm = max(pm, o);
+  }
+  lo = max(pm, carry);
+  hi = max(lo, e);
+  if (!valid) hi = lo;
+  const int last = min(63, groups - 1 - base);
+  return __builtin_amdgcn_readfirstlane(__shfl(hi, last, 64));
 }
 
 // Number of m-tiles over all groups, ceil(rows_g / bm) each (wave-uniform).
 __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int groups, int total_m, int bm) {
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-  for (int g = lane; g < groups; g += 64) {
+  int cnt = 0, carry = 0;
+  for (int base = 0; base < groups; base += 64) {
     int lo, hi;
-    group_rows(offsets, g, total_m, lo, hi);
+    carry = chunk_rows(offsets, groups, total_m, base, carry, lo, hi);
     cnt += (hi - lo + bm - 1) / bm;
   }
 #pragma unroll
@@ -684,19 +705,16 @@ __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int groups, 
 }
 
 // Finds the expert owning global m-tile `mt` (m-tiles are counted expert by
-// expert, ceil(rows_g / BM) per expert).  Every offset is clamped into
-// [0, total_m] and made non-decreasing first, so any offsets give in-range rows.
+// expert, ceil(rows_g / BM) per expert, over the segments of chunk_rows).
 __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, int total_m, int bm,
                                            int mt, int& g_out, RowRange& ar) {
   const int lane = threadIdx.x & 63;
-  int carry = 0;
+  int carry = 0, carry_rows = 0;
   for (int base = 0; base < groups; base += 64) {
     const int g = base + lane;
-    int lo = 0, hi = 0, cnt = 0;
-    if (g < groups) {
-      group_rows(offsets, g, total_m, lo, hi);
-      cnt = (hi - lo + bm - 1) / bm;
-    }
+    int lo, hi;
+    carry_rows = chunk_rows(offsets, groups, total_m, base, carry_rows, lo, hi);
+    const int cnt = (hi - lo + bm - 1) / bm;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {

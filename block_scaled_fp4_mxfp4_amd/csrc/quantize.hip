@@ -1,8 +1,7 @@
 // BF16 -> MXFP4 dynamic block quantization for gfx950.
 //
-// Operation ("fp4_quantization" Mojo module page, quantize_dynamic_block_scaled_mxfp4:
-// BF16 elements to packed MXFP4 with E8M0 block scales over a flat buffer):
-// per 32-element block, amax -> shared exponent e = floor(log2 amax) - 2 clamped
+// Operation ("fp4_quantization" Mojo module page, Functions,
+// quantize_dynamic_block_scaled_mxfp4): per 32-element block, amax -> shared exponent e = floor(log2 amax) - 2 clamped
 // to the E8M0 range -> each element x / 2^e rounded to nearest-even E2M1 with
 // saturation at 6, two codes per byte (element 2j in the low nibble).
 //

@@ -143,11 +143,14 @@ mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s,
  *   b_q, b_s  : [num_groups, n, k/2], [num_groups, n, k/32]
  *   offsets   : DEVICE int32 [num_groups + 1], 0 = offsets[0] <= ... <=
  *               offsets[num_groups] = total_m.  Not readable by the host
- *               without a synchronisation, so it is not validated: every row
- *               index the kernels form is clamped to [0, total_m), so
- *               malformed offsets cannot cause out-of-bounds accesses, but the
- *               result is then unspecified.  A group with no rows writes
- *               nothing.
+ *               without a synchronisation, so it is not validated; the kernel
+ *               sanitizes it instead: each offset is clamped into [0, total_m]
+ *               and replaced by the running maximum of the clamped offsets up
+ *               to it, and group g owns the rows from its sanitized offset to
+ *               the next.  Malformed offsets therefore give disjoint, in-range
+ *               groups (no row is written twice, no access leaves the
+ *               buffers); rows no group owns are not written.  A group with
+ *               no rows writes nothing.
  *   c         : [total_m, n], element type `c_type`
  *   k         : > 0, a multiple of 32, at most 2^24
  *   num_groups: 1 .. 1024

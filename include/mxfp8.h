@@ -86,8 +86,9 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt_ex(const void* a_q8, const void* a_s, const vo
 /*
  * Grouped per-expert W4A8 NT GEMM: as mxfp4_grouped_gemm_nt with A in MXFP8
  * ([total_m, k] codes, [total_m, k/32] scales), B in MXFP4 ([num_groups, n,
- * k/2], [num_groups, n, k/32]) and the same device `offsets` contract (every
- * row index clamped to [0, total_m); a group with no rows writes nothing);
+ * k/2], [num_groups, n, k/32]) and the same device `offsets` contract
+ * (offsets clamped into [0, total_m] and replaced by their running maximum,
+ * so groups are disjoint and in range; a group with no rows writes nothing);
  * num_groups 1..1024.  No workspace; one kernel launch.
  */
 mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,

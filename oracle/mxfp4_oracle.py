@@ -24,8 +24,8 @@ What it follows
     - element: x / 2**e rounded to the nearest E2M1 value, ties to the even
       code, magnitudes above 6 saturated to 6.
 * Nibble order.  "qgemm-mx" project page, "Where it actually stands": its
-  reference kernel reads "sequential nibble order"; read here as element 2j
-  in the low nibble of byte j.
+  reference kernel reads the packed codes in plain element order; read here
+  as element 2j in the low nibble of byte j.
 * GEMM.  Same DeepGEMM page, Summary: mxfp4_gemm_nt computes
   [M,K] @ [N,K].T -> [M,N] with BF16 out.  The oracle decodes both operands
   exactly and contracts in float64 (a BLAS matmul on the decoded values).

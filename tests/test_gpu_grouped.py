@@ -114,14 +114,38 @@ def test_grouped_moe_workload_full_size_sampled():
         assert_bf16_matches_rounded(got, ref)
 
 
-def test_grouped_malformed_offsets_stay_in_bounds():
-    """Offsets are only clamped on the device (the host cannot read them without a
-    sync): negative, decreasing and past-the-end offsets must neither write
-    outside C nor disturb rows that exactly one clamped group covers."""
+def _sanitized_segments(offsets, total):
+    """The segments the grouped kernel forms from any offsets: each offset clamped
+    into [0, total], then the running maximum, so group g owns [lo_g, lo_{g+1})."""
+    c = np.clip(np.asarray(offsets, np.int64), 0, total)
+    run = np.maximum.accumulate(c)
+    return [(int(run[g]), int(max(run[g], c[g + 1]))) for g in range(len(offsets) - 1)]
+
+
+@pytest.mark.parametrize("case", ["few_groups", "across_chunks"])
+def test_grouped_malformed_offsets_give_disjoint_segments(case):
+    """Offsets are only sanitized on the device (the host cannot read them without
+    a sync): clamped into [0, total_m] and replaced by their running maximum.
+    Negative, decreasing and past-the-end offsets must neither write outside C
+    nor give overlapping groups: every row belongs to exactly one segment and
+    holds that group's dense result, bit for bit."""
     dev = device()
-    total, n, k, groups = 300, 96, 512, 4
-    # clamped groups: g0 = [0, 120), g1 empty, g2 = [80, 300) (overlaps g0), g3 empty
-    offsets = np.array([-5, 120, 80, 500, 300], np.int32)
+    if case == "few_groups":
+        total, n, k = 300, 96, 512
+        # clamped: 0, 120, 80, 300, 300 -> segments [0,120), [120,120), [120,300), [300,300)
+        offsets = np.array([-5, 120, 80, 500, 300], np.int32)
+    else:
+        # 70 groups (two 64-group chunks), a drop inside each chunk and one at the chunk edge
+        total, n, k = 700, 64, 256
+        rng = np.random.default_rng(5)
+        offsets = np.sort(rng.integers(0, total, size=71)).astype(np.int32)
+        offsets[0], offsets[-1] = 0, total
+        offsets[10] = offsets[9] - 30
+        offsets[64] = offsets[63] - 50
+        offsets[66] = total + 40
+    groups = len(offsets) - 1
+    segs = _sanitized_segments(offsets, total)
+    assert segs[0][0] == 0 and all(segs[g][1] == segs[g + 1][0] for g in range(groups - 1))
     a = random_bf16((total, k), 31)
     w = random_bf16((groups * n, k), 32)
     aq, as_ = oracle.quantize(workloads.bf16_bits(a))
@@ -130,15 +154,20 @@ def test_grouped_malformed_offsets_stay_in_bounds():
     d_wq, d_ws = upload(wq.reshape(groups, n, k // 2), dev), upload(ws.reshape(groups, n, k // 32), dev)
     c_all = poisoned((total + 3, n), torch.float32, dev, 0xFF)
     c = c_all[:total]
+    log(f"malformed offsets {case}: {groups} groups, total_m {total}")
     mxfp4_grouped_gemm_nt(d_aq, d_as, d_wq, d_ws, upload(offsets, dev), c=c)
     torch.cuda.synchronize()
     assert torch.all(c_all[total:].view(torch.uint8) == 0xFF), "write past the end of C"
     got = to_np(c)
+    covered = np.zeros(total, bool)
     tile = _tile_for(total, groups)
-    g0 = to_np(mxfp4_gemm_nt(d_aq[0:120], d_as[0:120], d_wq[0], d_ws[0], out_dtype=torch.float32, kernel=tile))
-    g2 = to_np(mxfp4_gemm_nt(d_aq[80:300], d_as[80:300], d_wq[2], d_ws[2], out_dtype=torch.float32, kernel=tile))
-    torch.cuda.synchronize()
-    assert np.array_equal(got[0:80], g0[0:80])
-    assert np.array_equal(got[120:300], g2[40:220])
-    overlap = got[80:120]
-    assert np.all((overlap == g0[80:120]) | (overlap == g2[0:40])), "overlapping rows hold neither group's result"
+    for g, (lo, hi) in enumerate(segs):
+        if hi <= lo:
+            continue
+        ref = to_np(mxfp4_gemm_nt(d_aq[lo:hi], d_as[lo:hi], d_wq[g], d_ws[g], out_dtype=torch.float32, kernel=tile))
+        assert np.array_equal(got[lo:hi], ref), f"group {g} rows [{lo}, {hi})"
+        covered[lo:hi] = True
+    rows_end = segs[-1][1]
+    assert covered[:rows_end].all()
+    # rows past the last segment end are no group's: they keep the poison
+    assert torch.all(c[rows_end:].view(torch.uint8) == 0xFF)

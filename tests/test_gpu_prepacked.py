@@ -69,11 +69,13 @@ def _both(aq, as_, bq, bs, dev, out_dtype):
     return c_all[:m], ref
 
 
-# (m, n, k): K = 4096 runs the straight-line form; other K the looped form
-# (K = 512: one pair, fewer than the 4-pair register ring; 2048: one full trip
-# of the ring; 4608: 9 pairs, a partial last trip; 8192: four trips).
+# (m, n, k): K runs in straight-line chunks of 8, 4 and 1 pairs of 512 (K = 512:
+# one pair, fewer than the 4-pair register ring; 2048: one chunk of 4; 4096: one
+# chunk of 8; 4608: 8 + 1; 6144: 8 + 4; 8192: 8 + 8; 14336: 8 + 8 + 8 + 4, the
+# ffn-down decode shape; 1536: three chunks of 1).
 SHAPES = [(1, 64, 512), (5, 100, 1024), (33, 200, 512), (64, 256, 2048), (96, 130, 4096), (128, 192, 4096),
-          (17, 640, 4096), (130, 64, 4096), (128, 320, 4608), (40, 96, 8192), (200, 72, 1536)]
+          (17, 640, 4096), (130, 64, 4096), (128, 320, 4608), (100, 64, 6144), (40, 96, 8192), (200, 72, 1536),
+          (128, 192, 14336), (64, 130, 14336)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -116,9 +118,10 @@ def test_prepacked_rejects_bad_k_and_empty_problems_are_noops():
     assert c.shape == (0, 64)
 
 
-def test_prepacked_decode_full_size():
+@pytest.mark.parametrize("name", [workloads.DECODE.name, workloads.DECODE_DOWN.name])
+def test_prepacked_decode_full_size(name):
     dev = device()
-    w = workloads.DECODE
+    w = workloads.DENSE[name]
     log(f"prepacked gemm {w.name}")
     a, b = w.make()
     aq, as_ = mxfp4_quantize(a.to(dev))

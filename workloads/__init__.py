@@ -161,8 +161,11 @@ FFN_DOWN = DenseWorkload("ffn_down_4096x4096x14336", 4096, 4096, 14336, seed=400
                          b_sigma=0.02, weight_prequantized=True)
 SQUARE8192 = DenseWorkload("square_8192x8192x8192", 8192, 8192, 8192, seed=450, a_outliers=True,
                            b_sigma=0.02, weight_prequantized=True)
+# the ffn-down projection at decode: 128 tokens against the 4096 x 14336 down weight
+DECODE_DOWN = DenseWorkload("decode_down_128x4096x14336", 128, 4096, 14336, seed=250, a_outliers=True,
+                            b_sigma=0.02, weight_prequantized=True)
 MOE = MoEWorkload("moe_8192tok_top4_64x2816x4096", tokens=8192, experts=64, top_k=4,
                   n=2816, k=4096, seed=500)
 
-DENSE = {w.name: w for w in (TINY, DECODE, SQUARE4096, FFN_DOWN, SQUARE8192)}
+DENSE = {w.name: w for w in (TINY, DECODE, SQUARE4096, FFN_DOWN, SQUARE8192, DECODE_DOWN)}
 ALL = dict(DENSE, **{MOE.name: MOE})
