@@ -8,7 +8,7 @@ from .mxfp4_oracle import (  # noqa: F401
 )
 from .mxfp8_oracle import (  # noqa: F401
     E4M3_TABLE, E4M3_MAGNITUDES, E4M3_MAX, e4m3_value, shared_exponent_e4m3, encode_e4m3_magnitude,
-    quantize_block_values_e4m3, quantize_mxfp8, dequantize_mxfp8, gemm_w4a8_nt,
+    quantize_block_values_e4m3, quantize_mxfp8, dequantize_mxfp8, gemm_w4a8_nt, gemm_mxfp8_nt,
 )
 from .moe_oracle import (  # noqa: F401
     route_topk, permute, quantize_scatter, quantize_scatter_mxfp8, combine, combine_abs,

@@ -26,10 +26,13 @@ What it follows
 * W4A8 GEMM: C[m, n] = sum_k A[m, k] * B[n, k] with A in MXFP8 and B in
   MXFP4 (packed as in mxfp4_oracle), contracted in float64 on the exactly
   decoded values.
+* MXFP8 GEMM: the same contraction with both operands in MXFP8 (the
+  block_scaled_matmul entry of the "fp4_quantization" page's Functions list
+  takes MXFP8 operands on both sides).
 
 Pins: tests/test_oracle_mxfp8_pins.py checks every function here against
 closed forms, PyTorch's float8_e4m3fn conversion (a library routine), exact
-rational brute force and invariants.
+rational brute force, an integer matmul and invariants.
 """
 from __future__ import annotations
 
@@ -161,6 +164,15 @@ def gemm_w4a8_nt(a_q8, a_s, b_q, b_s) -> np.ndarray:
     """C[m, n] = sum_k A[m, k] * B[n, k]: A MXFP8 [m, K], B MXFP4 [n, K/2]; float64."""
     a = dequantize_mxfp8(a_q8, a_s)
     b = dequantize_mxfp4(b_q, b_s)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("K mismatch")
+    return a @ b.T
+
+
+def gemm_mxfp8_nt(a_q8, a_s, b_q8, b_s) -> np.ndarray:
+    """C[m, n] = sum_k A[m, k] * B[n, k]: A MXFP8 [m, K], B MXFP8 [n, K]; float64."""
+    a = dequantize_mxfp8(a_q8, a_s)
+    b = dequantize_mxfp8(b_q8, b_s)
     if a.shape[1] != b.shape[1]:
         raise ValueError("K mismatch")
     return a @ b.T

@@ -189,3 +189,67 @@ def test_gemm_w4a8_tiny_exact_rational(m, n, k, seed):
                 b = _frac_e2m1((byte >> 4) if t & 1 else (byte & 0xF)) * Fraction(2) ** (int(b_s[j, t // 32]) - 127)
                 acc += a * b
             assert got[i, j] == float(acc), (i, j)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(1, 1, 32, 3), (4, 3, 64, 4), (5, 6, 160, 5)])
+def test_gemm_mxfp8_tiny_exact_rational(m, n, k, seed):
+    """Both operands MXFP8, every non-NaN code, scale bytes 125..129.  Every
+    product is a multiple of 2**-9 * 2**-9 * 2**-2 * 2**-2 = 2**-22 and below
+    448 * 448 * 2**4 < 2**22, so in units of 2**-22 each is below 2**44 and a
+    sum of at most 160 of them below 2**52: the exact result fits float64 and
+    the float64 oracle must equal the rational sum exactly."""
+    rng = np.random.default_rng(seed)
+    aq = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+    bq = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0x7E
+    bq[(bq & 0x7F) == 0x7F] = 0xFE
+    a_s = rng.integers(125, 130, size=(m, k // 32), dtype=np.uint8)
+    b_s = rng.integers(125, 130, size=(n, k // 32), dtype=np.uint8)
+    got = O.gemm_mxfp8_nt(aq, a_s, bq, b_s)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for t in range(k):
+                a = _frac_e4m3(int(aq[i, t])) * Fraction(2) ** (int(a_s[i, t // 32]) - 127)
+                b = _frac_e4m3(int(bq[j, t])) * Fraction(2) ** (int(b_s[j, t // 32]) - 127)
+                acc += a * b
+            assert got[i, j] == float(acc), (i, j)
+
+
+def test_gemm_mxfp8_integer_codes_is_an_integer_matmul():
+    """Scale bytes 127 and codes whose E4M3 values are the integers -16..16: the
+    GEMM is an int64 matrix product, exactly (a textbook special case)."""
+    rng = np.random.default_rng(11)
+    ints = {int(v): c for c, v in enumerate(O.E4M3_TABLE) if np.isfinite(v) and float(v).is_integer()
+            and abs(v) <= 16 and (v != 0 or c == 0)}
+    m, n, k = 7, 9, 256
+    ai = rng.integers(-16, 17, size=(m, k))
+    bi = rng.integers(-16, 17, size=(n, k))
+    aq = np.vectorize(lambda v: ints[int(v)])(ai).astype(np.uint8)
+    bq = np.vectorize(lambda v: ints[int(v)])(bi).astype(np.uint8)
+    ones = np.full((m, k // 32), 127, np.uint8)
+    got = O.gemm_mxfp8_nt(aq, ones, bq, np.full((n, k // 32), 127, np.uint8))
+    assert np.array_equal(got, (ai @ bi.T).astype(np.float64))
+    # and it is not symmetric in its operands' roles: C = A . B^T, not B . A^T
+    assert got.shape == (m, n)
+
+
+def test_gemm_mxfp8_with_fp4_valued_b_equals_w4a8():
+    """Every E2M1 value is exact in E4M3: a B operand holding the E4M3 codes of
+    an MXFP4 operand's values (same scale bytes) gives the W4A8 GEMM exactly."""
+    rng = np.random.default_rng(12)
+    m, n, k = 6, 10, 128
+    aq = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0x00
+    a_s = rng.integers(120, 135, size=(m, k // 32), dtype=np.uint8)
+    bq4 = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    b_s = rng.integers(120, 135, size=(n, k // 32), dtype=np.uint8)
+    nib = np.empty((n, k), np.uint8)
+    nib[:, 0::2], nib[:, 1::2] = bq4 & 0xF, bq4 >> 4
+    to8 = {}
+    for c in range(16):
+        v = (-1.0 if c & 8 else 1.0) * GRID4[c & 7]
+        hits = [c8 for c8 in range(256) if O.E4M3_TABLE[c8] == v and (c8 >> 7) == (c >> 3)]
+        to8[c] = hits[0]
+    bq8 = np.vectorize(to8.get)(nib).astype(np.uint8)
+    np.testing.assert_array_equal(O.gemm_mxfp8_nt(aq, a_s, bq8, b_s), O.gemm_w4a8_nt(aq, a_s, bq4, b_s))
