@@ -137,7 +137,7 @@ def moe_inputs_record(w) -> dict:
 
 class DenseBench:
     """act = "mxfp4": the MXFP4 path; act = "mxfp8": W4A8 (MXFP8 activations,
-    MXFP4 weights)."""
+    MXFP4 weights); act = "mxfp8x8": both operands MXFP8."""
 
     def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4", quantize_b_in_step: bool = False):
         from block_scaled_fp4_mxfp4_amd import binding as B
@@ -146,13 +146,16 @@ class DenseBench:
         self.dev = dev
         self.act = act
         self.with_b = quantize_b_in_step
-        k_a = w.k if act == "mxfp8" else w.k // 2       # A code bytes per row
+        a8 = act in ("mxfp8", "mxfp8x8")
+        k_a = w.k if a8 else w.k // 2                    # A code bytes per row
+        k_b = w.k if act == "mxfp8x8" else w.k // 2      # B code bytes per row
         a, b = w.make()
         self.a_cpu, self.b_cpu = a, b
         a_d, b_d = a.to(dev), b.to(dev)
-        bq, bs = B.mxfp4_quantize(b_d)            # weight quantized once (not in the step)
+        # weight quantized once (not in the step)
+        bq, bs = B.mxfp8_quantize(b_d) if act == "mxfp8x8" else B.mxfp4_quantize(b_d)
         m, n, k = w.m, w.n, w.k
-        per_set = m * k * 2 + m * k_a + m * k // 32 + n * k // 2 + n * k // 32 + m * n * 2
+        per_set = m * k * 2 + m * k_a + m * k // 32 + n * k_b + n * k // 32 + m * n * 2
         if self.with_b:
             per_set += n * k * 2       # each set also holds the weight in BF16, quantized in the step
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
@@ -179,7 +182,7 @@ class DenseBench:
 
     def quantize(self, i):
         s = self.sets[i % self.sets_n]
-        if self.act == "mxfp8":
+        if self.act in ("mxfp8", "mxfp8x8"):
             self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
         else:
             self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
@@ -199,6 +202,8 @@ class DenseBench:
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
             self.B.mxfp8_gemm_w4a8_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+        elif self.act == "mxfp8x8":
+            self.B.mxfp8_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         else:
             self.B.mxfp4_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"], ws=self.ws)
 
@@ -695,6 +700,7 @@ KERNEL_SOURCES = {
     "swiglu_quantize_kernel": ("producers.hip", "common.hpp"),
     "nvfp4_quantize_kernel": ("nvfp4.hip", "common.hpp"),
     "nvfp4_gemm_kernel": ("nvfp4.hip", "common.hpp"),
+    "gemm_tile_kernel_f8f8": ("gemm_tile.hip", "common.hpp"),
 }
 
 
@@ -846,6 +852,26 @@ def measure_decode(args, dev, w2, primary: bool):
     return out
 
 
+def measure_mxfp8(args, dev, w):
+    """Both operands MXFP8 on the primary workload: step = MXFP8 quantization of
+    A + the MXFP8 x MXFP8 GEMM against a weight quantized to MXFP8 once, against
+    the FP8 MFMA peak."""
+    eprint(f"[bench] MXFP8 x MXFP8 on {w.name}")
+    b = DenseBench(w, dev, "mxfp8x8")
+    s = b.timed(b.step, args.steps, args.warmup)
+    g = b.timed(b.gemm, args.steps, args.warmup)
+    tf = w.flops / (g["mean"] * 1e-3) / 1e12
+    out = {"workload": w.name, "dtype": "mxfp8 e4m3 x mxfp8 e4m3, e8m0 block scales, fp32 accumulate, bf16 out",
+           "step": "quantize A (bf16->mxfp8) + mxfp8 x mxfp8 NT GEMM -> bf16 (B quantized to mxfp8 once)",
+           "step_us": us(s), "step_tflops": round(w.flops / (s["mean"] * 1e-3) / 1e12, 2), "gemm_us": us(g),
+           "roofline": roofline("mfma", tf, PEAK_FP8_TFLOPS, "TFLOP/s",
+                                traffic_from_profiles(w.name, "gemm_tile_kernel_f8f8"),
+                                kernel="gemm_tile_kernel (mxfp8 x mxfp8, 256x256)")}
+    eprint(f"[bench] MXFP8 x MXFP8 {w.name}: step {s['mean']*1e3:.2f} us, gemm {g['mean']*1e3:.2f} us ({tf:.0f} TFLOP/s)")
+    del b
+    return out
+
+
 def run_only(args, dev):
     """Eager launches for profiling runs."""
     if args.only == "copy":
@@ -870,7 +896,7 @@ def run_only(args, dev):
         eprint(f"[bench] {args.steps} eager '{args.only}' launches ({cl.cus} workgroups, {iters} iterations)")
         return
     w = workloads.ALL[args.workload]
-    act = "mxfp8" if args.w4a8_only else "mxfp4"
+    act = "mxfp8x8" if args.mxfp8_only else ("mxfp8" if args.w4a8_only else "mxfp4")
     if args.nvfp4_only and isinstance(w, workloads.DenseWorkload) and args.only in ("gemm", "quantize", "step"):
         bench = NvBench(w, dev)
     elif args.only in ("rmsnorm", "swiglu"):
@@ -932,6 +958,9 @@ def main():
     ap.add_argument("--w4a8-only", action="store_true",
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
+    ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 x MXFP8 measurement")
+    ap.add_argument("--mxfp8-only", action="store_true",
+                    help="with --only gemm/quantize/step: both operands MXFP8 (the MXFP8 x MXFP8 GEMM)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -1055,6 +1084,9 @@ def main():
 
     if not args.no_w4a8:
         result["w4a8"] = measure_w4a8(args, dev, w, us)
+
+    if not args.no_mxfp8:
+        result["mxfp8"] = measure_mxfp8(args, dev, w)
 
     if not args.no_nvfp4:
         result["nvfp4"] = measure_nvfp4(args, dev, w, us)

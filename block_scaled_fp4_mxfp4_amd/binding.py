@@ -31,7 +31,7 @@ EXPORTED = (
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
     "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
-    "mxfp4_quantize_prepacked",
+    "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex",
 )
 PROBE_SEED_BYTES = 6144
 
@@ -69,6 +69,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp8_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp8_gemm_w4a8_nt_ex.restype = ctypes.c_int
         lib.mxfp8_gemm_w4a8_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp]
+        lib.mxfp8_gemm_nt.restype = ctypes.c_int
+        lib.mxfp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp8_gemm_nt_ex.restype = ctypes.c_int
+        lib.mxfp8_gemm_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp]
         lib.mxfp8_grouped_gemm_w4a8_nt.restype = ctypes.c_int
         lib.mxfp8_grouped_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64, vp]
         lib.mxfp4_gemm_nt_workspace_size.restype = sz
@@ -344,6 +348,22 @@ def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, ke
     c, code = _out(c, m, n, out_dtype, a_q8.device)
     _check(lib.mxfp8_gemm_w4a8_nt_ex(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
                                      KERNELS[kernel], _stream(stream)))
+    return c
+
+
+def mxfp8_gemm_nt(a_q8, a_s, b_q8, b_s, c=None, out_dtype=torch.bfloat16, kernel: str = "auto", stream=None):
+    """C[m, n] = A[m, k] . B[n, k]^T with both operands in MXFP8 ([rows, k] E4M3 codes).
+    kernel: "auto", "tile256" (256 x 256 tiles) or "tile128"."""
+    lib = load_library()
+    m, k = a_q8.shape
+    n = b_q8.shape[0]
+    _require(a_q8, "a_q8", torch.uint8, (m, k))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    _require(b_q8, "b_q8", torch.uint8, (n, k))
+    _require(b_s, "b_s", torch.uint8, (n, k // 32))
+    c, code = _out(c, m, n, out_dtype, a_q8.device)
+    _check(lib.mxfp8_gemm_nt_ex(_ptr(a_q8), _ptr(a_s), _ptr(b_q8), _ptr(b_s), _ptr(c), code, m, n, k,
+                                KERNELS[kernel], _stream(stream)))
     return c
 
 

@@ -435,6 +435,38 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void*
   return mxfp8_gemm_w4a8_nt_ex(a_q8, a_s, b_q, b_s, c, c_type, m, n, k, MXFP4_KERNEL_AUTO, stream);
 }
 
+mxfp4_status_t mxfp8_gemm_nt_ex(const void* a_q8, const void* a_s, const void* b_q8, const void* b_s, void* c,
+                                mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel,
+                                void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s, b_q8, b_s, c, c_type, m, n, k));
+  // a tile's operand rows span 256 * k bytes of FP8 codes, addressed with 32-bit offsets
+  if (k > kMaxK / 2) return fail(MXFP4_ERR_INVALID_ARG, "k too large for MXFP8 operands (%lld > %lld)",
+                                 (long long)k, (long long)(kMaxK / 2));
+  if (kernel != MXFP4_KERNEL_AUTO && kernel != MXFP4_KERNEL_TILE256 && kernel != MXFP4_KERNEL_TILE128)
+    return fail(MXFP4_ERR_INVALID_ARG, "MXFP8 kernels: auto, tile256 or tile128 (got %d)", (int)kernel);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q8;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q8;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  mxfp4::TileKind kind = kernel == MXFP4_KERNEL_TILE128 ? mxfp4::kTile128 : mxfp4::kTile256;
+  if (kernel == MXFP4_KERNEL_AUTO && ((m + 255) / 256) * ((n + 255) / 256) < dev.num_cus) kind = mxfp4::kTile128;
+  return hip_status(mxfp4::launch_gemm_mxfp8_tile(args, kind, (hipStream_t)stream), "mxfp8 gemm launch");
+}
+
+mxfp4_status_t mxfp8_gemm_nt(const void* a_q8, const void* a_s, const void* b_q8, const void* b_s, void* c,
+                             mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  return mxfp8_gemm_nt_ex(a_q8, a_s, b_q8, b_s, c, c_type, m, n, k, MXFP4_KERNEL_AUTO, stream);
+}
+
 mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,
                                           const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
                                           mxfp4_out_t c_type, int64_t n, int64_t k, void* stream) {

@@ -87,6 +87,13 @@ __device__ __forceinline__ v16f mfma32_fp4_fp8(v4i a, v8i b, v16f acc, int sa, i
                                                          OPSEL, sa, OPSEL, sb);
 }
 
+// The same step with both operands in FP8 E4M3 (32 codes per lane in the
+// interleaved order above), at the FP8 rate.
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma32_fp8(v8i a, v8i b, v16f acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, kMfmaFmtFp8, kMfmaFmtFp8, OPSEL, sa, OPSEL, sb);
+}
+
 // Tile index -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
 // the 8 XCDs of MI355X, each XCD with a private L2.  When the tile count is a
 // multiple of 8, consecutive logical tiles are placed on one XCD; logical tiles

@@ -82,30 +82,41 @@
 namespace mxfp4 {
 namespace {
 
-constexpr int kBK = 256;            // K elements per stage
-constexpr int kRowBytes = kBK / 2;  // code bytes per row per stage
-
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Chunk swizzle of an A row: FP4 rows have 8 chunks, FP8 rows 16.
-template <class C>
-__device__ __forceinline__ int a_swz(int row) {
-  return C::A8 ? (row & 15) : swz(row);
+// Chunk swizzle of a row of SHIFT = log2(16-byte chunks): rows of 8 chunks use
+// (row >> 1) & 7, rows of 16 chunks row & 15.
+template <int SHIFT>
+__device__ __forceinline__ int row_swz(int row) {
+  return SHIFT == 4 ? (row & 15) : swz(row);
 }
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool A8_ = false>
+// Tile configuration.  A8: A in FP8 E4M3 (one byte per element) with B in FP4
+// (W4A8).  F8F8: both operands in FP8; a stage then covers 128 K elements, so
+// each operand row of a stage is 128 bytes, as an FP4 row of a 256-K stage.
+template <int BM_, int BN_, int WGM_, int WGN_, bool A8_ = false, bool F8F8_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;               // wave grid over the tile
   static constexpr int NWAVES = WGM * WGN, THREADS = 64 * NWAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NI = WN / 32;
-  static constexpr bool A8 = A8_;                            // A in FP8 E4M3 (W4A8) instead of FP4
-  static constexpr int A_ROW = A8 ? kBK : kRowBytes;         // A code bytes per row per stage
-  static constexpr int A_SHIFT = A8 ? 4 : 3;                 // log2 of the 16-byte chunks in an A row
+  static constexpr bool F8F8 = F8F8_;
+  static constexpr bool A8 = A8_ || F8F8_;                   // A in FP8 E4M3 instead of FP4
+  static constexpr bool B8 = F8F8_;                          // B in FP8 E4M3 instead of FP4
+  static constexpr int SK = F8F8 ? 128 : 256;                // K elements per stage
+  static constexpr int KSTEPS = SK / 64;                     // 64-deep MFMA k-steps per stage
+  static constexpr int SB = SK / 32;                         // scale bytes per row per stage
+  static constexpr int SPG_SHIFT = F8F8 ? 2 : 1;             // log2 of the stages per 16-byte scale piece
+  static constexpr int A_ROW = A8 ? SK : SK / 2;             // A code bytes per row per stage
+  static constexpr int B_ROW = B8 ? SK : SK / 2;             // B code bytes per row per stage
+  static constexpr int A_SHIFT = A_ROW == 256 ? 4 : 3;       // log2 of the 16-byte chunks in an A row
+  static constexpr int B_SHIFT = B_ROW == 256 ? 4 : 3;
   static constexpr int A_READS = A8 ? 2 : 1;                 // ds_read_b128 per A fragment
+  static constexpr int B_READS = B8 ? 2 : 1;
   using AFrag = typename std::conditional<A8, v8i, v4i>::type;
-  static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BN * kRowBytes;
+  using BFrag = typename std::conditional<B8, v8i, v4i>::type;
+  static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BN * B_ROW;
   static constexpr int CODE_STAGE = A_BYTES + B_BYTES;
   // 16-byte scale copies per thread per group (16 scale bytes per row = two
   // stages); when BM + BN is not a multiple of the thread count the last
@@ -114,12 +125,12 @@ struct TileCfg {
   static constexpr int SCALE_GROUP = S_LOADS * THREADS * 16;
   static constexpr int LDS_BYTES = 2 * CODE_STAGE + 2 * SCALE_GROUP;
   static constexpr int A_LOADS = BM * A_ROW / 16 / THREADS;      // 16-byte copies per thread per stage
-  static constexpr int B_LOADS = BN * kRowBytes / 16 / THREADS;
+  static constexpr int B_LOADS = BN * B_ROW / 16 / THREADS;
   static constexpr int CODE_LOADS = A_LOADS + B_LOADS;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
-  static_assert(BM * A_ROW % (16 * THREADS) == 0 && BN * kRowBytes % (16 * THREADS) == 0,
+  static_assert(BM * A_ROW % (16 * THREADS) == 0 && BN * B_ROW % (16 * THREADS) == 0,
                 "code copies must split evenly over the threads");
-  static_assert(!A8 || BM <= 128, "FP8 A: a tile's A bytes (BM * k) must stay below 2^32 for k <= 2^24");
+  static_assert(!A8 || BM <= 128 || F8F8, "FP8 A: a tile's A bytes (BM * k) must stay below 2^32 for k <= 2^24");
   static_assert(WGM == 2, "the fp32 epilogue stages the tile in two halves by wave row");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles of whole 32x32 MFMA blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -147,8 +158,8 @@ struct TileBases {
 template <class C>
 __device__ __forceinline__ TileBases tile_bases(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                                 const RowRange& ar, int n0) {
-  const int64_t kb = args.k / 2, ks = args.k / 32, ka = C::A8 ? args.k : kb;
-  return {args.a_q + ar.lo * ka, b_q + n0 * kb, args.a_s + ar.lo * ks, b_s + n0 * ks};
+  const int64_t ks = args.k / 32, ka = C::A8 ? args.k : args.k / 2, kbb = C::B8 ? args.k : args.k / 2;
+  return {args.a_q + ar.lo * ka, b_q + n0 * kbb, args.a_s + ar.lo * ks, b_s + n0 * ks};
 }
 
 // Buffer resources over the same tile operands, sized to the rows the tile
@@ -160,9 +171,9 @@ struct TileRsrc {
 
 template <class C>
 __device__ __forceinline__ TileRsrc tile_rsrc(const TileBases& tb, const RowRange& ar, int n0, int n, int k) {
-  const uint32_t kb = k / 2, ks = k / 32, ka = C::A8 ? k : kb;
+  const uint32_t ks = k / 32, ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
   const uint32_t a_rows = ar.last - ar.lo + 1, b_rows = min(C::BN, n - n0);
-  return {make_rsrc(tb.a_q, a_rows * ka), make_rsrc(tb.b_q, b_rows * kb), make_rsrc(tb.a_s, a_rows * ks),
+  return {make_rsrc(tb.a_q, a_rows * ka), make_rsrc(tb.b_q, b_rows * kbb), make_rsrc(tb.a_s, a_rows * ks),
           make_rsrc(tb.b_s, b_rows * ks)};
 }
 
@@ -187,19 +198,19 @@ __device__ __forceinline__ bool scale_is_b(int j, int w) {
 template <class C>
 __device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t kb = k / 2, ks = k / 32, ka = C::A8 ? k : kb;
+  const uint32_t ks = k / 32, ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
   const int a_rows = ar.last - ar.lo, b_rows = n - 1 - n0;   // largest valid row offsets
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int r = slot >> C::A_SHIFT, lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ a_swz<C>(r);
+    const int r = slot >> C::A_SHIFT, lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ row_swz<C::A_SHIFT>(r);
     src.a_code[j] = (uint32_t)min(r, a_rows) * ka + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int r = slot >> 3, lc = (slot & 7) ^ swz(r);
-    src.b_code[j] = (uint32_t)min(r, b_rows) * kb + lc * 16;
+    const int r = slot >> C::B_SHIFT, lc = (slot & ((1 << C::B_SHIFT) - 1)) ^ row_swz<C::B_SHIFT>(r);
+    src.b_code[j] = (uint32_t)min(r, b_rows) * kbb + lc * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
@@ -225,7 +236,7 @@ __device__ __forceinline__ void copy_codes_b(uint8_t MXFP4_LDS* stage, const Sou
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j)
-    buf2lds_16(tr.b_q, src.b_code[j], kt * kRowBytes,
+    buf2lds_16(tr.b_q, src.b_code[j], kt * C::B_ROW,
                (MXFP4_LDS void*)(stage + C::A_BYTES + (j * C::NWAVES + w) * 64 * 16));
 }
 
@@ -242,16 +253,17 @@ __device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sour
 
 // Stage kt through registers for any k % 32 == 0: 32-blocks at or past k get
 // zero codes and scale byte 127.  Writes the same LDS layout as the copies
-// (scale bytes of stage kt at byte 8 * (kt & 1) of each row's 16-byte piece).
+// (the SB scale bytes of stage kt at byte SB * (kt mod stages per piece) of
+// each row's 16-byte piece).
 template <class C>
 __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uint8_t MXFP4_LDS* group,
                                                    const Sources<C>& src, const TileBases& tb, int k, int kt) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int blocks_left = k / 32 - kt * 8;   // valid 32-blocks in this stage (may exceed 8)
+  const int blocks_left = k / 32 - kt * C::SB;   // valid 32-blocks in this stage (may exceed SB)
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ a_swz<C>(slot >> C::A_SHIFT);
+    const int lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ row_swz<C::A_SHIFT>(slot >> C::A_SHIFT);
     v4i v = {0, 0, 0, 0};
     // a 32-block is one chunk of FP4 codes or two chunks of FP8 codes
     if ((lc >> (C::A8 ? 1 : 0)) < blocks_left) v = *(const v4i*)(tb.a_q + kt * C::A_ROW + src.a_code[j]);
@@ -260,23 +272,28 @@ __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uin
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const int lc = (slot & 7) ^ swz(slot >> 3);
+    const int lc = (slot & ((1 << C::B_SHIFT) - 1)) ^ row_swz<C::B_SHIFT>(slot >> C::B_SHIFT);
     v4i v = {0, 0, 0, 0};
-    if (lc < blocks_left) v = *(const v4i*)(tb.b_q + kt * kRowBytes + src.b_code[j]);
+    if ((lc >> (C::B8 ? 1 : 0)) < blocks_left) v = *(const v4i*)(tb.b_q + kt * C::B_ROW + src.b_code[j]);
     *(v4i MXFP4_LDS*)(stage + C::A_BYTES + slot * 16) = v;
   }
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    const uint8_t* sp = (scale_is_b<C>(j, w) ? tb.b_s : tb.a_s) + kt * 8 + src.scale[j];
+    const uint8_t* sp = (scale_is_b<C>(j, w) ? tb.b_s : tb.a_s) + kt * C::SB + src.scale[j];
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       lo |= (b < blocks_left ? (uint32_t)sp[b] : 127u) << (8 * b);
-      hi |= (b + 4 < blocks_left ? (uint32_t)sp[b + 4] : 127u) << (8 * b);
+      if constexpr (C::SB == 8) hi |= (b + 4 < blocks_left ? (uint32_t)sp[b + 4] : 127u) << (8 * b);
     }
-    v2i word = {(int)lo, (int)hi};
-    *(v2i MXFP4_LDS*)(group + slot * 16 + 8 * (kt & 1)) = word;
+    const int piece = kt & ((1 << C::SPG_SHIFT) - 1);
+    if constexpr (C::SB == 8) {
+      v2i word = {(int)lo, (int)hi};
+      *(v2i MXFP4_LDS*)(group + slot * 16 + 8 * piece) = word;
+    } else {
+      *(int MXFP4_LDS*)(group + slot * 16 + 4 * piece) = (int)lo;
+    }
   }
 }
 
@@ -284,31 +301,43 @@ __device__ __forceinline__ void load_stage_generic(uint8_t MXFP4_LDS* stage, uin
 template <class C>
 struct Frags {
   typename C::AFrag a[C::MI];
-  v4i b[C::NI];
+  typename C::BFrag b[C::NI];
 };
 
-// Scale words of one stage.  Row r's 8 stage bytes are two 32-bit words:
-// word 0 for k-steps 0-1, word 1 for k-steps 2-3.  Lanes 32..63 feed the odd
-// 32-block of each k-step, so their words are shifted right by one byte; k-step
-// s then takes byte 2 * (s & 1) of word s / 2.
+// Scale words of one stage.  A 256-K stage has 8 scale bytes per row, two
+// 32-bit words: word 0 for k-steps 0-1, word 1 for k-steps 2-3.  A 128-K stage
+// (both operands FP8) has 4, one word for its two k-steps.  Lanes 32..63 feed
+// the odd 32-block of each k-step, so their words are shifted right by one
+// byte; k-step s then takes byte 2 * (s & 1) of word s / 2.
 template <class C>
 struct Scales {
   v2i a[C::MI];
   v2i b[C::NI];
 };
 
+template <class C>
+__device__ __forceinline__ v2i read_scale_word(const uint8_t MXFP4_LDS* p) {
+  if constexpr (C::SB == 8) {
+    return *(const v2i MXFP4_LDS*)p;
+  } else {
+    const int w = *(const int MXFP4_LDS*)p;
+    return v2i{w, w};
+  }
+}
+
 // MA is the number of the wave's 32-row MFMA blocks that are computed (see
-// run_tile); the others need no operands.
+// run_tile); the others need no operands.  `piece` is the stage's index
+// within its scale group (scale bytes at SB * piece of each row's 16 bytes).
 template <class C, int MA = C::MI>
-__device__ __forceinline__ void read_scales_raw(const uint8_t MXFP4_LDS* group, int parity, Scales<C>& sc,
+__device__ __forceinline__ void read_scales_raw(const uint8_t MXFP4_LDS* group, int piece, Scales<C>& sc,
                                                 int wm0, int wn0, int lane) {
   if constexpr (MA > 0) {
-    const uint8_t MXFP4_LDS* base = group + 8 * parity;
+    const uint8_t MXFP4_LDS* base = group + C::SB * piece;
 #pragma unroll
-    for (int i = 0; i < MA; ++i) sc.a[i] = *(const v2i MXFP4_LDS*)(base + (wm0 + 32 * i + (lane & 31)) * 16);
+    for (int i = 0; i < MA; ++i) sc.a[i] = read_scale_word<C>(base + (wm0 + 32 * i + (lane & 31)) * 16);
 #pragma unroll
     for (int j = 0; j < C::NI; ++j)
-      sc.b[j] = *(const v2i MXFP4_LDS*)(base + (C::BM + wn0 + 32 * j + (lane & 31)) * 16);
+      sc.b[j] = read_scale_word<C>(base + (C::BM + wn0 + 32 * j + (lane & 31)) * 16);
   }
 }
 
@@ -329,32 +358,36 @@ __device__ __forceinline__ void shift_scales(Scales<C>& sc, int lane) {
   }
 }
 
+// One operand fragment of k-step S of row r from a stage row of ROW bytes.
+// An FP4 operand: lane half h holds the 32 elements K [32h, 32h + 32) of the
+// k-step, chunk 2S + h.  An FP8 operand interleaves 16-element groups: lane
+// half h holds K [16h, 16h + 16) of the k-step in its first four registers and
+// [32 + 16h, 48 + 16h) in the last four (measured through the library with
+// one-hot rows), i.e. chunks 4S + h and 4S + 2 + h.
+template <bool FP8, int ROW, int SHIFT, int S>
+__device__ __forceinline__ typename std::conditional<FP8, v8i, v4i>::type read_frag(
+    const uint8_t MXFP4_LDS* rows, int r, int lane) {
+  const int h = lane >> 5;
+  const uint8_t MXFP4_LDS* row = rows + r * ROW;
+  if constexpr (FP8) {
+    const v4i lo = *(const v4i MXFP4_LDS*)(row + (((4 * S + h) ^ row_swz<SHIFT>(r)) << 4));
+    const v4i hi = *(const v4i MXFP4_LDS*)(row + (((4 * S + 2 + h) ^ row_swz<SHIFT>(r)) << 4));
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  } else {
+    return *(const v4i MXFP4_LDS*)(row + (((2 * S + h) ^ row_swz<SHIFT>(r)) << 4));
+  }
+}
+
 template <class C, int S, int MA = C::MI>
 __device__ __forceinline__ void read_frags(const uint8_t MXFP4_LDS* stage, Frags<C>& f, int wm0, int wn0,
                                            int lane) {
   if constexpr (MA > 0) {
-    const int c = 2 * S + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < MA; ++i) {
-      const int r = wm0 + 32 * i + (lane & 31);
-      if constexpr (C::A8) {
-        // An FP8 operand interleaves 16-element groups: lane half h holds K
-        // [16h, 16h + 16) of the k-step in its first four registers and
-        // [32 + 16h, 48 + 16h) in the last four (measured through the
-        // library with one-hot rows), i.e. chunks 4S + h and 4S + 2 + h.
-        const int h = lane >> 5;
-        const v4i lo = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * S + h) ^ a_swz<C>(r)) << 4));
-        const v4i hi = *(const v4i MXFP4_LDS*)(stage + r * C::A_ROW + (((4 * S + 2 + h) ^ a_swz<C>(r)) << 4));
-        f.a[i] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      } else {
-        f.a[i] = *(const v4i MXFP4_LDS*)(stage + r * kRowBytes + ((c ^ swz(r)) << 4));
-      }
-    }
+    for (int i = 0; i < MA; ++i)
+      f.a[i] = read_frag<C::A8, C::A_ROW, C::A_SHIFT, S>(stage, wm0 + 32 * i + (lane & 31), lane);
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
-      const int r = wn0 + 32 * j + (lane & 31);
-      f.b[j] = *(const v4i MXFP4_LDS*)(stage + C::A_BYTES + r * kRowBytes + ((c ^ swz(r)) << 4));
-    }
+    for (int j = 0; j < C::NI; ++j)
+      f.b[j] = read_frag<C::B8, C::B_ROW, C::B_SHIFT, S>(stage + C::A_BYTES, wn0 + 32 * j + (lane & 31), lane);
   }
 }
 
@@ -367,7 +400,9 @@ __device__ __forceinline__ void mma_kstep(const Frags<C>& f, const Scales<C>& sc
     for (int j = 0; j < C::NI; ++j) {
       const int sa = (S < 2) ? sc.a[i].x : sc.a[i].y;
       const int sb = (S < 2) ? sc.b[j].x : sc.b[j].y;
-      if constexpr (C::A8)
+      if constexpr (C::F8F8)
+        acc[i][j] = mfma32_fp8<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
+      else if constexpr (C::A8)
         acc[i][j] = mfma32_fp4_fp8<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
       else
         acc[i][j] = mfma32_fp4<2 * (S & 1)>(f.b[j], f.a[i], acc[i][j], sb, sa);
@@ -490,7 +525,7 @@ __device__ __forceinline__ void kstep_slots() {
 
 template <class C, int COPIES, int MA = C::MI>
 __device__ __forceinline__ void kstep_pattern() {
-  kstep_slots<(MA > 0 ? MA * C::A_READS + C::NI : 0), COPIES, MA * C::NI, 0>();
+  kstep_slots<(MA > 0 ? MA * C::A_READS + C::NI * C::B_READS : 0), COPIES, MA * C::NI, 0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -504,6 +539,8 @@ template <class C, int MA, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
 __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
                                                 Scales<C>& sc, const Sources<C>& src, const TileRsrc& tr,
                                                 uint8_t MXFP4_LDS* lds, int kt, int wm0, int wn0, int lane) {
+  constexpr int L = C::KSTEPS - 1;   // the last k-step; its fragments arrive in fb
+  constexpr int G = C::SPG_SHIFT;    // stages per scale group: 1 << G
   uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
   uint8_t MXFP4_LDS* nxt = lds + ((kt + 1) & 1) * C::CODE_STAGE;
   // Fragment reads run one k-step ahead of the MFMAs.  Before a new batch of
@@ -514,14 +551,16 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
   read_frags<C, 1, MA>(cur, fb, wm0, wn0, lane);
   mma_kstep<C, 0, 0, MA>(fa, sc, acc);
   kstep_pattern<C, 0, MA>();
-  MXFP4_WAIT_LGKM0();
-  read_frags<C, 2, MA>(cur, fa, wm0, wn0, lane);
-  mma_kstep<C, 1, 0, MA>(fb, sc, acc);
-  kstep_pattern<C, 0, MA>();
-  MXFP4_WAIT_LGKM0();
-  read_frags<C, 3, MA>(cur, fb, wm0, wn0, lane);
-  mma_kstep<C, 2, 0, MA>(fa, sc, acc);
-  kstep_pattern<C, 0, MA>();
+  if constexpr (C::KSTEPS == 4) {
+    MXFP4_WAIT_LGKM0();
+    read_frags<C, 2, MA>(cur, fa, wm0, wn0, lane);
+    mma_kstep<C, 1, 0, MA>(fb, sc, acc);
+    kstep_pattern<C, 0, MA>();
+    MXFP4_WAIT_LGKM0();
+    read_frags<C, 3, MA>(cur, fb, wm0, wn0, lane);
+    mma_kstep<C, 2, 0, MA>(fa, sc, acc);
+    kstep_pattern<C, 0, MA>();
+  }
   if (NEXT) {
     // stage kt+1 and its scales have landed; stage kt is fully read once every
     // wave has passed the barrier
@@ -530,33 +569,54 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
     __builtin_amdgcn_sched_barrier(0);
     read_frags<C, 0, MA>(nxt, fa, wm0, wn0, lane);
     if (COPY_SCALES)
-      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> 1) & 1) * C::SCALE_GROUP, src, tr, (kt + 2) >> 1);
+      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> G) & 1) * C::SCALE_GROUP, src, tr, (kt + 2) >> G);
     if (COPY_CODES) {
       copy_codes_a<C>(cur, src, tr, kt + 2);
       copy_codes_b<C>(cur, src, tr, kt + 2);
     }
-    mma_kstep<C, 3, 0, MA>(fb, sc, acc);
+    mma_kstep<C, L, 0, MA>(fb, sc, acc);
     // the next stage's first fragments go out before the copies (measured ~2 %
     // faster than interleaving them one per MFMA)
-    if constexpr (MA > 0) __builtin_amdgcn_sched_group_barrier(0x100, MA * C::A_READS + C::NI, 0);
+    if constexpr (MA > 0) __builtin_amdgcn_sched_group_barrier(0x100, MA * C::A_READS + C::NI * C::B_READS, 0);
     kstep_slots<0, (COPY_CODES ? C::CODE_LOADS : 0) + (COPY_SCALES ? C::S_LOADS : 0), MA * C::NI, 0>();
     __builtin_amdgcn_sched_barrier(0);
     // the next stage's scale words replace this stage's once its last MFMAs are issued
-    read_scales_raw<C, MA>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> 1) & 1) * C::SCALE_GROUP, (kt + 1) & 1, sc,
-                           wm0, wn0, lane);
+    read_scales_raw<C, MA>(lds + 2 * C::CODE_STAGE + (((kt + 1) >> G) & 1) * C::SCALE_GROUP,
+                           (kt + 1) & ((1 << G) - 1), sc, wm0, wn0, lane);
     shift_scales<C, MA>(sc, lane);
   } else {
     MXFP4_WAIT_LGKM0();
-    mma_kstep<C, 3, 0, MA>(fb, sc, acc);
+    mma_kstep<C, L, 0, MA>(fb, sc, acc);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Main loop of the copy path with MA computed row blocks per wave.
-// nk = k / 256 is even and >= 2 (k % 512 == 0).
+// Stages kt + J .. kt + SPG - 1 of one scale group's worth of stages (SPG =
+// stages per scale group).  In the loop body (TAIL false) stage kt + J copies
+// stage kt + J + 2, and the stage whose copies start a new scale group (J =
+// SPG - 2) also copies that group.  In the tail (the last SPG stages) only
+// stages before the last two copy, and the last stage has no successor.
+template <class C, int MA, int J, bool TAIL>
+__device__ __forceinline__ void group_stages(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb, Scales<C>& sc,
+                                             const Sources<C>& src, const TileRsrc& tr, uint8_t MXFP4_LDS* lds,
+                                             int kt, int wm0, int wn0, int lane) {
+  constexpr int SPG = 1 << C::SPG_SHIFT;
+  if constexpr (J < SPG) {
+    if constexpr (!TAIL)
+      pipelined_stage<C, MA, true, true, J == SPG - 2>(acc, fa, fb, sc, src, tr, lds, kt + J, wm0, wn0, lane);
+    else
+      pipelined_stage<C, MA, (J < SPG - 1), (J < SPG - 2), false>(acc, fa, fb, sc, src, tr, lds, kt + J, wm0,
+                                                                   wn0, lane);
+    group_stages<C, MA, J + 1, TAIL>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
+  }
+}
+
+// Main loop of the copy path with MA computed row blocks per wave.  nk = k /
+// SK stages, a multiple of the stages per scale group (k % 512 == 0).
 template <class C, int MA>
 __device__ __forceinline__ void copy_loop(v16f (&acc)[C::MI][C::NI], const Sources<C>& src, const TileRsrc& tr,
                                           uint8_t MXFP4_LDS* lds, int nk, int wm0, int wn0, int lane) {
+  constexpr int SPG = 1 << C::SPG_SHIFT;
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
   copy_scales<C>(group0, src, tr, 0);
   copy_codes_a<C>(lds, src, tr, 0);
@@ -571,26 +631,30 @@ __device__ __forceinline__ void copy_loop(v16f (&acc)[C::MI][C::NI], const Sourc
   read_frags<C, 0, MA>(lds, fa, wm0, wn0, lane);
   shift_scales<C, MA>(sc, lane);
   int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    pipelined_stage<C, MA, true, true, true>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
-    pipelined_stage<C, MA, true, true, false>(acc, fa, fb, sc, src, tr, lds, kt + 1, wm0, wn0, lane);
-  }
-  pipelined_stage<C, MA, true, false, false>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
-  pipelined_stage<C, MA, false, false, false>(acc, fa, fb, sc, src, tr, lds, kt + 1, wm0, wn0, lane);
+  for (; kt + SPG < nk; kt += SPG) group_stages<C, MA, 0, false>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
+  group_stages<C, MA, 0, true>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
 }
 
-// copy_loop<C, active> for a wave-uniform active in [0, C::MI].
-template <class C, int MA>
+// copy_loop<C, active> and then the epilogue `epi` for a wave-uniform active
+// in [0, C::MI].  The epilogue runs inside each branch: with the branches
+// merged before it, the accumulators of every branch meet in one set of
+// registers, and with 256 accumulators per wave (one wave per SIMD) the
+// register allocator moved all of them out of the accumulator registers at
+// once and spilled.
+template <class C, int MA, class Epi>
 __device__ __forceinline__ void copy_loop_dispatch(int active, v16f (&acc)[C::MI][C::NI], const Sources<C>& src,
                                                    const TileRsrc& tr, uint8_t MXFP4_LDS* lds, int nk, int wm0,
-                                                   int wn0, int lane) {
+                                                   int wn0, int lane, const Epi& epi) {
   if constexpr (MA == 0) {
     copy_loop<C, 0>(acc, src, tr, lds, nk, wm0, wn0, lane);
+    epi(acc);
   } else {
-    if (active >= MA)
+    if (active >= MA) {
       copy_loop<C, MA>(acc, src, tr, lds, nk, wm0, wn0, lane);
-    else
-      copy_loop_dispatch<C, MA - 1>(active, acc, src, tr, lds, nk, wm0, wn0, lane);
+      epi(acc);
+    } else {
+      copy_loop_dispatch<C, MA - 1>(active, acc, src, tr, lds, nk, wm0, wn0, lane, epi);
+    }
   }
 }
 
@@ -617,6 +681,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
   const TileBases tb = tile_bases<C>(args, b_q, b_s, ar, n0);
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
+  const auto epi = [&](v16f (&a)[C::MI][C::NI]) {
+    MXFP4_WAIT_VMCNT(0);
+    __syncthreads();   // every wave is done with the pipeline buffers
+    store_tile<C>(args, a, ar, n0, wm0, wn0, lane, lds);
+  };
   if (COPY) {
     // Row blocks of 32 that lie wholly past the tile's last stored row (the
     // tail of an expert's rows, or of a ragged M) need no MFMAs or operand
@@ -624,30 +693,30 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
     // still issues all copies and meets every barrier.
     const int active = __builtin_amdgcn_readfirstlane(min(max((ar.end - ar.lo - wm0 + 31) / 32, 0), C::MI));
     const TileRsrc tr = tile_rsrc<C>(tb, ar, n0, args.n, args.k);
-    copy_loop_dispatch<C, C::MI>(active, acc, src, tr, lds, args.k / kBK, wm0, wn0, lane);
+    copy_loop_dispatch<C, C::MI>(active, acc, src, tr, lds, args.k / C::SK, wm0, wn0, lane, epi);
   } else {
-    const int nk = (args.k + kBK - 1) / kBK;
+    const int nk = (args.k + C::SK - 1) / C::SK;
     for (int kt = 0; kt < nk; ++kt) {
       load_stage_generic<C>(lds, group0, src, tb, args.k, kt);
       __syncthreads();
       Scales<C> sc;
       Frags<C> f;
-      read_scales_raw<C>(group0, kt & 1, sc, wm0, wn0, lane);
+      read_scales_raw<C>(group0, kt & ((1 << C::SPG_SHIFT) - 1), sc, wm0, wn0, lane);
       shift_scales<C>(sc, lane);
       read_frags<C, 0>(lds, f, wm0, wn0, lane);
       mma_kstep<C, 0, 0, C::MI>(f, sc, acc);
       read_frags<C, 1>(lds, f, wm0, wn0, lane);
       mma_kstep<C, 1, 0, C::MI>(f, sc, acc);
-      read_frags<C, 2>(lds, f, wm0, wn0, lane);
-      mma_kstep<C, 2, 0, C::MI>(f, sc, acc);
-      read_frags<C, 3>(lds, f, wm0, wn0, lane);
-      mma_kstep<C, 3, 0, C::MI>(f, sc, acc);
+      if constexpr (C::KSTEPS == 4) {
+        read_frags<C, 2>(lds, f, wm0, wn0, lane);
+        mma_kstep<C, 2, 0, C::MI>(f, sc, acc);
+        read_frags<C, 3>(lds, f, wm0, wn0, lane);
+        mma_kstep<C, 3, 0, C::MI>(f, sc, acc);
+      }
       __syncthreads();
     }
+    epi(acc);
   }
-  MXFP4_WAIT_VMCNT(0);
-  __syncthreads();   // every wave is done with the pipeline buffers
-  store_tile<C>(args, acc, ar, n0, wm0, wn0, lane, lds);
 }
 
 template <class C, bool COPY>
@@ -761,7 +830,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
   int g;
   RowRange ar;
   if (!find_group(args.offsets, args.groups, args.m, C::BM, mt, g, ar)) return;
-  const int64_t kb = args.k / 2, ks = args.k / 32;
+  const int64_t kb = C::B8 ? args.k : args.k / 2, ks = args.k / 32;
   const uint8_t* b_q = args.b_q + (int64_t)g * args.n * kb;
   const uint8_t* b_s = args.b_s + (int64_t)g * args.n * ks;
   run_tile<C, COPY>(args, b_q, b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
@@ -770,6 +839,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
 using Cfg256 = TileCfg<256, 256, 2, 4>;
 using Cfg128 = TileCfg<128, 128, 2, 2>;
 using CfgW4A8 = TileCfg<128, 256, 2, 4, true>;
+// Both operands MXFP8: 128-K stages keep a stage at 64 KiB for 256 x 256
+// tiles.  An FP8 fragment is twice an FP4 one, so 8 waves of 128 x 64 would
+// need more than their 256 registers; 4 waves (one per SIMD) of 128 x 128
+// keep the 256 accumulators in the accumulator registers instead, and read
+// a third fewer LDS bytes per MFMA.
+using Cfg8x8_256 = TileCfg<256, 256, 2, 2, false, true>;
+using Cfg8x8_128 = TileCfg<128, 128, 2, 2, false, true>;
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel.
 template <class K>
@@ -783,7 +859,9 @@ bool use_copy_path(const GemmArgs& args) {
   return args.k % 512 == 0 && ((reinterpret_cast<uintptr_t>(args.a_s) | reinterpret_cast<uintptr_t>(args.b_s)) & 15) == 0;
 }
 
-template <class C>
+// GENERIC = false: the configuration has no register path (k % 512 != 0 or
+// unaligned scale arrays are refused with hipErrorInvalidValue).
+template <class C, bool GENERIC = true>
 hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (args.m + C::BM - 1) / C::BM;
   const int tiles_n = (args.n + C::BN - 1) / C::BN;
@@ -795,10 +873,12 @@ hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_tile_kernel<C, true>), grid, dim3(C::THREADS), lds, stream, args, tiles_m, tiles_n);
-  } else {
+  } else if constexpr (GENERIC) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, false>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_tile_kernel<C, false>), grid, dim3(C::THREADS), lds, stream, args, tiles_m, tiles_n);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -839,6 +919,12 @@ hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream) {
 
 hipError_t launch_grouped_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream) {
   return launch_grouped<CfgW4A8>(args, stream);
+}
+
+hipError_t launch_gemm_mxfp8_tile(const GemmArgs& args, TileKind kind, hipStream_t stream) {
+  // the 256 x 256 configuration has no register path: other k take 128 x 128 tiles
+  if (kind == kTile256 && use_copy_path(args)) return launch_dense<Cfg8x8_256, false>(args, stream);
+  return launch_dense<Cfg8x8_128>(args, stream);
 }
 
 }  // namespace mxfp4

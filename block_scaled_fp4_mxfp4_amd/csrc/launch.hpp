@@ -46,6 +46,11 @@ hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStre
 hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_grouped_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
 
+// MXFP8 x MXFP8 tile kernels (a_q and b_q are [rows, k] E4M3 codes): 256 x 256
+// or 128 x 128 output tiles over 128-K stages; a tile's operand rows span at
+// most 256 * k bytes, so k <= 2^23.
+hipError_t launch_gemm_mxfp8_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
+
 // Bandwidth path for m <= 128: 64- or 32-column tiles, K split over the 4 waves
 // of a workgroup and, when splits > 1, over `splits` workgroups per tile with
 // fp32 partials and per-tile arrival counters in `workspace`.

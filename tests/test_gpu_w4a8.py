@@ -4,15 +4,21 @@ Numerics of the hardware.  gfx950's scaled MFMA with an FP8 operand does not
 form an exact dot product: along K it sums products in aligned groups of 8
 (K [8g, 8g + 8)), first aligning them to the group's largest exponent sum
 (E4M3 exponent + E2M1 exponent, from the exponent fields) and truncating each
-toward zero to a multiple of 2**(E - 13); group sums then meet the fp32
+toward zero to a multiple of 2**(E - 13); within one 64-deep MFMA the group
+sums are aligned to the largest exponent sum E' of its products and rounded
+down to a multiple of 2**(E' - 24) (measured with both operands FP8,
+tests/test_gpu_mxfp8_gemm.py); the MFMA's sum then meets the fp32
 accumulator.  (Measured through this library with one big and one small
-element per row; test_w4a8_mfma_group_rule pins it.)  FP4 x FP4 never loses a
-bit under that rule, FP8 x FP4 can, so the FP4 GEMM's 1e-5 fp32 bar becomes a
-bound derived from the rule:
+element per row; test_w4a8_mfma_group_rule pins the group rule.)  FP4 x FP4
+never loses a bit under that rule, FP8 x FP4 can, so the FP4 GEMM's 1e-5 fp32
+bar becomes a bound derived from the rule:
     |C - C_exact| <= sum_g n_g * 2**(E_g - 13) * scale_a * scale_b
+                     + sum_t 8 * 2**(E'_t + S_t - 24)
                      + (k / 16) * 2**-24 * sum_k |a_k * b_k|
 with n_g the group's nonzero products and E_g taken over every element of
-the group (an upper bound whether or not the hardware skips zeros).
+the group (an upper bound whether or not the hardware skips zeros), E'_t over
+every element of 64-deep step t and S_t the step's largest sum of block
+scale exponents.
 
 Bars:
   * exact regime (no product can leave its group's grid and every partial sum
@@ -79,6 +85,11 @@ def w4a8_tolerance(aq, as_, bq, bs):
     sa = np.repeat(as_.astype(np.int64) - 127, 4, axis=1)        # scale exponent per group
     sb = np.repeat(bs.astype(np.int64) - 127, 4, axis=1)
     trunc = (cnt * np.ldexp(1.0, E - 13 + sa[:, None, :] + sb[None, :, :])).sum(-1)
+    cross = np.zeros((m, n))
+    for t in range((groups + 7) // 8):
+        g0, g1 = 8 * t, min(8 * t + 8, groups)
+        cross += 8 * np.ldexp(1.0, E[:, :, g0:g1].max(-1) + (sa[:, None, g0:g1] + sb[None, :, g0:g1]).max(-1) - 24)
+    trunc = trunc + cross
     a_abs = np.abs(oracle.dequantize_mxfp8(aq, as_))
     b_abs = np.abs(oracle.dequantize(bq, bs))
     acc = (k / 16) * 2.0 ** -24 * (a_abs @ b_abs.T)
