@@ -31,8 +31,9 @@ EXPORTED = (
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
     "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
-    "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex",
+    "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex", "mxfp4_gemm_nt_ex_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
 
 _lib = None
@@ -84,6 +85,9 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_gemm_nt_ex.restype = ctypes.c_int
         lib.mxfp4_gemm_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64,
                                          ctypes.c_int, i32, vp, sz, vp]
+        lib.mxfp4_gemm_nt_ex_noalloc.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64,
+                                                 ctypes.c_int, i32, vp]
         lib.mxfp4_prepacked_weight_size.restype = ctypes.c_int
         lib.mxfp4_prepacked_weight_size.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         lib.mxfp4_prepack_weight.restype = ctypes.c_int
@@ -236,6 +240,23 @@ def mxfp4_gemm_nt(a_q, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.mxfp4_gemm_nt_ex(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
                                 kid, splits, _ptr(ws), nbytes, _stream(stream)))
+    return c
+
+
+def mxfp4_gemm_nt_noalloc(a_q, a_s, b_q, b_s, c, kernel: str = "auto", splits: int = 0, stream=None):
+    """mxfp4_gemm_nt through the no-allocation entry point: the caller passes C
+    (bf16 or fp32); split-K scratch is the library's static device array."""
+    lib = load_library()
+    m, kh = a_q.shape
+    n = b_q.shape[0]
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (m, k // 2))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s, "b_s", torch.uint8, (n, k // 32))
+    c, code = _out(c, m, n, c.dtype, a_q.device)
+    _check(lib.mxfp4_gemm_nt_ex_noalloc(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
+                                        KERNELS[kernel], splits, _stream(stream)))
     return c
 
 

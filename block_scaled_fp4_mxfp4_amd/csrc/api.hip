@@ -223,10 +223,45 @@ size_t mxfp4_gemm_nt_workspace_size(int64_t m, int64_t n, int64_t k) {
   return mxfp4_gemm_nt_ex_workspace_size(m, n, k, MXFP4_KERNEL_AUTO, 0);
 }
 
-mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
-                                void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
-                                mxfp4_kernel_t kernel, int32_t splits, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The no-allocation variant's scratch: a file-scope device array (one copy on
+// each GPU the library runs on, held until the process ends).  Host code uses
+// only the per-device address hipGetSymbolAddress returns for it, never the
+// array's name.
+constexpr size_t kNoAllocScratchBytes = MXFP4_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current.
+mxfp4_status_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MXFP4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MXFP4_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MXFP4_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MXFP4_OK;
+}
+
+// mxfp4_gemm_nt_ex's body; with `noalloc`, the workspace is the library's
+// scratch array (workspace arguments ignored).
+mxfp4_status_t gemm_nt_ex_impl(const void* a_q, const void* a_s, const void* b_q, const void* b_s, void* c,
+                               mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel,
+                               int32_t splits, void* workspace, size_t workspace_bytes, void* stream,
+                               bool noalloc) {
   MXFP4_TRY(check_gemm_args(a_q, a_s, b_q, b_s, c, c_type, m, n, k));
   if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_STREAM)
     return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
@@ -237,7 +272,20 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_
   Choice ch;
   MXFP4_TRY(resolve(m, n, k, kernel, splits, dev.num_cus, stream_ok, ch));
   const size_t need = workspace_for(ch, m, n, k);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes)
+      return fail(MXFP4_ERR_WORKSPACE, "the no-allocation entry point's scratch holds %zu bytes; this call needs %zu",
+                  kNoAllocScratchBytes, need);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      MXFP4_TRY(device_scratch(&workspace));
+      workspace_bytes = kNoAllocScratchBytes;
+      // the array keeps the last call's contents: zero the arrival counters first
+      MXFP4_TRY(hip_status(mxfp4::launch_splitk_clear_counters(workspace, (hipStream_t)stream),
+                           "scratch counter clear launch"));
+    }
+  } else if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(MXFP4_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -262,6 +310,24 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_
     default: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile256, (hipStream_t)stream); break;
   }
   return hip_status(e, "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
+                                void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                mxfp4_kernel_t kernel, int32_t splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return gemm_nt_ex_impl(a_q, a_s, b_q, b_s, c, c_type, m, n, k, kernel, splits, workspace, workspace_bytes,
+                         stream, false);
+}
+
+mxfp4_status_t mxfp4_gemm_nt_ex_noalloc(const void* a_q, const void* a_s, const void* b_q, const void* b_s,
+                                        void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                        mxfp4_kernel_t kernel, int32_t splits, void* stream) {
+  return gemm_nt_ex_impl(a_q, a_s, b_q, b_s, c, c_type, m, n, k, kernel, splits, nullptr, 0, stream, true);
 }
 
 mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, void* c,

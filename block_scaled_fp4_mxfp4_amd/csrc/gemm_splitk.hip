@@ -308,6 +308,19 @@ int nblocks_for(int n, int num_cus) { return (n + 63) / 64 >= (num_cus * 3) / 4 
 
 }  // namespace
 
+namespace {
+__global__ __launch_bounds__(kThreads) void clear_counters_kernel(int* counters, int n) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) counters[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_splitk_clear_counters(void* workspace, hipStream_t stream) {
+  const int n = splitk_max_tiles();
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
+                     (int*)workspace, n);
+  return hipGetLastError();
+}
+
 size_t splitk_workspace_bytes(int m, int n, int k, int splits) {
   (void)k;
   if (splits <= 1) return 0;

@@ -59,6 +59,9 @@ int splitk_max_tiles();   // largest ceil(n / 64) that splits > 1 supports
 int splitk_auto_splits(int m, int n, int k, int num_cus);
 hipError_t launch_gemm_splitk(const GemmArgs& args, int splits, void* workspace,
                               hipStream_t stream, int num_cus);
+// Zeroes the per-tile arrival counters at the start of a split-K workspace
+// (every launch with splits > 1 leaves them at zero again).
+hipError_t launch_splitk_clear_counters(void* workspace, hipStream_t stream);
 
 // Small-M weight-streaming kernel: 64-column tiles over the whole K with the
 // 4 waves of a workgroup splitting each 256-K stage by k-step; needs

@@ -271,6 +271,33 @@ mxfp4_status_t mxfp4_gemm_nt_ex(const void* a_q, const void* a_s,
                                 mxfp4_kernel_t kernel, int32_t splits,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mxfp4_gemm_nt_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results as mxfp4_gemm_nt_ex (bit for bit), with
+ * no workspace argument: the split-K partial sums and arrival counters
+ * (MXFP4_KERNEL_SPLITK with splits > 1, the only choice that needs a
+ * workspace) live in a library-owned static device array of
+ * MXFP4_NOALLOC_SCRATCH_BYTES bytes, one on each GPU the library runs on,
+ * held until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); on its first call on a device it
+ * looks up that device's copy of the array (with the device current) and
+ * keeps the address.  A call whose workspace
+ * (mxfp4_gemm_nt_ex_workspace_size) exceeds the array returns
+ * MXFP4_ERR_WORKSPACE and launches nothing.  The array keeps the last call's
+ * contents; each split-K call first zeroes the counters with a small kernel
+ * on `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams, or from several threads)
+ * race on it and must be serialized by the caller.
+ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+mxfp4_status_t mxfp4_gemm_nt_ex_noalloc(const void* a_q, const void* a_s,
+                                        const void* b_q, const void* b_s,
+                                        void* c, mxfp4_out_t c_type,
+                                        int64_t m, int64_t n, int64_t k,
+                                        mxfp4_kernel_t kernel, int32_t splits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
