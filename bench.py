@@ -872,6 +872,91 @@ def measure_mxfp8(args, dev, w):
     return out
 
 
+class FusedDecodeBench:
+    """Decode from the activation's producer (the quantization fused into the
+    producer): RMSNorm of a [128, 4096] hidden state before the 14336 x 4096
+    up projection, and SwiGLU of a [128, 2 x 14336] gate|up buffer before the
+    4096 x 14336 down projection, each followed by the GEMM on prepacked
+    operands against its weight (quantized and prepacked once).  Two forms of
+    each step:
+      fused:      producer writing the prepacked layout, GEMM (2 launches);
+      two_launch: producer writing BF16 (and row-major MXFP4), the prepacked
+                  quantizer on the BF16 output, GEMM (3 launches)."""
+
+    def __init__(self, dev):
+        from block_scaled_fp4_mxfp4_amd import binding as B
+        self.B = B
+        self.m, self.hidden, self.inter = 128, 4096, 14336
+        m, h, f = self.m, self.hidden, self.inter
+        x = workloads.activation_bf16(m, h, 800, outliers=True).to(dev)
+        gamma = workloads.gaussian_bf16((h,), 0.1, 801).to(dev)
+        gu = workloads.gaussian_bf16((m, 2 * f), 1.0, 802).to(dev)
+        w_up = workloads.gaussian_bf16((f, h), 0.02, 803).to(dev)
+        w_dn = workloads.gaussian_bf16((h, f), 0.02, 804).to(dev)
+        up_p = B.mxfp4_prepack_weight(*B.mxfp4_quantize(w_up))
+        dn_p = B.mxfp4_prepack_weight(*B.mxfp4_quantize(w_dn))
+        del w_up, w_dn
+        per_set = sum(t.numel() for t in (*up_p, *dn_p)) + m * (h + 2 * f) * 2
+        self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
+        self.sets = []
+        for _ in range(self.sets_n):
+            st = dict(x=x.clone(), gamma=gamma.clone(), gu=gu.clone(), up=[t.clone() for t in up_p],
+                      dn=[t.clone() for t in dn_p], y=torch.empty((m, h), dtype=torch.bfloat16, device=dev),
+                      yd=torch.empty((m, f), dtype=torch.bfloat16, device=dev),
+                      q=torch.empty((m, h // 2), dtype=torch.uint8, device=dev),
+                      s=torch.empty((m, h // 32), dtype=torch.uint8, device=dev),
+                      qd=torch.empty((m, f // 2), dtype=torch.uint8, device=dev),
+                      sd=torch.empty((m, f // 32), dtype=torch.uint8, device=dev),
+                      c_up=torch.empty((m, f), dtype=torch.bfloat16, device=dev),
+                      c_dn=torch.empty((m, h), dtype=torch.bfloat16, device=dev))
+            st["ap"] = [torch.empty(n_, dtype=torch.uint8, device=dev) for n_ in B.mxfp4_prepacked_weight_size(m, h)]
+            st["apd"] = [torch.empty(n_, dtype=torch.uint8, device=dev) for n_ in B.mxfp4_prepacked_weight_size(m, f)]
+            self.sets.append(st)
+        del x, gamma, gu, up_p, dn_p
+        torch.cuda.synchronize()
+
+    def up_fused(self, i):
+        s, B = self.sets[i % self.sets_n], self.B
+        B.mxfp4_rmsnorm_quantize(s["x"], s["gamma"], 1e-5, q=s["ap"][0], scales=s["ap"][1], prepacked=True)
+        B.mxfp4_gemm_nt_prepacked_ab(*s["ap"], *s["up"], self.m, self.inter, self.hidden, c=s["c_up"])
+
+    def up_two_launch(self, i):
+        s, B = self.sets[i % self.sets_n], self.B
+        B.mxfp4_rmsnorm_quantize(s["x"], s["gamma"], 1e-5, y=s["y"], q=s["q"], scales=s["s"])
+        B.mxfp4_quantize_prepacked(s["y"], *s["ap"])
+        B.mxfp4_gemm_nt_prepacked_ab(*s["ap"], *s["up"], self.m, self.inter, self.hidden, c=s["c_up"])
+
+    def down_fused(self, i):
+        s, B, f = self.sets[i % self.sets_n], self.B, self.inter
+        B.mxfp4_swiglu_quantize(s["gu"][:, :f], s["gu"][:, f:], q=s["apd"][0], scales=s["apd"][1], prepacked=True)
+        B.mxfp4_gemm_nt_prepacked_ab(*s["apd"], *s["dn"], self.m, self.hidden, f, c=s["c_dn"])
+
+    def down_two_launch(self, i):
+        s, B, f = self.sets[i % self.sets_n], self.B, self.inter
+        B.mxfp4_swiglu_quantize(s["gu"][:, :f], s["gu"][:, f:], y=s["yd"], q=s["qd"], scales=s["sd"])
+        B.mxfp4_quantize_prepacked(s["yd"], *s["apd"])
+        B.mxfp4_gemm_nt_prepacked_ab(*s["apd"], *s["dn"], self.m, self.hidden, f, c=s["c_dn"])
+
+    _graph = staticmethod(DenseBench._graph)
+    timed = DenseBench.timed
+
+
+def measure_fused_decode(args, dev):
+    eprint("[bench] decode steps from the producer: quantization fused into RMSNorm / SwiGLU vs a separate launch")
+    fb = FusedDecodeBench(dev)
+    steps = max(64, args.steps)
+    out = {"rotating_input_sets": fb.sets_n, "steps": steps}
+    for name, shape in (("up", "RMSNorm 128x4096 -> GEMM 128x14336x4096"),
+                        ("down", "SwiGLU 128x14336 (gate|up 128x28672) -> GEMM 128x4096x14336")):
+        fused = fb.timed(getattr(fb, f"{name}_fused"), steps, 8)
+        two = fb.timed(getattr(fb, f"{name}_two_launch"), steps, 8)
+        out[name] = {"shape": shape, "fused_us": us(fused), "two_launch_us": us(two),
+                     "saving_frac": round(1.0 - fused["mean"] / two["mean"], 4)}
+        eprint(f"[bench] {name}: fused {fused['mean']*1e3:.2f} us, two-launch {two['mean']*1e3:.2f} us")
+    del fb
+    return out
+
+
 def run_only(args, dev):
     """Eager launches for profiling runs."""
     if args.only == "copy":
@@ -1081,6 +1166,7 @@ def main():
 
     if not args.no_producers:
         result["producers"] = measure_producers(args, dev, us)
+        result["fused_decode"] = measure_fused_decode(args, dev)
 
     if not args.no_w4a8:
         result["w4a8"] = measure_w4a8(args, dev, w, us)

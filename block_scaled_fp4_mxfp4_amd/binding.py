@@ -32,6 +32,7 @@ EXPORTED = (
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
     "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
     "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex", "mxfp4_gemm_nt_ex_noalloc",
+    "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -122,6 +123,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_rmsnorm_quantize.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
         lib.mxfp4_swiglu_quantize.restype = ctypes.c_int
         lib.mxfp4_swiglu_quantize.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
+        lib.mxfp4_rmsnorm_quantize_prepacked.restype = ctypes.c_int
+        lib.mxfp4_rmsnorm_quantize_prepacked.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
+        lib.mxfp4_swiglu_quantize_prepacked.restype = ctypes.c_int
+        lib.mxfp4_swiglu_quantize_prepacked.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.nvfp4_quantize.restype = ctypes.c_int
         lib.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         lib.nvfp4_gemm_nt.restype = ctypes.c_int
@@ -520,31 +525,45 @@ def mxfp4_moe_combine(y, token_rows, weights, out=None, out_dtype=torch.bfloat16
 # Fused producers (include/mxfp4_producers.h)
 # ---------------------------------------------------------------------------
 
+def _mxfp4_out(q, scales, rows, k, device, prepacked):
+    """Codes and scales of a [rows, k] MXFP4 output: row-major, or the prepacked layout's flat buffers."""
+    if prepacked:
+        cb, sb = mxfp4_prepacked_weight_size(rows, k)
+        qs, ss = (cb,), (sb,)
+    else:
+        qs, ss = (rows, k // 2), (rows, k // 32)
+    if q is None:
+        q = torch.empty(qs, dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty(ss, dtype=torch.uint8, device=device)
+    _require(q, "q", torch.uint8, qs)
+    _require(scales, "scales", torch.uint8, ss)
+    return q, scales
+
+
 def mxfp4_rmsnorm_quantize(x, gamma, eps: float, residual=None, residual_out=None, y=None, q=None, scales=None,
-                           stream=None):
-    """(x [+ residual]) -> RMSNorm(., gamma, eps) -> MXFP4 (q [rows, k/2], scales [rows, k/32]).
+                           stream=None, prepacked: bool = False):
+    """(x [+ residual]) -> RMSNorm(., gamma, eps) -> MXFP4 (q [rows, k/2], scales [rows, k/32], or with
+    prepacked=True the prepacked operand layout of the decode GEMM).
     residual_out (optional) receives x + residual; y (optional) the BF16 RMSNorm output."""
     lib = load_library()
     rows, k = x.shape
-    if q is None:
-        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    q, scales = _mxfp4_out(q, scales, rows, k, x.device, prepacked)
     _require(x, "x", torch.bfloat16, (rows, k))
     _require(gamma, "gamma", torch.bfloat16, (k,))
     for t, name in ((residual, "residual"), (residual_out, "residual_out"), (y, "y")):
         if t is not None:
             _require(t, name, torch.bfloat16, (rows, k))
-    _require(q, "q", torch.uint8, (rows, k // 2))
-    _require(scales, "scales", torch.uint8, (rows, k // 32))
-    _check(lib.mxfp4_rmsnorm_quantize(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), rows, k, _ptr(residual_out),
-                                      _ptr(y), _ptr(q), _ptr(scales), _stream(stream)))
+    fn = lib.mxfp4_rmsnorm_quantize_prepacked if prepacked else lib.mxfp4_rmsnorm_quantize
+    _check(fn(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), rows, k, _ptr(residual_out), _ptr(y), _ptr(q),
+              _ptr(scales), _stream(stream)))
     return q, scales
 
 
-def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None):
-    """silu(gate) * up -> MXFP4.  gate and up are [rows, k] views sharing one row stride (for example the two
-    halves of a [rows, 2k] projection output); y (optional) receives the BF16 activation."""
+def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None, prepacked: bool = False):
+    """silu(gate) * up -> MXFP4 (row-major, or with prepacked=True the prepacked operand layout).  gate and up
+    are [rows, k] views sharing one row stride (for example the two halves of a [rows, 2k] projection output);
+    y (optional) receives the BF16 activation."""
     lib = load_library()
     rows, k = gate.shape
     if tuple(up.shape) != (rows, k) or gate.stride() != up.stride() or gate.stride(1) != 1:
@@ -552,16 +571,11 @@ def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None):
     if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16 or not gate.is_cuda or not up.is_cuda:
         raise TypeError("gate and up must be bfloat16 device tensors")
     ld = gate.stride(0) if rows > 1 else k
-    if q is None:
-        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=gate.device)
-    if scales is None:
-        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=gate.device)
+    q, scales = _mxfp4_out(q, scales, rows, k, gate.device, prepacked)
     if y is not None:
         _require(y, "y", torch.bfloat16, (rows, k))
-    _require(q, "q", torch.uint8, (rows, k // 2))
-    _require(scales, "scales", torch.uint8, (rows, k // 32))
-    _check(lib.mxfp4_swiglu_quantize(_ptr(gate), _ptr(up), ld, rows, k, _ptr(y), _ptr(q), _ptr(scales),
-                                     _stream(stream)))
+    fn = lib.mxfp4_swiglu_quantize_prepacked if prepacked else lib.mxfp4_swiglu_quantize
+    _check(fn(_ptr(gate), _ptr(up), ld, rows, k, _ptr(y), _ptr(q), _ptr(scales), _stream(stream)))
     return q, scales
 
 

@@ -94,6 +94,20 @@ __device__ __forceinline__ v16f mfma32_fp8(v8i a, v8i b, v16f acc, int sa, int s
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, kMfmaFmtFp8, kMfmaFmtFp8, OPSEL, sa, OPSEL, sb);
 }
 
+// The prepacked operand layout (include/mxfp4.h, mxfp4_prepacked_weight_size):
+// for 32-element block kb of row r of an operand with `pairs` 512-K pairs per
+// row, the index of its first 4-byte code word (its four words are
+// consecutive) and of its scale byte.
+__device__ __forceinline__ void prepacked_index(int64_t r, int kb, int pairs, int64_t& word, int64_t& sbyte) {
+  const int64_t panel = r / 64;
+  const int rr = (int)(r - panel * 64);
+  const int j = rr >> 5, t = kb >> 4, s = (kb >> 3) & 1, w = (kb >> 1) & 3;
+  const int l = (rr & 31) + 32 * (kb & 1);
+  const int64_t blk = panel * pairs + t;
+  word = (blk * 16384 + w * 4096 + (2 * s + j) * 1024 + l * 16) / 4;
+  sbyte = blk * 1024 + w * 256 + l * 4 + 2 * s + j;
+}
+
 // Tile index -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
 // the 8 XCDs of MI355X, each XCD with a private L2.  When the tile count is a
 // multiple of 8, consecutive logical tiles are placed on one XCD; logical tiles

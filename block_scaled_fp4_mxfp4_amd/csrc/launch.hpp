@@ -96,10 +96,12 @@ hipError_t launch_moe_combine(const void* y, int total_rows, int n, const int32_
 
 // Fused producers emitting MXFP4 activations (include/mxfp4_producers.h).
 constexpr int kNormMaxSlots = 16;   // RMSNorm rows: k <= 256 threads * 8 elements * 16 = 32768
+// prepacked: codes and scales in the prepacked operand layout (k % 512 == 0)
 hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
-                                   void* h_out, void* y_out, void* q, void* scales, hipStream_t stream);
+                                   void* h_out, void* y_out, void* q, void* scales, bool prepacked,
+                                   hipStream_t stream);
 hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
-                                  void* scales, hipStream_t stream, int num_cus);
+                                  void* scales, bool prepacked, hipStream_t stream, int num_cus);
 
 // NVFP4 (include/nvfp4.h): quantization (k <= 32768, one workgroup per row) and
 // the dequantizing NT GEMM on the BF16 MFMA (k % 64 == 0).

@@ -25,6 +25,12 @@
 // Both quantize y exactly as the MXFP4 quantizer does (4 lanes per 32-element
 // block, integer amax, scale byte max(E - 2, 0), the CDNA4 scaled FP4 convert)
 // and can also store y itself.  HBM-bound.
+//
+// PREPACKED: the same code and scale bytes stored in the prepacked operand
+// layout of the decode GEMM (include/mxfp4.h), so the activation's producer
+// hands the small-M GEMM its operand with no quantization launch in between
+// (rows up to the next multiple of 64 are written as zero blocks, as the
+// prepacked quantizer writes them).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -94,14 +100,24 @@ __device__ __forceinline__ double sumsq_bf16x2(uint32_t w, double acc) {
   return fma(hi, hi, fma(lo, lo, acc));
 }
 
-template <bool HAS_RES, int SLOTS>
+template <bool HAS_RES, int SLOTS, bool PREPACKED>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
     // x, res, h_out and y_out may share memory (in-place residual and output): no __restrict__ on them
-    const uint4* x, const uint4* res, const uint4* __restrict__ gamma, float eps, int k,
+    const uint4* x, const uint4* res, const uint4* __restrict__ gamma, float eps, int rows, int k,
     uint4* h_out, uint4* y_out, uint32_t* __restrict__ q, uint8_t* __restrict__ scales) {
   __shared__ double red[kNormThreads / 64];
   const int chunks = k >> 3;                         // 8 elements (one uint4) per chunk
   const int64_t rbase = (int64_t)blockIdx.x * chunks;
+  if (PREPACKED && (int)blockIdx.x >= rows) {
+    // a padding row of the last 64-row panel: zero codes and scale bytes
+    for (int c = threadIdx.x; c < chunks; c += kNormThreads) {
+      int64_t word, sidx;
+      prepacked_index(blockIdx.x, c >> 2, k / 512, word, sidx);
+      q[word + (c & 3)] = 0u;
+      if ((c & 3) == 0) scales[sidx] = 0;
+    }
+    return;
+  }
   uint4 h[SLOTS], gm[SLOTS];
   double ss = 0.0;
 #pragma unroll
@@ -154,8 +170,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
     if (y_out) y_out[rbase + c] = y;
     uint32_t sbyte;
     const uint32_t codes = quantize8(y, sbyte);
-    q[rbase + c] = codes;
-    if ((threadIdx.x & 3) == 0) scales[(rbase + c) >> 2] = (uint8_t)sbyte;
+    if (PREPACKED) {
+      int64_t word, sidx;
+      prepacked_index(blockIdx.x, c >> 2, k / 512, word, sidx);
+      q[word + (threadIdx.x & 3)] = codes;
+      if ((threadIdx.x & 3) == 0) scales[sidx] = (uint8_t)sbyte;
+    } else {
+      q[rbase + c] = codes;
+      if ((threadIdx.x & 3) == 0) scales[(rbase + c) >> 2] = (uint8_t)sbyte;
+    }
   }
 }
 
@@ -174,9 +197,12 @@ __device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t g, uint32_t u) {
   return pack_bf16x2(silu_mul(bf16_lo(g), bf16_lo(u)), silu_mul(bf16_hi(g), bf16_hi(u)));
 }
 
+// nblocks counts the 32-blocks of `rows` rows, or with PREPACKED of the rows
+// rounded up to 64 (blocks of padding rows are written as zero blocks).
+template <bool PREPACKED>
 __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
-    const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int64_t ld, int kblocks, int nblocks,
-    uint4* __restrict__ y_out, uint32_t* __restrict__ q, uint8_t* __restrict__ scales) {
+    const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int64_t ld, int rows, int kblocks,
+    int nblocks, uint4* __restrict__ y_out, uint32_t* __restrict__ q, uint8_t* __restrict__ scales) {
   const int lane4 = threadIdx.x & 3;
   const int groups_per_grid = gridDim.x * (kProdThreads / 4);
   for (int blk = blockIdx.x * (kProdThreads / 4) + (threadIdx.x >> 2); blk < nblocks;
@@ -185,7 +211,8 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
 #pragma unroll
     for (int u = 0; u < kProdUnroll; ++u) {
       int b = blk + u * groups_per_grid;
-      b = b < nblocks ? b : 0;   // out-of-range groups load block 0 and store nothing
+      // out-of-range groups, and the padding rows of a prepacked output, load block 0
+      b = (b < nblocks && b / kblocks < rows) ? b : 0;
       const int row = b / kblocks, kb = b - row * kblocks;
       const int64_t off = (int64_t)row * ld + kb * 32 + lane4 * 8;
       // gate and up are read once: non-temporal (same-box A/B on 4096 x 14336: 48.6-49.2 vs 54.4-55.0 us;
@@ -201,11 +228,25 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
       const uint4 y = make_uint4(swiglu_bf16x2(gv[u].x, uv[u].x), swiglu_bf16x2(gv[u].y, uv[u].y),
                                  swiglu_bf16x2(gv[u].z, uv[u].z), swiglu_bf16x2(gv[u].w, uv[u].w));
       uint32_t sbyte;
-      const uint32_t codes = quantize8(y, sbyte);
+      uint32_t codes = quantize8(y, sbyte);
       if (b < nblocks) {
-        if (y_out) y_out[(int64_t)b * 4 + lane4] = y;
-        q[(int64_t)b * 4 + lane4] = codes;
-        if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+        const int row = b / kblocks;
+        if (PREPACKED) {
+          if (row >= rows) {   // padding row: a zero block
+            codes = 0u;
+            sbyte = 0u;
+          } else if (y_out) {
+            y_out[(int64_t)b * 4 + lane4] = y;
+          }
+          int64_t word, sidx;
+          prepacked_index(row, b - row * kblocks, kblocks / 16, word, sidx);
+          q[word + lane4] = codes;
+          if (lane4 == 0) scales[sidx] = (uint8_t)sbyte;
+        } else {
+          if (y_out) y_out[(int64_t)b * 4 + lane4] = y;
+          q[(int64_t)b * 4 + lane4] = codes;
+          if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+        }
       }
     }
   }
@@ -213,46 +254,68 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
 
 }  // namespace
 
-template <int SLOTS>
+template <int SLOTS, bool PREPACKED>
 void launch_rmsnorm_slots(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
                           void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
+  // prepacked: one more workgroup per padding row of the last 64-row panel
+  const unsigned grid = PREPACKED ? (unsigned)((rows + 63) / 64 * 64) : (unsigned)rows;
   if (residual)
-    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, SLOTS>), dim3((unsigned)rows), dim3(kNormThreads), 0, stream,
-                       (const uint4*)x, (const uint4*)residual, (const uint4*)gamma, eps, k, (uint4*)h_out,
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, SLOTS, PREPACKED>), dim3(grid), dim3(kNormThreads), 0, stream,
+                       (const uint4*)x, (const uint4*)residual, (const uint4*)gamma, eps, rows, k, (uint4*)h_out,
                        (uint4*)y_out, (uint32_t*)q, (uint8_t*)scales);
   else
-    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, SLOTS>), dim3((unsigned)rows), dim3(kNormThreads), 0, stream,
-                       (const uint4*)x, (const uint4*)nullptr, (const uint4*)gamma, eps, k, (uint4*)nullptr,
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, SLOTS, PREPACKED>), dim3(grid), dim3(kNormThreads), 0, stream,
+                       (const uint4*)x, (const uint4*)nullptr, (const uint4*)gamma, eps, rows, k, (uint4*)nullptr,
                        (uint4*)y_out, (uint32_t*)q, (uint8_t*)scales);
+}
+
+template <bool PREPACKED>
+void launch_rmsnorm(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
+                    void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
+  if (k <= 2 * 8 * kNormThreads)
+    launch_rmsnorm_slots<2, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  else if (k <= 4 * 8 * kNormThreads)
+    launch_rmsnorm_slots<4, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  else
+    launch_rmsnorm_slots<kNormMaxSlots, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales,
+                                                   stream);
 }
 
 // Rows stay in registers: 2, 4 or 16 chunks of 8 elements per thread (k up
 // to 4096, 8192 or 32768), so the common widths keep the register count, and
 // with it the rows in flight per CU, low.
 hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
-                                   void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
-  if (!grid_fits(rows, kNormThreads)) return hipErrorInvalidConfiguration;
-  if (k <= 2 * 8 * kNormThreads)
-    launch_rmsnorm_slots<2>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
-  else if (k <= 4 * 8 * kNormThreads)
-    launch_rmsnorm_slots<4>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
-  else
-    launch_rmsnorm_slots<kNormMaxSlots>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+                                   void* h_out, void* y_out, void* q, void* scales, bool prepacked,
+                                   hipStream_t stream) {
+  if (!grid_fits((int64_t)(rows + 63) / 64 * 64, kNormThreads)) return hipErrorInvalidConfiguration;
+  if (prepacked) {
+    if (k % 512) return hipErrorInvalidValue;
+    launch_rmsnorm<true>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  } else {
+    launch_rmsnorm<false>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
-                                  void* scales, hipStream_t stream, int num_cus) {
+                                  void* scales, bool prepacked, hipStream_t stream, int num_cus) {
+  if (prepacked && k % 512) return hipErrorInvalidValue;
   const int kblocks = k / 32;
-  const int nblocks = rows * kblocks;   // the host keeps this at most 2^30
+  // the host keeps this at most 2^30 (prepacked: rows rounded up to 64)
+  const int nblocks = (prepacked ? (rows + 63) / 64 * 64 : rows) * kblocks;
   const int64_t groups_needed = ((int64_t)nblocks + kProdUnroll - 1) / kProdUnroll;
   int64_t grid = (groups_needed + (kProdThreads / 4) - 1) / (kProdThreads / 4);
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(swiglu_quantize_kernel, dim3((unsigned)grid), dim3(kProdThreads), 0, stream,
-                     (const uint16_t*)gate, (const uint16_t*)up, ld, kblocks, nblocks, (uint4*)y_out, (uint32_t*)q,
-                     (uint8_t*)scales);
+  if (prepacked)
+    hipLaunchKernelGGL(swiglu_quantize_kernel<true>, dim3((unsigned)grid), dim3(kProdThreads), 0, stream,
+                       (const uint16_t*)gate, (const uint16_t*)up, ld, rows, kblocks, nblocks, (uint4*)y_out,
+                       (uint32_t*)q, (uint8_t*)scales);
+  else
+    hipLaunchKernelGGL(swiglu_quantize_kernel<false>, dim3((unsigned)grid), dim3(kProdThreads), 0, stream,
+                       (const uint16_t*)gate, (const uint16_t*)up, ld, rows, kblocks, nblocks, (uint4*)y_out,
+                       (uint32_t*)q, (uint8_t*)scales);
   return hipGetLastError();
 }
 

@@ -132,13 +132,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_prepacked_kernel(
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v.w), scale, 3);
-    const int64_t panel = r / 64;
-    const int rr = (int)(r - panel * 64);
-    const int j = rr >> 5, t = kb >> 4, s = (kb >> 3) & 1, w = (kb >> 1) & 3;
-    const int l = (rr & 31) + 32 * (kb & 1);
-    const int64_t blk = panel * pairs + t;
-    q[(blk * 16384 + w * 4096 + (2 * s + j) * 1024 + l * 16) / 4 + lane4] = packed;
-    if (lane4 == 0) scales[blk * 1024 + w * 256 + l * 4 + 2 * s + j] = (uint8_t)sbyte;
+    int64_t word, sidx;
+    prepacked_index(r, kb, pairs, word, sidx);
+    q[word + lane4] = packed;
+    if (lane4 == 0) scales[sidx] = (uint8_t)sbyte;
   }
 }
 

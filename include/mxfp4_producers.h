@@ -72,6 +72,31 @@ mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_b
 mxfp4_status_t mxfp4_swiglu_quantize(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
                                      int64_t k, void* y_bf16, void* q, void* scales, void* stream);
 
+/*
+ * The two producers with their MXFP4 output stored in the prepacked operand
+ * layout of mxfp4_gemm_nt_prepacked_ab (include/mxfp4.h, the layout of
+ * mxfp4_prepack_weight applied to [rows, k]): the quantization fused into the
+ * activation's producer, so the small-M (decode) GEMM on prepacked operands
+ * follows the producer with no quantization launch in between (the quadbit
+ * README, "The stack": producers that quantize in place; the "Packed MXFP4 &
+ * NVFP4 GEMM + mega-MoE" page, Summary: the decode GEMM's activation
+ * operand).  The code and scale bytes are those of mxfp4_rmsnorm_quantize /
+ * mxfp4_swiglu_quantize, byte for byte, at the positions the layout gives
+ * them; rows from `rows` up to the next multiple of 64 are written as zero
+ * blocks (code 0, scale byte 0), as mxfp4_quantize_prepacked writes them.
+ *   ap_q, ap_s : device buffers of the sizes mxfp4_prepacked_weight_size(rows,
+ *                k) gives (ap_q 16-byte aligned);
+ *   k          : a positive multiple of 512 (MXFP4_ERR_INVALID_ARG otherwise).
+ * Every other argument, limit and result as for the row-major producers above.
+ */
+mxfp4_status_t mxfp4_rmsnorm_quantize_prepacked(const void* x_bf16, const void* residual_bf16,
+                                                const void* gamma_bf16, float eps, int64_t rows, int64_t k,
+                                                void* residual_out_bf16, void* y_bf16, void* ap_q, void* ap_s,
+                                                void* stream);
+
+mxfp4_status_t mxfp4_swiglu_quantize_prepacked(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
+                                               int64_t k, void* y_bf16, void* ap_q, void* ap_s, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,9 @@ import torch
 
 import oracle
 import workloads
-from block_scaled_fp4_mxfp4_amd import mxfp4_rmsnorm_quantize, mxfp4_swiglu_quantize
+from block_scaled_fp4_mxfp4_amd import (mxfp4_gemm_nt_prepacked_ab, mxfp4_prepack_weight, mxfp4_prepacked_weight_size,
+                                        mxfp4_quantize, mxfp4_quantize_prepacked, mxfp4_rmsnorm_quantize,
+                                        mxfp4_swiglu_quantize)
 from tests.gpu_common import device, log, poisoned, random_bf16, sampled_indices, to_np
 
 pytestmark = pytest.mark.gpu
@@ -164,3 +166,82 @@ def test_swiglu_ffn_full_size_sampled():
     _assert_nearest_or_midpoint(yb, y64, _silu_window(gu[idx, :k]))
     rq, rs = oracle.quantize(yb)
     assert np.array_equal(to_np(q)[idx], rq) and np.array_equal(to_np(s)[idx], rs)
+
+
+# ---------------------------------------------------------------------------
+# producers writing the prepacked operand layout of the decode GEMM
+
+PREPACKED_CASES = [(1, 512), (64, 1024), (100, 4096), (128, 4096), (130, 2048)]
+
+
+@pytest.mark.parametrize("rows,k", PREPACKED_CASES)
+def test_rmsnorm_quantize_prepacked_is_the_layout_of_the_row_major_bytes(rows, k):
+    """The prepacked producer's buffers equal the prepacked layout (built on the
+    host from its definition) of the row-major producer's codes and scales, bit
+    for bit, padding rows as zero blocks; the BF16 outputs are the same."""
+    from tests.prepack_layout import prepack_numpy
+    dev = device()
+    log(f"rmsnorm prepacked rows={rows} k={k}")
+    x = random_bf16((rows, k), 40 + k, spread=5, outlier_frac=0.01)
+    res = random_bf16((rows, k), 41 + k, spread=5)
+    gamma = (1.0 + 0.2 * torch.randn(k, generator=torch.Generator().manual_seed(k))).to(torch.bfloat16)
+    xd, rd, gd = x.to(dev), res.to(dev), gamma.to(dev)
+    h1, y1 = (torch.empty((rows, k), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    h2, y2 = (torch.empty((rows, k), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    q, s = mxfp4_rmsnorm_quantize(xd, gd, 1e-5, residual=rd, residual_out=h1, y=y1)
+    cb, sb = mxfp4_prepacked_weight_size(rows, k)
+    pq, ps = poisoned((cb,), torch.uint8, dev, 0x77), poisoned((sb,), torch.uint8, dev, 0x77)
+    mxfp4_rmsnorm_quantize(xd, gd, 1e-5, residual=rd, residual_out=h2, y=y2, q=pq, scales=ps, prepacked=True)
+    torch.cuda.synchronize()
+    wq, ws = prepack_numpy(to_np(q), to_np(s))
+    assert np.array_equal(to_np(pq), wq) and np.array_equal(to_np(ps), ws)
+    assert torch.equal(h1, h2) and torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("rows,k", PREPACKED_CASES)
+def test_swiglu_quantize_prepacked_is_the_layout_of_the_row_major_bytes(rows, k):
+    from tests.prepack_layout import prepack_numpy
+    dev = device()
+    log(f"swiglu prepacked rows={rows} k={k}")
+    gate, up, _, _ = _gate_up(rows, k, 2 * k, rows * 3 + k, dev)
+    y1 = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+    q, s = mxfp4_swiglu_quantize(gate, up, y=y1)
+    cb, sb = mxfp4_prepacked_weight_size(rows, k)
+    pq, ps = poisoned((cb,), torch.uint8, dev, 0x77), poisoned((sb,), torch.uint8, dev, 0x77)
+    mxfp4_swiglu_quantize(gate, up, y=y2, q=pq, scales=ps, prepacked=True)
+    torch.cuda.synchronize()
+    wq, ws = prepack_numpy(to_np(q), to_np(s))
+    assert np.array_equal(to_np(pq), wq) and np.array_equal(to_np(ps), ws)
+    assert torch.equal(y1, y2)
+
+
+def test_fused_decode_step_matches_two_launch_step_and_oracle():
+    """Decode from the producer: RMSNorm writing the prepacked layout, then the
+    GEMM on prepacked operands, equals the two-launch step (producer BF16 output,
+    prepacked quantizer, the same GEMM) bit for bit, and the oracle within the
+    fp32 bar on sampled columns."""
+    dev = device()
+    w = workloads.DECODE
+    m, n, k = w.m, w.n, w.k
+    log(f"fused decode step {w.name}")
+    x = workloads.activation_bf16(m, k, 700, outliers=True)
+    gamma = workloads.gaussian_bf16((k,), 0.1, 701)
+    b = workloads.gaussian_bf16((n, k), w.b_sigma, 702)
+    bq, bs = mxfp4_quantize(b.to(dev))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    xd, gd = x.to(dev), gamma.to(dev)
+    y = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    mxfp4_rmsnorm_quantize(xd, gd, 1e-5, y=y)
+    ap_q, ap_s = mxfp4_quantize_prepacked(y)
+    c_two = mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, out_dtype=torch.float32)
+    fq, fs = mxfp4_rmsnorm_quantize(xd, gd, 1e-5, prepacked=True)
+    c_fused = mxfp4_gemm_nt_prepacked_ab(fq, fs, bp_q, bp_s, m, n, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(fq, ap_q) and torch.equal(fs, ap_s)
+    assert torch.equal(c_fused, c_two)
+    cols = sampled_indices(n, 96, seed=3)
+    aq, as_ = oracle.quantize(_bits(y))
+    obq, obs = oracle.quantize(workloads.bf16_bits(b[torch.from_numpy(cols)]))
+    ref = oracle.gemm_nt(aq, as_, obq, obs)
+    assert oracle.floored_max_rel(to_np(c_fused)[:, cols].astype(np.float64), ref) <= 1e-5
