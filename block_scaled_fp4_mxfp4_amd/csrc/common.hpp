@@ -113,6 +113,18 @@ __device__ __forceinline__ void prepacked_index(int64_t r, int kb, int pairs, in
 // multiple of 8, consecutive logical tiles are placed on one XCD; logical tiles
 // then walk `group_m` tile rows before moving one tile column, so an XCD's
 // tiles share a few A and B panels in its L2.
+// Logical tile t -> (tile_m, tile_n): logical tiles walk `group_m` tile rows
+// before moving one tile column.
+__device__ __forceinline__ void tile_order(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * group_m;
+  const int gsize = min(tiles_m - first_m, group_m);
+  const int r = t - g * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
                                             int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -121,13 +133,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     const int per_xcd = total >> 3;
     t = (bid & 7) * per_xcd + (bid >> 3);
   }
-  const int per_group = group_m * tiles_n;
-  const int g = t / per_group;
-  const int first_m = g * group_m;
-  const int gsize = min(tiles_m - first_m, group_m);
-  const int r = t - g * per_group;
-  tm = first_m + r % gsize;
-  tn = r / gsize;
+  tile_order(t, tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace mxfp4

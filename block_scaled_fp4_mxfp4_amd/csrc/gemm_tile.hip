@@ -426,7 +426,7 @@ __device__ __forceinline__ void barrier_lds() {
 // store).  BF16 uses the hardware packed convert (nearest-even).  The fp32
 // tile does not fit in LDS at once and goes out in two halves by wave row.
 // The caller must have ended every LDS read and copy of the main loop.
-template <class C, int ESIZE, int PITCH>
+template <class C, int ESIZE, int PITCH, int SWZ_MASK = 0>
 __device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXFP4_LDS* tile, int row_begin,
                                          int rows, const RowRange& ar, int n0) {
   constexpr int esize = ESIZE;
@@ -441,7 +441,7 @@ __device__ __forceinline__ void copy_out(const GemmArgs& args, const uint8_t MXF
     const int r = idx / CPR, cc = idx % CPR;
     const int col = cc * (16 / ESIZE);
     if (col >= valid_cols) continue;
-    const v4i v = *(const v4i MXFP4_LDS*)(tile + r * PITCH + cc * 16);
+    const v4i v = *(const v4i MXFP4_LDS*)(tile + r * PITCH + ((cc ^ (r & SWZ_MASK)) * 16));
     uint8_t* dst = cbase + r * row_bytes + cc * 16;
     const int cnt = min(16 / ESIZE, valid_cols - col);
     if (vec_ok && cnt * ESIZE == 16) {
@@ -535,10 +535,20 @@ __device__ __forceinline__ void kstep_pattern() {
 // fa/sc hold k-step 0 of stage kt+1.  COPY_CODES / COPY_SCALES issue the copies
 // of stage kt+2 (and of its scale group) once stage kt's buffer is released,
 // spread over the MFMAs of the last k-step.
+// The copies a stage issues (COPY_CODES / COPY_SCALES): stage `stage` and scale
+// group `group` of the tile that `src` / `tr` describe, into the code buffer this
+// stage releases and scale buffer `group_buf`.  In the main loop that is the
+// same tile's stage kt + 2; in the persistent loop's last stages, the next
+// tile's stage 0 and scale group 0.
+struct StageCopy {
+  int stage, group, group_buf;
+};
+
 template <class C, int MA, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
-__device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
-                                                Scales<C>& sc, const Sources<C>& src, const TileRsrc& tr,
-                                                uint8_t MXFP4_LDS* lds, int kt, int wm0, int wn0, int lane) {
+__device__ __forceinline__ void pipelined_stage_from(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
+                                                     Scales<C>& sc, const Sources<C>& src, const TileRsrc& tr,
+                                                     const StageCopy& cp, uint8_t MXFP4_LDS* lds, int kt, int wm0,
+                                                     int wn0, int lane) {
   constexpr int L = C::KSTEPS - 1;   // the last k-step; its fragments arrive in fb
   constexpr int G = C::SPG_SHIFT;    // stages per scale group: 1 << G
   uint8_t MXFP4_LDS* cur = lds + (kt & 1) * C::CODE_STAGE;
@@ -568,11 +578,10 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
     read_frags<C, 0, MA>(nxt, fa, wm0, wn0, lane);
-    if (COPY_SCALES)
-      copy_scales<C>(lds + 2 * C::CODE_STAGE + (((kt + 2) >> G) & 1) * C::SCALE_GROUP, src, tr, (kt + 2) >> G);
+    if (COPY_SCALES) copy_scales<C>(lds + 2 * C::CODE_STAGE + cp.group_buf * C::SCALE_GROUP, src, tr, cp.group);
     if (COPY_CODES) {
-      copy_codes_a<C>(cur, src, tr, kt + 2);
-      copy_codes_b<C>(cur, src, tr, kt + 2);
+      copy_codes_a<C>(cur, src, tr, cp.stage);
+      copy_codes_b<C>(cur, src, tr, cp.stage);
     }
     mma_kstep<C, L, 0, MA>(fb, sc, acc);
     // the next stage's first fragments go out before the copies (measured ~2 %
@@ -589,6 +598,16 @@ __device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags
     mma_kstep<C, L, 0, MA>(fb, sc, acc);
   }
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// A stage of the main loop: its copies are the same tile's stage kt + 2.
+template <class C, int MA, bool NEXT, bool COPY_CODES, bool COPY_SCALES>
+__device__ __forceinline__ void pipelined_stage(v16f (&acc)[C::MI][C::NI], Frags<C>& fa, Frags<C>& fb,
+                                                Scales<C>& sc, const Sources<C>& src, const TileRsrc& tr,
+                                                uint8_t MXFP4_LDS* lds, int kt, int wm0, int wn0, int lane) {
+  constexpr int G = C::SPG_SHIFT;
+  const StageCopy cp{kt + 2, (kt + 2) >> G, ((kt + 2) >> G) & 1};
+  pipelined_stage_from<C, MA, NEXT, COPY_CODES, COPY_SCALES>(acc, fa, fb, sc, src, tr, cp, lds, kt, wm0, wn0, lane);
 }
 
 // Stages kt + J .. kt + SPG - 1 of one scale group's worth of stages (SPG =
@@ -836,6 +855,238 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
   run_tile<C, COPY>(args, b_q, b_s, ar, tn * C::BN, (uint8_t MXFP4_LDS*)smem);
 }
 
+// ---------------------------------------------------------------------------
+// Persistent tile loop.  One workgroup per compute unit loops over its share
+// of the output tiles.  While its last stage of a tile runs, it already copies
+// the next tile's first stage and scale group into the LDS that the tile no
+// longer needs, and it stages the tile's epilogue through the last stage's
+// buffer alone, so the next tile's first data is in flight during the
+// epilogue instead of after it (a new workgroup would start from nothing).
+// Needs k % (512 * 2) == 0 for FP4 (an even number of scale groups per tile,
+// so every tile's scale group 0 lands in scale buffer 0).
+
+// The wave-uniform description of one output tile.
+struct TileJob {
+  RowRange ar;
+  int n0;
+  const uint8_t* b_q;   // the B operand of the tile's group (dense: args.b_q)
+  const uint8_t* b_s;
+};
+
+template <class C>
+__device__ __forceinline__ void job_sources(const GemmArgs& args, const TileJob& jb, Sources<C>& src, TileRsrc& tr) {
+  make_sources<C>(src, jb.ar, jb.n0, args.n, args.k);
+  const TileBases tb = tile_bases<C>(args, jb.b_q, jb.b_s, jb.ar, jb.n0);
+  tr = tile_rsrc<C>(tb, jb.ar, jb.n0, args.n, args.k);
+}
+
+// Epilogue through one 64 KiB region (the LDS buffer of the tile's last
+// stage): BF16 in two passes of 128 rows (one wave row each), fp32 in four
+// passes of 64 rows.  Rows are not padded: 16-byte chunk c of row r sits at
+// chunk c ^ (r mod chunks-per-row), so the 32 rows one wave writes at one
+// column fall in different chunks.  Ends with a barrier: the region is free.
+template <class C>
+__device__ __forceinline__ void store_tile_region(const GemmArgs& args, const v16f (&acc)[C::MI][C::NI],
+                                                  const RowRange& ar, int n0, int wm0, int wn0, int lane,
+                                                  uint8_t MXFP4_LDS* region) {
+  static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128, "the split epilogue is laid out for 256 x 256 tiles");
+  // The LDS addresses below are the same for every tile; computed from a lane
+  // index the compiler cannot see through, they are not hoisted out of the
+  // persistent loop (held across the main loop they overflowed the registers).
+  asm volatile("" : "+v"(lane));
+  if (!args.c_f32) {
+    constexpr int PITCH = C::BN * 2, CHUNKS = PITCH / 16;   // 512 bytes, 32 chunks per row
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm0 == half * C::WM) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 32 * i + (lane & 31);
+              const int col = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+              bf16x2_t lo = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1]};
+              bf16x2_t hi = {(__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
+              v2i pk = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+              *(v2i MXFP4_LDS*)(region + r * PITCH + (((col >> 3) ^ (r & (CHUNKS - 1))) << 4) + (col & 7) * 2) = pk;
+            }
+      }
+      __syncthreads();
+      copy_out<C, 2, PITCH, CHUNKS - 1>(args, region, half * C::WM, C::WM, ar, n0);
+      __syncthreads();
+    }
+  } else {
+    constexpr int PITCH = C::BN * 4, CHUNKS = PITCH / 16;   // 1024 bytes, 64 chunks per row
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      if (wm0 == (pass >> 1) * C::WM) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (pass & 1) + ii;
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 32 * ii + (lane & 31);
+              const int col = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+              v4f val = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              *(v4f MXFP4_LDS*)(region + r * PITCH + (((col >> 2) ^ (r & (CHUNKS - 1))) << 4)) = val;
+            }
+        }
+      }
+      __syncthreads();
+      copy_out<C, 4, PITCH, CHUNKS - 1>(args, region, pass * 64, 64, ar, n0);
+      __syncthreads();
+    }
+  }
+}
+
+// One tile of the persistent loop with MA computed row blocks per wave.  On
+// entry the tile's scale group 0 and stage 0 have been issued (or have landed)
+// and its stage 1 is in flight; `src` / `tr` describe the tile.  `next` is the
+// tile that follows (or this one again when none does): its scale group 0 and
+// stage 0 are copied during this tile's last two stages, and on return `src` /
+// `tr` describe it.
+template <class C, int MA>
+__device__ __forceinline__ void persistent_tile(const GemmArgs& args, const TileJob& cur, const TileJob& next,
+                                                v16f (&acc)[C::MI][C::NI], Sources<C>& src, TileRsrc& tr,
+                                                uint8_t MXFP4_LDS* lds, int nk, int wm0, int wn0, int lane) {
+  constexpr int G = C::SPG_SHIFT;
+  static_assert(G == 1, "the persistent loop is written for two stages per scale group");
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
+  MXFP4_WAIT_VMCNT(C::CODE_LOADS);            // scale group 0 and stage 0 have landed
+  barrier_lds();
+  Scales<C> sc;
+  Frags<C> fa, fb;
+  read_scales_raw<C, MA>(group0, 0, sc, wm0, wn0, lane);
+  read_frags<C, 0, MA>(lds, fa, wm0, wn0, lane);
+  shift_scales<C, MA>(sc, lane);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) group_stages<C, MA, 0, false>(acc, fa, fb, sc, src, tr, lds, kt, wm0, wn0, lane);
+  // stage nk - 2 releases buffer 0 and scale buffer 0 (nk / 2 groups, an even
+  // number): the next tile's stage 0 and scale group 0 go there
+  job_sources<C>(args, next, src, tr);
+  const StageCopy first{0, 0, 0};
+  pipelined_stage_from<C, MA, true, true, true>(acc, fa, fb, sc, src, tr, first, lds, kt, wm0, wn0, lane);
+  pipelined_stage<C, MA, false, false, false>(acc, fa, fb, sc, src, tr, lds, kt + 1, wm0, wn0, lane);
+  barrier_lds();   // every wave is done with stage nk - 1's buffer, the epilogue's region
+  store_tile_region<C>(args, acc, cur.ar, cur.n0, wm0, wn0, lane, lds + C::CODE_STAGE);
+}
+
+template <class C, int MA>
+__device__ __forceinline__ void persistent_tile_dispatch(int active, const GemmArgs& args, const TileJob& cur,
+                                                         const TileJob& next, v16f (&acc)[C::MI][C::NI],
+                                                         Sources<C>& src, TileRsrc& tr, uint8_t MXFP4_LDS* lds,
+                                                         int nk, int wm0, int wn0, int lane) {
+  if constexpr (MA == 0) {
+    persistent_tile<C, 0>(args, cur, next, acc, src, tr, lds, nk, wm0, wn0, lane);
+  } else {
+    if (active >= MA)
+      persistent_tile<C, MA>(args, cur, next, acc, src, tr, lds, nk, wm0, wn0, lane);
+    else
+      persistent_tile_dispatch<C, MA - 1>(active, args, cur, next, acc, src, tr, lds, nk, wm0, wn0, lane);
+  }
+}
+
+// The loop over the tiles t = first, first + step, ... < end; job(t) gives a
+// tile's description.
+template <class C, class JobOf>
+__device__ __forceinline__ void persistent_loop(const GemmArgs& args, int first, int step, int end, const JobOf& job_of,
+                                                uint8_t MXFP4_LDS* lds) {
+  if (first >= end) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm0 = (w / C::WGN) * C::WM, wn0 = (w % C::WGN) * C::WN;
+  const int nk = args.k / C::SK;
+  v16f acc[C::MI][C::NI];
+  Sources<C> src;
+  TileRsrc tr;
+  TileJob cur = job_of(first);
+  job_sources<C>(args, cur, src, tr);
+  copy_scales<C>(lds + 2 * C::CODE_STAGE, src, tr, 0);
+  copy_codes_a<C>(lds, src, tr, 0);
+  copy_codes_b<C>(lds, src, tr, 0);
+  copy_codes_a<C>(lds + C::CODE_STAGE, src, tr, 1);
+  copy_codes_b<C>(lds + C::CODE_STAGE, src, tr, 1);
+  for (int t = first;;) {
+    const int tn = t + step;
+    const bool has_next = tn < end;
+    // without a next tile the last stages re-copy this tile's first stage
+    // (read, never used) so that every path issues the same copies
+    const TileJob next = has_next ? job_of(tn) : cur;
+    const int active = __builtin_amdgcn_readfirstlane(min(max((cur.ar.end - cur.ar.lo - wm0 + 31) / 32, 0), C::MI));
+    persistent_tile_dispatch<C, C::MI>(active, args, cur, next, acc, src, tr, lds, nk, wm0, wn0, lane);
+    if (!has_next) break;
+    // the epilogue has freed buffer 1: the next tile's stage 1 goes there
+    copy_codes_a<C>(lds + C::CODE_STAGE, src, tr, 1);
+    copy_codes_b<C>(lds + C::CODE_STAGE, src, tr, 1);
+    cur = next;
+    t = tn;
+  }
+  MXFP4_WAIT_VMCNT(0);   // the last re-copy lands before the workgroup's LDS is released
+}
+
+// Dense persistent kernel: grid = a multiple of 8 workgroups, at most one per
+// CU; workgroup b runs on XCD b % 8 and takes that XCD's logical tiles
+// x * per_xcd + slot, + workgroups per XCD, ... (tile order as tile_coords).
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_persistent_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int total = tiles_m * tiles_n;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_wg = gridDim.x >> 3;
+  const int share = (total + 7) >> 3;
+  const int lo = xcd * share, hi = min(lo + share, total);
+  const auto job_of = [&](int t) {
+    int tm, tn;
+    tile_order(t, tiles_m, tiles_n, 4, tm, tn);
+    TileJob jb;
+    jb.ar.lo = tm * C::BM;
+    jb.ar.end = min(jb.ar.lo + C::BM, args.m);
+    jb.ar.last = jb.ar.end - 1;
+    jb.n0 = tn * C::BN;
+    jb.b_q = args.b_q;
+    jb.b_s = args.b_s;
+    return jb;
+  };
+  persistent_loop<C>(args, lo + slot, per_wg, hi, job_of, (uint8_t MXFP4_LDS*)smem);
+}
+
+// Grouped persistent kernel: the real tiles (counted from the sanitized
+// offsets) split evenly over the 8 XCDs as contiguous ranges, as in
+// grouped_tile_kernel, and each XCD's range dealt round-robin to its workgroups.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_persistent_kernel(GemmArgs args, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int total = count_mtiles(args.offsets, args.groups, args.m, C::BM) * tiles_n;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_wg = gridDim.x >> 3;
+  const int share = (total + 7) >> 3;
+  const int lo = xcd * share, hi = min(lo + share, total);
+  const int64_t kb = args.k / 2, ks = args.k / 32;
+  const auto job_of = [&](int t) {
+    const int mt = t / tiles_n, tn = t - mt * tiles_n;
+    TileJob jb;
+    int g = 0;
+    if (!find_group(args.offsets, args.groups, args.m, C::BM, mt, g, jb.ar)) {
+      // unreachable for t < total (the counts agree); an empty row range stores nothing
+      jb.ar.lo = 0;
+      jb.ar.end = 0;
+      jb.ar.last = 0;
+    }
+    jb.n0 = tn * C::BN;
+    jb.b_q = args.b_q + (int64_t)g * args.n * kb;
+    jb.b_s = args.b_s + (int64_t)g * args.n * ks;
+    return jb;
+  };
+  persistent_loop<C>(args, lo + slot, per_wg, hi, job_of, (uint8_t MXFP4_LDS*)smem);
+}
+
 using Cfg256 = TileCfg<256, 256, 2, 4>;
 using Cfg128 = TileCfg<128, 128, 2, 2>;
 using CfgW4A8 = TileCfg<128, 256, 2, 4, true>;
@@ -903,7 +1154,58 @@ hipError_t launch_grouped(const GemmArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The persistent kernels need the copy path with an even number of scale
+// groups per tile (k % 1024 == 0).
+bool persistent_ok(const GemmArgs& args) { return use_copy_path(args) && args.k % 1024 == 0; }
+
+// Workgroups of a persistent launch: one per compute unit, a multiple of 8
+// (one per XCD slot), capped by `max_wgs` (0: no cap) and by 8 x the tiles one
+// XCD takes.
+int persistent_grid(int num_cus, int max_wgs, int64_t tiles) {
+  int wgs = max(8, num_cus & ~7);
+  if (max_wgs > 0) wgs = min(wgs, max(8, max_wgs & ~7));
+  const int64_t per_xcd = (tiles + 7) / 8;
+  if (8 * per_xcd < wgs) wgs = (int)(8 * per_xcd);
+  return max(8, wgs);
+}
+
+template <class C>
+hipError_t launch_dense_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream) {
+  if (!persistent_ok(args)) return hipErrorInvalidValue;
+  const int tiles_m = (args.m + C::BM - 1) / C::BM;
+  const int tiles_n = (args.n + C::BN - 1) / C::BN;
+  const int grid = persistent_grid(num_cus, max_wgs, (int64_t)tiles_m * tiles_n);
+  hipError_t e = allow_lds(gemm_persistent_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_persistent_kernel<C>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, args, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_grouped_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream) {
+  if (!persistent_ok(args)) return hipErrorInvalidValue;
+  const int64_t mt_bound = (args.m + C::BM - 1) / C::BM + args.groups;
+  const int tiles_n = (args.n + C::BN - 1) / C::BN;
+  const int grid = persistent_grid(num_cus, max_wgs, mt_bound * tiles_n);
+  hipError_t e = allow_lds(grouped_persistent_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped_persistent_kernel<C>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, args,
+                     tiles_n);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool gemm_persistent_supported(const GemmArgs& args) { return persistent_ok(args); }
+
+hipError_t launch_gemm_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream) {
+  return launch_dense_persistent<Cfg256>(args, num_cus, max_wgs, stream);
+}
+
+hipError_t launch_grouped_gemm_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream) {
+  return launch_grouped_persistent<Cfg256>(args, num_cus, max_wgs, stream);
+}
 
 hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream) {
   return kind == kTile256 ? launch_dense<Cfg256>(args, stream) : launch_dense<Cfg128>(args, stream);

@@ -41,6 +41,14 @@ hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t str
 
 hipError_t launch_grouped_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
 
+// Persistent 256x256 tile kernels: at most one workgroup per compute unit
+// (capped by max_wgs when > 0), each looping over its tiles and copying the
+// next tile's first stage during the current tile's last stages and epilogue.
+// Need k % 1024 == 0 and 16-byte aligned scale arrays (gemm_persistent_supported).
+bool gemm_persistent_supported(const GemmArgs& args);
+hipError_t launch_gemm_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream);
+hipError_t launch_grouped_gemm_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream);
+
 // W4A8 tile kernels: A in MXFP8 (a_q is [m, k] E4M3 codes), B in MXFP4;
 // 128 x 256 output tiles.
 hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);

@@ -156,6 +156,10 @@ mxfp4_status_t mxfp4_gemm_nt(const void* a_q, const void* a_s,
  *   num_groups: 1 .. 1024
  *   workspace : at least mxfp4_grouped_gemm_nt_workspace_size(...) bytes.
  * One kernel launch; nothing depends on host knowledge of the group sizes.
+ * Groups averaging 192 rows or more use 256x256 tiles (through the persistent
+ * tile loop of MXFP4_KERNEL_PERSISTENT when k % 1024 == 0 and the scale
+ * arrays are 16-byte aligned), others 128x128 tiles.  Each group's rows equal
+ * mxfp4_gemm_nt_ex on that group's slices with the same tile size, bit for bit.
  */
 size_t mxfp4_grouped_gemm_nt_workspace_size(int64_t total_m, int32_t num_groups,
                                             int64_t n, int64_t k);
@@ -248,6 +252,12 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, co
  *                          the whole K, operands copied into LDS in 512-K
  *                          units; needs k % 512 == 0 and 16-byte aligned
  *                          scale arrays (MXFP4_ERR_INVALID_ARG otherwise)
+ *   MXFP4_KERNEL_PERSISTENT 256x256 tiles as TILE256, one workgroup per compute
+ *                          unit looping over its tiles and loading the next
+ *                          tile's first K stage during a tile's epilogue;
+ *                          results identical to TILE256; needs k % 1024 == 0
+ *                          and 16-byte aligned scale arrays
+ *                          (MXFP4_ERR_INVALID_ARG otherwise)
  * `splits` is only read for MXFP4_KERNEL_SPLITK (0 = automatic, else 1..64).
  * For m <= 128 the automatic choice is MXFP4_KERNEL_STREAM when its
  * requirements hold, else MXFP4_KERNEL_SPLITK; neither needs a workspace then.
@@ -258,7 +268,8 @@ typedef enum {
   MXFP4_KERNEL_TILE256 = 1,
   MXFP4_KERNEL_TILE128 = 2,
   MXFP4_KERNEL_SPLITK = 3,
-  MXFP4_KERNEL_STREAM = 4
+  MXFP4_KERNEL_STREAM = 4,
+  MXFP4_KERNEL_PERSISTENT = 5
 } mxfp4_kernel_t;
 
 size_t mxfp4_gemm_nt_ex_workspace_size(int64_t m, int64_t n, int64_t k,

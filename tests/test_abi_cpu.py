@@ -91,6 +91,14 @@ def test_gemm_rejects_bad_arguments_on_host(lib):
     assert call(m=-1) == 1
     assert call(c_type=7) == 1
     assert call(kernel=9) == 1
+    assert call(kernel=6) == 1
+    assert b"unknown kernel id 6" in lib.mxfp4_last_error()
+    # forced kernels' requirements are checked before any device call: the stream
+    # kernel needs k % 512 == 0, the persistent one k % 1024 == 0
+    assert call(kernel=4, k=1056) == 1
+    assert b"stream kernel needs" in lib.mxfp4_last_error()
+    assert call(kernel=5, k=1536) == 1
+    assert b"persistent kernel needs" in lib.mxfp4_last_error()
     assert call(b_s=None) == 1
     assert b"b_s is NULL" in lib.mxfp4_last_error()
     assert call(c=_fake(0x1004)) == 1

@@ -33,6 +33,9 @@ TILE_SHAPES = [  # (m, n, k): several tiles, ragged tails, k % 128 != 0 cases
 ]
 SPLITK_SHAPES = [(1, 64, 128), (17, 200, 1024), (32, 1000, 4096), (33, 70, 160), (100, 512, 2048),
                  (128, 320, 4096), (64, 129, 8192)]
+# the persistent loop needs k % 1024 == 0; k = 1024 is the two-stage tile (no loop body)
+PERSISTENT_SHAPES = [(300, 520, 1024), (513, 263, 2048), (257, 129, 4096), (352, 520, 1024), (1, 300, 1024),
+                     (200, 300, 3072)]
 STREAM_SHAPES = [(1, 64, 512), (17, 200, 1024), (32, 1000, 4096), (33, 70, 512), (64, 129, 8192),
                  (100, 512, 2048), (128, 320, 4096), (129, 66, 1536), (300, 190, 1024)]
 
@@ -58,6 +61,8 @@ def _cases():
             yield "splitk", splits, shape
     for shape in STREAM_SHAPES:
         yield "stream", 0, shape
+    for shape in PERSISTENT_SHAPES:
+        yield "persistent", 0, shape
 
 
 CASES = list(_cases())
@@ -129,7 +134,46 @@ def test_stream_kernel_rejects_unsupported_k():
         mxfp4_gemm_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), kernel="stream")
 
 
-@pytest.mark.parametrize("kernel", ["tile256", "tile128", "stream", "splitk"])
+def test_persistent_kernel_rejects_unsupported_k():
+    """The persistent loop takes an even number of 512-K scale groups per tile:
+    k = 1536 is refused, not miscomputed."""
+    dev = device()
+    aq, as_ = random_codes(300, 1536, 1)
+    bq, bs = random_codes(64, 1536, 2)
+    with pytest.raises(MXFP4Error):
+        mxfp4_gemm_nt(upload(aq, dev), upload(as_, dev), upload(bq, dev), upload(bs, dev), kernel="persistent")
+
+
+@pytest.mark.parametrize("shape", [(4400, 4200, 2048), (8192, 8192, 1024)])
+def test_persistent_matches_tile256_many_tiles_per_workgroup(shape):
+    """More output tiles than compute units: every workgroup of the persistent
+    launch runs several tiles back to back (the next tile's first stage is
+    loaded during the previous tile's epilogue).  The result is bit-identical
+    to the one-tile-per-workgroup kernel, and sampled entries match the oracle."""
+    dev = device()
+    m, n, k = shape
+    log(f"persistent vs tile256 {shape}")
+    a = random_bf16((m, k), 30 + m, spread=3, outlier_frac=0.01)
+    b = random_bf16((n, k), 40 + n, spread=3)
+    aq, as_ = mxfp4_quantize(a.to(dev))
+    bq, bs = mxfp4_quantize(b.to(dev))
+    got = {}
+    for dt, bits in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        ref = mxfp4_gemm_nt(aq, as_, bq, bs, out_dtype=dt, kernel="tile256")
+        got[dt] = mxfp4_gemm_nt(aq, as_, bq, bs, out_dtype=dt, kernel="persistent")
+        torch.cuda.synchronize()
+        assert torch.equal(got[dt].view(bits), ref.view(bits)), f"{dt} differs from the tile256 kernel"
+    rows = sampled_indices(m, 48, seed=3)
+    cols = sampled_indices(n, 48, seed=4)
+    oaq, oas = oracle.quantize(workloads.bf16_bits(a[torch.from_numpy(rows)]))
+    obq, obs = oracle.quantize(workloads.bf16_bits(b[torch.from_numpy(cols)]))
+    c64 = oracle.gemm_nt(oaq, oas, obq, obs)
+    assert oracle.floored_max_rel(to_np(got[torch.float32])[np.ix_(rows, cols)], c64) <= 1e-5
+    got16 = to_np(got[torch.bfloat16].view(torch.int16)).view(np.uint16)[np.ix_(rows, cols)]
+    assert_bf16_matches_rounded(got16, c64)
+
+
+@pytest.mark.parametrize("kernel", ["tile256", "tile128", "stream", "splitk", "persistent"])
 def test_gemm_long_k(kernel):
     """A long reduction (k = 2^19): row offsets inside a tile reach 255 * k/2
     bytes.  Codes of magnitude <= 1 with unit scales keep every partial sum a

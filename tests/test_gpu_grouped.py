@@ -48,6 +48,11 @@ PATTERNS = {
     "tile_boundaries_256": ([255, 256, 257, 511, 1], 256, 512),
     "ragged_k": ([33, 70, 5], 72, 160),
     "many_groups": (list(np.random.default_rng(0).integers(0, 40, size=70)), 64, 256),
+    # 256 x 256 tiles with k % 1024 == 0 take the persistent loop: k = 1024 (two
+    # stages, no loop body) with ragged groups, and more tiles than compute units
+    # (every workgroup runs several tiles of different experts)
+    "persistent_ragged": ([0, 255, 256, 257, 511, 1, 700, 0], 200, 1024),
+    "persistent_many_tiles": (list(np.random.default_rng(1).integers(0, 600, size=32)), 1536, 2048),
 }
 
 
