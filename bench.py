@@ -1152,8 +1152,12 @@ def main():
             "algorithmic_bytes": mbytes,
             # the workload sits near the ridge: report both roofs and the fraction of the
             # binding one (roof time = max(flops / MFMA peak, bytes / HBM peak))
-            "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s", kernel="grouped_persistent_kernel"),
-            "roofline_hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", kernel="grouped_persistent_kernel"),
+            "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s",
+                                 traffic_from_profiles(wm.name, "grouped_persistent_kernel"),
+                                 kernel="grouped_persistent_kernel"),
+            "roofline_hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                     traffic_from_profiles(wm.name, "grouped_persistent_kernel"),
+                                     kernel="grouped_persistent_kernel"),
             "min_roof_frac": round(max(wm.flops / (PEAK_FP4_TFLOPS * 1e12), mbytes / (PEAK_HBM_GBS * 1e9))
                                    / (gm["mean"] * 1e-3), 4),
             "inputs": moe_inputs_record(wm),

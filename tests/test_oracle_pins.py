@@ -314,6 +314,24 @@ def test_gemm_f32_within_float32_bound():
     assert c32.dtype == np.float32
 
 
+def test_gemm_f32_accumulates_in_float32():
+    """The fp32 reference really accumulates in float32, not in float64 then cast.
+    Every product is 0.5 * 2**-74 times 0.5 * 2**-74 = 2**-150: exactly half the
+    smallest float32 subnormal, which rounds (ties to even) to zero.  So in any
+    float32 order, with or without fused multiply-add, every partial sum stays
+    zero, while the exact sum of 64 such products is 2**-144, a float32
+    subnormal that a float64 accumulation followed by a cast would keep."""
+    k = 64
+    code_half = 0x1                                  # E2M1 code of 0.5
+    q = np.full((1, k // 2), code_half | (code_half << 4), np.uint8)
+    s = np.full((1, k // 32), 127 - 74, np.uint8)    # 2**-74
+    c64 = O.gemm_nt(q, s, q, s)
+    c32 = O.gemm_nt_f32(q, s, q, s)
+    assert c64[0, 0] == 2.0 ** -144
+    assert np.float32(c64[0, 0]) == np.float32(2.0 ** -144) != 0
+    assert c32[0, 0] == 0.0
+
+
 def test_grouped_gemm_tiny_exact_rational():
     rng = np.random.default_rng(9)
     k, n = 64, 3
