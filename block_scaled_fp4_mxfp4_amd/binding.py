@@ -31,6 +31,7 @@ EXPORTED = (
     "mxfp4_moe_route", "mxfp4_moe_permute", "mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
     "mxfp4_moe_combine", "mxfp4_rmsnorm_quantize", "mxfp4_swiglu_quantize", "nvfp4_quantize", "nvfp4_gemm_nt",
     "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
+    "mxfp4_gemm_nt_prepacked_ab_ex", "mxfp4_gemm_nt_prepacked_ab_workspace_size",
     "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex", "mxfp4_gemm_nt_ex_noalloc",
     "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked",
 )
@@ -99,6 +100,11 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_quantize_prepacked.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp4_gemm_nt_prepacked_ab.restype = ctypes.c_int
         lib.mxfp4_gemm_nt_prepacked_ab.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp4_gemm_nt_prepacked_ab_ex.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_prepacked_ab_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int32,
+                                                      vp, ctypes.c_size_t, vp]
+        lib.mxfp4_gemm_nt_prepacked_ab_workspace_size.restype = ctypes.c_size_t
+        lib.mxfp4_gemm_nt_prepacked_ab_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int32]
         lib.mxfp4_grouped_gemm_nt_workspace_size.restype = sz
         lib.mxfp4_grouped_gemm_nt_workspace_size.argtypes = [i64, i32, i64, i64]
         lib.mxfp4_grouped_gemm_nt.restype = ctypes.c_int
@@ -324,8 +330,11 @@ def mxfp4_quantize_prepacked(x, ap_q=None, ap_s=None, stream=None):
 
 
 def mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m: int, n: int, k: int, c=None, out_dtype=torch.bfloat16,
-                               stream=None):
-    """C[m, n] = A . B^T with both A [m, k] and B [n, k] prepacked (mxfp4_prepack_weight)."""
+                               splits: int = 0, ws: torch.Tensor | None = None, stream=None):
+    """C[m, n] = A . B^T with both A [m, k] and B [n, k] prepacked (mxfp4_prepack_weight).
+
+    splits: 0 = automatic K split over workgroups when the 64-column panels do
+    not fill the chip (reduced through a zero-filled workspace), 1 = none."""
     lib = load_library()
     for t, rows, name in ((ap_q, m, "ap_q"), (bp_q, n, "bp_q")):
         cb, _ = mxfp4_prepacked_weight_size(rows, k)
@@ -334,8 +343,12 @@ def mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m: int, n: int, k: int, c
         _, sb = mxfp4_prepacked_weight_size(rows, k)
         _require(t, name, torch.uint8, (sb,))
     c, code = _out(c, m, n, out_dtype, ap_q.device)
-    _check(lib.mxfp4_gemm_nt_prepacked_ab(_ptr(ap_q), _ptr(ap_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
-                                          _stream(stream)))
+    need = lib.mxfp4_gemm_nt_prepacked_ab_workspace_size(m, n, k, splits)
+    if ws is None:
+        ws = workspace(need, ap_q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.mxfp4_gemm_nt_prepacked_ab_ex(_ptr(ap_q), _ptr(ap_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
+                                             splits, _ptr(ws), nbytes, _stream(stream)))
     return c
 
 

@@ -61,6 +61,7 @@ mxfp4_status_t current_device(DeviceInfo& out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // m, n: keeps row and tile indices in int32 range
+constexpr int32_t kMaxPPSplits = 16;             // K ranges of the both-prepacked split-K GEMM
 // k: the tile kernels address a tile's operand rows with 32-bit byte offsets
 // from the tile's first row, (row in tile) * k/2 with up to 256 rows.
 constexpr int64_t kMaxK = (int64_t)1 << 24;
@@ -419,14 +420,24 @@ mxfp4_status_t mxfp4_quantize_prepacked(const void* x_bf16, int64_t rows, int64_
                     "prepacked quantize launch");
 }
 
-mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, const void* bp_q, const void* bp_s,
-                                          void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+size_t mxfp4_gemm_nt_prepacked_ab_workspace_size(int64_t m, int64_t n, int64_t k, int32_t splits) {
+  if (m <= 0 || n <= 0 || m > kMaxDim || n > kMaxDim || check_k(k) != MXFP4_OK || k % 512) return 0;
+  if (splits < 0 || splits > kMaxPPSplits) return 0;
+  const int s = splits == 0 ? mxfp4::pp_auto_splits((int)m, (int)n, (int)k, query_num_cus()) : splits;
+  return mxfp4::pp_workspace_bytes((int)m, (int)n, (int)k, s);
+}
+
+mxfp4_status_t mxfp4_gemm_nt_prepacked_ab_ex(const void* ap_q, const void* ap_s, const void* bp_q, const void* bp_s,
+                                             void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                             int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
   if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
   MXFP4_TRY(check_k(k));
   if (k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
   if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
     return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (splits < 0 || splits > kMaxPPSplits)
+    return fail(MXFP4_ERR_INVALID_ARG, "splits must be 0..%d (got %d)", kMaxPPSplits, splits);
   if (m == 0 || n == 0) return MXFP4_OK;
   MXFP4_TRY(check_ptr(ap_q, "ap_q"));
   MXFP4_TRY(check_ptr(ap_s, "ap_s"));
@@ -435,6 +446,16 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, co
   MXFP4_TRY(check_ptr(c, "c"));
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
+  const int s = splits == 0 ? mxfp4::pp_auto_splits((int)m, (int)n, (int)k, dev.num_cus) : splits;
+  const size_t need = mxfp4::pp_workspace_bytes((int)m, (int)n, (int)k, s);
+  if (s > 1 && mxfp4::pp_effective_splits((int)k, s) > 1 && need == 0)
+    return fail(MXFP4_ERR_INVALID_ARG, "split-K supports at most 16384 output tiles (64-column panels x row tiles)");
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(MXFP4_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  }
   mxfp4::GemmArgs args{};
   args.a_q = (const uint8_t*)ap_q;
   args.a_s = (const uint8_t*)ap_s;
@@ -445,7 +466,13 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, co
   args.m = (int)m;
   args.n = (int)n;
   args.k = (int)k;
-  return hip_status(mxfp4::launch_gemm_both_prepacked(args, (hipStream_t)stream), "prepacked gemm launch");
+  return hip_status(mxfp4::launch_gemm_both_prepacked(args, need > 0 ? s : 1, workspace, (hipStream_t)stream),
+                    "prepacked gemm launch");
+}
+
+mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, const void* bp_q, const void* bp_s,
+                                          void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  return mxfp4_gemm_nt_prepacked_ab_ex(ap_q, ap_s, bp_q, bp_s, c, c_type, m, n, k, 1, nullptr, 0, stream);
 }
 
 size_t mxfp4_grouped_gemm_nt_workspace_size(int64_t total_m, int32_t num_groups, int64_t n, int64_t k) {

@@ -41,6 +41,7 @@
 // Requirements (checked by the host): k % 512 == 0 and 16-byte aligned scale
 // arrays.  Rows past M and columns past N read a clamped valid row and are
 // never stored.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -57,6 +58,11 @@ constexpr int kRowBytes = 128;    // code bytes per row per 256-K stage
 // the prepacked decode GEMM, 1.5-2.5 % for this streaming kernel.
 constexpr int kLoadNT = 2;
 constexpr int kBN = 64;
+// Split-K workspace of the both-prepacked kernel: the arrival counters fill a
+// fixed region at the start (so one zeroed workspace serves every shape), the
+// partial tiles follow.
+constexpr size_t kPPCounterBytes = 65536;
+constexpr int kPPMaxTiles = (int)(kPPCounterBytes / sizeof(int));
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
@@ -218,14 +224,14 @@ __device__ __forceinline__ bool stream_coords(int b, int tiles_m, int tiles_n, i
   return tn < tiles_n;
 }
 
-// Reduce-scatter of the four waves' fp32 partial tiles and the stores of C.
+// Reduce-scatter of the four waves' fp32 partial tiles.  The accumulators
+// split into U units of 64 lanes x 4 floats (row block i, column block j,
+// column group q); wave w owns units [w*U/4, (w+1)*U/4).  Each wave parks the
+// units it does not own in LDS, then sums each of its units over the waves in
+// the fixed order 0, 1, 2, 3 into own[] (own[t] is unit w*U/4 + t).
 template <class C>
-__device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const GemmArgs& args, int m0, int n0,
-                                                uint8_t MXFP4_LDS* lds, int w, int lane) {
-  // The accumulators split into U units of 64 lanes x 4 floats (row block i,
-  // column block j, column group q); wave w owns units [w*U/4, (w+1)*U/4).
-  // Each wave parks the units it does not own in LDS, then sums each of its
-  // units over the waves in the fixed order 0, 1, 2, 3.
+__device__ __forceinline__ void reduce_units(const v16f (&acc)[C::MB][2], uint8_t MXFP4_LDS* lds, int w, int lane,
+                                             v4f (&own)[C::MB * 2]) {
   constexpr int U = C::MB * 8, UW = U / 4;
   v4f MXFP4_LDS* xch = (v4f MXFP4_LDS*)lds;
 #pragma unroll
@@ -237,7 +243,23 @@ __device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const Gem
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u / UW != w) continue;   // wave-uniform
+    const int i = u / 8, j = (u / 4) % 2, q = u % 4;
+    const v4f mine = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    v4f v = (w == 0) ? mine : xch[u * 64 + lane];
+#pragma unroll
+    for (int src = 1; src < 4; ++src) v += (w == src) ? mine : xch[(src * U + u) * 64 + lane];
+    own[u % UW] = v;
+  }
+}
 
+// The stores of C from each wave's summed units (reduce_units).
+template <class C>
+__device__ __forceinline__ void store_units(const v4f (&own)[C::MB * 2], const GemmArgs& args, int m0, int n0,
+                                            uint8_t MXFP4_LDS* lds, int w, int lane) {
+  constexpr int U = C::MB * 8, UW = U / 4;
   const int rows = min(C::BM, args.m - m0);
   const int cols = min(kBN, args.n - n0);
   const int n = args.n;
@@ -247,13 +269,10 @@ __device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const Gem
     // scattered over 32 rows measured far slower in the tile kernels).
     uint8_t MXFP4_LDS* ctile = lds + C::XCH;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u / UW != w) continue;   // wave-uniform
+    for (int t = 0; t < UW; ++t) {
+      const int u = w * UW + t;
       const int i = u / 8, j = (u / 4) % 2, q = u % 4;
-      const v4f own = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-      v4f v = (w == 0) ? own : xch[u * 64 + lane];
-#pragma unroll
-      for (int src = 1; src < 4; ++src) v += (w == src) ? own : xch[(src * U + u) * 64 + lane];
+      const v4f v = own[t];
       const int r = 32 * i + (lane & 31);
       const int col = 32 * j + 8 * q + 4 * (lane >> 5);
       bf16x2_t lo = {(__bf16)v.x, (__bf16)v.y};
@@ -282,13 +301,10 @@ __device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const Gem
     return;
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u / UW != w) continue;   // wave-uniform
+  for (int t = 0; t < UW; ++t) {
+    const int u = w * UW + t;
     const int i = u / 8, j = (u / 4) % 2, q = u % 4;
-    const v4f own = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    v4f v = (w == 0) ? own : xch[u * 64 + lane];
-#pragma unroll
-    for (int src = 1; src < 4; ++src) v += (w == src) ? own : xch[(src * U + u) * 64 + lane];
+    const v4f v = own[t];
     const int r = 32 * i + (lane & 31);
     const int col = 32 * j + 8 * q + 4 * (lane >> 5);
     const int cnt = min(4, cols - col);
@@ -300,6 +316,15 @@ __device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const Gem
       for (int e = 0; e < cnt; ++e) dst[e] = v[e];
     }
   }
+}
+
+// Reduction of the four waves' partial tiles and the stores of C.
+template <class C>
+__device__ __forceinline__ void stream_epilogue(v16f (&acc)[C::MB][2], const GemmArgs& args, int m0, int n0,
+                                                uint8_t MXFP4_LDS* lds, int w, int lane) {
+  v4f own[C::MB * 2];
+  reduce_units<C>(acc, lds, w, lane, own);
+  store_units<C>(own, args, m0, n0, lds, w, lane);
 }
 
 template <class C>
@@ -781,20 +806,110 @@ __device__ __forceinline__ void pp_chunk(int p0, __amdgpu_buffer_rsrc_t ra, __am
   }
 }
 
+// Split-K of the both-prepacked kernel, for shapes with fewer output tiles
+// than compute units (the decode down projection: 64 column panels).  Each
+// output tile's K is cut into `splits` ranges of `pairs_per_split` 512-K pairs
+// (the last may be shorter), one workgroup each.  A workgroup writes its
+// reduced fp32 tile to the workspace and bumps the tile's arrival counter; the
+// last to arrive sums the partial tiles in split order 0, 1, ... (so results
+// do not depend on timing), stores C and returns the counter to zero.
+//
+// Visibility across workgroups, which may run on different XCDs with separate
+// L2 caches: the partial tiles are written and read with device-coherent
+// accesses (the sc1 cache policy, the one relaxed device-scope atomic loads
+// and stores compile to), and every writer waits for its stores to complete
+// before its arrival.  Only these lines bypass the L2; the device-scope
+// release / acquire fences would instead write back and invalidate the whole
+// L2, which made the older split-K kernel many times slower.
+struct PPSplit {
+  int splits;            // K ranges per output tile
+  int pairs_per_split;   // 512-K pairs per range
+  int* counters;         // [tiles], zero between launches
+  float* partials;       // [tiles][splits][units][64 lanes][4 floats]
+};
+
+constexpr int kCoherent = 16;   // buffer cache policy bits: sc1 (device-coherent)
+
+// This workgroup's part of the split-K reduction of output tile `tile`: own[]
+// holds the wave's summed units of K range `split`.  Returns false for every
+// workgroup but the last to arrive; that one gets the sum over all ranges in
+// own[].
+template <class C>
+__device__ __forceinline__ bool combine_splits(v4f (&own)[C::MB * 2], const PPSplit& sk, int tile, int split,
+                                               uint8_t MXFP4_LDS* lds, int w, int lane) {
+  constexpr int U = C::MB * 8, UW = U / 4;
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc((const uint8_t*)(sk.partials + (int64_t)tile * sk.splits * U * 256),
+                                                 (uint32_t)(sk.splits * U * 1024));
+#pragma unroll
+  for (int t = 0; t < UW; ++t)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, own[t]), rp,
+                                           (uint32_t)(((split * U + w * UW + t) * 64 + lane) * 16), 0, kCoherent);
+  MXFP4_WAIT_VMCNT(0);   // this thread's partial stores have completed
+  __syncthreads();
+  // the reduction exchange area is free again: its first word carries the verdict
+  int MXFP4_LDS* last = (int MXFP4_LDS*)lds;
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(&sk.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = prev == sk.splits - 1;
+    if (prev == sk.splits - 1) __hip_atomic_store(&sk.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!*last) return false;
+  // The partial tiles in groups of four ranges: a group's loads are all issued
+  // before any is used (one memory round trip per group; loaded one at a time
+  // the sum took longer than the whole main loop), then added in range order.
+  // The loads are unconditional (past the last range they reread it; this
+  // workgroup's own range is read back and not used) so that no branch makes
+  // the compiler wait between them.
+  constexpr int G = 4;
+  v4f sum[UW];
+  for (int sp0 = 0; sp0 < sk.splits; sp0 += G) {
+    v4f part[G][UW];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int sp = min(sp0 + g, sk.splits - 1);
+#pragma unroll
+      for (int t = 0; t < UW; ++t)
+        part[g][t] = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(((sp * U + w * UW + t) * 64 + lane) * 16), 0,
+                                                       kCoherent));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the group before the first add
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int sp = sp0 + g;
+      if (sp >= sk.splits) break;
+#pragma unroll
+      for (int t = 0; t < UW; ++t) {
+        const v4f v = sp == split ? own[t] : part[g][t];
+        sum[t] = sp == 0 ? v : sum[t] + v;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < UW; ++t) own[t] = sum[t];
+  return true;
+}
+
 // K in chunks of 8 pairs (K = 4096 is one chunk), then one of 4, then single
-// pairs; the pipeline refills at each chunk boundary.
-template <int MB>
-__global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int tiles_m, int tiles_n) {
+// pairs; the pipeline refills at each chunk boundary.  SPLIT: the workgroup
+// covers one K range of its tile (combine_splits).
+template <int MB, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int tiles_m, int tiles_n, PPSplit sk) {
   using EC = StreamCfg<MB, 2, false, true>;   // epilogue layout (reduction area and C tile)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t MXFP4_LDS* lds = (uint8_t MXFP4_LDS*)smem;
-  int tm, tn;
-  if (!stream_coords(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  const int splits = SPLIT ? sk.splits : 1;
+  int tm, tv;
+  if (!stream_coords(blockIdx.x, tiles_m, tiles_n * splits, tm, tv)) return;
   tm = __builtin_amdgcn_readfirstlane(tm);
-  tn = __builtin_amdgcn_readfirstlane(tn);
+  tv = __builtin_amdgcn_readfirstlane(tv);
+  const int tn = tv / splits, split = tv - tn * splits;
   const int m0 = tm * EC::BM, n0 = tn * kBN;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int np = __builtin_amdgcn_readfirstlane(args.k / 512);
+  const int p_begin = SPLIT ? split * sk.pairs_per_split : 0;
+  const int p_end = SPLIT ? min(np, p_begin + sk.pairs_per_split) : np;
 
   // B: this column panel.  A: the tile's row panels (MB = 1: half of one);
   // the A panels that exist for this tile (the last tile of a ragged m may
@@ -818,31 +933,67 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int ti
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const uint32_t pq = (uint32_t)panel_q, ps = (uint32_t)panel_s;
-  int p0 = 0;
-  for (; p0 + 8 <= np; p0 += 8) pp_chunk<MB, 8>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
-  if (p0 + 4 <= np) {
+  int p0 = p_begin;
+  for (; p0 + 8 <= p_end; p0 += 8) pp_chunk<MB, 8>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+  if (p0 + 4 <= p_end) {
     pp_chunk<MB, 4>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
     p0 += 4;
   }
-  for (; p0 < np; ++p0) pp_chunk<MB, 1>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+  for (; p0 < p_end; ++p0) pp_chunk<MB, 1>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
 
-  stream_epilogue<EC>(acc, args, m0, n0, lds, w, lane);
+  v4f own[MB * 2];
+  reduce_units<EC>(acc, lds, w, lane, own);
+  if constexpr (SPLIT) {
+    if (!combine_splits<EC>(own, sk, tm * tiles_n + tn, split, lds, w, lane)) return;
+  }
+  store_units<EC>(own, args, m0, n0, lds, w, lane);
 }
 
 template <int MB>
-hipError_t launch_pp_cfg(const GemmArgs& args, hipStream_t stream) {
+int pp_tiles(const GemmArgs& args) {
+  return ((args.m + 32 * MB - 1) / (32 * MB)) * ((args.n + kBN - 1) / kBN);
+}
+
+template <int MB, bool SPLIT>
+hipError_t launch_pp_cfg(const GemmArgs& args, const PPSplit& sk, hipStream_t stream) {
   using EC = StreamCfg<MB, 2, false, true>;
   constexpr int lds_bytes = EC::XCH + EC::C_TILE;
-  const auto kernel = gemm_pp_kernel<MB>;
+  const auto kernel = gemm_pp_kernel<MB, SPLIT>;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   const int tiles_n = (args.n + kBN - 1) / kBN;
   const int tiles_m = (args.m + EC::BM - 1) / EC::BM;
-  const int64_t blocks = (int64_t)tiles_m * ((tiles_n + 7) / 8) * 8;
-  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), lds_bytes, stream, args, tiles_m, tiles_n);
+  const int64_t virt_n = (int64_t)tiles_n * (SPLIT ? sk.splits : 1);
+  const int64_t blocks = (int64_t)tiles_m * ((virt_n + 7) / 8) * 8;
+  if (virt_n > 0x7FFFFFFF || !grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), lds_bytes, stream, args, tiles_m, tiles_n, sk);
   return hipGetLastError();
 }
+
+// Pairs per K range for a request of `splits` ranges over np pairs:
+// ceil(np / splits), rounded up to a multiple of 4 when above 4, so that a
+// range runs as whole 8- and 4-pair chunks (single pairs run with no loads in
+// flight behind them: 7-pair ranges measured about twice as slow per pair).
+int pp_range_pairs(int np, int splits) {
+  int pps = (np + splits - 1) / splits;
+  if (pps > 4) pps = (pps + 3) & ~3;
+  return pps;
+}
+
+template <int MB>
+hipError_t launch_pp(const GemmArgs& args, int splits, void* workspace, hipStream_t stream) {
+  PPSplit sk{1, args.k / 512, nullptr, nullptr};
+  if (splits <= 1) return launch_pp_cfg<MB, false>(args, sk, stream);
+  const int np = args.k / 512;
+  sk.pairs_per_split = pp_range_pairs(np, splits);
+  sk.splits = (np + sk.pairs_per_split - 1) / sk.pairs_per_split;   // no empty range
+  if (sk.splits <= 1) return launch_pp_cfg<MB, false>(args, sk, stream);
+  if (pp_tiles<MB>(args) > kPPMaxTiles) return hipErrorInvalidValue;
+  sk.counters = (int*)workspace;
+  sk.partials = (float*)((uint8_t*)workspace + kPPCounterBytes);
+  return launch_pp_cfg<MB, true>(args, sk, stream);
+}
+
 }  // namespace
 
 bool stream_supported(const GemmArgs& args) {
@@ -891,12 +1042,43 @@ hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream
   return launch_pre_cfg<Pre4>(args, stream);
 }
 
-hipError_t launch_gemm_both_prepacked(const GemmArgs& args, hipStream_t stream) {
+// Row blocks per tile of the both-prepacked kernel for m rows.
+static int pp_mb(int m) { return m <= 32 ? 1 : (m <= 64 ? 2 : 4); }
+
+int pp_effective_splits(int k, int splits) {
+  const int np = k / 512;
+  if (splits <= 1 || np <= 1) return 1;
+  const int pps = pp_range_pairs(np, splits);
+  return (np + pps - 1) / pps;
+}
+
+int pp_auto_splits(int m, int n, int k, int num_cus) {
+  const int mb = pp_mb(m);
+  const int64_t tiles = (int64_t)((m + 32 * mb - 1) / (32 * mb)) * ((n + kBN - 1) / kBN);
+  const int np = k / 512;
+  // enough K ranges to give most compute units a workgroup, each at least
+  // two pairs long, and at most 16
+  int s = (int)std::min<int64_t>(16, std::max<int64_t>(1, num_cus / std::max<int64_t>(1, tiles)));
+  s = std::min(s, std::max(1, np / 2));
+  if (tiles > kPPMaxTiles) s = 1;
+  return pp_effective_splits(k, s);
+}
+
+size_t pp_workspace_bytes(int m, int n, int k, int splits) {
+  const int s = pp_effective_splits(k, splits);
+  if (s <= 1) return 0;
+  const int mb = pp_mb(m);
+  const int64_t tiles = (int64_t)((m + 32 * mb - 1) / (32 * mb)) * ((n + kBN - 1) / kBN);
+  if (tiles > kPPMaxTiles) return 0;
+  return kPPCounterBytes + (size_t)tiles * s * (32 * mb) * kBN * sizeof(float);
+}
+
+hipError_t launch_gemm_both_prepacked(const GemmArgs& args, int splits, void* workspace, hipStream_t stream) {
   if (args.m <= 0 || args.n <= 0) return hipSuccess;
   if (args.k <= 0 || args.k % 512) return hipErrorInvalidValue;
-  if (args.m <= 32) return launch_pp_cfg<1>(args, stream);
-  if (args.m <= 64) return launch_pp_cfg<2>(args, stream);
-  return launch_pp_cfg<4>(args, stream);
+  if (args.m <= 32) return launch_pp<1>(args, splits, workspace, stream);
+  if (args.m <= 64) return launch_pp<2>(args, splits, workspace, stream);
+  return launch_pp<4>(args, splits, workspace, stream);
 }
 
 }  // namespace mxfp4

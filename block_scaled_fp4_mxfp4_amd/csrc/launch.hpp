@@ -86,8 +86,21 @@ hipError_t launch_prepack_weight(const uint8_t* b_q, const uint8_t* b_s, int n, 
                                  hipStream_t stream);
 hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream);
 // Both operands prepacked (a_q / a_s and b_q / b_s in the prepacked layout):
-// no LDS in the main loop.
-hipError_t launch_gemm_both_prepacked(const GemmArgs& args, hipStream_t stream);
+// no LDS in the main loop.  splits > 1: each output tile's K is cut into that
+// many ranges (fewer when K has fewer 512-K pairs) reduced through
+// `workspace` (pp_workspace_bytes; zero-filled before first use, left
+// zero-filled); hipErrorInvalidValue when the shape has more output tiles
+// than the workspace's counter region holds.
+hipError_t launch_gemm_both_prepacked(const GemmArgs& args, int splits, void* workspace, hipStream_t stream);
+// The K ranges a request for `splits` gives: ranges of ceil(pairs / splits)
+// 512-K pairs, rounded up to a multiple of 4 above 4 (at most `splits`, none
+// empty).
+int pp_effective_splits(int k, int splits);
+// The automatic choice: enough ranges to give most compute units a workgroup.
+int pp_auto_splits(int m, int n, int k, int num_cus);
+// Workspace bytes for `splits` (0 when the effective count is 1 or the shape
+// has too many output tiles for split-K).
+size_t pp_workspace_bytes(int m, int n, int k, int splits);
 
 // MoE steps around the grouped GEMM (include/mxfp4_moe.h).
 constexpr int kMoeMaxTopK = 8;          // routing: experts per token

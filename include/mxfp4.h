@@ -240,6 +240,39 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked_ab(const void* ap_q, const void* ap_s, co
                                           void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
 
 /*
+ * mxfp4_gemm_nt_prepacked_ab with K split over workgroups, for shapes with
+ * fewer 64-column output panels than compute units (the decode down
+ * projection, n = 4096: 64 panels).  The same GEMM ("Packed MXFP4 & NVFP4
+ * GEMM + mega-MoE" page, Summary: mxfp4_gemm_nt at its decode shapes; the
+ * quadbit README's serving section splits the down projection's K over more
+ * CTAs with an fp32 reduction to fill the machine).
+ *   splits    : 0 = automatic (enough K ranges to give most compute units a
+ *               workgroup, each at least 1024 K long; 1 when the panels
+ *               already fill the chip), 1 = no split (exactly
+ *               mxfp4_gemm_nt_prepacked_ab), else 2..16 requested ranges of
+ *               ceil(pairs / splits) 512-K pairs, rounded up to a multiple of
+ *               4 pairs when above 4 (so fewer ranges than asked may result,
+ *               none empty).  MXFP4_ERR_INVALID_ARG outside 0..16.
+ *   workspace : at least mxfp4_gemm_nt_prepacked_ab_workspace_size(m, n, k,
+ *               splits) bytes, 16-byte aligned, zero-filled before its first
+ *               use; every call leaves its first 64 KiB (the arrival
+ *               counters) zero again, so one workspace serves consecutive
+ *               stream-ordered calls of any shape.  Calls that may overlap
+ *               (other streams) need workspaces of their own.  NULL / 0 when
+ *               the size is 0 (MXFP4_ERR_WORKSPACE if too small).
+ * Each output is the sum of the ranges' fp32 partial sums in range order
+ * (deterministic, not bit-identical to the unsplit kernel), rounded once to
+ * the output type.  Split-K needs at most 16384 output tiles (64-column
+ * panels x 128-row tiles); MXFP4_ERR_INVALID_ARG beyond.  Other arguments as
+ * for mxfp4_gemm_nt_prepacked_ab.
+ */
+size_t mxfp4_gemm_nt_prepacked_ab_workspace_size(int64_t m, int64_t n, int64_t k, int32_t splits);
+
+mxfp4_status_t mxfp4_gemm_nt_prepacked_ab_ex(const void* ap_q, const void* ap_s, const void* bp_q, const void* bp_s,
+                                             void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                             int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel selection for tests and tuning.  mxfp4_gemm_nt chooses a kernel per
  * shape; mxfp4_gemm_nt_ex lets a caller force one so every kernel can be
  * checked on any shape.  `kernel` values:

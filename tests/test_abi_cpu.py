@@ -278,6 +278,26 @@ def test_row_per_workgroup_kernels_cap_rows(lib):
     assert b"2^24" in lib.mxfp4_last_error()
 
 
+def test_prepacked_split_k_arguments_on_host(lib):
+    f = _fake
+    ex = lib.mxfp4_gemm_nt_prepacked_ab_ex
+    assert ex(f(), f(), f(), f(), f(), 0, 128, 4096, 1000, 0, None, 0, None) == 1      # k % 512
+    assert ex(f(), f(), f(), f(), f(), 0, 128, 4096, 14336, 17, None, 0, None) == 1    # splits 0..16
+    assert b"splits must be 0..16" in lib.mxfp4_last_error()
+    assert ex(f(), f(), f(), f(), f(), 0, 128, 4096, 14336, -1, None, 0, None) == 1
+    assert ex(None, None, f(), f(), None, 0, 0, 4096, 14336, 4, None, 0, None) == 0    # empty: no-op
+    size = lib.mxfp4_gemm_nt_prepacked_ab_workspace_size
+    # 64 panels x 4 ranges of 7 pairs: the 64 KiB counter region + 4 fp32 128 x 64 tiles per panel
+    assert size(128, 4096, 14336, 4) == 65536 + 64 * 4 * 128 * 64 * 4
+    assert size(128, 4096, 14336, 1) == 0
+    # 2048 = 4 pairs: 3 ranges asked give ranges of 2 pairs, so two
+    assert size(64, 640, 2048, 3) == 65536 + 10 * 2 * 64 * 64 * 4
+    # automatic with no device: 256 compute units assumed; 224 panels need no split
+    assert size(128, 14336, 4096, 0) == 0
+    assert size(128, 4096, 14336, 0) == 65536 + 64 * 4 * 128 * 64 * 4
+    assert size(128, 4096, 14336, 17) == 0 and size(128, 4096, 1000, 4) == 0
+
+
 def test_prepacked_entry_points_reject_bad_arguments_on_host(lib):
     f = _fake
     cb, sb = ctypes.c_int64(), ctypes.c_int64()

@@ -4,6 +4,8 @@ The sampled full-size tests elsewhere check a few rows and columns; these
 compare the whole output of the benchmarked paths:
   * decode 128 x 14336 x 4096: A quantized into the prepacked layout, the
     weight prepacked, the both-prepacked decode GEMM (BF16 and fp32 output);
+  * the decode down projection 128 x 4096 x 14336 through the same path,
+    where the automatic choice splits K over four workgroups per panel;
   * prefill 4096 x 4096 x 4096: GPU quantize of both operands and the
     automatic GEMM (256x256 tiles), BF16 and fp32 output;
   * the 64-expert MoE layer: every element of the smallest non-empty and of
@@ -40,6 +42,24 @@ def test_decode_full_output():
     w = workloads.DECODE
     a, b = w.make()
     log(f"{w.name}: every output element, prepacked A and B")
+    bq, bs = mxfp4_quantize(b.to(dev))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    ap_q, ap_s = mxfp4_quantize_prepacked(a.to(dev))
+    c16 = mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, w.m, w.n, w.k, out_dtype=torch.bfloat16)
+    c32 = mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, w.m, w.n, w.k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oaq, oas = oracle.quantize(workloads.bf16_bits(a))
+    obq, obs = oracle.quantize(workloads.bf16_bits(b))
+    _check(_bf16_bits(c16), to_np(c32), oracle.gemm_nt(oaq, oas, obq, obs))
+
+
+def test_decode_down_split_k_full_output():
+    """The down projection at decode, 128 x 4096 x 14336: 64 column panels, so
+    the automatic choice splits K over four workgroups per panel."""
+    dev = device()
+    w = workloads.DECODE_DOWN
+    a, b = w.make()
+    log(f"{w.name}: every output element, prepacked A and B, automatic split-K")
     bq, bs = mxfp4_quantize(b.to(dev))
     bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
     ap_q, ap_s = mxfp4_quantize_prepacked(a.to(dev))

@@ -27,7 +27,9 @@ import workloads
 from block_scaled_fp4_mxfp4_amd import (MXFP4Error, mxfp4_gemm_nt, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,
                                         mxfp4_prepack_weight, mxfp4_prepacked_weight_size, mxfp4_quantize,
                                         mxfp4_quantize_prepacked)
-from tests.gpu_common import device, log, poisoned, random_bf16, random_codes, sampled_indices, to_np, upload
+from block_scaled_fp4_mxfp4_amd import binding
+from tests.gpu_common import (assert_bf16_matches_rounded, device, log, poisoned, random_bf16, random_codes,
+                              sampled_indices, to_np, upload)
 from tests.prepack_layout import prepack_numpy as _prepack_numpy
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +62,7 @@ def _both(aq, as_, bq, bs, dev, out_dtype):
     c_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
     mxfp4_gemm_nt_prepacked(a_q, a_s, bp_q, bp_s, n, c=c_all[:m])
     c2_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
-    mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, c=c2_all[:m])
+    mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, c=c2_all[:m], splits=1)
     ref = mxfp4_gemm_nt(a_q, a_s, b_q, b_s, out_dtype=out_dtype, kernel="stream")
     torch.cuda.synchronize()
     assert torch.all(c_all[m:].view(torch.uint8) == 0x7F), "write past C"
@@ -250,3 +252,98 @@ def test_prepacked_ab_decode_full_size_and_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.int16), s.view(torch.int16)), f"replay {rep}"
+
+
+# Split-K of the both-prepacked kernel: (m, n, k, splits).  K ranges of
+# ceil(pairs / splits) pairs, rounded up to a multiple of 4 above 4: 14336 / 4
+# -> 8 + 8 + 8 + 4; 14336 / 3 -> 12 + 12 + 4 (chunks 8 + 4); 2048 / 3 -> 2 + 2
+# (two ranges: fewer than asked); 8192 / 16 -> one pair each; 1536 / 2 -> 2 + 1
+# (a shorter last range); 5120 / 5 -> 2 each; 10240 / 3 -> 8 + 8 + 4; m = 200
+# and 130: two row tiles; n = 130 and 200: a ragged last panel; 0 = the
+# automatic choice.
+SPLIT_SHAPES = [(128, 640, 14336, 4), (40, 256, 14336, 3), (64, 320, 2048, 3), (1, 200, 8192, 16),
+                (33, 130, 1536, 2), (96, 64, 5120, 5), (200, 130, 2048, 4), (128, 130, 10240, 3),
+                (130, 192, 4096, 0), (17, 64, 4096, 0)]
+
+
+def _split_case(m, n, k, seed, dev):
+    a = random_bf16((m, k), seed, spread=3, outlier_frac=0.01)
+    b = random_bf16((n, k), seed + 1, spread=2)
+    aq, as_ = oracle.quantize(workloads.bf16_bits(a))
+    bq, bs = oracle.quantize(workloads.bf16_bits(b))
+    bp_q, bp_s = mxfp4_prepack_weight(upload(bq, dev), upload(bs, dev))
+    ap_q, ap_s = mxfp4_prepack_weight(upload(aq, dev), upload(as_, dev))
+    return (aq, as_, bq, bs), (ap_q, ap_s, bp_q, bp_s)
+
+
+@pytest.mark.parametrize("m,n,k,splits", SPLIT_SHAPES)
+def test_prepacked_ab_split_k_matches_oracle(m, n, k, splits):
+    """Every K split (including ranges fewer than asked and a shorter last range):
+    fp32 within 1e-5 of the float64 oracle, BF16 the nearest-even rounding of the
+    exact result, nothing written past C, the same bits on a second call, and the
+    workspace's arrival counters back at zero."""
+    dev = device()
+    log(f"split-K prepacked m={m} n={n} k={k} splits={splits}")
+    host, (ap_q, ap_s, bp_q, bp_s) = _split_case(m, n, k, 3 * m + n + k, dev)
+    lib = binding.load_library()
+    need = lib.mxfp4_gemm_nt_prepacked_ab_workspace_size(m, n, k, splits)
+    ws = torch.zeros(max(need, 65536) + 4096, dtype=torch.uint8, device=dev)
+    c64 = oracle.gemm_nt(*host)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        c_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
+        mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, c=c_all[:m], splits=splits, ws=ws)
+        again = mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m, n, k, out_dtype=out_dtype, splits=splits, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.all(c_all[m:].view(torch.uint8) == 0x7F), "write past C"
+        assert torch.all(ws[:65536] == 0), "arrival counters not returned to zero"
+        c = c_all[:m]
+        bits = torch.int32 if out_dtype == torch.float32 else torch.int16
+        assert torch.equal(c.view(bits), again.view(bits)), "split-K result not deterministic"
+        if out_dtype == torch.float32:
+            assert oracle.floored_max_rel(to_np(c).astype(np.float64), c64) <= 1e-5
+        else:
+            assert_bf16_matches_rounded(to_np(c.view(torch.int16)).view(np.uint16), c64)
+
+
+def test_prepacked_ab_split_k_workspace_reuse_and_graph():
+    """One zero-filled workspace serves consecutive calls of different shapes and
+    split counts; the split-K launch replayed from a HIP graph gives the eager
+    result on every replay (the counters reset in the kernel, no memset)."""
+    dev = device()
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=dev)
+    for idx, (m, n, k, splits) in enumerate([(128, 256, 4096, 8), (64, 640, 2048, 2), (1, 64, 14336, 14)]):
+        host, dev_ops = _split_case(m, n, k, 100 + idx, dev)
+        c = mxfp4_gemm_nt_prepacked_ab(*dev_ops, m, n, k, out_dtype=torch.float32, splits=splits, ws=ws)
+        torch.cuda.synchronize()
+        assert oracle.floored_max_rel(to_np(c).astype(np.float64), oracle.gemm_nt(*host)) <= 1e-5
+        assert torch.all(ws[:65536] == 0)
+    m, n, k = 128, 512, 8192
+    host, dev_ops = _split_case(m, n, k, 200, dev)
+    eager = mxfp4_gemm_nt_prepacked_ab(*dev_ops, m, n, k, splits=4, ws=ws)
+    c = torch.empty_like(eager)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        mxfp4_gemm_nt_prepacked_ab(*dev_ops, m, n, k, c=c, splits=4, ws=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mxfp4_gemm_nt_prepacked_ab(*dev_ops, m, n, k, c=c, splits=4, ws=ws)
+    for rep in range(3):
+        c.view(torch.uint8).fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.all(ws[:65536] == 0)
+
+
+def test_prepacked_ab_split_k_refusals():
+    dev = device()
+    _, dev_ops = _split_case(128, 64, 2048, 5, dev)
+    with pytest.raises(MXFP4Error):   # more than 16 ranges
+        mxfp4_gemm_nt_prepacked_ab(*dev_ops, 128, 64, 2048, splits=17)
+    small = torch.zeros(1024, dtype=torch.uint8, device=dev)
+    with pytest.raises(MXFP4Error):   # workspace too small
+        mxfp4_gemm_nt_prepacked_ab(*dev_ops, 128, 64, 2048, splits=4, ws=small)
