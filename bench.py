@@ -85,6 +85,10 @@ def w4a8_algorithmic_bytes(m, n, k, out_bytes=2):
     return m * k + m * k // 32 + n * k // 2 + n * k // 32 + m * n * out_bytes
 
 
+DETAIL_STEPS = 200    # calls timed for every line but the headline step (at least)
+DETAIL_WARMUP = 20
+
+
 def calls_per_replay(steps: int) -> int:
     """Calls per graph replay for `steps` timed calls: the largest divisor of
     `steps` that leaves at least four replays (samples), at most 64 calls; one
@@ -421,7 +425,7 @@ def measure_moe_layer(args, dev, us):
     lb = MoELayerBench(wm, dev)
     # at least 16 launches per graph replay (64 steps = 4 samples of 16): replays of only a few
     # short routing and permutation launches would add the replay gap to each of them
-    msteps = max(64, args.steps // 2)
+    msteps = max(64, args.detail_steps // 2)
     nbytes = lb.algorithmic_bytes()
     out = {"workload": wm.name, "steps": msteps, "rotating_input_sets": lb.sets_n,
            "step": "route + permute + scatter-quantize + grouped mxfp4 GEMM + combine",
@@ -504,7 +508,7 @@ def measure_producers(args, dev, us):
     out = {}
     for name, shape in (("rmsnorm", f"{pb.rows}x{pb.hidden}, residual add"),
                         ("swiglu", f"{pb.rows}x{pb.inter} from a {pb.rows}x{2 * pb.inter} gate|up buffer")):
-        t = pb.timed(getattr(pb, name), max(64, args.steps // 2), 4)
+        t = pb.timed(getattr(pb, name), max(64, args.detail_steps // 2), 4)
         gbs = nbytes[name] / (t["mean"] * 1e-3) / 1e9
         kname = f"{name}_quantize_kernel"
         out[name] = {"shape": shape, "us": us(t), "algorithmic_bytes": nbytes[name], "gbs": round(gbs, 1),
@@ -562,9 +566,9 @@ class NvBench:
 def measure_nvfp4(args, dev, w, us):
     eprint(f"[bench] NVFP4 on {w.name}")
     nb = NvBench(w, dev)
-    s = nb.timed(nb.step, args.steps, args.warmup)
-    g = nb.timed(nb.gemm, args.steps, args.warmup)
-    q = nb.timed(nb.quantize, args.steps, args.warmup)
+    s = nb.timed(nb.step, args.detail_steps, args.detail_warmup)
+    g = nb.timed(nb.gemm, args.detail_steps, args.detail_warmup)
+    q = nb.timed(nb.quantize, args.detail_steps, args.detail_warmup)
     tf = w.flops / (g["mean"] * 1e-3) / 1e12
     qbytes = w.m * w.k * 2 + w.m * (w.k // 2 + w.k // 16 + 4)
     out = {"workload": w.name,
@@ -737,9 +741,9 @@ def measure_w4a8(args, dev, w, us):
     out = {"dtype": "mxfp8 e4m3 x mxfp4 e2m1, e8m0 block scales, fp32 accumulate, bf16 out"}
     eprint(f"[bench] W4A8 on {w.name}")
     b = DenseBench(w, dev, "mxfp8")
-    s = b.timed(b.step, args.steps, args.warmup)
-    g = b.timed(b.gemm, args.steps, args.warmup)
-    q = b.timed(b.quantize, args.steps, args.warmup)
+    s = b.timed(b.step, args.detail_steps, args.detail_warmup)
+    g = b.timed(b.gemm, args.detail_steps, args.detail_warmup)
+    q = b.timed(b.quantize, args.detail_steps, args.detail_warmup)
     tf = w.flops / (g["mean"] * 1e-3) / 1e12
     qbytes = quant_algorithmic_bytes(w.m, w.k, 1.0)
     out["prefill"] = {
@@ -754,8 +758,8 @@ def measure_w4a8(args, dev, w, us):
     if args.secondary != "none":
         w2 = workloads.DENSE[args.secondary]
         b2 = DenseBench(w2, dev, "mxfp8")
-        s2 = b2.timed(b2.step, args.steps, args.warmup)
-        g2 = b2.timed(b2.gemm, args.steps, args.warmup)
+        s2 = b2.timed(b2.step, args.detail_steps, args.detail_warmup)
+        g2 = b2.timed(b2.gemm, args.detail_steps, args.detail_warmup)
         gbytes = w4a8_algorithmic_bytes(w2.m, w2.n, w2.k)
         gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
         out["decode"] = {
@@ -768,7 +772,7 @@ def measure_w4a8(args, dev, w, us):
     if args.moe != "none":
         wm = workloads.ALL[args.moe]
         mb = MoEBench(wm, dev, "mxfp8")
-        msteps = max(8, args.steps // 2)
+        msteps = max(16, args.detail_steps // 2)
         sm = mb.timed(mb.step, msteps, 2)
         gm = mb.timed(mb.gemm, msteps, 2)
         tfm = wm.flops / (gm["mean"] * 1e-3) / 1e12
@@ -791,9 +795,9 @@ def measure_large(args, dev):
     for wl in (workloads.FFN_DOWN, workloads.SQUARE8192):
         eprint(f"[bench] building inputs for {wl.name}")
         b = DenseBench(wl, dev)
-        s = b.timed(b.step, args.steps, args.warmup)
-        g = b.timed(b.gemm, args.steps, args.warmup)
-        q = b.timed(b.quantize, args.steps, args.warmup)
+        s = b.timed(b.step, args.detail_steps, args.detail_warmup)
+        g = b.timed(b.gemm, args.detail_steps, args.detail_warmup)
+        q = b.timed(b.quantize, args.detail_steps, args.detail_warmup)
         tf = wl.flops / (g["mean"] * 1e-3) / 1e12
         qbytes = quant_algorithmic_bytes(wl.m, wl.k)
         out[wl.name] = {
@@ -819,11 +823,11 @@ def measure_decode(args, dev, w2, primary: bool):
     eprint(f"[bench] building inputs for {w2.name}")
     b2 = DenseBench(w2, dev)
     pre = b2.prepacked
-    s2 = b2.timed(b2.step_prepacked_ab if pre else b2.step, args.steps, args.warmup)
-    g2 = b2.timed(b2.gemm_prepacked_ab if pre else b2.gemm, args.steps, args.warmup)
-    gb = b2.timed(b2.gemm_prepacked, args.steps, args.warmup) if pre else g2
-    gu = b2.timed(b2.gemm, args.steps, args.warmup) if pre else g2
-    q2 = b2.timed(b2.quantize_prepacked if pre else b2.quantize, args.steps, args.warmup)
+    s2 = b2.timed(b2.step_prepacked_ab if pre else b2.step, args.detail_steps, args.detail_warmup)
+    g2 = b2.timed(b2.gemm_prepacked_ab if pre else b2.gemm, args.detail_steps, args.detail_warmup)
+    gb = b2.timed(b2.gemm_prepacked, args.detail_steps, args.detail_warmup) if pre else g2
+    gu = b2.timed(b2.gemm, args.detail_steps, args.detail_warmup) if pre else g2
+    q2 = b2.timed(b2.quantize_prepacked if pre else b2.quantize, args.detail_steps, args.detail_warmup)
     gbytes = gemm_algorithmic_bytes(w2.m, w2.n, w2.k)
     qb2 = quant_algorithmic_bytes(w2.m, w2.k)
     gemm_gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
@@ -859,8 +863,8 @@ def measure_mxfp8(args, dev, w):
     the FP8 MFMA peak."""
     eprint(f"[bench] MXFP8 x MXFP8 on {w.name}")
     b = DenseBench(w, dev, "mxfp8x8")
-    s = b.timed(b.step, args.steps, args.warmup)
-    g = b.timed(b.gemm, args.steps, args.warmup)
+    s = b.timed(b.step, args.detail_steps, args.detail_warmup)
+    g = b.timed(b.gemm, args.detail_steps, args.detail_warmup)
     tf = w.flops / (g["mean"] * 1e-3) / 1e12
     out = {"workload": w.name, "dtype": "mxfp8 e4m3 x mxfp8 e4m3, e8m0 block scales, fp32 accumulate, bf16 out",
            "step": "quantize A (bf16->mxfp8) + mxfp8 x mxfp8 NT GEMM -> bf16 (B quantized to mxfp8 once)",
@@ -945,7 +949,7 @@ class FusedDecodeBench:
 def measure_fused_decode(args, dev):
     eprint("[bench] decode steps from the producer: quantization fused into RMSNorm / SwiGLU vs a separate launch")
     fb = FusedDecodeBench(dev)
-    steps = max(64, args.steps)
+    steps = max(64, args.detail_steps)
     out = {"rotating_input_sets": fb.sets_n, "steps": steps}
     for name, shape in (("up", "RMSNorm 128x4096 -> GEMM 128x14336x4096"),
                         ("down", "SwiGLU 128x14336 (gate|up 128x28672) -> GEMM 128x4096x14336")):
@@ -1048,6 +1052,12 @@ def main():
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="with --only gemm/quantize/step: both operands MXFP8 (the MXFP8 x MXFP8 GEMM)")
     args = ap.parse_args()
+    # The headline step is timed over exactly --steps calls; every other line
+    # (the step's kernels, decode, MoE, widenings, ceilings) over at least 200
+    # calls after at least 20 warm-ups, so that microsecond kernels are not
+    # timed in replays of a handful of calls whatever --steps is.
+    args.detail_steps = max(args.steps, DETAIL_STEPS)
+    args.detail_warmup = max(args.warmup, DETAIL_WARMUP)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         eprint("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -1072,10 +1082,10 @@ def main():
     bench = DenseBench(w, dev, quantize_b_in_step=True)
     eprint(f"[bench] {bench.sets_n} rotating input sets of {bench.per_set_bytes / 2**20:.1f} MiB")
     step = bench.timed(bench.step, args.steps, args.warmup)
-    gemm = bench.timed(bench.gemm, args.steps, args.warmup)
-    quant = bench.timed(bench.quantize, args.steps, args.warmup)
-    quant_b = bench.timed(bench.quantize_b, args.steps, args.warmup)
-    step_ab = bench.timed(bench.step_quantize_both, args.steps, args.warmup)
+    gemm = bench.timed(bench.gemm, args.detail_steps, args.detail_warmup)
+    quant = bench.timed(bench.quantize, args.detail_steps, args.detail_warmup)
+    quant_b = bench.timed(bench.quantize_b, args.detail_steps, args.detail_warmup)
+    step_ab = bench.timed(bench.step_quantize_both, args.detail_steps, args.detail_warmup)
     eprint(f"[bench] step {step['mean']*1e3:.2f} us, gemm {gemm['mean']*1e3:.2f} us, "
            f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us, "
            f"step quantizing both operands {step_ab['mean']*1e3:.2f} us")
@@ -1093,6 +1103,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "detail_steps": args.detail_steps,
         "ms_per_step": round(step["mean"], 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -1132,7 +1143,7 @@ def main():
         wm = workloads.ALL[args.moe]
         eprint(f"[bench] building inputs for {wm.name}")
         mb = MoEBench(wm, dev)
-        msteps = max(8, args.steps // 2)
+        msteps = max(16, args.detail_steps // 2)
         sm = mb.timed(mb.step, msteps, 2)
         gm = mb.timed(mb.gemm, msteps, 2)
         qm = mb.timed(mb.quantize, msteps, 2)
@@ -1185,7 +1196,7 @@ def main():
     if not args.no_ceilings:
         eprint("[bench] measuring MFMA and streaming-read ceilings with the probe kernels")
         cl = Ceilings(dev)
-        ceil = cl.measure(args.steps)
+        ceil = cl.measure(args.detail_steps)
         del cl
         ceil["gemm_frac_of_mfma_ceiling"] = round(gemm_tflops / ceil["mfma_fp4_tflops_short"], 4)
         if "w4a8" in result:

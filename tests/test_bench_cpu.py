@@ -83,3 +83,12 @@ def test_inputs_record_names_seeds_and_digests():
     mrec = bench.moe_inputs_record(small)
     assert set(mrec["sha256"]) == {"x_bf16", "logits_f32", "w_bf16", "offsets_i32"}
     assert mrec["seeds"]["route_noise"] == 900 + workloads.ROLE_ROUTE_NOISE
+
+
+def test_detail_lines_are_timed_over_at_least_200_calls():
+    """Only the headline step follows --steps; the other lines time at least
+    DETAIL_STEPS calls (so --steps 20 does not time microsecond kernels in
+    replays of five calls)."""
+    import bench
+    assert bench.DETAIL_STEPS >= 200 and bench.DETAIL_WARMUP >= 20
+    assert bench.calls_per_replay(max(20, bench.DETAIL_STEPS)) >= 50
