@@ -444,12 +444,14 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked_ab_ex(const void* ap_q, const void* ap_s,
   MXFP4_TRY(check_ptr(bp_q, "bp_q"));
   MXFP4_TRY(check_ptr(bp_s, "bp_s"));
   MXFP4_TRY(check_ptr(c, "c"));
+  // an explicit split of a shape with too many output tiles is refused before any device call
+  if (splits > 1 && mxfp4::pp_effective_splits((int)k, splits) > 1 &&
+      mxfp4::pp_workspace_bytes((int)m, (int)n, (int)k, splits) == 0)
+    return fail(MXFP4_ERR_INVALID_ARG, "split-K supports at most 16384 output tiles (64-column panels x row tiles)");
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   const int s = splits == 0 ? mxfp4::pp_auto_splits((int)m, (int)n, (int)k, dev.num_cus) : splits;
   const size_t need = mxfp4::pp_workspace_bytes((int)m, (int)n, (int)k, s);
-  if (s > 1 && mxfp4::pp_effective_splits((int)k, s) > 1 && need == 0)
-    return fail(MXFP4_ERR_INVALID_ARG, "split-K supports at most 16384 output tiles (64-column panels x row tiles)");
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(MXFP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

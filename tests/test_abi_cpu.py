@@ -296,6 +296,11 @@ def test_prepacked_split_k_arguments_on_host(lib):
     assert size(128, 14336, 4096, 0) == 0
     assert size(128, 4096, 14336, 0) == 65536 + 64 * 4 * 128 * 64 * 4
     assert size(128, 4096, 14336, 17) == 0 and size(128, 4096, 1000, 4) == 0
+    # split-K needs at most 16384 output tiles (one arrival counter each in the 64 KiB region)
+    assert size(128, 64 * 16384, 4096, 4) == 65536 + 16384 * 4 * 128 * 64 * 4
+    assert size(128, 64 * 16385, 4096, 4) == 0
+    assert ex(f(), f(), f(), f(), f(), 0, 128, 64 * 16385, 4096, 4, None, 0, None) == 1
+    assert b"at most 16384 output tiles" in lib.mxfp4_last_error()
 
 
 def test_prepacked_entry_points_reject_bad_arguments_on_host(lib):
