@@ -166,15 +166,18 @@ class DenseBench:
         self.per_set_bytes = per_set
         self.sets = []
         # the small-M workloads also keep each weight copy prepacked for mxfp4_gemm_nt_prepacked
+        # (and, with MXFP8 activations, for mxfp8_gemm_w4a8_nt_prepacked)
         self.prepacked = act == "mxfp4" and m <= 128 and k % 512 == 0
+        self.prepacked_b = act in ("mxfp4", "mxfp8") and m <= 128 and k % 512 == 0
         for _ in range(self.sets_n):
             st = dict(a=a_d.clone(), aq=torch.empty((m, k_a), dtype=torch.uint8, device=dev),
                       as_=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
                       bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev))
             if self.with_b:
                 st["b"] = b_d.clone()
-            if self.prepacked:
+            if self.prepacked_b:
                 st["bp_q"], st["bp_s"] = B.mxfp4_prepack_weight(st["bq"], st["bs"])
+            if self.prepacked:
                 cb, sb = B.mxfp4_prepacked_weight_size(m, k)
                 st["ap_q"] = torch.empty(cb, dtype=torch.uint8, device=dev)
                 st["ap_s"] = torch.empty(sb, dtype=torch.uint8, device=dev)
@@ -214,6 +217,14 @@ class DenseBench:
     def gemm_prepacked(self, i):
         s = self.sets[i % self.sets_n]
         self.B.mxfp4_gemm_nt_prepacked(s["aq"], s["as_"], s["bp_q"], s["bp_s"], self.w.n, c=s["c"])
+
+    def gemm_w4a8_prepacked(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp8_gemm_w4a8_nt_prepacked(s["aq"], s["as_"], s["bp_q"], s["bp_s"], self.w.n, c=s["c"])
+
+    def step_w4a8_prepacked(self, i):
+        self.quantize(i)
+        self.gemm_w4a8_prepacked(i)
 
     def step(self, i):
         self.quantize(i)
@@ -758,16 +769,25 @@ def measure_w4a8(args, dev, w, us):
     if args.secondary != "none":
         w2 = workloads.DENSE[args.secondary]
         b2 = DenseBench(w2, dev, "mxfp8")
-        s2 = b2.timed(b2.step, args.detail_steps, args.detail_warmup)
-        g2 = b2.timed(b2.gemm, args.detail_steps, args.detail_warmup)
+        pre = b2.prepacked_b
+        # with the weight held prepacked: the prepacked-weight kernel; the streaming
+        # kernel on the row-major weight timed beside it
+        s2 = b2.timed(b2.step_w4a8_prepacked if pre else b2.step, args.detail_steps, args.detail_warmup)
+        g2 = b2.timed(b2.gemm_w4a8_prepacked if pre else b2.gemm, args.detail_steps, args.detail_warmup)
+        gu = b2.timed(b2.gemm, args.detail_steps, args.detail_warmup) if pre else g2
         gbytes = w4a8_algorithmic_bytes(w2.m, w2.n, w2.k)
         gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
         out["decode"] = {
             "workload": w2.name, "step_us": us(s2), "gemm_us": us(g2),
+            "step": ("quantize A to MXFP8 + W4A8 GEMM on the prepacked weight" if pre
+                     else "quantize A to MXFP8 + streaming W4A8 GEMM"),
+            "gemm_unpacked_weight_us": us(gu),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4)},
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "kernel": "gemm_stream_pre_kernel (fp8 A)" if pre else "gemm_stream_kernel (fp8 A)"},
         }
-        eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s)")
+        eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s; "
+               f"row-major weight {gu['mean']*1e3:.2f} us)")
         del b2
     if args.moe != "none":
         wm = workloads.ALL[args.moe]
@@ -1030,6 +1050,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "gemm_prepacked_ab",
+                                       "gemm_w4a8_prepacked",
                                        "step_prepacked_ab", "quantize_prepacked", "quantize", "quantize_b", "copy",
                                        "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu",
                                        "probe_mfma", "probe_mfma_w4a8", "step_quantize_both"],

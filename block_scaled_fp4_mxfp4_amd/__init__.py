@@ -8,7 +8,7 @@ behind a C ABI (include/mxfp4.h, include/mxfp8.h, include/mxfp4_moe.h,
 include/mxfp4_producers.h, include/nvfp4.h).  The Python layer is a thin ctypes binding."""
 from .binding import (  # noqa: F401
     MXFP4Error, load_library, mxfp4_quantize, mxfp8_quantize, mxfp4_gemm_nt, mxfp4_grouped_gemm_nt, workspace,
-    mxfp8_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt, mxfp8_gemm_nt,
+    mxfp8_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt, mxfp8_gemm_nt, mxfp8_gemm_w4a8_nt_prepacked,
     mxfp4_moe_route, mxfp4_moe_permute, mxfp4_moe_quantize_scatter, mxfp8_moe_quantize_scatter, mxfp4_moe_combine,
     mxfp4_rmsnorm_quantize, mxfp4_swiglu_quantize, nvfp4_quantize, nvfp4_gemm_nt,
     mxfp4_prepacked_weight_size, mxfp4_prepack_weight, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,

@@ -33,7 +33,7 @@ EXPORTED = (
     "mxfp4_prepacked_weight_size", "mxfp4_prepack_weight", "mxfp4_gemm_nt_prepacked", "mxfp4_gemm_nt_prepacked_ab",
     "mxfp4_gemm_nt_prepacked_ab_ex", "mxfp4_gemm_nt_prepacked_ab_workspace_size",
     "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex", "mxfp4_gemm_nt_ex_noalloc",
-    "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked",
+    "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp8_gemm_w4a8_nt.restype = ctypes.c_int
         lib.mxfp8_gemm_w4a8_nt.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp8_gemm_w4a8_nt_prepacked.restype = ctypes.c_int
+        lib.mxfp8_gemm_w4a8_nt_prepacked.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp8_gemm_w4a8_nt_ex.restype = ctypes.c_int
         lib.mxfp8_gemm_w4a8_nt_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp]
         lib.mxfp8_gemm_nt.restype = ctypes.c_int
@@ -387,6 +389,21 @@ def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, ke
     c, code = _out(c, m, n, out_dtype, a_q8.device)
     _check(lib.mxfp8_gemm_w4a8_nt_ex(_ptr(a_q8), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(c), code, m, n, k,
                                      KERNELS[kernel], _stream(stream)))
+    return c
+
+
+def mxfp8_gemm_w4a8_nt_prepacked(a_q8, a_s, bp_q, bp_s, n: int, c=None, out_dtype=torch.bfloat16, stream=None):
+    """W4A8 C[m, n] = A[m, k] . B^T with A in MXFP8 and B prepacked (mxfp4_prepack_weight)."""
+    lib = load_library()
+    m, k = a_q8.shape
+    _require(a_q8, "a_q8", torch.uint8, (m, k))
+    _require(a_s, "a_s", torch.uint8, (m, k // 32))
+    cb, sb = mxfp4_prepacked_weight_size(n, k)
+    _require(bp_q, "bp_q", torch.uint8, (cb,))
+    _require(bp_s, "bp_s", torch.uint8, (sb,))
+    c, code = _out(c, m, n, out_dtype, a_q8.device)
+    _check(lib.mxfp8_gemm_w4a8_nt_prepacked(_ptr(a_q8), _ptr(a_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n, k,
+                                            _stream(stream)))
     return c
 
 

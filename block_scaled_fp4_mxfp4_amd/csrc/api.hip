@@ -405,6 +405,37 @@ mxfp4_status_t mxfp4_gemm_nt_prepacked(const void* a_q, const void* a_s, const v
   return hip_status(mxfp4::launch_gemm_stream_prepacked(args, (hipStream_t)stream), "prepacked gemm launch");
 }
 
+mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked(const void* a_q8, const void* a_s, const void* bp_q, const void* bp_s,
+                                            void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                            void* stream) {
+  if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
+  MXFP4_TRY(check_k(k));
+  if (k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(a_q8, "a_q8"));
+  MXFP4_TRY(check_ptr(a_s, "a_s"));
+  MXFP4_TRY(check_ptr(bp_q, "bp_q"));
+  MXFP4_TRY(check_ptr(bp_s, "bp_s"));
+  MXFP4_TRY(check_ptr(c, "c"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q8;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)bp_q;
+  args.b_s = (const uint8_t*)bp_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  return hip_status(mxfp4::launch_gemm_w4a8_stream_prepacked(args, (hipStream_t)stream),
+                    "prepacked w4a8 gemm launch");
+}
+
 mxfp4_status_t mxfp4_quantize_prepacked(const void* x_bf16, int64_t rows, int64_t k, void* ap_q, void* ap_s,
                                         void* stream) {
   int64_t cb, sb;

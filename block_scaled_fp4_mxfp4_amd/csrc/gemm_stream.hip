@@ -463,15 +463,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint8_t* ba
 template <class C>
 __device__ __forceinline__ void make_pre_copies(PreCopies<C>& cp, const GemmArgs& args, int m0, int tn, int np,
                                                 int w, int lane) {
-  const int kb = args.k / 2, ks = args.k / 32;
+  const int ka = C::A8 ? args.k : args.k / 2, ks = args.k / 32;   // A bytes per row
   const int rows = min(C::BM, args.m - m0);
-  cp.code = uniform_rsrc(args.a_q + (int64_t)m0 * kb, (uint32_t)rows * kb);
+  cp.code = uniform_rsrc(args.a_q + (int64_t)m0 * ka, (uint32_t)rows * ka);
 #pragma unroll
   for (int j = 0; j < C::CODE_LOADS; ++j) {
     const int slot = (j * 4 + w) * 64 + lane;
-    const int r = slot >> 3;
-    const int lc = (slot & 7) ^ swz(r);
-    cp.code_off[j] = (uint32_t)min(r, rows - 1) * kb + lc * 16;
+    const int r = slot >> C::A_SHIFT;
+    const int lc = (slot & ((1 << C::A_SHIFT) - 1)) ^ (C::A8 ? (r & 15) : swz(r));
+    cp.code_off[j] = (uint32_t)min(r, rows - 1) * ka + lc * 16;
   }
   if (w == 3) {
     cp.scale = uniform_rsrc(args.b_s + (int64_t)tn * np * kPreScaleBlock, (uint32_t)np * kPreScaleBlock);
@@ -491,7 +491,7 @@ __device__ __forceinline__ void copy_pair_pre(uint8_t MXFP4_LDS* buf, const PreC
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int j = 0; j < C::CODE_LOADS; ++j)
-      buf2lds_16(cp.code, cp.code_off[j], (uint32_t)(2 * p + s) * kRowBytes,
+      buf2lds_16(cp.code, cp.code_off[j], (uint32_t)(2 * p + s) * C::A_ROW,
                  (MXFP4_LDS void*)(buf + s * C::STAGE + (j * 4 + w) * 64 * 16));
   buf2lds_16(cp.scale, cp.scale_off, (uint32_t)p * cp.scale_step, (MXFP4_LDS void*)(buf + 2 * C::STAGE + w * 64 * 16));
 }
@@ -573,12 +573,26 @@ __device__ __forceinline__ v16f mfma32_fp4_sel(v4i a, v4i b, v16f acc, int sa, i
                                                          OPSEL_A, sa, OPSEL_B, sb);
 }
 
+// The same with the second operand in FP8 E4M3 (W4A8: 32 codes per lane, as
+// mfma32_fp4_fp8).
+template <int OPSEL_A, int OPSEL_B>
+__device__ __forceinline__ v16f mfma32_fp4_fp8_sel(v4i a, v8i b, v16f acc, int sa, int sb) {
+  v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, acc, kMfmaFmtFp4, kMfmaFmtFp8,
+                                                         OPSEL_A, sa, OPSEL_B, sb);
+}
+
 template <class C, int S>
 __device__ __forceinline__ void mma_pre(const Step<C>& st, const BPair& b, int bsc, v16f (&acc)[C::MB][2]) {
 #pragma unroll
   for (int i = 0; i < C::MB; ++i) {
-    acc[i][0] = mfma32_fp4_sel<2 * S, 0>(b.q[2 * S], st.a[i], acc[i][0], bsc, st.sa[i]);
-    acc[i][1] = mfma32_fp4_sel<2 * S + 1, 0>(b.q[2 * S + 1], st.a[i], acc[i][1], bsc, st.sa[i]);
+    if constexpr (C::A8) {
+      acc[i][0] = mfma32_fp4_fp8_sel<2 * S, 0>(b.q[2 * S], st.a[i], acc[i][0], bsc, st.sa[i]);
+      acc[i][1] = mfma32_fp4_fp8_sel<2 * S + 1, 0>(b.q[2 * S + 1], st.a[i], acc[i][1], bsc, st.sa[i]);
+    } else {
+      acc[i][0] = mfma32_fp4_sel<2 * S, 0>(b.q[2 * S], st.a[i], acc[i][0], bsc, st.sa[i]);
+      acc[i][1] = mfma32_fp4_sel<2 * S + 1, 0>(b.q[2 * S + 1], st.a[i], acc[i][1], bsc, st.sa[i]);
+    }
   }
 }
 
@@ -641,7 +655,7 @@ __device__ __forceinline__ void pre_chunk(uint8_t MXFP4_LDS* lds, const PreCopie
 // both rings refill at each chunk boundary.
 template <class C>
 __global__ __launch_bounds__(kThreads) void gemm_stream_pre_kernel(GemmArgs args, int tiles_m, int tiles_n) {
-  static_assert(C::PRE && !C::A8, "prepacked-B configuration");
+  static_assert(C::PRE, "prepacked-B configuration");
   static_assert(kPreDepth >= C::NP, "B runs at least as far ahead as A");
   static_assert((C::NP - 1) * C::PAIR_LOADS + (kPreDepth - 1) * kPreBLoads <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1071,6 +1085,18 @@ size_t pp_workspace_bytes(int m, int n, int k, int splits) {
   const int64_t tiles = (int64_t)((m + 32 * mb - 1) / (32 * mb)) * ((n + kBN - 1) / kBN);
   if (tiles > kPPMaxTiles) return 0;
   return kPPCounterBytes + (size_t)tiles * s * (32 * mb) * kBN * sizeof(float);
+}
+
+hipError_t launch_gemm_w4a8_stream_prepacked(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (!stream_supported(args)) return hipErrorInvalidValue;
+  // FP8 A rows are twice as long: a 128-row tile fits two pairs of A in LDS
+  using Pre1 = StreamCfg<1, 4, true, true>;
+  using Pre2 = StreamCfg<2, 4, true, true>;
+  using Pre4 = StreamCfg<4, 2, true, true>;
+  if (args.m <= 32) return launch_pre_cfg<Pre1>(args, stream);
+  if (args.m <= 64) return launch_pre_cfg<Pre2>(args, stream);
+  return launch_pre_cfg<Pre4>(args, stream);
 }
 
 hipError_t launch_gemm_both_prepacked(const GemmArgs& args, int splits, void* workspace, hipStream_t stream) {

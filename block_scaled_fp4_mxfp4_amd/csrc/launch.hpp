@@ -85,6 +85,9 @@ void prepacked_sizes(int64_t n, int64_t k, int64_t* code_bytes, int64_t* scale_b
 hipError_t launch_prepack_weight(const uint8_t* b_q, const uint8_t* b_s, int n, int k, uint8_t* bp_q, uint8_t* bp_s,
                                  hipStream_t stream);
 hipError_t launch_gemm_stream_prepacked(const GemmArgs& args, hipStream_t stream);
+// W4A8 on a prepacked weight: A in MXFP8 (a_q [m, k] E4M3 codes) through the
+// LDS ring, B prepacked into registers; k % 512 == 0, 16-byte aligned scales.
+hipError_t launch_gemm_w4a8_stream_prepacked(const GemmArgs& args, hipStream_t stream);
 // Both operands prepacked (a_q / a_s and b_q / b_s in the prepacked layout):
 // no LDS in the main loop.  splits > 1: each output tile's K is cut into that
 // many ranges (fewer when K has fewer 512-K pairs) reduced through

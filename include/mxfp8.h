@@ -84,6 +84,22 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt_ex(const void* a_q8, const void* a_s, const vo
                                      void* stream);
 
 /*
+ * mxfp8_gemm_w4a8_nt on a prepacked weight: bp_q / bp_s are B rearranged by
+ * mxfp4_prepack_weight (include/mxfp4.h), so each wave loads B straight into
+ * registers; A (MXFP8) goes through LDS as in the streaming kernel, in
+ * 128-row tiles for m up to 128 (one workgroup per 64 columns: a single
+ * round of workgroups at the decode shape).  The same numerics and, output
+ * for output, the same result bit for bit as mxfp8_gemm_w4a8_nt_ex with
+ * MXFP4_KERNEL_STREAM (same per-wave K split, MFMA order and reduction).
+ * a_q8, a_s: A as in mxfp8_gemm_w4a8_nt, 16-byte aligned; c: [m, n] of type
+ * c_type, 16-byte aligned; k a positive multiple of 512, at most 2^24
+ * (MXFP4_ERR_INVALID_ARG otherwise).  No workspace; one kernel launch.
+ */
+mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked(const void* a_q8, const void* a_s, const void* bp_q, const void* bp_s,
+                                            void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k,
+                                            void* stream);
+
+/*
  * MXFP8 x MXFP8 NT GEMM: C[m][n] = sum_k A[m][k] * B[n][k] with both operands
  * in MXFP8 ("fp4_quantization" page, Functions: block_scaled_matmul, the
  * block-scaled matmul over MXFP4 / MXFP8 operands; its quantizer

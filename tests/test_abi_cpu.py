@@ -303,6 +303,17 @@ def test_prepacked_split_k_arguments_on_host(lib):
     assert b"at most 16384 output tiles" in lib.mxfp4_last_error()
 
 
+def test_w4a8_prepacked_rejects_bad_arguments_on_host(lib):
+    f = _fake
+    g = lib.mxfp8_gemm_w4a8_nt_prepacked
+    assert g(f(), f(), f(), f(), f(), 0, 4, 64, 992, None) == 1           # k % 512
+    assert b"multiple of 512" in lib.mxfp4_last_error()
+    assert g(f(), f(), f(), f(), f(), 3, 4, 64, 512, None) == 1           # output type
+    assert g(f(), f(), None, f(), f(), 0, 4, 64, 512, None) == 1          # null bp_q
+    assert g(f(), f(), f(), f(), f(), 0, -1, 64, 512, None) == 1
+    assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0        # empty: no-op
+
+
 def test_prepacked_entry_points_reject_bad_arguments_on_host(lib):
     f = _fake
     cb, sb = ctypes.c_int64(), ctypes.c_int64()

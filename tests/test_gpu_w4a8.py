@@ -36,8 +36,8 @@ import torch
 
 import oracle
 import workloads
-from block_scaled_fp4_mxfp4_amd import (mxfp4_quantize, mxfp8_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt,
-                                        mxfp8_quantize)
+from block_scaled_fp4_mxfp4_amd import (mxfp4_prepack_weight, mxfp4_quantize, mxfp8_gemm_w4a8_nt,
+                                        mxfp8_gemm_w4a8_nt_prepacked, mxfp8_grouped_gemm_w4a8_nt, mxfp8_quantize)
 from tests.gpu_common import device, log, poisoned, random_bf16, random_codes, sampled_indices, to_np, upload
 
 pytestmark = pytest.mark.gpu
@@ -254,6 +254,45 @@ def test_w4a8_kernels_agree_and_stream_rejects_unsupported_k():
     aq2, as2, bq2, bs2 = (upload(t, dev) for t in _quantized_operands(8, 64, 1056, 3))
     with pytest.raises(MXFP4Error):
         mxfp8_gemm_w4a8_nt(aq2, as2, bq2, bs2, kernel="stream")
+
+
+# the W4A8 GEMM on a prepacked weight: 32-, 64- and 128-row A tiles (two pairs of
+# FP8 A in LDS at 128 rows), K in chunks of 8, 4 and 1 pairs, ragged M and N
+PREPACKED_SHAPES = [(1, 64, 512), (17, 200, 1024), (32, 1000, 4096), (33, 70, 512), (64, 129, 8192),
+                    (100, 512, 2048), (128, 320, 4096), (128, 192, 4608), (129, 66, 1536), (200, 190, 14336),
+                    (128, 14336, 512)]
+
+
+@pytest.mark.parametrize("shape", PREPACKED_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in PREPACKED_SHAPES])
+def test_w4a8_prepacked_weight_matches_stream_kernel(shape):
+    """Bit-identical to the streaming kernel (same per-wave K split, MFMA order
+    and reduction) in fp32 and BF16, within the derived bound of the oracle,
+    nothing written past C."""
+    dev = device()
+    m, n, k = shape
+    log(f"w4a8 prepacked weight {shape}")
+    aq, as_, bq, bs = _quantized_operands(m, n, k, 3 * m + n)
+    d_aq, d_as, d_bq, d_bs = (upload(t, dev) for t in (aq, as_, bq, bs))
+    bp_q, bp_s = mxfp4_prepack_weight(d_bq, d_bs)
+    for out_dtype, bits in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        c_all = poisoned((m + 1, n), out_dtype, dev, 0x7F)
+        mxfp8_gemm_w4a8_nt_prepacked(d_aq, d_as, bp_q, bp_s, n, c=c_all[:m])
+        ref = mxfp8_gemm_w4a8_nt(d_aq, d_as, d_bq, d_bs, out_dtype=out_dtype, kernel="stream")
+        torch.cuda.synchronize()
+        assert torch.all(c_all[m:].view(torch.uint8) == 0x7F), "write past C"
+        assert torch.equal(c_all[:m].view(bits), ref.view(bits)), f"{out_dtype} differs from the streaming kernel"
+        if out_dtype == torch.float32:
+            _check_general(to_np(c_all[:m]), None, oracle.gemm_w4a8_nt(aq, as_, bq, bs),
+                           w4a8_tolerance(aq, as_, bq, bs))
+
+
+def test_w4a8_prepacked_rejects_bad_k():
+    from block_scaled_fp4_mxfp4_amd import MXFP4Error
+    dev = device()
+    aq, as_, bq, bs = (upload(t, dev) for t in _quantized_operands(8, 64, 1024, 3))
+    bp_q, bp_s = mxfp4_prepack_weight(bq, bs)
+    with pytest.raises(MXFP4Error):   # the weight is prepacked for k = 1024; A claims 992
+        mxfp8_gemm_w4a8_nt_prepacked(aq[:, :992].contiguous(), as_[:, :31].contiguous(), bp_q, bp_s, 64)
 
 
 def test_w4a8_empty_problems():
