@@ -127,7 +127,7 @@ def _sanitized_segments(offsets, total):
     return [(int(run[g]), int(max(run[g], c[g + 1]))) for g in range(len(offsets) - 1)]
 
 
-@pytest.mark.parametrize("case", ["few_groups", "across_chunks"])
+@pytest.mark.parametrize("case", ["few_groups", "across_chunks", "persistent"])
 def test_grouped_malformed_offsets_give_disjoint_segments(case):
     """Offsets are only sanitized on the device (the host cannot read them without
     a sync): clamped into [0, total_m] and replaced by their running maximum.
@@ -139,6 +139,11 @@ def test_grouped_malformed_offsets_give_disjoint_segments(case):
         total, n, k = 300, 96, 512
         # clamped: 0, 120, 80, 300, 300 -> segments [0,120), [120,120), [120,300), [300,300)
         offsets = np.array([-5, 120, 80, 500, 300], np.int32)
+    elif case == "persistent":
+        # 256 x 256 tiles with k % 1024 == 0: the persistent tile loop; clamped and
+        # running max: 0, 500, 500, 1200, 1200 -> [0,500), [500,500), [500,1200), [1200,1200)
+        total, n, k = 1200, 300, 1024
+        offsets = np.array([-5, 500, 300, 1400, 1200], np.int32)
     else:
         # 70 groups (two 64-group chunks), a drop inside each chunk and one at the chunk edge
         total, n, k = 700, 64, 256
