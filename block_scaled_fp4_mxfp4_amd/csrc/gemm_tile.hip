@@ -792,10 +792,16 @@ __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int groups, 
   return __builtin_amdgcn_readfirstlane(cnt);   // uniform: keep it (and what follows) in scalar registers
 }
 
+// An expert's share of the m-tiles: m-tiles [first, first + cnt) over its
+// sanitized rows [lo, hi).
+struct ExpertTiles {
+  int g, first, cnt, lo, hi;
+};
+
 // Finds the expert owning global m-tile `mt` (m-tiles are counted expert by
 // expert, ceil(rows_g / BM) per expert, over the segments of chunk_rows).
-__device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, int total_m, int bm,
-                                           int mt, int& g_out, RowRange& ar) {
+__device__ __forceinline__ bool find_expert(const int32_t* offsets, int groups, int total_m, int bm, int mt,
+                                            ExpertTiles& e) {
   const int lane = threadIdx.x & 63;
   int carry = 0, carry_rows = 0;
   for (int base = 0; base < groups; base += 64) {
@@ -818,18 +824,28 @@ __device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, i
       // (a per-lane resource wraps every copy in a waterfall loop: measured
       // 10 % slower on the MoE layer)
       const int src = __ffsll((long long)mask) - 1;
-      g_out = __builtin_amdgcn_readfirstlane(__shfl(g, src, 64));
-      const int glo = __builtin_amdgcn_readfirstlane(__shfl(lo, src, 64));
-      const int ghi = __builtin_amdgcn_readfirstlane(__shfl(hi, src, 64));
-      const int first = carry + __builtin_amdgcn_readfirstlane(__shfl(excl, src, 64));
-      ar.lo = glo + (mt - first) * bm;
-      ar.end = min(ghi, ar.lo + bm);
-      ar.last = ar.end - 1;
+      e.g = __builtin_amdgcn_readfirstlane(__shfl(g, src, 64));
+      e.lo = __builtin_amdgcn_readfirstlane(__shfl(lo, src, 64));
+      e.hi = __builtin_amdgcn_readfirstlane(__shfl(hi, src, 64));
+      e.cnt = __builtin_amdgcn_readfirstlane(__shfl(cnt, src, 64));
+      e.first = carry + __builtin_amdgcn_readfirstlane(__shfl(excl, src, 64));
       return true;
     }
     carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
   }
   return false;
+}
+
+// The expert and row range of global m-tile `mt`.
+__device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, int total_m, int bm,
+                                           int mt, int& g_out, RowRange& ar) {
+  ExpertTiles e;
+  if (!find_expert(offsets, groups, total_m, bm, mt, e)) return false;
+  g_out = e.g;
+  ar.lo = e.lo + (mt - e.first) * bm;
+  ar.end = min(e.hi, ar.lo + bm);
+  ar.last = ar.end - 1;
+  return true;
 }
 
 // The grid is a multiple of 8 workgroups covering at least every possible
@@ -1058,9 +1074,14 @@ __global__ __launch_bounds__(C::THREADS) void gemm_persistent_kernel(GemmArgs ar
   persistent_loop<C>(args, lo + slot, per_wg, hi, job_of, (uint8_t MXFP4_LDS*)smem);
 }
 
-// Grouped persistent kernel: the real tiles (counted from the sanitized
-// offsets) split evenly over the 8 XCDs as contiguous ranges, as in
-// grouped_tile_kernel, and each XCD's range dealt round-robin to its workgroups.
+// Grouped persistent kernel.  The real tiles (counted from the sanitized
+// offsets) are numbered expert by expert and, inside an expert, n-tile-major:
+// the m-tiles that share one weight panel are neighbours, dealt to
+// neighbouring workgroups of one XCD in the same round, so the later readers
+// of the panel can find it in that XCD's L2 (measured ~1 % faster than
+// m-tile-major on a 64-expert MoE layer).  The numbered tiles split evenly
+// over the 8 XCDs as contiguous ranges, each range dealt round-robin to its
+// XCD's workgroups.
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_persistent_kernel(GemmArgs args, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1070,18 +1091,25 @@ __global__ __launch_bounds__(C::THREADS) void grouped_persistent_kernel(GemmArgs
   const int lo = xcd * share, hi = min(lo + share, total);
   const int64_t kb = args.k / 2, ks = args.k / 32;
   const auto job_of = [&](int t) {
-    const int mt = t / tiles_n, tn = t - mt * tiles_n;
     TileJob jb;
-    int g = 0;
-    if (!find_group(args.offsets, args.groups, args.m, C::BM, mt, g, jb.ar)) {
+    ExpertTiles e;
+    int tn = 0;
+    if (find_expert(args.offsets, args.groups, args.m, C::BM, t / tiles_n, e)) {
+      const int local = t - e.first * tiles_n;   // in [0, cnt * tiles_n)
+      tn = local / e.cnt;
+      jb.ar.lo = e.lo + (local - tn * e.cnt) * C::BM;
+      jb.ar.end = min(e.hi, jb.ar.lo + C::BM);
+      jb.ar.last = jb.ar.end - 1;
+    } else {
       // unreachable for t < total (the counts agree); an empty row range stores nothing
+      e.g = 0;
       jb.ar.lo = 0;
       jb.ar.end = 0;
       jb.ar.last = 0;
     }
     jb.n0 = tn * C::BN;
-    jb.b_q = args.b_q + (int64_t)g * args.n * kb;
-    jb.b_s = args.b_s + (int64_t)g * args.n * ks;
+    jb.b_q = args.b_q + (int64_t)e.g * args.n * kb;
+    jb.b_s = args.b_s + (int64_t)e.g * args.n * ks;
     return jb;
   };
   persistent_loop<C>(args, lo + slot, per_wg, hi, job_of, (uint8_t MXFP4_LDS*)smem);
