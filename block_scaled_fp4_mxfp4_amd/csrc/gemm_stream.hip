@@ -869,19 +869,26 @@ __device__ __forceinline__ bool combine_splits(v4f (&own)[C::MB * 2], const PPSp
   }
   __syncthreads();
   if (!*last) return false;
-  // The partial tiles in groups of four ranges: a group's loads are all issued
-  // before any is used (one memory round trip per group; loaded one at a time
-  // the sum took longer than the whole main loop), then added in range order.
-  // The loads are unconditional (past the last range they reread it; this
-  // workgroup's own range is read back and not used) so that no branch makes
-  // the compiler wait between them.
+  // The other ranges' partial tiles in groups of four: a group's loads are all
+  // issued before any is used (one memory round trip per group; loaded one at
+  // a time the sum took longer than the whole main loop), then added in range
+  // order, this workgroup's own range (already in registers) taking its place
+  // in that order.  The loads are unconditional (past the last range they
+  // reread it) so that no branch makes the compiler wait between them.
   constexpr int G = 4;
+  const int others = sk.splits - 1;
   v4f sum[UW];
-  for (int sp0 = 0; sp0 < sk.splits; sp0 += G) {
+  bool own_done = false;
+  const auto add = [&](int sp, const v4f (&v)[UW]) {
+#pragma unroll
+    for (int t = 0; t < UW; ++t) sum[t] = sp == 0 ? v[t] : sum[t] + v[t];
+  };
+  for (int o0 = 0; o0 < others; o0 += G) {
     v4f part[G][UW];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int sp = min(sp0 + g, sk.splits - 1);
+      const int o = min(o0 + g, others - 1);
+      const int sp = o < split ? o : o + 1;
 #pragma unroll
       for (int t = 0; t < UW; ++t)
         part[g][t] = __builtin_bit_cast(
@@ -891,15 +898,17 @@ __device__ __forceinline__ bool combine_splits(v4f (&own)[C::MB * 2], const PPSp
     __builtin_amdgcn_sched_barrier(0);   // every load of the group before the first add
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int sp = sp0 + g;
-      if (sp >= sk.splits) break;
-#pragma unroll
-      for (int t = 0; t < UW; ++t) {
-        const v4f v = sp == split ? own[t] : part[g][t];
-        sum[t] = sp == 0 ? v : sum[t] + v;
+      const int o = o0 + g;
+      if (o >= others) break;
+      const int sp = o < split ? o : o + 1;
+      if (!own_done && sp > split) {
+        add(split, own);
+        own_done = true;
       }
+      add(sp, part[g]);
     }
   }
+  if (!own_done) add(split, own);
 #pragma unroll
   for (int t = 0; t < UW; ++t) own[t] = sum[t];
   return true;
