@@ -53,6 +53,9 @@ PATTERNS = {
     # (every workgroup runs several tiles of different experts)
     "persistent_ragged": ([0, 255, 256, 257, 511, 1, 700, 0], 200, 1024),
     "persistent_many_tiles": (list(np.random.default_rng(1).integers(0, 600, size=32)), 1536, 2048),
+    # several n-tiles with a ragged last one, and experts of 1 to 4 m-tiles: the
+    # tiles of an expert run n-tile-major (its m-tiles of one n-tile adjacent)
+    "persistent_ragged_n": ([300, 0, 600, 45, 256, 1000], 600, 1024),
 }
 
 
