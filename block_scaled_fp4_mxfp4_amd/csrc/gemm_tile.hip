@@ -836,23 +836,14 @@ __device__ __forceinline__ bool find_expert(const int32_t* offsets, int groups, 
   return false;
 }
 
-// The expert and row range of global m-tile `mt`.
-__device__ __forceinline__ bool find_group(const int32_t* offsets, int groups, int total_m, int bm,
-                                           int mt, int& g_out, RowRange& ar) {
-  ExpertTiles e;
-  if (!find_expert(offsets, groups, total_m, bm, mt, e)) return false;
-  g_out = e.g;
-  ar.lo = e.lo + (mt - e.first) * bm;
-  ar.end = min(e.hi, ar.lo + bm);
-  ar.last = ar.end - 1;
-  return true;
-}
-
 // The grid is a multiple of 8 workgroups covering at least every possible
 // m-tile (the host cannot see the device offsets).  Workgroups are dispatched
 // to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; the real tiles
 // are split evenly over the XCDs as contiguous ranges (consecutive tiles of one
 // expert share that XCD's L2), and the spare workgroups of every XCD exit.
+// Inside an expert the tiles run n-tile-major, as in the persistent kernel:
+// the m-tiles that read one weight panel start together on one XCD (W4A8 MoE
+// layer 412 -> 407 us on one box).
 template <class C, bool COPY>
 __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -861,10 +852,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
   const int slot = blockIdx.x >> 3;
   const int t = (blockIdx.x & 7) * share + slot;
   if (slot >= share || t >= total) return;
-  const int mt = t / tiles_n, tn = t - mt * tiles_n;
-  int g;
+  ExpertTiles e;
+  if (!find_expert(args.offsets, args.groups, args.m, C::BM, t / tiles_n, e)) return;
+  const int local = t - e.first * tiles_n;   // in [0, cnt * tiles_n)
+  const int tn = local / e.cnt;
   RowRange ar;
-  if (!find_group(args.offsets, args.groups, args.m, C::BM, mt, g, ar)) return;
+  ar.lo = e.lo + (local - tn * e.cnt) * C::BM;
+  ar.end = min(e.hi, ar.lo + C::BM);
+  ar.last = ar.end - 1;
+  const int g = e.g;
   const int64_t kb = C::B8 ? args.k : args.k / 2, ks = args.k / 32;
   const uint8_t* b_q = args.b_q + (int64_t)g * args.n * kb;
   const uint8_t* b_s = args.b_s + (int64_t)g * args.n * ks;
