@@ -76,6 +76,22 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
   return sign | (uint32_t)n;
 }
 
+__device__ __attribute__((noinline)) uint32_t f64_to_bf16_rne_slow(double d) { return f64_to_bf16_rne(d); }
+
+// f64_to_bf16_rne through the hardware conversions: d -> fp32 (nearest even)
+// -> BF16 (nearest even).  The first rounding never steps over an fp32 value,
+// and every BF16 midpoint is one, so the two agree with the direct rounding
+// unless the fp32 value lands exactly on a midpoint (its last 16 bits 0x8000)
+// or is subnormal, zero, at or above 2^127, or not finite: those take the
+// direct path.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne_fast(double d) {
+  const uint32_t b = __float_as_uint((float)d);
+  const uint32_t ex = (b >> 23) & 0xFFu;
+  if (__builtin_expect(ex >= 1u && ex <= 253u && (b & 0xFFFFu) != 0x8000u, 1))
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  return f64_to_bf16_rne_slow(d);
+}
+
 // 8 BF16 codes -> packed E2M1 word and the block's scale byte (quad-wide amax)
 __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint32_t& sbyte) {
   const uint32_t m = umax16x2(umax16x2(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
@@ -162,8 +178,8 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
     uint32_t yw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f64_to_bf16_rne((double)bf16_lo(hw[i]) * inv * (double)bf16_lo(gw[i]));
-      const uint32_t hi = f64_to_bf16_rne((double)bf16_hi(hw[i]) * inv * (double)bf16_hi(gw[i]));
+      const uint32_t lo = f64_to_bf16_rne_fast((double)bf16_lo(hw[i]) * inv * (double)bf16_lo(gw[i]));
+      const uint32_t hi = f64_to_bf16_rne_fast((double)bf16_hi(hw[i]) * inv * (double)bf16_hi(gw[i]));
       yw[i] = lo | (hi << 16);
     }
     const uint4 y = make_uint4(yw[0], yw[1], yw[2], yw[3]);

@@ -79,6 +79,37 @@ def test_rmsnorm_quantize_matches_oracle(rows, k, with_res, eps):
     assert torch.equal(q, q2) and torch.equal(s, s2)
 
 
+def test_rmsnorm_exact_midpoints_round_to_even():
+    """Rows whose RMSNorm output is exact in float64 and lands on BF16 rounding
+    midpoints (and on quarter points and zeros): each row repeats
+    [1.5, 1.5, 1.5, 0.5, 0.5, 0.5, 0.5, 0.5] times 2^r, so mean(h^2) = 4^r and
+    with eps = 0 the scale is exactly 2^-r; gamma runs over 1 + j/128 (with
+    signs and zeros), so y = h * gamma has up to 10 significant bits.  The BF16
+    output must be the nearest-even rounding exactly, ties included."""
+    dev = device()
+    rows, k = 6, 1024
+    base = np.array([1.5, 1.5, 1.5, 0.5, 0.5, 0.5, 0.5, 0.5])
+    h = np.stack([np.tile(base, k // 8) * 2.0 ** (r - 2) * (-1) ** r for r in range(rows)])
+    j = np.arange(k) % 128
+    gamma = (1.0 + j / 128.0) * np.where(np.arange(k) % 3 == 0, -1.0, 1.0) * 2.0 ** ((np.arange(k) // 128) % 4 - 1)
+    gamma[::97] = 0.0
+    hb = oracle.f64_to_bf16_bits(h)
+    gb = oracle.f64_to_bf16_bits(gamma)
+    assert np.array_equal(oracle.bf16_bits_to_f64(hb), h) and np.array_equal(oracle.bf16_bits_to_f64(gb), gamma)
+    want = oracle.rmsnorm_bf16(hb, gb, 0.0)
+    ties = oracle.rmsnorm_f64(hb, gb, 0.0)
+    lo = oracle.bf16_bits_to_f64(want)
+    log(f"rmsnorm exact midpoints: {int(np.sum(np.abs(ties) != np.abs(lo)))} of {ties.size} outputs rounded")
+    x = torch.from_numpy(hb.astype(np.int16)).view(torch.bfloat16).to(dev)
+    g = torch.from_numpy(gb.astype(np.int16)).view(torch.bfloat16).to(dev)
+    y = poisoned((rows, k), torch.bfloat16, dev, 0x7F)
+    q, s = mxfp4_rmsnorm_quantize(x, g, 0.0, y=y)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y), want)
+    rq, rs = oracle.quantize(want)
+    assert np.array_equal(to_np(q), rq) and np.array_equal(to_np(s), rs)
+
+
 def test_rmsnorm_in_place_residual_and_zero_rows():
     dev = device()
     rows, k, eps = 16, 1024, 1e-5
