@@ -633,6 +633,11 @@ mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, con
   args.k = (int)k;
   args.offsets = offsets;
   args.groups = num_groups;
+  // k % 1024 == 0 with 16-byte aligned scale arrays: the persistent tile loop
+  // (results identical to the one-tile-per-workgroup kernel)
+  if (mxfp4::gemm_persistent_supported(args))
+    return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile_persistent(args, dev.num_cus, 0, (hipStream_t)stream),
+                      "grouped w4a8 gemm launch");
   return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile(args, (hipStream_t)stream), "grouped w4a8 gemm launch");
 }
 

@@ -893,31 +893,35 @@ __device__ __forceinline__ void job_sources(const GemmArgs& args, const TileJob&
 }
 
 // Epilogue through one 64 KiB region (the LDS buffer of the tile's last
-// stage): BF16 in two passes of 128 rows (one wave row each), fp32 in four
-// passes of 64 rows.  Rows are not padded: 16-byte chunk c of row r sits at
-// chunk c ^ (r mod chunks-per-row), so the 32 rows one wave writes at one
-// column fall in different chunks.  Ends with a barrier: the region is free.
+// stage).  256 x 256 tiles: BF16 in two passes of 128 rows (one wave row
+// each), fp32 in four passes of 64 rows.  128 x 256 tiles (W4A8): BF16 in one
+// pass of both wave rows, fp32 in two passes of 64 rows (one wave row each).
+// Rows are not padded: 16-byte chunk c of row r sits at chunk
+// c ^ (r mod chunks-per-row), so the 32 rows one wave writes at one column
+// fall in different chunks.  Ends with a barrier: the region is free.
 template <class C>
 __device__ __forceinline__ void store_tile_region(const GemmArgs& args, const v16f (&acc)[C::MI][C::NI],
                                                   const RowRange& ar, int n0, int wm0, int wn0, int lane,
                                                   uint8_t MXFP4_LDS* region) {
-  static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128, "the split epilogue is laid out for 256 x 256 tiles");
+  static_assert(C::BN == 256 && ((C::BM == 256 && C::WM == 128) || (C::BM == 128 && C::WM == 64)),
+                "the split epilogue is laid out for 256 x 256 and 128 x 256 tiles");
   // The LDS addresses below are the same for every tile; computed from a lane
   // index the compiler cannot see through, they are not hoisted out of the
   // persistent loop (held across the main loop they overflowed the registers).
   asm volatile("" : "+v"(lane));
   if (!args.c_f32) {
     constexpr int PITCH = C::BN * 2, CHUNKS = PITCH / 16;   // 512 bytes, 32 chunks per row
+    constexpr int RP = 65536 / PITCH;                        // 128 rows per pass
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm0 == half * C::WM) {
+    for (int pass = 0; pass < C::BM / RP; ++pass) {
+      if (C::BM == RP || wm0 == pass * C::WM) {
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
 #pragma unroll
           for (int j = 0; j < C::NI; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int r = 32 * i + (lane & 31);
+              const int r = (C::BM == RP ? wm0 : 0) + 32 * i + (lane & 31);
               const int col = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
               bf16x2_t lo = {(__bf16)acc[i][j][4 * q + 0], (__bf16)acc[i][j][4 * q + 1]};
               bf16x2_t hi = {(__bf16)acc[i][j][4 * q + 2], (__bf16)acc[i][j][4 * q + 3]};
@@ -926,17 +930,18 @@ __device__ __forceinline__ void store_tile_region(const GemmArgs& args, const v1
             }
       }
       __syncthreads();
-      copy_out<C, 2, PITCH, CHUNKS - 1>(args, region, half * C::WM, C::WM, ar, n0);
+      copy_out<C, 2, PITCH, CHUNKS - 1>(args, region, pass * RP, RP, ar, n0);
       __syncthreads();
     }
   } else {
     constexpr int PITCH = C::BN * 4, CHUNKS = PITCH / 16;   // 1024 bytes, 64 chunks per row
+    constexpr int PASSES_PER_ROW = C::WM / 64;               // 64-row passes per wave row
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      if (wm0 == (pass >> 1) * C::WM) {
+    for (int pass = 0; pass < C::BM / 64; ++pass) {
+      if (wm0 == (pass / PASSES_PER_ROW) * C::WM) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * (pass & 1) + ii;
+          const int i = 2 * (pass % PASSES_PER_ROW) + ii;
 #pragma unroll
           for (int j = 0; j < C::NI; ++j)
 #pragma unroll
@@ -1229,6 +1234,11 @@ hipError_t launch_gemm_tile_persistent(const GemmArgs& args, int num_cus, int ma
 
 hipError_t launch_grouped_gemm_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs, hipStream_t stream) {
   return launch_grouped_persistent<Cfg256>(args, num_cus, max_wgs, stream);
+}
+
+hipError_t launch_grouped_gemm_w4a8_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs,
+                                                    hipStream_t stream) {
+  return launch_grouped_persistent<CfgW4A8>(args, num_cus, max_wgs, stream);
 }
 
 hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream) {

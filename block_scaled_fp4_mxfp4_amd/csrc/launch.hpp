@@ -53,6 +53,10 @@ hipError_t launch_grouped_gemm_tile_persistent(const GemmArgs& args, int num_cus
 // 128 x 256 output tiles.
 hipError_t launch_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_grouped_gemm_w4a8_tile(const GemmArgs& args, hipStream_t stream);
+// The grouped W4A8 GEMM through the persistent tile loop (128 x 256 tiles;
+// needs what gemm_persistent_supported checks).
+hipError_t launch_grouped_gemm_w4a8_tile_persistent(const GemmArgs& args, int num_cus, int max_wgs,
+                                                    hipStream_t stream);
 
 // MXFP8 x MXFP8 tile kernels (a_q and b_q are [rows, k] E4M3 codes): 256 x 256
 // or 128 x 128 output tiles over 128-K stages; a tile's operand rows span at

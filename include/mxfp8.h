@@ -149,7 +149,10 @@ mxfp4_status_t mxfp8_gemm_nt_ex(const void* a_q8, const void* a_s, const void* b
  * k/2], [num_groups, n, k/32]) and the same device `offsets` contract
  * (offsets clamped into [0, total_m] and replaced by their running maximum,
  * so groups are disjoint and in range; a group with no rows writes nothing);
- * num_groups 1..1024.  No workspace; one kernel launch.
+ * num_groups 1..1024.  No workspace; one kernel launch of 128 x 256 tiles,
+ * through the persistent tile loop when k % 1024 == 0 and the scale arrays
+ * are 16-byte aligned.  Each group's rows equal mxfp8_gemm_w4a8_nt_ex with
+ * MXFP4_KERNEL_TILE128 on that group's slices, bit for bit.
  */
 mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, const void* b_q, const void* b_s,
                                           const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
