@@ -192,8 +192,11 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(GemmArgs args, in
   // Every workgroup reads all of A.  Were they all to walk K in the same order,
   // every CU would ask for the same A lines at the same moment and queue on
   // one L2 channel; with splits == 1 each workgroup instead starts its K walk
-  // at its own offset (A is small enough to stay resident in L2).
-  const int rot = (splits == 1) ? (int)(((int64_t)tn * 7) % nchunks) : 0;
+  // at its own offset (A is small enough to stay resident in L2).  Only when
+  // the four waves' ranges are equal: then they all take the same loop, and a
+  // rotation that only some of them applied would cover chunks twice or not
+  // at all.
+  const int rot = (splits == 1 && nchunks % 4 == 0) ? (int)(((int64_t)tn * 7) % nchunks) : 0;
   if (args.k % kChunk == 0 && (splits == 1 || rot == 0)) {
     switch (whi - wlo) {   // wave-uniform
       case 8: wave_mainloop_fixed<MB, NI, 8>(acc, args, n0, wlo, rot, nchunks, lane); break;

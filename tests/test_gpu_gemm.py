@@ -32,7 +32,10 @@ TILE_SHAPES = [  # (m, n, k): several tiles, ragged tails, k % 128 != 0 cases
     (352, 520, 1024), (200, 300, 512),
 ]
 SPLITK_SHAPES = [(1, 64, 128), (17, 200, 1024), (32, 1000, 4096), (33, 70, 160), (100, 512, 2048),
-                 (128, 320, 4096), (64, 129, 8192)]
+                 (128, 320, 4096), (64, 129, 8192),
+                 # K in 128-chunks not divisible by 4 (15, 17, 30): waves of unequal K
+                 # ranges over several column tiles
+                 (2, 281, 1920), (64, 300, 2176), (128, 200, 3840)]
 # the persistent loop needs k % 1024 == 0; k = 1024 is the two-stage tile (no loop body)
 PERSISTENT_SHAPES = [(300, 520, 1024), (513, 263, 2048), (257, 129, 4096), (352, 520, 1024), (1, 300, 1024),
                      (200, 300, 3072)]
