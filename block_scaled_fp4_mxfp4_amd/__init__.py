@@ -1,5 +1,5 @@
 """MI355X (gfx950) MXFP4 engine: BF16 -> MXFP4 quantization, block-scaled FP4 NT GEMM,
-grouped per-expert GEMM, a decode GEMM on prepacked weights, BF16 -> MXFP8 quantization, W4A8 GEMMs
+grouped per-expert GEMM (also on an interleaved scale layout), a decode GEMM on prepacked weights, BF16 -> MXFP8 quantization, W4A8 GEMMs
 (MXFP8 A x MXFP4 B) and the MXFP8 x MXFP8 GEMM, and the MoE steps around the grouped GEMM (top-k routing,
 expert-sorted permutation, scatter-quantize, combine) and fused producers that
 emit MXFP4 (residual add + RMSNorm, SwiGLU), and NVFP4 (two-level: UE4M3 per
@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     mxfp4_moe_route, mxfp4_moe_permute, mxfp4_moe_quantize_scatter, mxfp8_moe_quantize_scatter, mxfp4_moe_combine,
     mxfp4_rmsnorm_quantize, mxfp4_swiglu_quantize, nvfp4_quantize, nvfp4_gemm_nt,
     mxfp4_prepacked_weight_size, mxfp4_prepack_weight, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,
-    mxfp4_quantize_prepacked,
+    mxfp4_quantize_prepacked, mxfp4_scales_interleave, mxfp4_quantize_interleaved, mxfp4_gemm_nt_interleaved,
+    mxfp4_grouped_gemm_nt_interleaved, mxfp4_moe_quantize_scatter_interleaved,
     LIB_PATH, EXPORTED, KERNELS,
 )

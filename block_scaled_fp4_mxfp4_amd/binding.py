@@ -34,6 +34,8 @@ EXPORTED = (
     "mxfp4_gemm_nt_prepacked_ab_ex", "mxfp4_gemm_nt_prepacked_ab_workspace_size",
     "mxfp4_quantize_prepacked", "mxfp8_gemm_nt", "mxfp8_gemm_nt_ex", "mxfp4_gemm_nt_ex_noalloc",
     "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked",
+    "mxfp4_scales_interleave", "mxfp4_quantize_interleaved", "mxfp4_gemm_nt_interleaved",
+    "mxfp4_grouped_gemm_nt_interleaved", "mxfp4_moe_quantize_scatter_interleaved",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -124,7 +126,16 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         lib.mxfp4_moe_permute.restype = ctypes.c_int
         lib.mxfp4_moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
-        for name in ("mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter"):
+        lib.mxfp4_scales_interleave.restype = ctypes.c_int
+        lib.mxfp4_scales_interleave.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.mxfp4_quantize_interleaved.restype = ctypes.c_int
+        lib.mxfp4_quantize_interleaved.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_gemm_nt_interleaved.restype = ctypes.c_int
+        lib.mxfp4_gemm_nt_interleaved.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp4_grouped_gemm_nt_interleaved.restype = ctypes.c_int
+        lib.mxfp4_grouped_gemm_nt_interleaved.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64, vp]
+        for name in ("mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
+                     "mxfp4_moe_quantize_scatter_interleaved"):
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = [vp, i64, i64, i32, vp, i64, vp, vp, vp]
         lib.mxfp4_rmsnorm_quantize.restype = ctypes.c_int
@@ -376,6 +387,72 @@ def mxfp4_grouped_gemm_nt(a_q, a_s, b_q, b_s, offsets, c=None, out_dtype=torch.b
     return c
 
 
+def mxfp4_scales_interleave(scales, out=None, stream=None):
+    """Row-major scale bytes [rows, k/32] (or [groups, rows, k/32]) -> the
+    interleaved layout [k/512, rows, 16] (or [groups, k/512, rows, 16])."""
+    lib = load_library()
+    grouped = scales.dim() == 3
+    groups, rows, kb = scales.shape if grouped else (1, *scales.shape)
+    k = kb * 32
+    shape = (groups, k // 512, rows, 16) if grouped else (k // 512, rows, 16)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=scales.device)
+    _require(scales, "scales", torch.uint8, scales.shape)
+    _require(out, "out", torch.uint8, shape)
+    _check(lib.mxfp4_scales_interleave(_ptr(scales), groups, rows, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def mxfp4_quantize_interleaved(x: torch.Tensor, q=None, scales_il=None, stream=None):
+    """x: bf16 [rows, k] -> (q uint8 [rows, k/2], scales_il uint8 [k/512, rows, 16])."""
+    lib = load_library()
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales_il is None:
+        scales_il = torch.empty((k // 512, rows, 16), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(q, "q", torch.uint8, (rows, k // 2))
+    _require(scales_il, "scales_il", torch.uint8, (k // 512, rows, 16))
+    _check(lib.mxfp4_quantize_interleaved(_ptr(x), rows, k, _ptr(q), _ptr(scales_il), _stream(stream)))
+    return q, scales_il
+
+
+def mxfp4_gemm_nt_interleaved(a_q, a_s_il, b_q, b_s_il, c=None, out_dtype=torch.bfloat16, stream=None):
+    """mxfp4_gemm_nt with interleaved scales: a_s_il [k/512, m, 16], b_s_il [k/512, n, 16]."""
+    lib = load_library()
+    m, kh = a_q.shape
+    n = b_q.shape[0]
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (m, k // 2))
+    _require(a_s_il, "a_s_il", torch.uint8, (k // 512, m, 16))
+    _require(b_q, "b_q", torch.uint8, (n, k // 2))
+    _require(b_s_il, "b_s_il", torch.uint8, (k // 512, n, 16))
+    c, code = _out(c, m, n, out_dtype, a_q.device)
+    _check(lib.mxfp4_gemm_nt_interleaved(_ptr(a_q), _ptr(a_s_il), _ptr(b_q), _ptr(b_s_il), _ptr(c), code, m, n, k,
+                                         _stream(stream)))
+    return c
+
+
+def mxfp4_grouped_gemm_nt_interleaved(a_q, a_s_il, b_q, b_s_il, offsets, c=None, out_dtype=torch.bfloat16,
+                                      stream=None):
+    """mxfp4_grouped_gemm_nt with interleaved scales: a_s_il [k/512, total_m, 16],
+    b_s_il [groups, k/512, n, 16]."""
+    lib = load_library()
+    total_m, kh = a_q.shape
+    groups, n, _ = b_q.shape
+    k = kh * 2
+    _require(a_q, "a_q", torch.uint8, (total_m, k // 2))
+    _require(a_s_il, "a_s_il", torch.uint8, (k // 512, total_m, 16))
+    _require(b_q, "b_q", torch.uint8, (groups, n, k // 2))
+    _require(b_s_il, "b_s_il", torch.uint8, (groups, k // 512, n, 16))
+    _require(offsets, "offsets", torch.int32, (groups + 1,))
+    c, code = _out(c, total_m, n, out_dtype, a_q.device)
+    _check(lib.mxfp4_grouped_gemm_nt_interleaved(_ptr(a_q), _ptr(a_s_il), _ptr(b_q), _ptr(b_s_il), _ptr(offsets),
+                                                 groups, total_m, _ptr(c), code, n, k, _stream(stream)))
+    return c
+
+
 def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: str = "auto", stream=None):
     """C[m, n] = A[m, k] . B[n, k]^T with A in MXFP8 ([m, k] codes) and B in MXFP4.
     kernel: "auto", "tile128" (128 x 256 tiles) or "stream"."""
@@ -506,17 +583,18 @@ def mxfp4_moe_permute(ids: torch.Tensor, experts: int, offsets=None, row_token=N
     return offsets, row_token, token_rows
 
 
-def _quantize_scatter(fn, x, token_rows, total_rows, q, scales, code_cols, stream):
+def _quantize_scatter(fn, x, token_rows, total_rows, q, scales, code_cols, stream, interleaved=False):
     tokens, k = x.shape
     top_k = token_rows.shape[1]
+    s_shape = (k // 512, total_rows, 16) if interleaved else (total_rows, k // 32)
     if q is None:
         q = torch.empty((total_rows, code_cols), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((total_rows, k // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(s_shape, dtype=torch.uint8, device=x.device)
     _require(x, "x", torch.bfloat16, (tokens, k))
     _require(token_rows, "token_rows", torch.int32, (tokens, top_k))
     _require(q, "q", torch.uint8, (total_rows, code_cols))
-    _require(scales, "scales", torch.uint8, (total_rows, k // 32))
+    _require(scales, "scales", torch.uint8, s_shape)
     _check(fn(_ptr(x), tokens, k, top_k, _ptr(token_rows), total_rows, _ptr(q), _ptr(scales), _stream(stream)))
     return q, scales
 
@@ -527,6 +605,13 @@ def mxfp4_moe_quantize_scatter(x, token_rows, total_rows: int, q=None, scales=No
     lib = load_library()
     return _quantize_scatter(lib.mxfp4_moe_quantize_scatter, x, token_rows, total_rows, q, scales,
                              x.shape[1] // 2, stream)
+
+
+def mxfp4_moe_quantize_scatter_interleaved(x, token_rows, total_rows: int, q=None, scales_il=None, stream=None):
+    """mxfp4_moe_quantize_scatter with the scales interleaved: scales_il [k/512, total_rows, 16]."""
+    lib = load_library()
+    return _quantize_scatter(lib.mxfp4_moe_quantize_scatter_interleaved, x, token_rows, total_rows, q, scales_il,
+                             x.shape[1] // 2, stream, interleaved=True)
 
 
 def mxfp8_moe_quantize_scatter(x, token_rows, total_rows: int, q8=None, scales=None, stream=None):

@@ -547,6 +547,109 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s, const voi
   return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "grouped gemm launch");
 }
 
+namespace {
+// Checks shared by the entry points that take interleaved scales: k % 512 ==
+// 0, 16-byte aligned scale arrays, and rows * k/32 < 2^31 for each operand
+// (the kernels index a slab of rows with 32-bit byte offsets).
+mxfp4_status_t check_interleaved(const void* a_s, const void* b_s, int64_t m, int64_t n, int64_t k) {
+  if (k % 512 != 0) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need k %% 512 == 0 (got %lld)", (long long)k);
+  if (m * (k / 32) >= ((int64_t)1 << 31) || n * (k / 32) >= ((int64_t)1 << 31))
+    return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need rows * k / 32 < 2^31 for each operand");
+  if (m > 0) MXFP4_TRY(check_ptr(a_s, "a_s"));
+  if (n > 0) MXFP4_TRY(check_ptr(b_s, "b_s"));
+  return MXFP4_OK;
+}
+}  // namespace
+
+mxfp4_status_t mxfp4_scales_interleave(const void* scales, int64_t groups, int64_t rows, int64_t k, void* scales_il,
+                                       void* stream) {
+  if (groups < 0 || rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  MXFP4_TRY(check_k(k));
+  if (k % 512 != 0) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need k %% 512 == 0 (got %lld)", (long long)k);
+  if (groups > 0 && rows > ((int64_t)1 << 40) / k / groups) return fail(MXFP4_ERR_INVALID_ARG, "groups * rows * k too large");
+  if (groups == 0 || rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(scales, "scales"));
+  MXFP4_TRY(check_ptr(scales_il, "scales_il"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_scales_interleave(scales, groups, rows, k, scales_il, (hipStream_t)stream,
+                                                    dev.num_cus), "scale interleave launch");
+}
+
+mxfp4_status_t mxfp4_quantize_interleaved(const void* x_bf16, int64_t rows, int64_t k, void* q, void* scales_il,
+                                          void* stream) {
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
+  MXFP4_TRY(check_k(k));
+  if (k % 512 != 0) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need k %% 512 == 0 (got %lld)", (long long)k);
+  if (rows * (k / 32) >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need rows * k / 32 < 2^31");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(q, "q", 4));
+  MXFP4_TRY(check_ptr(scales_il, "scales_il", 1));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_quantize(x_bf16, rows, k, q, scales_il, (hipStream_t)stream, dev.num_cus, true),
+                    "interleaved quantize launch");
+}
+
+mxfp4_status_t mxfp4_gemm_nt_interleaved(const void* a_q, const void* a_s_il, const void* b_q, const void* b_s_il,
+                                         void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q, a_s_il, b_q, b_s_il, c, c_type, m, n, k));
+  MXFP4_TRY(check_interleaved(a_s_il, b_s_il, m, n, k));
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s_il;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s_il;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  args.scale_il = 1;
+  // the tile kernels at every m (the small-M kernels read row-major scales):
+  // 256 x 256 tiles once they fill the device, else 128 x 128
+  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const mxfp4::TileKind kind = tiles256 >= dev.num_cus ? mxfp4::kTile256 : mxfp4::kTile128;
+  return hip_status(mxfp4::launch_gemm_tile(args, kind, (hipStream_t)stream), "interleaved gemm launch");
+}
+
+mxfp4_status_t mxfp4_grouped_gemm_nt_interleaved(const void* a_q, const void* a_s_il, const void* b_q,
+                                                 const void* b_s_il, const int32_t* offsets, int32_t num_groups,
+                                                 int64_t total_m, void* c, mxfp4_out_t c_type, int64_t n, int64_t k,
+                                                 void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q, a_s_il, b_q, b_s_il, c, c_type, total_m, n, k));
+  MXFP4_TRY(check_interleaved(a_s_il, b_s_il, total_m, n, k));
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(MXFP4_ERR_INVALID_ARG, "num_groups must be 1..1024 (got %d)", num_groups);
+  if (total_m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(offsets, "offsets", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s_il;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s_il;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)total_m;
+  args.n = (int)n;
+  args.k = (int)k;
+  args.offsets = offsets;
+  args.groups = num_groups;
+  args.scale_il = 1;
+  // the same kernel choice as mxfp4_grouped_gemm_nt
+  const mxfp4::TileKind kind = (total_m / num_groups >= 192) ? mxfp4::kTile256 : mxfp4::kTile128;
+  if (kind == mxfp4::kTile256 && mxfp4::gemm_persistent_supported(args))
+    return hip_status(mxfp4::launch_grouped_gemm_tile_persistent(args, dev.num_cus, 0, (hipStream_t)stream),
+                      "interleaved grouped gemm launch");
+  return hip_status(mxfp4::launch_grouped_gemm_tile(args, kind, (hipStream_t)stream), "interleaved grouped gemm launch");
+}
+
 mxfp4_status_t mxfp8_gemm_w4a8_nt_ex(const void* a_q8, const void* a_s, const void* b_q, const void* b_s, void* c,
                                      mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, mxfp4_kernel_t kernel,
                                      void* stream) {
@@ -721,12 +824,17 @@ mxfp4_status_t mxfp4_moe_permute(const int32_t* topk_ids, int64_t tokens, int32_
 namespace {
 mxfp4_status_t moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
                                     const int32_t* token_rows, int64_t total_rows, void* q, void* scales,
-                                    bool fp8, void* stream) {
+                                    bool fp8, void* stream, bool interleaved = false) {
   if (tokens < 0 || total_rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
   MXFP4_TRY(check_k(k));
   if (top_k < 1 || top_k > 256) return fail(MXFP4_ERR_INVALID_ARG, "top_k must be 1..256 (got %d)", top_k);
   if (tokens > ((int64_t)1 << 30) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "tokens * k / 32 too large");
   if (total_rows >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "total_rows too large");
+  if (interleaved) {
+    if (k % 512 != 0) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need k %% 512 == 0 (got %lld)", (long long)k);
+    if (total_rows * (k / 32) >= ((int64_t)1 << 31))
+      return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need total_rows * k / 32 < 2^31");
+  }
   if (tokens == 0 || total_rows == 0) return MXFP4_OK;
   MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
   MXFP4_TRY(check_ptr(token_rows, "token_rows", 4));
@@ -736,7 +844,7 @@ mxfp4_status_t moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t 
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_moe_quantize_scatter(x_bf16, (int)tokens, (int)k, top_k, token_rows,
                                                        (int)total_rows, q, scales, fp8, (hipStream_t)stream,
-                                                       dev.num_cus), "moe quantize-scatter launch");
+                                                       dev.num_cus, interleaved), "moe quantize-scatter launch");
 }
 }  // namespace
 
@@ -744,6 +852,12 @@ mxfp4_status_t mxfp4_moe_quantize_scatter(const void* x_bf16, int64_t tokens, in
                                           const int32_t* token_rows, int64_t total_rows, void* q, void* scales,
                                           void* stream) {
   return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q, scales, false, stream);
+}
+
+mxfp4_status_t mxfp4_moe_quantize_scatter_interleaved(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                                      const int32_t* token_rows, int64_t total_rows, void* q,
+                                                      void* scales_il, void* stream) {
+  return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q, scales_il, false, stream, true);
 }
 
 mxfp4_status_t mxfp8_moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,

@@ -144,6 +144,17 @@ struct RowRange {
   int end;    // one past the last row that is stored
 };
 
+// Scale layouts.  The copy path reads a row's scale bytes as 16-byte pieces,
+// piece g holding the scales of the row's 32-blocks 16g .. 16g + 15 (512 K).
+// Row-major scales ([rows, k/32]): piece g of row r at r * k/32 + 16 g, so the
+// 64 rows of one copy instruction touch 64 cache lines.  Interleaved scales
+// ([k/512, rows, 16], `scale_il`): piece g of row r at g * rows * 16 + r * 16,
+// so those 64 pieces are 1 KB of consecutive bytes (8 lines).  Scale byte
+// offset of a row from the tile's first row: row * scale_row_stride.
+__device__ __forceinline__ uint32_t scale_row_stride(const GemmArgs& args) {
+  return args.scale_il ? 16u : (uint32_t)args.k / 32;
+}
+
 // Workgroup-uniform bases of one output tile: its first A row, first B row,
 // and their scale rows.  Per-thread copy offsets are taken from these, so they
 // fit 32 bits (a tile spans at most 256 rows) and the bases stay in scalar
@@ -158,23 +169,32 @@ struct TileBases {
 template <class C>
 __device__ __forceinline__ TileBases tile_bases(const GemmArgs& args, const uint8_t* b_q, const uint8_t* b_s,
                                                 const RowRange& ar, int n0) {
-  const int64_t ks = args.k / 32, ka = C::A8 ? args.k : args.k / 2, kbb = C::B8 ? args.k : args.k / 2;
-  return {args.a_q + ar.lo * ka, b_q + n0 * kbb, args.a_s + ar.lo * ks, b_s + n0 * ks};
+  const int64_t ss = scale_row_stride(args), ka = C::A8 ? args.k : args.k / 2, kbb = C::B8 ? args.k : args.k / 2;
+  return {args.a_q + ar.lo * ka, b_q + n0 * kbb, args.a_s + ar.lo * ss, b_s + n0 * ss};
 }
 
 // Buffer resources over the same tile operands, sized to the rows the tile
 // reads (at most 256 FP4 rows or 128 FP8 rows, so at most 2^31 code bytes
-// for k <= 2^24).
+// for k <= 2^24), and the byte distance between consecutive scale pieces of
+// a row (row-major 16; interleaved rows * 16, at most 2^31 / (k/512)).
+// Copy path only (k % 512 == 0).
 struct TileRsrc {
   __amdgpu_buffer_rsrc_t a_q, b_q, a_s, b_s;
+  uint32_t a_sg, b_sg;
 };
 
 template <class C>
-__device__ __forceinline__ TileRsrc tile_rsrc(const TileBases& tb, const RowRange& ar, int n0, int n, int k) {
-  const uint32_t ks = k / 32, ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
-  const uint32_t a_rows = ar.last - ar.lo + 1, b_rows = min(C::BN, n - n0);
+__device__ __forceinline__ TileRsrc tile_rsrc(const TileBases& tb, const RowRange& ar, int n0, const GemmArgs& args) {
+  const uint32_t k = args.k, ks = k / 32, ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
+  const uint32_t a_rows = ar.last - ar.lo + 1, b_rows = min(C::BN, args.n - n0);
+  if (args.scale_il) {
+    // the tile's rows in each of the k/512 slabs: the last slab's rows end the range
+    const uint32_t a_sg = (uint32_t)args.m * 16, b_sg = (uint32_t)args.n * 16, last = k / 512 - 1;
+    return {make_rsrc(tb.a_q, a_rows * ka), make_rsrc(tb.b_q, b_rows * kbb), make_rsrc(tb.a_s, last * a_sg + a_rows * 16),
+            make_rsrc(tb.b_s, last * b_sg + b_rows * 16), a_sg, b_sg};
+  }
   return {make_rsrc(tb.a_q, a_rows * ka), make_rsrc(tb.b_q, b_rows * kbb), make_rsrc(tb.a_s, a_rows * ks),
-          make_rsrc(tb.b_s, b_rows * ks)};
+          make_rsrc(tb.b_s, b_rows * ks), 16u, 16u};
 }
 
 // Per-thread byte offsets of the copies from the tile bases, at stage 0 / scale
@@ -196,9 +216,9 @@ __device__ __forceinline__ bool scale_is_b(int j, int w) {
 }
 
 template <class C>
-__device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k) {
+__device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar, int n0, int n, int k, uint32_t ss) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t ks = k / 32, ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
+  const uint32_t ka = C::A8 ? k : k / 2, kbb = C::B8 ? k : k / 2;
   const int a_rows = ar.last - ar.lo, b_rows = n - 1 - n0;   // largest valid row offsets
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
@@ -215,7 +235,7 @@ __device__ __forceinline__ void make_sources(Sources<C>& src, const RowRange& ar
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j) {
     const int slot = (j * C::NWAVES + w) * 64 + lane;
-    src.scale[j] = slot >= C::BM ? (uint32_t)min(slot - C::BM, b_rows) * ks : (uint32_t)min(slot, a_rows) * ks;
+    src.scale[j] = slot >= C::BM ? (uint32_t)min(slot - C::BM, b_rows) * ss : (uint32_t)min(slot, a_rows) * ss;
   }
 }
 
@@ -240,14 +260,14 @@ __device__ __forceinline__ void copy_codes_b(uint8_t MXFP4_LDS* stage, const Sou
                (MXFP4_LDS void*)(stage + C::A_BYTES + (j * C::NWAVES + w) * 64 * 16));
 }
 
-// Scale copies of group g (stages 2g and 2g+1): 16 bytes of every row.
+// Scale copies of group g (stages 2g and 2g+1): piece g of every row.
 template <class C>
 __device__ __forceinline__ void copy_scales(uint8_t MXFP4_LDS* group, const Sources<C>& src, const TileRsrc& tr,
                                             int g) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < C::S_LOADS; ++j)
-    buf2lds_16(scale_is_b<C>(j, w) ? tr.b_s : tr.a_s, src.scale[j], g * 16,
+    buf2lds_16(scale_is_b<C>(j, w) ? tr.b_s : tr.a_s, src.scale[j], g * (scale_is_b<C>(j, w) ? tr.b_sg : tr.a_sg),
                (MXFP4_LDS void*)(group + (j * C::NWAVES + w) * 64 * 16));
 }
 
@@ -696,7 +716,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   Sources<C> src;
-  make_sources<C>(src, ar, n0, args.n, args.k);
+  make_sources<C>(src, ar, n0, args.n, args.k, scale_row_stride(args));
   const TileBases tb = tile_bases<C>(args, b_q, b_s, ar, n0);
   uint8_t MXFP4_LDS* group0 = lds + 2 * C::CODE_STAGE;
 
@@ -711,7 +731,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& args, const uint8_t* b_
     // reads; their accumulators stay zero and are never stored.  Every wave
     // still issues all copies and meets every barrier.
     const int active = __builtin_amdgcn_readfirstlane(min(max((ar.end - ar.lo - wm0 + 31) / 32, 0), C::MI));
-    const TileRsrc tr = tile_rsrc<C>(tb, ar, n0, args.n, args.k);
+    const TileRsrc tr = tile_rsrc<C>(tb, ar, n0, args);
     copy_loop_dispatch<C, C::MI>(active, acc, src, tr, lds, args.k / C::SK, wm0, wn0, lane, epi);
   } else {
     const int nk = (args.k + C::SK - 1) / C::SK;
@@ -887,9 +907,9 @@ struct TileJob {
 
 template <class C>
 __device__ __forceinline__ void job_sources(const GemmArgs& args, const TileJob& jb, Sources<C>& src, TileRsrc& tr) {
-  make_sources<C>(src, jb.ar, jb.n0, args.n, args.k);
+  make_sources<C>(src, jb.ar, jb.n0, args.n, args.k, scale_row_stride(args));
   const TileBases tb = tile_bases<C>(args, jb.b_q, jb.b_s, jb.ar, jb.n0);
-  tr = tile_rsrc<C>(tb, jb.ar, jb.n0, args.n, args.k);
+  tr = tile_rsrc<C>(tb, jb.ar, jb.n0, args);
 }
 
 // Epilogue through one 64 KiB region (the LDS buffer of the tile's last
@@ -1134,10 +1154,13 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 // The copy path reads 16-byte scale pieces: k % 512 == 0 and 16-byte aligned
-// scale arrays (row starts are then aligned too).
+// scale arrays (row starts are then aligned too).  Interleaved scales exist
+// only on the copy path (the register path reads row-major scales).
 bool use_copy_path(const GemmArgs& args) {
   return args.k % 512 == 0 && ((reinterpret_cast<uintptr_t>(args.a_s) | reinterpret_cast<uintptr_t>(args.b_s)) & 15) == 0;
 }
+
+bool scale_layout_ok(const GemmArgs& args) { return !args.scale_il || use_copy_path(args); }
 
 // GENERIC = false: the configuration has no register path (k % 512 != 0 or
 // unaligned scale arrays are refused with hipErrorInvalidValue).
@@ -1148,6 +1171,7 @@ hipError_t launch_dense(const GemmArgs& args, hipStream_t stream) {
   const size_t lds = C::LDS_BYTES;
   const int64_t blocks = (int64_t)tiles_m * tiles_n;
   if (!grid_fits(blocks, C::THREADS)) return hipErrorInvalidConfiguration;
+  if (!scale_layout_ok(args)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(gemm_tile_kernel<C, true>, lds);
@@ -1170,6 +1194,7 @@ hipError_t launch_grouped(const GemmArgs& args, hipStream_t stream) {
   const size_t lds = C::LDS_BYTES;
   const int64_t blocks = (mt_bound * tiles_n + 7) / 8 * 8;
   if (!grid_fits(blocks, C::THREADS)) return hipErrorInvalidConfiguration;
+  if (!scale_layout_ok(args)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
   if (use_copy_path(args)) {
     hipError_t e = allow_lds(grouped_tile_kernel<C, true>, lds);

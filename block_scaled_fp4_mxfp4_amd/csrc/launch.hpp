@@ -7,14 +7,15 @@ namespace mxfp4 {
 
 struct GemmArgs {
   const uint8_t* a_q;      // [m, k/2]
-  const uint8_t* a_s;      // [m, k/32]
+  const uint8_t* a_s;      // [m, k/32], or interleaved [k/512, m, 16]
   const uint8_t* b_q;      // [n, k/2] (grouped: [groups, n, k/2])
-  const uint8_t* b_s;      // [n, k/32] (grouped: [groups, n, k/32])
+  const uint8_t* b_s;      // [n, k/32] (grouped: [groups, n, k/32]), or interleaved [(groups,) k/512, n, 16]
   void* c;                 // [m, n]
   int c_f32;               // 0: bf16 output, 1: fp32 output
   int m, n, k;             // grouped: m = total_m
   const int32_t* offsets;  // grouped only: device [groups + 1]
   int groups;              // grouped only
+  int scale_il;            // 1: both scale arrays interleaved (tile kernels' copy path only)
 };
 
 // One HIP launch holds at most 2^32 - 1 threads.  Grid sizes are computed in
@@ -28,8 +29,13 @@ inline bool grid_fits(int64_t blocks, int threads) {
 // Tile kernels (TILE256: 256x256 output tiles, TILE128: 128x128 output tiles).
 enum TileKind { kTile256 = 0, kTile128 = 1 };
 
+// interleaved: scale bytes in the tile GEMMs' interleaved layout [k/512, rows, 16]
+// (k % 512 == 0, rows * k/32 < 2^31; hipErrorInvalidValue otherwise).
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
-                           hipStream_t stream, int num_cus);
+                           hipStream_t stream, int num_cus, bool interleaved = false);
+// Scale bytes [groups, rows, k/32] rearranged into [groups, k/512, rows, 16].
+hipError_t launch_scales_interleave(const void* scales, int64_t groups, int64_t rows, int64_t k, void* out,
+                                    hipStream_t stream, int num_cus);
 // The same codes and scale bytes stored in the prepacked GEMM operand layout
 // (k % 512 == 0; rows up to the next multiple of 64 written as zero blocks).
 hipError_t launch_quantize_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
@@ -116,9 +122,11 @@ hipError_t launch_moe_route(const float* logits, int tokens, int experts, int to
                             hipStream_t stream);
 hipError_t launch_moe_permute(const int32_t* ids, int n, int top_k, int experts, int32_t* offsets,
                               int32_t* row_token, int32_t* token_rows, hipStream_t stream);
+// interleaved: the MXFP4 scale bytes in the interleaved layout [k/512, total_rows, 16]
+// (k % 512 == 0, total_rows * k/32 < 2^31).
 hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top_k, const int32_t* token_rows,
                                        int total_rows, void* q, void* scales, bool fp8, hipStream_t stream,
-                                       int num_cus);
+                                       int num_cus, bool interleaved = false);
 hipError_t launch_moe_combine(const void* y, int total_rows, int n, const int32_t* token_rows, const float* weights,
                               int tokens, int top_k, void* out, bool f32_out, bool vec, hipStream_t stream);
 

@@ -346,7 +346,7 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(uint32_t w01, uint32_t w23, float 
 template <bool FP8>
 __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
     const uint4* __restrict__ x, int kblocks, int nblocks, int top_k, const int32_t* __restrict__ token_rows,
-    int total_rows, uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+    int total_rows, uint8_t* __restrict__ q, uint8_t* __restrict__ scales, int s_row, int s_piece) {
   const int lane4 = threadIdx.x & 3;
   const int groups_per_grid = gridDim.x * (kScatterThreads / 4);
   // kScatterUnroll blocks per lane group per iteration: all their loads are in
@@ -390,7 +390,9 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
         } else {
           *(uint32_t*)(q + (int64_t)r * kblocks * 16 + kb * 16 + lane4 * 4) = codes4;
         }
-        if (lane4 == 0) scales[(int64_t)r * kblocks + kb] = (uint8_t)sbyte;
+        // scale byte of 32-block kb of row r: piece kb / 16 at r * s_row + (kb / 16) * s_piece
+        // (row-major: s_row = k/32, s_piece = 16; interleaved: 16 and total_rows * 16)
+        if (lane4 == 0) scales[(int64_t)r * s_row + (int64_t)(kb >> 4) * s_piece + (kb & 15)] = (uint8_t)sbyte;
       }
     }
   }
@@ -505,8 +507,11 @@ hipError_t launch_moe_permute(const int32_t* ids, int n, int top_k, int experts,
 
 hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top_k, const int32_t* token_rows,
                                        int total_rows, void* q, void* scales, bool fp8, hipStream_t stream,
-                                       int num_cus) {
+                                       int num_cus, bool interleaved) {
   const int kblocks = k / 32;
+  if (interleaved && (fp8 || k % 512 != 0 || (int64_t)total_rows * kblocks >= ((int64_t)1 << 31)))
+    return hipErrorInvalidValue;
+  const int s_row = interleaved ? 16 : kblocks, s_piece = interleaved ? total_rows * 16 : 16;
   const int nblocks = tokens * kblocks;   // the host keeps this below 2^31
   const int64_t groups_needed = ((int64_t)nblocks + kScatterUnroll - 1) / kScatterUnroll;
   int64_t grid = (groups_needed + (kScatterThreads / 4) - 1) / (kScatterThreads / 4);
@@ -516,11 +521,11 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
   if (fp8)
     hipLaunchKernelGGL(quantize_scatter_kernel<true>, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream,
                        (const uint4*)x, kblocks, nblocks, top_k, token_rows, total_rows, (uint8_t*)q,
-                       (uint8_t*)scales);
+                       (uint8_t*)scales, s_row, s_piece);
   else
     hipLaunchKernelGGL(quantize_scatter_kernel<false>, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream,
                        (const uint4*)x, kblocks, nblocks, top_k, token_rows, total_rows, (uint8_t*)q,
-                       (uint8_t*)scales);
+                       (uint8_t*)scales, s_row, s_piece);
   return hipGetLastError();
 }
 

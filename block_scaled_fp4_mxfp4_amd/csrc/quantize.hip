@@ -7,7 +7,10 @@
 //
 // Layout: because K is a multiple of 32 and all three arrays are row-major, the
 // rows x K input is a flat sequence of blocks; block b reads bytes [64b, 64b+64)
-// of x, writes bytes [16b, 16b+16) of q and byte b of the scales.
+// of x, writes bytes [16b, 16b+16) of q and byte b of the scales.  With
+// interleaved scales (k % 512 == 0, the tile GEMMs' copy layout
+// [k/512, rows, 16]) the scale byte of block kb of row r goes to
+// (kb / 16) * rows * 16 + r * 16 + kb % 16 instead.
 //
 // Mapping: 4 lanes per block, 16 bytes (8 BF16) per lane, so one wave64 covers
 // 16 blocks with 1 KiB of fully coalesced loads.  HBM-bound: 2.53125 bytes per
@@ -55,9 +58,12 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return max(v, o);
 }
 
+// IL: interleaved scales; then rows * k/32 < 2^31 (`bpr` = k/32 blocks per
+// row, a multiple of 16), so the scale index fits 32 bits.
+template <bool IL>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ scales,
-    int64_t nblocks) {
+    int64_t nblocks, uint32_t bpr, uint32_t rows) {
   const int lane4 = threadIdx.x & 3;
   const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
   int64_t blk = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2);
@@ -90,9 +96,30 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].w), scale, 3);
       if (b < nblocks) {
         q[b * 4 + lane4] = packed;
-        if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+        if (lane4 == 0) {
+          if constexpr (IL) {
+            const uint32_t r = (uint32_t)b / bpr, kb = (uint32_t)b - r * bpr;
+            scales[(kb >> 4) * rows * 16 + r * 16 + (kb & 15)] = (uint8_t)sbyte;
+          } else {
+            scales[b] = (uint8_t)sbyte;
+          }
+        }
       }
     }
+  }
+}
+
+// Scale bytes [groups, rows, k/32] -> interleaved [groups, k/512, rows, 16]:
+// one 16-byte piece per thread, in the output's order (coalesced stores).
+__global__ __launch_bounds__(256) void scales_interleave_kernel(const uint4* __restrict__ src,
+                                                                uint4* __restrict__ dst, int64_t pieces,
+                                                                int64_t rows, int64_t gpr) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < pieces; d += stride) {
+    // d = (e * gpr + g) * rows + r  <-  source piece (e * rows + r) * gpr + g
+    const int64_t eg = d / rows, r = d - eg * rows;
+    const int64_t e = eg / gpr, g = eg - e * gpr;
+    dst[d] = src[(e * rows + r) * gpr + g];
   }
 }
 
@@ -225,15 +252,32 @@ hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q
 }
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t k, void* q, void* scales,
-                           hipStream_t stream, int num_cus) {
+                           hipStream_t stream, int num_cus, bool interleaved) {
   const int64_t nblocks = rows * (k / 32);
+  if (interleaved && (k % 512 != 0 || nblocks >= ((int64_t)1 << 31))) return hipErrorInvalidValue;
   const int64_t groups_needed = (nblocks + kQuantUnroll - 1) / kQuantUnroll;
   int64_t grid = (groups_needed + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
-                     (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, nblocks);
+  if (interleaved)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                       (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, nblocks, (uint32_t)(k / 32), (uint32_t)rows);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                       (const uint4*)x, (uint32_t*)q, (uint8_t*)scales, nblocks, (uint32_t)(k / 32), (uint32_t)rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_scales_interleave(const void* scales, int64_t groups, int64_t rows, int64_t k, void* out,
+                                    hipStream_t stream, int num_cus) {
+  if (k % 512 != 0 || groups < 1 || rows < 1) return hipErrorInvalidValue;
+  const int64_t gpr = k / 512, pieces = groups * rows * gpr;
+  int64_t grid = (pieces + 255) / 256;
+  const int64_t max_grid = (int64_t)num_cus * 8;
+  if (grid > max_grid) grid = max_grid;
+  hipLaunchKernelGGL(scales_interleave_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)scales,
+                     (uint4*)out, pieces, rows, gpr);
   return hipGetLastError();
 }
 

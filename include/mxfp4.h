@@ -172,6 +172,62 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Interleaved scale layout for the tile GEMMs (the counterpart on this
+ * machine of the "fp4_quantization" page's block_scales_interleave /
+ * block_scales_interleave_fp4: rank-2 scale factors rearranged into the
+ * layout the matrix path reads, and of grouped_quantize_dynamic_scaled_fp4_async,
+ * which stores scale factors in that layout as it quantizes).
+ *
+ * For an operand of `rows` rows and k % 512 == 0, the scale bytes of the
+ * row-major array scales[rows][k/32] are stored as scales_il[k/512][rows][16]:
+ *
+ *   scales_il[(kb / 16) * rows * 16 + r * 16 + kb % 16] = scales[r * k/32 + kb]
+ *
+ * so the sixteen scale bytes that cover one 512-wide K slab of a row sit next
+ * to the next row's.  The GEMM kernels copy a slab's scales of 64 rows with
+ * one 1 KB read instead of 64 reads of 16 bytes, each from its own cache line.
+ * The values are those of the row-major array: results are bit-identical to
+ * the row-major entry points'.  A grouped weight [num_groups, n, k/32] is
+ * interleaved per group: [num_groups][k/512][n][16].
+ *
+ * mxfp4_scales_interleave: scales [groups, rows, k/32] -> scales_il
+ *   [groups, k/512, rows, 16] (weights quantized once, offline).  Both arrays
+ *   16-byte aligned, not overlapping.  k a positive multiple of 512, at most
+ *   2^24; groups * rows * k <= 2^40.  groups == 0 or rows == 0 is a no-op.
+ * mxfp4_quantize_interleaved: mxfp4_quantize with the scales written
+ *   interleaved (codes as mxfp4_quantize).  k % 512 == 0 and
+ *   rows * k / 32 < 2^31.
+ * mxfp4_gemm_nt_interleaved: mxfp4_gemm_nt with both scale arrays
+ *   interleaved (A over its m rows, B over its n rows), always on the tile
+ *   kernels (256 x 256 tiles once they number at least the compute units,
+ *   else 128 x 128; mxfp4_gemm_nt_ex with MXFP4_KERNEL_TILE256 / TILE128 on
+ *   the row-major arrays gives the same bits).  No workspace.
+ * mxfp4_grouped_gemm_nt_interleaved: mxfp4_grouped_gemm_nt with a_s_il over
+ *   total_m rows and b_s_il interleaved per group; same kernels, offsets
+ *   handling and bits.  No workspace.
+ * For the GEMMs: k a positive multiple of 512, at most 2^24; m * k / 32 and
+ * n * k / 32 (total_m * k / 32 for the grouped A) below 2^31; scale arrays
+ * 16-byte aligned; every other argument as for the row-major entry point.
+ * Violations return MXFP4_ERR_INVALID_ARG.
+ */
+mxfp4_status_t mxfp4_scales_interleave(const void* scales, int64_t groups, int64_t rows, int64_t k,
+                                       void* scales_il, void* stream);
+
+mxfp4_status_t mxfp4_quantize_interleaved(const void* x_bf16, int64_t rows, int64_t k,
+                                          void* q, void* scales_il, void* stream);
+
+mxfp4_status_t mxfp4_gemm_nt_interleaved(const void* a_q, const void* a_s_il,
+                                         const void* b_q, const void* b_s_il,
+                                         void* c, mxfp4_out_t c_type,
+                                         int64_t m, int64_t n, int64_t k, void* stream);
+
+mxfp4_status_t mxfp4_grouped_gemm_nt_interleaved(const void* a_q, const void* a_s_il,
+                                                 const void* b_q, const void* b_s_il,
+                                                 const int32_t* offsets, int32_t num_groups,
+                                                 int64_t total_m, void* c, mxfp4_out_t c_type,
+                                                 int64_t n, int64_t k, void* stream);
+
+/*
  * Prepacked weights for the small-M (decode) GEMM.  The same NT GEMM as
  * mxfp4_gemm_nt (the "Packed MXFP4 & NVFP4 GEMM + mega-MoE" page, Summary:
  * mxfp4_gemm_nt; its decode shapes are the small-M case), with B, a weight

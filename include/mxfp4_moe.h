@@ -90,6 +90,18 @@ mxfp4_status_t mxfp4_moe_quantize_scatter(const void* x_bf16, int64_t tokens, in
                                           void* scales, void* stream);
 
 /*
+ * mxfp4_moe_quantize_scatter with the scale bytes written in the interleaved
+ * layout of include/mxfp4.h (scales_il [k/512, total_rows, 16]), the A operand
+ * of mxfp4_grouped_gemm_nt_interleaved; codes, and which rows are written, as
+ * mxfp4_moe_quantize_scatter.  k a positive multiple of 512 and
+ * total_rows * k / 32 < 2^31 (MXFP4_ERR_INVALID_ARG otherwise); other limits as
+ * above.
+ */
+mxfp4_status_t mxfp4_moe_quantize_scatter_interleaved(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                                      const int32_t* token_rows, int64_t total_rows, void* q,
+                                                      void* scales_il, void* stream);
+
+/*
  * The same with MXFP8 rows (mxfp8.h's format: q8 [total_rows, k] E4M3 codes,
  * 8-byte aligned), for the W4A8 grouped GEMM.
  */

@@ -148,6 +148,38 @@ def test_grouped_rejects_bad_arguments_on_host(lib):
     assert lib.mxfp4_grouped_gemm_nt(None, None, f, f, None, 4, 0, None, 0, 64, 128, None, 0, None) == 0
 
 
+def test_interleaved_entry_points_reject_bad_arguments_on_host(lib):
+    f = _fake
+    # interleaving: k a positive multiple of 512, 16-byte aligned arrays
+    assert lib.mxfp4_scales_interleave(f(), 1, 64, 256, f(), None) == 1
+    assert b"k % 512" in lib.mxfp4_last_error()
+    assert lib.mxfp4_scales_interleave(f(), -1, 64, 512, f(), None) == 1
+    assert lib.mxfp4_scales_interleave(f(0x1004), 1, 64, 512, f(), None) == 1
+    assert lib.mxfp4_scales_interleave(f(), 1, 64, 512, None, None) == 1
+    assert lib.mxfp4_scales_interleave(None, 0, 64, 512, None, None) == 0        # no groups: no-op
+    # quantizer: k % 512, rows * k / 32 < 2^31
+    assert lib.mxfp4_quantize_interleaved(f(), 4, 1024 + 32, f(), f(), None) == 1
+    assert lib.mxfp4_quantize_interleaved(f(), 1 << 27, 512, f(), f(), None) == 1
+    assert lib.mxfp4_quantize_interleaved(None, 0, 512, None, None, None) == 0   # no rows: no-op
+    # dense GEMM: k % 512, 16-byte aligned scale arrays, rows * k / 32 < 2^31 per operand
+    assert lib.mxfp4_gemm_nt_interleaved(f(), f(), f(), f(), f(), 0, 64, 64, 256, None) == 1
+    assert lib.mxfp4_gemm_nt_interleaved(f(), f(0x1004), f(), f(), f(), 0, 64, 64, 512, None) == 1
+    assert lib.mxfp4_gemm_nt_interleaved(f(), f(), f(), f(0x1004), f(), 0, 64, 64, 512, None) == 1
+    assert lib.mxfp4_gemm_nt_interleaved(f(), f(), f(), f(), f(), 0, 1 << 27, 64, 512, None) == 1
+    assert lib.mxfp4_gemm_nt_interleaved(f(), f(), f(), f(), f(), 7, 64, 64, 512, None) == 1
+    assert lib.mxfp4_gemm_nt_interleaved(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0   # m == 0: no-op
+    # grouped GEMM: the same plus the group count and the offsets pointer
+    assert lib.mxfp4_grouped_gemm_nt_interleaved(f(), f(), f(), f(), f(), 4, 64, f(), 0, 64, 1536 + 32, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt_interleaved(f(), f(), f(), f(), f(), 0, 64, f(), 0, 64, 512, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt_interleaved(f(), f(), f(), f(), None, 4, 64, f(), 0, 64, 512, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt_interleaved(f(), f(0x1008), f(), f(), f(), 4, 64, f(), 0, 64, 512, None) == 1
+    assert lib.mxfp4_grouped_gemm_nt_interleaved(None, None, f(), f(), None, 4, 0, None, 0, 64, 512, None) == 0
+    # scatter-quantize: k % 512, total_rows * k / 32 < 2^31
+    assert lib.mxfp4_moe_quantize_scatter_interleaved(f(), 4, 256, 2, f(), 8, f(), f(), None) == 1
+    assert lib.mxfp4_moe_quantize_scatter_interleaved(f(), 4, 512, 2, f(), (1 << 27), f(), f(), None) == 1
+    assert lib.mxfp4_moe_quantize_scatter_interleaved(None, 0, 512, 2, None, 8, None, None, None) == 0
+
+
 def test_workspace_queries(lib):
     assert lib.mxfp4_grouped_gemm_nt_workspace_size(100, 4, 64, 128) == 0
     # tile kernels need no workspace; split-K with one split needs none either
