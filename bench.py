@@ -5,7 +5,11 @@ One step = the whole path over one batch of synthetic input:
   dynamic BF16 -> MXFP4 quantization of the activation A, then the
   block-scaled FP4 NT GEMM to BF16.  The weight B is quantized once beforehand
   with the same kernel (a weight packer's job, outside the step); its
-  quantization time is reported separately.
+  quantization time is reported separately.  The prefill GEMMs and the MoE
+  layer keep their scale bytes in the interleaved layout the tile kernels copy
+  from (include/mxfp4.h): the activation quantizers write it directly, the
+  weights' scales are interleaved once with the weights; the same GEMMs on
+  row-major scales are reported beside them (`row_major_scales`).
 Primary workload: M = N = K = 4096 (TFLOP/s, 2*M*N*K per step).
 Secondary workload: decode M=128, N=14336, K=4096 (achieved HBM GB/s).
 Also reported: the grouped MoE layer (8192 tokens, top-4 of 64 experts,
@@ -39,7 +43,8 @@ measured with events over a region of back-to-back GEMM launches.
 `--only {step,gemm,quantize,quantize_b,copy}` instead runs that work eagerly
 `--steps` times and prints nothing on stdout: the mode used under rocprofv3
 (kernel traces and counter passes; `copy` is the plain device copy that
-calibrates the byte counters; `--w4a8-only` selects the W4A8 kernels).
+calibrates the byte counters; `--w4a8-only` selects the W4A8 kernels,
+`--row-major-scales` the MXFP4 path on row-major scales).
 """
 from __future__ import annotations
 
@@ -143,13 +148,18 @@ class DenseBench:
     """act = "mxfp4": the MXFP4 path; act = "mxfp8": W4A8 (MXFP8 activations,
     MXFP4 weights); act = "mxfp8x8": both operands MXFP8."""
 
-    def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4", quantize_b_in_step: bool = False):
+    def __init__(self, w: workloads.DenseWorkload, dev, act: str = "mxfp4", quantize_b_in_step: bool = False,
+                 interleaved: bool | None = None):
         from block_scaled_fp4_mxfp4_amd import binding as B
         self.B = B
         self.w = w
         self.dev = dev
         self.act = act
         self.with_b = quantize_b_in_step
+        # interleaved scales (the tile kernels' copy layout) wherever the MXFP4
+        # tile kernels run: prefill shapes with k % 512 == 0
+        il_ok = act == "mxfp4" and w.m > 128 and w.k % 512 == 0
+        self.il = il_ok if interleaved is None else (interleaved and il_ok)
         a8 = act in ("mxfp8", "mxfp8x8")
         k_a = w.k if a8 else w.k // 2                    # A code bytes per row
         k_b = w.k if act == "mxfp8x8" else w.k // 2      # B code bytes per row
@@ -158,6 +168,8 @@ class DenseBench:
         a_d, b_d = a.to(dev), b.to(dev)
         # weight quantized once (not in the step)
         bq, bs = B.mxfp8_quantize(b_d) if act == "mxfp8x8" else B.mxfp4_quantize(b_d)
+        if self.il:
+            bs = B.mxfp4_scales_interleave(bs)
         m, n, k = w.m, w.n, w.k
         per_set = m * k * 2 + m * k_a + m * k // 32 + n * k_b + n * k // 32 + m * n * 2
         if self.with_b:
@@ -170,8 +182,9 @@ class DenseBench:
         self.prepacked = act == "mxfp4" and m <= 128 and k % 512 == 0
         self.prepacked_b = act in ("mxfp4", "mxfp8") and m <= 128 and k % 512 == 0
         for _ in range(self.sets_n):
+            a_s_shape = (k // 512, m, 16) if self.il else (m, k // 32)
             st = dict(a=a_d.clone(), aq=torch.empty((m, k_a), dtype=torch.uint8, device=dev),
-                      as_=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
+                      as_=torch.empty(a_s_shape, dtype=torch.uint8, device=dev),
                       bq=bq.clone(), bs=bs.clone(), c=torch.empty((m, n), dtype=torch.bfloat16, device=dev))
             if self.with_b:
                 st["b"] = b_d.clone()
@@ -191,6 +204,8 @@ class DenseBench:
         s = self.sets[i % self.sets_n]
         if self.act in ("mxfp8", "mxfp8x8"):
             self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+        elif self.il:
+            self.B.mxfp4_quantize_interleaved(s["a"], s["aq"], s["as_"])
         else:
             self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
@@ -198,7 +213,10 @@ class DenseBench:
         """Quantizes the set's BF16 weight into the set's B operand (the bytes it
         already holds: the same quantization of the same weight)."""
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_quantize(s["b"], s["bq"], s["bs"])
+        if self.il:
+            self.B.mxfp4_quantize_interleaved(s["b"], s["bq"], s["bs"])
+        else:
+            self.B.mxfp4_quantize(s["b"], s["bq"], s["bs"])
 
     def step_quantize_both(self, i):
         self.quantize(i)
@@ -211,6 +229,8 @@ class DenseBench:
             self.B.mxfp8_gemm_w4a8_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         elif self.act == "mxfp8x8":
             self.B.mxfp8_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+        elif self.il:
+            self.B.mxfp4_gemm_nt_interleaved(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         else:
             self.B.mxfp4_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"], ws=self.ws)
 
@@ -289,11 +309,12 @@ class MoEBench:
     """The grouped per-expert workload: routed rows sorted by expert, one
     weight matrix per expert (quantized once), device offsets."""
 
-    def __init__(self, w: workloads.MoEWorkload, dev, act: str = "mxfp4"):
+    def __init__(self, w: workloads.MoEWorkload, dev, act: str = "mxfp4", interleaved: bool = True):
         from block_scaled_fp4_mxfp4_amd import binding as B
         self.B = B
         self.w = w
         self.act = act
+        self.il = interleaved and act == "mxfp4" and w.k % 512 == 0   # interleaved scales (see DenseBench)
         a, wts, offsets = w.make()
         self.counts = (offsets[1:] - offsets[:-1]).tolist()
         rows, n, k, e = w.total_rows, w.n, w.k, w.experts
@@ -301,6 +322,8 @@ class MoEBench:
         wq, ws = B.mxfp4_quantize(wts.view(e * n, k).to(dev))
         del wts
         wq, ws = wq.view(e, n, k // 2), ws.view(e, n, k // 32)
+        if self.il:
+            ws = B.mxfp4_scales_interleave(ws)
         off_d = offsets.to(dev)
         k_a = k if act == "mxfp8" else k // 2
         per_set = rows * k * 2 + rows * k_a + rows * k // 32 + e * n * k // 2 + e * n * k // 32 + rows * n * 2
@@ -309,7 +332,7 @@ class MoEBench:
         for _ in range(self.sets_n):
             self.sets.append(dict(
                 a=a_d.clone(), aq=torch.empty((rows, k_a), dtype=torch.uint8, device=dev),
-                as_=torch.empty((rows, k // 32), dtype=torch.uint8, device=dev),
+                as_=torch.empty((k // 512, rows, 16) if self.il else (rows, k // 32), dtype=torch.uint8, device=dev),
                 wq=wq.clone(), ws=ws.clone(), off=off_d.clone(),
                 c=torch.empty((rows, n), dtype=torch.bfloat16, device=dev)))
         del a_d, wq, ws
@@ -319,6 +342,8 @@ class MoEBench:
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
             self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+        elif self.il:
+            self.B.mxfp4_quantize_interleaved(s["a"], s["aq"], s["as_"])
         else:
             self.B.mxfp4_quantize(s["a"], s["aq"], s["as_"])
 
@@ -326,6 +351,8 @@ class MoEBench:
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
             self.B.mxfp8_grouped_gemm_w4a8_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
+        elif self.il:
+            self.B.mxfp4_grouped_gemm_nt_interleaved(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
         else:
             self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
 
@@ -349,8 +376,9 @@ class MoEBench:
 class MoELayerBench:
     """The whole MoE layer on the device: top-k routing of the router logits,
     the expert-sorted permutation, MXFP4 quantization scattered into the routed
-    rows, the grouped GEMM over the expert weights (quantized once), and the
-    weighted combine back to tokens."""
+    rows (scales interleaved), the grouped GEMM over the expert weights
+    (quantized once, scales interleaved once), and the weighted combine back to
+    tokens."""
 
     def __init__(self, w: workloads.MoEWorkload, dev):
         from block_scaled_fp4_mxfp4_amd import binding as B
@@ -363,7 +391,7 @@ class MoELayerBench:
         wts = workloads.gaussian_bf16((e * n, k), w.w_sigma, w.seed + workloads.ROLE_B)
         wq, ws = B.mxfp4_quantize(wts.to(dev))
         del wts
-        wq, ws = wq.view(e, n, k // 2), ws.view(e, n, k // 32)
+        wq, ws = wq.view(e, n, k // 2), B.mxfp4_scales_interleave(ws.view(e, n, k // 32))
         per_set = (t * k * 2 + t * e * 4 + rows * (k // 2 + k // 32) + e * n * (k // 2 + k // 32)
                    + rows * n * 2 + t * n * 2)
         self.sets_n = max(2, math.ceil(ROTATION_BYTES / per_set))
@@ -377,7 +405,7 @@ class MoELayerBench:
                 rt=torch.empty((rows,), dtype=torch.int32, device=dev),
                 tr=torch.empty((t, kk), dtype=torch.int32, device=dev),
                 aq=torch.empty((rows, k // 2), dtype=torch.uint8, device=dev),
-                as_=torch.empty((rows, k // 32), dtype=torch.uint8, device=dev),
+                as_=torch.empty((k // 512, rows, 16), dtype=torch.uint8, device=dev),
                 y=torch.empty((rows, n), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((t, n), dtype=torch.bfloat16, device=dev)))
         del x_d, lg_d, wq, ws
@@ -396,11 +424,11 @@ class MoELayerBench:
 
     def scatter(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_moe_quantize_scatter(s["x"], s["tr"], self.w.total_rows, s["aq"], s["as_"])
+        self.B.mxfp4_moe_quantize_scatter_interleaved(s["x"], s["tr"], self.w.total_rows, s["aq"], s["as_"])
 
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
-        self.B.mxfp4_grouped_gemm_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["y"])
+        self.B.mxfp4_grouped_gemm_nt_interleaved(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["y"])
 
     def combine(self, i):
         s = self.sets[i % self.sets_n]
@@ -439,7 +467,7 @@ def measure_moe_layer(args, dev, us):
     msteps = max(64, args.detail_steps // 2)
     nbytes = lb.algorithmic_bytes()
     out = {"workload": wm.name, "steps": msteps, "rotating_input_sets": lb.sets_n,
-           "step": "route + permute + scatter-quantize + grouped mxfp4 GEMM + combine",
+           "step": "route + permute + scatter-quantize + grouped mxfp4 GEMM + combine (interleaved scales)",
            "rows_per_expert": {"min": min(lb.counts), "max": max(lb.counts),
                                "empty": sum(c == 0 for c in lb.counts)}}
     st = lb.timed(lb.step, msteps, 2)
@@ -815,23 +843,30 @@ def measure_large(args, dev):
     for wl in (workloads.FFN_DOWN, workloads.SQUARE8192):
         eprint(f"[bench] building inputs for {wl.name}")
         b = DenseBench(wl, dev)
+        rows_sets = b.sets_n
         s = b.timed(b.step, args.detail_steps, args.detail_warmup)
         g = b.timed(b.gemm, args.detail_steps, args.detail_warmup)
         q = b.timed(b.quantize, args.detail_steps, args.detail_warmup)
         tf = wl.flops / (g["mean"] * 1e-3) / 1e12
         qbytes = quant_algorithmic_bytes(wl.m, wl.k)
+        del b
+        rm = DenseBench(wl, dev, interleaved=False)
+        g_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
+        del rm
         out[wl.name] = {
-            "m": wl.m, "n": wl.n, "k": wl.k, "rotating_input_sets": b.sets_n,
-            "step": "quantize A + mxfp4 NT GEMM -> bf16 (B pre-quantized)",
+            "m": wl.m, "n": wl.n, "k": wl.k, "rotating_input_sets": rows_sets,
+            "step": "quantize A + mxfp4 NT GEMM -> bf16 (B pre-quantized; interleaved scales)",
             "step_us": us(s), "step_tflops": round(wl.flops / (s["mean"] * 1e-3) / 1e12, 2),
             "gemm_us": us(g), "gemm_tflops": round(tf, 2),
             "quantize_a_us": us(q), "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
             "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s",
                                  traffic_from_profiles(wl.name, "gemm_tile_kernel"), kernel="gemm_tile_kernel"),
+            "row_major_scales": {"gemm_us": us(g_rm),
+                                 "gemm_tflops": round(wl.flops / (g_rm["mean"] * 1e-3) / 1e12, 2)},
             "inputs": dense_inputs_record(wl),
         }
-        eprint(f"[bench] {wl.name}: step {s['mean']*1e3:.1f} us, gemm {g['mean']*1e3:.1f} us ({tf:.0f} TFLOP/s)")
-        del b
+        eprint(f"[bench] {wl.name}: step {s['mean']*1e3:.1f} us, gemm {g['mean']*1e3:.1f} us ({tf:.0f} TFLOP/s); "
+               f"row-major scales {g_rm['mean']*1e3:.1f} us")
     return out
 
 
@@ -1019,9 +1054,10 @@ def run_only(args, dev):
         if args.only == "layer":
             args.only = "step"
     elif isinstance(w, workloads.MoEWorkload):
-        bench = MoEBench(w, dev, act)
+        bench = MoEBench(w, dev, act, interleaved=not args.row_major_scales)
     else:
-        bench = DenseBench(w, dev, act, quantize_b_in_step=args.only in ("quantize_b", "step_quantize_both"))
+        bench = DenseBench(w, dev, act, quantize_b_in_step=args.only in ("quantize_b", "step_quantize_both"),
+                           interleaved=False if args.row_major_scales else None)
     if not hasattr(bench, args.only):
         eprint(f"'{args.only}' is not a mode of {w.name}")
         sys.exit(2)
@@ -1070,6 +1106,8 @@ def main():
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
     ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 x MXFP8 measurement")
+    ap.add_argument("--row-major-scales", action="store_true",
+                    help="with --only: the MXFP4 dense and grouped kernels on row-major scales")
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="with --only gemm/quantize/step: both operands MXFP8 (the MXFP8 x MXFP8 GEMM)")
     args = ap.parse_args()
@@ -1110,6 +1148,14 @@ def main():
     eprint(f"[bench] step {step['mean']*1e3:.2f} us, gemm {gemm['mean']*1e3:.2f} us, "
            f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us, "
            f"step quantizing both operands {step_ab['mean']*1e3:.2f} us")
+    # the same step and GEMM on row-major scales (the quantizer's default layout)
+    rm = DenseBench(w, dev, interleaved=False)
+    step_rm = rm.timed(rm.step, args.detail_steps, args.detail_warmup)
+    gemm_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
+    quant_rm = rm.timed(rm.quantize, args.detail_steps, args.detail_warmup)
+    del rm
+    eprint(f"[bench] row-major scales: step {step_rm['mean']*1e3:.2f} us, gemm {gemm_rm['mean']*1e3:.2f} us, "
+           f"quantize {quant_rm['mean']*1e3:.2f} us")
 
     flops = w.flops
     gemm_tflops = flops / (gemm["mean"] * 1e-3) / 1e12
@@ -1133,6 +1179,7 @@ def main():
         "data": "synthetic (seeded Gaussian BF16; weights pre-quantized once)",
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k,
                    "step": "quantize A (bf16->mxfp4) + mxfp4 NT GEMM -> bf16",
+                   "scales": "interleaved [k/512, rows, 16] (written by the quantizer; the weight's once)",
                    "rotating_input_sets": bench.sets_n, "parallelism": "single GPU"},
         "roofline": roofline("mfma", gemm_tflops, PEAK_FP4_TFLOPS, "TFLOP/s",
                              traffic_from_profiles(w.name, "gemm_tile_kernel"), kernel="gemm_tile_kernel"),
@@ -1150,6 +1197,12 @@ def main():
         "step_quantize_both": {"step": "quantize A + quantize B + mxfp4 NT GEMM -> bf16",
                                "step_us": us(step_ab),
                                "step_tflops": round(flops / (step_ab["mean"] * 1e-3) / 1e12, 2)},
+        "row_major_scales": {"step": "the same step and GEMM with row-major scales [rows, k/32]",
+                             "step_us": us(step_rm),
+                             "step_tflops": round(flops / (step_rm["mean"] * 1e-3) / 1e12, 2),
+                             "gemm_us": us(gemm_rm),
+                             "gemm_tflops": round(flops / (gemm_rm["mean"] * 1e-3) / 1e12, 2),
+                             "quantize_a_us": us(quant_rm)},
     }
 
     if not args.no_large:
@@ -1176,7 +1229,7 @@ def main():
             "workload": wm.name, "tokens": wm.tokens, "experts": wm.experts, "top_k": wm.top_k,
             "n": wm.n, "k": wm.k, "steps": msteps, "rotating_input_sets": mb.sets_n,
             "rows_per_expert": {"min": min(counts), "max": max(counts), "empty": sum(c == 0 for c in counts)},
-            "step": "quantize routed A + grouped mxfp4 GEMM (expert weights pre-quantized)",
+            "step": "quantize routed A + grouped mxfp4 GEMM (expert weights pre-quantized; interleaved scales)",
             "step_us": us(sm), "step_tflops": round(wm.flops / (sm["mean"] * 1e-3) / 1e12, 2),
             "gemm_us": us(gm), "quantize_a_us": us(qm),
             "gemm_tflops": round(tf, 2), "gemm_mfma_frac": round(tf / PEAK_FP4_TFLOPS, 4),
@@ -1197,6 +1250,12 @@ def main():
         eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
         del mb
+        mr = MoEBench(wm, dev, interleaved=False)
+        gm_rm = mr.timed(mr.gemm, msteps, 2)
+        del mr
+        result["moe"]["row_major_scales"] = {
+            "gemm_us": us(gm_rm), "gemm_tflops": round(wm.flops / (gm_rm["mean"] * 1e-3) / 1e12, 2)}
+        eprint(f"[bench] {wm.name}: grouped gemm on row-major scales {gm_rm['mean']*1e3:.1f} us")
 
     if args.moe != "none" and not args.no_moe_layer:
         result["moe_layer"] = measure_moe_layer(args, dev, us)

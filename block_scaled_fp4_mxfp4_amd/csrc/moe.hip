@@ -342,11 +342,12 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(uint32_t w01, uint32_t w23, float 
 // FP8 = false: MXFP4 rows (K/2 code bytes, 4 per lane); true: MXFP8 rows
 // (K code bytes, 8 per lane).  Scale rule and converts as in the dense
 // quantizers: byte = max(E - 2, 0) (FP4) or max(E - 8, 0) (FP8) for amax's
-// biased exponent E.
-template <bool FP8>
+// biased exponent E.  IL (MXFP4 only): scale bytes in the interleaved layout
+// [k/512, total_rows, 16].
+template <bool FP8, bool IL>
 __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
     const uint4* __restrict__ x, int kblocks, int nblocks, int top_k, const int32_t* __restrict__ token_rows,
-    int total_rows, uint8_t* __restrict__ q, uint8_t* __restrict__ scales, int s_row, int s_piece) {
+    int total_rows, uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
   const int lane4 = threadIdx.x & 3;
   const int groups_per_grid = gridDim.x * (kScatterThreads / 4);
   // kScatterUnroll blocks per lane group per iteration: all their loads are in
@@ -390,9 +391,12 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
         } else {
           *(uint32_t*)(q + (int64_t)r * kblocks * 16 + kb * 16 + lane4 * 4) = codes4;
         }
-        // scale byte of 32-block kb of row r: piece kb / 16 at r * s_row + (kb / 16) * s_piece
-        // (row-major: s_row = k/32, s_piece = 16; interleaved: 16 and total_rows * 16)
-        if (lane4 == 0) scales[(int64_t)r * s_row + (int64_t)(kb >> 4) * s_piece + (kb & 15)] = (uint8_t)sbyte;
+        if (lane4 == 0) {
+          if constexpr (IL)   // interleaved [k/512, total_rows, 16]: total_rows * k/32 < 2^31
+            scales[(uint32_t)(kb >> 4) * (uint32_t)total_rows * 16 + (uint32_t)r * 16 + (kb & 15)] = (uint8_t)sbyte;
+          else
+            scales[(int64_t)r * kblocks + kb] = (uint8_t)sbyte;
+        }
       }
     }
   }
@@ -511,21 +515,16 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
   const int kblocks = k / 32;
   if (interleaved && (fp8 || k % 512 != 0 || (int64_t)total_rows * kblocks >= ((int64_t)1 << 31)))
     return hipErrorInvalidValue;
-  const int s_row = interleaved ? 16 : kblocks, s_piece = interleaved ? total_rows * 16 : 16;
   const int nblocks = tokens * kblocks;   // the host keeps this below 2^31
   const int64_t groups_needed = ((int64_t)nblocks + kScatterUnroll - 1) / kScatterUnroll;
   int64_t grid = (groups_needed + (kScatterThreads / 4) - 1) / (kScatterThreads / 4);
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  if (fp8)
-    hipLaunchKernelGGL(quantize_scatter_kernel<true>, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream,
-                       (const uint4*)x, kblocks, nblocks, top_k, token_rows, total_rows, (uint8_t*)q,
-                       (uint8_t*)scales, s_row, s_piece);
-  else
-    hipLaunchKernelGGL(quantize_scatter_kernel<false>, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream,
-                       (const uint4*)x, kblocks, nblocks, top_k, token_rows, total_rows, (uint8_t*)q,
-                       (uint8_t*)scales, s_row, s_piece);
+  const auto kernel = fp8 ? quantize_scatter_kernel<true, false>
+                          : (interleaved ? quantize_scatter_kernel<false, true> : quantize_scatter_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream, (const uint4*)x, kblocks,
+                     nblocks, top_k, token_rows, total_rows, (uint8_t*)q, (uint8_t*)scales);
   return hipGetLastError();
 }
 

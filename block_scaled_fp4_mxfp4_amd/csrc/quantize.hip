@@ -9,8 +9,13 @@
 // rows x K input is a flat sequence of blocks; block b reads bytes [64b, 64b+64)
 // of x, writes bytes [16b, 16b+16) of q and byte b of the scales.  With
 // interleaved scales (k % 512 == 0, the tile GEMMs' copy layout
-// [k/512, rows, 16]) the scale byte of block kb of row r goes to
-// (kb / 16) * rows * 16 + r * 16 + kb % 16 instead.
+// [k/512, rows, 16]) the blocks are walked in the order of that layout
+// instead: step b is block 16 g + b % 16 of row r, where b / 16 = g * rows + r,
+// and writes scale byte b.  Each wave still reads one 1 KB run of x (the 16
+// blocks of one 512-wide slab of a row), and each 128-byte line of scales is
+// written by neighbouring waves: walked in row order, a line of the
+// interleaved layout would collect the pieces of 8 rows from workgroups on
+// different XCDs, each writing back its part of the line.
 //
 // Mapping: 4 lanes per block, 16 bytes (8 BF16) per lane, so one wave64 covers
 // 16 blocks with 1 KiB of fully coalesced loads.  HBM-bound: 2.53125 bytes per
@@ -59,7 +64,7 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 }
 
 // IL: interleaved scales; then rows * k/32 < 2^31 (`bpr` = k/32 blocks per
-// row, a multiple of 16), so the scale index fits 32 bits.
+// row, a multiple of 16), so block indices fit 32 bits.
 template <bool IL>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ scales,
@@ -70,12 +75,18 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
 
   for (; blk < nblocks; blk += groups_per_grid * kQuantUnroll) {
     uint4 v[kQuantUnroll];
+    int64_t src[kQuantUnroll];   // the step's block in x and q (row-major order)
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
       const int64_t b = blk + u * groups_per_grid;
+      src[u] = b;
+      if constexpr (IL) {
+        const uint32_t piece = (uint32_t)b >> 4, g = piece / rows, r = piece - g * rows;
+        src[u] = (int64_t)r * bpr + g * 16 + ((uint32_t)b & 15);
+      }
       // out-of-range groups load a valid block (block 0) and store nothing
       // BF16 input read once: non-temporal (same-box A/B on 4096 x 4096: 9.73-9.84 vs 9.84-10.19 us)
-      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? b : 0) * 4 + lane4));
+      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? src[u] : 0) * 4 + lane4));
       v[u] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
     }
 #pragma unroll
@@ -95,15 +106,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].z), scale, 2);
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2_t, v[u].w), scale, 3);
       if (b < nblocks) {
-        q[b * 4 + lane4] = packed;
-        if (lane4 == 0) {
-          if constexpr (IL) {
-            const uint32_t r = (uint32_t)b / bpr, kb = (uint32_t)b - r * bpr;
-            scales[(kb >> 4) * rows * 16 + r * 16 + (kb & 15)] = (uint8_t)sbyte;
-          } else {
-            scales[b] = (uint8_t)sbyte;
-          }
-        }
+        q[src[u] * 4 + lane4] = packed;
+        if (lane4 == 0) scales[b] = (uint8_t)sbyte;
       }
     }
   }
