@@ -850,9 +850,11 @@ def measure_large(args, dev):
         tf = wl.flops / (g["mean"] * 1e-3) / 1e12
         qbytes = quant_algorithmic_bytes(wl.m, wl.k)
         del b
-        rm = DenseBench(wl, dev, interleaved=False)
-        g_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
-        del rm
+        g_rm = None
+        if not args.no_row_major:
+            rm = DenseBench(wl, dev, interleaved=False)
+            g_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
+            del rm
         out[wl.name] = {
             "m": wl.m, "n": wl.n, "k": wl.k, "rotating_input_sets": rows_sets,
             "step": "quantize A + mxfp4 NT GEMM -> bf16 (B pre-quantized; interleaved scales)",
@@ -861,12 +863,13 @@ def measure_large(args, dev):
             "quantize_a_us": us(q), "quantize_a_gbs": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1),
             "roofline": roofline("mfma", tf, PEAK_FP4_TFLOPS, "TFLOP/s",
                                  traffic_from_profiles(wl.name, "gemm_tile_kernel"), kernel="gemm_tile_kernel"),
-            "row_major_scales": {"gemm_us": us(g_rm),
-                                 "gemm_tflops": round(wl.flops / (g_rm["mean"] * 1e-3) / 1e12, 2)},
             "inputs": dense_inputs_record(wl),
         }
-        eprint(f"[bench] {wl.name}: step {s['mean']*1e3:.1f} us, gemm {g['mean']*1e3:.1f} us ({tf:.0f} TFLOP/s); "
-               f"row-major scales {g_rm['mean']*1e3:.1f} us")
+        if g_rm:
+            out[wl.name]["row_major_scales"] = {"gemm_us": us(g_rm),
+                                                "gemm_tflops": round(wl.flops / (g_rm["mean"] * 1e-3) / 1e12, 2)}
+        eprint(f"[bench] {wl.name}: step {s['mean']*1e3:.1f} us, gemm {g['mean']*1e3:.1f} us ({tf:.0f} TFLOP/s)"
+               + (f"; row-major scales {g_rm['mean']*1e3:.1f} us" if g_rm else ""))
     return out
 
 
@@ -1106,6 +1109,8 @@ def main():
                     help="with --only: MXFP8 activations (W4A8 quantizer / GEMM) instead of MXFP4")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 activation) measurements")
     ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 x MXFP8 measurement")
+    ap.add_argument("--no-row-major", action="store_true",
+                    help="skip the row-major-scale comparisons (the same kernels on the other scale layout)")
     ap.add_argument("--row-major-scales", action="store_true",
                     help="with --only: the MXFP4 dense and grouped kernels on row-major scales")
     ap.add_argument("--mxfp8-only", action="store_true",
@@ -1149,13 +1154,14 @@ def main():
            f"quantize {quant['mean']*1e3:.2f} us, weight quantize {quant_b['mean']*1e3:.2f} us, "
            f"step quantizing both operands {step_ab['mean']*1e3:.2f} us")
     # the same step and GEMM on row-major scales (the quantizer's default layout)
-    rm = DenseBench(w, dev, interleaved=False)
-    step_rm = rm.timed(rm.step, args.detail_steps, args.detail_warmup)
-    gemm_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
-    quant_rm = rm.timed(rm.quantize, args.detail_steps, args.detail_warmup)
-    del rm
-    eprint(f"[bench] row-major scales: step {step_rm['mean']*1e3:.2f} us, gemm {gemm_rm['mean']*1e3:.2f} us, "
-           f"quantize {quant_rm['mean']*1e3:.2f} us")
+    if not args.no_row_major:
+        rm = DenseBench(w, dev, interleaved=False)
+        step_rm = rm.timed(rm.step, args.detail_steps, args.detail_warmup)
+        gemm_rm = rm.timed(rm.gemm, args.detail_steps, args.detail_warmup)
+        quant_rm = rm.timed(rm.quantize, args.detail_steps, args.detail_warmup)
+        del rm
+        eprint(f"[bench] row-major scales: step {step_rm['mean']*1e3:.2f} us, gemm {gemm_rm['mean']*1e3:.2f} us, "
+               f"quantize {quant_rm['mean']*1e3:.2f} us")
 
     flops = w.flops
     gemm_tflops = flops / (gemm["mean"] * 1e-3) / 1e12
@@ -1197,13 +1203,14 @@ def main():
         "step_quantize_both": {"step": "quantize A + quantize B + mxfp4 NT GEMM -> bf16",
                                "step_us": us(step_ab),
                                "step_tflops": round(flops / (step_ab["mean"] * 1e-3) / 1e12, 2)},
-        "row_major_scales": {"step": "the same step and GEMM with row-major scales [rows, k/32]",
-                             "step_us": us(step_rm),
-                             "step_tflops": round(flops / (step_rm["mean"] * 1e-3) / 1e12, 2),
-                             "gemm_us": us(gemm_rm),
-                             "gemm_tflops": round(flops / (gemm_rm["mean"] * 1e-3) / 1e12, 2),
-                             "quantize_a_us": us(quant_rm)},
     }
+    if not args.no_row_major:
+        result["row_major_scales"] = {"step": "the same step and GEMM with row-major scales [rows, k/32]",
+                                      "step_us": us(step_rm),
+                                      "step_tflops": round(flops / (step_rm["mean"] * 1e-3) / 1e12, 2),
+                                      "gemm_us": us(gemm_rm),
+                                      "gemm_tflops": round(flops / (gemm_rm["mean"] * 1e-3) / 1e12, 2),
+                                      "quantize_a_us": us(quant_rm)}
 
     if not args.no_large:
         result["prefill_large"] = measure_large(args, dev)
@@ -1250,12 +1257,13 @@ def main():
         eprint(f"[bench] {wm.name}: step {sm['mean']*1e3:.1f} us, grouped gemm {gm['mean']*1e3:.1f} us "
                f"({tf:.0f} TFLOP/s, {gbs:.0f} GB/s)")
         del mb
-        mr = MoEBench(wm, dev, interleaved=False)
-        gm_rm = mr.timed(mr.gemm, msteps, 2)
-        del mr
-        result["moe"]["row_major_scales"] = {
-            "gemm_us": us(gm_rm), "gemm_tflops": round(wm.flops / (gm_rm["mean"] * 1e-3) / 1e12, 2)}
-        eprint(f"[bench] {wm.name}: grouped gemm on row-major scales {gm_rm['mean']*1e3:.1f} us")
+        if not args.no_row_major:
+            mr = MoEBench(wm, dev, interleaved=False)
+            gm_rm = mr.timed(mr.gemm, msteps, 2)
+            del mr
+            result["moe"]["row_major_scales"] = {
+                "gemm_us": us(gm_rm), "gemm_tflops": round(wm.flops / (gm_rm["mean"] * 1e-3) / 1e12, 2)}
+            eprint(f"[bench] {wm.name}: grouped gemm on row-major scales {gm_rm['mean']*1e3:.1f} us")
 
     if args.moe != "none" and not args.no_moe_layer:
         result["moe_layer"] = measure_moe_layer(args, dev, us)
