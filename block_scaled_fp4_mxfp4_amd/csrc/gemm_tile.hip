@@ -856,14 +856,32 @@ __device__ __forceinline__ bool find_expert(const int32_t* offsets, int groups, 
   return false;
 }
 
+// Tile `local` of an expert with `cnt` m-tiles: the expert's m-tiles go in
+// groups of four, and inside a group the m-tile runs fastest, then the
+// n-tile.  Consecutive tiles (dealt to neighbouring workgroups of one XCD in
+// the same round) then share a weight panel across the group's m-tiles and an
+// A panel across the n-tiles a round covers: about 4 A panels and 8 weight
+// panels per 32 tiles.  Plain n-tile-major order (the same thing for experts
+// of at most four m-tiles) reads the A panels of all of a large expert's
+// m-tiles in every round: MoE layer 255.5-256.1 -> 251.3-252.2 us on one box
+// (groups of two 252.5-253.8, of eight 252.1-254.1).
+__device__ __forceinline__ void expert_tile(int local, int cnt, int tiles_n, int& tn, int& mi) {
+  constexpr int GM = 4;
+  const int grp = local / (GM * tiles_n);
+  const int rest = local - grp * GM * tiles_n;
+  const int gm = min(GM, cnt - grp * GM);   // the last group may hold fewer m-tiles
+  tn = rest / gm;
+  mi = grp * GM + rest - tn * gm;
+}
+
 // The grid is a multiple of 8 workgroups covering at least every possible
 // m-tile (the host cannot see the device offsets).  Workgroups are dispatched
 // to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; the real tiles
 // are split evenly over the XCDs as contiguous ranges (consecutive tiles of one
 // expert share that XCD's L2), and the spare workgroups of every XCD exit.
-// Inside an expert the tiles run n-tile-major, as in the persistent kernel:
-// the m-tiles that read one weight panel start together on one XCD (W4A8 MoE
-// layer 412 -> 407 us on one box).
+// Inside an expert the tiles run in the order of expert_tile, as in the
+// persistent kernel (n-tile-major, its special case for small experts: W4A8
+// MoE layer 412 -> 407 us on one box against m-tile-major).
 template <class C, bool COPY>
 __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -875,9 +893,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_tile_kernel(GemmArgs args,
   ExpertTiles e;
   if (!find_expert(args.offsets, args.groups, args.m, C::BM, t / tiles_n, e)) return;
   const int local = t - e.first * tiles_n;   // in [0, cnt * tiles_n)
-  const int tn = local / e.cnt;
+  int tn, mi;
+  expert_tile(local, e.cnt, tiles_n, tn, mi);
   RowRange ar;
-  ar.lo = e.lo + (local - tn * e.cnt) * C::BM;
+  ar.lo = e.lo + mi * C::BM;
   ar.end = min(e.hi, ar.lo + C::BM);
   ar.last = ar.end - 1;
   const int g = e.g;
@@ -1096,13 +1115,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_persistent_kernel(GemmArgs ar
 }
 
 // Grouped persistent kernel.  The real tiles (counted from the sanitized
-// offsets) are numbered expert by expert and, inside an expert, n-tile-major:
-// the m-tiles that share one weight panel are neighbours, dealt to
-// neighbouring workgroups of one XCD in the same round, so the later readers
-// of the panel can find it in that XCD's L2 (measured ~1 % faster than
-// m-tile-major on a 64-expert MoE layer).  The numbered tiles split evenly
-// over the 8 XCDs as contiguous ranges, each range dealt round-robin to its
-// XCD's workgroups.
+// offsets) are numbered expert by expert and, inside an expert, in the order
+// of expert_tile: the m-tiles that share one weight panel are neighbours,
+// dealt to neighbouring workgroups of one XCD in the same round, so the later
+// readers of the panel can find it in that XCD's L2 (n-tile-major measured
+// ~1 % faster than m-tile-major on a 64-expert MoE layer, the groups of four
+// m-tiles another ~1.5 %).  The numbered tiles split evenly over the 8 XCDs
+// as contiguous ranges, each range dealt round-robin to its XCD's workgroups.
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_persistent_kernel(GemmArgs args, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1117,8 +1136,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_persistent_kernel(GemmArgs
     int tn = 0;
     if (find_expert(args.offsets, args.groups, args.m, C::BM, t / tiles_n, e)) {
       const int local = t - e.first * tiles_n;   // in [0, cnt * tiles_n)
-      tn = local / e.cnt;
-      jb.ar.lo = e.lo + (local - tn * e.cnt) * C::BM;
+      int mi;
+      expert_tile(local, e.cnt, tiles_n, tn, mi);
+      jb.ar.lo = e.lo + mi * C::BM;
       jb.ar.end = min(e.hi, jb.ar.lo + C::BM);
       jb.ar.last = jb.ar.end - 1;
     } else {
