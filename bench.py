@@ -190,9 +190,10 @@ class DenseBench:
                 st["b"] = b_d.clone()
             if self.prepacked_b:
                 st["bp_q"], st["bp_s"] = B.mxfp4_prepack_weight(st["bq"], st["bs"])
-            if self.prepacked:
+            if self.prepacked or (self.prepacked_b and act == "mxfp8"):
                 cb, sb = B.mxfp4_prepacked_weight_size(m, k)
-                st["ap_q"] = torch.empty(cb, dtype=torch.uint8, device=dev)
+                # the activation in the MXFP4 prepacked layout, or in the FP8 one (twice the code bytes)
+                st["ap_q"] = torch.empty(cb if act == "mxfp4" else 2 * cb, dtype=torch.uint8, device=dev)
                 st["ap_s"] = torch.empty(sb, dtype=torch.uint8, device=dev)
             self.sets.append(st)
         need = B.load_library().mxfp4_gemm_nt_workspace_size(m, n, k)
@@ -245,6 +246,19 @@ class DenseBench:
     def step_w4a8_prepacked(self, i):
         self.quantize(i)
         self.gemm_w4a8_prepacked(i)
+
+    def quantize_w4a8_both_prepacked(self, i):
+        s = self.sets[i % self.sets_n]
+        self.B.mxfp8_quantize_prepacked(s["a"], s["ap_q"], s["ap_s"])
+
+    def gemm_w4a8_both_prepacked(self, i):
+        s = self.sets[i % self.sets_n]
+        w = self.w
+        self.B.mxfp8_gemm_w4a8_nt_prepacked_ab(s["ap_q"], s["ap_s"], s["bp_q"], s["bp_s"], w.m, w.n, w.k, c=s["c"])
+
+    def step_w4a8_both_prepacked(self, i):
+        self.quantize_w4a8_both_prepacked(i)
+        self.gemm_w4a8_both_prepacked(i)
 
     def step(self, i):
         self.quantize(i)
@@ -803,6 +817,8 @@ def measure_w4a8(args, dev, w, us):
         s2 = b2.timed(b2.step_w4a8_prepacked if pre else b2.step, args.detail_steps, args.detail_warmup)
         g2 = b2.timed(b2.gemm_w4a8_prepacked if pre else b2.gemm, args.detail_steps, args.detail_warmup)
         gu = b2.timed(b2.gemm, args.detail_steps, args.detail_warmup) if pre else g2
+        gpp = b2.timed(b2.gemm_w4a8_both_prepacked, args.detail_steps, args.detail_warmup) if pre else None
+        spp = b2.timed(b2.step_w4a8_both_prepacked, args.detail_steps, args.detail_warmup) if pre else None
         gbytes = w4a8_algorithmic_bytes(w2.m, w2.n, w2.k)
         gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
         out["decode"] = {
@@ -814,8 +830,16 @@ def measure_w4a8(args, dev, w, us):
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "kernel": "gemm_stream_pre_kernel (fp8 A)" if pre else "gemm_stream_kernel (fp8 A)"},
         }
+        if pre:
+            # both operands prepacked: A quantized straight into the FP8 prepacked layout, no LDS in the GEMM
+            gbs_pp = gbytes / (gpp["mean"] * 1e-3) / 1e9
+            out["decode"]["both_prepacked"] = {
+                "step": "quantize A into the FP8 prepacked layout + W4A8 GEMM on both prepacked operands",
+                "step_us": us(spp), "gemm_us": us(gpp), "gemm_gbs": round(gbs_pp, 1),
+                "gemm_hbm_frac": round(gbs_pp / PEAK_HBM_GBS, 4), "kernel": "gemm_pp_kernel (fp8 A)"}
         eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s; "
-               f"row-major weight {gu['mean']*1e3:.2f} us)")
+               f"row-major weight {gu['mean']*1e3:.2f} us"
+               + (f"; both prepacked {gpp['mean']*1e3:.2f} us)" if pre else ")"))
         del b2
     if args.moe != "none":
         wm = workloads.ALL[args.moe]

@@ -36,6 +36,7 @@ EXPORTED = (
     "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked",
     "mxfp4_scales_interleave", "mxfp4_quantize_interleaved", "mxfp4_gemm_nt_interleaved",
     "mxfp4_grouped_gemm_nt_interleaved", "mxfp4_moe_quantize_scatter_interleaved",
+    "mxfp8_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked_ab",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -126,6 +127,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         lib.mxfp4_moe_permute.restype = ctypes.c_int
         lib.mxfp4_moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+        lib.mxfp8_quantize_prepacked.restype = ctypes.c_int
+        lib.mxfp8_quantize_prepacked.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp8_gemm_w4a8_nt_prepacked_ab.restype = ctypes.c_int
+        lib.mxfp8_gemm_w4a8_nt_prepacked_ab.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.mxfp4_scales_interleave.restype = ctypes.c_int
         lib.mxfp4_scales_interleave.argtypes = [vp, i64, i64, i64, vp, vp]
         lib.mxfp4_quantize_interleaved.restype = ctypes.c_int
@@ -340,6 +345,39 @@ def mxfp4_quantize_prepacked(x, ap_q=None, ap_s=None, stream=None):
     _require(ap_s, "ap_s", torch.uint8, (sb,))
     _check(lib.mxfp4_quantize_prepacked(_ptr(x), rows, k, _ptr(ap_q), _ptr(ap_s), _stream(stream)))
     return ap_q, ap_s
+
+
+def mxfp8_quantize_prepacked(x, ap_q8=None, ap_s=None, stream=None):
+    """BF16 [rows, k] -> MXFP8 in the FP8 prepacked layout (include/mxfp8.h); returns (ap_q8, ap_s) as flat
+    uint8 (ap_q8 twice the MXFP4 prepacked code bytes, ap_s the same scale bytes)."""
+    lib = load_library()
+    rows, k = x.shape
+    _require(x, "x", torch.bfloat16, (rows, k))
+    cb, sb = mxfp4_prepacked_weight_size(rows, k)
+    if ap_q8 is None:
+        ap_q8 = torch.empty(2 * cb, dtype=torch.uint8, device=x.device)
+    if ap_s is None:
+        ap_s = torch.empty(sb, dtype=torch.uint8, device=x.device)
+    _require(ap_q8, "ap_q8", torch.uint8, (2 * cb,))
+    _require(ap_s, "ap_s", torch.uint8, (sb,))
+    _check(lib.mxfp8_quantize_prepacked(_ptr(x), rows, k, _ptr(ap_q8), _ptr(ap_s), _stream(stream)))
+    return ap_q8, ap_s
+
+
+def mxfp8_gemm_w4a8_nt_prepacked_ab(ap_q8, ap_s, bp_q, bp_s, m: int, n: int, k: int, c=None,
+                                    out_dtype=torch.bfloat16, stream=None):
+    """W4A8 C[m, n] = A . B^T with A in the FP8 prepacked layout and B prepacked (mxfp4_prepack_weight)."""
+    lib = load_library()
+    cba, sba = mxfp4_prepacked_weight_size(m, k)
+    cbb, sbb = mxfp4_prepacked_weight_size(n, k)
+    _require(ap_q8, "ap_q8", torch.uint8, (2 * cba,))
+    _require(ap_s, "ap_s", torch.uint8, (sba,))
+    _require(bp_q, "bp_q", torch.uint8, (cbb,))
+    _require(bp_s, "bp_s", torch.uint8, (sbb,))
+    c, code = _out(c, m, n, out_dtype, ap_q8.device)
+    _check(lib.mxfp8_gemm_w4a8_nt_prepacked_ab(_ptr(ap_q8), _ptr(ap_s), _ptr(bp_q), _ptr(bp_s), _ptr(c), code, m, n,
+                                               k, _stream(stream)))
+    return c
 
 
 def mxfp4_gemm_nt_prepacked_ab(ap_q, ap_s, bp_q, bp_s, m: int, n: int, k: int, c=None, out_dtype=torch.bfloat16,

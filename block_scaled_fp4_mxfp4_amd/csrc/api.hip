@@ -436,6 +436,52 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked(const void* a_q8, const void* a_s, c
                     "prepacked w4a8 gemm launch");
 }
 
+mxfp4_status_t mxfp8_quantize_prepacked(const void* x_bf16, int64_t rows, int64_t k, void* ap_q8, void* ap_s,
+                                        void* stream) {
+  int64_t cb, sb;
+  MXFP4_TRY(mxfp4_prepacked_weight_size(rows, k, &cb, &sb));
+  if (rows == 0) return MXFP4_OK;
+  if ((rows + 63) / 64 * 64 > ((int64_t)1 << 40) / k) return fail(MXFP4_ERR_INVALID_ARG, "rows * k too large");
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(ap_q8, "ap_q8"));
+  MXFP4_TRY(check_ptr(ap_s, "ap_s", 1));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_quantize_mxfp8_prepacked(x_bf16, rows, k, ap_q8, ap_s, (hipStream_t)stream,
+                                                           dev.num_cus), "mxfp8 prepacked quantize launch");
+}
+
+mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked_ab(const void* ap_q8, const void* ap_s, const void* bp_q,
+                                               const void* bp_s, void* c, mxfp4_out_t c_type, int64_t m, int64_t n,
+                                               int64_t k, void* stream) {
+  if (m < 0 || n < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative size");
+  if (m > kMaxDim || n > kMaxDim) return fail(MXFP4_ERR_INVALID_ARG, "m or n too large");
+  MXFP4_TRY(check_k(k));
+  if (k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (c_type != MXFP4_OUT_BF16 && c_type != MXFP4_OUT_F32)
+    return fail(MXFP4_ERR_INVALID_ARG, "unknown output type %d", (int)c_type);
+  if (m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(ap_q8, "ap_q8"));
+  MXFP4_TRY(check_ptr(ap_s, "ap_s"));
+  MXFP4_TRY(check_ptr(bp_q, "bp_q"));
+  MXFP4_TRY(check_ptr(bp_s, "bp_s"));
+  MXFP4_TRY(check_ptr(c, "c"));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)ap_q8;
+  args.a_s = (const uint8_t*)ap_s;
+  args.b_q = (const uint8_t*)bp_q;
+  args.b_s = (const uint8_t*)bp_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  return hip_status(mxfp4::launch_gemm_w4a8_both_prepacked(args, (hipStream_t)stream),
+                    "both-prepacked w4a8 gemm launch");
+}
+
 mxfp4_status_t mxfp4_quantize_prepacked(const void* x_bf16, int64_t rows, int64_t k, void* ap_q, void* ap_s,
                                         void* stream) {
   int64_t cb, sb;

@@ -725,20 +725,30 @@ hipError_t launch_pre_cfg(const GemmArgs& args, hipStream_t stream) {
 //
 // Row tiles: BM = 32 * MB rows of A.  MB = 4 and 2 cover whole 64-row A
 // panels (two and one); MB = 1 covers half a panel (j_a = tile % 2).
-template <int MB>
+//
+// A8 (W4A8): A in the FP8 prepacked layout (include/mxfp8.h): per pair, wave
+// and u = 2s + j, two 1 KB pieces holding each lane's first and last 16 codes
+// (32 KB per panel and pair instead of 16 KB); the scale bytes as for MXFP4.
+// The per-wave k-step split, the MFMA order and the reduction are those of
+// the W4A8 prepacked-weight streaming kernel, so the results are bit-identical
+// to it.
+template <int MB, bool A8>
 struct PPPair {
-  v4i a[MB][2];   // [row block][stage]
+  typename std::conditional<A8, v8i, v4i>::type a[MB][2];   // [row block][stage]
   v4i b[4];       // [2s + j]
   int sa[MB > 1 ? MB / 2 : 1];   // one scale word per A panel
   int sb;
 };
 
-constexpr int kPPDepth = 4;   // pairs in each wave's register ring
+constexpr int kPPDepth = 4;    // pairs in each wave's register ring
+constexpr int kPPDepth8 = 2;   // the same with FP8 A (twice the A registers per pair)
+constexpr int kPre8CodeBlock = 32 * 1024;   // FP8 A codes per 64-row panel and 512-K pair
 
-template <int MB>
-__device__ __forceinline__ void pp_load(PPPair<MB>& r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
+template <int MB, bool A8>
+__device__ __forceinline__ void pp_load(PPPair<MB, A8>& r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsb, uint32_t qoff,
-                                        uint32_t soff, uint32_t a_panel_q, uint32_t a_panel_s, int ja, int p) {
+                                        uint32_t aoff, uint32_t soff, uint32_t a_panel_q, uint32_t a_panel_s, int ja,
+                                        int p) {
   // Every offset is in the per-lane offset, which the buffer range check
   // covers: a pair past the last reads zeros without touching memory.  The
   // scheduling barriers keep each pair's loads together where they are
@@ -756,9 +766,17 @@ __device__ __forceinline__ void pp_load(PPPair<MB>& r, __amdgpu_buffer_rsrc_t ra
     const int panel = MB > 1 ? i / 2 : 0;
     const int j = MB > 1 ? (i & 1) : ja;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      r.a[i][s] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, pq + panel * a_panel_q + (2 * s + j) * 1024, 0, 0));
+    for (int s = 0; s < 2; ++s) {
+      if constexpr (A8) {
+        const uint32_t pa = aoff + (uint32_t)p * kPre8CodeBlock + panel * a_panel_q + (2 * s + j) * 2048;
+        const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, pa, 0, 0));
+        const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, pa + 1024, 0, 0));
+        r.a[i][s] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        r.a[i][s] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, pq + panel * a_panel_q + (2 * s + j) * 1024, 0, 0));
+      }
+    }
   }
 #pragma unroll
   for (int pn = 0; pn < (MB > 1 ? MB / 2 : 1); ++pn)
@@ -766,32 +784,42 @@ __device__ __forceinline__ void pp_load(PPPair<MB>& r, __amdgpu_buffer_rsrc_t ra
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MB, int S>
-__device__ __forceinline__ void pp_mma_stage(const PPPair<MB>& r, int ja, v16f (&acc)[MB][2]) {
+// One MFMA of the pair: B column block (op_sel OB of sb) times A row block
+// (op_sel OA of sa), FP4 x FP4 or FP4 x FP8.
+template <bool A8, int OB, int OA, class AV>
+__device__ __forceinline__ v16f pp_mfma(v4i b, AV a, v16f acc, int sb, int sa) {
+  if constexpr (A8)
+    return mfma32_fp4_fp8_sel<OB, OA>(b, a, acc, sb, sa);
+  else
+    return mfma32_fp4_sel<OB, OA>(b, a, acc, sb, sa);
+}
+
+template <int MB, int S, bool A8>
+__device__ __forceinline__ void pp_mma_stage(const PPPair<MB, A8>& r, int ja, v16f (&acc)[MB][2]) {
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     if constexpr (MB > 1) {
       const int sa = r.sa[i / 2];
       if (i & 1) {
-        acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S + 1>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
-        acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S + 1>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+        acc[i][0] = pp_mfma<A8, 2 * S, 2 * S + 1>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+        acc[i][1] = pp_mfma<A8, 2 * S + 1, 2 * S + 1>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
       } else {
-        acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
-        acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+        acc[i][0] = pp_mfma<A8, 2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+        acc[i][1] = pp_mfma<A8, 2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
       }
     } else {
       const int sa = r.sa[0] >> (8 * ja);   // byte 2s + ja moved to byte 2s
-      acc[i][0] = mfma32_fp4_sel<2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
-      acc[i][1] = mfma32_fp4_sel<2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
+      acc[i][0] = pp_mfma<A8, 2 * S, 2 * S>(r.b[2 * S], r.a[i][S], acc[i][0], r.sb, sa);
+      acc[i][1] = pp_mfma<A8, 2 * S + 1, 2 * S>(r.b[2 * S + 1], r.a[i][S], acc[i][1], r.sb, sa);
     }
   }
 }
 
 // Stage 0 then stage 1, row blocks in order: the streaming kernel's order.
-template <int MB>
-__device__ __forceinline__ void pp_mma(const PPPair<MB>& r, int ja, v16f (&acc)[MB][2]) {
-  pp_mma_stage<MB, 0>(r, ja, acc);
-  pp_mma_stage<MB, 1>(r, ja, acc);
+template <int MB, bool A8>
+__device__ __forceinline__ void pp_mma(const PPPair<MB, A8>& r, int ja, v16f (&acc)[MB][2]) {
+  pp_mma_stage<MB, 0, A8>(r, ja, acc);
+  pp_mma_stage<MB, 1, A8>(r, ja, acc);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pp_rsrc(const uint8_t* base, int64_t bytes) {
@@ -802,21 +830,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pp_rsrc(const uint8_t* base, i
 // pairs, loads for pair p + kPPDepth - 1 issued before the MFMAs of pair p.
 // The ring lives only inside one chunk, so no register crosses a loop
 // back-edge (a ring carried round a loop made the compiler copy and spill it).
-template <int MB, int CH>
+template <int MB, int CH, bool A8>
 __device__ __forceinline__ void pp_chunk(int p0, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                          __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsb, uint32_t qoff,
-                                         uint32_t soff, uint32_t panel_q, uint32_t panel_s, int ja,
+                                         uint32_t aoff, uint32_t soff, uint32_t a_panel_q, uint32_t panel_s, int ja,
                                          v16f (&acc)[MB][2]) {
-  PPPair<MB> ring[kPPDepth];
+  constexpr int D = A8 ? kPPDepth8 : kPPDepth;
+  PPPair<MB, A8> ring[D];
 #pragma unroll
-  for (int q = 0; q < kPPDepth - 1; ++q)
-    if (q < CH) pp_load<MB>(ring[q], ra, rsa, rb, rsb, qoff, soff, panel_q, panel_s, ja, p0 + q);
+  for (int q = 0; q < D - 1; ++q)
+    if (q < CH) pp_load<MB, A8>(ring[q], ra, rsa, rb, rsb, qoff, aoff, soff, a_panel_q, panel_s, ja, p0 + q);
 #pragma unroll
   for (int p = 0; p < CH; ++p) {
-    if (p + kPPDepth - 1 < CH)
-      pp_load<MB>(ring[(p + kPPDepth - 1) % kPPDepth], ra, rsa, rb, rsb, qoff, soff, panel_q, panel_s, ja,
-                  p0 + p + kPPDepth - 1);
-    pp_mma<MB>(ring[p % kPPDepth], ja, acc);
+    if (p + D - 1 < CH)
+      pp_load<MB, A8>(ring[(p + D - 1) % D], ra, rsa, rb, rsb, qoff, aoff, soff, a_panel_q, panel_s, ja,
+                      p0 + p + D - 1);
+    pp_mma<MB, A8>(ring[p % D], ja, acc);
   }
 }
 
@@ -917,7 +946,7 @@ __device__ __forceinline__ bool combine_splits(v4f (&own)[C::MB * 2], const PPSp
 // K in chunks of 8 pairs (K = 4096 is one chunk), then one of 4, then single
 // pairs; the pipeline refills at each chunk boundary.  SPLIT: the workgroup
 // covers one K range of its tile (combine_splits).
-template <int MB, bool SPLIT>
+template <int MB, bool SPLIT, bool A8 = false>
 __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int tiles_m, int tiles_n, PPSplit sk) {
   using EC = StreamCfg<MB, 2, false, true>;   // epilogue layout (reduction area and C tile)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -938,14 +967,16 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int ti
   // the A panels that exist for this tile (the last tile of a ragged m may
   // have fewer): loads past them fall outside the resource and read zeros.
   const int64_t panel_q = (int64_t)np * kPreCodeBlock, panel_s = (int64_t)np * kPreScaleBlock;
+  const int64_t a_panel_q = (int64_t)np * (A8 ? kPre8CodeBlock : kPreCodeBlock);
   const int a_panel0 = m0 / 64;
   const int a_panels = min(MB > 1 ? MB / 2 : 1, (args.m + 63) / 64 - a_panel0);
   const int ja = MB > 1 ? 0 : (tm & 1);
   const __amdgpu_buffer_rsrc_t rb = pp_rsrc(args.b_q + tn * panel_q, panel_q);
   const __amdgpu_buffer_rsrc_t rsb = pp_rsrc(args.b_s + tn * panel_s, panel_s);
-  const __amdgpu_buffer_rsrc_t ra = pp_rsrc(args.a_q + a_panel0 * panel_q, a_panels * panel_q);
+  const __amdgpu_buffer_rsrc_t ra = pp_rsrc(args.a_q + a_panel0 * a_panel_q, a_panels * a_panel_q);
   const __amdgpu_buffer_rsrc_t rsa = pp_rsrc(args.a_s + a_panel0 * panel_s, a_panels * panel_s);
   const uint32_t qoff = w * 4096 + lane * 16, soff = w * 256 + lane * 4;
+  const uint32_t aoff = A8 ? w * 8192 + lane * 16 : qoff;   // FP8 A: 8 KB per wave and pair
 
   v16f acc[MB][2];
 #pragma unroll
@@ -955,14 +986,14 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs args, int ti
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const uint32_t pq = (uint32_t)panel_q, ps = (uint32_t)panel_s;
+  const uint32_t apq = (uint32_t)a_panel_q, ps = (uint32_t)panel_s;
   int p0 = p_begin;
-  for (; p0 + 8 <= p_end; p0 += 8) pp_chunk<MB, 8>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+  for (; p0 + 8 <= p_end; p0 += 8) pp_chunk<MB, 8, A8>(p0, ra, rsa, rb, rsb, qoff, aoff, soff, apq, ps, ja, acc);
   if (p0 + 4 <= p_end) {
-    pp_chunk<MB, 4>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+    pp_chunk<MB, 4, A8>(p0, ra, rsa, rb, rsb, qoff, aoff, soff, apq, ps, ja, acc);
     p0 += 4;
   }
-  for (; p0 < p_end; ++p0) pp_chunk<MB, 1>(p0, ra, rsa, rb, rsb, qoff, soff, pq, ps, ja, acc);
+  for (; p0 < p_end; ++p0) pp_chunk<MB, 1, A8>(p0, ra, rsa, rb, rsb, qoff, aoff, soff, apq, ps, ja, acc);
 
   v4f own[MB * 2];
   reduce_units<EC>(acc, lds, w, lane, own);
@@ -977,11 +1008,11 @@ int pp_tiles(const GemmArgs& args) {
   return ((args.m + 32 * MB - 1) / (32 * MB)) * ((args.n + kBN - 1) / kBN);
 }
 
-template <int MB, bool SPLIT>
+template <int MB, bool SPLIT, bool A8 = false>
 hipError_t launch_pp_cfg(const GemmArgs& args, const PPSplit& sk, hipStream_t stream) {
   using EC = StreamCfg<MB, 2, false, true>;
   constexpr int lds_bytes = EC::XCH + EC::C_TILE;
-  const auto kernel = gemm_pp_kernel<MB, SPLIT>;
+  const auto kernel = gemm_pp_kernel<MB, SPLIT, A8>;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   const int tiles_n = (args.n + kBN - 1) / kBN;
@@ -1106,6 +1137,15 @@ hipError_t launch_gemm_w4a8_stream_prepacked(const GemmArgs& args, hipStream_t s
   if (args.m <= 32) return launch_pre_cfg<Pre1>(args, stream);
   if (args.m <= 64) return launch_pre_cfg<Pre2>(args, stream);
   return launch_pre_cfg<Pre4>(args, stream);
+}
+
+hipError_t launch_gemm_w4a8_both_prepacked(const GemmArgs& args, hipStream_t stream) {
+  if (args.m <= 0 || args.n <= 0) return hipSuccess;
+  if (args.k <= 0 || args.k % 512) return hipErrorInvalidValue;
+  const PPSplit sk{1, args.k / 512, nullptr, nullptr};
+  if (args.m <= 32) return launch_pp_cfg<1, false, true>(args, sk, stream);
+  if (args.m <= 64) return launch_pp_cfg<2, false, true>(args, sk, stream);
+  return launch_pp_cfg<4, false, true>(args, sk, stream);
 }
 
 hipError_t launch_gemm_both_prepacked(const GemmArgs& args, int splits, void* workspace, hipStream_t stream) {

@@ -42,6 +42,10 @@ hipError_t launch_quantize_prepacked(const void* x, int64_t rows, int64_t k, voi
                                      hipStream_t stream, int num_cus);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                                  hipStream_t stream, int num_cus);
+// MXFP8 codes and scales stored in the FP8 prepacked operand layout (k % 512 == 0;
+// rows up to the next multiple of 64 written as zero blocks).
+hipError_t launch_quantize_mxfp8_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                           hipStream_t stream, int num_cus);
 
 hipError_t launch_gemm_tile(const GemmArgs& args, TileKind kind, hipStream_t stream);
 
@@ -105,6 +109,9 @@ hipError_t launch_gemm_w4a8_stream_prepacked(const GemmArgs& args, hipStream_t s
 // zero-filled); hipErrorInvalidValue when the shape has more output tiles
 // than the workspace's counter region holds.
 hipError_t launch_gemm_both_prepacked(const GemmArgs& args, int splits, void* workspace, hipStream_t stream);
+// W4A8 on both operands prepacked: A in the FP8 prepacked layout, B in the MXFP4
+// prepacked layout (k % 512 == 0; bit-identical to launch_gemm_w4a8_stream_prepacked).
+hipError_t launch_gemm_w4a8_both_prepacked(const GemmArgs& args, hipStream_t stream);
 // The K ranges a request for `splits` gives: ranges of ceil(pairs / splits)
 // 512-K pairs, rounded up to a multiple of 4 above 4 (at most `splits`, none
 // empty).

@@ -240,6 +240,58 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The MXFP8 quantization written straight into the FP8 prepacked operand
+// layout of the W4A8 GEMM on both operands prepacked (include/mxfp8.h).  The
+// FP8 operand of the scaled MFMA takes, in lane half h of a 64-K step, the
+// 16 codes at K [16h, 16h + 16) in its first four registers and those at
+// [32 + 16h, 48 + 16h) in its last four, with the scale byte of the step's
+// 32-block h.  Per 64-row panel P and 512-K pair t the layout therefore holds,
+// for wave w (the 64-K step w of each 256-K stage s), u = 2s + j (row block j
+// of the panel) and register half e, one 1 KB piece of the 64 lanes' 16-byte
+// halves:
+//   codes (P * pairs + t) * 32768 + w * 8192 + u * 2048 + e * 1024 + l * 16,
+// and the scale bytes exactly where the MXFP4 prepacked layout keeps them.
+// A lane quad of this kernel quantizes 32-block kb of row r (the step's block
+// e = kb % 2); quad lane q holds its K [8q, 8q + 8), which is lane
+// l = r % 32 + 32 (q / 2), register half e, bytes [8 (q % 2), 8 (q % 2) + 8).
+// Rows from `rows` up to the panel boundary are written as zero blocks.  Codes
+// and scale bytes are those of quantize_mxfp8_kernel, bit for bit.
+__global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_prepacked_kernel(
+    const uint4* __restrict__ x, uint8_t* __restrict__ q, uint8_t* __restrict__ scales, int64_t rows,
+    int kblocks, int64_t nblocks) {
+  const int lane4 = threadIdx.x & 3;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
+  const int pairs = kblocks / 16;
+  for (int64_t b = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2); b < nblocks;
+       b += groups_per_grid) {
+    const int64_t r = b / kblocks;
+    const int kb = (int)(b - r * kblocks);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < rows) v = x[b * 4 + lane4];   // padded rows past `rows` encode a zero block
+    const uint32_t m01 = umax16x2(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu);
+    const uint32_t m23 = umax16x2(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu);
+    const uint32_t m = umax16x2(m01, m23);
+    uint32_t amax_bits = max(m & 0xFFFFu, m >> 16);
+    amax_bits = quad_max(amax_bits);
+    const uint32_t sbyte = (uint32_t)max((int)(amax_bits >> 7) - 8, 0);
+    const float scale = __uint_as_float(sbyte << 23);
+    const uint32_t bound = ((8u + sbyte) << 7) | 0x60u;      // 448 * 2^e as BF16 magnitude bits
+    const uint32_t lo = cvt_fp8x4(clamp_mag16x2(v.x, bound), clamp_mag16x2(v.y, bound), scale);
+    const uint32_t hi = cvt_fp8x4(clamp_mag16x2(v.z, bound), clamp_mag16x2(v.w, bound), scale);
+    int64_t word, sidx;
+    prepacked_index(r, kb, pairs, word, sidx);   // the scale byte's place (the code word's is FP4's)
+    const int64_t panel = r / 64;
+    const int rr = (int)(r - panel * 64);
+    const int j = rr >> 5, t = kb >> 4, s = (kb >> 3) & 1, w = (kb >> 1) & 3, e = kb & 1;
+    const int l = (rr & 31) + 32 * (lane4 >> 1);
+    const int64_t off = (panel * pairs + t) * 32768 + w * 8192 + (2 * s + j) * 2048 + e * 1024 + l * 16 +
+                        8 * (lane4 & 1);
+    *(uint2*)(q + off) = make_uint2(lo, hi);
+    if (lane4 == 0) scales[sidx] = (uint8_t)sbyte;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
@@ -282,6 +334,19 @@ hipError_t launch_scales_interleave(const void* scales, int64_t groups, int64_t 
   if (grid > max_grid) grid = max_grid;
   hipLaunchKernelGGL(scales_interleave_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)scales,
                      (uint4*)out, pieces, rows, gpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
+                                           hipStream_t stream, int num_cus) {
+  const int64_t padded = (rows + 63) / 64 * 64;
+  const int64_t nblocks = padded * (k / 32);
+  int64_t grid = (nblocks + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
+  const int64_t max_grid = (int64_t)num_cus * 8;
+  if (grid > max_grid) grid = max_grid;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quantize_mxfp8_prepacked_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
+                     (const uint4*)x, (uint8_t*)q, (uint8_t*)scales, rows, (int)(k / 32), nblocks);
   return hipGetLastError();
 }
 

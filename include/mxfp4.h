@@ -174,9 +174,10 @@ mxfp4_status_t mxfp4_grouped_gemm_nt(const void* a_q, const void* a_s,
 /*
  * Interleaved scale layout for the tile GEMMs (the counterpart on this
  * machine of the "fp4_quantization" page's block_scales_interleave /
- * block_scales_interleave_fp4: rank-2 scale factors rearranged into the
- * layout the matrix path reads, and of grouped_quantize_dynamic_scaled_fp4_async,
- * which stores scale factors in that layout as it quantizes).
+ * block_scales_interleave_fp4, which reorder a two-dimensional scale array
+ * into the order another GPU's tensor cores consume, and of
+ * grouped_quantize_dynamic_scaled_fp4_async, which writes its scales in that
+ * order while it quantizes).
  *
  * For an operand of `rows` rows and k % 512 == 0, the scale bytes of the
  * row-major array scales[rows][k/32] are stored as scales_il[k/512][rows][16]:

@@ -100,6 +100,44 @@ mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked(const void* a_q8, const void* a_s, c
                                             void* stream);
 
 /*
+ * Both W4A8 operands prepacked: the decode GEMM with the activation also in a
+ * prepacked layout, so every wave loads A straight into registers as well and
+ * the main loop touches no LDS (the FP8 counterpart of
+ * mxfp4_gemm_nt_prepacked_ab; the quadbit README's "The stack": the
+ * activation quantized straight into the layout the GEMM reads).
+ *
+ * FP8 prepacked layout of an MXFP8 operand [rows, k] (k % 512 == 0), per
+ * 64-row panel P and 512-K pair t (rows padded to a multiple of 64 with zero
+ * blocks): the scaled MFMA's FP8 operand takes, in lane half h of a 64-K step,
+ * the codes at K [16h, 16h + 16) in its first four registers and at
+ * [32 + 16h, 48 + 16h) in its last four.  For wave w (64-K step w of each
+ * 256-K stage s), u = 2s + j (32-row block j of the panel), register half e
+ * and lane l = r % 32 + 32h, the 16 codes sit at byte
+ *   (P * pairs + t) * 32768 + w * 8192 + u * 2048 + e * 1024 + l * 16
+ * of ap_q8: codes of row 64P + 32j + l % 32 at K 512t + 256s + 64w + 32e +
+ * 16h + [0, 16).  The scale bytes sit exactly where mxfp4_prepack_weight's
+ * layout keeps an MXFP4 operand's (include/mxfp4.h).  Sizes: ap_q8 twice the
+ * code bytes mxfp4_prepacked_weight_size(rows, k) gives, ap_s the same scale
+ * bytes.
+ *
+ * mxfp8_quantize_prepacked: mxfp8_quantize with the codes and scale bytes
+ *   stored in that layout, bit for bit the same bytes (padding rows zero);
+ *   ap_q8 16-byte aligned; k a positive multiple of 512, at most 2^24.
+ * mxfp8_gemm_w4a8_nt_prepacked_ab: C[m, n] = A . B^T with A in the FP8
+ *   prepacked layout (m rows) and B prepacked by mxfp4_prepack_weight (n rows);
+ *   the same result, bit for bit, as mxfp8_gemm_w4a8_nt_prepacked on the
+ *   row-major A (same per-wave K split, MFMA order and reduction).  c: [m, n]
+ *   of type c_type, 16-byte aligned; k as above.  No workspace; one launch.
+ * Violations return MXFP4_ERR_INVALID_ARG.
+ */
+mxfp4_status_t mxfp8_quantize_prepacked(const void* x_bf16, int64_t rows, int64_t k, void* ap_q8, void* ap_s,
+                                        void* stream);
+
+mxfp4_status_t mxfp8_gemm_w4a8_nt_prepacked_ab(const void* ap_q8, const void* ap_s, const void* bp_q,
+                                               const void* bp_s, void* c, mxfp4_out_t c_type, int64_t m, int64_t n,
+                                               int64_t k, void* stream);
+
+/*
  * MXFP8 x MXFP8 NT GEMM: C[m][n] = sum_k A[m][k] * B[n][k] with both operands
  * in MXFP8 ("fp4_quantization" page, Functions: block_scaled_matmul, the
  * block-scaled matmul over MXFP4 / MXFP8 operands; its quantizer

@@ -27,3 +27,25 @@ def prepack_numpy(bq, bs):
                         codes[:, t, w, 2 * s + j, l, :] = qpad[rows, off:off + 16]
                         scales[:, t, w, l, 2 * s + j] = spad[rows, 16 * t + 8 * s + 2 * w + l // 32]
     return codes.reshape(-1), scales.reshape(-1)
+
+
+def prepack_fp8_numpy(q8, s):
+    """The FP8 prepacked layout of include/mxfp8.h from its definition: per 64-row panel P and 512-K
+    pair t, codes[w, u=2s+j, e, l, c] = FP8 code of row 64P + 32j + l%32 at K 512t + 256s + 64w + 32e +
+    16(l//32) + c; the scale bytes as in the MXFP4 prepacked layout."""
+    n, k = q8.shape
+    panels, pairs = -(-n // 64), k // 512
+    qpad = np.zeros((panels * 64, k), np.uint8)
+    qpad[:n] = q8
+    codes = np.zeros((panels, pairs, 4, 4, 2, 64, 16), np.uint8)
+    for w in range(4):
+        for st in range(2):
+            for j in range(2):
+                for e in range(2):
+                    for l in range(64):
+                        rows = np.arange(panels) * 64 + 32 * j + l % 32
+                        for t in range(pairs):
+                            off = 512 * t + 256 * st + 64 * w + 32 * e + 16 * (l // 32)
+                            codes[:, t, w, 2 * st + j, e, l, :] = qpad[rows, off:off + 16]
+    _, scales = prepack_numpy(np.zeros((n, k // 2), np.uint8), s)
+    return codes.reshape(-1), scales

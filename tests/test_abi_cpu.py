@@ -346,6 +346,22 @@ def test_w4a8_prepacked_rejects_bad_arguments_on_host(lib):
     assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0        # empty: no-op
 
 
+def test_w4a8_both_prepacked_rejects_bad_arguments_on_host(lib):
+    f = _fake
+    q = lib.mxfp8_quantize_prepacked
+    assert q(f(), 4, 992, f(), f(), None) == 1                           # k % 512
+    assert q(f(), -1, 512, f(), f(), None) == 1
+    assert q(f(0x1004), 4, 512, f(), f(), None) == 1                     # x alignment
+    assert q(None, 0, 512, None, None, None) == 0                        # no rows: no-op
+    g = lib.mxfp8_gemm_w4a8_nt_prepacked_ab
+    assert g(f(), f(), f(), f(), f(), 0, 4, 64, 992, None) == 1          # k % 512
+    assert b"multiple of 512" in lib.mxfp4_last_error()
+    assert g(f(), f(), f(), f(), f(), 3, 4, 64, 512, None) == 1          # output type
+    assert g(None, f(), f(), f(), f(), 0, 4, 64, 512, None) == 1         # null ap_q8
+    assert g(f(), f(), f(), f(), f(), 0, -1, 64, 512, None) == 1
+    assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0       # empty: no-op
+
+
 def test_prepacked_entry_points_reject_bad_arguments_on_host(lib):
     f = _fake
     cb, sb = ctypes.c_int64(), ctypes.c_int64()
