@@ -36,7 +36,8 @@ EXPORTED = (
     "mxfp4_rmsnorm_quantize_prepacked", "mxfp4_swiglu_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked",
     "mxfp4_scales_interleave", "mxfp4_quantize_interleaved", "mxfp4_gemm_nt_interleaved",
     "mxfp4_grouped_gemm_nt_interleaved", "mxfp4_moe_quantize_scatter_interleaved",
-    "mxfp8_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked_ab",
+    "mxfp8_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked_ab", "mxfp4_rmsnorm_quantize_interleaved",
+    "mxfp4_swiglu_quantize_interleaved",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -151,6 +152,10 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_rmsnorm_quantize_prepacked.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
         lib.mxfp4_swiglu_quantize_prepacked.restype = ctypes.c_int
         lib.mxfp4_swiglu_quantize_prepacked.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
+        lib.mxfp4_rmsnorm_quantize_interleaved.restype = ctypes.c_int
+        lib.mxfp4_rmsnorm_quantize_interleaved.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp]
+        lib.mxfp4_swiglu_quantize_interleaved.restype = ctypes.c_int
+        lib.mxfp4_swiglu_quantize_interleaved.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.nvfp4_quantize.restype = ctypes.c_int
         lib.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         lib.nvfp4_gemm_nt.restype = ctypes.c_int
@@ -678,11 +683,16 @@ def mxfp4_moe_combine(y, token_rows, weights, out=None, out_dtype=torch.bfloat16
 # Fused producers (include/mxfp4_producers.h)
 # ---------------------------------------------------------------------------
 
-def _mxfp4_out(q, scales, rows, k, device, prepacked):
-    """Codes and scales of a [rows, k] MXFP4 output: row-major, or the prepacked layout's flat buffers."""
+def _mxfp4_out(q, scales, rows, k, device, prepacked, interleaved=False):
+    """Codes and scales of a [rows, k] MXFP4 output: row-major, the prepacked layout's flat buffers, or
+    row-major codes with interleaved scales [k/512, rows, 16]."""
+    if prepacked and interleaved:
+        raise ValueError("prepacked and interleaved are different layouts: choose one")
     if prepacked:
         cb, sb = mxfp4_prepacked_weight_size(rows, k)
         qs, ss = (cb,), (sb,)
+    elif interleaved:
+        qs, ss = (rows, k // 2), (k // 512, rows, 16)
     else:
         qs, ss = (rows, k // 2), (rows, k // 32)
     if q is None:
@@ -695,26 +705,30 @@ def _mxfp4_out(q, scales, rows, k, device, prepacked):
 
 
 def mxfp4_rmsnorm_quantize(x, gamma, eps: float, residual=None, residual_out=None, y=None, q=None, scales=None,
-                           stream=None, prepacked: bool = False):
-    """(x [+ residual]) -> RMSNorm(., gamma, eps) -> MXFP4 (q [rows, k/2], scales [rows, k/32], or with
-    prepacked=True the prepacked operand layout of the decode GEMM).
+                           stream=None, prepacked: bool = False, interleaved: bool = False):
+    """(x [+ residual]) -> RMSNorm(., gamma, eps) -> MXFP4 (q [rows, k/2], scales [rows, k/32]; with
+    prepacked=True the prepacked operand layout of the decode GEMM; with interleaved=True the scales as
+    [k/512, rows, 16] for mxfp4_gemm_nt_interleaved).
     residual_out (optional) receives x + residual; y (optional) the BF16 RMSNorm output."""
     lib = load_library()
     rows, k = x.shape
-    q, scales = _mxfp4_out(q, scales, rows, k, x.device, prepacked)
+    q, scales = _mxfp4_out(q, scales, rows, k, x.device, prepacked, interleaved)
     _require(x, "x", torch.bfloat16, (rows, k))
     _require(gamma, "gamma", torch.bfloat16, (k,))
     for t, name in ((residual, "residual"), (residual_out, "residual_out"), (y, "y")):
         if t is not None:
             _require(t, name, torch.bfloat16, (rows, k))
-    fn = lib.mxfp4_rmsnorm_quantize_prepacked if prepacked else lib.mxfp4_rmsnorm_quantize
+    fn = (lib.mxfp4_rmsnorm_quantize_prepacked if prepacked else
+          lib.mxfp4_rmsnorm_quantize_interleaved if interleaved else lib.mxfp4_rmsnorm_quantize)
     _check(fn(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), rows, k, _ptr(residual_out), _ptr(y), _ptr(q),
               _ptr(scales), _stream(stream)))
     return q, scales
 
 
-def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None, prepacked: bool = False):
-    """silu(gate) * up -> MXFP4 (row-major, or with prepacked=True the prepacked operand layout).  gate and up
+def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None, prepacked: bool = False,
+                          interleaved: bool = False):
+    """silu(gate) * up -> MXFP4 (row-major; with prepacked=True the prepacked operand layout; with
+    interleaved=True row-major codes and scales [k/512, rows, 16]).  gate and up
     are [rows, k] views sharing one row stride (for example the two halves of a [rows, 2k] projection output);
     y (optional) receives the BF16 activation."""
     lib = load_library()
@@ -724,10 +738,11 @@ def mxfp4_swiglu_quantize(gate, up, y=None, q=None, scales=None, stream=None, pr
     if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16 or not gate.is_cuda or not up.is_cuda:
         raise TypeError("gate and up must be bfloat16 device tensors")
     ld = gate.stride(0) if rows > 1 else k
-    q, scales = _mxfp4_out(q, scales, rows, k, gate.device, prepacked)
+    q, scales = _mxfp4_out(q, scales, rows, k, gate.device, prepacked, interleaved)
     if y is not None:
         _require(y, "y", torch.bfloat16, (rows, k))
-    fn = lib.mxfp4_swiglu_quantize_prepacked if prepacked else lib.mxfp4_swiglu_quantize
+    fn = (lib.mxfp4_swiglu_quantize_prepacked if prepacked else
+          lib.mxfp4_swiglu_quantize_interleaved if interleaved else lib.mxfp4_swiglu_quantize)
     _check(fn(_ptr(gate), _ptr(up), ld, rows, k, _ptr(y), _ptr(q), _ptr(scales), _stream(stream)))
     return q, scales
 

@@ -942,14 +942,18 @@ mxfp4_status_t mxfp4_moe_combine(const void* y_bf16, int64_t total_rows, int64_t
 namespace {
 mxfp4_status_t rmsnorm_quantize(const void* x_bf16, const void* residual_bf16, const void* gamma_bf16, float eps,
                                 int64_t rows, int64_t k, void* residual_out_bf16, void* y_bf16, void* q, void* scales,
-                                bool prepacked, void* stream) {
+                                int layout, void* stream) {
+  const bool prepacked = layout == mxfp4::kLayoutPrepacked;
   // one 256-thread workgroup per row (prepacked: per row of whole 64-row panels)
   if (rows < 0 || rows > ((int64_t)1 << 24)) return fail(MXFP4_ERR_INVALID_ARG, "rows must be 0..2^24 (got %lld)", (long long)rows);
   MXFP4_TRY(check_k(k));
   if (k > 256 * 8 * mxfp4::kNormMaxSlots)
     return fail(MXFP4_ERR_INVALID_ARG, "k must be at most %d for the RMSNorm producer (got %lld)",
                 256 * 8 * mxfp4::kNormMaxSlots, (long long)k);
-  if (prepacked && k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (layout != mxfp4::kLayoutRowMajor && k % 512)
+    return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (layout == mxfp4::kLayoutInterleaved && rows * (k / 32) >= ((int64_t)1 << 31))
+    return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need rows * k / 32 < 2^31");
   if (!(eps >= 0.0f) || eps == __builtin_huge_valf()) return fail(MXFP4_ERR_INVALID_ARG, "eps must be finite and non-negative");
   if (rows == 0) return MXFP4_OK;
   MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
@@ -965,16 +969,18 @@ mxfp4_status_t rmsnorm_quantize(const void* x_bf16, const void* residual_bf16, c
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_rmsnorm_quantize(x_bf16, residual_bf16, gamma_bf16, eps, (int)rows, (int)k,
-                                                   residual_out_bf16, y_bf16, q, scales, prepacked,
+                                                   residual_out_bf16, y_bf16, q, scales, layout,
                                                    (hipStream_t)stream),
                     "rmsnorm quantize launch");
 }
 
 mxfp4_status_t swiglu_quantize(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows, int64_t k,
-                               void* y_bf16, void* q, void* scales, bool prepacked, void* stream) {
+                               void* y_bf16, void* q, void* scales, int layout, void* stream) {
+  const bool prepacked = layout == mxfp4::kLayoutPrepacked;
   if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
   MXFP4_TRY(check_k(k));
-  if (prepacked && k % 512) return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
+  if (layout != mxfp4::kLayoutRowMajor && k % 512)
+    return fail(MXFP4_ERR_INVALID_ARG, "k must be a multiple of 512 (got %lld)", (long long)k);
   if (ld < k || ld % 8 != 0) return fail(MXFP4_ERR_INVALID_ARG, "ld must be a multiple of 8 and at least k (got %lld)", (long long)ld);
   if ((rows + 63) / 64 * 64 > ((int64_t)1 << 30) / (k / 32)) return fail(MXFP4_ERR_INVALID_ARG, "rows * k / 32 too large");
   if (rows == 0) return MXFP4_OK;
@@ -986,7 +992,7 @@ mxfp4_status_t swiglu_quantize(const void* gate_bf16, const void* up_bf16, int64
   DeviceInfo dev;
   MXFP4_TRY(current_device(dev));
   return hip_status(mxfp4::launch_swiglu_quantize(gate_bf16, up_bf16, ld, (int)rows, (int)k, y_bf16, q, scales,
-                                                  prepacked, (hipStream_t)stream, dev.num_cus),
+                                                  layout, (hipStream_t)stream, dev.num_cus),
                     "swiglu quantize launch");
 }
 }  // namespace
@@ -995,7 +1001,15 @@ mxfp4_status_t mxfp4_rmsnorm_quantize(const void* x_bf16, const void* residual_b
                                       float eps, int64_t rows, int64_t k, void* residual_out_bf16, void* y_bf16,
                                       void* q, void* scales, void* stream) {
   return rmsnorm_quantize(x_bf16, residual_bf16, gamma_bf16, eps, rows, k, residual_out_bf16, y_bf16, q, scales,
-                          false, stream);
+                          mxfp4::kLayoutRowMajor, stream);
+}
+
+mxfp4_status_t mxfp4_rmsnorm_quantize_interleaved(const void* x_bf16, const void* residual_bf16,
+                                                  const void* gamma_bf16, float eps, int64_t rows, int64_t k,
+                                                  void* residual_out_bf16, void* y_bf16, void* q, void* scales_il,
+                                                  void* stream) {
+  return rmsnorm_quantize(x_bf16, residual_bf16, gamma_bf16, eps, rows, k, residual_out_bf16, y_bf16, q, scales_il,
+                          mxfp4::kLayoutInterleaved, stream);
 }
 
 mxfp4_status_t mxfp4_rmsnorm_quantize_prepacked(const void* x_bf16, const void* residual_bf16,
@@ -1003,17 +1017,23 @@ mxfp4_status_t mxfp4_rmsnorm_quantize_prepacked(const void* x_bf16, const void* 
                                                 void* residual_out_bf16, void* y_bf16, void* ap_q, void* ap_s,
                                                 void* stream) {
   return rmsnorm_quantize(x_bf16, residual_bf16, gamma_bf16, eps, rows, k, residual_out_bf16, y_bf16, ap_q, ap_s,
-                          true, stream);
+                          mxfp4::kLayoutPrepacked, stream);
 }
 
 mxfp4_status_t mxfp4_swiglu_quantize(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
                                      int64_t k, void* y_bf16, void* q, void* scales, void* stream) {
-  return swiglu_quantize(gate_bf16, up_bf16, ld, rows, k, y_bf16, q, scales, false, stream);
+  return swiglu_quantize(gate_bf16, up_bf16, ld, rows, k, y_bf16, q, scales, mxfp4::kLayoutRowMajor, stream);
+}
+
+mxfp4_status_t mxfp4_swiglu_quantize_interleaved(const void* gate_bf16, const void* up_bf16, int64_t ld,
+                                                 int64_t rows, int64_t k, void* y_bf16, void* q, void* scales_il,
+                                                 void* stream) {
+  return swiglu_quantize(gate_bf16, up_bf16, ld, rows, k, y_bf16, q, scales_il, mxfp4::kLayoutInterleaved, stream);
 }
 
 mxfp4_status_t mxfp4_swiglu_quantize_prepacked(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
                                                int64_t k, void* y_bf16, void* ap_q, void* ap_s, void* stream) {
-  return swiglu_quantize(gate_bf16, up_bf16, ld, rows, k, y_bf16, ap_q, ap_s, true, stream);
+  return swiglu_quantize(gate_bf16, up_bf16, ld, rows, k, y_bf16, ap_q, ap_s, mxfp4::kLayoutPrepacked, stream);
 }
 
 // ---------------------------------------------------------------------------

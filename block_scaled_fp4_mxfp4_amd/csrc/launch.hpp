@@ -139,12 +139,16 @@ hipError_t launch_moe_combine(const void* y, int total_rows, int n, const int32_
 
 // Fused producers emitting MXFP4 activations (include/mxfp4_producers.h).
 constexpr int kNormMaxSlots = 16;   // RMSNorm rows: k <= 256 threads * 8 elements * 16 = 32768
-// prepacked: codes and scales in the prepacked operand layout (k % 512 == 0)
+// Where a producer writes its MXFP4 bytes: row-major codes and scales; codes and
+// scales in the prepacked operand layout; or row-major codes with interleaved
+// scales [k/512, rows, 16] (the last two need k % 512 == 0, interleaved also
+// rows * k/32 < 2^31).
+enum ProducerLayout { kLayoutRowMajor = 0, kLayoutPrepacked = 1, kLayoutInterleaved = 2 };
 hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
-                                   void* h_out, void* y_out, void* q, void* scales, bool prepacked,
+                                   void* h_out, void* y_out, void* q, void* scales, int layout,
                                    hipStream_t stream);
 hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
-                                  void* scales, bool prepacked, hipStream_t stream, int num_cus);
+                                  void* scales, int layout, hipStream_t stream, int num_cus);
 
 // NVFP4 (include/nvfp4.h): quantization (k <= 32768, one workgroup per row) and
 // the dequantizing NT GEMM on the BF16 MFMA (k % 64 == 0).

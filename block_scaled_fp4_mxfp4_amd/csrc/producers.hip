@@ -116,12 +116,16 @@ __device__ __forceinline__ double sumsq_bf16x2(uint32_t w, double acc) {
   return fma(hi, hi, fma(lo, lo, acc));
 }
 
-template <bool HAS_RES, int SLOTS, bool PREPACKED>
+// LAYOUT: where the MXFP4 bytes go (ProducerLayout in launch.hpp): row-major,
+// the prepacked operand layout, or row-major codes with interleaved scales
+// ([k/512, rows, 16], the tile GEMMs' copy layout; rows * k/32 < 2^31).
+template <bool HAS_RES, int SLOTS, int LAYOUT>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
     // x, res, h_out and y_out may share memory (in-place residual and output): no __restrict__ on them
     const uint4* x, const uint4* res, const uint4* __restrict__ gamma, float eps, int rows, int k,
     uint4* h_out, uint4* y_out, uint32_t* __restrict__ q, uint8_t* __restrict__ scales) {
   __shared__ double red[kNormThreads / 64];
+  constexpr bool PREPACKED = LAYOUT == kLayoutPrepacked;
   const int chunks = k >> 3;                         // 8 elements (one uint4) per chunk
   const int64_t rbase = (int64_t)blockIdx.x * chunks;
   if (PREPACKED && (int)blockIdx.x >= rows) {
@@ -193,7 +197,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quantize_kernel(
       if ((threadIdx.x & 3) == 0) scales[sidx] = (uint8_t)sbyte;
     } else {
       q[rbase + c] = codes;
-      if ((threadIdx.x & 3) == 0) scales[(rbase + c) >> 2] = (uint8_t)sbyte;
+      if ((threadIdx.x & 3) == 0) {
+        if (LAYOUT == kLayoutInterleaved) {   // piece kb / 16 of this row in slab-major order
+          const uint32_t kb = (uint32_t)c >> 2;
+          scales[(kb >> 4) * (uint32_t)rows * 16 + blockIdx.x * 16 + (kb & 15)] = (uint8_t)sbyte;
+        } else {
+          scales[(rbase + c) >> 2] = (uint8_t)sbyte;
+        }
+      }
     }
   }
 }
@@ -213,12 +224,20 @@ __device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t g, uint32_t u) {
   return pack_bf16x2(silu_mul(bf16_lo(g), bf16_lo(u)), silu_mul(bf16_hi(g), bf16_hi(u)));
 }
 
-// nblocks counts the 32-blocks of `rows` rows, or with PREPACKED of the rows
-// rounded up to 64 (blocks of padding rows are written as zero blocks).
-template <bool PREPACKED>
+// nblocks counts the 32-blocks of `rows` rows, or with the prepacked layout of
+// the rows rounded up to 64 (blocks of padding rows are written as zero
+// blocks).  With interleaved scales the walk stays row-major (the reads of
+// gate and up run along the rows) and each scale byte goes to its place in
+// the interleaved layout.  Walks in the layout's order, which let neighbouring
+// waves fill whole lines of scales as in the interleaved quantizer, made
+// neighbouring waves read different rows a whole row stride apart: 53.0 us
+// (slab-major over all rows) and 55.7 us (slab-major inside groups of 8 rows)
+// against 48.7 us row-major for 4096 x 14336 on one box.
+template <int LAYOUT>
 __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
     const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int64_t ld, int rows, int kblocks,
     int nblocks, uint4* __restrict__ y_out, uint32_t* __restrict__ q, uint8_t* __restrict__ scales) {
+  constexpr bool PREPACKED = LAYOUT == kLayoutPrepacked;
   const int lane4 = threadIdx.x & 3;
   const int groups_per_grid = gridDim.x * (kProdThreads / 4);
   for (int blk = blockIdx.x * (kProdThreads / 4) + (threadIdx.x >> 2); blk < nblocks;
@@ -261,7 +280,14 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
         } else {
           if (y_out) y_out[(int64_t)b * 4 + lane4] = y;
           q[(int64_t)b * 4 + lane4] = codes;
-          if (lane4 == 0) scales[b] = (uint8_t)sbyte;
+          if (lane4 == 0) {
+            if (LAYOUT == kLayoutInterleaved) {   // rows * kblocks < 2^31
+              const uint32_t row = (uint32_t)b / (uint32_t)kblocks, kb = (uint32_t)b - row * (uint32_t)kblocks;
+              scales[(kb >> 4) * (uint32_t)rows * 16 + row * 16 + (kb & 15)] = (uint8_t)sbyte;
+            } else {
+              scales[b] = (uint8_t)sbyte;
+            }
+          }
         }
       }
     }
@@ -270,52 +296,55 @@ __global__ __launch_bounds__(kProdThreads) void swiglu_quantize_kernel(
 
 }  // namespace
 
-template <int SLOTS, bool PREPACKED>
+template <int SLOTS, int LAYOUT>
 void launch_rmsnorm_slots(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
                           void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
+  constexpr bool PREPACKED = LAYOUT == kLayoutPrepacked;
   // prepacked: one more workgroup per padding row of the last 64-row panel
   const unsigned grid = PREPACKED ? (unsigned)((rows + 63) / 64 * 64) : (unsigned)rows;
   if (residual)
-    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, SLOTS, PREPACKED>), dim3(grid), dim3(kNormThreads), 0, stream,
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true, SLOTS, LAYOUT>), dim3(grid), dim3(kNormThreads), 0, stream,
                        (const uint4*)x, (const uint4*)residual, (const uint4*)gamma, eps, rows, k, (uint4*)h_out,
                        (uint4*)y_out, (uint32_t*)q, (uint8_t*)scales);
   else
-    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, SLOTS, PREPACKED>), dim3(grid), dim3(kNormThreads), 0, stream,
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false, SLOTS, LAYOUT>), dim3(grid), dim3(kNormThreads), 0, stream,
                        (const uint4*)x, (const uint4*)nullptr, (const uint4*)gamma, eps, rows, k, (uint4*)nullptr,
                        (uint4*)y_out, (uint32_t*)q, (uint8_t*)scales);
 }
 
-template <bool PREPACKED>
+template <int LAYOUT>
 void launch_rmsnorm(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
                     void* h_out, void* y_out, void* q, void* scales, hipStream_t stream) {
   if (k <= 2 * 8 * kNormThreads)
-    launch_rmsnorm_slots<2, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+    launch_rmsnorm_slots<2, LAYOUT>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
   else if (k <= 4 * 8 * kNormThreads)
-    launch_rmsnorm_slots<4, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+    launch_rmsnorm_slots<4, LAYOUT>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
   else
-    launch_rmsnorm_slots<kNormMaxSlots, PREPACKED>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales,
-                                                   stream);
+    launch_rmsnorm_slots<kNormMaxSlots, LAYOUT>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
 }
 
 // Rows stay in registers: 2, 4 or 16 chunks of 8 elements per thread (k up
 // to 4096, 8192 or 32768), so the common widths keep the register count, and
 // with it the rows in flight per CU, low.
 hipError_t launch_rmsnorm_quantize(const void* x, const void* residual, const void* gamma, float eps, int rows, int k,
-                                   void* h_out, void* y_out, void* q, void* scales, bool prepacked,
+                                   void* h_out, void* y_out, void* q, void* scales, int layout,
                                    hipStream_t stream) {
   if (!grid_fits((int64_t)(rows + 63) / 64 * 64, kNormThreads)) return hipErrorInvalidConfiguration;
-  if (prepacked) {
-    if (k % 512) return hipErrorInvalidValue;
-    launch_rmsnorm<true>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
-  } else {
-    launch_rmsnorm<false>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
-  }
+  if (layout != kLayoutRowMajor && k % 512) return hipErrorInvalidValue;
+  if (layout == kLayoutInterleaved && (int64_t)rows * (k / 32) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (layout == kLayoutPrepacked)
+    launch_rmsnorm<kLayoutPrepacked>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  else if (layout == kLayoutInterleaved)
+    launch_rmsnorm<kLayoutInterleaved>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
+  else
+    launch_rmsnorm<kLayoutRowMajor>(x, residual, gamma, eps, rows, k, h_out, y_out, q, scales, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, int rows, int k, void* y_out, void* q,
-                                  void* scales, bool prepacked, hipStream_t stream, int num_cus) {
-  if (prepacked && k % 512) return hipErrorInvalidValue;
+                                  void* scales, int layout, hipStream_t stream, int num_cus) {
+  const bool prepacked = layout == kLayoutPrepacked;
+  if (layout != kLayoutRowMajor && k % 512) return hipErrorInvalidValue;
   const int kblocks = k / 32;
   // the host keeps this at most 2^30 (prepacked: rows rounded up to 64)
   const int nblocks = (prepacked ? (rows + 63) / 64 * 64 : rows) * kblocks;
@@ -324,14 +353,11 @@ hipError_t launch_swiglu_quantize(const void* gate, const void* up, int64_t ld, 
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  if (prepacked)
-    hipLaunchKernelGGL(swiglu_quantize_kernel<true>, dim3((unsigned)grid), dim3(kProdThreads), 0, stream,
-                       (const uint16_t*)gate, (const uint16_t*)up, ld, rows, kblocks, nblocks, (uint4*)y_out,
-                       (uint32_t*)q, (uint8_t*)scales);
-  else
-    hipLaunchKernelGGL(swiglu_quantize_kernel<false>, dim3((unsigned)grid), dim3(kProdThreads), 0, stream,
-                       (const uint16_t*)gate, (const uint16_t*)up, ld, rows, kblocks, nblocks, (uint4*)y_out,
-                       (uint32_t*)q, (uint8_t*)scales);
+  const auto kernel = prepacked ? swiglu_quantize_kernel<kLayoutPrepacked>
+                                 : (layout == kLayoutInterleaved ? swiglu_quantize_kernel<kLayoutInterleaved>
+                                                                 : swiglu_quantize_kernel<kLayoutRowMajor>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kProdThreads), 0, stream, (const uint16_t*)gate,
+                     (const uint16_t*)up, ld, rows, kblocks, nblocks, (uint4*)y_out, (uint32_t*)q, (uint8_t*)scales);
   return hipGetLastError();
 }
 

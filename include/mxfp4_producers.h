@@ -97,6 +97,27 @@ mxfp4_status_t mxfp4_rmsnorm_quantize_prepacked(const void* x_bf16, const void* 
 mxfp4_status_t mxfp4_swiglu_quantize_prepacked(const void* gate_bf16, const void* up_bf16, int64_t ld, int64_t rows,
                                                int64_t k, void* y_bf16, void* ap_q, void* ap_s, void* stream);
 
+/*
+ * The two producers with their scale bytes in the interleaved layout of
+ * include/mxfp4.h (scales_il [k/512, rows, 16]), the A operand scales of
+ * mxfp4_gemm_nt_interleaved: a prefill activation produced and quantized in
+ * one launch for the tile GEMM's faster scale layout (the "fp4_quantization"
+ * page, grouped_quantize_dynamic_scaled_fp4_async: scales written in the
+ * matrix path's order as they are produced).  Codes q [rows, k/2] row-major;
+ * codes, scale values and the BF16 outputs those of mxfp4_rmsnorm_quantize /
+ * mxfp4_swiglu_quantize, byte for byte.  k a positive multiple of 512 and
+ * rows * k / 32 < 2^31 (MXFP4_ERR_INVALID_ARG otherwise); every other
+ * argument, limit and result as for the row-major producers.
+ */
+mxfp4_status_t mxfp4_rmsnorm_quantize_interleaved(const void* x_bf16, const void* residual_bf16,
+                                                  const void* gamma_bf16, float eps, int64_t rows, int64_t k,
+                                                  void* residual_out_bf16, void* y_bf16, void* q, void* scales_il,
+                                                  void* stream);
+
+mxfp4_status_t mxfp4_swiglu_quantize_interleaved(const void* gate_bf16, const void* up_bf16, int64_t ld,
+                                                 int64_t rows, int64_t k, void* y_bf16, void* q, void* scales_il,
+                                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -346,6 +346,19 @@ def test_w4a8_prepacked_rejects_bad_arguments_on_host(lib):
     assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0        # empty: no-op
 
 
+def test_interleaved_producers_reject_bad_arguments_on_host(lib):
+    f = _fake
+    r = lib.mxfp4_rmsnorm_quantize_interleaved
+    assert r(f(), None, f(), 1e-5, 4, 1024 + 32, None, None, f(), f(), None) == 1   # k % 512
+    assert b"multiple of 512" in lib.mxfp4_last_error()
+    assert r(f(), None, f(), -1.0, 4, 512, None, None, f(), f(), None) == 1          # eps
+    assert r(None, None, None, 1e-5, 0, 512, None, None, None, None, None) == 0      # no rows: no-op
+    w = lib.mxfp4_swiglu_quantize_interleaved
+    assert w(f(), f(), 1024 + 32, 4, 1024 + 32, None, f(), f(), None) == 1           # k % 512
+    assert w(f(), f(), 500, 4, 512, None, f(), f(), None) == 1                       # ld < k
+    assert w(None, None, 512, 0, 512, None, None, None, None) == 0                   # no rows: no-op
+
+
 def test_w4a8_both_prepacked_rejects_bad_arguments_on_host(lib):
     f = _fake
     q = lib.mxfp8_quantize_prepacked

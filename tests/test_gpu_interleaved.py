@@ -206,3 +206,71 @@ def test_moe_layer_interleaved_equals_row_major():
     torch.cuda.synchronize()
     assert torch.equal(aq, aq2)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+PRODUCER_CASES = [(1, 512, True), (37, 1536, False), (130, 4096, True), (64, 14336, False)]
+
+
+@pytest.mark.parametrize("rows,k,with_res", PRODUCER_CASES)
+def test_rmsnorm_interleaved_equals_row_major(rows, k, with_res):
+    """Same BF16 outputs and codes as the row-major producer; scales = its scales interleaved."""
+    from block_scaled_fp4_mxfp4_amd import mxfp4_rmsnorm_quantize
+    dev = device()
+    log(f"interleaved rmsnorm rows={rows} k={k} residual={with_res}")
+    x = random_bf16((rows, k), 60 + k, spread=5, outlier_frac=0.01).to(dev)
+    res = random_bf16((rows, k), 61 + k, spread=5).to(dev) if with_res else None
+    gamma = (1.0 + 0.2 * torch.randn(k, generator=torch.Generator().manual_seed(k))).to(torch.bfloat16).to(dev)
+    outs = []
+    for il in (False, True):
+        h = torch.empty((rows, k), dtype=torch.bfloat16, device=dev) if with_res else None
+        y = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+        if il:
+            sf, s = _with_canary((k // 512, rows, 16), torch.uint8, dev, 0x5A)
+            q, s = mxfp4_rmsnorm_quantize(x, gamma, 1e-5, residual=res, residual_out=h, y=y, scales=s, interleaved=True)
+        else:
+            q, s = mxfp4_rmsnorm_quantize(x, gamma, 1e-5, residual=res, residual_out=h, y=y)
+        outs.append((q, s, h, y))
+    torch.cuda.synchronize()
+    (q1, s1, h1, y1), (q2, s2, h2, y2) = outs
+    assert torch.equal(q1, q2) and torch.equal(y1, y2) and (not with_res or torch.equal(h1, h2))
+    assert np.array_equal(to_np(s2), interleave_numpy(to_np(s1)))
+    assert np.all(to_np(sf)[s2.numel():] == 0x5A)
+
+
+@pytest.mark.parametrize("rows,k,with_ld", [(1, 512, False), (37, 1536, True), (130, 4096, False), (64, 14336, True)])
+def test_swiglu_interleaved_equals_row_major(rows, k, with_ld):
+    from block_scaled_fp4_mxfp4_amd import mxfp4_swiglu_quantize
+    dev = device()
+    log(f"interleaved swiglu rows={rows} k={k}")
+    ld = 2 * k + (64 if with_ld else 0)
+    g = torch.Generator().manual_seed(rows + k)
+    base = (torch.randn(rows, ld, generator=g) * 3).to(torch.bfloat16).to(dev)
+    gate, up = base[:, :k], base[:, k:2 * k]
+    y1 = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((rows, k), dtype=torch.bfloat16, device=dev)
+    q1, s1 = mxfp4_swiglu_quantize(gate, up, y=y1)
+    sf, s = _with_canary((k // 512, rows, 16), torch.uint8, dev, 0x5A)
+    q2, s2 = mxfp4_swiglu_quantize(gate, up, y=y2, scales=s, interleaved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(y1, y2)
+    assert np.array_equal(to_np(s2), interleave_numpy(to_np(s1)))
+    assert np.all(to_np(sf)[s2.numel():] == 0x5A)
+
+
+def test_prefill_producer_to_interleaved_gemm():
+    """RMSNorm producer -> GEMM on interleaved scales gives the bits of RMSNorm producer -> GEMM on
+    row-major scales (the same tile kernel)."""
+    from block_scaled_fp4_mxfp4_amd import mxfp4_rmsnorm_quantize
+    dev = device()
+    m, n, k = 1024, 2048, 4096
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    x = random_bf16((m, k), 9, spread=4).to(dev)
+    gamma = torch.ones(k, dtype=torch.bfloat16, device=dev)
+    bq, bs = random_codes(n, k, 10)
+    d_bq, d_bs = upload(bq, dev), upload(bs, dev)
+    q1, s1 = mxfp4_rmsnorm_quantize(x, gamma, 1e-5)
+    q2, s2 = mxfp4_rmsnorm_quantize(x, gamma, 1e-5, interleaved=True)
+    c1 = mxfp4_gemm_nt(q1, s1, d_bq, d_bs, out_dtype=torch.float32, kernel=_tile_kernel_for(m, n, num_cus))
+    c2 = mxfp4_gemm_nt_interleaved(q2, s2, d_bq, mxfp4_scales_interleave(d_bs), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
