@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     mxfp4_prepacked_weight_size, mxfp4_prepack_weight, mxfp4_gemm_nt_prepacked, mxfp4_gemm_nt_prepacked_ab,
     mxfp4_quantize_prepacked, mxfp4_scales_interleave, mxfp4_quantize_interleaved, mxfp4_gemm_nt_interleaved,
     mxfp4_grouped_gemm_nt_interleaved, mxfp4_moe_quantize_scatter_interleaved, mxfp8_quantize_prepacked,
-    mxfp8_gemm_w4a8_nt_prepacked_ab,
+    mxfp8_gemm_w4a8_nt_prepacked_ab, mxfp8_quantize_interleaved, mxfp8_gemm_w4a8_nt_interleaved,
+    mxfp8_grouped_gemm_w4a8_nt_interleaved, mxfp8_gemm_nt_interleaved, mxfp8_moe_quantize_scatter_interleaved,
     LIB_PATH, EXPORTED, KERNELS,
 )

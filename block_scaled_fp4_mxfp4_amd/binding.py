@@ -37,7 +37,8 @@ EXPORTED = (
     "mxfp4_scales_interleave", "mxfp4_quantize_interleaved", "mxfp4_gemm_nt_interleaved",
     "mxfp4_grouped_gemm_nt_interleaved", "mxfp4_moe_quantize_scatter_interleaved",
     "mxfp8_quantize_prepacked", "mxfp8_gemm_w4a8_nt_prepacked_ab", "mxfp4_rmsnorm_quantize_interleaved",
-    "mxfp4_swiglu_quantize_interleaved",
+    "mxfp4_swiglu_quantize_interleaved", "mxfp8_quantize_interleaved", "mxfp8_gemm_w4a8_nt_interleaved",
+    "mxfp8_grouped_gemm_w4a8_nt_interleaved", "mxfp8_gemm_nt_interleaved", "mxfp8_moe_quantize_scatter_interleaved",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 PROBE_SEED_BYTES = 6144
@@ -128,6 +129,14 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         lib.mxfp4_moe_permute.restype = ctypes.c_int
         lib.mxfp4_moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+        lib.mxfp8_quantize_interleaved.restype = ctypes.c_int
+        lib.mxfp8_quantize_interleaved.argtypes = [vp, i64, i64, vp, vp, vp]
+        for name in ("mxfp8_gemm_w4a8_nt_interleaved", "mxfp8_gemm_nt_interleaved"):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.mxfp8_grouped_gemm_w4a8_nt_interleaved.restype = ctypes.c_int
+        lib.mxfp8_grouped_gemm_w4a8_nt_interleaved.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64,
+                                                               i64, vp]
         lib.mxfp8_quantize_prepacked.restype = ctypes.c_int
         lib.mxfp8_quantize_prepacked.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp8_gemm_w4a8_nt_prepacked_ab.restype = ctypes.c_int
@@ -141,7 +150,7 @@ def load_library(path: str = LIB_PATH):
         lib.mxfp4_grouped_gemm_nt_interleaved.restype = ctypes.c_int
         lib.mxfp4_grouped_gemm_nt_interleaved.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, ctypes.c_int, i64, i64, vp]
         for name in ("mxfp4_moe_quantize_scatter", "mxfp8_moe_quantize_scatter",
-                     "mxfp4_moe_quantize_scatter_interleaved"):
+                     "mxfp4_moe_quantize_scatter_interleaved", "mxfp8_moe_quantize_scatter_interleaved"):
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = [vp, i64, i64, i32, vp, i64, vp, vp, vp]
         lib.mxfp4_rmsnorm_quantize.restype = ctypes.c_int
@@ -496,6 +505,65 @@ def mxfp4_grouped_gemm_nt_interleaved(a_q, a_s_il, b_q, b_s_il, offsets, c=None,
     return c
 
 
+def mxfp8_quantize_interleaved(x: torch.Tensor, q8=None, scales_il=None, stream=None):
+    """x: bf16 [rows, k] -> (q8 uint8 [rows, k] E4M3 codes, scales_il uint8 [k/512, rows, 16])."""
+    lib = load_library()
+    rows, k = x.shape
+    if q8 is None:
+        q8 = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales_il is None:
+        scales_il = torch.empty((k // 512, rows, 16), dtype=torch.uint8, device=x.device)
+    _require(x, "x", torch.bfloat16, (rows, k))
+    _require(q8, "q8", torch.uint8, (rows, k))
+    _require(scales_il, "scales_il", torch.uint8, (k // 512, rows, 16))
+    _check(lib.mxfp8_quantize_interleaved(_ptr(x), rows, k, _ptr(q8), _ptr(scales_il), _stream(stream)))
+    return q8, scales_il
+
+
+def _gemm8_interleaved(fn, a_q8, a_s_il, b_q, b_s_il, b_cols, c, out_dtype, stream):
+    m, k = a_q8.shape
+    n = b_q.shape[0]
+    _require(a_q8, "a_q8", torch.uint8, (m, k))
+    _require(a_s_il, "a_s_il", torch.uint8, (k // 512, m, 16))
+    _require(b_q, "b_q", torch.uint8, (n, b_cols(k)))
+    _require(b_s_il, "b_s_il", torch.uint8, (k // 512, n, 16))
+    c, code = _out(c, m, n, out_dtype, a_q8.device)
+    _check(fn(_ptr(a_q8), _ptr(a_s_il), _ptr(b_q), _ptr(b_s_il), _ptr(c), code, m, n, k, _stream(stream)))
+    return c
+
+
+def mxfp8_gemm_w4a8_nt_interleaved(a_q8, a_s_il, b_q, b_s_il, c=None, out_dtype=torch.bfloat16, stream=None):
+    """W4A8 with interleaved scales: a_s_il [k/512, m, 16], b_s_il [k/512, n, 16] (128 x 256 tiles)."""
+    lib = load_library()
+    return _gemm8_interleaved(lib.mxfp8_gemm_w4a8_nt_interleaved, a_q8, a_s_il, b_q, b_s_il, lambda k: k // 2, c,
+                              out_dtype, stream)
+
+
+def mxfp8_gemm_nt_interleaved(a_q8, a_s_il, b_q8, b_s_il, c=None, out_dtype=torch.bfloat16, stream=None):
+    """MXFP8 x MXFP8 with interleaved scales: a_s_il [k/512, m, 16], b_s_il [k/512, n, 16]."""
+    lib = load_library()
+    return _gemm8_interleaved(lib.mxfp8_gemm_nt_interleaved, a_q8, a_s_il, b_q8, b_s_il, lambda k: k, c, out_dtype,
+                              stream)
+
+
+def mxfp8_grouped_gemm_w4a8_nt_interleaved(a_q8, a_s_il, b_q, b_s_il, offsets, c=None, out_dtype=torch.bfloat16,
+                                           stream=None):
+    """Grouped W4A8 with interleaved scales: a_s_il [k/512, total_m, 16], b_s_il [groups, k/512, n, 16]."""
+    lib = load_library()
+    total_m, k = a_q8.shape
+    groups, n, _ = b_q.shape
+    _require(a_q8, "a_q8", torch.uint8, (total_m, k))
+    _require(a_s_il, "a_s_il", torch.uint8, (k // 512, total_m, 16))
+    _require(b_q, "b_q", torch.uint8, (groups, n, k // 2))
+    _require(b_s_il, "b_s_il", torch.uint8, (groups, k // 512, n, 16))
+    _require(offsets, "offsets", torch.int32, (groups + 1,))
+    c, code = _out(c, total_m, n, out_dtype, a_q8.device)
+    _check(lib.mxfp8_grouped_gemm_w4a8_nt_interleaved(_ptr(a_q8), _ptr(a_s_il), _ptr(b_q), _ptr(b_s_il),
+                                                      _ptr(offsets), groups, total_m, _ptr(c), code, n, k,
+                                                      _stream(stream)))
+    return c
+
+
 def mxfp8_gemm_w4a8_nt(a_q8, a_s, b_q, b_s, c=None, out_dtype=torch.bfloat16, kernel: str = "auto", stream=None):
     """C[m, n] = A[m, k] . B[n, k]^T with A in MXFP8 ([m, k] codes) and B in MXFP4.
     kernel: "auto", "tile128" (128 x 256 tiles) or "stream"."""
@@ -655,6 +723,13 @@ def mxfp4_moe_quantize_scatter_interleaved(x, token_rows, total_rows: int, q=Non
     lib = load_library()
     return _quantize_scatter(lib.mxfp4_moe_quantize_scatter_interleaved, x, token_rows, total_rows, q, scales_il,
                              x.shape[1] // 2, stream, interleaved=True)
+
+
+def mxfp8_moe_quantize_scatter_interleaved(x, token_rows, total_rows: int, q8=None, scales_il=None, stream=None):
+    """mxfp8_moe_quantize_scatter with the scales interleaved: scales_il [k/512, total_rows, 16]."""
+    lib = load_library()
+    return _quantize_scatter(lib.mxfp8_moe_quantize_scatter_interleaved, x, token_rows, total_rows, q8, scales_il,
+                             x.shape[1], stream, interleaved=True)
 
 
 def mxfp8_moe_quantize_scatter(x, token_rows, total_rows: int, q8=None, scales=None, stream=None):

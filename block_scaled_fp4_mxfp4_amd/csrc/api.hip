@@ -790,6 +790,91 @@ mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, con
   return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile(args, (hipStream_t)stream), "grouped w4a8 gemm launch");
 }
 
+mxfp4_status_t mxfp8_quantize_interleaved(const void* x_bf16, int64_t rows, int64_t k, void* q8, void* scales_il,
+                                          void* stream) {
+  if (rows < 0) return fail(MXFP4_ERR_INVALID_ARG, "negative rows");
+  MXFP4_TRY(check_k(k));
+  if (k % 512 != 0) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need k %% 512 == 0 (got %lld)", (long long)k);
+  if (rows * (k / 32) >= ((int64_t)1 << 31)) return fail(MXFP4_ERR_INVALID_ARG, "interleaved scales need rows * k / 32 < 2^31");
+  if (rows == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(x_bf16, "x_bf16"));
+  MXFP4_TRY(check_ptr(q8, "q8", 8));
+  MXFP4_TRY(check_ptr(scales_il, "scales_il", 1));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  return hip_status(mxfp4::launch_quantize_mxfp8(x_bf16, rows, k, q8, scales_il, (hipStream_t)stream, dev.num_cus,
+                                                 true), "interleaved mxfp8 quantize launch");
+}
+
+namespace {
+mxfp4::GemmArgs interleaved_args(const void* a_q, const void* a_s, const void* b_q, const void* b_s, void* c,
+                                 mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k) {
+  mxfp4::GemmArgs args{};
+  args.a_q = (const uint8_t*)a_q;
+  args.a_s = (const uint8_t*)a_s;
+  args.b_q = (const uint8_t*)b_q;
+  args.b_s = (const uint8_t*)b_s;
+  args.c = c;
+  args.c_f32 = c_type == MXFP4_OUT_F32;
+  args.m = (int)m;
+  args.n = (int)n;
+  args.k = (int)k;
+  args.scale_il = 1;
+  return args;
+}
+}  // namespace
+
+mxfp4_status_t mxfp8_gemm_w4a8_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q,
+                                              const void* b_s_il, void* c, mxfp4_out_t c_type, int64_t m, int64_t n,
+                                              int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s_il, b_q, b_s_il, c, c_type, m, n, k));
+  MXFP4_TRY(check_interleaved(a_s_il, b_s_il, m, n, k));
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  // the 128 x 256 tile kernel at every m (the small-M kernels read row-major scales)
+  return hip_status(mxfp4::launch_gemm_w4a8_tile(interleaved_args(a_q8, a_s_il, b_q, b_s_il, c, c_type, m, n, k),
+                                                 (hipStream_t)stream), "interleaved w4a8 gemm launch");
+}
+
+mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q,
+                                                      const void* b_s_il, const int32_t* offsets, int32_t num_groups,
+                                                      int64_t total_m, void* c, mxfp4_out_t c_type, int64_t n,
+                                                      int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s_il, b_q, b_s_il, c, c_type, total_m, n, k));
+  MXFP4_TRY(check_interleaved(a_s_il, b_s_il, total_m, n, k));
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(MXFP4_ERR_INVALID_ARG, "num_groups must be 1..1024 (got %d)", num_groups);
+  if (total_m == 0 || n == 0) return MXFP4_OK;
+  MXFP4_TRY(check_ptr(offsets, "offsets", 4));
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  mxfp4::GemmArgs args = interleaved_args(a_q8, a_s_il, b_q, b_s_il, c, c_type, total_m, n, k);
+  args.offsets = offsets;
+  args.groups = num_groups;
+  // the same kernel choice as mxfp8_grouped_gemm_w4a8_nt
+  if (mxfp4::gemm_persistent_supported(args))
+    return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile_persistent(args, dev.num_cus, 0, (hipStream_t)stream),
+                      "interleaved grouped w4a8 gemm launch");
+  return hip_status(mxfp4::launch_grouped_gemm_w4a8_tile(args, (hipStream_t)stream),
+                    "interleaved grouped w4a8 gemm launch");
+}
+
+mxfp4_status_t mxfp8_gemm_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q8, const void* b_s_il,
+                                         void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream) {
+  MXFP4_TRY(check_gemm_args(a_q8, a_s_il, b_q8, b_s_il, c, c_type, m, n, k));
+  if (k > kMaxK / 2) return fail(MXFP4_ERR_INVALID_ARG, "k too large for MXFP8 operands (%lld > %lld)",
+                                 (long long)k, (long long)(kMaxK / 2));
+  MXFP4_TRY(check_interleaved(a_s_il, b_s_il, m, n, k));
+  if (m == 0 || n == 0) return MXFP4_OK;
+  DeviceInfo dev;
+  MXFP4_TRY(current_device(dev));
+  // the same tile choice as mxfp8_gemm_nt
+  const mxfp4::TileKind kind = ((m + 255) / 256) * ((n + 255) / 256) < dev.num_cus ? mxfp4::kTile128 : mxfp4::kTile256;
+  return hip_status(mxfp4::launch_gemm_mxfp8_tile(interleaved_args(a_q8, a_s_il, b_q8, b_s_il, c, c_type, m, n, k),
+                                                  kind, (hipStream_t)stream), "interleaved mxfp8 gemm launch");
+}
+
 namespace {
 mxfp4_status_t probe_mfma(const void* seed, void* out, int32_t blocks, int32_t iters, bool a_fp8, void* stream) {
   if (blocks < 1 || blocks > 65536) return fail(MXFP4_ERR_INVALID_ARG, "blocks must be 1..65536 (got %d)", blocks);
@@ -904,6 +989,12 @@ mxfp4_status_t mxfp4_moe_quantize_scatter_interleaved(const void* x_bf16, int64_
                                                       const int32_t* token_rows, int64_t total_rows, void* q,
                                                       void* scales_il, void* stream) {
   return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q, scales_il, false, stream, true);
+}
+
+mxfp4_status_t mxfp8_moe_quantize_scatter_interleaved(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                                      const int32_t* token_rows, int64_t total_rows, void* q8,
+                                                      void* scales_il, void* stream) {
+  return moe_quantize_scatter(x_bf16, tokens, k, top_k, token_rows, total_rows, q8, scales_il, true, stream, true);
 }
 
 mxfp4_status_t mxfp8_moe_quantize_scatter(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,

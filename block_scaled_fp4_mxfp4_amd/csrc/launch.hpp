@@ -41,7 +41,7 @@ hipError_t launch_scales_interleave(const void* scales, int64_t groups, int64_t 
 hipError_t launch_quantize_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
                                      hipStream_t stream, int num_cus);
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
-                                 hipStream_t stream, int num_cus);
+                                 hipStream_t stream, int num_cus, bool interleaved = false);
 // MXFP8 codes and scales stored in the FP8 prepacked operand layout (k % 512 == 0;
 // rows up to the next multiple of 64 written as zero blocks).
 hipError_t launch_quantize_mxfp8_prepacked(const void* x, int64_t rows, int64_t k, void* q, void* scales,
@@ -129,7 +129,7 @@ hipError_t launch_moe_route(const float* logits, int tokens, int experts, int to
                             hipStream_t stream);
 hipError_t launch_moe_permute(const int32_t* ids, int n, int top_k, int experts, int32_t* offsets,
                               int32_t* row_token, int32_t* token_rows, hipStream_t stream);
-// interleaved: the MXFP4 scale bytes in the interleaved layout [k/512, total_rows, 16]
+// interleaved: the scale bytes in the interleaved layout [k/512, total_rows, 16]
 // (k % 512 == 0, total_rows * k/32 < 2^31).
 hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top_k, const int32_t* token_rows,
                                        int total_rows, void* q, void* scales, bool fp8, hipStream_t stream,

@@ -342,7 +342,7 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(uint32_t w01, uint32_t w23, float 
 // FP8 = false: MXFP4 rows (K/2 code bytes, 4 per lane); true: MXFP8 rows
 // (K code bytes, 8 per lane).  Scale rule and converts as in the dense
 // quantizers: byte = max(E - 2, 0) (FP4) or max(E - 8, 0) (FP8) for amax's
-// biased exponent E.  IL (MXFP4 only): scale bytes in the interleaved layout
+// biased exponent E.  IL: scale bytes in the interleaved layout
 // [k/512, total_rows, 16].
 template <bool FP8, bool IL>
 __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
@@ -513,7 +513,7 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
                                        int total_rows, void* q, void* scales, bool fp8, hipStream_t stream,
                                        int num_cus, bool interleaved) {
   const int kblocks = k / 32;
-  if (interleaved && (fp8 || k % 512 != 0 || (int64_t)total_rows * kblocks >= ((int64_t)1 << 31)))
+  if (interleaved && (k % 512 != 0 || (int64_t)total_rows * kblocks >= ((int64_t)1 << 31)))
     return hipErrorInvalidValue;
   const int nblocks = tokens * kblocks;   // the host keeps this below 2^31
   const int64_t groups_needed = ((int64_t)nblocks + kScatterUnroll - 1) / kScatterUnroll;
@@ -521,7 +521,7 @@ hipError_t launch_moe_quantize_scatter(const void* x, int tokens, int k, int top
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  const auto kernel = fp8 ? quantize_scatter_kernel<true, false>
+  const auto kernel = fp8 ? (interleaved ? quantize_scatter_kernel<true, true> : quantize_scatter_kernel<true, false>)
                           : (interleaved ? quantize_scatter_kernel<false, true> : quantize_scatter_kernel<false, false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream, (const uint4*)x, kblocks,
                      nblocks, top_k, token_rows, total_rows, (uint8_t*)q, (uint8_t*)scales);

@@ -203,19 +203,29 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(uint32_t w01, uint32_t w23, float 
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// IL: interleaved scales, the blocks walked in that layout's order as in
+// quantize_kernel (rows * k/32 < 2^31).
+template <bool IL>
 __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
-    const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ scales, int64_t nblocks) {
+    const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ scales, int64_t nblocks,
+    uint32_t bpr, uint32_t rows) {
   const int lane4 = threadIdx.x & 3;
   const int64_t groups_per_grid = (int64_t)gridDim.x * (kQuantThreads / 4);
   int64_t blk = (int64_t)blockIdx.x * (kQuantThreads / 4) + (threadIdx.x >> 2);
 
   for (; blk < nblocks; blk += groups_per_grid * kQuantUnroll) {
     uint4 v[kQuantUnroll];
+    int64_t src[kQuantUnroll];   // the step's block in x and q (row-major order)
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
       const int64_t b = blk + u * groups_per_grid;
+      src[u] = b;
+      if constexpr (IL) {
+        const uint32_t piece = (uint32_t)b >> 4, g = piece / rows, r = piece - g * rows;
+        src[u] = (int64_t)r * bpr + g * 16 + ((uint32_t)b & 15);
+      }
       // BF16 input read once: non-temporal (same-box A/B on 4096 x 4096: 9.73-9.84 vs 9.84-10.19 us)
-      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? b : 0) * 4 + lane4));
+      const v4i t = __builtin_nontemporal_load((const v4i*)(x + (b < nblocks ? src[u] : 0) * 4 + lane4));
       v[u] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
     }
 #pragma unroll
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
       const uint32_t lo = cvt_fp8x4(clamp_mag16x2(v[u].x, bound), clamp_mag16x2(v[u].y, bound), scale);
       const uint32_t hi = cvt_fp8x4(clamp_mag16x2(v[u].z, bound), clamp_mag16x2(v[u].w, bound), scale);
       if (b < nblocks) {
-        q[b * 4 + lane4] = make_uint2(lo, hi);
+        q[src[u] * 4 + lane4] = make_uint2(lo, hi);
         if (lane4 == 0) scales[b] = (uint8_t)sbyte;
       }
     }
@@ -295,15 +305,17 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_prepacked_kernel
 }  // namespace
 
 hipError_t launch_quantize_mxfp8(const void* x, int64_t rows, int64_t k, void* q, void* scales,
-                                 hipStream_t stream, int num_cus) {
+                                 hipStream_t stream, int num_cus, bool interleaved) {
   const int64_t nblocks = rows * (k / 32);
+  if (interleaved && (k % 512 != 0 || nblocks >= ((int64_t)1 << 31))) return hipErrorInvalidValue;
   const int64_t groups_needed = (nblocks + kQuantUnroll - 1) / kQuantUnroll;
   int64_t grid = (groups_needed + (kQuantThreads / 4) - 1) / (kQuantThreads / 4);
   const int64_t max_grid = (int64_t)num_cus * 8;
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream,
-                     (const uint4*)x, (uint2*)q, (uint8_t*)scales, nblocks);
+  const auto kernel = interleaved ? quantize_mxfp8_kernel<true> : quantize_mxfp8_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, stream, (const uint4*)x, (uint2*)q,
+                     (uint8_t*)scales, nblocks, (uint32_t)(k / 32), (uint32_t)rows);
   return hipGetLastError();
 }
 

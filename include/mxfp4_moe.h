@@ -109,6 +109,14 @@ mxfp4_status_t mxfp8_moe_quantize_scatter(const void* x_bf16, int64_t tokens, in
                                           const int32_t* token_rows, int64_t total_rows, void* q8,
                                           void* scales, void* stream);
 
+/* mxfp8_moe_quantize_scatter with the scale bytes interleaved (scales_il
+ * [k/512, total_rows, 16]), the A operand of
+ * mxfp8_grouped_gemm_w4a8_nt_interleaved; limits as for
+ * mxfp4_moe_quantize_scatter_interleaved. */
+mxfp4_status_t mxfp8_moe_quantize_scatter_interleaved(const void* x_bf16, int64_t tokens, int64_t k, int32_t top_k,
+                                                      const int32_t* token_rows, int64_t total_rows, void* q8,
+                                                      void* scales_il, void* stream);
+
 /*
  * Weighted combine: out[t, :] = sum over slots j in order 0..top_k-1 whose row
  * r = token_rows[t, j] lies in [0, total_rows) of topk_weights[t, j] *

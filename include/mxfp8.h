@@ -196,6 +196,43 @@ mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt(const void* a_q8, const void* a_s, con
                                           const int32_t* offsets, int32_t num_groups, int64_t total_m, void* c,
                                           mxfp4_out_t c_type, int64_t n, int64_t k, void* stream);
 
+/*
+ * The MXFP8 and W4A8 tile GEMMs on interleaved scales: the interleaved layout
+ * of include/mxfp4.h ([k/512, rows, 16] per operand: the sixteen scale bytes
+ * of a 512-wide K slab of a row next to the next row's; mxfp4_scales_interleave
+ * converts row-major scales, and the quantizers below write it directly) for
+ * the MXFP8 operands as for the MXFP4 ones.  Same values, bit-identical results
+ * to the row-major entry points on the same tile kernels.
+ *
+ * mxfp8_quantize_interleaved: mxfp8_quantize with the scales written
+ *   interleaved (codes as mxfp8_quantize).
+ * mxfp8_gemm_w4a8_nt_interleaved: mxfp8_gemm_w4a8_nt_ex with
+ *   MXFP4_KERNEL_TILE128 (128 x 256 tiles) at every m, both scale arrays
+ *   interleaved.
+ * mxfp8_grouped_gemm_w4a8_nt_interleaved: mxfp8_grouped_gemm_w4a8_nt with
+ *   a_s_il over total_m rows and b_s_il interleaved per group.
+ * mxfp8_gemm_nt_interleaved: mxfp8_gemm_nt (MXFP8 x MXFP8) with both scale
+ *   arrays interleaved; the same tile choice.
+ * Limits: k a positive multiple of 512 (MXFP8 x MXFP8: at most 2^23, else
+ * 2^24); m * k / 32 and n * k / 32 (total_m * k / 32) below 2^31; scale arrays
+ * 16-byte aligned; every other argument as for the row-major entry point.
+ * Violations return MXFP4_ERR_INVALID_ARG.
+ */
+mxfp4_status_t mxfp8_quantize_interleaved(const void* x_bf16, int64_t rows, int64_t k, void* q8, void* scales_il,
+                                          void* stream);
+
+mxfp4_status_t mxfp8_gemm_w4a8_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q,
+                                              const void* b_s_il, void* c, mxfp4_out_t c_type, int64_t m, int64_t n,
+                                              int64_t k, void* stream);
+
+mxfp4_status_t mxfp8_grouped_gemm_w4a8_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q,
+                                                      const void* b_s_il, const int32_t* offsets, int32_t num_groups,
+                                                      int64_t total_m, void* c, mxfp4_out_t c_type, int64_t n,
+                                                      int64_t k, void* stream);
+
+mxfp4_status_t mxfp8_gemm_nt_interleaved(const void* a_q8, const void* a_s_il, const void* b_q8, const void* b_s_il,
+                                         void* c, mxfp4_out_t c_type, int64_t m, int64_t n, int64_t k, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -178,6 +178,21 @@ def test_interleaved_entry_points_reject_bad_arguments_on_host(lib):
     assert lib.mxfp4_moe_quantize_scatter_interleaved(f(), 4, 256, 2, f(), 8, f(), f(), None) == 1
     assert lib.mxfp4_moe_quantize_scatter_interleaved(f(), 4, 512, 2, f(), (1 << 27), f(), f(), None) == 1
     assert lib.mxfp4_moe_quantize_scatter_interleaved(None, 0, 512, 2, None, 8, None, None, None) == 0
+    # the MXFP8 / W4A8 counterparts: the same k % 512 and size rules
+    assert lib.mxfp8_quantize_interleaved(f(), 4, 1024 + 32, f(), f(), None) == 1
+    assert lib.mxfp8_quantize_interleaved(None, 0, 512, None, None, None) == 0
+    for g in (lib.mxfp8_gemm_w4a8_nt_interleaved, lib.mxfp8_gemm_nt_interleaved):
+        assert g(f(), f(), f(), f(), f(), 0, 64, 64, 256, None) == 1
+        assert g(f(), f(0x1004), f(), f(), f(), 0, 64, 64, 512, None) == 1
+        assert g(f(), f(), f(), f(), f(), 0, 1 << 27, 64, 512, None) == 1
+        assert g(None, None, f(), f(), None, 0, 0, 64, 512, None) == 0
+    assert lib.mxfp8_gemm_nt_interleaved(f(), f(), f(), f(), f(), 0, 64, 64, 1 << 24, None) == 1   # k > 2^23
+    gw = lib.mxfp8_grouped_gemm_w4a8_nt_interleaved
+    assert gw(f(), f(), f(), f(), f(), 4, 64, f(), 0, 64, 1536 + 32, None) == 1
+    assert gw(f(), f(), f(), f(), None, 4, 64, f(), 0, 64, 512, None) == 1
+    assert gw(None, None, f(), f(), None, 4, 0, None, 0, 64, 512, None) == 0
+    assert lib.mxfp8_moe_quantize_scatter_interleaved(f(), 4, 256, 2, f(), 8, f(), f(), None) == 1
+    assert lib.mxfp8_moe_quantize_scatter_interleaved(None, 0, 512, 2, None, 8, None, None, None) == 0
 
 
 def test_workspace_queries(lib):

@@ -274,3 +274,100 @@ def test_prefill_producer_to_interleaved_gemm():
     c2 = mxfp4_gemm_nt_interleaved(q2, s2, d_bq, mxfp4_scales_interleave(d_bs), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 activations (W4A8) and MXFP8 x MXFP8 on interleaved scales
+
+
+@pytest.mark.parametrize("rows,k", [(1, 512), (3, 1024), (257, 4096), (1000, 1536)])
+def test_mxfp8_quantize_interleaved_is_the_layout_of_the_oracle_bytes(rows, k):
+    from block_scaled_fp4_mxfp4_amd import mxfp8_quantize_interleaved
+    dev = device()
+    log(f"interleaved mxfp8 quantize rows={rows} k={k}")
+    bits = _random_bits(rows, k, rows * 5 + k)
+    sf, s = _with_canary((k // 512, rows, 16), torch.uint8, dev, 0x5A)
+    q, s = mxfp8_quantize_interleaved(bf16_from_np_bits(bits).to(dev), scales_il=s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_mxfp8(bits)
+    assert np.array_equal(to_np(q), rq), "code bytes"
+    assert np.array_equal(to_np(s), interleave_numpy(rs)), "interleaved scale bytes"
+    assert np.all(to_np(sf)[s.numel():] == 0x5A)
+
+
+def _w4a8_operands(m, n, k, seed, b_fp8=False):
+    a = random_bf16((m, k), seed, spread=3, outlier_frac=0.01)
+    b = random_bf16((n, k), seed + 1, spread=3)
+    aq, as_ = oracle.quantize_mxfp8(workloads.bf16_bits(a))
+    bq, bs = (oracle.quantize_mxfp8 if b_fp8 else oracle.quantize)(workloads.bf16_bits(b))
+    return aq, as_, bq, bs
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 512), (100, 300, 1536), (300, 257, 1024), (1024, 1000, 4096)])
+def test_w4a8_and_mxfp8_interleaved_equal_row_major(m, n, k):
+    from block_scaled_fp4_mxfp4_amd import (mxfp8_gemm_nt, mxfp8_gemm_nt_interleaved, mxfp8_gemm_w4a8_nt,
+                                            mxfp8_gemm_w4a8_nt_interleaved)
+    dev = device()
+    log(f"interleaved w4a8 / mxfp8 m={m} n={n} k={k}")
+    for b_fp8 in (False, True):
+        aq, as_, bq, bs = (upload(t, dev) for t in _w4a8_operands(m, n, k, m + n + k, b_fp8))
+        as_il, bs_il = mxfp4_scales_interleave(as_), mxfp4_scales_interleave(bs)
+        for dt in (torch.float32, torch.bfloat16):
+            cf, c = _with_canary((m, n), dt, dev, 0xFF)
+            if b_fp8:
+                mxfp8_gemm_nt_interleaved(aq, as_il, bq, bs_il, c=c)
+                ref = mxfp8_gemm_nt(aq, as_, bq, bs, out_dtype=dt)
+            else:
+                mxfp8_gemm_w4a8_nt_interleaved(aq, as_il, bq, bs_il, c=c)
+                ref = mxfp8_gemm_w4a8_nt(aq, as_, bq, bs, out_dtype=dt, kernel="tile128")
+            torch.cuda.synchronize()
+            assert torch.equal(c.view(torch.uint8), ref.view(torch.uint8)), f"b_fp8={b_fp8} {dt}"
+            assert np.all(to_np(cf)[c.numel() * c.element_size():] == 0xFF), "write past the end of C"
+
+
+@pytest.mark.parametrize("name", ["all_rows_one_expert", "empty_first_middle_last", "persistent_ragged",
+                                  "persistent_many_tiles"])
+def test_grouped_w4a8_interleaved_equals_row_major(name):
+    from block_scaled_fp4_mxfp4_amd import mxfp8_grouped_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt_interleaved
+    dev = device()
+    counts, n, k = GROUP_CASES[name]
+    counts = np.asarray(counts)
+    groups, total = len(counts), int(np.sum(counts))
+    log(f"interleaved grouped w4a8 {name}: {groups} groups, {total} rows")
+    offsets = upload(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), dev)
+    aq, as_, _, _ = _w4a8_operands(total, 1, k, total + k)
+    wq, ws = random_codes(groups * n, k, groups + n)
+    d_aq, d_as = upload(aq, dev), upload(as_, dev)
+    d_wq, d_ws = upload(wq, dev).view(groups, n, k // 2), upload(ws, dev).view(groups, n, k // 32)
+    cf, c = _with_canary((total, n), torch.float32, dev, 0xFF)
+    mxfp8_grouped_gemm_w4a8_nt_interleaved(d_aq, mxfp4_scales_interleave(d_as), d_wq, mxfp4_scales_interleave(d_ws),
+                                           offsets, c=c)
+    ref = mxfp8_grouped_gemm_w4a8_nt(d_aq, d_as, d_wq, d_ws, offsets, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
+    assert np.all(to_np(cf)[c.numel() * 4:] == 0xFF)
+
+
+def test_w4a8_moe_layer_interleaved_equals_row_major():
+    """Route -> permute -> MXFP8 scatter-quantize -> grouped W4A8 GEMM -> combine, 2048 tokens, 16 experts,
+    on interleaved scales against row-major scales, bit for bit."""
+    from block_scaled_fp4_mxfp4_amd import (mxfp8_grouped_gemm_w4a8_nt, mxfp8_grouped_gemm_w4a8_nt_interleaved,
+                                            mxfp8_moe_quantize_scatter, mxfp8_moe_quantize_scatter_interleaved)
+    dev = device()
+    tokens, experts, top_k, n, k = 2048, 16, 4, 1024, 2048
+    x = random_bf16((tokens, k), 77, spread=4).to(dev)
+    lg = torch.from_numpy(np.random.default_rng(78).standard_normal((tokens, experts)).astype(np.float32)).to(dev)
+    wq, ws = random_codes(experts * n, k, 79)
+    d_wq, d_ws = upload(wq, dev).view(experts, n, k // 2), upload(ws, dev).view(experts, n, k // 32)
+    ids, gate = mxfp4_moe_route(lg, top_k)
+    off, _, tr = mxfp4_moe_permute(ids, experts)
+    rows = tokens * top_k
+    aq, as_ = mxfp8_moe_quantize_scatter(x, tr, rows)
+    out = mxfp4_moe_combine(mxfp8_grouped_gemm_w4a8_nt(aq, as_, d_wq, d_ws, off), tr, gate)
+    aq2, as_il = mxfp8_moe_quantize_scatter_interleaved(x, tr, rows)
+    out2 = mxfp4_moe_combine(mxfp8_grouped_gemm_w4a8_nt_interleaved(aq2, as_il, d_wq, mxfp4_scales_interleave(d_ws),
+                                                                    off), tr, gate)
+    torch.cuda.synchronize()
+    assert torch.equal(aq, aq2)
+    assert np.array_equal(to_np(as_il), interleave_numpy(to_np(as_)))
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
