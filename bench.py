@@ -156,9 +156,9 @@ class DenseBench:
         self.dev = dev
         self.act = act
         self.with_b = quantize_b_in_step
-        # interleaved scales (the tile kernels' copy layout) wherever the MXFP4
-        # tile kernels run: prefill shapes with k % 512 == 0
-        il_ok = act == "mxfp4" and w.m > 128 and w.k % 512 == 0
+        # interleaved scales (the tile kernels' copy layout) wherever the tile
+        # kernels run: prefill shapes with k % 512 == 0
+        il_ok = w.m > 128 and w.k % 512 == 0
         self.il = il_ok if interleaved is None else (interleaved and il_ok)
         a8 = act in ("mxfp8", "mxfp8x8")
         k_a = w.k if a8 else w.k // 2                    # A code bytes per row
@@ -204,7 +204,7 @@ class DenseBench:
     def quantize(self, i):
         s = self.sets[i % self.sets_n]
         if self.act in ("mxfp8", "mxfp8x8"):
-            self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+            (self.B.mxfp8_quantize_interleaved if self.il else self.B.mxfp8_quantize)(s["a"], s["aq"], s["as_"])
         elif self.il:
             self.B.mxfp4_quantize_interleaved(s["a"], s["aq"], s["as_"])
         else:
@@ -227,9 +227,15 @@ class DenseBench:
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
-            self.B.mxfp8_gemm_w4a8_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+            if self.il:
+                self.B.mxfp8_gemm_w4a8_nt_interleaved(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+            else:
+                self.B.mxfp8_gemm_w4a8_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         elif self.act == "mxfp8x8":
-            self.B.mxfp8_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+            if self.il:
+                self.B.mxfp8_gemm_nt_interleaved(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
+            else:
+                self.B.mxfp8_gemm_nt(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         elif self.il:
             self.B.mxfp4_gemm_nt_interleaved(s["aq"], s["as_"], s["bq"], s["bs"], c=s["c"])
         else:
@@ -328,7 +334,7 @@ class MoEBench:
         self.B = B
         self.w = w
         self.act = act
-        self.il = interleaved and act == "mxfp4" and w.k % 512 == 0   # interleaved scales (see DenseBench)
+        self.il = interleaved and w.k % 512 == 0   # interleaved scales (see DenseBench)
         a, wts, offsets = w.make()
         self.counts = (offsets[1:] - offsets[:-1]).tolist()
         rows, n, k, e = w.total_rows, w.n, w.k, w.experts
@@ -355,7 +361,7 @@ class MoEBench:
     def quantize(self, i):
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
-            self.B.mxfp8_quantize(s["a"], s["aq"], s["as_"])
+            (self.B.mxfp8_quantize_interleaved if self.il else self.B.mxfp8_quantize)(s["a"], s["aq"], s["as_"])
         elif self.il:
             self.B.mxfp4_quantize_interleaved(s["a"], s["aq"], s["as_"])
         else:
@@ -364,7 +370,8 @@ class MoEBench:
     def gemm(self, i):
         s = self.sets[i % self.sets_n]
         if self.act == "mxfp8":
-            self.B.mxfp8_grouped_gemm_w4a8_nt(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
+            fn = self.B.mxfp8_grouped_gemm_w4a8_nt_interleaved if self.il else self.B.mxfp8_grouped_gemm_w4a8_nt
+            fn(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
         elif self.il:
             self.B.mxfp4_grouped_gemm_nt_interleaved(s["aq"], s["as_"], s["wq"], s["ws"], s["off"], c=s["c"])
         else:
@@ -791,7 +798,9 @@ def traffic_from_profiles(workload: str, kernel: str):
 def measure_w4a8(args, dev, w, us):
     """W4A8 (MXFP8 activations x MXFP4 weights) on the primary, decode and MoE
     workloads: step = MXFP8 quantization of A + the W4A8 GEMM."""
-    out = {"dtype": "mxfp8 e4m3 x mxfp4 e2m1, e8m0 block scales, fp32 accumulate, bf16 out"}
+    out = {"dtype": "mxfp8 e4m3 x mxfp4 e2m1, e8m0 block scales, fp32 accumulate, bf16 out",
+           "scales": "interleaved for the prefill and MoE GEMMs (written by the quantizers); decode: row-major A, "
+                     "prepacked weight"}
     eprint(f"[bench] W4A8 on {w.name}")
     b = DenseBench(w, dev, "mxfp8")
     s = b.timed(b.step, args.detail_steps, args.detail_warmup)
@@ -949,7 +958,8 @@ def measure_mxfp8(args, dev, w):
     g = b.timed(b.gemm, args.detail_steps, args.detail_warmup)
     tf = w.flops / (g["mean"] * 1e-3) / 1e12
     out = {"workload": w.name, "dtype": "mxfp8 e4m3 x mxfp8 e4m3, e8m0 block scales, fp32 accumulate, bf16 out",
-           "step": "quantize A (bf16->mxfp8) + mxfp8 x mxfp8 NT GEMM -> bf16 (B quantized to mxfp8 once)",
+           "step": "quantize A (bf16->mxfp8) + mxfp8 x mxfp8 NT GEMM -> bf16 (B quantized to mxfp8 once; "
+                   "interleaved scales)",
            "step_us": us(s), "step_tflops": round(w.flops / (s["mean"] * 1e-3) / 1e12, 2), "gemm_us": us(g),
            "roofline": roofline("mfma", tf, PEAK_FP8_TFLOPS, "TFLOP/s",
                                 traffic_from_profiles(w.name, "gemm_tile_kernel_f8f8"),
