@@ -312,6 +312,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
 
 constexpr int kScatterThreads = 256;
 constexpr int kScatterUnroll = 4;
+constexpr int kScatterSlots = 4;   // slots whose destination rows are loaded with the blocks
 
 __device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
   return max(a & 0xFFFFu, b & 0xFFFFu) | (max(a >> 16, b >> 16) << 16);
@@ -360,6 +361,17 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
       const int b = blk + u * groups_per_grid;
       v[u] = x[(int64_t)(b < nblocks ? b : 0) * 4 + lane4];   // out-of-range groups load block 0, store nothing
     }
+    // the destination rows of the first kScatterSlots slots of every block,
+    // loaded with the blocks rather than one slot at a time before each store
+    int rws[kScatterUnroll][kScatterSlots];
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      const int b = blk + u * groups_per_grid;
+      const int t = b / kblocks;
+#pragma unroll
+      for (int j = 0; j < kScatterSlots; ++j)
+        rws[u][j] = (b < nblocks && j < top_k) ? token_rows[(int64_t)t * top_k + j] : -1;
+    }
 #pragma unroll
     for (int u = 0; u < kScatterUnroll; ++u) {
       const int b = blk + u * groups_per_grid;
@@ -384,7 +396,14 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
       }
       if (b >= nblocks) continue;   // uniform over the lane group
       for (int j = 0; j < top_k; ++j) {
-        const int r = token_rows[(int64_t)t * top_k + j];
+        int r;
+        if (j < kScatterSlots) {
+          r = -1;
+#pragma unroll
+          for (int i = 0; i < kScatterSlots; ++i) r = (i == j) ? rws[u][i] : r;
+        } else {
+          r = token_rows[(int64_t)t * top_k + j];
+        }
         if (r < 0 || r >= total_rows) continue;   // dropped entry (or a malformed row index)
         if constexpr (FP8) {
           *(uint2*)(q + (int64_t)r * kblocks * 32 + kb * 32 + lane4 * 8) = codes8;
@@ -407,6 +426,7 @@ __global__ __launch_bounds__(kScatterThreads) void quantize_scatter_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineSlots = 8;   // slots whose rows are loaded together
 
 template <bool F32_OUT, bool VEC>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y, int total_rows,
@@ -422,29 +442,53 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const int r = token_rows[(int64_t)t * top_k + j];
-    if (r < 0 || r >= total_rows) continue;
-    const float w = weights[(int64_t)t * top_k + j];
-    const uint16_t* src = y + (int64_t)r * n + col0;
-    uint32_t word[4];
-    if (VEC) {
-      // each expert-output row is read once: non-temporal (same-box A/B on the
-      // MoE workload's combine: 45.4-47.3 vs 48.6-50.0 us)
-      const v4i v = __builtin_nontemporal_load((const v4i*)src);
-      word[0] = (uint32_t)v.x; word[1] = (uint32_t)v.y; word[2] = (uint32_t)v.z; word[3] = (uint32_t)v.w;
-    } else {
+  // per group of kCombineSlots slots, all row indices and then all row loads
+  // are issued before the group's first sum: up to kCombineSlots independent
+  // 16-byte loads in flight per lane instead of one index-then-row chain per
+  // slot.  The sums still run in slot order.
+  for (int j0 = 0; j0 < top_k; j0 += kCombineSlots) {
+    int rows[kCombineSlots];
+    float wts[kCombineSlots];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (2 * e < cnt) ? src[2 * e] : 0u;
-        const uint32_t hi = (2 * e + 1 < cnt) ? src[2 * e + 1] : 0u;
-        word[e] = lo | (hi << 16);
+    for (int j = 0; j < kCombineSlots; ++j) {
+      rows[j] = -1;
+      wts[j] = 0.0f;
+      if (j0 + j < top_k) {
+        const int64_t slot = (int64_t)t * top_k + j0 + j;
+        const int r = token_rows[slot];
+        rows[j] = (r >= 0 && r < total_rows) ? r : -1;
+        wts[j] = weights[slot];
+      }
+    }
+    uint32_t word[kCombineSlots][4];
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) word[j][e] = 0u;
+      if (rows[j] < 0) continue;
+      const uint16_t* src = y + (int64_t)rows[j] * n + col0;
+      if (VEC) {
+        // each expert-output row is read once: non-temporal (same-box A/B on
+        // the MoE workload's combine: 45.4-47.3 vs 48.6-50.0 us)
+        const v4i v = __builtin_nontemporal_load((const v4i*)src);
+        word[j][0] = (uint32_t)v.x; word[j][1] = (uint32_t)v.y; word[j][2] = (uint32_t)v.z; word[j][3] = (uint32_t)v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (2 * e < cnt) ? src[2 * e] : 0u;
+          const uint32_t hi = (2 * e + 1 < cnt) ? src[2 * e + 1] : 0u;
+          word[j][e] = lo | (hi << 16);
+        }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float yv = __uint_as_float(((word[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
-      acc[e] = fmaf(w, yv, acc[e]);
+    for (int j = 0; j < kCombineSlots; ++j) {
+      if (rows[j] < 0) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yv = __uint_as_float(((word[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+        acc[e] = fmaf(wts[j], yv, acc[e]);
+      }
     }
   }
   if (F32_OUT) {
