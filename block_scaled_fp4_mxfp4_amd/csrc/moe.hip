@@ -40,7 +40,8 @@ namespace {
 // routing
 // ---------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 256;   // four lanes per token, 64 tokens per workgroup
+constexpr int kRouteLanes = 8;       // lanes per token (one half-row)
+constexpr int kRouteThreads = 256;   // 32 tokens per workgroup
 
 // Order-preserving map of a float onto uint32 (negative zero taken as +0, so
 // the two zeros tie as they compare equal).
@@ -75,7 +76,7 @@ __device__ __forceinline__ void topk_insert(uint64_t (&bk)[K], int (&bi)[K], uin
   }
 }
 
-// Merge the partner lane's top-K list (DPP quad permute CTRL) into this one.
+// Merge the partner lane's top-K list (DPP control CTRL) into this one.
 // The lane whose bit MASK is clear holds the lower expert ids; both lanes end
 // with that lane's list as the base and the other's entries inserted into it
 // in order, so ties keep going to the lower id.
@@ -109,18 +110,21 @@ __device__ __forceinline__ void topk_merge(uint64_t (&bk)[K], int (&bi)[K], int 
   }
 }
 
-// Four lanes (one quad) per token: lane L takes the contiguous experts
-// [L * span, (L + 1) * span), keeps their top K in registers, then two quad
-// merges (lanes 0+1 and 2+3, then the pairs) give every lane the token's top K.
+// Eight lanes (one half-row) per token: lane L takes the contiguous experts
+// [L * span, (L + 1) * span), keeps their top K in registers, then three
+// merges (lanes 2i+1 into 2i, then pairs within a quad, then the quads through
+// the half-row mirror, lane i with lane 7 - i) give every lane the token's top
+// K.  Eight lanes rather than four halve each lane's serial insertions and
+// double the waves on the chip.
 template <int K, bool VEC>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int tokens,
                                                              int experts, int32_t* __restrict__ ids,
                                                              float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kRouteThreads / 4) + (threadIdx.x >> 2);
-  if (t >= tokens) return;   // uniform over the quad
-  const int q = lane & 3;
-  const int span = (experts + 3) >> 2;
+  const int t = blockIdx.x * (kRouteThreads / kRouteLanes) + (threadIdx.x / kRouteLanes);
+  if (t >= tokens) return;   // uniform over the token's lanes
+  const int q = lane & (kRouteLanes - 1);
+  const int span = (experts + kRouteLanes - 1) / kRouteLanes;
   const int e_lo = min(q * span, experts), e_hi = min(e_lo + span, experts);
   const float* row = logits + (int64_t)t * experts;
   uint64_t bk[K];
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
     bk[j] = 0;
     bi[j] = 0;
   }
-  if (VEC) {   // experts % 16 == 0 and 16-byte aligned rows: span is a multiple of 4
+  if (VEC) {   // experts % 32 == 0 and 16-byte aligned rows: span is a multiple of 4
     for (int e0 = e_lo; e0 < e_hi; e0 += 16) {
       float v[16];
 #pragma unroll
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   }
   topk_merge<K, 0xB1, 1>(bk, bi, lane);   // quad lanes 1,0,3,2
   topk_merge<K, 0x4E, 2>(bk, bi, lane);   // quad lanes 2,3,0,1
+  topk_merge<K, 0x141, 4>(bk, bi, lane);  // half-row mirror: lane i <-> 7 - i, the other quad
   // softmax of the selected logits; the first is the largest
   const float top = key_value((uint32_t)(bk[0] >> 1));
   float ex[K];
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   }
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    if ((j & 3) == q) {
+    if ((j & (kRouteLanes - 1)) == q) {
       ids[(int64_t)t * K + j] = bi[j];
       weights[(int64_t)t * K + j] = ex[j] / sum;
     }
@@ -515,9 +520,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
 template <int K>
 hipError_t launch_route_k(const float* logits, int tokens, int experts, int32_t* ids, float* weights,
                           hipStream_t stream) {
-  const int64_t blocks = ((int64_t)tokens + kRouteThreads / 4 - 1) / (kRouteThreads / 4);
+  const int64_t blocks = ((int64_t)tokens + kRouteThreads / kRouteLanes - 1) / (kRouteThreads / kRouteLanes);
   if (!grid_fits(blocks, kRouteThreads)) return hipErrorInvalidConfiguration;
-  const bool vec = experts % 16 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  const bool vec = experts % (4 * kRouteLanes) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
   if (vec)
     hipLaunchKernelGGL((route_kernel<K, true>), dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream, logits,
                        tokens, experts, ids, weights);
