@@ -44,7 +44,9 @@ def _check_route(lg: np.ndarray, top_k: int, dev):
     assert np.all(np.abs(got_w - rw) <= bound), float(np.max(np.abs(got_w - rw) / rw))
 
 
-ROUTE_CASES = [(1, 1, 1), (257, 8, 2), (1000, 64, 4), (333, 200, 8), (100, 256, 8), (64, 3, 3), (50, 65, 1)]
+# experts % 32 == 0 takes the vector loads (64, 256, 32, 96); 16 and 48 the scalar ones
+ROUTE_CASES = [(1, 1, 1), (257, 8, 2), (1000, 64, 4), (333, 200, 8), (100, 256, 8), (64, 3, 3), (50, 65, 1),
+               (77, 16, 4), (129, 48, 6), (64, 32, 8), (40, 96, 5)]
 
 
 @pytest.mark.parametrize("tokens,experts,top_k", ROUTE_CASES)
@@ -113,7 +115,9 @@ def test_permute_routing_of_moe_workload():
     log(f"rows per expert min {counts.min()} max {counts.max()} empty {(counts == 0).sum()}")
 
 
-SCATTER_CASES = [(1, 32, 1, 1), (37, 96, 8, 3), (300, 1024, 64, 4), (129, 4160, 5, 2)]
+# top_k > 4: the slots past the four whose rows load with the blocks
+SCATTER_CASES = [(1, 32, 1, 1), (37, 96, 8, 3), (300, 1024, 64, 4), (129, 4160, 5, 2), (41, 256, 16, 6),
+                 (23, 512, 12, 12)]
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
@@ -164,7 +168,9 @@ def _check_combine(y_bits, tr, w, dev):
     assert np.array_equal(to_np(out16.view(torch.int16)).view(np.uint16), oracle.f64_to_bf16_bits(got))
 
 
-COMBINE_CASES = [(1, 8, 1, 1), (300, 64, 4, 64), (97, 100, 3, 7), (1000, 2816, 4, 64), (5, 1, 2, 3)]
+# top_k > 8: more than one group of slots loaded together, the last one partial
+COMBINE_CASES = [(1, 8, 1, 1), (300, 64, 4, 64), (97, 100, 3, 7), (1000, 2816, 4, 64), (5, 1, 2, 3), (33, 200, 12, 16), (11, 100, 10, 12),
+                 (9, 72, 20, 24)]
 
 
 @pytest.mark.parametrize("tokens,n,top_k,experts", COMBINE_CASES)
