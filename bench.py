@@ -799,8 +799,8 @@ def measure_w4a8(args, dev, w, us):
     """W4A8 (MXFP8 activations x MXFP4 weights) on the primary, decode and MoE
     workloads: step = MXFP8 quantization of A + the W4A8 GEMM."""
     out = {"dtype": "mxfp8 e4m3 x mxfp4 e2m1, e8m0 block scales, fp32 accumulate, bf16 out",
-           "scales": "interleaved for the prefill and MoE GEMMs (written by the quantizers); decode: row-major A, "
-                     "prepacked weight"}
+           "scales": "interleaved for the prefill and MoE GEMMs (written by the quantizers); decode: both operands "
+                     "prepacked (A in the FP8 prepacked layout)"}
     eprint(f"[bench] W4A8 on {w.name}")
     b = DenseBench(w, dev, "mxfp8")
     s = b.timed(b.step, args.detail_steps, args.detail_warmup)
@@ -830,25 +830,32 @@ def measure_w4a8(args, dev, w, us):
         spp = b2.timed(b2.step_w4a8_both_prepacked, args.detail_steps, args.detail_warmup) if pre else None
         gbytes = w4a8_algorithmic_bytes(w2.m, w2.n, w2.k)
         gbs = gbytes / (g2["mean"] * 1e-3) / 1e9
-        out["decode"] = {
-            "workload": w2.name, "step_us": us(s2), "gemm_us": us(g2),
-            "step": ("quantize A to MXFP8 + W4A8 GEMM on the prepacked weight" if pre
-                     else "quantize A to MXFP8 + streaming W4A8 GEMM"),
-            "gemm_unpacked_weight_us": us(gu),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "kernel": "gemm_stream_pre_kernel (fp8 A)" if pre else "gemm_stream_kernel (fp8 A)"},
-        }
         if pre:
-            # both operands prepacked: A quantized straight into the FP8 prepacked layout, no LDS in the GEMM
+            # both operands prepacked leads, as on the MXFP4 decode line: A quantized
+            # straight into the FP8 prepacked layout, no LDS in the GEMM; the
+            # prepacked-weight kernel (row-major A) and the streaming kernel beside it
             gbs_pp = gbytes / (gpp["mean"] * 1e-3) / 1e9
-            out["decode"]["both_prepacked"] = {
+            out["decode"] = {
+                "workload": w2.name, "step_us": us(spp), "gemm_us": us(gpp),
                 "step": "quantize A into the FP8 prepacked layout + W4A8 GEMM on both prepacked operands",
-                "step_us": us(spp), "gemm_us": us(gpp), "gemm_gbs": round(gbs_pp, 1),
-                "gemm_hbm_frac": round(gbs_pp / PEAK_HBM_GBS, 4), "kernel": "gemm_pp_kernel (fp8 A)"}
-        eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s; "
-               f"row-major weight {gu['mean']*1e3:.2f} us"
-               + (f"; both prepacked {gpp['mean']*1e3:.2f} us)" if pre else ")"))
+                "roofline": {"bound": "hbm", "achieved": round(gbs_pp, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs_pp / PEAK_HBM_GBS, 4), "kernel": "gemm_pp_kernel (fp8 A)"},
+                "prepacked_weight": {
+                    "step": "quantize A to MXFP8 (row-major) + W4A8 GEMM on the prepacked weight",
+                    "step_us": us(s2), "gemm_us": us(g2), "gemm_gbs": round(gbs, 1),
+                    "gemm_hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "gemm_stream_pre_kernel (fp8 A)"},
+                "gemm_unpacked_weight_us": us(gu),
+            }
+            eprint(f"[bench] W4A8 {w2.name}: gemm {gpp['mean']*1e3:.2f} us ({gbs_pp:.0f} GB/s, both operands "
+                   f"prepacked; prepacked weight {g2['mean']*1e3:.2f} us, row-major weight {gu['mean']*1e3:.2f} us)")
+        else:
+            out["decode"] = {
+                "workload": w2.name, "step_us": us(s2), "gemm_us": us(g2),
+                "step": "quantize A to MXFP8 + streaming W4A8 GEMM",
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "gemm_stream_kernel (fp8 A)"},
+            }
+            eprint(f"[bench] W4A8 {w2.name}: gemm {g2['mean']*1e3:.2f} us ({gbs:.0f} GB/s)")
         del b2
     if args.moe != "none":
         wm = workloads.ALL[args.moe]
