@@ -1130,7 +1130,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA and read-rate probes")
     ap.add_argument("--only", choices=["step", "gemm", "gemm_prepacked", "step_prepacked", "gemm_prepacked_ab",
-                                       "gemm_w4a8_prepacked",
+                                       "gemm_w4a8_prepacked", "gemm_w4a8_both_prepacked",
                                        "step_prepacked_ab", "quantize_prepacked", "quantize", "quantize_b", "copy",
                                        "route", "permute", "scatter", "combine", "layer", "rmsnorm", "swiglu",
                                        "probe_mfma", "probe_mfma_w4a8", "step_quantize_both"],
